@@ -1,0 +1,296 @@
+/*
+ * llmk.h -- C ABI of libllmk.so: one greedy decode step of a Llama/Qwen-style
+ * grouped-query decoder, hand-written HIP for gfx950 (MI355X).
+ *
+ * Pages cited below (by title and section):
+ *   [llmk]  "LLM inference kernels" (docs.algenta.ai, compute-and-kernel-primitives)
+ *   [dops]  "decode-ops" (Hugging Face kernels page)
+ *   [xpu]   "Inside the engine" (cajeta.dev, xpu/llm/inside)
+ *   [fwd]   "The forward pass end to end: a Llama-style engine in 100 lines" (inferenceacademy.com)
+ *
+ * Conventions shared by every entry point
+ *   - Every function that does work returns an int32 status from the vocabulary
+ *     below. LLMK_OK means every check passed and the work is enqueued on `stream`
+ *     (a hipStream_t; NULL is the null stream). Nothing is synchronised.
+ *   - All checks run on the host before any HIP call and before any element is
+ *     read ([llmk] "Guarantees": exact-length checks before any read). On any
+ *     refusal nothing is enqueued and every output is left untouched.
+ *   - Check order when several fail: null pointer or unknown enum (578), then a
+ *     dimension < 1 or of the wrong sign (561), then a dimension > LLMK_MAX_DIM
+ *     (564), then buffer lengths in argument order (the specific code), then
+ *     value ranges (571-575), then workspace size (578).
+ *   - A C pointer carries no length, so every buffer is passed with its element
+ *     count; the pages' "claimed length vs real length" checks become a comparison
+ *     of those counts.
+ *   - Ownership: the caller allocates and owns all device memory (weights, K/V
+ *     pool, workspace, outputs). The library allocates no device memory and keeps
+ *     no pointer past the call ([xpu] "1. CausalLM": zero-allocation decode,
+ *     every buffer sized at load).
+ *   - Determinism: no float atomics; every reduction has a fixed order, so the
+ *     same inputs on the same GPU give bit-identical outputs ([llmk] "Guarantees").
+ *   - A launch failure reported by the HIP runtime after enqueue returns 579.
+ *   - Pointers named `*_h` or documented as host are host memory; every other
+ *     buffer pointer is device memory.
+ */
+#ifndef LLMK_H
+#define LLMK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status vocabulary. 560-571 are the llmk page's codes with their meanings
+ * ([llmk] "Status vocabulary and the shape checks (contract)"); the page reserves
+ * 560-579 for this family and renumbers nothing, so the codes this library adds
+ * take the free 572-579. 562/563 also serve as "first/second operand length
+ * mismatch" for entry points the page does not have (rope, add_rmsnorm). */
+enum {
+  LLMK_OK = 560,                      /* every element of every output is defined */
+  LLMK_EMPTY_DIMENSION = 561,         /* a required dimension was < 1 (or negative where 0 is allowed) */
+  LLMK_A_LENGTH_MISMATCH = 562,       /* first operand's length != its dimension */
+  LLMK_B_LENGTH_MISMATCH = 563,       /* second operand's length != its dimension */
+  LLMK_DIMENSION_TOO_LARGE = 564,     /* a dimension exceeds LLMK_MAX_DIM */
+  LLMK_CODE_OUT_OF_RANGE = 565,       /* not a code of this vocabulary (llmk_status_name's fallback) */
+  LLMK_CACHE_LENGTH_MISMATCH = 566,   /* cache fill claimed != recorded */
+  LLMK_NEW_LENGTH_MISMATCH = 567,     /* len(new_vals) != n_new */
+  LLMK_LOGITS_LENGTH_MISMATCH = 568,  /* len(logits) != rows * n */
+  LLMK_GEMV_A_LENGTH_MISMATCH = 569,  /* len(a) != m * n */
+  LLMK_GEMV_X_LENGTH_MISMATCH = 570,  /* len(x) != m */
+  LLMK_CACHE_CAPACITY_EXCEEDED = 571, /* the append would overrun the reserved buffer */
+  LLMK_TOKEN_OUT_OF_RANGE = 572,      /* token id not in [0, vocab) */
+  LLMK_POSITION_OUT_OF_RANGE = 573,   /* position < 0, or >= the RoPE table / max_seq */
+  LLMK_HEAD_SHAPE_INVALID = 574,      /* n_head % n_kv != 0, odd head_dim, head_dim > 256, or unaligned widths */
+  LLMK_SLOT_OUT_OF_RANGE = 575,       /* K/V pool slot not in [0, n_slots) */
+  LLMK_WEIGHT_LENGTH_MISMATCH = 576,  /* a model tensor's element count disagrees with the config */
+  LLMK_OUTPUT_LENGTH_MISMATCH = 577,  /* an output buffer's element count disagrees with the shape */
+  LLMK_INVALID_ARGUMENT = 578,        /* null pointer, unknown enum value, or workspace too small */
+  LLMK_DEVICE_ERROR = 579             /* the HIP runtime reported an error */
+};
+
+/* Ceiling on every dimension: refuses byte counts passed as element counts
+ * ([llmk] "Status vocabulary and the shape checks (contract)", "Guarantees"). */
+#define LLMK_MAX_DIM (1LL << 24)
+
+typedef enum { LLMK_F32 = 0, LLMK_BF16 = 1 } llmk_dtype;
+/* Half-split pairs (j, j + hd/2) are the GPT-NeoX/Qwen3 convention ([llmk] "Two
+ * gaps, not three"); interleaved pairs (2j, 2j+1) are the layout of [fwd] "The
+ * code". [dops] "Method" supports both. */
+typedef enum { LLMK_ROPE_HALF_SPLIT = 0, LLMK_ROPE_INTERLEAVED = 1 } llmk_rope_layout;
+
+/* ------------------------------------------------------------------------- */
+/* Contract: host-only, no device needed ([llmk] "Status vocabulary and the    */
+/* shape checks (contract)": four dimension checks, one per consumer).        */
+/* ------------------------------------------------------------------------- */
+
+/* Name of a status code, e.g. 562 -> "llmk_a_length_mismatch"; any other value
+ * returns the name of 565, "llmk_code_out_of_range". Static string, never NULL. */
+const char* llmk_status_name(int32_t code);
+
+/* residual add: 561 if n < 1; 564 if n > LLMK_MAX_DIM; 562 if len_a != n; 563 if len_b != n.
+ * [llmk] example: (6, 6, 6) -> 560; (6, 2, 6) -> 562. */
+int32_t llmk_residual_dims_check(int64_t n, int64_t len_a, int64_t len_b);
+
+/* K/V append: 561 if cache_len < 0 or n_new < 1 (an empty cache is allowed, an empty append is not,
+ * [llmk] "Guarantees"); 564 if either exceeds LLMK_MAX_DIM; 566 if len_cache != cache_len;
+ * 567 if len_new != n_new. */
+int32_t llmk_kv_append_dims_check(int64_t cache_len, int64_t len_cache, int64_t n_new, int64_t len_new);
+
+/* argmax: 561 if n < 1; 564 if n > LLMK_MAX_DIM; 568 if len_logits != n. */
+int32_t llmk_argmax_dims_check(int64_t n, int64_t len_logits);
+
+/* transposed GEMV: 561 if m < 1 or n < 1; 564 if m or n > LLMK_MAX_DIM; 569 if len_a != m*n;
+ * 570 if len_x != m. */
+int32_t llmk_gemv_dims_check(int64_t m, int64_t n, int64_t len_a, int64_t len_x);
+
+/* ------------------------------------------------------------------------- */
+/* Primitives (device buffers, caller's stream)                               */
+/* ------------------------------------------------------------------------- */
+
+/* Bytes of workspace llmk_gemv_t needs for an m x n matrix of dtype a_dtype (0 if none);
+ * negative status if the shape itself is refused. */
+int64_t llmk_gemv_t_workspace_bytes(int64_t m, int64_t n, int32_t a_dtype);
+
+/* y = A^T x: y[j] = sum_i A[i*n + j] * x[i], A is m x n row-major ([in][out]), fp32 accumulation.
+ * [llmk] "A parallel path for one frozen kernel's known-slow shape"; worked example
+ * A = [[1,2,3],[4,5,6]], x = [1,1] -> y = [5,7,9].
+ *   a      : device, m*n elements of a_dtype (LLMK_F32 or LLMK_BF16)
+ *   x      : device fp32 [m];   y: device fp32 [n] (written)
+ *   ws     : device workspace of len_ws bytes, >= llmk_gemv_t_workspace_bytes(m, n, a_dtype)
+ * Codes: 578 (null / dtype / workspace), 561, 564, 569, 570, 577 (len_y != n). */
+int32_t llmk_gemv_t(const void* a, int64_t len_a, int32_t a_dtype, const float* x, int64_t len_x,
+                    int64_t m, int64_t n, float* y, int64_t len_y, void* ws, int64_t len_ws, void* stream);
+
+/* y = W x (untransposed, row dots): y[r] = sum_c W[r*cols + c] * x[c]; the output head's form
+ * ([llmk] "A parallel path...": the untransposed lm_head; [fwd] "The code": matvec).
+ * Codes: 578, 561, 564, 569 (len_w != rows*cols), 570 (len_x != cols), 577 (len_y != rows). */
+int32_t llmk_gemv(const void* w, int64_t len_w, int32_t w_dtype, const float* x, int64_t len_x,
+                  int64_t rows, int64_t cols, float* y, int64_t len_y, void* stream);
+
+/* out[i] = a[i] + b[i], fp32 ([llmk] "Residual add"). out may alias a or b.
+ * Codes: 578, 561, 564, 562, 563, 577 (len_out != n). */
+int32_t llmk_residual_add(const float* a, int64_t len_a, const float* b, int64_t len_b, int64_t n,
+                          float* out, int64_t len_out, void* stream);
+
+/* For each of `rows` rows of width n: if x != NULL, residual += x (in place, fp32); then
+ * h = residual * (mean(residual^2) + eps)^(-1/2) * gain, with the square sum in fp32
+ * ([dops] "Usage", "Method"; [fwd] "The code": rmsnorm). x == NULL gives the plain norm.
+ *   residual: device fp32 [rows*n] (read, and written when x != NULL); x: device fp32 [rows*n] or NULL
+ *   gain: device fp32 [n]; h: device fp32 [rows*n] (written; may not alias residual)
+ * Codes: 578 (null residual/gain/h, eps <= 0 or not finite), 561, 564, 562 (len_r != rows*n),
+ * 563 (x given and len_x != rows*n), 576 (len_g != n), 577 (len_h != rows*n). */
+int32_t llmk_add_rmsnorm(float* residual, int64_t len_r, const float* x, int64_t len_x,
+                         const float* gain, int64_t len_g, int64_t rows, int64_t n, float eps,
+                         float* h, int64_t len_h, void* stream);
+
+/* out[i] = silu(gate[i]) * up[i], silu(z) = z / (1 + e^-z) ([dops] "Usage"; [fwd] "The code").
+ * Codes: 578, 561, 564, 562, 563, 577. */
+int32_t llmk_silu_mul(const float* gate, int64_t len_gate, const float* up, int64_t len_up, int64_t n,
+                      float* out, int64_t len_out, void* stream);
+
+/* RoPE cos/sin table: table[(p*(hd/2) + j)*2 + {0,1}] = {cos, sin}(p * base^(-2j/hd)) for
+ * p in [0, max_pos), j in [0, hd/2); angles and trig in fp64, stored fp32 ([dops] "Method":
+ * angle pairs in f64; [llmk] "The hot loop doesn't call kv_cache_append_flat": one shared table
+ * sized to the longest sequence). len_table must be max_pos * head_dim.
+ * Codes: 578 (null, base <= 1 or not finite), 561, 564, 574 (odd head_dim or > 256), 577. */
+int32_t llmk_rope_table_init(float* table, int64_t len_table, int64_t max_pos, int64_t head_dim,
+                             double base, void* stream);
+
+/* In-place rotary embedding of q [rows][n_q_heads][hd] and k [rows][n_k_heads][hd]; row r is at
+ * position pos0 + r. layout selects half-split or interleaved pairs ([dops] "Usage": rope(q, k, pos)
+ * in place). k may be NULL with n_k_heads == 0.
+ * Codes: 578, 561 (rows, n_q_heads, head_dim < 1, or n_k_heads < 0), 564, 574 (odd hd or > 256),
+ * 562 (len_q), 563 (len_k), 576 (len_table != max_pos*hd), 573 (pos0 < 0 or pos0 + rows > max_pos). */
+int32_t llmk_rope(float* q, int64_t len_q, float* k, int64_t len_k, int64_t rows, int64_t n_q_heads,
+                  int64_t n_k_heads, int64_t head_dim, int64_t pos0, const float* table, int64_t len_table,
+                  int64_t max_pos, int32_t layout, void* stream);
+
+/* In-place append into a reserved cache buffer: cache[cache_len + i] = round(new_vals[i]) for
+ * i in [0, n_new), rounded to the cache dtype (fp32 -> bf16 round-to-nearest-even, NaN kept).
+ * Existing content is never copied ([llmk] "KV-cache growth and greedy argmax" and "The hot loop
+ * doesn't call kv_cache_append_flat": the reserved-capacity, in-place append).
+ *   cache     : device buffer of `capacity` elements of `dtype`
+ *   cache_len : claimed filled length; len_cache: the caller's record of it (566 if different)
+ *   new_len_h : host int64, receives cache_len + n_new on success (may be NULL)
+ * Codes: 578, 561 (capacity < 1, cache_len < 0, n_new < 1), 564, 566, 567, 571 (cache_len + n_new >
+ * capacity). Worked example: cache [0..5], new [100,101,102] -> 9 elements, n = 9. */
+int32_t llmk_kv_append(void* cache, int64_t capacity, int32_t dtype, int64_t cache_len, int64_t len_cache,
+                       const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h, void* stream);
+
+/* Bytes of workspace llmk_gqa_attend needs. */
+int64_t llmk_gqa_attend_workspace_bytes(int64_t ctx_len, int64_t n_head, int64_t head_dim);
+
+/* Grouped-query decode attention for one query position over a cache of ctx_len positions:
+ * for head h with K/V head g = h / (n_head / n_kv): s_t = q_h . K[t][g] / sqrt(hd), w = softmax(s),
+ * out_h = sum_t w_t V[t][g] ([fwd] "The code": forward_token's attention loop). The context is
+ * split into chunks whose partial (max, sum, output) are merged by log-sum-exp ([xpu] "1. CausalLM":
+ * flash attention split across the context and reduced).
+ *   q: device fp32 [n_head][hd]; k_cache, v_cache: device [>= ctx_len][n_kv][hd] of kv_dtype
+ *   len_cache: elements in each of k_cache and v_cache; out: device fp32 [n_head][hd]
+ * Codes: 578, 561, 564, 574 (n_head % n_kv, odd hd, hd > 256), 562 (len_q), 563 (len_cache <
+ * ctx_len*n_kv*hd), 577 (len_out), 578 (workspace). */
+int32_t llmk_gqa_attend(const float* q, int64_t len_q, const void* k_cache, const void* v_cache,
+                        int64_t len_cache, int32_t kv_dtype, int64_t ctx_len, int64_t n_head, int64_t n_kv,
+                        int64_t head_dim, float* out, int64_t len_out, void* ws, int64_t len_ws, void* stream);
+
+/* Bytes of workspace llmk_argmax needs. */
+int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n);
+
+/* Greedy argmax per row: token[r] = the lowest i with logits[r*n + i] equal to the row maximum,
+ * logit[r] = that maximum ([llmk] "KV-cache growth and greedy argmax": first matching id on ties;
+ * [dops] "Correctness": exact against torch.argmax including ties). NaN counts as larger than every
+ * number and the first NaN wins (numpy/torch convention). +0.0 and -0.0 compare equal.
+ *   token: device int32 [rows]; logit: device fp32 [rows] (may be NULL)
+ * Codes: 578, 561, 564, 568 (len_logits != rows*n), 578 (workspace). */
+int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token,
+                    float* logit, void* ws, int64_t len_ws, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Model, K/V pool and the decode step                                        */
+/* ------------------------------------------------------------------------- */
+
+/* Decoder shape and numerics. head_dim is independent of d (Qwen3 shapes have n_head*head_dim != d). */
+typedef struct {
+  int64_t vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq;
+  double eps;          /* RMSNorm epsilon, inside the mean ([fwd] "The code": rmsnorm) */
+  double rope_base;    /* RoPE base (1e4 for the toy decoder, 1e6 Qwen3-shaped, 5e5 Llama-3-shaped) */
+  int32_t rope_layout; /* llmk_rope_layout */
+  int32_t w_dtype;     /* llmk_dtype of every weight matrix and the embedding table */
+  int32_t kv_dtype;    /* llmk_dtype of the K/V pool */
+} llmk_config;
+
+/* A device tensor and its element count. */
+typedef struct {
+  const void* ptr;
+  int64_t len;
+} llmk_tensor;
+
+/* Per-layer tensors, in this order, LLMK_LAYER_TENSORS per layer. Projections are in the transposed
+ * layout A[in][out] (y = A^T x), as the llmk page's decode driver uses them:
+ *   wq [d][H*hd]  wk [d][Hkv*hd]  wv [d][Hkv*hd]  wo [H*hd][d]
+ *   w_gate [d][F]  w_up [d][F]  w_down [F][d]  (w_dtype)
+ *   g_attn [d]  g_ffn [d]  (fp32 RMSNorm gains) */
+enum { LLMK_WQ = 0, LLMK_WK, LLMK_WV, LLMK_WO, LLMK_WGATE, LLMK_WUP, LLMK_WDOWN, LLMK_GATTN, LLMK_GFFN,
+       LLMK_LAYER_TENSORS };
+
+typedef struct {
+  llmk_tensor emb;         /* [vocab][d], w_dtype */
+  llmk_tensor w_out;       /* [vocab][d], w_dtype (untransposed output head) */
+  llmk_tensor g_final;     /* [d] fp32 */
+  llmk_tensor rope_table;  /* fp32 [max_seq][hd/2][2] from llmk_rope_table_init(max_seq, hd, rope_base) */
+  const llmk_tensor* layers; /* host array [n_layer * LLMK_LAYER_TENSORS] */
+} llmk_model;
+
+/* Slot-indexed device K/V pool ([xpu] "3. The K/V cache and the block store": one K and one V
+ * buffer per layer, slot s at element s * plane). Layer l's K buffer holds n_slots * capacity *
+ * n_kv * head_dim elements; position p of slot s, K/V head g, element i sits at
+ *   s * plane + p * n_kv * head_dim + g * head_dim + i,   plane = capacity * n_kv * head_dim.
+ * slot_len_h records how many positions each slot holds; decode steps check it (566) and advance it. */
+typedef struct {
+  void* const* k;          /* host array [n_layer] of device pointers */
+  void* const* v;          /* host array [n_layer] of device pointers */
+  int64_t n_layer, n_slots, capacity, n_kv, head_dim;
+  int32_t dtype;           /* llmk_dtype */
+  int64_t* slot_len_h;     /* host array [n_slots] */
+} llmk_kv_pool;
+
+/* Element offset of (slot, pos, kv_head) in each layer buffer of the pool (closed form above).
+ * Codes: 578, 575 (slot), 573 (pos not in [0, capacity)), 574 (kv_head not in [0, n_kv)). */
+int32_t llmk_kv_slot_offset(const llmk_kv_pool* pool, int64_t slot, int64_t pos, int64_t kv_head,
+                            int64_t* offset_h);
+
+/* Bytes of workspace a decode call needs for `batch` rows (negative status if cfg is refused). */
+int64_t llmk_decode_workspace_bytes(const llmk_config* cfg, int64_t batch);
+
+/* One decode step of one sequence ([fwd] "What a forward step does"; [llmk] "How this composes into
+ * a decode step"): x = emb[token]; per layer h = rmsnorm(x) g_attn; q|k|v = h W; RoPE(pos) on q, k;
+ * append k, v to the slot at pos; grouped-query attention over positions 0..pos; x += att Wo;
+ * h = rmsnorm(x) g_ffn; x += (silu(h Wgate) * (h Wup)) Wdown; then logits = W_out rmsnorm(x) g_final
+ * and the greedy token ([xpu] "1. CausalLM": the fused tail reads back one integer).
+ *   token, pos : the input token and its position; pos must equal pool->slot_len_h[slot] (566)
+ *   logits     : device fp32 [vocab] or NULL;  token_out: device int32 [1]
+ *   hidden     : device fp32 [n_layer][d] (the residual after each layer) or NULL
+ * On success pool->slot_len_h[slot] becomes pos + 1.
+ * Codes: 578, 561/564/574 (config), 576 (model tensor lengths), 575, 572, 573 (pos < 0 or >= max_seq),
+ * 566, 571 (pos >= capacity), 568 (len_logits != vocab), 577 (len_hidden), 578 (workspace). */
+int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                         int64_t token, int64_t pos, float* logits, int64_t len_logits, int32_t* token_out,
+                         float* hidden, int64_t len_hidden, void* ws, int64_t len_ws, void* stream);
+
+/* n_steps greedy steps of one sequence: step i consumes the token at position pos0 + i (token0 for
+ * i = 0, else the previous step's output, fed back on the device) and writes its greedy token to
+ * tokens_out[i]. The step's launch sequence is captured once into a HIP graph and replayed, and the
+ * host reads nothing between steps ([xpu] "4. The pipelined decode").
+ *   tokens_out: device int32 [n_steps] (len_tokens elements)
+ * Codes: as llmk_decode_step, plus 561/564 for n_steps and 571 if pos0 + n_steps > capacity,
+ * 573 if pos0 + n_steps > max_seq. On success slot_len_h[slot] = pos0 + n_steps. */
+int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                          int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
+                          void* ws, int64_t len_ws, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLMK_H */

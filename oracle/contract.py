@@ -1,0 +1,306 @@
+"""THE ORACLE's status expectations -- test infrastructure only.
+
+For every library entry point, the status code its arguments must produce, written
+independently of the library from the llmk page's status vocabulary ("LLM inference
+kernels", section "Status vocabulary and the shape checks (contract)") and its guarantees
+(section "Guarantees": exact-length checks before any read, zero or negative dimensions
+refused, n_new = 0 refused, every dimension bounded by 1 << 24).
+
+Precedence when several checks fail: null pointer / unknown enum (578), dimension < 1
+(561), dimension > MAX_DIM (564), buffer lengths in argument order, value ranges, workspace.
+Pointers are modelled as booleans (True = non-null); workspace sizes are the library's
+business, so these functions assume a sufficient workspace unless `ws_short` is given.
+"""
+from __future__ import annotations
+
+MAX_DIM = 1 << 24
+
+NAMES = {
+    560: "llmk_ok",
+    561: "llmk_empty_dimension",
+    562: "llmk_a_length_mismatch",
+    563: "llmk_b_length_mismatch",
+    564: "llmk_dimension_too_large",
+    565: "llmk_code_out_of_range",
+    566: "llmk_cache_length_mismatch",
+    567: "llmk_new_length_mismatch",
+    568: "llmk_logits_length_mismatch",
+    569: "llmk_gemv_a_length_mismatch",
+    570: "llmk_gemv_x_length_mismatch",
+    571: "llmk_cache_capacity_exceeded",
+    572: "llmk_token_out_of_range",
+    573: "llmk_position_out_of_range",
+    574: "llmk_head_shape_invalid",
+    575: "llmk_slot_out_of_range",
+    576: "llmk_weight_length_mismatch",
+    577: "llmk_output_length_mismatch",
+    578: "llmk_invalid_argument",
+    579: "llmk_device_error",
+}
+OK, EMPTY, A_LEN, B_LEN, TOO_LARGE, OUT_OF_RANGE = 560, 561, 562, 563, 564, 565
+CACHE_LEN, NEW_LEN, LOGITS_LEN, GEMV_A, GEMV_X, CAPACITY = 566, 567, 568, 569, 570, 571
+TOKEN, POSITION, HEAD_SHAPE, SLOT, WEIGHT_LEN, OUTPUT_LEN, INVALID, DEVICE = 572, 573, 574, 575, 576, 577, 578, 579
+
+
+def status_name(code: int) -> str:
+    return NAMES.get(int(code), NAMES[OUT_OF_RANGE])
+
+
+def _dims(*dims, allow_zero=()):
+    """561 / 564 over dimensions; indices in allow_zero may be 0 (but not negative)."""
+    for i, v in enumerate(dims):
+        if v < (0 if i in allow_zero else 1):
+            return EMPTY
+    for v in dims:
+        if v > MAX_DIM:
+            return TOO_LARGE
+    return OK
+
+
+# ---- the four contract checks -------------------------------------------------------------
+
+def residual_dims_check(n, len_a, len_b):
+    c = _dims(n)
+    if c != OK:
+        return c
+    if len_a != n:
+        return A_LEN
+    if len_b != n:
+        return B_LEN
+    return OK
+
+
+def kv_append_dims_check(cache_len, len_cache, n_new, len_new):
+    c = _dims(cache_len, n_new, allow_zero=(0,))
+    if c != OK:
+        return c
+    if len_cache != cache_len:
+        return CACHE_LEN
+    if len_new != n_new:
+        return NEW_LEN
+    return OK
+
+
+def argmax_dims_check(n, len_logits):
+    c = _dims(n)
+    if c != OK:
+        return c
+    return LOGITS_LEN if len_logits != n else OK
+
+
+def gemv_dims_check(m, n, len_a, len_x):
+    c = _dims(m, n)
+    if c != OK:
+        return c
+    if len_a != m * n:
+        return GEMV_A
+    if len_x != m:
+        return GEMV_X
+    return OK
+
+
+# ---- entry points ----------------------------------------------------------------------------
+
+def gemv_t(a=True, len_a=0, a_dtype=0, x=True, len_x=0, m=0, n=0, y=True, len_y=0, ws=True, ws_short=False):
+    if not (a and x and y and ws) or a_dtype not in (0, 1):
+        return INVALID
+    c = gemv_dims_check(m, n, len_a, len_x)
+    if c != OK:
+        return c
+    if len_y != n:
+        return OUTPUT_LEN
+    return INVALID if ws_short else OK
+
+
+def gemv(w=True, len_w=0, w_dtype=0, x=True, len_x=0, rows=0, cols=0, y=True, len_y=0):
+    if not (w and x and y) or w_dtype not in (0, 1):
+        return INVALID
+    c = _dims(rows, cols)
+    if c != OK:
+        return c
+    if len_w != rows * cols:
+        return GEMV_A
+    if len_x != cols:
+        return GEMV_X
+    if len_y != rows:
+        return OUTPUT_LEN
+    return OK
+
+
+def residual_add(a=True, len_a=0, b=True, len_b=0, n=0, out=True, len_out=0):
+    if not (a and b and out):
+        return INVALID
+    c = residual_dims_check(n, len_a, len_b)
+    if c != OK:
+        return c
+    return OUTPUT_LEN if len_out != n else OK
+
+
+def add_rmsnorm(residual=True, len_r=0, x=True, len_x=0, gain=True, len_g=0, rows=0, n=0, eps=1e-5, h=True, len_h=0):
+    import math
+    if not (residual and gain and h) or not (eps > 0 and math.isfinite(eps)):
+        return INVALID
+    c = _dims(rows, n)
+    if c != OK:
+        return c
+    if len_r != rows * n:
+        return A_LEN
+    if x and len_x != rows * n:
+        return B_LEN
+    if len_g != n:
+        return WEIGHT_LEN
+    if len_h != rows * n:
+        return OUTPUT_LEN
+    return OK
+
+
+def silu_mul(gate=True, len_gate=0, up=True, len_up=0, n=0, out=True, len_out=0):
+    if not (gate and up and out):
+        return INVALID
+    c = _dims(n)
+    if c != OK:
+        return c
+    if len_gate != n:
+        return A_LEN
+    if len_up != n:
+        return B_LEN
+    return OUTPUT_LEN if len_out != n else OK
+
+
+def _head_dim_ok(hd):
+    return hd % 2 == 0 and hd <= 256
+
+
+def rope_table_init(table=True, len_table=0, max_pos=0, head_dim=0, base=1e4):
+    import math
+    if not table or not (math.isfinite(base) and base > 1.0):
+        return INVALID
+    c = _dims(max_pos, head_dim)
+    if c != OK:
+        return c
+    if not _head_dim_ok(head_dim):
+        return HEAD_SHAPE
+    return OUTPUT_LEN if len_table != max_pos * head_dim else OK
+
+
+def rope(q=True, len_q=0, k=True, len_k=0, rows=0, n_q_heads=0, n_k_heads=0, head_dim=0, pos0=0, table=True,
+         len_table=0, max_pos=0, layout=0):
+    if not q or not table or layout not in (0, 1) or (not k and n_k_heads != 0):
+        return INVALID
+    c = _dims(rows, n_q_heads, head_dim, max_pos, n_k_heads, allow_zero=(4,))
+    if c != OK:
+        return c
+    if not _head_dim_ok(head_dim):
+        return HEAD_SHAPE
+    if len_q != rows * n_q_heads * head_dim:
+        return A_LEN
+    if len_k != rows * n_k_heads * head_dim:
+        return B_LEN
+    if len_table != max_pos * head_dim:
+        return WEIGHT_LEN
+    if pos0 < 0 or pos0 + rows > max_pos:
+        return POSITION
+    return OK
+
+
+def kv_append(cache=True, capacity=0, dtype=0, cache_len=0, len_cache=0, new_vals=True, len_new=0, n_new=0):
+    if not (cache and new_vals) or dtype not in (0, 1):
+        return INVALID
+    c = _dims(capacity)
+    if c != OK:
+        return c
+    c = kv_append_dims_check(cache_len, len_cache, n_new, len_new)
+    if c != OK:
+        return c
+    if cache_len + n_new > capacity:
+        return CAPACITY
+    return OK
+
+
+def gqa_attend(q=True, len_q=0, k_cache=True, v_cache=True, len_cache=0, kv_dtype=0, ctx_len=0, n_head=0, n_kv=0,
+               head_dim=0, out=True, len_out=0, ws=True, ws_short=False):
+    if not (q and k_cache and v_cache and out and ws) or kv_dtype not in (0, 1):
+        return INVALID
+    c = _dims(ctx_len, n_head, n_kv, head_dim)
+    if c != OK:
+        return c
+    if n_head % n_kv != 0 or not _head_dim_ok(head_dim):
+        return HEAD_SHAPE
+    if len_q != n_head * head_dim:
+        return A_LEN
+    if len_cache < ctx_len * n_kv * head_dim:
+        return B_LEN
+    if len_out != n_head * head_dim:
+        return OUTPUT_LEN
+    return INVALID if ws_short else OK
+
+
+def argmax(logits=True, len_logits=0, rows=0, n=0, token=True, ws=True, ws_short=False):
+    if not (logits and token and ws):
+        return INVALID
+    c = _dims(rows, n)
+    if c != OK:
+        return c
+    if len_logits != rows * n:
+        return LOGITS_LEN
+    return INVALID if ws_short else OK
+
+
+def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head):
+    """(status, offset): offset = slot*plane + pos*n_kv*hd + kv_head*hd, plane = capacity*n_kv*hd
+    (the pool layout of "Inside the engine", section "3. The K/V cache and the block store")."""
+    if not (0 <= slot < n_slots):
+        return SLOT, None
+    if not (0 <= pos < capacity):
+        return POSITION, None
+    if not (0 <= kv_head < n_kv):
+        return HEAD_SHAPE, None
+    plane = capacity * n_kv * head_dim
+    return OK, slot * plane + pos * n_kv * head_dim + kv_head * head_dim
+
+
+def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4, rope_layout=0,
+                 w_dtype=0, kv_dtype=0):
+    import math
+    if rope_layout not in (0, 1) or w_dtype not in (0, 1) or kv_dtype not in (0, 1):
+        return INVALID
+    if not (eps > 0 and math.isfinite(eps)) or not (rope_base > 1 and math.isfinite(rope_base)):
+        return INVALID
+    c = _dims(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq)
+    if c != OK:
+        return c
+    if n_head % n_kv != 0 or not _head_dim_ok(head_dim):
+        return HEAD_SHAPE
+    vec = 4 if w_dtype == 0 else 8
+    for width in (d, n_head * head_dim, n_kv * head_dim, hidden):
+        if width % vec != 0:
+            return HEAD_SHAPE
+    return OK
+
+
+def decode_step(cfg: dict, lens_ok=True, n_slots=1, capacity=0, slot=0, slot_len=0, token=0, pos=0,
+                logits=False, len_logits=0, hidden=False, len_hidden=0, pool_ok=True, ws_short=False):
+    """Expected status of llmk_decode_step. cfg is a dict of config_check's arguments; lens_ok says
+    whether every model tensor length matches the config; pool_ok whether the pool's shape matches it."""
+    c = config_check(**cfg)
+    if c != OK:
+        return c
+    if not lens_ok:
+        return WEIGHT_LEN
+    if not pool_ok:
+        return INVALID
+    if not (0 <= slot < n_slots):
+        return SLOT
+    if not (0 <= token < cfg["vocab"]):
+        return TOKEN
+    if pos < 0 or pos >= cfg["max_seq"]:
+        return POSITION
+    if pos != slot_len:
+        return CACHE_LEN
+    if pos >= capacity:
+        return CAPACITY
+    if logits and len_logits != cfg["vocab"]:
+        return LOGITS_LEN
+    if hidden and len_hidden != cfg["n_layer"] * cfg["d"]:
+        return OUTPUT_LEN
+    return INVALID if ws_short else OK
