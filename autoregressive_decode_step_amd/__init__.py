@@ -1,0 +1,326 @@
+"""Python binding of libllmk.so: one greedy decode step of a Llama/Qwen-style grouped-query decoder,
+hand-written HIP for gfx950 (MI355X).
+
+Argument marshalling only: every function here passes device pointers, element counts and the current
+torch stream to the C entry point of the same name (prefix `llmk_` dropped) and returns its int32
+status. Every step of the decode path runs in the library's kernels; there is no Python or CPU
+fallback, and importing this package fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libllmk.so")
+
+OK = 560
+F32, BF16 = 0, 1
+ROPE_HALF_SPLIT, ROPE_INTERLEAVED = 0, 1
+WQ, WK, WV, WO, WGATE, WUP, WDOWN, GATTN, GFFN = range(9)
+LAYER_TENSORS = 9
+MAX_DIM = 1 << 24
+
+
+class LlmkError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {code} {status_name(code)}" if what else f"{code} {status_name(code)}")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libllmk.so is not built ({LIB_PATH}); run `python autoregressive_decode_step_amd/build.py`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i64, _i32, _f32, _f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_double
+
+
+class Config(ctypes.Structure):
+    """llmk_config"""
+    _fields_ = [("vocab", _i64), ("d", _i64), ("n_layer", _i64), ("n_head", _i64), ("n_kv", _i64),
+                ("head_dim", _i64), ("hidden", _i64), ("max_seq", _i64), ("eps", _f64), ("rope_base", _f64),
+                ("rope_layout", _i32), ("w_dtype", _i32), ("kv_dtype", _i32)]
+
+
+class Tensor(ctypes.Structure):
+    """llmk_tensor"""
+    _fields_ = [("ptr", _p), ("len", _i64)]
+
+
+class ModelStruct(ctypes.Structure):
+    """llmk_model"""
+    _fields_ = [("emb", Tensor), ("w_out", Tensor), ("g_final", Tensor), ("rope_table", Tensor),
+                ("layers", ctypes.POINTER(Tensor))]
+
+
+class PoolStruct(ctypes.Structure):
+    """llmk_kv_pool"""
+    _fields_ = [("k", ctypes.POINTER(_p)), ("v", ctypes.POINTER(_p)), ("n_layer", _i64), ("n_slots", _i64),
+                ("capacity", _i64), ("n_kv", _i64), ("head_dim", _i64), ("dtype", _i32),
+                ("slot_len_h", ctypes.POINTER(_i64))]
+
+
+_SIGS = {
+    "llmk_status_name": ([_i32], ctypes.c_char_p),
+    "llmk_residual_dims_check": ([_i64, _i64, _i64], _i32),
+    "llmk_kv_append_dims_check": ([_i64, _i64, _i64, _i64], _i32),
+    "llmk_argmax_dims_check": ([_i64, _i64], _i32),
+    "llmk_gemv_dims_check": ([_i64, _i64, _i64, _i64], _i32),
+    "llmk_gemv_t_workspace_bytes": ([_i64, _i64, _i32], _i64),
+    "llmk_gemv_t": ([_p, _i64, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_gemv": ([_p, _i64, _i32, _p, _i64, _i64, _i64, _p, _i64, _p], _i32),
+    "llmk_residual_add": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p], _i32),
+    "llmk_add_rmsnorm": ([_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _f32, _p, _i64, _p], _i32),
+    "llmk_silu_mul": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p], _i32),
+    "llmk_rope_table_init": ([_p, _i64, _i64, _i64, _f64, _p], _i32),
+    "llmk_rope": ([_p, _i64, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p, _i64, _i64, _i32, _p], _i32),
+    "llmk_kv_append": ([_p, _i64, _i32, _i64, _i64, _p, _i64, _i64, ctypes.POINTER(_i64), _p], _i32),
+    "llmk_gqa_attend_workspace_bytes": ([_i64, _i64, _i64], _i64),
+    "llmk_gqa_attend": ([_p, _i64, _p, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_argmax_workspace_bytes": ([_i64, _i64], _i64),
+    "llmk_argmax": ([_p, _i64, _i64, _i64, _p, _p, _p, _i64, _p], _i32),
+    "llmk_kv_slot_offset": ([ctypes.POINTER(PoolStruct), _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
+    "llmk_decode_workspace_bytes": ([ctypes.POINTER(Config), _i64], _i64),
+    "llmk_decode_step": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _i64,
+                          _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_decode_steps": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _i64,
+                           _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_decode_kernel_count": ([ctypes.POINTER(Config)], _i64),
+    "llmk_decode_step_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
+                                   _i64, _i64, _i64, _p, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _len(t):
+    return 0 if t is None else t.numel()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def status_name(code: int) -> str:
+    return lib.llmk_status_name(int(code)).decode()
+
+
+def check(code: int, what: str = "") -> None:
+    if code != OK:
+        raise LlmkError(code, what)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# contract
+# ---------------------------------------------------------------------------------------------------------
+
+def residual_dims_check(n, len_a, len_b) -> int:
+    return lib.llmk_residual_dims_check(n, len_a, len_b)
+
+
+def kv_append_dims_check(cache_len, len_cache, n_new, len_new) -> int:
+    return lib.llmk_kv_append_dims_check(cache_len, len_cache, n_new, len_new)
+
+
+def argmax_dims_check(n, len_logits) -> int:
+    return lib.llmk_argmax_dims_check(n, len_logits)
+
+
+def gemv_dims_check(m, n, len_a, len_x) -> int:
+    return lib.llmk_gemv_dims_check(m, n, len_a, len_x)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# primitives (torch device tensors)
+# ---------------------------------------------------------------------------------------------------------
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def gemv_t_workspace_bytes(m, n, a_dtype) -> int:
+    return lib.llmk_gemv_t_workspace_bytes(m, n, a_dtype)
+
+
+def gemv_t(a, x, y, m, n, ws, stream=None) -> int:
+    """y = A^T x; a holds m*n elements (fp32 or bf16)."""
+    return lib.llmk_gemv_t(_ptr(a), _len(a), _dtype_code(a), _ptr(x), _len(x), m, n, _ptr(y), _len(y), _ptr(ws),
+                            _len(ws), _stream(stream))
+
+
+def gemv(w, x, y, rows, cols, stream=None) -> int:
+    """y = W x (row dots)."""
+    return lib.llmk_gemv(_ptr(w), _len(w), _dtype_code(w), _ptr(x), _len(x), rows, cols, _ptr(y), _len(y),
+                         _stream(stream))
+
+
+def residual_add(a, b, out, n=None, stream=None) -> int:
+    n = _len(a) if n is None else n
+    return lib.llmk_residual_add(_ptr(a), _len(a), _ptr(b), _len(b), n, _ptr(out), _len(out), _stream(stream))
+
+
+def add_rmsnorm(residual, x, gain, h, rows, n, eps, stream=None) -> int:
+    return lib.llmk_add_rmsnorm(_ptr(residual), _len(residual), _ptr(x), _len(x), _ptr(gain), _len(gain), rows, n,
+                                eps, _ptr(h), _len(h), _stream(stream))
+
+
+def silu_mul(gate, up, out, n=None, stream=None) -> int:
+    n = _len(gate) if n is None else n
+    return lib.llmk_silu_mul(_ptr(gate), _len(gate), _ptr(up), _len(up), n, _ptr(out), _len(out), _stream(stream))
+
+
+def rope_table_init(table, max_pos, head_dim, base, stream=None) -> int:
+    return lib.llmk_rope_table_init(_ptr(table), _len(table), max_pos, head_dim, base, _stream(stream))
+
+
+def rope(q, k, rows, n_q_heads, n_k_heads, head_dim, pos0, table, max_pos, layout, stream=None) -> int:
+    return lib.llmk_rope(_ptr(q), _len(q), _ptr(k), _len(k), rows, n_q_heads, n_k_heads, head_dim, pos0, _ptr(table),
+                         _len(table), max_pos, layout, _stream(stream))
+
+
+def kv_append(cache, cache_len, len_cache, new_vals, n_new=None, stream=None):
+    """Returns (status, new_len)."""
+    n_new = _len(new_vals) if n_new is None else n_new
+    out = _i64(-1)
+    st = lib.llmk_kv_append(_ptr(cache), _len(cache), _dtype_code(cache), cache_len, len_cache, _ptr(new_vals),
+                            _len(new_vals), n_new, ctypes.byref(out), _stream(stream))
+    return st, out.value
+
+
+def gqa_attend_workspace_bytes(ctx_len, n_head, head_dim) -> int:
+    return lib.llmk_gqa_attend_workspace_bytes(ctx_len, n_head, head_dim)
+
+
+def gqa_attend(q, k_cache, v_cache, ctx_len, n_head, n_kv, head_dim, out, ws, stream=None) -> int:
+    return lib.llmk_gqa_attend(_ptr(q), _len(q), _ptr(k_cache), _ptr(v_cache), _len(k_cache), _dtype_code(k_cache),
+                               ctx_len, n_head, n_kv, head_dim, _ptr(out), _len(out), _ptr(ws), _len(ws),
+                               _stream(stream))
+
+
+def argmax_workspace_bytes(rows, n) -> int:
+    return lib.llmk_argmax_workspace_bytes(rows, n)
+
+
+def argmax(logits, rows, n, token, logit, ws, stream=None) -> int:
+    return lib.llmk_argmax(_ptr(logits), _len(logits), rows, n, _ptr(token), _ptr(logit), _ptr(ws), _len(ws),
+                           _stream(stream))
+
+
+# ---------------------------------------------------------------------------------------------------------
+# model, pool, decode
+# ---------------------------------------------------------------------------------------------------------
+
+def make_config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4,
+                rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16) -> Config:
+    return Config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps, rope_base, rope_layout, w_dtype,
+                  kv_dtype)
+
+
+class Model:
+    """Device weights in the llmk_model layout. `layers` is a list of dicts with keys wq, wk, wv, wo, w_gate,
+    w_up, w_down (w_dtype, [in][out]) and g_attn, g_ffn (fp32)."""
+
+    KEYS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "g_attn", "g_ffn")
+
+    def __init__(self, cfg: Config, emb, w_out, g_final, rope_table, layers):
+        self.cfg = cfg
+        self._keep = [emb, w_out, g_final, rope_table] + [L[k] for L in layers for k in self.KEYS]
+        arr = (Tensor * (len(layers) * LAYER_TENSORS))()
+        for l, L in enumerate(layers):
+            for i, k in enumerate(self.KEYS):
+                arr[l * LAYER_TENSORS + i] = Tensor(_ptr(L[k]), _len(L[k]))
+        self._layers = arr
+        self.struct = ModelStruct(Tensor(_ptr(emb), _len(emb)), Tensor(_ptr(w_out), _len(w_out)),
+                                  Tensor(_ptr(g_final), _len(g_final)), Tensor(_ptr(rope_table), _len(rope_table)),
+                                  arr)
+
+
+class KVPool:
+    """Slot-indexed K/V pool: per layer one K and one V tensor of n_slots*capacity*n_kv*head_dim elements."""
+
+    def __init__(self, n_layer, n_slots, capacity, n_kv, head_dim, dtype, device="cuda", tensors=None):
+        import torch
+        tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+        n = n_slots * capacity * n_kv * head_dim
+        if tensors is None:
+            self.k = [torch.zeros(n, dtype=tdt, device=device) for _ in range(n_layer)]
+            self.v = [torch.zeros(n, dtype=tdt, device=device) for _ in range(n_layer)]
+        else:
+            self.k, self.v = tensors
+        self.slot_len = np.zeros(n_slots, dtype=np.int64)
+        self._kp = (_p * n_layer)(*[_ptr(t) for t in self.k])
+        self._vp = (_p * n_layer)(*[_ptr(t) for t in self.v])
+        self.struct = PoolStruct(self._kp, self._vp, n_layer, n_slots, capacity, n_kv, head_dim, dtype,
+                                 self.slot_len.ctypes.data_as(ctypes.POINTER(_i64)))
+        self.capacity, self.n_kv, self.head_dim, self.n_slots = capacity, n_kv, head_dim, n_slots
+
+    def slot_view(self, layer: int, slot: int, which: str = "k"):
+        """[capacity][n_kv][head_dim] view of one slot of one layer's K or V buffer."""
+        t = (self.k if which == "k" else self.v)[layer]
+        plane = self.capacity * self.n_kv * self.head_dim
+        return t[slot * plane:(slot + 1) * plane].view(self.capacity, self.n_kv, self.head_dim)
+
+
+def kv_slot_offset(pool: KVPool, slot, pos, kv_head):
+    out = _i64(-1)
+    st = lib.llmk_kv_slot_offset(ctypes.byref(pool.struct), slot, pos, kv_head, ctypes.byref(out))
+    return st, out.value
+
+
+def decode_workspace_bytes(cfg: Config, batch: int = 1) -> int:
+    return lib.llmk_decode_workspace_bytes(ctypes.byref(cfg), batch)
+
+
+def decode_step(cfg: Config, model: Model, pool: KVPool, slot, token, pos, token_out, ws, logits=None, hidden=None,
+                stream=None) -> int:
+    return lib.llmk_decode_step(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot, token,
+                                pos, _ptr(logits), _len(logits), _ptr(token_out), _ptr(hidden), _len(hidden),
+                                _ptr(ws), _len(ws), _stream(stream))
+
+
+def decode_steps(cfg: Config, model: Model, pool: KVPool, slot, token0, pos0, n_steps, tokens_out, ws,
+                 stream=None) -> int:
+    return lib.llmk_decode_steps(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot,
+                                 token0, pos0, n_steps, _ptr(tokens_out), _len(tokens_out), _ptr(ws), _len(ws),
+                                 _stream(stream))
+
+
+def decode_kernel_count(cfg: Config) -> int:
+    return lib.llmk_decode_kernel_count(ctypes.byref(cfg))
+
+
+def decode_step_profiled(cfg: Config, model: Model, pool: KVPool, slot, token, pos, token_out, ws, stream=None):
+    """Returns (status, per-kernel milliseconds in launch order)."""
+    n = decode_kernel_count(cfg)
+    ms = (_f32 * max(n, 1))()
+    st = lib.llmk_decode_step_profiled(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot,
+                                       token, pos, _ptr(token_out), ms, n, _ptr(ws), _len(ws), _stream(stream))
+    return st, [ms[i] for i in range(n)]

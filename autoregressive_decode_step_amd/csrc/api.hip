@@ -1,0 +1,724 @@
+// C ABI of libllmk: host-side checks (all before any HIP call), workspace layout and the assembly of
+// the decode step from the gfx950 kernels. See include/llmk.h for the contract of every entry point.
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+#include "llmk.h"
+
+using namespace llmk;
+
+namespace {
+
+constexpr int64_t kMaxDim = LLMK_MAX_DIM;
+constexpr int64_t kAlign = 256;
+
+inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// 561 / 564 over a list of dimensions (all must be >= 1)
+int32_t dims_check(std::initializer_list<int64_t> dims) {
+  for (int64_t d : dims)
+    if (d < 1) return LLMK_EMPTY_DIMENSION;
+  for (int64_t d : dims)
+    if (d > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  return LLMK_OK;
+}
+
+inline bool is_dtype(int32_t t) { return t == LLMK_F32 || t == LLMK_BF16; }
+inline int64_t dtype_size(int32_t t) { return t == LLMK_BF16 ? 2 : 4; }
+inline bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+inline bool rope_head_dim_ok(int64_t hd) { return hd >= 2 && hd <= 256 && hd % 2 == 0; }
+inline bool attn_head_dim_ok(int64_t hd) { return hd >= 2 && hd <= 256 && pow2(hd); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t finish(hipError_t e) { return e == hipSuccess ? LLMK_OK : LLMK_DEVICE_ERROR; }
+
+// Workspace carving: a bump allocator over the caller's buffer (nullptr base = size query).
+struct Carve {
+  char* base;
+  int64_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T> T* take(int64_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(count * (int64_t)sizeof(T));
+    return p;
+  }
+};
+
+// ---- gemv_t plan shared by the primitive and its workspace query ---------------------------------------
+
+struct GemvT {
+  GemvParams p{};
+  int vec1 = 0;
+};
+
+GemvT plan_gemv_t(int64_t m, int64_t n, int32_t dt, const void* a) {
+  GemvT g;
+  const int64_t vec = dt == LLMK_BF16 ? 8 : 4;
+  g.vec1 = (n % vec != 0) || (a && !aligned16(a));
+  g.p.K = m;
+  g.p.N = n;
+  gemv_plan(g.p, dt == LLMK_BF16, g.vec1, 512, 64);
+  return g;
+}
+
+int64_t gemv_t_ws(const GemvT& g) {
+  if (g.p.ksplit <= 1) return 0;
+  Carve c(nullptr);
+  c.take<float>((int64_t)g.p.ksplit * g.p.N);
+  c.take<unsigned>(g.p.n_cblk);
+  return c.off;
+}
+
+// Workspace for either path (vector or scalar), so the answer does not depend on the pointer's alignment.
+int64_t gemv_t_ws_any(int64_t m, int64_t n, int32_t dt) {
+  int64_t w = gemv_t_ws(plan_gemv_t(m, n, dt, nullptr));
+  GemvT s;
+  s.vec1 = 1;
+  s.p.K = m;
+  s.p.N = n;
+  gemv_plan(s.p, dt == LLMK_BF16, 1, 512, 64);
+  const int64_t ws = gemv_t_ws(s);
+  return ws > w ? ws : w;
+}
+
+// ---- decode plan --------------------------------------------------------------------------------------
+
+int32_t config_check(const llmk_config* c) {
+  if (!c) return LLMK_INVALID_ARGUMENT;
+  if (!is_dtype(c->w_dtype) || !is_dtype(c->kv_dtype)) return LLMK_INVALID_ARGUMENT;
+  if (c->rope_layout != LLMK_ROPE_HALF_SPLIT && c->rope_layout != LLMK_ROPE_INTERLEAVED) return LLMK_INVALID_ARGUMENT;
+  if (!(c->eps > 0) || !isfinite(c->eps) || !(c->rope_base > 1.0) || !isfinite(c->rope_base))
+    return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({c->vocab, c->d, c->n_layer, c->n_head, c->n_kv, c->head_dim, c->hidden, c->max_seq});
+  if (st != LLMK_OK) return st;
+  if (c->n_head % c->n_kv != 0 || c->n_head / c->n_kv > 8 || !attn_head_dim_ok(c->head_dim))
+    return LLMK_HEAD_SHAPE_INVALID;
+  const int64_t vec = c->w_dtype == LLMK_BF16 ? 8 : 4;
+  const int64_t widths[4] = {c->d, c->n_head * c->head_dim, c->n_kv * c->head_dim, c->hidden};
+  for (int64_t w : widths)
+    if (w % vec != 0) return LLMK_HEAD_SHAPE_INVALID;
+  if (c->d > 64 * vec * 16) return LLMK_HEAD_SHAPE_INVALID;  // the head kernel holds d in registers
+  return LLMK_OK;
+}
+
+struct DecodePlan {
+  GemvParams qkv{}, o{}, gu{}, down{};
+  HeadParams head{};
+  AttnParams attn{};
+  // workspace regions
+  DecodeState* state = nullptr;
+  float* x = nullptr;
+  float* q = nullptr;
+  float* att = nullptr;
+  float* u = nullptr;
+  float* logits = nullptr;
+  float* partial = nullptr;
+  unsigned* counters = nullptr;
+  float* attn_part = nullptr;
+  float* head_val = nullptr;
+  int32_t* head_idx = nullptr;
+  int64_t bytes = 0;
+  int n_gemv_counters = 0;
+};
+
+constexpr int kGemvTargetBlocks = 512;
+constexpr int kGemvMinRows = 64;
+
+void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
+  const int bf = c->w_dtype == LLMK_BF16;
+  const int64_t d = c->d, qd = c->n_head * c->head_dim, kvd = c->n_kv * c->head_dim, F = c->hidden;
+  D.qkv.K = d; D.qkv.N = qd + 2 * kvd; D.qkv.n0 = qd; D.qkv.n1 = kvd;
+  D.o.K = qd; D.o.N = d;
+  D.gu.K = d; D.gu.N = F;
+  D.down.K = F; D.down.N = d;
+  gemv_plan(D.qkv, bf, 0, kGemvTargetBlocks, kGemvMinRows);
+  gemv_plan(D.o, bf, 0, kGemvTargetBlocks, kGemvMinRows);
+  gemv_plan(D.gu, bf, 0, kGemvTargetBlocks, kGemvMinRows);
+  gemv_plan(D.down, bf, 0, kGemvTargetBlocks, kGemvMinRows);
+  D.head.rows = c->vocab;
+  D.head.cols = d;
+  head_plan(D.head, bf);
+  D.attn.H = (int32_t)c->n_head;
+  D.attn.Hkv = (int32_t)c->n_kv;
+  D.attn.hd = (int32_t)c->head_dim;
+  D.attn.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
+  attn_plan(D.attn, c->max_seq);
+
+  int64_t part = 0;
+  const GemvParams* gs[4] = {&D.qkv, &D.o, &D.gu, &D.down};
+  int ncnt = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int nacc = (i == 2) ? 2 : 1;
+    const int64_t f = gs[i]->ksplit > 1 ? (int64_t)gs[i]->ksplit * nacc * gs[i]->N : 0;
+    if (f > part) part = f;
+    if (gs[i]->n_cblk > ncnt) ncnt = gs[i]->n_cblk;
+  }
+  D.n_gemv_counters = ncnt;
+  Carve cv(ws);
+  D.state = cv.take<DecodeState>(1);
+  D.x = cv.take<float>(d);
+  D.q = cv.take<float>(qd);
+  D.att = cv.take<float>(qd);
+  D.u = cv.take<float>(F);
+  D.logits = cv.take<float>(c->vocab);
+  D.partial = cv.take<float>(part > 0 ? part : 1);
+  D.counters = cv.take<unsigned>(ncnt + c->n_kv + 1);
+  D.attn_part = cv.take<float>((int64_t)D.attn.n_parts * c->n_head * (c->head_dim + 2));
+  D.head_val = cv.take<float>(D.head.n_blocks);
+  D.head_idx = cv.take<int32_t>(D.head.n_blocks);
+  D.bytes = cv.off;
+}
+
+int64_t counters_total(const llmk_config* c, const DecodePlan& D) { return D.n_gemv_counters + c->n_kv + 1; }
+
+const llmk_tensor& layer_t(const llmk_model* m, int64_t l, int which) { return m->layers[l * LLMK_LAYER_TENSORS + which]; }
+
+int32_t model_check(const llmk_config* c, const llmk_model* m) {
+  if (!m || !m->layers) return LLMK_INVALID_ARGUMENT;
+  if (!m->emb.ptr || !m->w_out.ptr || !m->g_final.ptr || !m->rope_table.ptr) return LLMK_INVALID_ARGUMENT;
+  for (int64_t l = 0; l < c->n_layer; ++l)
+    for (int t = 0; t < LLMK_LAYER_TENSORS; ++t)
+      if (!layer_t(m, l, t).ptr) return LLMK_INVALID_ARGUMENT;
+  return LLMK_OK;
+}
+
+int32_t model_lengths(const llmk_config* c, const llmk_model* m) {
+  const int64_t d = c->d, qd = c->n_head * c->head_dim, kvd = c->n_kv * c->head_dim, F = c->hidden;
+  if (m->emb.len != c->vocab * d || m->w_out.len != c->vocab * d || m->g_final.len != d) return LLMK_WEIGHT_LENGTH_MISMATCH;
+  if (m->rope_table.len != c->max_seq * c->head_dim) return LLMK_WEIGHT_LENGTH_MISMATCH;
+  const int64_t want[LLMK_LAYER_TENSORS] = {d * qd, d * kvd, d * kvd, qd * d, d * F, d * F, F * d, d, d};
+  for (int64_t l = 0; l < c->n_layer; ++l)
+    for (int t = 0; t < LLMK_LAYER_TENSORS; ++t)
+      if (layer_t(m, l, t).len != want[t]) return LLMK_WEIGHT_LENGTH_MISMATCH;
+  return LLMK_OK;
+}
+
+bool weights_aligned(const llmk_config* c, const llmk_model* m) {
+  if (!aligned16(m->emb.ptr) || !aligned16(m->w_out.ptr)) return false;
+  for (int64_t l = 0; l < c->n_layer; ++l)
+    for (int t = 0; t < LLMK_WDOWN + 1; ++t)
+      if (!aligned16(layer_t(m, l, t).ptr)) return false;
+  return true;
+}
+
+int32_t pool_check(const llmk_config* c, const llmk_kv_pool* p) {
+  if (!p || !p->k || !p->v || !p->slot_len_h) return LLMK_INVALID_ARGUMENT;
+  if (p->n_layer != c->n_layer || p->n_kv != c->n_kv || p->head_dim != c->head_dim || p->dtype != c->kv_dtype)
+    return LLMK_INVALID_ARGUMENT;
+  for (int64_t l = 0; l < p->n_layer; ++l)
+    if (!p->k[l] || !p->v[l]) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({p->n_slots, p->capacity});
+  return st;
+}
+
+// Enqueue one decode step's kernels. Token and position are read from D.state on the device.
+hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, int64_t slot,
+                        DecodePlan& D, float* logits, int32_t* token_out, float* hidden, hipStream_t s,
+                        hipEvent_t* ev = nullptr) {
+  const int bf = c->w_dtype == LLMK_BF16;
+  const int64_t d = c->d, kvd = c->n_kv * c->head_dim;
+  const int64_t plane = pool->capacity * kvd;
+  const int64_t kv_off = slot * plane;
+  const int64_t kvsz = dtype_size(c->kv_dtype);
+  unsigned* gcnt = D.counters;
+  unsigned* acnt = D.counters + D.n_gemv_counters;
+  unsigned* hcnt = acnt + c->n_kv;
+  hipError_t e = hipSuccess;
+  int kidx = 0;
+  // optional timing: event 2k before and 2k+1 after kernel k, on the kernels' own stream
+  auto mark = [&](int which) -> hipError_t { return ev ? hipEventRecord(ev[2 * kidx + which], s) : hipSuccess; };
+  auto timed = [&](hipError_t launched) -> hipError_t {
+    if (launched != hipSuccess) return launched;
+    hipError_t r = mark(1);
+    ++kidx;
+    return r;
+  };
+  for (int64_t l = 0; l < c->n_layer; ++l) {
+    // 1. h = rmsnorm(x) g_attn;  q|k|v = h W;  RoPE;  k, v -> pool
+    GemvParams g = D.qkv;
+    g.w0 = layer_t(m, l, LLMK_WQ).ptr;
+    g.w1 = layer_t(m, l, LLMK_WK).ptr;
+    g.w2 = layer_t(m, l, LLMK_WV).ptr;
+    if (l == 0) { g.in = m->emb.ptr; g.in_is_w = 1; g.in_state = D.state; }
+    else { g.in = D.x; g.in_is_w = 0; g.in_state = nullptr; }
+    g.gain = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
+    g.eps = (float)c->eps;
+    g.partial = D.partial;
+    g.counters = gcnt;
+    g.y = D.q;
+    g.state = D.state;
+    g.kcache = pool->k[l];
+    g.vcache = pool->v[l];
+    g.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
+    g.kv_off = kv_off;
+    g.head_dim = (int32_t)c->head_dim;
+    g.rope_layout = c->rope_layout;
+    g.rope_table = static_cast<const float*>(m->rope_table.ptr);
+    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(g, GM_QKV, bf, 0, s))) != hipSuccess) return e;
+    // 2. attention over positions 0..pos of this slot
+    AttnParams a = D.attn;
+    a.q = D.q;
+    a.k = static_cast<const char*>(pool->k[l]) + kv_off * kvsz;
+    a.v = static_cast<const char*>(pool->v[l]) + kv_off * kvsz;
+    a.state = D.state;
+    a.ctx = 0;
+    a.part = D.attn_part;
+    a.counters = acnt;
+    a.out = D.att;
+    if ((e = mark(0)) != hipSuccess || (e = timed(attn_launch(a, s))) != hipSuccess) return e;
+    // 3. x = x + att Wo   (layer 0: x = emb[token] + att Wo)
+    GemvParams o = D.o;
+    o.w0 = layer_t(m, l, LLMK_WO).ptr;
+    o.in = D.att;
+    o.in_is_w = 0;
+    o.gain = nullptr;
+    o.partial = D.partial;
+    o.counters = gcnt;
+    o.x = D.x;
+    if (l == 0) { o.base = m->emb.ptr; o.base_is_w = 1; o.base_state = D.state; }
+    else { o.base = D.x; o.base_is_w = 0; o.base_state = nullptr; }
+    o.hidden = nullptr;
+    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(o, GM_RESID, bf, 0, s))) != hipSuccess) return e;
+    // 4. h = rmsnorm(x) g_ffn;  u = silu(h Wgate) * (h Wup)
+    GemvParams gu = D.gu;
+    gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
+    gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
+    gu.in = D.x;
+    gu.in_is_w = 0;
+    gu.gain = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
+    gu.eps = (float)c->eps;
+    gu.partial = D.partial;
+    gu.counters = gcnt;
+    gu.y = D.u;
+    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(gu, GM_GATEUP, bf, 0, s))) != hipSuccess) return e;
+    // 5. x = x + u Wdown
+    GemvParams dn = D.down;
+    dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
+    dn.in = D.u;
+    dn.in_is_w = 0;
+    dn.gain = nullptr;
+    dn.partial = D.partial;
+    dn.counters = gcnt;
+    dn.x = D.x;
+    dn.base = D.x;
+    dn.base_is_w = 0;
+    dn.hidden = hidden ? hidden + l * d : nullptr;
+    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(dn, GM_RESID, bf, 0, s))) != hipSuccess) return e;
+  }
+  // tail: logits = W_out rmsnorm(x) g_final; greedy token; state advances
+  HeadParams h = D.head;
+  h.w = m->w_out.ptr;
+  h.x = D.x;
+  h.gain = static_cast<const float*>(m->g_final.ptr);
+  h.eps = (float)c->eps;
+  h.y = logits ? logits : D.logits;
+  h.part_val = D.head_val;
+  h.part_idx = D.head_idx;
+  h.counter = hcnt;
+  h.token_out = token_out;
+  h.logit_out = nullptr;
+  h.state = D.state;
+  if ((e = mark(0)) != hipSuccess) return e;
+  return timed(head_launch(h, bf, s));
+}
+
+// Common checks of decode_step / decode_steps, in the documented order.
+int32_t decode_checks(const llmk_config* cfg, const llmk_model* model, const llmk_kv_pool* pool, int64_t slot,
+                      int64_t token, int64_t pos, int64_t n_steps, const void* out_ptr, const void* ws) {
+  if (!cfg || !model || !pool || !out_ptr || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return st;
+  if ((st = model_check(cfg, model)) != LLMK_OK) return st;
+  if ((st = model_lengths(cfg, model)) != LLMK_OK) return st;
+  if ((st = pool_check(cfg, pool)) != LLMK_OK) return st;
+  if (!weights_aligned(cfg, model)) return LLMK_INVALID_ARGUMENT;
+  if (slot < 0 || slot >= pool->n_slots) return LLMK_SLOT_OUT_OF_RANGE;
+  if (token < 0 || token >= cfg->vocab) return LLMK_TOKEN_OUT_OF_RANGE;
+  if (pos < 0 || pos + n_steps > cfg->max_seq) return LLMK_POSITION_OUT_OF_RANGE;
+  if (pos != pool->slot_len_h[slot]) return LLMK_CACHE_LENGTH_MISMATCH;
+  if (pos + n_steps > pool->capacity) return LLMK_CACHE_CAPACITY_EXCEEDED;
+  return LLMK_OK;
+}
+
+}  // namespace
+
+// =========================================================================================================
+// C ABI
+// =========================================================================================================
+
+extern "C" {
+
+const char* llmk_status_name(int32_t code) {
+  switch (code) {
+    case 560: return "llmk_ok";
+    case 561: return "llmk_empty_dimension";
+    case 562: return "llmk_a_length_mismatch";
+    case 563: return "llmk_b_length_mismatch";
+    case 564: return "llmk_dimension_too_large";
+    case 565: return "llmk_code_out_of_range";
+    case 566: return "llmk_cache_length_mismatch";
+    case 567: return "llmk_new_length_mismatch";
+    case 568: return "llmk_logits_length_mismatch";
+    case 569: return "llmk_gemv_a_length_mismatch";
+    case 570: return "llmk_gemv_x_length_mismatch";
+    case 571: return "llmk_cache_capacity_exceeded";
+    case 572: return "llmk_token_out_of_range";
+    case 573: return "llmk_position_out_of_range";
+    case 574: return "llmk_head_shape_invalid";
+    case 575: return "llmk_slot_out_of_range";
+    case 576: return "llmk_weight_length_mismatch";
+    case 577: return "llmk_output_length_mismatch";
+    case 578: return "llmk_invalid_argument";
+    case 579: return "llmk_device_error";
+    default: return "llmk_code_out_of_range";
+  }
+}
+
+int32_t llmk_residual_dims_check(int64_t n, int64_t len_a, int64_t len_b) {
+  int32_t st = dims_check({n});
+  if (st != LLMK_OK) return st;
+  if (len_a != n) return LLMK_A_LENGTH_MISMATCH;
+  if (len_b != n) return LLMK_B_LENGTH_MISMATCH;
+  return LLMK_OK;
+}
+
+int32_t llmk_kv_append_dims_check(int64_t cache_len, int64_t len_cache, int64_t n_new, int64_t len_new) {
+  if (cache_len < 0 || n_new < 1) return LLMK_EMPTY_DIMENSION;
+  if (cache_len > kMaxDim || n_new > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  if (len_cache != cache_len) return LLMK_CACHE_LENGTH_MISMATCH;
+  if (len_new != n_new) return LLMK_NEW_LENGTH_MISMATCH;
+  return LLMK_OK;
+}
+
+int32_t llmk_argmax_dims_check(int64_t n, int64_t len_logits) {
+  int32_t st = dims_check({n});
+  if (st != LLMK_OK) return st;
+  return len_logits != n ? LLMK_LOGITS_LENGTH_MISMATCH : LLMK_OK;
+}
+
+int32_t llmk_gemv_dims_check(int64_t m, int64_t n, int64_t len_a, int64_t len_x) {
+  int32_t st = dims_check({m, n});
+  if (st != LLMK_OK) return st;
+  if (len_a != m * n) return LLMK_GEMV_A_LENGTH_MISMATCH;
+  if (len_x != m) return LLMK_GEMV_X_LENGTH_MISMATCH;
+  return LLMK_OK;
+}
+
+int64_t llmk_gemv_t_workspace_bytes(int64_t m, int64_t n, int32_t a_dtype) {
+  if (!is_dtype(a_dtype)) return -LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({m, n});
+  if (st != LLMK_OK) return -st;
+  return gemv_t_ws_any(m, n, a_dtype);
+}
+
+int32_t llmk_gemv_t(const void* a, int64_t len_a, int32_t a_dtype, const float* x, int64_t len_x, int64_t m, int64_t n,
+                    float* y, int64_t len_y, void* ws, int64_t len_ws, void* stream) {
+  if (!a || !x || !y || !ws || !is_dtype(a_dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = llmk_gemv_dims_check(m, n, len_a, len_x);
+  if (st != LLMK_OK) return st;
+  if (len_y != n) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  GemvT g = plan_gemv_t(m, n, a_dtype, a);
+  if (len_ws < gemv_t_ws_any(m, n, a_dtype)) return LLMK_INVALID_ARGUMENT;
+  // the vector path needs 16-byte aligned rows; otherwise the scalar path (its own, smaller plan)
+  g.p.w0 = a;
+  g.p.in = x;
+  g.p.in_is_w = 0;
+  g.p.y = y;
+  if (g.p.ksplit > 1) {
+    Carve cv(ws);
+    g.p.partial = cv.take<float>((int64_t)g.p.ksplit * g.p.N);
+    g.p.counters = cv.take<unsigned>(g.p.n_cblk);
+    if (cv.off > len_ws) return LLMK_INVALID_ARGUMENT;
+    hipError_t e = fill_u32_launch(g.p.counters, g.p.n_cblk, 0u, as_stream(stream));
+    if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  }
+  return finish(gemv_launch(g.p, GM_PLAIN, a_dtype == LLMK_BF16, g.vec1, as_stream(stream)));
+}
+
+int32_t llmk_gemv(const void* w, int64_t len_w, int32_t w_dtype, const float* x, int64_t len_x, int64_t rows,
+                  int64_t cols, float* y, int64_t len_y, void* stream) {
+  if (!w || !x || !y || !is_dtype(w_dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, cols});
+  if (st != LLMK_OK) return st;
+  if (len_w != rows * cols) return LLMK_GEMV_A_LENGTH_MISMATCH;
+  if (len_x != cols) return LLMK_GEMV_X_LENGTH_MISMATCH;
+  if (len_y != rows) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  const int64_t vec = w_dtype == LLMK_BF16 ? 8 : 4;
+  if (cols % vec != 0 || !aligned16(w) || cols > 64 * vec * 16)
+    return finish(rowdot_simple_launch(w, w_dtype == LLMK_BF16, x, y, rows, cols, as_stream(stream)));
+  HeadParams h{};
+  h.w = w;
+  h.rows = rows;
+  h.cols = cols;
+  head_plan(h, w_dtype == LLMK_BF16);
+  h.x = x;
+  h.gain = nullptr;
+  h.y = y;
+  h.part_val = nullptr;
+  return finish(head_launch(h, w_dtype == LLMK_BF16, as_stream(stream)));
+}
+
+int32_t llmk_residual_add(const float* a, int64_t len_a, const float* b, int64_t len_b, int64_t n, float* out,
+                          int64_t len_out, void* stream) {
+  if (!a || !b || !out) return LLMK_INVALID_ARGUMENT;
+  int32_t st = llmk_residual_dims_check(n, len_a, len_b);
+  if (st != LLMK_OK) return st;
+  if (len_out != n) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  return finish(residual_add_launch(a, b, out, n, as_stream(stream)));
+}
+
+int32_t llmk_add_rmsnorm(float* residual, int64_t len_r, const float* x, int64_t len_x, const float* gain,
+                         int64_t len_g, int64_t rows, int64_t n, float eps, float* h, int64_t len_h, void* stream) {
+  if (!residual || !gain || !h || !(eps > 0.0f) || !isfinite(eps)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, n});
+  if (st != LLMK_OK) return st;
+  if (len_r != rows * n) return LLMK_A_LENGTH_MISMATCH;
+  if (x && len_x != rows * n) return LLMK_B_LENGTH_MISMATCH;
+  if (len_g != n) return LLMK_WEIGHT_LENGTH_MISMATCH;
+  if (len_h != rows * n) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  return finish(add_rmsnorm_launch(residual, x, gain, rows, n, eps, h, as_stream(stream)));
+}
+
+int32_t llmk_silu_mul(const float* gate, int64_t len_gate, const float* up, int64_t len_up, int64_t n, float* out,
+                      int64_t len_out, void* stream) {
+  if (!gate || !up || !out) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({n});
+  if (st != LLMK_OK) return st;
+  if (len_gate != n) return LLMK_A_LENGTH_MISMATCH;
+  if (len_up != n) return LLMK_B_LENGTH_MISMATCH;
+  if (len_out != n) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  return finish(silu_mul_launch(gate, up, out, n, as_stream(stream)));
+}
+
+int32_t llmk_rope_table_init(float* table, int64_t len_table, int64_t max_pos, int64_t head_dim, double base,
+                             void* stream) {
+  if (!table || !(base > 1.0) || !isfinite(base)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({max_pos, head_dim});
+  if (st != LLMK_OK) return st;
+  if (!rope_head_dim_ok(head_dim)) return LLMK_HEAD_SHAPE_INVALID;
+  if (len_table != max_pos * head_dim) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  return finish(rope_table_launch(table, max_pos, head_dim, base, as_stream(stream)));
+}
+
+int32_t llmk_rope(float* q, int64_t len_q, float* k, int64_t len_k, int64_t rows, int64_t n_q_heads, int64_t n_k_heads,
+                  int64_t head_dim, int64_t pos0, const float* table, int64_t len_table, int64_t max_pos,
+                  int32_t layout, void* stream) {
+  if (!q || !table || (layout != LLMK_ROPE_HALF_SPLIT && layout != LLMK_ROPE_INTERLEAVED) || (!k && n_k_heads != 0))
+    return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, n_q_heads, head_dim, max_pos});
+  if (st != LLMK_OK) return st;
+  if (n_k_heads < 0) return LLMK_EMPTY_DIMENSION;
+  if (n_k_heads > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  if (!rope_head_dim_ok(head_dim)) return LLMK_HEAD_SHAPE_INVALID;
+  if (len_q != rows * n_q_heads * head_dim) return LLMK_A_LENGTH_MISMATCH;
+  if (len_k != rows * n_k_heads * head_dim) return LLMK_B_LENGTH_MISMATCH;
+  if (len_table != max_pos * head_dim) return LLMK_WEIGHT_LENGTH_MISMATCH;
+  if (pos0 < 0 || pos0 + rows > max_pos) return LLMK_POSITION_OUT_OF_RANGE;
+  return finish(rope_launch(q, k, rows, n_q_heads, n_k_heads, head_dim, pos0, table, layout, as_stream(stream)));
+}
+
+int32_t llmk_kv_append(void* cache, int64_t capacity, int32_t dtype, int64_t cache_len, int64_t len_cache,
+                       const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h, void* stream) {
+  if (!cache || !new_vals || !is_dtype(dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({capacity});
+  if (st != LLMK_OK) return st;
+  st = llmk_kv_append_dims_check(cache_len, len_cache, n_new, len_new);
+  if (st != LLMK_OK) return st;
+  if (cache_len + n_new > capacity) return LLMK_CACHE_CAPACITY_EXCEEDED;
+  st = finish(kv_append_launch(cache, dtype == LLMK_BF16, cache_len, new_vals, n_new, as_stream(stream)));
+  if (st == LLMK_OK && new_len_h) *new_len_h = cache_len + n_new;
+  return st;
+}
+
+int64_t llmk_gqa_attend_workspace_bytes(int64_t ctx_len, int64_t n_head, int64_t head_dim) {
+  int32_t st = dims_check({ctx_len, n_head, head_dim});
+  if (st != LLMK_OK) return -st;
+  Carve c(nullptr);
+  c.take<float>(attn_part_floats(n_head, head_dim));
+  c.take<unsigned>(n_head);
+  return c.off;
+}
+
+int32_t llmk_gqa_attend(const float* q, int64_t len_q, const void* k_cache, const void* v_cache, int64_t len_cache,
+                        int32_t kv_dtype, int64_t ctx_len, int64_t n_head, int64_t n_kv, int64_t head_dim, float* out,
+                        int64_t len_out, void* ws, int64_t len_ws, void* stream) {
+  if (!q || !k_cache || !v_cache || !out || !ws || !is_dtype(kv_dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({ctx_len, n_head, n_kv, head_dim});
+  if (st != LLMK_OK) return st;
+  if (n_head % n_kv != 0 || n_head / n_kv > 8 || !attn_head_dim_ok(head_dim)) return LLMK_HEAD_SHAPE_INVALID;
+  if (len_q != n_head * head_dim) return LLMK_A_LENGTH_MISMATCH;
+  if (len_cache < ctx_len * n_kv * head_dim) return LLMK_B_LENGTH_MISMATCH;
+  if (len_out != n_head * head_dim) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (len_ws < llmk_gqa_attend_workspace_bytes(ctx_len, n_head, head_dim)) return LLMK_INVALID_ARGUMENT;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return LLMK_INVALID_ARGUMENT;
+  AttnParams a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.kv_is_bf16 = kv_dtype == LLMK_BF16;
+  a.H = (int32_t)n_head;
+  a.Hkv = (int32_t)n_kv;
+  a.hd = (int32_t)head_dim;
+  a.ctx = (int32_t)ctx_len;
+  a.state = nullptr;
+  attn_plan(a, ctx_len);
+  Carve cv(ws);
+  a.part = cv.take<float>(attn_part_floats(n_head, head_dim));
+  a.counters = cv.take<unsigned>(n_head);
+  a.out = out;
+  hipError_t e = fill_u32_launch(a.counters, n_kv, 0u, as_stream(stream));
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  return finish(attn_launch(a, as_stream(stream)));
+}
+
+int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n) {
+  int32_t st = dims_check({rows, n});
+  if (st != LLMK_OK) return -st;
+  const int64_t bpr = n >= 65536 ? 64 : (n + 1023) / 1024;
+  Carve c(nullptr);
+  c.take<float>(rows * bpr);
+  c.take<int32_t>(rows * bpr);
+  c.take<unsigned>(rows);
+  return c.off;
+}
+
+int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token, float* logit,
+                    void* ws, int64_t len_ws, void* stream) {
+  if (!logits || !token || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, n});
+  if (st != LLMK_OK) return st;
+  if (len_logits != rows * n) return LLMK_LOGITS_LENGTH_MISMATCH;
+  if (len_ws < llmk_argmax_workspace_bytes(rows, n)) return LLMK_INVALID_ARGUMENT;
+  if (rows > 65535) return LLMK_DIMENSION_TOO_LARGE;
+  const int64_t bpr = n >= 65536 ? 64 : (n + 1023) / 1024;
+  Carve cv(ws);
+  float* pv = cv.take<float>(rows * bpr);
+  int32_t* pi = cv.take<int32_t>(rows * bpr);
+  unsigned* cnt = cv.take<unsigned>(rows);
+  hipError_t e = fill_u32_launch(cnt, rows, 0u, as_stream(stream));
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  return finish(argmax_launch(logits, rows, n, token, logit, pv, pi, cnt, (int32_t)bpr, as_stream(stream)));
+}
+
+int32_t llmk_kv_slot_offset(const llmk_kv_pool* pool, int64_t slot, int64_t pos, int64_t kv_head, int64_t* offset_h) {
+  if (!pool || !offset_h) return LLMK_INVALID_ARGUMENT;
+  if (slot < 0 || slot >= pool->n_slots) return LLMK_SLOT_OUT_OF_RANGE;
+  if (pos < 0 || pos >= pool->capacity) return LLMK_POSITION_OUT_OF_RANGE;
+  if (kv_head < 0 || kv_head >= pool->n_kv) return LLMK_HEAD_SHAPE_INVALID;
+  const int64_t row = pool->n_kv * pool->head_dim;
+  *offset_h = slot * pool->capacity * row + pos * row + kv_head * pool->head_dim;
+  return LLMK_OK;
+}
+
+int64_t llmk_decode_workspace_bytes(const llmk_config* cfg, int64_t batch) {
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return -st;
+  if (batch != 1) return -LLMK_INVALID_ARGUMENT;
+  DecodePlan D;
+  plan_decode(cfg, nullptr, D);
+  return D.bytes;
+}
+
+int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                         int64_t token, int64_t pos, float* logits, int64_t len_logits, int32_t* token_out,
+                         float* hidden, int64_t len_hidden, void* ws, int64_t len_ws, void* stream) {
+  int32_t st = decode_checks(cfg, model, pool, slot, token, pos, 1, token_out, ws);
+  if (st != LLMK_OK) return st;
+  if (logits && len_logits != cfg->vocab) return LLMK_LOGITS_LENGTH_MISMATCH;
+  if (hidden && len_hidden != cfg->n_layer * cfg->d) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  DecodePlan D;
+  plan_decode(cfg, nullptr, D);
+  if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
+  plan_decode(cfg, ws, D);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
+  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
+  if (e == hipSuccess) e = enqueue_step(cfg, model, pool, slot, D, logits, token_out, hidden, s);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  pool->slot_len_h[slot] = pos + 1;
+  return LLMK_OK;
+}
+
+int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                          int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
+                          void* ws, int64_t len_ws, void* stream) {
+  if (!cfg || !model || !pool || !tokens_out || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return st;
+  if (n_steps < 1) return LLMK_EMPTY_DIMENSION;
+  if (n_steps > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  st = decode_checks(cfg, model, pool, slot, token0, pos0, n_steps, tokens_out, ws);
+  if (st != LLMK_OK) return st;
+  if (len_tokens != n_steps) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  DecodePlan D;
+  plan_decode(cfg, nullptr, D);
+  if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
+  plan_decode(cfg, ws, D);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
+  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token0, (int32_t)pos0, s);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+
+  // capture one step (token and position come from the device state) and replay it n_steps times
+  hipStream_t cs = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t ee = enqueue_step(cfg, model, pool, slot, D, nullptr, tokens_out, nullptr, cs);
+    e = hipStreamEndCapture(cs, &graph);
+    if (ee != hipSuccess) e = ee;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  for (int64_t i = 0; e == hipSuccess && i < n_steps; ++i) e = hipGraphLaunch(exec, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (cs) (void)hipStreamDestroy(cs);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  pool->slot_len_h[slot] = pos0 + n_steps;
+  return LLMK_OK;
+}
+
+int64_t llmk_decode_kernel_count(const llmk_config* cfg) {
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return -st;
+  return 5 * cfg->n_layer + 1;
+}
+
+int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                  int64_t token, int64_t pos, int32_t* token_out, float* kernel_ms_h,
+                                  int64_t len_kernel_ms, void* ws, int64_t len_ws, void* stream) {
+  if (!kernel_ms_h) return LLMK_INVALID_ARGUMENT;
+  int32_t st = decode_checks(cfg, model, pool, slot, token, pos, 1, token_out, ws);
+  if (st != LLMK_OK) return st;
+  const int64_t nk = 5 * cfg->n_layer + 1;
+  if (len_kernel_ms < nk) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  DecodePlan D;
+  plan_decode(cfg, nullptr, D);
+  if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
+  plan_decode(cfg, ws, D);
+  hipStream_t s = as_stream(stream);
+  hipEvent_t* ev = new hipEvent_t[2 * nk]();
+  hipError_t e = hipSuccess;
+  int64_t made = 0;
+  for (; made < 2 * nk && e == hipSuccess; ++made) e = hipEventCreate(&ev[made]);
+  if (e == hipSuccess) e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
+  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
+  if (e == hipSuccess) e = enqueue_step(cfg, model, pool, slot, D, nullptr, token_out, nullptr, s, ev);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  for (int64_t k = 0; e == hipSuccess && k < nk; ++k) e = hipEventElapsedTime(&kernel_ms_h[k], ev[2 * k], ev[2 * k + 1]);
+  for (int64_t i = 0; i < made; ++i)
+    if (ev[i]) (void)hipEventDestroy(ev[i]);
+  delete[] ev;
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  pool->slot_len_h[slot] = pos + 1;
+  return LLMK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Device helpers shared by the gfx950 kernels of libllmk.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LLMK_WAVE 64
+
+namespace llmk {
+
+typedef uint16_t bf16_t;
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// ---- typed element access ----------------------------------------------------------------------
+
+template <typename T> __device__ __forceinline__ float load_elem(const T* p, int64_t i);
+template <> __device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T> __device__ __forceinline__ void store_elem(T* p, int64_t i, float v);
+template <> __device__ __forceinline__ void store_elem<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+// A VEC-element slice of a row, loaded as one raw register group (16 B for the vector paths).
+template <typename T, int VEC> struct Raw;
+template <> struct Raw<bf16_t, 8> { typedef uint4 type; };
+template <> struct Raw<float, 4> { typedef uint4 type; };
+template <> struct Raw<bf16_t, 1> { typedef uint16_t type; };
+template <> struct Raw<float, 1> { typedef float type; };
+
+template <typename T, int VEC>
+__device__ __forceinline__ typename Raw<T, VEC>::type load_raw(const T* p) {
+  return *reinterpret_cast<const typename Raw<T, VEC>::type*>(p);
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack(const typename Raw<T, VEC>::type& r, float* out);
+template <> __device__ __forceinline__ void unpack<bf16_t, 8>(const uint4& r, float* o) {
+  o[0] = bf16_lo(r.x); o[1] = bf16_hi(r.x); o[2] = bf16_lo(r.y); o[3] = bf16_hi(r.y);
+  o[4] = bf16_lo(r.z); o[5] = bf16_hi(r.z); o[6] = bf16_lo(r.w); o[7] = bf16_hi(r.w);
+}
+template <> __device__ __forceinline__ void unpack<float, 4>(const uint4& r, float* o) {
+  o[0] = __uint_as_float(r.x); o[1] = __uint_as_float(r.y); o[2] = __uint_as_float(r.z); o[3] = __uint_as_float(r.w);
+}
+template <> __device__ __forceinline__ void unpack<bf16_t, 1>(const uint16_t& r, float* o) { o[0] = bf16_to_f32(r); }
+template <> __device__ __forceinline__ void unpack<float, 1>(const float& r, float* o) { o[0] = r; }
+
+// ---- wave reductions (wave64) --------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// sum over groups of `width` adjacent lanes (width a power of two <= 64); every lane of a group gets the sum
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ---- argmax order: NaN above every number (first NaN wins); ties (and +0 == -0) to the lower index --
+
+__device__ __forceinline__ bool argmax_better(float a, int ia, float b, int ib) {
+  const bool na = a != a, nb = b != b;
+  if (na || nb) {
+    if (na && nb) return ia < ib;
+    return na;
+  }
+  if (a > b) return true;
+  if (a < b) return false;
+  return ia < ib;
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, 64);
+    int oi = __shfl_xor(idx, o, 64);
+    if (argmax_better(ov, oi, v, idx)) { v = ov; idx = oi; }
+  }
+}
+
+// ---- device-resident decode state ---------------------------------------------------------------
+
+struct DecodeState {
+  int32_t token;   // token consumed by the next step
+  int32_t pos;     // its position
+  int32_t step;    // index of the next step within a multi-step call
+  int32_t pad;
+};
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace llmk

@@ -1,0 +1,131 @@
+// Launch interface of the gfx950 kernels (host side of libllmk).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace llmk {
+
+// ------------------------------------------------------------------------------------------------
+// Transposed GEMV, y = A^T x, split over K with a deterministic last-block reduction.
+// ------------------------------------------------------------------------------------------------
+
+enum GemvMode { GM_PLAIN = 0, GM_QKV = 1, GM_RESID = 2, GM_GATEUP = 3 };
+
+struct GemvParams {
+  // weights ([in][out] row-major). PLAIN/RESID: w0. GATEUP: w0 = gate, w1 = up (same shape).
+  // QKV: w0 = wq (n0 columns), w1 = wk (n1 columns), w2 = wv (N - n0 - n1 columns).
+  const void* w0;
+  const void* w1;
+  const void* w2;
+  int64_t n0, n1;
+  int64_t K, N;            // rows of A (= length of the input), output columns
+  int64_t rows_per_split;  // rows handled by one workgroup
+  int32_t ksplit, n_cblk;  // grid = ksplit * n_cblk workgroups
+  // input vector of length K: fp32, or a row of the weight dtype (the embedding table) chosen by token
+  const void* in;
+  int32_t in_is_w;               // 1: `in` has the weight dtype
+  const DecodeState* in_state;   // non-null: in += state->token * K (embedding row)
+  const float* gain;             // non-null: RMSNorm the input first (h = in * rsqrt(mean(in^2)+eps) * gain)
+  float eps;
+  // split-K workspace
+  float* partial;                // [ksplit][NACC][N]
+  unsigned* counters;            // [n_cblk], zero on entry, left zero on exit
+  // epilogue
+  float* y;                      // PLAIN: y[N]; GATEUP: u[N]; QKV: q[n0]
+  float* x;                      // RESID: residual stream, x = base + A^T in
+  const void* base;              // RESID: base (fp32 x itself, or the embedding table of weight dtype)
+  int32_t base_is_w;             // 1: base is the embedding table, row chosen by base_state->token
+  const DecodeState* base_state;
+  float* hidden;                 // RESID: optional copy of the new x
+  const DecodeState* state;      // QKV: position of the token
+  void* kcache;                  // QKV: layer's K buffer; element offset kv_off + pos*n1 + col
+  void* vcache;
+  int32_t kv_is_bf16;
+  int64_t kv_off;
+  int32_t head_dim;
+  int32_t rope_layout;
+  const float* rope_table;       // [max_pos][hd/2][2]
+};
+
+// columns per workgroup of the vector path for a weight dtype (64 lanes x 16 B)
+inline int gemv_cols_per_block(int w_is_bf16, int vec1) { return vec1 ? 64 : (w_is_bf16 ? 512 : 256); }
+
+// Fills ksplit/n_cblk/rows_per_split for a K x N problem (rows_per_split a multiple of 4 x 8).
+void gemv_plan(GemvParams& p, int w_is_bf16, int vec1, int target_blocks, int min_rows);
+hipError_t gemv_launch(const GemvParams& p, int mode, int w_is_bf16, int vec1, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------------
+// Untransposed GEMV (row dots), the output head: y[r] = W[r] . h, optionally h = rmsnorm(x) * gain,
+// optionally followed by the greedy argmax of y.
+// ------------------------------------------------------------------------------------------------
+
+struct HeadParams {
+  const void* w;          // [rows][cols]
+  int64_t rows, cols;
+  int64_t rows_per_block;
+  int32_t n_blocks;
+  const float* x;         // [cols]
+  const float* gain;      // non-null: RMSNorm first
+  float eps;
+  float* y;               // [rows]
+  // argmax (when part_val != nullptr)
+  float* part_val;        // [n_blocks]
+  int32_t* part_idx;      // [n_blocks]
+  unsigned* counter;      // one counter, zero on entry and exit
+  int32_t* token_out;     // token written at token_out[state ? state->step : 0]
+  float* logit_out;       // optional
+  DecodeState* state;     // optional: token <- argmax, pos += 1, step += 1
+};
+
+void head_plan(HeadParams& p, int w_is_bf16);
+hipError_t head_launch(const HeadParams& p, int w_is_bf16, hipStream_t s);
+hipError_t rowdot_simple_launch(const void* w, int w_is_bf16, const float* x, float* y, int64_t rows, int64_t cols,
+                                hipStream_t s);
+
+// ------------------------------------------------------------------------------------------------
+// Split-context grouped-query attention for one query position, plus the log-sum-exp merge.
+// ------------------------------------------------------------------------------------------------
+
+struct AttnParams {
+  const float* q;        // [H][hd]
+  const void* k;         // [>= ctx][Hkv][hd] (the sequence's region)
+  const void* v;
+  int32_t kv_is_bf16;
+  int32_t H, Hkv, hd;
+  int32_t ctx;                 // used when state == nullptr
+  const DecodeState* state;    // non-null: ctx = state->pos + 1
+  int32_t chunk;               // positions per sub-chunk (<= 64)
+  int32_t sub_per_wg;          // consecutive sub-chunks one workgroup walks (online softmax)
+  int32_t n_parts;             // grid.x; parts past ctx exit at once (<= ATTN_MAX_PARTS)
+  float* part;                 // [Hkv][n_parts][G][hd + 2]: max, sum, unnormalised output
+  unsigned* counters;          // [Hkv], zero on entry and exit
+  float* out;                  // [H][hd]
+};
+
+constexpr int ATTN_MAX_PARTS = 32;
+// Fills chunk / sub_per_wg / n_parts for contexts up to max_ctx.
+void attn_plan(AttnParams& p, int64_t max_ctx);
+hipError_t attn_launch(const AttnParams& p, hipStream_t s);
+inline int64_t attn_part_floats(int64_t H, int64_t hd) { return (int64_t)ATTN_MAX_PARTS * H * (hd + 2); }
+
+// ------------------------------------------------------------------------------------------------
+// Elementwise and small kernels
+// ------------------------------------------------------------------------------------------------
+
+hipError_t residual_add_launch(const float* a, const float* b, float* out, int64_t n, hipStream_t s);
+hipError_t add_rmsnorm_launch(float* residual, const float* x, const float* gain, int64_t rows, int64_t n, float eps,
+                              float* h, hipStream_t s);
+hipError_t silu_mul_launch(const float* gate, const float* up, float* out, int64_t n, hipStream_t s);
+hipError_t rope_table_launch(float* table, int64_t max_pos, int64_t hd, double base, hipStream_t s);
+hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, int64_t pos0,
+                       const float* table, int layout, hipStream_t s);
+hipError_t kv_append_launch(void* cache, int is_bf16, int64_t offset, const float* src, int64_t n, hipStream_t s);
+hipError_t argmax_launch(const float* logits, int64_t rows, int64_t n, int32_t* token, float* logit, float* part_val,
+                         int32_t* part_idx, unsigned* counters, int32_t blocks_per_row, hipStream_t s);
+hipError_t fill_u32_launch(unsigned* p, int64_t n, unsigned v, hipStream_t s);
+hipError_t set_state_launch(DecodeState* st, int32_t token, int32_t pos, hipStream_t s);
+
+}  // namespace llmk

@@ -1,0 +1,82 @@
+"""Moving host weights and K/V into device memory in the library's layouts (marshalling only).
+
+Weights come as a dict of numpy arrays: 'emb' and 'out' [vocab][d], 'norm' [d] (fp32), and 'layers', a
+list of dicts with 'wq', 'wk', 'wv', 'wo', 'gate', 'up', 'down' in the [in][out] layout and 'n1', 'n2'
+(fp32 gains). Weight arrays are float32, or uint16 holding bf16 bit patterns.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (BF16, F32, Config, KVPool, Model, check, decode_step, decode_steps, decode_workspace_bytes,
+               make_config, rope_table_init, workspace)
+
+_LAYER_MAP = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("gate", "w_gate"), ("up", "w_up"),
+              ("down", "w_down"), ("n1", "g_attn"), ("n2", "g_ffn"))
+
+
+def config_from(shape) -> Config:
+    """llmk_config from any object with vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps,
+    rope_base, rope_layout, w_dtype ('f32'/'bf16') and kv_dtype attributes."""
+    code = {"f32": F32, "bf16": BF16}
+    return make_config(shape.vocab, shape.d, shape.n_layer, shape.n_head, shape.n_kv, shape.head_dim, shape.hidden,
+                       shape.max_seq, shape.eps, shape.rope_base, shape.rope_layout, code[shape.w_dtype],
+                       code[shape.kv_dtype])
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """float32 -> float32 tensor; uint16 (bf16 bits) -> bfloat16 tensor. Flattened."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        t = torch.from_numpy(a.reshape(-1))
+    elif a.dtype == np.uint16:
+        t = torch.from_numpy(a.reshape(-1).view(np.int16)).view(torch.bfloat16)
+    else:
+        raise TypeError(f"weights must be float32 or bf16 bits (uint16), got {a.dtype}")
+    return t.to(device)
+
+
+def upload_model(cfg: Config, W: dict, device="cuda", stream=None) -> Model:
+    emb = to_device(W["emb"], device)
+    out = to_device(W["out"], device)
+    norm = to_device(np.asarray(W["norm"], dtype=np.float32), device)
+    layers = []
+    for L in W["layers"]:
+        layers.append({dst: to_device(L[src] if src not in ("n1", "n2") else np.asarray(L[src], np.float32), device)
+                       for src, dst in _LAYER_MAP})
+    table = torch.empty(cfg.max_seq * cfg.head_dim, dtype=torch.float32, device=device)
+    check(rope_table_init(table, cfg.max_seq, cfg.head_dim, cfg.rope_base, stream), "rope_table_init")
+    return Model(cfg, emb, out, norm, table, layers)
+
+
+def new_pool(cfg: Config, n_slots: int, capacity: int, device="cuda") -> KVPool:
+    return KVPool(cfg.n_layer, n_slots, capacity, cfg.n_kv, cfg.head_dim, cfg.kv_dtype, device)
+
+
+def fill_prefix(pool: KVPool, slot: int, prefix: list) -> None:
+    """Copy host K/V for positions 0..n-1 (per layer (K, V), each [n][n_kv][hd] in the pool dtype) into a
+    slot and record its length."""
+    n = prefix[0][0].shape[0]
+    for l, (kk, vv) in enumerate(prefix):
+        pool.slot_view(l, slot, "k")[:n] = to_device(kk, pool.k[l].device).view(n, pool.n_kv, pool.head_dim)
+        pool.slot_view(l, slot, "v")[:n] = to_device(vv, pool.v[l].device).view(n, pool.n_kv, pool.head_dim)
+    pool.slot_len[slot] = n
+
+
+class Decoder:
+    """One sequence slot of a pool driven through decode_step / decode_steps."""
+
+    def __init__(self, cfg: Config, model: Model, pool: KVPool, device="cuda"):
+        self.cfg, self.model, self.pool = cfg, model, pool
+        nbytes = decode_workspace_bytes(cfg, 1)
+        if nbytes < 0:
+            raise ValueError(f"config refused: {-nbytes}")
+        self.ws = workspace(nbytes, device)
+        self.token_out = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def step(self, token: int, pos: int, slot: int = 0, logits=None, hidden=None) -> int:
+        return decode_step(self.cfg, self.model, self.pool, slot, token, pos, self.token_out, self.ws, logits, hidden)
+
+    def steps(self, token0: int, pos0: int, n: int, tokens_out, slot: int = 0) -> int:
+        return decode_steps(self.cfg, self.model, self.pool, slot, token0, pos0, n, tokens_out, self.ws)

@@ -281,13 +281,28 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
 /* n_steps greedy steps of one sequence: step i consumes the token at position pos0 + i (token0 for
  * i = 0, else the previous step's output, fed back on the device) and writes its greedy token to
  * tokens_out[i]. The step's launch sequence is captured once into a HIP graph and replayed, and the
- * host reads nothing between steps ([xpu] "4. The pipelined decode").
+ * host reads nothing between steps ([xpu] "4. The pipelined decode"). Returns after `stream` has
+ * finished the steps, so the graph can be released.
  *   tokens_out: device int32 [n_steps] (len_tokens elements)
  * Codes: as llmk_decode_step, plus 561/564 for n_steps and 571 if pos0 + n_steps > capacity,
  * 573 if pos0 + n_steps > max_seq. On success slot_len_h[slot] = pos0 + n_steps. */
 int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                           int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
                           void* ws, int64_t len_ws, void* stream);
+
+/* Measurement aid (not on the decode path): the number of kernels one decode step launches, in launch
+ * order per layer q|k|v, attention, o, gate|up, down, then the output head (5 * n_layer + 1), or a
+ * negative status if cfg is refused. */
+int64_t llmk_decode_kernel_count(const llmk_config* cfg);
+
+/* One decode step exactly as llmk_decode_step (logits and hidden not returned), with a HIP event
+ * recorded on `stream` right before and right after every kernel launch. Waits for the step, then
+ * writes each kernel's duration in milliseconds to kernel_ms_h[k] (host, len_kernel_ms >=
+ * llmk_decode_kernel_count(cfg)), in launch order. Codes: as llmk_decode_step; 578 if kernel_ms_h is
+ * NULL; 577 if len_kernel_ms is too small. On success slot_len_h[slot] becomes pos + 1. */
+int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                  int64_t token, int64_t pos, int32_t* token_out, float* kernel_ms_h,
+                                  int64_t len_kernel_ms, void* ws, int64_t len_ws, void* stream);
 
 #ifdef __cplusplus
 }

@@ -168,7 +168,14 @@ def silu_mul(gate=True, len_gate=0, up=True, len_up=0, n=0, out=True, len_out=0)
 
 
 def _head_dim_ok(hd):
-    return hd % 2 == 0 and hd <= 256
+    """RoPE needs pairs: an even head dimension of at most 256."""
+    return hd % 2 == 0 and 2 <= hd <= 256
+
+
+def _attn_shape_ok(n_head, n_kv, hd):
+    """Attention and the decode step: whole query-head groups of at most 8 heads per K/V head, and a
+    power-of-two head dimension in [2, 256]."""
+    return n_head % n_kv == 0 and n_head // n_kv <= 8 and 2 <= hd <= 256 and (hd & (hd - 1)) == 0
 
 
 def rope_table_init(table=True, len_table=0, max_pos=0, head_dim=0, base=1e4):
@@ -224,7 +231,7 @@ def gqa_attend(q=True, len_q=0, k_cache=True, v_cache=True, len_cache=0, kv_dtyp
     c = _dims(ctx_len, n_head, n_kv, head_dim)
     if c != OK:
         return c
-    if n_head % n_kv != 0 or not _head_dim_ok(head_dim):
+    if not _attn_shape_ok(n_head, n_kv, head_dim):
         return HEAD_SHAPE
     if len_q != n_head * head_dim:
         return A_LEN
@@ -269,35 +276,47 @@ def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps
     c = _dims(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq)
     if c != OK:
         return c
-    if n_head % n_kv != 0 or not _head_dim_ok(head_dim):
+    if not _attn_shape_ok(n_head, n_kv, head_dim):
         return HEAD_SHAPE
     vec = 4 if w_dtype == 0 else 8
     for width in (d, n_head * head_dim, n_kv * head_dim, hidden):
         if width % vec != 0:
             return HEAD_SHAPE
+    if d > 64 * vec * 16:
+        return HEAD_SHAPE
     return OK
 
 
-def decode_step(cfg: dict, lens_ok=True, n_slots=1, capacity=0, slot=0, slot_len=0, token=0, pos=0,
-                logits=False, len_logits=0, hidden=False, len_hidden=0, pool_ok=True, ws_short=False):
-    """Expected status of llmk_decode_step. cfg is a dict of config_check's arguments; lens_ok says
-    whether every model tensor length matches the config; pool_ok whether the pool's shape matches it."""
+def decode_step(cfg: dict, tensors_ok=True, lens_ok=True, pool_ok=True, pool_dims_bad=False, n_slots=1,
+                capacity=0, slot=0, slot_len=0, token=0, pos=0, n_steps=1, logits=False, len_logits=0, hidden=False,
+                len_hidden=0, ws_short=False):
+    """Expected status of llmk_decode_step (n_steps = 1) and llmk_decode_steps. cfg holds config_check's
+    arguments; tensors_ok / lens_ok say whether every model tensor is non-null / has the length the config
+    implies; pool_ok whether the pool matches the config; pool_dims_bad whether n_slots or capacity < 1."""
     c = config_check(**cfg)
     if c != OK:
         return c
+    if n_steps < 1:
+        return EMPTY
+    if n_steps > MAX_DIM:
+        return TOO_LARGE
+    if not tensors_ok:
+        return INVALID
     if not lens_ok:
         return WEIGHT_LEN
     if not pool_ok:
         return INVALID
+    if pool_dims_bad:
+        return EMPTY
     if not (0 <= slot < n_slots):
         return SLOT
     if not (0 <= token < cfg["vocab"]):
         return TOKEN
-    if pos < 0 or pos >= cfg["max_seq"]:
+    if pos < 0 or pos + n_steps > cfg["max_seq"]:
         return POSITION
     if pos != slot_len:
         return CACHE_LEN
-    if pos >= capacity:
+    if pos + n_steps > capacity:
         return CAPACITY
     if logits and len_logits != cfg["vocab"]:
         return LOGITS_LEN

@@ -1,0 +1,264 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/llmk.h declares, and every
+host-side refusal returns the status the oracle's independent contract expects (CPU only).
+
+Refusals are checked with stand-in pointers: the library validates every argument before its first
+HIP call, so a refused call never touches them. Calls the oracle expects to succeed are not made here
+(they would launch kernels); the GPU tests cover them. On a machine with a visible GPU the stand-in
+pointer tests are skipped, so a library bug can never launch a kernel on them.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+from oracle import contract
+from tests.conftest import ROOT, golden
+
+llmk = pytest.importorskip("autoregressive_decode_step_amd")
+
+FAKE = 0x1000  # a non-null stand-in; never dereferenced by a refused call
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="stand-in pointers are only safe without a GPU")
+
+
+def test_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "llmk.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(llmk_\w+)\s*\(", header, flags=re.M))
+    assert len(declared) >= 20
+    lib = ctypes.CDLL(llmk.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in llmk.h but not exported"
+    assert declared == set(llmk.EXPORTED)
+
+
+def test_status_names_match_pages_and_oracle():
+    g = golden("contract_examples.json")
+    for code, name in g["status_table"].items():
+        assert llmk.status_name(int(code)) == name
+    for code in range(555, 585):
+        assert llmk.status_name(code) == contract.status_name(code)
+    assert llmk.status_name(-7) == contract.status_name(g["fallback_name_code"])
+
+
+def test_page_contract_examples():
+    g = golden("contract_examples.json")
+    for case in g["residual_dims_check"]:
+        assert llmk.residual_dims_check(*case["args"]) == case["status"]
+
+
+VALS = [-1, 0, 1, 2, 3, 6, (1 << 24), (1 << 24) + 1]
+
+
+def test_dims_checks_agree_with_oracle():
+    for n, la, lb in itertools.product(VALS, repeat=3):
+        assert llmk.residual_dims_check(n, la, lb) == contract.residual_dims_check(n, la, lb)
+        assert llmk.argmax_dims_check(n, la) == contract.argmax_dims_check(n, la)
+    for c, lc, nn, ln in itertools.product([-1, 0, 3, 6, (1 << 24) + 1], [0, 3, 6], [-1, 0, 1, 3], [0, 1, 3]):
+        assert llmk.kv_append_dims_check(c, lc, nn, ln) == contract.kv_append_dims_check(c, lc, nn, ln)
+    for m, n in itertools.product([-1, 0, 2, 3, (1 << 24) + 1], repeat=2):
+        for la, lx in itertools.product([0, 6, m * n], [0, 2, m]):
+            assert llmk.gemv_dims_check(m, n, la, lx) == contract.gemv_dims_check(m, n, la, lx)
+
+
+def _nz(flag):
+    return FAKE if flag else None
+
+
+@no_gpu
+def test_gemv_t_refusals():
+    L = llmk.lib
+    cases = 0
+    for a, x, y, ws in itertools.product([True, False], repeat=4):
+        for dt, m, n in itertools.product([0, 1, 5], [0, 2, (1 << 24) + 1], [3, -1]):
+            for la, lx, ly in itertools.product([6, 5], [2, 1], [3, 4]):
+                exp = contract.gemv_t(a, la, dt, x, lx, m, n, y, ly, ws)
+                if exp == contract.OK:
+                    continue
+                got = L.llmk_gemv_t(_nz(a), la, dt, _nz(x), lx, m, n, _nz(y), ly, _nz(ws), 1 << 30, None)
+                assert got == exp, (a, x, y, ws, dt, m, n, la, lx, ly)
+                cases += 1
+    assert cases > 100
+    # a workspace shorter than the library asks for
+    need = llmk.gemv_t_workspace_bytes(4096, 4096, 1)
+    assert need > 0
+    assert L.llmk_gemv_t(FAKE, 4096 * 4096, 1, FAKE, 4096, 4096, 4096, FAKE, 4096, FAKE, need - 1, None) == 578
+
+
+@no_gpu
+def test_elementwise_refusals():
+    L = llmk.lib
+    for a, b, o in itertools.product([True, False], repeat=3):
+        for n, la, lb, lo in itertools.product([0, 4, (1 << 24) + 1], [4, 3], [4, 5], [4, 2]):
+            exp = contract.residual_add(a, la, b, lb, n, o, lo)
+            if exp != contract.OK:
+                assert L.llmk_residual_add(_nz(a), la, _nz(b), lb, n, _nz(o), lo, None) == exp
+            exp = contract.silu_mul(a, la, b, lb, n, o, lo)
+            if exp != contract.OK:
+                assert L.llmk_silu_mul(_nz(a), la, _nz(b), lb, n, _nz(o), lo, None) == exp
+    for r, x, g, h in itertools.product([True, False], repeat=4):
+        for rows, n, eps in itertools.product([0, 2], [0, 8], [1e-5, 0.0, float("nan")]):
+            for lr, lx, lg, lh in itertools.product([16, 15], [16, 3], [8, 7], [16, 1]):
+                exp = contract.add_rmsnorm(r, lr, x, lx, g, lg, rows, n, eps, h, lh)
+                if exp != contract.OK:
+                    got = L.llmk_add_rmsnorm(_nz(r), lr, _nz(x), lx, _nz(g), lg, rows, n, eps, _nz(h), lh, None)
+                    assert got == exp, (r, x, g, h, rows, n, eps, lr, lx, lg, lh)
+
+
+@no_gpu
+def test_rope_refusals():
+    L = llmk.lib
+    for t, mp, hd, base in itertools.product([True, False], [0, 10], [0, 3, 8, 512], [1e4, 1.0, float("inf")]):
+        for lt in (mp * hd, 5):
+            exp = contract.rope_table_init(t, lt, mp, hd, base)
+            if exp != contract.OK:
+                assert L.llmk_rope_table_init(_nz(t), lt, mp, hd, base, None) == exp
+    for q, k, tab in itertools.product([True, False], repeat=3):
+        for rows, nq, nk, hd, pos0, layout in itertools.product([0, 2], [0, 4], [-1, 0, 2], [6, 7], [-1, 0, 9],
+                                                                [0, 1, 2]):
+            for lq, lk, lt in itertools.product([rows * nq * hd, 1], [rows * max(nk, 0) * hd, 1], [10 * hd, 3]):
+                exp = contract.rope(q, lq, k, lk, rows, nq, nk, hd, pos0, tab, lt, 10, layout)
+                if exp != contract.OK:
+                    got = L.llmk_rope(_nz(q), lq, _nz(k), lk, rows, nq, nk, hd, pos0, _nz(tab), lt, 10, layout, None)
+                    assert got == exp, (q, k, tab, rows, nq, nk, hd, pos0, layout, lq, lk, lt)
+
+
+@no_gpu
+def test_kv_append_refusals():
+    L = llmk.lib
+    out = ctypes.c_int64(-7)
+    for c, nv, dt in itertools.product([True, False], [True, False], [0, 1, 2]):
+        for cap, cl, lc, nn, ln in itertools.product([0, 9, 8], [-1, 0, 6], [6, 5], [0, 3], [3, 2]):
+            exp = contract.kv_append(c, cap, dt, cl, lc, nv, ln, nn)
+            if exp != contract.OK:
+                got = L.llmk_kv_append(_nz(c), cap, dt, cl, lc, _nz(nv), ln, nn, ctypes.byref(out), None)
+                assert got == exp, (c, nv, dt, cap, cl, lc, nn, ln)
+                assert out.value == -7  # untouched on refusal
+
+
+@no_gpu
+def test_attend_and_argmax_refusals():
+    L = llmk.lib
+    for ctx, H, Hkv, hd, dt in itertools.product([0, 5], [4, 6], [2, 4, 3], [4, 6, 512], [0, 1, 7]):
+        for lq, lc, lo in itertools.product([H * hd, 1], [ctx * Hkv * hd, 2], [H * hd, 3]):
+            exp = contract.gqa_attend(True, lq, True, True, lc, dt, ctx, H, Hkv, hd, True, lo)
+            if exp != contract.OK:
+                got = L.llmk_gqa_attend(FAKE, lq, FAKE, FAKE, lc, dt, ctx, H, Hkv, hd, FAKE, lo, FAKE, 1 << 30, None)
+                assert got == exp, (ctx, H, Hkv, hd, dt, lq, lc, lo)
+    for rows, n, ll in itertools.product([0, 1, 3], [0, 7], [21, 7, 0]):
+        exp = contract.argmax(True, ll, rows, n, True)
+        if exp != contract.OK:
+            assert L.llmk_argmax(FAKE, ll, rows, n, FAKE, None, FAKE, 1 << 30, None) == exp
+    assert L.llmk_argmax(None, 7, 1, 7, FAKE, None, FAKE, 1 << 30, None) == 578
+    need = llmk.argmax_workspace_bytes(1, 128256)
+    assert L.llmk_argmax(FAKE, 128256, 1, 128256, FAKE, None, FAKE, need - 1, None) == 578
+
+
+def test_kv_slot_offset_closed_form():
+    import numpy as np
+
+    class FakePool:
+        pass
+
+    n_slots, cap, n_kv, hd = 3, 10, 2, 4
+    ks = (ctypes.c_void_p * 1)(FAKE)
+    lens = np.zeros(n_slots, np.int64)
+    ps = llmk.PoolStruct(ks, ks, 1, n_slots, cap, n_kv, hd, 0, lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    fp = FakePool()
+    fp.struct = ps
+    for slot, pos, g in itertools.product([-1, 0, 2, 3], [-1, 0, 9, 10], [-1, 0, 1, 2]):
+        exp_st, exp_off = contract.kv_slot_offset(n_slots, cap, n_kv, hd, slot, pos, g)
+        st, off = llmk.kv_slot_offset(fp, slot, pos, g)
+        assert st == exp_st
+        if st == contract.OK:
+            assert off == exp_off
+
+
+def _cfg_kwargs(**over):
+    kw = dict(vocab=40, d=16, n_layer=2, n_head=4, n_kv=2, head_dim=4, hidden=24, max_seq=64, eps=1e-5,
+              rope_base=1e4, rope_layout=0, w_dtype=0, kv_dtype=0)
+    kw.update(over)
+    return kw
+
+
+def test_config_checks_agree_with_oracle():
+    variants = [dict(), dict(vocab=0), dict(d=(1 << 24) + 1), dict(n_head=6), dict(n_kv=3), dict(head_dim=6),
+                dict(head_dim=512), dict(n_head=32, n_kv=2), dict(hidden=22), dict(w_dtype=1), dict(w_dtype=3),
+                dict(rope_layout=2), dict(eps=0.0), dict(rope_base=1.0), dict(max_seq=-4), dict(kv_dtype=1),
+                dict(d=12, w_dtype=0), dict(d=24, w_dtype=1)]
+    for v in variants:
+        kw = _cfg_kwargs(**v)
+        cfg = llmk.make_config(**kw)
+        got = llmk.decode_workspace_bytes(cfg, 1)
+        exp = contract.config_check(**kw)
+        if exp == contract.OK:
+            assert got > 0, v
+        else:
+            assert got == -exp, v
+
+
+@no_gpu
+def test_decode_step_refusals():
+    import numpy as np
+    kw = _cfg_kwargs()
+    cfg = llmk.make_config(**kw)
+    d, qd, kvd, F, V, L = 16, 16, 8, 24, 40, 2
+    lens = [d * qd, d * kvd, d * kvd, qd * d, d * F, d * F, F * d, d, d]
+    FA = 0x10000  # 16-byte aligned stand-in
+
+    def model(bad_len=False, null=False):
+        arr = (llmk.Tensor * (L * 9))()
+        for l in range(L):
+            for t in range(9):
+                arr[l * 9 + t] = llmk.Tensor(None if (null and l == 1 and t == 3) else FA,
+                                             lens[t] + (1 if (bad_len and l == 1 and t == 5) else 0))
+        m = llmk.ModelStruct(llmk.Tensor(FA, V * d), llmk.Tensor(FA, V * d), llmk.Tensor(FA, d),
+                             llmk.Tensor(FA, 64 * 4), arr)
+        return m, arr
+
+    ws_need = llmk.decode_workspace_bytes(cfg, 1)
+
+    def call(m, n_slots=2, cap=32, slot=0, slot_len=0, token=0, pos=0, logits=False, len_logits=V, hidden=False,
+             len_hidden=L * d, ws_len=None, pool_nkv=2):
+        ks = (ctypes.c_void_p * L)(FA, FA)
+        sl = np.full(max(n_slots, 1), slot_len, np.int64)
+        ps = llmk.PoolStruct(ks, ks, L, n_slots, cap, pool_nkv, 4, 0, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        return llmk.lib.llmk_decode_step(ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), slot, token, pos,
+                                         FA if logits else None, len_logits, FA, FA if hidden else None, len_hidden,
+                                         FA, ws_need if ws_len is None else ws_len, None)
+
+    good, _a = model()
+    cases = [
+        (dict(slot=2), dict(slot=2, n_slots=2)),
+        (dict(token=40), dict(token=40)),
+        (dict(token=-1), dict(token=-1)),
+        (dict(pos=64, slot_len=64, cap=128), dict(pos=64, slot_len=64, capacity=128)),
+        (dict(pos=3, slot_len=2), dict(pos=3, slot_len=2)),
+        (dict(pos=32, slot_len=32, cap=32), dict(pos=32, slot_len=32, capacity=32)),
+        (dict(logits=True, len_logits=39), dict(logits=True, len_logits=39)),
+        (dict(hidden=True, len_hidden=31), dict(hidden=True, len_hidden=31)),
+        (dict(ws_len=ws_need - 1), dict(ws_short=True)),
+        (dict(n_slots=0), dict(n_slots=0, pool_dims_bad=True)),
+        (dict(pool_nkv=4), dict(pool_ok=False)),
+    ]
+    for call_kw, exp_kw in cases:
+        base = dict(n_slots=2, capacity=32, slot=0, slot_len=0, token=0, pos=0)
+        base.update(exp_kw)
+        exp = contract.decode_step(kw, **base)
+        assert exp != contract.OK
+        assert call(good, **call_kw) == exp, call_kw
+    bad, _b = model(bad_len=True)
+    assert call(bad) == contract.decode_step(kw, lens_ok=False) == 576
+    nul, _c = model(null=True)
+    assert call(nul) == contract.decode_step(kw, tensors_ok=False) == 578
