@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libllmk.so")
 OK = 560
 F32, BF16 = 0, 1
 ROPE_HALF_SPLIT, ROPE_INTERLEAVED = 0, 1
+W_IN_OUT, W_OUT_IN = 0, 1
 WQ, WK, WV, WO, WGATE, WUP, WDOWN, GATTN, GFFN = range(9)
 LAYER_TENSORS = 9
 MAX_DIM = 1 << 24
@@ -42,7 +43,7 @@ class Config(ctypes.Structure):
     """llmk_config"""
     _fields_ = [("vocab", _i64), ("d", _i64), ("n_layer", _i64), ("n_head", _i64), ("n_kv", _i64),
                 ("head_dim", _i64), ("hidden", _i64), ("max_seq", _i64), ("eps", _f64), ("rope_base", _f64),
-                ("rope_layout", _i32), ("w_dtype", _i32), ("kv_dtype", _i32)]
+                ("rope_layout", _i32), ("w_dtype", _i32), ("kv_dtype", _i32), ("w_layout", _i32)]
 
 
 class Tensor(ctypes.Structure):
@@ -89,6 +90,7 @@ _SIGS = {
     "llmk_decode_steps": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _i64,
                            _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_decode_kernel_count": ([ctypes.POINTER(Config)], _i64),
+    "llmk_transpose": ([_p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
     "llmk_decode_step_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                    _i64, _i64, _i64, _p, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
 }
@@ -239,9 +241,15 @@ def argmax(logits, rows, n, token, logit, ws, stream=None) -> int:
 # ---------------------------------------------------------------------------------------------------------
 
 def make_config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4,
-                rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16) -> Config:
+                rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16, w_layout=W_IN_OUT) -> Config:
     return Config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps, rope_base, rope_layout, w_dtype,
-                  kv_dtype)
+                  kv_dtype, w_layout)
+
+
+def transpose(src, dst, rows, cols, stream=None) -> int:
+    """dst = src^T (src rows x cols, row-major)."""
+    return lib.llmk_transpose(_ptr(src), _len(src), _ptr(dst), _len(dst), rows, cols, _dtype_code(src),
+                              _stream(stream))
 
 
 class Model:

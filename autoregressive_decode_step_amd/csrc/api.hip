@@ -61,7 +61,7 @@ GemvT plan_gemv_t(int64_t m, int64_t n, int32_t dt, const void* a) {
   g.vec1 = (n % vec != 0) || (a && !aligned16(a));
   g.p.K = m;
   g.p.N = n;
-  gemv_plan(g.p, dt == LLMK_BF16, g.vec1, 512, 64);
+  gemv_plan(g.p, dt == LLMK_BF16, g.vec1, 512, 0);
   return g;
 }
 
@@ -80,7 +80,7 @@ int64_t gemv_t_ws_any(int64_t m, int64_t n, int32_t dt) {
   s.vec1 = 1;
   s.p.K = m;
   s.p.N = n;
-  gemv_plan(s.p, dt == LLMK_BF16, 1, 512, 64);
+  gemv_plan(s.p, dt == LLMK_BF16, 1, 512, 0);
   const int64_t ws = gemv_t_ws(s);
   return ws > w ? ws : w;
 }
@@ -91,6 +91,7 @@ int32_t config_check(const llmk_config* c) {
   if (!c) return LLMK_INVALID_ARGUMENT;
   if (!is_dtype(c->w_dtype) || !is_dtype(c->kv_dtype)) return LLMK_INVALID_ARGUMENT;
   if (c->rope_layout != LLMK_ROPE_HALF_SPLIT && c->rope_layout != LLMK_ROPE_INTERLEAVED) return LLMK_INVALID_ARGUMENT;
+  if (c->w_layout != LLMK_W_IN_OUT && c->w_layout != LLMK_W_OUT_IN) return LLMK_INVALID_ARGUMENT;
   if (!(c->eps > 0) || !isfinite(c->eps) || !(c->rope_base > 1.0) || !isfinite(c->rope_base))
     return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({c->vocab, c->d, c->n_layer, c->n_head, c->n_kv, c->head_dim, c->hidden, c->max_seq});
@@ -102,17 +103,28 @@ int32_t config_check(const llmk_config* c) {
   for (int64_t w : widths)
     if (w % vec != 0) return LLMK_HEAD_SHAPE_INVALID;
   if (c->d > 64 * vec * 16) return LLMK_HEAD_SHAPE_INVALID;  // the head kernel holds d in registers
+  if (c->w_layout == LLMK_W_OUT_IN) {   // the row-dot kernels hold a K segment per lane in registers
+    const int64_t ks[3] = {c->d, c->n_head * c->head_dim, c->hidden};
+    for (int64_t k : ks) {
+      RowdotParams r{};
+      r.K = k;
+      r.N = 1;
+      if (rowdot_plan(r, c->w_dtype == LLMK_BF16, GM_PLAIN) != 0) return LLMK_HEAD_SHAPE_INVALID;
+    }
+  }
   return LLMK_OK;
 }
 
 struct DecodePlan {
+  int rowdot = 0;                       // 1: output-major weights (row-dot kernels), 0: split-K kernels
   GemvParams qkv{}, o{}, gu{}, down{};
+  RowdotParams rqkv{}, ro{}, rgu{}, rdown{};
   HeadParams head{};
   AttnParams attn{};
   // workspace regions
   DecodeState* state = nullptr;
   float* x = nullptr;
-  float* q = nullptr;
+  float* qkv_buf = nullptr;             // raw q|k|v of the step's position
   float* att = nullptr;
   float* u = nullptr;
   float* logits = nullptr;
@@ -126,7 +138,7 @@ struct DecodePlan {
 };
 
 constexpr int kGemvTargetBlocks = 512;
-constexpr int kGemvMinRows = 64;
+
 
 void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   const int bf = c->w_dtype == LLMK_BF16;
@@ -135,10 +147,21 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.o.K = qd; D.o.N = d;
   D.gu.K = d; D.gu.N = F;
   D.down.K = F; D.down.N = d;
-  gemv_plan(D.qkv, bf, 0, kGemvTargetBlocks, kGemvMinRows);
-  gemv_plan(D.o, bf, 0, kGemvTargetBlocks, kGemvMinRows);
-  gemv_plan(D.gu, bf, 0, kGemvTargetBlocks, kGemvMinRows);
-  gemv_plan(D.down, bf, 0, kGemvTargetBlocks, kGemvMinRows);
+  gemv_plan(D.qkv, bf, 0, kGemvTargetBlocks, 0);
+  gemv_plan(D.o, bf, 0, kGemvTargetBlocks, 0);
+  gemv_plan(D.gu, bf, 0, kGemvTargetBlocks, 0);
+  gemv_plan(D.down, bf, 0, kGemvTargetBlocks, 0);
+  D.rowdot = c->w_layout == LLMK_W_OUT_IN;
+  D.rqkv.K = d; D.rqkv.N = qd + 2 * kvd; D.rqkv.n0 = qd; D.rqkv.n1 = kvd;
+  D.ro.K = qd; D.ro.N = d;
+  D.rgu.K = d; D.rgu.N = F;
+  D.rdown.K = F; D.rdown.N = d;
+  if (D.rowdot) {
+    rowdot_plan(D.rqkv, bf, GM_QKV);
+    rowdot_plan(D.ro, bf, GM_RESID);
+    rowdot_plan(D.rgu, bf, GM_GATEUP);
+    rowdot_plan(D.rdown, bf, GM_RESID);
+  }
   D.head.rows = c->vocab;
   D.head.cols = d;
   head_plan(D.head, bf);
@@ -151,7 +174,7 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   int64_t part = 0;
   const GemvParams* gs[4] = {&D.qkv, &D.o, &D.gu, &D.down};
   int ncnt = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4 && !D.rowdot; ++i) {
     const int nacc = (i == 2) ? 2 : 1;
     const int64_t f = gs[i]->ksplit > 1 ? (int64_t)gs[i]->ksplit * nacc * gs[i]->N : 0;
     if (f > part) part = f;
@@ -161,7 +184,7 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   Carve cv(ws);
   D.state = cv.take<DecodeState>(1);
   D.x = cv.take<float>(d);
-  D.q = cv.take<float>(qd);
+  D.qkv_buf = cv.take<float>(qd + 2 * kvd);
   D.att = cv.take<float>(qd);
   D.u = cv.take<float>(F);
   D.logits = cv.take<float>(c->vocab);
@@ -238,32 +261,44 @@ hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv
     return r;
   };
   for (int64_t l = 0; l < c->n_layer; ++l) {
-    // 1. h = rmsnorm(x) g_attn;  q|k|v = h W;  RoPE;  k, v -> pool
-    GemvParams g = D.qkv;
-    g.w0 = layer_t(m, l, LLMK_WQ).ptr;
-    g.w1 = layer_t(m, l, LLMK_WK).ptr;
-    g.w2 = layer_t(m, l, LLMK_WV).ptr;
-    if (l == 0) { g.in = m->emb.ptr; g.in_is_w = 1; g.in_state = D.state; }
-    else { g.in = D.x; g.in_is_w = 0; g.in_state = nullptr; }
-    g.gain = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
-    g.eps = (float)c->eps;
-    g.partial = D.partial;
-    g.counters = gcnt;
-    g.y = D.q;
-    g.state = D.state;
-    g.kcache = pool->k[l];
-    g.vcache = pool->v[l];
-    g.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
-    g.kv_off = kv_off;
-    g.head_dim = (int32_t)c->head_dim;
-    g.rope_layout = c->rope_layout;
-    g.rope_table = static_cast<const float*>(m->rope_table.ptr);
-    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(g, GM_QKV, bf, 0, s))) != hipSuccess) return e;
-    // 2. attention over positions 0..pos of this slot
+    const float* g_attn = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
+    const float* g_ffn = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
+    // 1. h = rmsnorm(x) g_attn;  q|k|v = h W  (raw; layer 0 reads x = emb[token])
+    if (D.rowdot) {
+      RowdotParams r = D.rqkv;
+      r.w0 = layer_t(m, l, LLMK_WQ).ptr;
+      r.w1 = layer_t(m, l, LLMK_WK).ptr;
+      r.w2 = layer_t(m, l, LLMK_WV).ptr;
+      if (l == 0) { r.in = m->emb.ptr; r.in_is_w = 1; r.in_state = D.state; }
+      else { r.in = D.x; r.in_is_w = 0; r.in_state = nullptr; }
+      r.gain = g_attn;
+      r.eps = (float)c->eps;
+      r.y = D.qkv_buf;
+      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(r, GM_QKV, bf, s))) != hipSuccess) return e;
+    } else {
+      GemvParams g = D.qkv;
+      g.w0 = layer_t(m, l, LLMK_WQ).ptr;
+      g.w1 = layer_t(m, l, LLMK_WK).ptr;
+      g.w2 = layer_t(m, l, LLMK_WV).ptr;
+      if (l == 0) { g.in = m->emb.ptr; g.in_is_w = 1; g.in_state = D.state; }
+      else { g.in = D.x; g.in_is_w = 0; g.in_state = nullptr; }
+      g.gain = g_attn;
+      g.eps = (float)c->eps;
+      g.partial = D.partial;
+      g.counters = gcnt;
+      g.y = D.qkv_buf;
+      if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(g, GM_QKV, bf, 0, s))) != hipSuccess) return e;
+    }
+    // 2. RoPE on q and k, append k, v at pos, attention over positions 0..pos of this slot
     AttnParams a = D.attn;
-    a.q = D.q;
+    a.q = nullptr;
+    a.qkv_raw = D.qkv_buf;
     a.k = static_cast<const char*>(pool->k[l]) + kv_off * kvsz;
     a.v = static_cast<const char*>(pool->v[l]) + kv_off * kvsz;
+    a.k_w = static_cast<char*>(pool->k[l]) + kv_off * kvsz;
+    a.v_w = static_cast<char*>(pool->v[l]) + kv_off * kvsz;
+    a.rope_table = static_cast<const float*>(m->rope_table.ptr);
+    a.rope_layout = c->rope_layout;
     a.state = D.state;
     a.ctx = 0;
     a.part = D.attn_part;
@@ -271,6 +306,33 @@ hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv
     a.out = D.att;
     if ((e = mark(0)) != hipSuccess || (e = timed(attn_launch(a, s))) != hipSuccess) return e;
     // 3. x = x + att Wo   (layer 0: x = emb[token] + att Wo)
+    // 4. h = rmsnorm(x) g_ffn;  u = silu(h Wgate) * (h Wup)
+    // 5. x = x + u Wdown
+    if (D.rowdot) {
+      RowdotParams o = D.ro;
+      o.w0 = layer_t(m, l, LLMK_WO).ptr;
+      o.in = D.att;
+      o.x = D.x;
+      if (l == 0) { o.base = m->emb.ptr; o.base_is_w = 1; o.base_state = D.state; }
+      else { o.base = D.x; o.base_is_w = 0; o.base_state = nullptr; }
+      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(o, GM_RESID, bf, s))) != hipSuccess) return e;
+      RowdotParams gu = D.rgu;
+      gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
+      gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
+      gu.in = D.x;
+      gu.gain = g_ffn;
+      gu.eps = (float)c->eps;
+      gu.y = D.u;
+      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(gu, GM_GATEUP, bf, s))) != hipSuccess) return e;
+      RowdotParams dn = D.rdown;
+      dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
+      dn.in = D.u;
+      dn.x = D.x;
+      dn.base = D.x;
+      dn.hidden = hidden ? hidden + l * d : nullptr;
+      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(dn, GM_RESID, bf, s))) != hipSuccess) return e;
+      continue;
+    }
     GemvParams o = D.o;
     o.w0 = layer_t(m, l, LLMK_WO).ptr;
     o.in = D.att;
@@ -283,19 +345,17 @@ hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv
     else { o.base = D.x; o.base_is_w = 0; o.base_state = nullptr; }
     o.hidden = nullptr;
     if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(o, GM_RESID, bf, 0, s))) != hipSuccess) return e;
-    // 4. h = rmsnorm(x) g_ffn;  u = silu(h Wgate) * (h Wup)
     GemvParams gu = D.gu;
     gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
     gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
     gu.in = D.x;
     gu.in_is_w = 0;
-    gu.gain = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
+    gu.gain = g_ffn;
     gu.eps = (float)c->eps;
     gu.partial = D.partial;
     gu.counters = gcnt;
     gu.y = D.u;
     if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(gu, GM_GATEUP, bf, 0, s))) != hipSuccess) return e;
-    // 5. x = x + u Wdown
     GemvParams dn = D.down;
     dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
     dn.in = D.u;
@@ -719,6 +779,17 @@ int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* mode
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos + 1;
   return LLMK_OK;
+}
+
+int32_t llmk_transpose(const void* src, int64_t len_src, void* dst, int64_t len_dst, int64_t rows, int64_t cols,
+                       int32_t dtype, void* stream) {
+  if (!src || !dst || !is_dtype(dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, cols});
+  if (st != LLMK_OK) return st;
+  if (len_src != rows * cols) return LLMK_A_LENGTH_MISMATCH;
+  if (len_dst != rows * cols) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (src == dst) return LLMK_INVALID_ARGUMENT;
+  return finish(transpose_launch(src, dst, rows, cols, dtype == LLMK_BF16, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -1,16 +1,22 @@
 // Split-context grouped-query decode attention for gfx950.
 //
-// One query position; head h reads K/V head g = h / G (G = H / Hkv query heads share every K/V row,
-// so each row is read once for all G of them). The context is cut into parts; a workgroup (4 waves)
-// walks the consecutive sub-chunks of its part with an online softmax (running max and sum per head,
-// output rescaled when the max grows), keeping the next sub-chunk's K and V rows in flight while it
-// scores the current one. A row of hd elements is spread over hd/VEC lanes with 16-byte loads; the
-// dot products reduce inside those lanes with xor shuffles. Each part writes (max, sum, unnormalised
-// output) per head; the last workgroup of a K/V head merges the parts by log-sum-exp in part order:
-// m* = max m_c, out = sum_c e^(m_c - m*) o_c / sum_c e^(m_c - m*) l_c.
+// One query position; head h reads K/V head g = h / G (G = H / Hkv query heads share every K/V row, so
+// each row is read from HBM once for all G of them). The context is cut into parts of consecutive
+// tiles; a workgroup (4 waves) owns one (K/V head, part) and walks its tiles with an online softmax.
+//   - A tile of K and V rows is loaded cooperatively with 16-byte loads into registers while the
+//     previous tile is being computed, then written to LDS (rows padded by 16 B so that a lane reading
+//     its own row and lanes reading one row's consecutive elements are both bank-conflict free).
+//   - Scores: wave w takes query heads w, w+4; lane t computes q . K[t] from LDS (q broadcast from LDS),
+//     so no cross-lane reduction is needed per row. Softmax statistics are two wave reductions.
+//   - Output: lanes own consecutive head-dim elements and accumulate p_t V[t][e] over the tile, p_t
+//     taken from lane t with readlane.
+//   - Each part writes (max, sum, unnormalised output) per head; the last workgroup of a K/V head merges
+//     the parts by log-sum-exp in part order: m* = max m_c, out = sum_c e^(m_c - m*) o_c /
+//     sum_c e^(m_c - m*) l_c.
 // ("Inside the engine", "1. CausalLM": flash attention split across the context and reduced;
 // "The forward pass end to end", "The code": the per-head softmax attention it computes.)
 #include <float.h>
+#include <stdlib.h>
 
 #include "kernels.h"
 
@@ -18,236 +24,305 @@ namespace llmk {
 
 constexpr int ATTN_THREADS = 256;
 constexpr int ATTN_WAVES = 4;
-constexpr int ATTN_MAXC = 64;     // positions per sub-chunk, at most
-constexpr int ATTN_MAXNI = 4;     // row loads per lane per sub-chunk, at most
+constexpr int ATTN_MAXG_PER_WAVE = 2;   // query heads per wave (G <= 8)
 
-template <typename T, int VEC, int G>
+// positions per tile for a row of `row_bytes`: at most 64, tile of one of K/V at most 16 KiB
+__host__ __device__ constexpr int attn_tile_rows(int row_bytes) {
+  return (16384 / row_bytes) < 64 ? (16384 / row_bytes) : 64;
+}
+
+template <typename T, int HD>
 __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) {
-  typedef typename Raw<T, VEC>::type RawT;
-  __shared__ float s_p[G][ATTN_MAXC];
-  __shared__ float s_alpha[G], s_m[G], s_l[G], s_inv[G];
-  __shared__ float s_o[ATTN_WAVES][G][256];
-  __shared__ float s_wm[ATTN_MAX_PARTS][G];
-  __shared__ float s_wl[ATTN_MAX_PARTS][G];
+  constexpr int EPV = 16 / (int)sizeof(T);               // elements per 16-byte vector
+  constexpr int RV = (HD + EPV - 1) / EPV;               // vectors per row (a partial vector when HD < EPV)
+  constexpr int ROWB = (HD * (int)sizeof(T) + 15) / 16 * 16;
+  constexpr int CH = attn_tile_rows(ROWB);               // positions per tile
+  constexpr int RS = RV + 1;                             // padded row stride in vectors
+  constexpr int NVT = 2 * CH * RV;                       // vectors in a K+V tile
+  constexpr int NVL = (NVT + ATTN_THREADS - 1) / ATTN_THREADS;   // per thread
+  constexpr int LPV = RV;                                // V phase: lanes per row (one 16-B vector each)
+  constexpr int RGV = 64 / LPV;                          // V phase: rows processed at once by a wave
+  constexpr int HDP = HD < 4 ? 4 : HD;                   // q row stride in LDS (float4 reads)
+
+  __shared__ uint4 s_kv[2][CH][RS];
+  __shared__ float s_q[8][HDP];
+  __shared__ float s_p[8][CH];
+  __shared__ T s_new[2][HDP];                            // the appended k and v row (decode), cache dtype
   __shared__ int s_last;
 
-  const int hd = p.hd, chunk = p.chunk;
+  const int G = p.H / p.Hkv;
   const int kvh = blockIdx.y, part = blockIdx.x;
   const int ctx = p.state ? p.state->pos + 1 : p.ctx;
-  const int span = chunk * p.sub_per_wg;
+  const int span = CH * p.sub_per_wg;
   const int tb = part * span;
   if (tb >= ctx) return;
   const int te = min(tb + span, ctx);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int LPR = hd / VEC;               // lanes per row
-  const int RPL = 64 / LPR;               // rows per wave load
-  const int sub = lane % LPR, rsub = lane / LPR, e0 = sub * VEC;
-  const int NI = (chunk + ATTN_WAVES * RPL - 1) / (ATTN_WAVES * RPL);
-  const int64_t rstride = (int64_t)p.Hkv * hd;
-  const T* Kb = static_cast<const T*>(p.k) + (int64_t)kvh * hd + e0;
-  const T* Vb = static_cast<const T*>(p.v) + (int64_t)kvh * hd + e0;
-  const float scale = 1.0f / sqrtf((float)hd);
+  const int64_t rstride = (int64_t)p.Hkv * HD;                 // elements between positions
+  const T* Kb = static_cast<const T*>(p.k) + (int64_t)kvh * HD;
+  const T* Vb = static_cast<const T*>(p.v) + (int64_t)kvh * HD;
+  const float scale = 1.0f / sqrtf((float)HD);
 
-  float qv[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) qv[g][v] = p.q[(int64_t)(kvh * G + g) * hd + e0 + v];
-
-  float o[G][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) o[g][v] = 0.0f;
-  if (threadIdx.x < G) { s_m[threadIdx.x] = -INFINITY; s_l[threadIdx.x] = 0.0f; }
-
-  RawT kc[ATTN_MAXNI], vc[ATTN_MAXNI];
-#pragma unroll
-  for (int i = 0; i < ATTN_MAXNI; ++i) {
-    const int t = tb + (i * ATTN_WAVES + wave) * RPL + rsub;
-    if (i < NI && t < min(tb + chunk, te)) { kc[i] = load_raw<T, VEC>(Kb + t * rstride); vc[i] = load_raw<T, VEC>(Vb + t * rstride); }
-    else { kc[i] = RawT{}; vc[i] = RawT{}; }
-  }
-  __syncthreads();
-
-  for (int t0 = tb; t0 < te; t0 += chunk) {
-    const int t1 = min(t0 + chunk, te);
-    const int tn0 = t0 + chunk, tn1 = min(tn0 + chunk, te);
-    RawT kn[ATTN_MAXNI], vn[ATTN_MAXNI];
-#pragma unroll
-    for (int i = 0; i < ATTN_MAXNI; ++i) {
-      const int t = tn0 + (i * ATTN_WAVES + wave) * RPL + rsub;
-      if (i < NI && t < tn1) { kn[i] = load_raw<T, VEC>(Kb + t * rstride); vn[i] = load_raw<T, VEC>(Vb + t * rstride); }
-      else { kn[i] = RawT{}; vn[i] = RawT{}; }
+  // q of the group into LDS. In the decode step q, k and v arrive unrotated (p.qkv_raw): every
+  // workgroup rotates its q heads by the position, and the workgroup whose part holds that position
+  // rotates k, rounds k and v to the cache dtype, appends them to the cache and patches its tile.
+  const int pos = ctx - 1;
+  const bool owner = p.qkv_raw && pos >= tb && pos < te;
+  if (p.qkv_raw) {
+    constexpr int HALF = HD / 2;
+    const float* tab = p.rope_table + (int64_t)pos * HALF * 2;
+    for (int i = threadIdx.x; i < (G + (owner ? 1 : 0)) * HALF; i += ATTN_THREADS) {
+      const int g = i / HALF, j = i % HALF;
+      const int ia = p.rope_layout == 0 ? j : 2 * j;
+      const int ib = p.rope_layout == 0 ? j + HALF : 2 * j + 1;
+      const float cs = tab[2 * j], sn = tab[2 * j + 1];
+      const float* src = g < G ? p.qkv_raw + (int64_t)(kvh * G + g) * HD
+                               : p.qkv_raw + (int64_t)p.H * HD + (int64_t)kvh * HD;   // this head's k
+      const float a = src[ia], b = src[ib];
+      const float ra = a * cs - b * sn, rb = a * sn + b * cs;
+      if (g < G) {
+        s_q[g][ia] = ra;
+        s_q[g][ib] = rb;
+      } else {
+        store_elem<T>(&s_new[0][0], ia, ra);
+        store_elem<T>(&s_new[0][0], ib, rb);
+      }
     }
-    // scores s_t = q . k_t / sqrt(hd)
+    if (owner) {
+      const float* vsrc = p.qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD;
+      for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, vsrc[e]);
+    }
+    __syncthreads();
+    if (owner) {
+      const int64_t off = (int64_t)pos * p.Hkv * HD + (int64_t)kvh * HD;
+      for (int e = threadIdx.x; e < 2 * HD; e += ATTN_THREADS) {
+        const int w = e / HD, ee = e % HD;
+        (w == 0 ? static_cast<T*>(p.k_w) : static_cast<T*>(p.v_w))[off + ee] = s_new[w][ee];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < G * HD; i += ATTN_THREADS) s_q[i / HD][i % HD] = p.q[(int64_t)kvh * G * HD + i];
+  }
+
+  // cooperative tile load: vector idx -> (K or V, row, vector); rows past te are clamped to te - 1
+  uint4 reg[NVL];
+#define LLMK_LOAD_TILE(T0)                                                                        \
+  _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
+    const int idx = threadIdx.x + k * ATTN_THREADS;                                               \
+    const int which = idx / (CH * RV), rem = idx % (CH * RV);                                     \
+    const int t = min((T0) + rem / RV, te - 1);                                                    \
+    const T* src = (which == 0 ? Kb : Vb) + (int64_t)t * rstride + (rem % RV) * EPV;               \
+    if (HD >= EPV) {                                                                              \
+      reg[k] = idx < NVT ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);          \
+    } else {                                                                                      \
+      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);                               \
+      reg[k] = make_uint4(idx < NVT ? s32[0] : 0u,                                                \
+                          (idx < NVT && HD * (int)sizeof(T) >= 8) ? s32[1] : 0u, 0u, 0u);          \
+    }                                                                                             \
+  }
+#define LLMK_STORE_TILE()                                                                         \
+  _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
+    const int idx = threadIdx.x + k * ATTN_THREADS;                                               \
+    if (idx < NVT) {                                                                              \
+      const int which = idx / (CH * RV), rem = idx % (CH * RV);                                   \
+      s_kv[which][rem / RV][rem % RV] = reg[k];                                                   \
+    }                                                                                             \
+  }
+
+  // per wave and query head: running max and sum (uniform), and a partial output per lane for the
+  // EPV elements of vector `vl` over the rows of row group `rg` (reduced over row groups at the end)
+  const int vl = lane % LPV, rg = lane / LPV;
+  float m_run[ATTN_MAXG_PER_WAVE], l_run[ATTN_MAXG_PER_WAVE], o[ATTN_MAXG_PER_WAVE][EPV];
 #pragma unroll
-    for (int i = 0; i < ATTN_MAXNI; ++i) {
-      if (i < NI) {
-        const int t = t0 + (i * ATTN_WAVES + wave) * RPL + rsub;
-        float kf[VEC];
-        unpack<T, VEC>(kc[i], kf);
+  for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
+    m_run[gi] = -INFINITY;
+    l_run[gi] = 0.0f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.0f;
+    for (int k = 0; k < EPV; ++k) o[gi][k] = 0.0f;
+  }
+
+  LLMK_LOAD_TILE(tb)
+  for (int t0 = tb; t0 < te; t0 += CH) {
+    __syncthreads();                       // previous tile fully consumed (and q in LDS on entry)
+    LLMK_STORE_TILE()
+    __syncthreads();
+    if (owner && pos >= t0 && pos < t0 + CH) {   // the appended position: use the new row, not the stale one
+      for (int e = threadIdx.x; e < 2 * HD; e += ATTN_THREADS) {
+        const int w = e / HD, ee = e % HD;
+        reinterpret_cast<T*>(&s_kv[w][pos - t0][0])[ee] = s_new[w][ee];
+      }
+      __syncthreads();
+    }
+    if (t0 + CH < te) { LLMK_LOAD_TILE(t0 + CH) }   // next tile in flight while this one is computed
+    const int n = min(CH, te - t0);
+
+    // scores and softmax statistics: wave w takes heads w, w + 4; lane t scores position t0 + t
+    float alpha_g[ATTN_MAXG_PER_WAVE];
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) d = fmaf(qv[g][v], kf[v], d);
-          d = group_sum(d, LPR);
-          if (sub == 0 && t < t1) s_p[g][t - t0] = d * scale;
+    for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
+      const int g = wave + gi * ATTN_WAVES;
+      alpha_g[gi] = 1.0f;
+      if (g < G) {
+      float s = -INFINITY;
+      if (lane < CH) {
+        float part8[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) part8[e] = 0.0f;
+        const float* qg = s_q[g];
+#pragma unroll
+        for (int v = 0; v < RV; ++v) {
+          float kf[EPV];
+          if constexpr (sizeof(T) == 2) unpack<bf16_t, 8>(s_kv[0][lane][v], kf);
+          else unpack<float, 4>(s_kv[0][lane][v], kf);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e)
+            if (v * EPV + e < HD) part8[e] = fmaf(qg[v * EPV + e], kf[e], part8[e]);
+        }
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) dot += part8[e];
+        if (lane < n) s = dot * scale;
+      }
+      const float m_new = fmaxf(m_run[gi], wave_max(s));
+      const float pr = (lane < n) ? expf(s - m_new) : 0.0f;
+      const float alpha = expf(m_run[gi] - m_new);
+      l_run[gi] = l_run[gi] * alpha + wave_sum(pr);
+      m_run[gi] = m_new;
+      alpha_g[gi] = alpha;
+      if (lane < CH) s_p[g][lane] = pr;
+      }
+    }
+    __syncthreads();
+    // o = alpha o + sum_t p_t V[t]: lane (rg, vl) accumulates rows rg, rg + RGV, ... of the tile
+#pragma unroll
+    for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
+      const int g = wave + gi * ATTN_WAVES;
+      if (g < G) {
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) o[gi][k] *= alpha_g[gi];
+#pragma unroll 4
+        for (int t = rg; t < n; t += RGV) {
+          const float pt = s_p[g][t];
+          float vf[EPV];
+          if constexpr (sizeof(T) == 2) unpack<bf16_t, 8>(s_kv[1][t][vl], vf);
+          else unpack<float, 4>(s_kv[1][t][vl], vf);
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) o[gi][k] = fmaf(pt, vf[k], o[gi][k]);
         }
       }
     }
-    __syncthreads();
-    // online softmax update, one wave per head
-    for (int g = wave; g < G; g += ATTN_WAVES) {
-      const int n = t1 - t0;
-      const float sv = lane < n ? s_p[g][lane] : -INFINITY;
-      const float cm = wave_max(sv);
-      const float m_old = s_m[g];
-      const float m_new = fmaxf(m_old, cm);
-      const float e = lane < n ? expf(sv - m_new) : 0.0f;
-      const float es = wave_sum(e);
-      if (lane < n) s_p[g][lane] = e;
-      if (lane == 0) {
-        const float alpha = expf(m_old - m_new);
-        s_alpha[g] = alpha;
-        s_l[g] = s_l[g] * alpha + es;
-        s_m[g] = m_new;
-      }
-    }
-    __syncthreads();
-    // o = alpha * o + sum_t p_t v_t
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float a = s_alpha[g];
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) o[g][v] *= a;
-    }
-#pragma unroll
-    for (int i = 0; i < ATTN_MAXNI; ++i) {
-      const int t = t0 + (i * ATTN_WAVES + wave) * RPL + rsub;
-      if (i < NI && t < t1) {
-        float vf[VEC];
-        unpack<T, VEC>(vc[i], vf);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pr = s_p[g][t - t0];
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) o[g][v] = fmaf(pr, vf[v], o[g][v]);
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < ATTN_MAXNI; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
   }
+  // reduce the partial outputs over the row groups of each wave (xor shuffles, fixed order)
+#pragma unroll
+  for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k)
+#pragma unroll
+      for (int off = LPV; off < 64; off <<= 1) o[gi][k] += __shfl_xor(o[gi][k], off, 64);
 
-  // reduce o over the row groups of each wave, then over the waves (fixed order)
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v)
-      for (int off = 32; off >= LPR; off >>= 1) o[g][v] += __shfl_xor(o[g][v], off, 64);
-  if (rsub == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) s_o[wave][g][e0 + v] = o[g][v];
-  }
-  __syncthreads();
-  const int64_t pstride = hd + 2;
+#undef LLMK_LOAD_TILE
+#undef LLMK_STORE_TILE
+  // ---- this part's (max, sum, output) per head ----
+  const int64_t pstride = HD + 2;
   float* P = p.part + ((int64_t)kvh * p.n_parts + part) * G * pstride;
-  for (int idx = threadIdx.x; idx < G * hd; idx += ATTN_THREADS) {
-    const int g = idx / hd, e = idx % hd;
-    P[g * pstride + 2 + e] = ((s_o[0][g][e] + s_o[1][g][e]) + s_o[2][g][e]) + s_o[3][g][e];
-  }
-  if (threadIdx.x < G) {
-    P[threadIdx.x * pstride + 0] = s_m[threadIdx.x];
-    P[threadIdx.x * pstride + 1] = s_l[threadIdx.x];
+#pragma unroll
+  for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
+    const int g = wave + gi * ATTN_WAVES;
+    if (g >= G) continue;
+    if (rg == 0) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k)
+        if (vl * EPV + k < HD) st_dev(&P[g * pstride + 2 + vl * EPV + k], o[gi][k]);
+    }
+    if (lane == 0) {
+      st_dev(&P[g * pstride + 0], m_run[gi]);
+      st_dev(&P[g * pstride + 1], l_run[gi]);
+    }
   }
 
   // ---- last workgroup of this K/V head: log-sum-exp merge of the parts, in part order ----
-  __threadfence();
+  stores_done();
   __syncthreads();
   const int np = (ctx + span - 1) / span;
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&p.counters[kvh], 1u);
-    s_last = (prev == (unsigned)(np - 1));
-  }
+  if (threadIdx.x == 0) s_last = (take_ticket(&p.counters[kvh]) == (unsigned)(np - 1));
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  // every thread issues all its loads at once (max, sum and its output element of every part), so the
+  // merge costs one round trip; parts are combined in part order
   const float* PB = p.part + (int64_t)kvh * p.n_parts * G * pstride;
-  for (int idx = threadIdx.x; idx < np * G; idx += ATTN_THREADS) {
-    const int c = idx / G, g = idx % G;
-    s_wm[c][g] = PB[(int64_t)(c * G + g) * pstride + 0];
-    s_wl[c][g] = PB[(int64_t)(c * G + g) * pstride + 1];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float ms = -INFINITY;
-    for (int c = 0; c < np; ++c) ms = fmaxf(ms, s_wm[c][g]);
-    float L = 0.0f;
-    for (int c = 0; c < np; ++c) {
-      const float w = expf(s_wm[c][g] - ms);
-      s_wm[c][g] = w;
-      L += s_wl[c][g] * w;
+  const int64_t cstride = (int64_t)G * pstride;
+  for (int idx = threadIdx.x; idx < G * HD; idx += ATTN_THREADS) {
+    const int g = idx / HD, e = idx % HD;
+    const float* pg = PB + (int64_t)g * pstride;
+    float mc[ATTN_MAX_PARTS], lc[ATTN_MAX_PARTS], oc[ATTN_MAX_PARTS];
+#pragma unroll
+    for (int c = 0; c < ATTN_MAX_PARTS; ++c) {
+      const int cc = c < np ? c : np - 1;
+      mc[c] = ld_dev(pg + cc * cstride + 0);
+      lc[c] = ld_dev(pg + cc * cstride + 1);
+      oc[c] = ld_dev(pg + cc * cstride + 2 + e);
     }
-    s_inv[g] = 1.0f / L;
+    float ms = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < ATTN_MAX_PARTS; ++c) ms = c < np ? fmaxf(ms, mc[c]) : ms;
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int c = 0; c < ATTN_MAX_PARTS; ++c) {
+      if (c < np) {
+        const float w = expf(mc[c] - ms);
+        L = fmaf(lc[c], w, L);
+        O = fmaf(oc[c], w, O);
+      }
+    }
+    p.out[(int64_t)(kvh * G + g) * HD + e] = O / L;
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * hd; idx += ATTN_THREADS) {
-    const int g = idx / hd, e = idx % hd;
-    float acc = 0.0f;
-#pragma unroll 16
-    for (int c = 0; c < np; ++c) acc = fmaf(s_wm[c][g], PB[(int64_t)(c * G + g) * pstride + 2 + e], acc);
-    p.out[(int64_t)(kvh * G + g) * hd + e] = acc * s_inv[g];
-  }
-  if (threadIdx.x == 0) p.counters[kvh] = 0u;
+  if (threadIdx.x == 0) reset_ticket(&p.counters[kvh]);
+}
+
+static int tile_rows(int kv_is_bf16, int hd) {
+  const int row_bytes = ((hd * (kv_is_bf16 ? 2 : 4)) + 15) / 16 * 16;
+  return attn_tile_rows(row_bytes);
 }
 
 void attn_plan(AttnParams& p, int64_t max_ctx) {
-  const int vec = p.kv_is_bf16 ? 8 : 4;
-  const int v = p.hd < vec ? 1 : vec;
-  const int rpl = 64 / (p.hd / v);
-  int chunk = ATTN_WAVES * rpl * ATTN_MAXNI;
-  if (chunk > ATTN_MAXC) chunk = ATTN_MAXC;
-  p.chunk = chunk;
-  const int64_t n_sub = (max_ctx + chunk - 1) / chunk;
-  const int64_t target = 32;
+  p.chunk = tile_rows(p.kv_is_bf16, p.hd);
+  const int64_t n_sub = (max_ctx + p.chunk - 1) / p.chunk;
+  const char* env = getenv("LLMK_ATTN_PARTS");    // measurement sweeps only
+  int64_t target = (env && *env) ? atoi(env) : ATTN_MAX_PARTS;
+  if (target < 1) target = 1;
+  if (target > ATTN_MAX_PARTS) target = ATTN_MAX_PARTS;
   int64_t spw = (n_sub + target - 1) / target;
   if (spw < 1) spw = 1;
   p.sub_per_wg = (int32_t)spw;
   p.n_parts = (int32_t)((n_sub + spw - 1) / spw);
 }
 
-template <typename T, int VEC, int G>
+template <typename T, int HD>
 static hipError_t attn_one(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attn_kernel<T, VEC, G>), dim3((unsigned)p.n_parts, (unsigned)p.Hkv), dim3(ATTN_THREADS), 0, s, p);
+  hipLaunchKernelGGL((attn_kernel<T, HD>), dim3((unsigned)p.n_parts, (unsigned)p.Hkv), dim3(ATTN_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
-template <typename T, int VEC>
-static hipError_t attn_g(const AttnParams& p, hipStream_t s) {
-  switch (p.H / p.Hkv) {
-    case 1: return attn_one<T, VEC, 1>(p, s);
-    case 2: return attn_one<T, VEC, 2>(p, s);
-    case 3: return attn_one<T, VEC, 3>(p, s);
-    case 4: return attn_one<T, VEC, 4>(p, s);
-    case 5: return attn_one<T, VEC, 5>(p, s);
-    case 6: return attn_one<T, VEC, 6>(p, s);
-    case 7: return attn_one<T, VEC, 7>(p, s);
-    case 8: return attn_one<T, VEC, 8>(p, s);
+template <typename T>
+static hipError_t attn_hd(const AttnParams& p, hipStream_t s) {
+  switch (p.hd) {
+    case 2: return attn_one<T, 2>(p, s);
+    case 4: return attn_one<T, 4>(p, s);
+    case 8: return attn_one<T, 8>(p, s);
+    case 16: return attn_one<T, 16>(p, s);
+    case 32: return attn_one<T, 32>(p, s);
+    case 64: return attn_one<T, 64>(p, s);
+    case 128: return attn_one<T, 128>(p, s);
+    case 256: return attn_one<T, 256>(p, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t attn_launch(const AttnParams& p, hipStream_t s) {
-  if (p.kv_is_bf16) return p.hd < 8 ? attn_g<bf16_t, 1>(p, s) : attn_g<bf16_t, 8>(p, s);
-  return p.hd < 4 ? attn_g<float, 1>(p, s) : attn_g<float, 4>(p, s);
+  if (p.H / p.Hkv > 8 || p.H % p.Hkv != 0) return hipErrorInvalidValue;
+  return p.kv_is_bf16 ? attn_hd<bf16_t>(p, s) : attn_hd<float>(p, s);
 }
 
 }  // namespace llmk

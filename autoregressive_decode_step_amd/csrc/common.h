@@ -104,6 +104,27 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
   }
 }
 
+// ---- hand-off between workgroups of one launch (split-K partials, argmax and attention partials) ----
+// The producer stores with device scope (written through its XCD's L2), waits for its own stores, and
+// after a workgroup barrier one thread takes a ticket; the workgroup whose ticket is last reads every
+// partial with device-scope loads (served past the non-coherent L2s). No device-wide fence is used: on
+// this multi-XCD part a fence writes back and invalidates the whole L2 of the issuing XCD.
+
+__device__ __forceinline__ void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_dev(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_dev(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this thread's memory operations (the device-scope stores above all) have completed
+__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ unsigned take_ticket(unsigned* c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_ticket(unsigned* c) { __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
 // ---- device-resident decode state ---------------------------------------------------------------
 
 struct DecodeState {

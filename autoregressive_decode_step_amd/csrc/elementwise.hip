@@ -156,23 +156,18 @@ __global__ __launch_bounds__(EW_THREADS) void argmax_kernel(const float* logits,
     ix = s_i[0];
     for (int w = 1; w < EW_THREADS / 64; ++w)
       if (argmax_better(s_v[w], s_i[w], v, ix)) { v = s_v[w]; ix = s_i[w]; }
-    part_val[row * bpr + b] = v;
-    part_idx[row * bpr + b] = ix;
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&counters[row], 1u);
-    s_last = (prev == (unsigned)(bpr - 1));
+    st_dev(&part_val[row * bpr + b], v);
+    st_dev(&part_idx[row * bpr + b], ix);
+    stores_done();
+    s_last = (take_ticket(&counters[row]) == (unsigned)(bpr - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   v = -INFINITY;
   ix = INT_MAX;
   for (int q = threadIdx.x; q < bpr; q += EW_THREADS) {
-    const float bv = part_val[row * bpr + q];
-    const int bi = part_idx[row * bpr + q];
+    const float bv = ld_dev(&part_val[row * bpr + q]);
+    const int bi = ld_dev(&part_idx[row * bpr + q]);
     if (argmax_better(bv, bi, v, ix)) { v = bv; ix = bi; }
   }
   wave_argmax(v, ix);
@@ -185,7 +180,7 @@ __global__ __launch_bounds__(EW_THREADS) void argmax_kernel(const float* logits,
       if (argmax_better(s_v[w], s_i[w], v, ix)) { v = s_v[w]; ix = s_i[w]; }
     token[row] = ix;
     if (logit) logit[row] = v;
-    counters[row] = 0u;
+    reset_ticket(&counters[row]);
   }
 }
 

@@ -21,6 +21,7 @@
 // workgroup; ties to the lower index, NaN first).
 #include <float.h>
 #include <limits.h>
+#include <stdlib.h>
 
 #include "kernels.h"
 
@@ -28,38 +29,84 @@ namespace llmk {
 
 constexpr int GEMV_THREADS = 256;
 constexpr int GEMV_WAVES = 4;
+constexpr int GEMV_MAX_ROWS = 2048;   // input rows one workgroup stages in LDS
 
 __device__ __forceinline__ void store_kv(void* base, int is_bf16, int64_t i, float v) {
   if (is_bf16) static_cast<bf16_t*>(base)[i] = f32_to_bf16(v);
   else static_cast<float*>(base)[i] = v;
 }
 
-template <typename T, int VEC, int MODE>
+// Sum of squares of the K-element input (fp32, or a row of the weight dtype), by one wave. Loads go out
+// in groups of 8 per lane with clamped addresses and masked values, so a group is one round trip.
+template <typename T>
+__device__ __forceinline__ float input_sumsq(const float* inf, const T* inw, int in_is_w, int64_t K, int lane) {
+  float ss = 0.0f;
+  if (in_is_w && sizeof(T) == 2) {
+    const uint4* src = reinterpret_cast<const uint4*>(inw);   // 8 bf16 per 16 B; K % 8 == 0
+    const int64_t nv = K / 8;
+    for (int64_t b = lane; b < nv; b += 8 * 64) {
+      uint4 t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = src[min(b + k * 64, nv - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float v[8];
+        unpack<bf16_t, 8>(t[k], v);
+        const float m = (b + k * 64 < nv) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(v[e] * m, v[e], ss);
+      }
+    }
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(in_is_w ? reinterpret_cast<const float*>(inw) : inf);
+    const int64_t nv = K / 4;
+    for (int64_t b = lane; b < nv; b += 8 * 64) {
+      float4 t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = src[min(b + k * 64, nv - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float m = (b + k * 64 < nv) ? 1.0f : 0.0f;
+        ss = fmaf(t[k].x * m, t[k].x, ss);
+        ss = fmaf(t[k].y * m, t[k].y, ss);
+        ss = fmaf(t[k].z * m, t[k].z, ss);
+        ss = fmaf(t[k].w * m, t[k].w, ss);
+      }
+    }
+  }
+  return wave_sum(ss);
+}
+
+template <typename T, int VEC, int MODE, int LPR>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_t_kernel(const GemvParams p) {
-  constexpr int CB = 64 * VEC;
+  constexpr int RPI = 64 / LPR;                      // rows covered by one wave load instruction
+  constexpr int CB = LPR * VEC;                      // output columns of this workgroup
   constexpr int NACC = (MODE == GM_GATEUP) ? 2 : 1;
-  constexpr int U = (MODE == GM_GATEUP) ? 4 : 8;   // rows per load batch (divides 64)
+  constexpr int U = (MODE == GM_GATEUP) ? 8 : 16;    // load instructions per batch and matrix
   typedef typename Raw<T, VEC>::type RawT;
 
+  __shared__ float x_lds[GEMV_MAX_ROWS];
   __shared__ float red[GEMV_WAVES][NACC][CB];
   __shared__ float fin[NACC][CB];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lc = lane % LPR;                         // column slot of this lane
+  const int lr = lane / LPR;                         // row slot of this lane within an instruction
   const int cblk = blockIdx.x % p.n_cblk;
   const int ks = blockIdx.x / p.n_cblk;
   const int64_t col0 = (int64_t)cblk * CB;
   const int64_t k0 = (int64_t)ks * p.rows_per_split;
   const int64_t k1 = min(k0 + p.rows_per_split, p.K);
   const int64_t span = k1 - k0;
-  const int64_t per_wave = ((span + GEMV_WAVES - 1) / GEMV_WAVES + U - 1) / U * U;
+  const int64_t per_wave = ((span + GEMV_WAVES - 1) / GEMV_WAVES + RPI - 1) / RPI * RPI;
   const int64_t kw0 = k0 + min(span, (int64_t)wave * per_wave);
   const int64_t kw1 = k0 + min(span, (int64_t)(wave + 1) * per_wave);
 
-  // this lane's columns and the matrix they live in
-  const int64_t c = col0 + (int64_t)lane * VEC;
-  const bool active = c < p.N;
+  // this lane's columns and the matrix they live in; lanes past N read column 0 (results discarded)
+  const int64_t c_raw = col0 + (int64_t)lc * VEC;
+  const int64_t c = c_raw < p.N ? c_raw : 0;
   const T* wa = static_cast<const T*>(p.w0);
   const T* wb = static_cast<const T*>(p.w1);
   int64_t lda = p.N;
@@ -72,34 +119,32 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_t_kernel(const GemvParams p
     if (MODE == GM_GATEUP) wb += c;
   }
 
-  RawT ca[U], cb[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t r = kw0 + u;
-    if (active && r < kw1) {
-      ca[u] = load_raw<T, VEC>(wa + r * lda);
-      if (NACC == 2) cb[u] = load_raw<T, VEC>(wb + r * lda);
-    } else {
-      ca[u] = RawT{};
-      cb[u] = RawT{};
-    }
+  const int64_t last = max(kw1 - 1, k0);
+  constexpr int64_t STEP = (int64_t)U * RPI;   // rows per batch
+  // two register sets, A and B, alternate: the next batch is always in flight while one is consumed
+  RawT a0[U], a1[U], b0[U], b1[U];
+#define LLMK_ISSUE(RA, RB, R)                                         \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                     \
+    const int64_t rr = min((R) + u * RPI + lr, last);                 \
+    RA[u] = load_raw<T, VEC>(wa + rr * lda);                          \
+    if (NACC == 2) RB[u] = load_raw<T, VEC>(wb + rr * lda);           \
   }
+  LLMK_ISSUE(a0, b0, kw0)
 
-  // ---- prologue: the input vector (optionally RMSNormed), overlapping the first loads ----
+  // input rows of this workgroup into LDS (RMSNormed when gain is given), zero past k1
   const float* inf = static_cast<const float*>(p.in);
   const T* inw = static_cast<const T*>(p.in);
   if (p.in_state) inw += (int64_t)p.in_state->token * p.K;
   float scale = 1.0f;
-  if (p.gain) {
-    float ss = 0.0f;
-#pragma unroll 8
-    for (int64_t i = lane; i < p.K; i += 64) {
-      const float v = p.in_is_w ? load_elem<T>(inw, i) : inf[i];
-      ss += v * v;
-    }
-    ss = wave_sum(ss);
-    scale = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+  if (p.gain) scale = 1.0f / sqrtf(input_sumsq<T>(inf, inw, p.in_is_w, p.K, lane) / (float)p.K + p.eps);
+  const int64_t xr = per_wave * GEMV_WAVES;
+  for (int64_t i = threadIdx.x; i < xr; i += GEMV_THREADS) {
+    const int64_t row = min(k0 + i, p.K - 1);
+    float v = p.in_is_w ? load_elem<T>(inw, row) : inf[row];
+    if (p.gain) v = v * scale * p.gain[row];
+    x_lds[i] = (k0 + i < k1) ? v : 0.0f;
   }
+  __syncthreads();
 
   float acc[NACC][VEC];
 #pragma unroll
@@ -107,55 +152,49 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_t_kernel(const GemvParams p
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[a][v] = 0.0f;
 
-  float xseg = 0.0f;
-  for (int64_t r = kw0; r < kw1; r += U) {
-    const int seg_lane = (int)((r - kw0) & 63);
-    if (seg_lane == 0) {
-      const int64_t rr = r + lane;
-      float v = 0.0f;
-      if (rr < kw1) {
-        v = p.in_is_w ? load_elem<T>(inw, rr) : inf[rr];
-        if (p.gain) v = v * scale * p.gain[rr];
-      }
-      xseg = v;
-    }
-    RawT na[U], nb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t rn = r + U + u;
-      if (active && rn < kw1) {
-        na[u] = load_raw<T, VEC>(wa + rn * lda);
-        if (NACC == 2) nb[u] = load_raw<T, VEC>(wb + rn * lda);
-      } else {
-        na[u] = RawT{};
-        nb[u] = RawT{};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float xv = readlane_f(xseg, seg_lane + u);
-      float w[VEC];
-      unpack<T, VEC>(ca[u], w);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[0][v] = fmaf(w[v], xv, acc[0][v]);
-      if (NACC == 2) {
-        unpack<T, VEC>(cb[u], w);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[NACC - 1][v] = fmaf(w[v], xv, acc[NACC - 1][v]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      ca[u] = na[u];
-      cb[u] = nb[u];
-    }
+#define LLMK_CONSUME(RA, RB, R)                                               \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                             \
+    const int64_t row = (R) + u * RPI + lr;                                   \
+    const float xu = row < kw1 ? x_lds[row - k0] : 0.0f;                      \
+    float w[VEC];                                                             \
+    unpack<T, VEC>(RA[u], w);                                                 \
+    _Pragma("unroll") for (int v = 0; v < VEC; ++v) acc[0][v] = fmaf(w[v], xu, acc[0][v]); \
+    if (NACC == 2) {                                                          \
+      unpack<T, VEC>(RB[u], w);                                               \
+      _Pragma("unroll") for (int v = 0; v < VEC; ++v) acc[NACC - 1][v] = fmaf(w[v], xu, acc[NACC - 1][v]); \
+    }                                                                         \
   }
 
-  // ---- reduce the 4 waves (fixed order) ----
+  if (kw1 > kw0) {
+    int64_t r = kw0;
+    if (r + STEP < kw1) { LLMK_ISSUE(a1, b1, r + STEP) }
+    for (;;) {
+      LLMK_CONSUME(a0, b0, r)
+      r += STEP;
+      if (r >= kw1) break;
+      if (r + STEP < kw1) { LLMK_ISSUE(a0, b0, r + STEP) }
+      LLMK_CONSUME(a1, b1, r)
+      r += STEP;
+      if (r >= kw1) break;
+      if (r + STEP < kw1) { LLMK_ISSUE(a1, b1, r + STEP) }
+    }
+  }
+#undef LLMK_ISSUE
+#undef LLMK_CONSUME
+
+  // ---- reduce the row slots of each wave (xor shuffles), then the 4 waves (fixed order) ----
 #pragma unroll
   for (int a = 0; a < NACC; ++a)
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) red[wave][a][lane * VEC + v] = acc[a][v];
+    for (int v = 0; v < VEC; ++v)
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) acc[a][v] += __shfl_xor(acc[a][v], off, 64);
+  if (lr == 0) {
+#pragma unroll
+    for (int a = 0; a < NACC; ++a)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) red[wave][a][lc * VEC + v] = acc[a][v];
+  }
   __syncthreads();
 
   if (p.ksplit == 1) {
@@ -167,72 +206,35 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_t_kernel(const GemvParams p
       if (col0 + j < p.N) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a)
-          p.partial[((int64_t)ks * NACC + a) * p.N + col0 + j] =
-              ((red[0][a][j] + red[1][a][j]) + red[2][a][j]) + red[3][a][j];
+          st_dev(&p.partial[((int64_t)ks * NACC + a) * p.N + col0 + j],
+                 ((red[0][a][j] + red[1][a][j]) + red[2][a][j]) + red[3][a][j]);
       }
     }
-    __threadfence();
+    stores_done();
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev = atomicAdd(&p.counters[cblk], 1u);
-      s_last = (prev == (unsigned)(p.ksplit - 1));
-    }
+    if (threadIdx.x == 0) s_last = (take_ticket(&p.counters[cblk]) == (unsigned)(p.ksplit - 1));
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    // sum the partials of this strip in split order; P threads share a column group
-    if constexpr (VEC >= 4) {
-      constexpr int NG = CB / 4;                  // float4 column groups
-      constexpr int P = GEMV_THREADS / NG;        // split ranges per group (2 for bf16, 4 for fp32)
-      float4* tmp = reinterpret_cast<float4*>(&red[0][0][0]);   // reuse: [NACC][P][NG] float4
-      const int g = threadIdx.x % NG, part = threadIdx.x / NG;
-      const int per = (p.ksplit + P - 1) / P;
-      const int kb = part * per, ke = min(p.ksplit, kb + per);
-      const int64_t col = col0 + (int64_t)g * 4;
+    // sum the partials of this strip in split order (all loads of a thread issued together)
+    for (int j = threadIdx.x; j < CB * NACC; j += GEMV_THREADS) {
+      const int a = j / CB, jj = j % CB;
+      float s = 0.0f;
+      if (col0 + jj < p.N) {
+        const float* src = p.partial + (int64_t)a * p.N + col0 + jj;
+        const int64_t stride = (int64_t)NACC * p.N;
+        int k = 0;
+        for (; k + 16 <= p.ksplit; k += 16) {
+          float t[16];
 #pragma unroll
-      for (int a = 0; a < NACC; ++a) {
-        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (col < p.N) {
-          int k = kb;
-          for (; k + 8 <= ke; k += 8) {
-            float4 t[8];
+          for (int i = 0; i < 16; ++i) t[i] = ld_dev(src + (int64_t)(k + i) * stride);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              t[i] = *reinterpret_cast<const float4*>(p.partial + ((int64_t)(k + i) * NACC + a) * p.N + col);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { s.x += t[i].x; s.y += t[i].y; s.z += t[i].z; s.w += t[i].w; }
-          }
-          for (; k < ke; ++k) {
-            const float4 t = *reinterpret_cast<const float4*>(p.partial + ((int64_t)k * NACC + a) * p.N + col);
-            s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
-          }
+          for (int i = 0; i < 16; ++i) s += t[i];
         }
-        tmp[(a * P + part) * NG + g] = s;
+        for (; k < p.ksplit; ++k) s += ld_dev(src + (int64_t)k * stride);
       }
-      __syncthreads();
-      if (part == 0) {
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) {
-          float4 s = tmp[(a * P) * NG + g];
-          for (int q = 1; q < P; ++q) {
-            const float4 t = tmp[(a * P + q) * NG + g];
-            s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
-          }
-          fin[a][g * 4 + 0] = s.x; fin[a][g * 4 + 1] = s.y; fin[a][g * 4 + 2] = s.z; fin[a][g * 4 + 3] = s.w;
-        }
-      }
-    } else {
-      for (int j = threadIdx.x; j < CB; j += GEMV_THREADS) {
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) {
-          float s = 0.0f;
-          if (col0 + j < p.N)
-            for (int k = 0; k < p.ksplit; ++k) s += p.partial[((int64_t)k * NACC + a) * p.N + col0 + j];
-          fin[a][j] = s;
-        }
-      }
+      fin[a][jj] = s;
     }
-    if (threadIdx.x == 0) p.counters[cblk] = 0u;
+    if (threadIdx.x == 0) reset_ticket(&p.counters[cblk]);
   }
   __syncthreads();
 
@@ -251,74 +253,80 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_t_kernel(const GemvParams p
       const float xn = b + fin[0][j];
       p.x[col] = xn;
       if (p.hidden) p.hidden[col] = xn;
-    } else {  // GM_QKV
-      const int hd = p.head_dim, half = hd >> 1;
-      const int i = (int)(col % hd);
-      const int pos = p.state->pos;
-      const bool is_q = col < p.n0;
-      const bool is_k = !is_q && col < p.n0 + p.n1;
-      float val = fin[0][j];
-      if (is_q || is_k) {
-        bool first;
-        int jj, partner;
-        if (p.rope_layout == 0) {
-          first = i < half;
-          jj = first ? i : i - half;
-          partner = first ? j + half : j - half;
-        } else {
-          first = (i & 1) == 0;
-          jj = i >> 1;
-          partner = j ^ 1;
-        }
-        const float cs = p.rope_table[((int64_t)pos * half + jj) * 2 + 0];
-        const float sn = p.rope_table[((int64_t)pos * half + jj) * 2 + 1];
-        const float other = fin[0][partner];
-        val = first ? (val * cs - other * sn) : (other * sn + val * cs);
-      }
-      if (is_q) p.y[col] = val;
-      else if (is_k) store_kv(p.kcache, p.kv_is_bf16, p.kv_off + (int64_t)pos * p.n1 + (col - p.n0), val);
-      else store_kv(p.vcache, p.kv_is_bf16, p.kv_off + (int64_t)pos * p.n1 + (col - p.n0 - p.n1), val);
+    } else {  // GM_QKV: raw q|k|v (rotation and the K/V append happen in the attention kernel)
+      p.y[col] = fin[0][j];
     }
   }
 }
 
-void gemv_plan(GemvParams& p, int w_is_bf16, int vec1, int target_blocks, int min_rows) {
-  const int cb = gemv_cols_per_block(w_is_bf16, vec1);
+int gemv_vec(int w_is_bf16, int vec1) { return vec1 ? 1 : (w_is_bf16 ? 8 : 4); }
+
+// Tuning knobs for measurement sweeps (unset in normal use): LLMK_GEMV_BLOCKS overrides the target
+// workgroup count, LLMK_GEMV_LPR the lanes per row segment (16, 32 or 64).
+static int env_int(const char* name, int def) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : def;
+}
+
+void gemv_plan(GemvParams& p, int w_is_bf16, int vec1, int target_blocks, int min_cols) {
+  const int vec = gemv_vec(w_is_bf16, vec1);
+  target_blocks = env_int("LLMK_GEMV_BLOCKS", target_blocks);
+  int lpr = vec1 ? 64 : env_int("LLMK_GEMV_LPR", 16);
+  if (lpr != 16 && lpr != 32 && lpr != 64) lpr = 16;
+  while (lpr < 64 && lpr * vec < min_cols) lpr *= 2;
+  p.lpr = lpr;
+  const int cb = lpr * vec;
+  const int rpi = 64 / lpr;
   p.n_cblk = (int32_t)((p.N + cb - 1) / cb);
-  int64_t want = target_blocks / p.n_cblk;
-  if (want < 1) want = 1;
-  int64_t rps = (p.K + want - 1) / want;
-  if (rps < min_rows) rps = min_rows;
-  rps = (rps + 31) / 32 * 32;
-  if (rps >= p.K) rps = p.K;
+  int64_t ksplit = (target_blocks + p.n_cblk / 2) / p.n_cblk;
+  if (ksplit < 1) ksplit = 1;
+  // a workgroup's rows must fit the LDS input stage (with the per-wave rounding)
+  const int64_t max_rows = GEMV_MAX_ROWS - GEMV_WAVES * rpi;
+  const int64_t min_split = (p.K + max_rows - 1) / max_rows;
+  if (ksplit < min_split) ksplit = min_split;
+  if (ksplit > p.K) ksplit = p.K;
+  int64_t rps = (p.K + ksplit - 1) / ksplit;
+  rps = (rps + GEMV_WAVES * rpi - 1) / (GEMV_WAVES * rpi) * (GEMV_WAVES * rpi);
+  if (rps > max_rows) rps = max_rows / (GEMV_WAVES * rpi) * (GEMV_WAVES * rpi);
   p.rows_per_split = rps;
   p.ksplit = (int32_t)((p.K + rps - 1) / rps);
 }
 
-template <typename T, int VEC, int MODE>
+template <typename T, int VEC, int MODE, int LPR>
 static hipError_t launch_one(const GemvParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_t_kernel<T, VEC, MODE>), dim3((unsigned)(p.n_cblk * p.ksplit)), dim3(GEMV_THREADS), 0, s, p);
+  hipLaunchKernelGGL((gemv_t_kernel<T, VEC, MODE, LPR>), dim3((unsigned)(p.n_cblk * p.ksplit)), dim3(GEMV_THREADS), 0,
+                     s, p);
   return hipGetLastError();
+}
+
+template <typename T, int VEC, int MODE>
+static hipError_t launch_lpr(const GemvParams& p, hipStream_t s) {
+  switch (p.lpr) {
+    case 16: return launch_one<T, VEC, MODE, 16>(p, s);
+    case 32: return launch_one<T, VEC, MODE, 32>(p, s);
+    case 64: return launch_one<T, VEC, MODE, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t gemv_launch(const GemvParams& p, int mode, int w_is_bf16, int vec1, hipStream_t s) {
   if (vec1) {
-    if (mode != GM_PLAIN) return hipErrorInvalidValue;
-    return w_is_bf16 ? launch_one<bf16_t, 1, GM_PLAIN>(p, s) : launch_one<float, 1, GM_PLAIN>(p, s);
+    if (mode != GM_PLAIN || p.lpr != 64) return hipErrorInvalidValue;
+    return w_is_bf16 ? launch_one<bf16_t, 1, GM_PLAIN, 64>(p, s) : launch_one<float, 1, GM_PLAIN, 64>(p, s);
   }
   if (w_is_bf16) {
     switch (mode) {
-      case GM_PLAIN: return launch_one<bf16_t, 8, GM_PLAIN>(p, s);
-      case GM_QKV: return launch_one<bf16_t, 8, GM_QKV>(p, s);
-      case GM_RESID: return launch_one<bf16_t, 8, GM_RESID>(p, s);
-      case GM_GATEUP: return launch_one<bf16_t, 8, GM_GATEUP>(p, s);
+      case GM_PLAIN: return launch_lpr<bf16_t, 8, GM_PLAIN>(p, s);
+      case GM_QKV: return launch_lpr<bf16_t, 8, GM_QKV>(p, s);
+      case GM_RESID: return launch_lpr<bf16_t, 8, GM_RESID>(p, s);
+      case GM_GATEUP: return launch_lpr<bf16_t, 8, GM_GATEUP>(p, s);
     }
   } else {
     switch (mode) {
-      case GM_PLAIN: return launch_one<float, 4, GM_PLAIN>(p, s);
-      case GM_QKV: return launch_one<float, 4, GM_QKV>(p, s);
-      case GM_RESID: return launch_one<float, 4, GM_RESID>(p, s);
-      case GM_GATEUP: return launch_one<float, 4, GM_GATEUP>(p, s);
+      case GM_PLAIN: return launch_lpr<float, 4, GM_PLAIN>(p, s);
+      case GM_QKV: return launch_lpr<float, 4, GM_QKV>(p, s);
+      case GM_RESID: return launch_lpr<float, 4, GM_RESID>(p, s);
+      case GM_GATEUP: return launch_lpr<float, 4, GM_GATEUP>(p, s);
     }
   }
   return hipErrorInvalidValue;
@@ -341,54 +349,68 @@ __global__ __launch_bounds__(GEMV_THREADS) void head_kernel(const HeadParams p) 
   const int64_t r1 = min(r0 + p.rows_per_block, p.rows);
   const T* W = static_cast<const T*>(p.w);
 
-  // rows handled by this wave: groups of R consecutive rows, groups dealt round-robin to the 4 waves
+  // rows handled by this wave: groups of R consecutive rows, groups dealt round-robin to the 4 waves.
+  // Loads are clamped to the block's last row (a duplicate row is computed and discarded) so every
+  // batch is straight-line code: R*NP independent 16-byte loads, then the dots.
+  const int64_t last = r1 - 1;
   int64_t rb = r0 + (int64_t)wave * R;
   RawT cur[R][NP];
+  auto issue = [&](int64_t base) {
 #pragma unroll
-  for (int rr = 0; rr < R; ++rr)
+    for (int rr = 0; rr < R; ++rr) {
+      const int64_t row = min(base + rr, last);
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int64_t c = (int64_t)(pp * 64 + lane) * VEC;
-      if (rb + rr < r1 && c < p.cols) cur[rr][pp] = load_raw<T, VEC>(W + (rb + rr) * p.cols + c);
-      else cur[rr][pp] = RawT{};
+      for (int pp = 0; pp < NP; ++pp) {
+        const int64_t cidx = (int64_t)(pp * 64 + lane) * VEC;
+        const int64_t cc = cidx < p.cols ? cidx : 0;
+        cur[rr][pp] = load_raw<T, VEC>(W + row * p.cols + cc);
+      }
     }
+  };
+  if (rb < r1) issue(rb);
 
   // input (optionally RMSNormed), held in registers: lane owns columns (pp*64 + lane)*VEC + v
+  // (clamped addresses, masked values: no branches between the weight loads and their use)
   float xr[NP][VEC];
   float ss = 0.0f;
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
-    const int64_t c = (int64_t)(pp * 64 + lane) * VEC;
+    const int64_t cidx = (int64_t)(pp * 64 + lane) * VEC;
+    const bool ok = cidx < p.cols;
+    const float4* x4 = reinterpret_cast<const float4*>(p.x + (ok ? cidx : 0));
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      xr[pp][v] = (c + v < p.cols) ? p.x[c + v] : 0.0f;
-      ss += xr[pp][v] * xr[pp][v];
+    for (int v4 = 0; v4 < VEC / 4; ++v4) {
+      const float4 t = x4[v4];
+      xr[pp][v4 * 4 + 0] = ok ? t.x : 0.0f;
+      xr[pp][v4 * 4 + 1] = ok ? t.y : 0.0f;
+      xr[pp][v4 * 4 + 2] = ok ? t.z : 0.0f;
+      xr[pp][v4 * 4 + 3] = ok ? t.w : 0.0f;
     }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) ss = fmaf(xr[pp][v], xr[pp][v], ss);
   }
   if (p.gain) {
     ss = wave_sum(ss);
     const float sc = 1.0f / sqrtf(ss / (float)p.cols + p.eps);
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
-      const int64_t c = (int64_t)(pp * 64 + lane) * VEC;
+      const int64_t cidx = (int64_t)(pp * 64 + lane) * VEC;
+      const bool ok = cidx < p.cols;
+      const float4* g4 = reinterpret_cast<const float4*>(p.gain + (ok ? cidx : 0));
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) xr[pp][v] = (c + v < p.cols) ? xr[pp][v] * sc * p.gain[c + v] : 0.0f;
+      for (int v4 = 0; v4 < VEC / 4; ++v4) {
+        const float4 g = g4[v4];
+        xr[pp][v4 * 4 + 0] = xr[pp][v4 * 4 + 0] * sc * g.x;
+        xr[pp][v4 * 4 + 1] = xr[pp][v4 * 4 + 1] * sc * g.y;
+        xr[pp][v4 * 4 + 2] = xr[pp][v4 * 4 + 2] * sc * g.z;
+        xr[pp][v4 * 4 + 3] = xr[pp][v4 * 4 + 3] * sc * g.w;
+      }
     }
   }
 
   float best = -INFINITY;
   int best_i = INT_MAX;
-  for (; rb < r1; rb += (int64_t)GEMV_WAVES * R) {
-    const int64_t rn = rb + (int64_t)GEMV_WAVES * R;
-    RawT nxt[R][NP];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        const int64_t c = (int64_t)(pp * 64 + lane) * VEC;
-        if (rn + rr < r1 && c < p.cols) nxt[rr][pp] = load_raw<T, VEC>(W + (rn + rr) * p.cols + c);
-        else nxt[rr][pp] = RawT{};
-      }
+  while (rb < r1) {
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       float dot = 0.0f;
@@ -406,10 +428,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void head_kernel(const HeadParams p) 
         if (argmax_better(dot, (int)row, best, best_i)) { best = dot; best_i = (int)row; }
       }
     }
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp) cur[rr][pp] = nxt[rr][pp];
+    rb += (int64_t)GEMV_WAVES * R;
+    if (rb < r1) issue(rb);
   }
 
   if (!p.part_val) return;
@@ -422,25 +442,20 @@ __global__ __launch_bounds__(GEMV_THREADS) void head_kernel(const HeadParams p) 
     int ix = s_idx[0];
     for (int w = 1; w < GEMV_WAVES; ++w)
       if (argmax_better(s_val[w], s_idx[w], v, ix)) { v = s_val[w]; ix = s_idx[w]; }
-    p.part_val[blockIdx.x] = v;
-    p.part_idx[blockIdx.x] = ix;
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(p.counter, 1u);
-    s_last = (prev == (unsigned)(gridDim.x - 1));
+    st_dev(&p.part_val[blockIdx.x], v);
+    st_dev(&p.part_idx[blockIdx.x], ix);
+    stores_done();
+    s_last = (take_ticket(p.counter) == (unsigned)(gridDim.x - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   // ---- pass 2 (last workgroup): best over all workgroups ----
   float v = -INFINITY;
   int ix = INT_MAX;
   for (int b = threadIdx.x; b < (int)gridDim.x; b += GEMV_THREADS) {
-    const float bv = p.part_val[b];
-    const int bi = p.part_idx[b];
+    const float bv = ld_dev(&p.part_val[b]);
+    const int bi = ld_dev(&p.part_idx[b]);
     if (argmax_better(bv, bi, v, ix)) { v = bv; ix = bi; }
   }
   wave_argmax(v, ix);
@@ -459,7 +474,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void head_kernel(const HeadParams p) 
       p.state->pos = p.state->pos + 1;
       p.state->step = step + 1;
     }
-    *p.counter = 0u;
+    reset_ticket(p.counter);
   }
 }
 
@@ -482,8 +497,8 @@ static hipError_t head_one(const HeadParams& p, hipStream_t s) {
 template <typename T, int VEC>
 static hipError_t head_dispatch(const HeadParams& p, hipStream_t s) {
   const int64_t np = (p.cols + 64 * VEC - 1) / (64 * VEC);
-  if (np <= 1) return head_one<T, VEC, 1, 8>(p, s);
-  if (np <= 2) return head_one<T, VEC, 2, 4>(p, s);
+  if (np <= 1) return head_one<T, VEC, 1, 16>(p, s);
+  if (np <= 2) return head_one<T, VEC, 2, 8>(p, s);
   if (np <= 4) return head_one<T, VEC, 4, 4>(p, s);
   if (np <= 8) return head_one<T, VEC, 8, 2>(p, s);
   if (np <= 16) return head_one<T, VEC, 16, 1>(p, s);

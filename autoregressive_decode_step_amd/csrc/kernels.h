@@ -24,6 +24,7 @@ struct GemvParams {
   int64_t K, N;            // rows of A (= length of the input), output columns
   int64_t rows_per_split;  // rows handled by one workgroup
   int32_t ksplit, n_cblk;  // grid = ksplit * n_cblk workgroups
+  int32_t lpr;             // lanes per row segment (16, 32 or 64): a workgroup owns lpr * VEC columns
   // input vector of length K: fp32, or a row of the weight dtype (the embedding table) chosen by token
   const void* in;
   int32_t in_is_w;               // 1: `in` has the weight dtype
@@ -34,27 +35,17 @@ struct GemvParams {
   float* partial;                // [ksplit][NACC][N]
   unsigned* counters;            // [n_cblk], zero on entry, left zero on exit
   // epilogue
-  float* y;                      // PLAIN: y[N]; GATEUP: u[N]; QKV: q[n0]
+  float* y;                      // PLAIN and QKV: y[N] (q|k|v raw); GATEUP: u[N]
   float* x;                      // RESID: residual stream, x = base + A^T in
   const void* base;              // RESID: base (fp32 x itself, or the embedding table of weight dtype)
   int32_t base_is_w;             // 1: base is the embedding table, row chosen by base_state->token
   const DecodeState* base_state;
   float* hidden;                 // RESID: optional copy of the new x
-  const DecodeState* state;      // QKV: position of the token
-  void* kcache;                  // QKV: layer's K buffer; element offset kv_off + pos*n1 + col
-  void* vcache;
-  int32_t kv_is_bf16;
-  int64_t kv_off;
-  int32_t head_dim;
-  int32_t rope_layout;
-  const float* rope_table;       // [max_pos][hd/2][2]
 };
 
-// columns per workgroup of the vector path for a weight dtype (64 lanes x 16 B)
-inline int gemv_cols_per_block(int w_is_bf16, int vec1) { return vec1 ? 64 : (w_is_bf16 ? 512 : 256); }
-
-// Fills ksplit/n_cblk/rows_per_split for a K x N problem (rows_per_split a multiple of 4 x 8).
-void gemv_plan(GemvParams& p, int w_is_bf16, int vec1, int target_blocks, int min_rows);
+// Fills lpr/ksplit/n_cblk/rows_per_split for a K x N problem: about target_blocks workgroups, each
+// owning at least min_cols output columns (the q|k|v epilogue needs whole heads in one workgroup).
+void gemv_plan(GemvParams& p, int w_is_bf16, int vec1, int target_blocks, int min_cols);
 hipError_t gemv_launch(const GemvParams& p, int mode, int w_is_bf16, int vec1, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------
@@ -86,6 +77,38 @@ hipError_t rowdot_simple_launch(const void* w, int w_is_bf16, const float* x, fl
                                 hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------
+// Row-dot GEMV over output-major weights (W [rows][K]): y[r] = W[r] . h with per-row epilogues.
+// ------------------------------------------------------------------------------------------------
+
+constexpr int RD_MAX_ROWS = 256;   // rows one workgroup owns, at most
+
+struct RowdotParams {
+  const void* w0;          // PLAIN/RESID: the matrix; GATEUP: gate; QKV: wq
+  const void* w1;          // GATEUP: up; QKV: wk
+  const void* w2;          // QKV: wv
+  int64_t n0, n1;          // QKV: rows of wq and wk
+  int64_t N, K;            // output rows, input length
+  int64_t rows_per_block;
+  int32_t n_blocks, kw, np, r;
+  const void* in;          // input: fp32, or the embedding row (weight dtype) chosen by in_state->token
+  int32_t in_is_w;
+  const DecodeState* in_state;
+  const float* gain;       // non-null: RMSNorm the input first
+  float eps;
+  float* y;                // PLAIN/QKV: y[N]; GATEUP: u[N]
+  float* x;                // RESID: x = base + y
+  const void* base;
+  int32_t base_is_w;
+  const DecodeState* base_state;
+  float* hidden;
+};
+
+// Fills kw/np/r/rows_per_block/n_blocks (N and K set); -1 if K does not fit the kernel.
+int rowdot_plan(RowdotParams& p, int w_is_bf16, int mode);
+hipError_t rowdot_launch(const RowdotParams& p, int mode, int w_is_bf16, hipStream_t s);
+hipError_t transpose_launch(const void* src, void* dst, int64_t rows, int64_t cols, int is_bf16, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------------
 // Split-context grouped-query attention for one query position, plus the log-sum-exp merge.
 // ------------------------------------------------------------------------------------------------
 
@@ -103,9 +126,16 @@ struct AttnParams {
   float* part;                 // [Hkv][n_parts][G][hd + 2]: max, sum, unnormalised output
   unsigned* counters;          // [Hkv], zero on entry and exit
   float* out;                  // [H][hd]
+  // decode step: q|k|v of this position arrive unrotated; q and k are rotated by the position here and
+  // k, v are appended (rounded to the cache dtype) to k_w / v_w, the writable views of k / v
+  const float* qkv_raw;        // [H*hd | Hkv*hd | Hkv*hd] or nullptr (then q is used as given)
+  void* k_w;
+  void* v_w;
+  const float* rope_table;     // [max_pos][hd/2][2]
+  int32_t rope_layout;
 };
 
-constexpr int ATTN_MAX_PARTS = 32;
+constexpr int ATTN_MAX_PARTS = 16;
 // Fills chunk / sub_per_wg / n_parts for contexts up to max_ctx.
 void attn_plan(AttnParams& p, int64_t max_ctx);
 hipError_t attn_launch(const AttnParams& p, hipStream_t s);

@@ -9,20 +9,21 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BF16, F32, Config, KVPool, Model, check, decode_step, decode_steps, decode_workspace_bytes,
-               make_config, rope_table_init, workspace)
+from . import (BF16, F32, W_IN_OUT, W_OUT_IN, Config, KVPool, Model, check, decode_step, decode_steps,
+               decode_workspace_bytes, make_config, rope_table_init, transpose, workspace)
 
 _LAYER_MAP = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("gate", "w_gate"), ("up", "w_up"),
               ("down", "w_down"), ("n1", "g_attn"), ("n2", "g_ffn"))
 
 
-def config_from(shape) -> Config:
+def config_from(shape, w_layout=W_OUT_IN) -> Config:
     """llmk_config from any object with vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps,
-    rope_base, rope_layout, w_dtype ('f32'/'bf16') and kv_dtype attributes."""
+    rope_base, rope_layout, w_dtype ('f32'/'bf16') and kv_dtype attributes. upload_model repacks the
+    projections to match w_layout."""
     code = {"f32": F32, "bf16": BF16}
     return make_config(shape.vocab, shape.d, shape.n_layer, shape.n_head, shape.n_kv, shape.head_dim, shape.hidden,
                        shape.max_seq, shape.eps, shape.rope_base, shape.rope_layout, code[shape.w_dtype],
-                       code[shape.kv_dtype])
+                       code[shape.kv_dtype], w_layout)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -43,8 +44,20 @@ def upload_model(cfg: Config, W: dict, device="cuda", stream=None) -> Model:
     norm = to_device(np.asarray(W["norm"], dtype=np.float32), device)
     layers = []
     for L in W["layers"]:
-        layers.append({dst: to_device(L[src] if src not in ("n1", "n2") else np.asarray(L[src], np.float32), device)
-                       for src, dst in _LAYER_MAP})
+        dev_layer = {}
+        for src, dst in _LAYER_MAP:
+            if src in ("n1", "n2"):
+                dev_layer[dst] = to_device(np.asarray(L[src], np.float32), device)
+                continue
+            a = to_device(L[src], device)               # [in][out], as given
+            if cfg.w_layout == W_OUT_IN:                # repack once, on the device, into [out][in]
+                rows, cols = L[src].shape
+                t = torch.empty_like(a)
+                check(transpose(a, t, rows, cols, stream), "transpose")
+                del a
+                a = t
+            dev_layer[dst] = a
+        layers.append(dev_layer)
     table = torch.empty(cfg.max_seq * cfg.head_dim, dtype=torch.float32, device=device)
     check(rope_table_init(table, cfg.max_seq, cfg.head_dim, cfg.rope_base, stream), "rope_table_init")
     return Model(cfg, emb, out, norm, table, layers)

@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Decode throughput at batch 1 on the Llama-3-8B-shaped decoder, one MI355X.
+
+Workload: bf16 weights N(0, 0.02) (seeded, random init), unit norm gains, RoPE base 5e5, a bf16 K/V
+pool whose positions 0..4095 hold seeded N(0, 1) values, then greedy steps from position 4096 with
+device-side token feedback (one captured step replayed per token). A step is the whole decode step:
+embedding, 32 layers of norm + q|k|v + RoPE + K/V append + attention + o + norm + gate|up + SiLU-gate +
+down, final norm, output head and argmax. Inputs are resident in HBM before the timed region.
+
+Prints one JSON line: tokens/s, ms per step, algorithmic HBM GB/s of the whole step, the roofline of
+the dominant kernel (the gate|up GEMV, timed live with HIP events on its own stream), and the oracle's
+throughput on the host cores for a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+N_PRE = 4096                    # filled context before the first timed step
+PMC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemv_llama8b_pmc.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(s, ctx: int) -> int:
+    """Algorithmic HBM bytes of one decode step attending `ctx` positions: every weight once, the
+    embedding row, the gains, the RoPE table row, the K/V of the attended context, the appended K/V,
+    and the logits written once."""
+    wsz = 2 if s.w_dtype == "bf16" else 4
+    kvsz = 2 if s.kv_dtype == "bf16" else 4
+    d, qd, kvd, F, V, L = s.d, s.n_head * s.head_dim, s.n_kv * s.head_dim, s.hidden, s.vocab, s.n_layer
+    weights = L * (d * qd + 2 * d * kvd + qd * d + 3 * d * F) * wsz + V * d * wsz + d * wsz
+    gains = (2 * L + 1) * d * 4
+    rope = s.head_dim * 4
+    kv = L * ctx * kvd * 2 * kvsz + L * kvd * 2 * kvsz
+    logits = V * 4
+    return weights + gains + rope + kv + logits
+
+
+def gate_up_bytes(s) -> int:
+    """Algorithmic bytes of one gate|up launch: both weight matrices, the input row, its gain, u written."""
+    wsz = 2 if s.w_dtype == "bf16" else 4
+    return 2 * s.d * s.hidden * wsz + 2 * s.d * 4 + s.hidden * 4
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "autoregressive_decode_step_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(per_launch_algorithmic: int):
+    """HBM bytes per gate|up launch from the committed counter runs, if they were taken on this source."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed greedy decode steps")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--profile-steps", type=int, default=4, help="steps timed kernel by kernel with HIP events")
+    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps in the CPU baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: the "
+              f"decode step here is single-GPU by design", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd import loader
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 3
+
+    s = synth.L8B
+    max_steps_per_call = s.max_seq - N_PRE
+    t_start = time.time()
+    log(f"generating {s.name} weights")
+    W = synth.model(s, seed=0)
+    prefix = synth.kv_prefix(s, N_PRE, seed=2)
+    first = int(synth.prompt(1, s.vocab, stream=7)[0])
+    log(f"generated in {time.time() - t_start:.1f} s; uploading")
+    cfg = loader.config_from(s)
+    model = loader.upload_model(cfg, W)
+    pool = loader.new_pool(cfg, 1, s.max_seq)
+    loader.fill_prefix(pool, 0, prefix)
+    dec = loader.Decoder(cfg, model, pool)
+    torch.cuda.synchronize()
+    log(f"resident in HBM after {time.time() - t_start:.1f} s")
+
+    def run(n: int, out) -> None:
+        done = 0
+        while done < n:
+            k = min(max_steps_per_call, n - done)
+            pool.slot_len[0] = N_PRE
+            st = dec.steps(first, N_PRE, k, out[done:done + k])
+            if st != llmk.OK:
+                raise RuntimeError(f"decode_steps: {st} {llmk.status_name(st)}")
+            done += k
+
+    # warm-up (not timed)
+    warm = torch.zeros(max(args.warmup, 1), dtype=torch.int32, device="cuda")
+    if args.warmup > 0:
+        run(args.warmup, warm)
+    torch.cuda.synchronize()
+
+    # timed region
+    toks = torch.zeros(args.steps, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps, toks)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    ctxs = [N_PRE + 1 + (i % max_steps_per_call) for i in range(args.steps)]
+    total_bytes = sum(step_bytes(s, c) for c in ctxs)
+    step_gbps = total_bytes / elapsed / 1e9
+    tokens = toks.cpu().numpy().tolist()
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {step_gbps:.0f} GB/s algorithmic")
+
+    # live per-kernel timing with HIP events (the same kernels, launched one by one on their stream)
+    names = ("qkv", "attention", "o", "gate_up", "down")
+    per = {n: [] for n in names + ("head",)}
+    pool.slot_len[0] = N_PRE
+    tok = first
+    for i in range(args.profile_steps):
+        st, ms = llmk.decode_step_profiled(cfg, model, pool, 0, tok, N_PRE + i, dec.token_out, dec.ws)
+        if st != llmk.OK:
+            raise RuntimeError(f"decode_step_profiled: {st}")
+        for l in range(s.n_layer):
+            for j, n in enumerate(names):
+                per[n].append(ms[5 * l + j])
+        per["head"].append(ms[-1])
+        tok = int(dec.token_out.cpu()[0])
+    avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    gu_bytes = gate_up_bytes(s)
+    gu_gbps = gu_bytes / (avg_ms["gate_up"] * 1e-3) / 1e9
+    kernel_sum_ms = sum(avg_ms[n] for n in names) * s.n_layer + avg_ms["head"]
+    log("avg kernel ms: " + ", ".join(f"{n} {v * 1e3:.1f} us" for n, v in avg_ms.items()))
+
+    result = {
+        "metric": "decode tokens/s at batch 1 (8B-shaped) + achieved HBM GB/s vs peak",
+        "value": args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama-3-8b-shaped greedy decode, batch 1, bf16 weights and K/V, context 4096",
+                   "vocab": s.vocab, "d": s.d, "n_layer": s.n_layer, "n_head": s.n_head, "n_kv": s.n_kv,
+                   "head_dim": s.head_dim, "hidden": s.hidden, "batch": 1, "context_start": N_PRE,
+                   "weights": "bf16", "kv": "bf16", "accumulation": "f32"},
+        "step_hbm_gbps": step_gbps,
+        "step_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "step_bytes_mean": total_bytes / args.steps,
+        "roofline": {"bound": "hbm", "kernel": "gate_up GEMV (gemv_t_kernel<bf16,8,GATEUP>)",
+                     "achieved": gu_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gu_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic_from_profiles(gu_bytes), "bytes_per_launch": gu_bytes,
+                     "avg_launch_us": avg_ms["gate_up"] * 1e3},
+        "kernels_avg_us": {n: v * 1e3 for n, v in avg_ms.items()},
+        "kernel_sum_ms_per_step": kernel_sum_ms,
+        "first_tokens": tokens[:8],
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        n = args.cpu_steps
+        log(f"oracle baseline: {n} steps on the host cores")
+        m = oracle.Model(s, W)
+        c = m.new_cache(N_PRE + n)
+        c.fill_prefix(prefix)
+        t = first
+        otoks = []
+        tc0 = time.perf_counter()
+        for i in range(n):
+            lg, _ = m.forward_token(t, N_PRE + i, c)
+            t = oracle.argmax(lg)[0]
+            otoks.append(t)
+        tc = time.perf_counter() - tc0
+        result["cpu_baseline"] = {"value": n / tc, "unit": "tokens/s", "cores": oracle.lib().orc_num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{n} greedy decode steps of the same workload at positions "
+                                            f"{N_PRE}..{N_PRE + n - 1} (fp64, OpenMP)",
+                                  "tokens_agree_with_gpu": otoks == tokens[:n]}
+        log(f"oracle: {tc / n:.2f} s/step, tokens {otoks} vs gpu {tokens[:n]}")
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+    log(f"total {time.time() - t_start:.1f} s")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -78,6 +78,11 @@ typedef enum { LLMK_F32 = 0, LLMK_BF16 = 1 } llmk_dtype;
  * gaps, not three"); interleaved pairs (2j, 2j+1) are the layout of [fwd] "The
  * code". [dops] "Method" supports both. */
 typedef enum { LLMK_ROPE_HALF_SPLIT = 0, LLMK_ROPE_INTERLEAVED = 1 } llmk_rope_layout;
+/* Storage of the seven per-layer projection matrices. LLMK_W_IN_OUT is the transposed-GEMV layout the
+ * llmk page's decode driver uses (A[in][out], y = A^T x); LLMK_W_OUT_IN stores the same matrix output-major
+ * (A^T, [out][in]), so every output is one contiguous row dot product. Both compute the same y; the
+ * second streams faster and is what llmk_transpose produces, once, at load time. */
+typedef enum { LLMK_W_IN_OUT = 0, LLMK_W_OUT_IN = 1 } llmk_weight_layout;
 
 /* ------------------------------------------------------------------------- */
 /* Contract: host-only, no device needed ([llmk] "Status vocabulary and the    */
@@ -218,6 +223,7 @@ typedef struct {
   int32_t rope_layout; /* llmk_rope_layout */
   int32_t w_dtype;     /* llmk_dtype of every weight matrix and the embedding table */
   int32_t kv_dtype;    /* llmk_dtype of the K/V pool */
+  int32_t w_layout;    /* llmk_weight_layout of the seven per-layer projections */
 } llmk_config;
 
 /* A device tensor and its element count. */
@@ -226,10 +232,11 @@ typedef struct {
   int64_t len;
 } llmk_tensor;
 
-/* Per-layer tensors, in this order, LLMK_LAYER_TENSORS per layer. Projections are in the transposed
- * layout A[in][out] (y = A^T x), as the llmk page's decode driver uses them:
+/* Per-layer tensors, in this order, LLMK_LAYER_TENSORS per layer. With LLMK_W_IN_OUT the projections are
+ * in the transposed layout A[in][out] (y = A^T x), as the llmk page's decode driver uses them:
  *   wq [d][H*hd]  wk [d][Hkv*hd]  wv [d][Hkv*hd]  wo [H*hd][d]
  *   w_gate [d][F]  w_up [d][F]  w_down [F][d]  (w_dtype)
+ * With LLMK_W_OUT_IN each of these seven is stored transposed ([out][in]); element counts are the same.
  *   g_attn [d]  g_ffn [d]  (fp32 RMSNorm gains) */
 enum { LLMK_WQ = 0, LLMK_WK, LLMK_WV, LLMK_WO, LLMK_WGATE, LLMK_WUP, LLMK_WDOWN, LLMK_GATTN, LLMK_GFFN,
        LLMK_LAYER_TENSORS };
@@ -289,6 +296,12 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
 int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                           int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
                           void* ws, int64_t len_ws, void* stream);
+
+/* dst = src^T for a rows x cols row-major matrix (dst is cols x rows), both device buffers of rows*cols
+ * elements of dtype; the one-time repacking of projections into LLMK_W_OUT_IN. dst may not alias src.
+ * Codes: 578 (null, dtype, aliasing), 561, 564, 562 (len_src), 577 (len_dst). */
+int32_t llmk_transpose(const void* src, int64_t len_src, void* dst, int64_t len_dst, int64_t rows, int64_t cols,
+                       int32_t dtype, void* stream);
 
 /* Measurement aid (not on the decode path): the number of kernels one decode step launches, in launch
  * order per layer q|k|v, attention, o, gate|up, down, then the output head (5 * n_layer + 1), or a

@@ -267,9 +267,9 @@ def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head):
 
 
 def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4, rope_layout=0,
-                 w_dtype=0, kv_dtype=0):
+                 w_dtype=0, kv_dtype=0, w_layout=0):
     import math
-    if rope_layout not in (0, 1) or w_dtype not in (0, 1) or kv_dtype not in (0, 1):
+    if rope_layout not in (0, 1) or w_dtype not in (0, 1) or kv_dtype not in (0, 1) or w_layout not in (0, 1):
         return INVALID
     if not (eps > 0 and math.isfinite(eps)) or not (rope_base > 1 and math.isfinite(rope_base)):
         return INVALID
@@ -284,6 +284,12 @@ def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps
             return HEAD_SHAPE
     if d > 64 * vec * 16:
         return HEAD_SHAPE
+    if w_layout == 1:
+        # output-major projections: an input row of K elements is split over at most 4 waves, each holding
+        # at most 8 vectors of 64 lanes x vec elements
+        for k in (d, n_head * head_dim, hidden):
+            if not any((k // kw) % vec == 0 and k % kw == 0 and -(-(k // kw) // (64 * vec)) <= 8 for kw in (1, 2, 4)):
+                return HEAD_SHAPE
     return OK
 
 

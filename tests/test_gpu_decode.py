@@ -82,8 +82,8 @@ def compare_runs(o, g, label):
     say(f"{label}: {len(toks_in)} steps, worst logits err {worst_l:.2e}, worst hidden err {worst_h:.2e}")
 
 
-def build(shape, W, n_slots=1, capacity=None):
-    cfg = loader.config_from(shape)
+def build(shape, W, n_slots=1, capacity=None, w_layout=llmk.W_OUT_IN):
+    cfg = loader.config_from(shape, w_layout)
     model = loader.upload_model(cfg, W)
     pool = loader.new_pool(cfg, n_slots, capacity or shape.max_seq)
     return cfg, model, pool, loader.Decoder(cfg, model, pool)
@@ -93,16 +93,17 @@ def build(shape, W, n_slots=1, capacity=None):
 # toy decoder (fp32 weights, the page's draws), both RoPE layouts
 # ---------------------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("w_layout", [llmk.W_IN_OUT, llmk.W_OUT_IN])
 @pytest.mark.parametrize("layout", [synth.ROPE_HALF_SPLIT, synth.ROPE_INTERLEAVED])
-def test_tiny_decode_matches_oracle(layout):
+def test_tiny_decode_matches_oracle(layout, w_layout):
     g = golden("page_decode.json")
     s = synth.TINY.with_(rope_layout=layout)
     W = synth.as_f32(synth.page_draws(s, seed=g["config"]["seed"], std=g["config"]["weight_std"]))
     m = oracle.Model(s, W)
     o = oracle_run(m, s, g["prompt"], n_greedy=g["n_new"])
-    cfg, model, pool, dec = build(s, W, n_slots=2)
+    cfg, model, pool, dec = build(s, W, n_slots=2, w_layout=w_layout)
     gr = gpu_teacher_forced(dec, s, o[0], 0)
-    compare_runs(o, gr, f"tiny layout={layout}")
+    compare_runs(o, gr, f"tiny rope={layout} weights={w_layout}")
     oracle_tokens = o[3][len(g["prompt"]) - 1:len(g["prompt"]) - 1 + g["n_new"]]
     if layout == synth.ROPE_INTERLEAVED:
         assert gr[0][len(g["prompt"]) - 1:][:3] == g["printed_first_tokens"]   # the page's printed tokens
@@ -218,13 +219,14 @@ def q06():
     return s, W
 
 
-def test_q06_short_prefix_matches_oracle(q06):
+@pytest.mark.parametrize("w_layout", [llmk.W_IN_OUT, llmk.W_OUT_IN])
+def test_q06_short_prefix_matches_oracle(q06, w_layout):
     s, W = q06
     m = oracle.Model(s, W)
     prompt = synth.prompt(8, s.vocab).tolist()
     o = oracle_run(m, s, prompt, n_greedy=3, max_seq=64)
-    cfg, model, pool, dec = build(s, W, capacity=s.max_seq)
-    compare_runs(o, gpu_teacher_forced(dec, s, o[0], 0), "q06 8-token prefix")
+    cfg, model, pool, dec = build(s, W, capacity=s.max_seq, w_layout=w_layout)
+    compare_runs(o, gpu_teacher_forced(dec, s, o[0], 0), f"q06 8-token prefix weights={w_layout}")
 
 
 def test_q06_full_context_matches_oracle(q06):

@@ -308,3 +308,18 @@ def test_argmax_signed_zero_nan_and_rows():
     rows[3, :] = -np.inf
     tok, _ = run_argmax(rows, 4, 1000)
     assert tok.tolist() == [oracle.argmax(r)[0] for r in rows] == [10, 10, 5, 0]
+
+
+# ---------------------------------------------------------------------------------------------
+# transpose (the one-time repacking into output-major weights)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,dt", [(1, 1, "f32"), (3, 5, "f32"), (65, 130, "bf16"), (4096, 14336, "bf16"),
+                                          (1000, 24, "f32")])
+def test_transpose_bit_exact(rows, cols, dt):
+    a = synth.normal((rows, cols), 40, rows + cols, 1.0, dt)
+    src = dev(a)
+    dst = torch.empty_like(src)
+    assert llmk.transpose(src, dst, rows, cols) == llmk.OK
+    _sync()
+    assert np.array_equal(host(dst).reshape(cols, rows), a.T)

@@ -288,12 +288,17 @@ def test_rope_frequency_schedule():
         assert abs(math.remainder(angle - expect, 2 * math.pi)) < 1e-12
 
 
-def test_rope_table_matches_angles():
-    t = oracle.rope_table_f32(50, 8, 1e4).reshape(50, 4, 2)
-    for p in (0, 1, 49):
-        for j in range(4):
-            th = p * 1e4 ** (-2 * j / 8)
-            assert t[p, j, 0] == np.float32(math.cos(th)) and t[p, j, 1] == np.float32(math.sin(th))
+def test_rope_table_is_the_rotation_of_unit_vectors():
+    # rotating the unit vector of pair j's first element gives (cos, sin) of that pair's angle,
+    # so the table must hold exactly what the (separately pinned) rotation does, rounded to fp32
+    hd, base = 8, 1e4
+    t = oracle.rope_table_f32(50, hd, base).reshape(50, hd // 2, 2)
+    for p in (0, 1, 17, 49):
+        for j in range(hd // 2):
+            e = np.zeros(hd)
+            e[j] = 1.0
+            r = oracle.rope(e, 1, hd, p, base, oracle.HALF_SPLIT)
+            assert t[p, j, 0] == np.float32(r[j]) and t[p, j, 1] == np.float32(r[j + hd // 2])
 
 
 # ---------------------------------------------------------------------------------------------
