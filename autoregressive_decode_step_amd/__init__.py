@@ -93,6 +93,8 @@ _SIGS = {
     "llmk_transpose": ([_p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
     "llmk_decode_step_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                    _i64, _i64, _i64, _p, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
+    "llmk_decode_kernel_time": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
+                                 _i64, _i64, _i64, _i32, _i32, _p, ctypes.POINTER(_f32), _p, _i64, _p], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -332,3 +334,16 @@ def decode_step_profiled(cfg: Config, model: Model, pool: KVPool, slot, token, p
     st = lib.llmk_decode_step_profiled(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot,
                                        token, pos, _ptr(token_out), ms, n, _ptr(ws), _len(ws), _stream(stream))
     return st, [ms[i] for i in range(n)]
+
+
+KERNEL_CLASSES = ("qkv", "attention", "o", "gate_up", "down", "head")
+
+
+def decode_kernel_time(cfg: Config, model: Model, pool: KVPool, slot, token, pos, kernel, reps, token_out, ws,
+                       stream=None):
+    """Returns (status, milliseconds per launch) of kernel class `kernel` (an index into KERNEL_CLASSES)."""
+    ms = _f32(0.0)
+    st = lib.llmk_decode_kernel_time(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot,
+                                     token, pos, kernel, reps, _ptr(token_out), ctypes.byref(ms), _ptr(ws), _len(ws),
+                                     _stream(stream))
+    return st, ms.value

@@ -133,11 +133,13 @@ struct DecodePlan {
   float* attn_part = nullptr;
   float* head_val = nullptr;
   int32_t* head_idx = nullptr;
+  int32_t* tok_scratch = nullptr;   // kTimeMaxReps tokens: where repeated timing launches of the head write
   int64_t bytes = 0;
   int n_gemv_counters = 0;
 };
 
 constexpr int kGemvTargetBlocks = 512;
+constexpr int kTimeMaxReps = 64;   // llmk_decode_kernel_time: at most this many replays of a kernel class
 
 
 void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
@@ -193,6 +195,7 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.attn_part = cv.take<float>((int64_t)D.attn.n_parts * c->n_head * (c->head_dim + 2));
   D.head_val = cv.take<float>(D.head.n_blocks);
   D.head_idx = cv.take<int32_t>(D.head.n_blocks);
+  D.tok_scratch = cv.take<int32_t>(kTimeMaxReps);
   D.bytes = cv.off;
 }
 
@@ -238,58 +241,40 @@ int32_t pool_check(const llmk_config* c, const llmk_kv_pool* p) {
   return st;
 }
 
-// Enqueue one decode step's kernels. Token and position are read from D.state on the device.
-hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, int64_t slot,
-                        DecodePlan& D, float* logits, int32_t* token_out, float* hidden, hipStream_t s,
-                        hipEvent_t* ev = nullptr) {
+// The kernels of one decode step, in order: per layer K_QKV, K_ATTN, K_O, K_GATEUP, K_DOWN, then K_HEAD.
+enum StepKernel { K_QKV = 0, K_ATTN = 1, K_O = 2, K_GATEUP = 3, K_DOWN = 4, K_HEAD = 5, K_CLASSES = 6 };
+
+// Launch kernel `which` of layer l (K_HEAD: the tail, l ignored). Token and position are read from D.state.
+hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, int64_t slot,
+                         DecodePlan& D, int64_t l, int which, float* logits, int32_t* token_out, float* hidden,
+                         hipStream_t s) {
   const int bf = c->w_dtype == LLMK_BF16;
   const int64_t d = c->d, kvd = c->n_kv * c->head_dim;
-  const int64_t plane = pool->capacity * kvd;
-  const int64_t kv_off = slot * plane;
+  const int64_t kv_off = slot * pool->capacity * kvd;
   const int64_t kvsz = dtype_size(c->kv_dtype);
   unsigned* gcnt = D.counters;
   unsigned* acnt = D.counters + D.n_gemv_counters;
   unsigned* hcnt = acnt + c->n_kv;
-  hipError_t e = hipSuccess;
-  int kidx = 0;
-  // optional timing: event 2k before and 2k+1 after kernel k, on the kernels' own stream
-  auto mark = [&](int which) -> hipError_t { return ev ? hipEventRecord(ev[2 * kidx + which], s) : hipSuccess; };
-  auto timed = [&](hipError_t launched) -> hipError_t {
-    if (launched != hipSuccess) return launched;
-    hipError_t r = mark(1);
-    ++kidx;
-    return r;
-  };
-  for (int64_t l = 0; l < c->n_layer; ++l) {
-    const float* g_attn = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
-    const float* g_ffn = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
-    // 1. h = rmsnorm(x) g_attn;  q|k|v = h W  (raw; layer 0 reads x = emb[token])
-    if (D.rowdot) {
-      RowdotParams r = D.rqkv;
-      r.w0 = layer_t(m, l, LLMK_WQ).ptr;
-      r.w1 = layer_t(m, l, LLMK_WK).ptr;
-      r.w2 = layer_t(m, l, LLMK_WV).ptr;
-      if (l == 0) { r.in = m->emb.ptr; r.in_is_w = 1; r.in_state = D.state; }
-      else { r.in = D.x; r.in_is_w = 0; r.in_state = nullptr; }
-      r.gain = g_attn;
-      r.eps = (float)c->eps;
-      r.y = D.qkv_buf;
-      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(r, GM_QKV, bf, s))) != hipSuccess) return e;
-    } else {
-      GemvParams g = D.qkv;
-      g.w0 = layer_t(m, l, LLMK_WQ).ptr;
-      g.w1 = layer_t(m, l, LLMK_WK).ptr;
-      g.w2 = layer_t(m, l, LLMK_WV).ptr;
-      if (l == 0) { g.in = m->emb.ptr; g.in_is_w = 1; g.in_state = D.state; }
-      else { g.in = D.x; g.in_is_w = 0; g.in_state = nullptr; }
-      g.gain = g_attn;
-      g.eps = (float)c->eps;
-      g.partial = D.partial;
-      g.counters = gcnt;
-      g.y = D.qkv_buf;
-      if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(g, GM_QKV, bf, 0, s))) != hipSuccess) return e;
-    }
-    // 2. RoPE on q and k, append k, v at pos, attention over positions 0..pos of this slot
+  if (which == K_HEAD) {
+    // logits = W_out rmsnorm(x) g_final; greedy token; state advances
+    HeadParams h = D.head;
+    h.w = m->w_out.ptr;
+    h.x = D.x;
+    h.gain = static_cast<const float*>(m->g_final.ptr);
+    h.eps = (float)c->eps;
+    h.y = logits ? logits : D.logits;
+    h.part_val = D.head_val;
+    h.part_idx = D.head_idx;
+    h.counter = hcnt;
+    h.token_out = token_out;
+    h.logit_out = nullptr;
+    h.state = D.state;
+    return head_launch(h, bf, s);
+  }
+  const float* g_attn = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
+  const float* g_ffn = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
+  if (which == K_ATTN) {
+    // RoPE on q and k, append k, v at pos, attention over positions 0..pos of this slot
     AttnParams a = D.attn;
     a.q = nullptr;
     a.qkv_raw = D.qkv_buf;
@@ -304,86 +289,131 @@ hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv
     a.part = D.attn_part;
     a.counters = acnt;
     a.out = D.att;
-    if ((e = mark(0)) != hipSuccess || (e = timed(attn_launch(a, s))) != hipSuccess) return e;
-    // 3. x = x + att Wo   (layer 0: x = emb[token] + att Wo)
-    // 4. h = rmsnorm(x) g_ffn;  u = silu(h Wgate) * (h Wup)
-    // 5. x = x + u Wdown
-    if (D.rowdot) {
-      RowdotParams o = D.ro;
+    return attn_launch(a, s);
+  }
+  if (D.rowdot) {
+    switch (which) {
+      case K_QKV: {   // h = rmsnorm(x) g_attn;  q|k|v = h W  (raw; layer 0 reads x = emb[token])
+        RowdotParams r = D.rqkv;
+        r.w0 = layer_t(m, l, LLMK_WQ).ptr;
+        r.w1 = layer_t(m, l, LLMK_WK).ptr;
+        r.w2 = layer_t(m, l, LLMK_WV).ptr;
+        if (l == 0) { r.in = m->emb.ptr; r.in_is_w = 1; r.in_state = D.state; }
+        else { r.in = D.x; r.in_is_w = 0; r.in_state = nullptr; }
+        r.gain = g_attn;
+        r.eps = (float)c->eps;
+        r.y = D.qkv_buf;
+        return rowdot_launch(r, GM_QKV, bf, s);
+      }
+      case K_O: {     // x = x + att Wo   (layer 0: x = emb[token] + att Wo)
+        RowdotParams o = D.ro;
+        o.w0 = layer_t(m, l, LLMK_WO).ptr;
+        o.in = D.att;
+        o.x = D.x;
+        if (l == 0) { o.base = m->emb.ptr; o.base_is_w = 1; o.base_state = D.state; }
+        else { o.base = D.x; o.base_is_w = 0; o.base_state = nullptr; }
+        return rowdot_launch(o, GM_RESID, bf, s);
+      }
+      case K_GATEUP: {   // h = rmsnorm(x) g_ffn;  u = silu(h Wgate) * (h Wup)
+        RowdotParams gu = D.rgu;
+        gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
+        gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
+        gu.in = D.x;
+        gu.gain = g_ffn;
+        gu.eps = (float)c->eps;
+        gu.y = D.u;
+        return rowdot_launch(gu, GM_GATEUP, bf, s);
+      }
+      case K_DOWN: {  // x = x + u Wdown
+        RowdotParams dn = D.rdown;
+        dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
+        dn.in = D.u;
+        dn.x = D.x;
+        dn.base = D.x;
+        dn.hidden = hidden ? hidden + l * d : nullptr;
+        return rowdot_launch(dn, GM_RESID, bf, s);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (which) {
+    case K_QKV: {
+      GemvParams g = D.qkv;
+      g.w0 = layer_t(m, l, LLMK_WQ).ptr;
+      g.w1 = layer_t(m, l, LLMK_WK).ptr;
+      g.w2 = layer_t(m, l, LLMK_WV).ptr;
+      if (l == 0) { g.in = m->emb.ptr; g.in_is_w = 1; g.in_state = D.state; }
+      else { g.in = D.x; g.in_is_w = 0; g.in_state = nullptr; }
+      g.gain = g_attn;
+      g.eps = (float)c->eps;
+      g.partial = D.partial;
+      g.counters = gcnt;
+      g.y = D.qkv_buf;
+      return gemv_launch(g, GM_QKV, bf, 0, s);
+    }
+    case K_O: {
+      GemvParams o = D.o;
       o.w0 = layer_t(m, l, LLMK_WO).ptr;
       o.in = D.att;
+      o.in_is_w = 0;
+      o.gain = nullptr;
+      o.partial = D.partial;
+      o.counters = gcnt;
       o.x = D.x;
       if (l == 0) { o.base = m->emb.ptr; o.base_is_w = 1; o.base_state = D.state; }
       else { o.base = D.x; o.base_is_w = 0; o.base_state = nullptr; }
-      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(o, GM_RESID, bf, s))) != hipSuccess) return e;
-      RowdotParams gu = D.rgu;
+      o.hidden = nullptr;
+      return gemv_launch(o, GM_RESID, bf, 0, s);
+    }
+    case K_GATEUP: {
+      GemvParams gu = D.gu;
       gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
       gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
       gu.in = D.x;
+      gu.in_is_w = 0;
       gu.gain = g_ffn;
       gu.eps = (float)c->eps;
+      gu.partial = D.partial;
+      gu.counters = gcnt;
       gu.y = D.u;
-      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(gu, GM_GATEUP, bf, s))) != hipSuccess) return e;
-      RowdotParams dn = D.rdown;
+      return gemv_launch(gu, GM_GATEUP, bf, 0, s);
+    }
+    case K_DOWN: {
+      GemvParams dn = D.down;
       dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
       dn.in = D.u;
+      dn.in_is_w = 0;
+      dn.gain = nullptr;
+      dn.partial = D.partial;
+      dn.counters = gcnt;
       dn.x = D.x;
       dn.base = D.x;
+      dn.base_is_w = 0;
       dn.hidden = hidden ? hidden + l * d : nullptr;
-      if ((e = mark(0)) != hipSuccess || (e = timed(rowdot_launch(dn, GM_RESID, bf, s))) != hipSuccess) return e;
-      continue;
+      return gemv_launch(dn, GM_RESID, bf, 0, s);
     }
-    GemvParams o = D.o;
-    o.w0 = layer_t(m, l, LLMK_WO).ptr;
-    o.in = D.att;
-    o.in_is_w = 0;
-    o.gain = nullptr;
-    o.partial = D.partial;
-    o.counters = gcnt;
-    o.x = D.x;
-    if (l == 0) { o.base = m->emb.ptr; o.base_is_w = 1; o.base_state = D.state; }
-    else { o.base = D.x; o.base_is_w = 0; o.base_state = nullptr; }
-    o.hidden = nullptr;
-    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(o, GM_RESID, bf, 0, s))) != hipSuccess) return e;
-    GemvParams gu = D.gu;
-    gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
-    gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
-    gu.in = D.x;
-    gu.in_is_w = 0;
-    gu.gain = g_ffn;
-    gu.eps = (float)c->eps;
-    gu.partial = D.partial;
-    gu.counters = gcnt;
-    gu.y = D.u;
-    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(gu, GM_GATEUP, bf, 0, s))) != hipSuccess) return e;
-    GemvParams dn = D.down;
-    dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
-    dn.in = D.u;
-    dn.in_is_w = 0;
-    dn.gain = nullptr;
-    dn.partial = D.partial;
-    dn.counters = gcnt;
-    dn.x = D.x;
-    dn.base = D.x;
-    dn.base_is_w = 0;
-    dn.hidden = hidden ? hidden + l * d : nullptr;
-    if ((e = mark(0)) != hipSuccess || (e = timed(gemv_launch(dn, GM_RESID, bf, 0, s))) != hipSuccess) return e;
   }
-  // tail: logits = W_out rmsnorm(x) g_final; greedy token; state advances
-  HeadParams h = D.head;
-  h.w = m->w_out.ptr;
-  h.x = D.x;
-  h.gain = static_cast<const float*>(m->g_final.ptr);
-  h.eps = (float)c->eps;
-  h.y = logits ? logits : D.logits;
-  h.part_val = D.head_val;
-  h.part_idx = D.head_idx;
-  h.counter = hcnt;
-  h.token_out = token_out;
-  h.logit_out = nullptr;
-  h.state = D.state;
-  if ((e = mark(0)) != hipSuccess) return e;
-  return timed(head_launch(h, bf, s));
+  return hipErrorInvalidValue;
+}
+
+// Enqueue one decode step's kernels. With ev, event 2k is recorded before and 2k+1 after kernel k, on the
+// kernels' own stream.
+hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, int64_t slot,
+                        DecodePlan& D, float* logits, int32_t* token_out, float* hidden, hipStream_t s,
+                        hipEvent_t* ev = nullptr) {
+  int kidx = 0;
+  auto one = [&](int64_t l, int which) -> hipError_t {
+    hipError_t e = ev ? hipEventRecord(ev[2 * kidx], s) : hipSuccess;
+    if (e == hipSuccess) e = launch_kernel(c, m, pool, slot, D, l, which, logits, token_out, hidden, s);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2 * kidx + 1], s);
+    ++kidx;
+    return e;
+  };
+  hipError_t e = hipSuccess;
+  for (int64_t l = 0; l < c->n_layer && e == hipSuccess; ++l)
+    for (int k = K_QKV; k <= K_DOWN && e == hipSuccess; ++k) e = one(l, k);
+  if (e == hipSuccess) e = one(0, K_HEAD);
+  return e;
 }
 
 // Common checks of decode_step / decode_steps, in the documented order.
@@ -778,6 +808,70 @@ int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* mode
   delete[] ev;
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos + 1;
+  return LLMK_OK;
+}
+
+int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                int64_t token, int64_t pos, int32_t kernel, int32_t reps, int32_t* token_out,
+                                float* ms_per_launch_h, void* ws, int64_t len_ws, void* stream) {
+  if (!ms_per_launch_h) return LLMK_INVALID_ARGUMENT;
+  int32_t st = decode_checks(cfg, model, pool, slot, token, pos, 1, token_out, ws);
+  if (st != LLMK_OK) return st;
+  if (kernel < 0 || kernel >= K_CLASSES) return LLMK_INVALID_ARGUMENT;
+  if (reps < 1) return LLMK_EMPTY_DIMENSION;
+  if (reps > kTimeMaxReps) return LLMK_DIMENSION_TOO_LARGE;
+  DecodePlan D;
+  plan_decode(cfg, nullptr, D);
+  if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
+  plan_decode(cfg, ws, D);
+  hipStream_t s = as_stream(stream);
+  // one ordinary step leaves valid activations in the workspace; the state is then reset to (token, pos)
+  // so that repeated attention launches stay at pos
+  hipError_t e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
+  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
+  if (e == hipSuccess) e = enqueue_step(cfg, model, pool, slot, D, nullptr, token_out, nullptr, s);
+  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+
+  // the class's launches (every layer, reps times) captured back to back into one graph, replayed once
+  // between two events on the caller's stream
+  const int64_t per_rep = kernel == K_HEAD ? 1 : cfg->n_layer;
+  hipStream_t cs = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t ee = hipSuccess;
+    for (int32_t r = 0; r < reps && ee == hipSuccess; ++r)
+      for (int64_t l = 0; l < per_rep && ee == hipSuccess; ++l)
+        ee = launch_kernel(cfg, model, pool, slot, D, l, kernel, nullptr, D.tok_scratch, nullptr, cs);
+    e = hipStreamEndCapture(cs, &graph);
+    if (ee != hipSuccess) e = ee;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  if (e == hipSuccess) e = hipGraphLaunch(exec, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  // the repeated launches scrambled the workspace and (attention) the K/V at pos of every layer: one more
+  // ordinary step puts back exactly what llmk_decode_step leaves
+  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
+  if (e == hipSuccess) e = enqueue_step(cfg, model, pool, slot, D, nullptr, token_out, nullptr, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (cs) (void)hipStreamDestroy(cs);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  pool->slot_len_h[slot] = pos + 1;
+  *ms_per_launch_h = ms / (float)(reps * per_rep);
   return LLMK_OK;
 }
 

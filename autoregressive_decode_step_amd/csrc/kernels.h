@@ -135,7 +135,7 @@ struct AttnParams {
   int32_t rope_layout;
 };
 
-constexpr int ATTN_MAX_PARTS = 16;
+constexpr int ATTN_MAX_PARTS = 32;
 // Fills chunk / sub_per_wg / n_parts for contexts up to max_ctx.
 void attn_plan(AttnParams& p, int64_t max_ctx);
 hipError_t attn_launch(const AttnParams& p, hipStream_t s);

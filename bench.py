@@ -8,7 +8,7 @@ embedding, 32 layers of norm + q|k|v + RoPE + K/V append + attention + o + norm 
 down, final norm, output head and argmax. Inputs are resident in HBM before the timed region.
 
 Prints one JSON line: tokens/s, ms per step, algorithmic HBM GB/s of the whole step, the roofline of
-the dominant kernel (the gate|up GEMV, timed live with HIP events on its own stream), and the oracle's
+the dominant kernel (the gate|up GEMV, timed with HIP events on the stream it runs on), and the oracle's
 throughput on the host cores for a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 N_PRE = 4096                    # filled context before the first timed step
-PMC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemv_llama8b_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "rowdot_gate_up_llama8b_pmc.md")
 
 
 def log(msg: str) -> None:
@@ -55,22 +55,45 @@ def gate_up_bytes(s) -> int:
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("gemv.hip", "common.h", "kernels.h"):
+    for f in ("rowdot.hip", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "autoregressive_decode_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(per_launch_algorithmic: int):
-    """HBM bytes per gate|up launch from the committed counter runs, if they were taken on this source."""
+def traffic_from_profiles():
+    """HBM bytes per gate|up launch from the committed counter summary ("key: value" lines), if its counters
+    were taken on the current kernel source; None otherwise."""
+    rec = {}
     try:
         with open(PMC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                k, sep, v = line.partition(":")
+                if sep:
+                    rec[k.strip()] = v.strip()
+    except OSError:
         return None
     if rec.get("source_sha") != kernel_source_sha():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib: int) -> int:
+    """A plain device-to-device copy of `mib` MiB, run 4 times: reads and writes that many bytes per launch.
+    Run under the same counters as the decode step, it gives the scale between what FETCH_SIZE / WRITE_SIZE
+    report and bytes actually moved."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": n * 4, "launches": 4}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -78,9 +101,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256, help="timed greedy decode steps")
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--profile-steps", type=int, default=4, help="steps timed kernel by kernel with HIP events")
-    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps in the CPU baseline sample")
+    ap.add_argument("--kernel-reps", type=int, default=4,
+                    help="times each kernel class's per-layer launches are replayed for its HIP-event timing")
+    ap.add_argument("--cpu-steps", type=int, default=20, help="oracle steps in the CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -89,7 +115,6 @@ def main() -> int:
               f"decode step here is single-GPU by design", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import synth
@@ -99,6 +124,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 3
+    if args.copy_probe > 0:
+        return copy_probe(args.copy_probe)
 
     s = synth.L8B
     max_steps_per_call = s.max_seq - N_PRE
@@ -147,25 +174,20 @@ def main() -> int:
     tokens = toks.cpu().numpy().tolist()
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {step_gbps:.0f} GB/s algorithmic")
 
-    # live per-kernel timing with HIP events (the same kernels, launched one by one on their stream)
-    names = ("qkv", "attention", "o", "gate_up", "down")
-    per = {n: [] for n in names + ("head",)}
+    # per-kernel timing with HIP events on the stream the kernels run on: each class's launches (every layer,
+    # several times over) replayed back to back in one graph, as the step graph runs them
     pool.slot_len[0] = N_PRE
-    tok = first
-    for i in range(args.profile_steps):
-        st, ms = llmk.decode_step_profiled(cfg, model, pool, 0, tok, N_PRE + i, dec.token_out, dec.ws)
+    avg_ms = {}
+    for k, n in enumerate(llmk.KERNEL_CLASSES):
+        st, ms = llmk.decode_kernel_time(cfg, model, pool, 0, first, N_PRE, k, args.kernel_reps, dec.token_out, dec.ws)
         if st != llmk.OK:
-            raise RuntimeError(f"decode_step_profiled: {st}")
-        for l in range(s.n_layer):
-            for j, n in enumerate(names):
-                per[n].append(ms[5 * l + j])
-        per["head"].append(ms[-1])
-        tok = int(dec.token_out.cpu()[0])
-    avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
+            raise RuntimeError(f"decode_kernel_time({n}): {st} {llmk.status_name(st)}")
+        avg_ms[n] = ms
+        pool.slot_len[0] = N_PRE
     gu_bytes = gate_up_bytes(s)
     gu_gbps = gu_bytes / (avg_ms["gate_up"] * 1e-3) / 1e9
-    kernel_sum_ms = sum(avg_ms[n] for n in names) * s.n_layer + avg_ms["head"]
-    log("avg kernel ms: " + ", ".join(f"{n} {v * 1e3:.1f} us" for n, v in avg_ms.items()))
+    kernel_sum_ms = sum(avg_ms[n] for n in llmk.KERNEL_CLASSES[:5]) * s.n_layer + avg_ms["head"]
+    log("avg kernel us: " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in avg_ms.items()))
 
     result = {
         "metric": "decode tokens/s at batch 1 (8B-shaped) + achieved HBM GB/s vs peak",
@@ -187,9 +209,9 @@ def main() -> int:
         "step_hbm_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "step_bytes_mean": total_bytes / args.steps,
-        "roofline": {"bound": "hbm", "kernel": "gate_up GEMV (gemv_t_kernel<bf16,8,GATEUP>)",
+        "roofline": {"bound": "hbm", "kernel": "gate|up row-dot GEMV (rowdot_kernel, GATEUP epilogue)",
                      "achieved": gu_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gu_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic_from_profiles(gu_bytes), "bytes_per_launch": gu_bytes,
+                     "traffic": traffic_from_profiles(), "bytes_per_launch": gu_bytes,
                      "avg_launch_us": avg_ms["gate_up"] * 1e3},
         "kernels_avg_us": {n: v * 1e3 for n, v in avg_ms.items()},
         "kernel_sum_ms_per_step": kernel_sum_ms,

@@ -317,6 +317,21 @@ int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* mode
                                   int64_t token, int64_t pos, int32_t* token_out, float* kernel_ms_h,
                                   int64_t len_kernel_ms, void* ws, int64_t len_ws, void* stream);
 
+/* Measurement aid (not on the decode path): the average duration of one launch of one of the step's
+ * kernel classes, timed the way the step runs it. kernel: 0 q|k|v, 1 attention, 2 o, 3 gate|up, 4 down,
+ * 5 output head. Runs one ordinary decode step at (token, pos), captures that class's launches for every
+ * layer (the head: once), `reps` times over, back to back into one HIP graph, replays it once between two
+ * HIP events recorded on `stream`, then runs the ordinary step at (token, pos) once more. The repeated
+ * launches work on the workspace only (the head's tokens go to workspace scratch, never to token_out), and
+ * the final step rewrites what they disturbed, so the call leaves the pool, token_out (the greedy token)
+ * and slot_len_h[slot] = pos + 1 exactly as llmk_decode_step does. *ms_per_launch_h (host) receives the
+ * elapsed time divided by the number of launches. Synchronizes `stream`.
+ * Codes: as llmk_decode_step; 578 if ms_per_launch_h is NULL or kernel is not 0..5; 561 if reps < 1; 564
+ * if reps > 64. */
+int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                int64_t token, int64_t pos, int32_t kernel, int32_t reps, int32_t* token_out,
+                                float* ms_per_launch_h, void* ws, int64_t len_ws, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -207,6 +207,38 @@ def test_decode_steps_equal_decode_step_loop_and_deterministic():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and np.array_equal(b.view(np.uint32), c.view(np.uint32))
 
 
+def test_kernel_time_leaves_the_step_state_of_decode_step():
+    """The timing aid runs one ordinary step first: the slot's K/V at pos and every earlier position are
+    those decode_step leaves, and decoding on from pos + 1 gives decode_step's tokens."""
+    s = synth.TINY
+    W = synth.as_f32(synth.page_draws(s))
+    cfg, model, pool, dec = build(s, W, n_slots=2)
+    for slot in (0, 1):
+        tok = 3
+        for pos in range(5):
+            assert dec.step(tok, pos, slot) == llmk.OK
+            torch.cuda.synchronize()
+            tok = int(host(dec.token_out)[0])
+    ref = []
+    assert dec.step(tok, 5, 0) == llmk.OK
+    torch.cuda.synchronize()
+    nxt = int(host(dec.token_out)[0])
+    for k, name in enumerate(llmk.KERNEL_CLASSES):
+        pool.slot_len[1] = 5
+        st, ms = llmk.decode_kernel_time(cfg, model, pool, 1, tok, 5, k, 2, dec.token_out, dec.ws)
+        say(f"{name}: {ms * 1e3:.2f} us per launch")
+        assert st == llmk.OK and ms > 0.0 and pool.slot_len[1] == 6
+    for l in range(s.n_layer):
+        for kv in ("k", "v"):
+            a, b = host(pool.slot_view(l, 0, kv))[:6], host(pool.slot_view(l, 1, kv))[:6]
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for slot in (0, 1):
+        assert dec.step(nxt, 6, slot) == llmk.OK
+        torch.cuda.synchronize()
+        ref.append(int(host(dec.token_out)[0]))
+    assert ref[0] == ref[1]
+
+
 # ---------------------------------------------------------------------------------------------
 # Qwen3-0.6B-shaped (bf16 weights, fp32 K/V)
 # ---------------------------------------------------------------------------------------------

@@ -262,3 +262,18 @@ def test_decode_step_refusals():
     assert call(bad) == contract.decode_step(kw, lens_ok=False) == 576
     nul, _c = model(null=True)
     assert call(nul) == contract.decode_step(kw, tensors_ok=False) == 578
+
+    # the kernel-timing aid refuses exactly as the step does, then checks its own arguments
+    def kt(kernel=3, reps=4, ms=True, token=0):
+        ks = (ctypes.c_void_p * L)(FA, FA)
+        sl = np.zeros(2, np.int64)
+        ps = llmk.PoolStruct(ks, ks, L, 2, 32, 2, 4, 0, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        out = ctypes.c_float(0.0)
+        return llmk.lib.llmk_decode_kernel_time(ctypes.byref(cfg), ctypes.byref(good), ctypes.byref(ps), 0, token, 0,
+                                                kernel, reps, FA, ctypes.byref(out) if ms else None, FA, ws_need,
+                                                None)
+    assert kt(token=40) == contract.decode_step(kw, token=40) == 572
+    assert kt(ms=False) == 578
+    assert kt(kernel=6) == 578 and kt(kernel=-1) == 578
+    assert kt(reps=0) == 561
+    assert kt(reps=65) == 564
