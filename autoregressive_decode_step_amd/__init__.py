@@ -93,6 +93,10 @@ _SIGS = {
     "llmk_transpose": ([_p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
     "llmk_decode_step_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                    _i64, _i64, _i64, _p, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
+    "llmk_decode_step_batch": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64,
+                                _p, _p, _p, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_decode_steps_batch": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64,
+                                 _p, _p, _p, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_decode_kernel_time": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                  _i64, _i64, _i64, _i32, _i32, _p, ctypes.POINTER(_f32), _p, _i64, _p], _i32),
 }
@@ -321,6 +325,35 @@ def decode_steps(cfg: Config, model: Model, pool: KVPool, slot, token0, pos0, n_
     return lib.llmk_decode_steps(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot,
                                  token0, pos0, n_steps, _ptr(tokens_out), _len(tokens_out), _ptr(ws), _len(ws),
                                  _stream(stream))
+
+
+def _host_i64(v):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.int64).reshape(-1))
+    return a, a.ctypes.data
+
+
+def decode_step_batch(cfg: Config, model: Model, pool: KVPool, slots, tokens, pos, tokens_out, ws, logits=None,
+                      hidden=None, stream=None) -> int:
+    """One batched step: row r is slot slots[r] consuming tokens[r] at pos[r] (host sequences)."""
+    sl, psl = _host_i64(slots)
+    tk, ptk = _host_i64(tokens)
+    ps, pps = _host_i64(pos)
+    return lib.llmk_decode_step_batch(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct),
+                                      len(sl), psl, ptk, pps, _ptr(logits), _len(logits), _ptr(tokens_out),
+                                      _len(tokens_out), _ptr(hidden), _len(hidden), _ptr(ws), _len(ws),
+                                      _stream(stream))
+
+
+def decode_steps_batch(cfg: Config, model: Model, pool: KVPool, slots, tokens0, pos0, n_steps, tokens_out, ws,
+                       stream=None) -> int:
+    """n_steps batched greedy steps; tokens_out is device int32 [n_steps][batch]."""
+    sl, psl = _host_i64(slots)
+    tk, ptk = _host_i64(tokens0)
+    ps, pps = _host_i64(pos0)
+    return lib.llmk_decode_steps_batch(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct),
+                                       len(sl), psl, ptk, pps, n_steps, _ptr(tokens_out), _len(tokens_out), _ptr(ws),
+                                       _len(ws), _stream(stream))
 
 
 def decode_kernel_count(cfg: Config) -> int:

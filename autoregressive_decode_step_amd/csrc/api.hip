@@ -1,6 +1,7 @@
 // C ABI of libllmk: host-side checks (all before any HIP call), workspace layout and the assembly of
 // the decode step from the gfx950 kernels. See include/llmk.h for the contract of every entry point.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include <hip/hip_runtime.h>
@@ -434,6 +435,210 @@ int32_t decode_checks(const llmk_config* cfg, const llmk_model* model, const llm
   return LLMK_OK;
 }
 
+// ---- batched decode ------------------------------------------------------------------------------------
+
+constexpr int kBatchTargetBlocks = 256;   // the matrix-core kernels hold one workgroup per CU
+
+struct BatchPlan {
+  int64_t B = 0;
+  BgemmParams qkv{}, o{}, gu{}, down{}, head{};
+  AttnParams attn{};
+  BatchState* state = nullptr;
+  float* x = nullptr;                   // [B][d] residual stream
+  bf16_t* h_hi = nullptr;               // [B][max(d)] normed input of q|k|v, gate|up and the head
+  bf16_t* h_lo = nullptr;
+  float* qkv_buf = nullptr;             // [B][(H + 2 Hkv) hd] raw q|k|v
+  bf16_t* att_hi = nullptr;             // [B][H hd]
+  bf16_t* att_lo = nullptr;
+  bf16_t* u_hi = nullptr;               // [B][F]
+  bf16_t* u_lo = nullptr;
+  float* partial = nullptr;
+  unsigned* counters = nullptr;         // gemm counters, then B * Hkv attention counters
+  float* attn_part = nullptr;
+  float* head_val = nullptr;
+  int32_t* head_idx = nullptr;
+  int64_t n_gemm_counters = 0;
+  int64_t bytes = 0;
+};
+
+// The batched path runs bf16 weights in the output-major layout (matrix-core operands).
+bool batch_config_ok(const llmk_config* c) { return c->w_dtype == LLMK_BF16 && c->w_layout == LLMK_W_OUT_IN; }
+
+void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P) {
+  const int64_t d = c->d, qd = c->n_head * c->head_dim, kvd = c->n_kv * c->head_dim, F = c->hidden;
+  P.B = B;
+  BgemmParams* gs[5] = {&P.qkv, &P.o, &P.gu, &P.down, &P.head};
+  const int modes[5] = {BG_QKV, BG_RESID, BG_GATEUP, BG_RESID, BG_HEAD};
+  const int64_t Ns[5] = {qd + 2 * kvd, d, F, d, c->vocab};
+  const int64_t Ks[5] = {d, qd, d, F, d};
+  int64_t part = 0, ncnt = 0;
+  for (int i = 0; i < 5; ++i) {
+    gs[i]->N = Ns[i];
+    gs[i]->K = Ks[i];
+    gs[i]->B = (int32_t)B;
+    bgemm_plan(*gs[i], modes[i], kBatchTargetBlocks);
+    part = std::max(part, bgemm_partial_floats(*gs[i]));
+    ncnt = std::max(ncnt, (int64_t)gs[i]->n_rblk + 1);
+  }
+  P.qkv.n0 = qd;
+  P.qkv.n1 = kvd;
+  P.n_gemm_counters = ncnt;
+  P.attn.H = (int32_t)c->n_head;
+  P.attn.Hkv = (int32_t)c->n_kv;
+  P.attn.hd = (int32_t)c->head_dim;
+  P.attn.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
+  attn_plan(P.attn, c->max_seq);
+  P.attn.rows = (int32_t)B;
+
+  Carve cv(ws);
+  P.state = cv.take<BatchState>(1);
+  P.x = cv.take<float>(B * d);
+  P.h_hi = cv.take<bf16_t>(B * d);
+  P.h_lo = cv.take<bf16_t>(B * d);
+  P.qkv_buf = cv.take<float>(B * (qd + 2 * kvd));
+  P.att_hi = cv.take<bf16_t>(B * qd);
+  P.att_lo = cv.take<bf16_t>(B * qd);
+  P.u_hi = cv.take<bf16_t>(B * F);
+  P.u_lo = cv.take<bf16_t>(B * F);
+  P.partial = cv.take<float>(part > 0 ? part : 1);
+  P.counters = cv.take<unsigned>(ncnt + B * c->n_kv);
+  P.attn_part = cv.take<float>(B * (int64_t)P.attn.n_parts * c->n_head * (c->head_dim + 2));
+  P.head_val = cv.take<float>(B * (int64_t)P.head.n_rblk);
+  P.head_idx = cv.take<int32_t>(B * (int64_t)P.head.n_rblk);
+  P.bytes = cv.off;
+}
+
+int64_t batch_counters_total(const llmk_config* c, const BatchPlan& P) { return P.n_gemm_counters + P.B * c->n_kv; }
+
+// Enqueue one batched decode step; tokens, positions and slots are read from P.state on the device.
+hipError_t enqueue_batch(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, BatchPlan& P,
+                         float* logits, int32_t* tokens_out, float* hidden, hipStream_t s) {
+  const int64_t d = c->d, kvd = c->n_kv * c->head_dim;
+  const int32_t B = (int32_t)P.B;
+  const float eps = (float)c->eps;
+  unsigned* acnt = P.counters + P.n_gemm_counters;
+  hipError_t e = hipSuccess;
+  for (int64_t l = 0; l < c->n_layer && e == hipSuccess; ++l) {
+    const float* g_attn = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
+    const float* g_ffn = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
+    // h = rmsnorm(x) g_attn (layer 0: x = emb[token] first); q|k|v = W h
+    e = bnorm_launch(P.x, l == 0 ? m->emb.ptr : nullptr, 1, P.state, B, d, g_attn, eps, P.h_hi, P.h_lo, s);
+    if (e != hipSuccess) break;
+    BgemmParams q = P.qkv;
+    q.w0 = layer_t(m, l, LLMK_WQ).ptr;
+    q.w1 = layer_t(m, l, LLMK_WK).ptr;
+    q.w2 = layer_t(m, l, LLMK_WV).ptr;
+    q.xhi = P.h_hi;
+    q.xlo = P.h_lo;
+    q.partial = P.partial;
+    q.counters = P.counters;
+    q.y = P.qkv_buf;
+    if ((e = bgemm_launch(q, BG_QKV, s)) != hipSuccess) break;
+    // RoPE, K/V append at each row's position in its slot, attention over the row's context
+    AttnParams a = P.attn;
+    a.q = nullptr;
+    a.qkv_raw = P.qkv_buf;
+    a.qkv_stride = P.qkv.N;
+    a.k = pool->k[l];
+    a.v = pool->v[l];
+    a.k_w = pool->k[l];
+    a.v_w = pool->v[l];
+    a.slot_elems = pool->capacity * kvd;
+    a.rope_table = static_cast<const float*>(m->rope_table.ptr);
+    a.rope_layout = c->rope_layout;
+    a.state = nullptr;
+    a.bstate = P.state;
+    a.part = P.attn_part;
+    a.counters = acnt;
+    a.out = nullptr;
+    a.out_hi = P.att_hi;
+    a.out_lo = P.att_lo;
+    if ((e = attn_launch(a, s)) != hipSuccess) break;
+    // x += Wo att
+    BgemmParams o = P.o;
+    o.w0 = layer_t(m, l, LLMK_WO).ptr;
+    o.xhi = P.att_hi;
+    o.xlo = P.att_lo;
+    o.partial = P.partial;
+    o.counters = P.counters;
+    o.x = P.x;
+    if ((e = bgemm_launch(o, BG_RESID, s)) != hipSuccess) break;
+    // h = rmsnorm(x) g_ffn; u = silu(Wg h) * (Wu h); x += Wd u
+    if ((e = bnorm_launch(P.x, nullptr, 1, P.state, B, d, g_ffn, eps, P.h_hi, P.h_lo, s)) != hipSuccess) break;
+    BgemmParams gu = P.gu;
+    gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
+    gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
+    gu.xhi = P.h_hi;
+    gu.xlo = P.h_lo;
+    gu.partial = P.partial;
+    gu.counters = P.counters;
+    gu.uhi = P.u_hi;
+    gu.ulo = P.u_lo;
+    if ((e = bgemm_launch(gu, BG_GATEUP, s)) != hipSuccess) break;
+    BgemmParams dn = P.down;
+    dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
+    dn.xhi = P.u_hi;
+    dn.xlo = P.u_lo;
+    dn.partial = P.partial;
+    dn.counters = P.counters;
+    dn.x = P.x;
+    dn.hidden = hidden ? hidden + l * d : nullptr;
+    dn.hidden_stride = c->n_layer * d;
+    e = bgemm_launch(dn, BG_RESID, s);
+  }
+  if (e != hipSuccess) return e;
+  // logits = W_out rmsnorm(x) g_final; greedy token per row; state advances
+  e = bnorm_launch(P.x, nullptr, 1, P.state, B, d, static_cast<const float*>(m->g_final.ptr), eps, P.h_hi, P.h_lo, s);
+  if (e != hipSuccess) return e;
+  BgemmParams h = P.head;
+  h.w0 = m->w_out.ptr;
+  h.xhi = P.h_hi;
+  h.xlo = P.h_lo;
+  h.counters = P.counters;
+  h.y = logits;
+  h.part_val = P.head_val;
+  h.part_idx = P.head_idx;
+  h.token_out = tokens_out;
+  h.state = P.state;
+  return bgemm_launch(h, BG_HEAD, s);
+}
+
+// Checks of the batched entry points, in the documented order; fills init on success.
+int32_t batch_checks(const llmk_config* cfg, const llmk_model* model, const llmk_kv_pool* pool, int64_t B,
+                     const int64_t* slots_h, const int64_t* tokens_h, const int64_t* pos_h, int64_t n_steps,
+                     const void* out_ptr, const void* ws, BatchInit& init) {
+  if (!cfg || !model || !pool || !slots_h || !tokens_h || !pos_h || !out_ptr || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return st;
+  if (B < 1) return LLMK_EMPTY_DIMENSION;
+  if (B > LLMK_MAX_BATCH) return LLMK_DIMENSION_TOO_LARGE;
+  if ((st = model_check(cfg, model)) != LLMK_OK) return st;
+  if ((st = model_lengths(cfg, model)) != LLMK_OK) return st;
+  if ((st = pool_check(cfg, pool)) != LLMK_OK) return st;
+  if (!weights_aligned(cfg, model) || !batch_config_ok(cfg)) return LLMK_INVALID_ARGUMENT;
+  for (int64_t r = 0; r < B; ++r)
+    if (slots_h[r] < 0 || slots_h[r] >= pool->n_slots) return LLMK_SLOT_OUT_OF_RANGE;
+  for (int64_t r = 0; r < B; ++r)
+    for (int64_t q = 0; q < r; ++q)
+      if (slots_h[q] == slots_h[r]) return LLMK_INVALID_ARGUMENT;
+  for (int64_t r = 0; r < B; ++r)
+    if (tokens_h[r] < 0 || tokens_h[r] >= cfg->vocab) return LLMK_TOKEN_OUT_OF_RANGE;
+  for (int64_t r = 0; r < B; ++r)
+    if (pos_h[r] < 0 || pos_h[r] + n_steps > cfg->max_seq) return LLMK_POSITION_OUT_OF_RANGE;
+  for (int64_t r = 0; r < B; ++r)
+    if (pos_h[r] != pool->slot_len_h[slots_h[r]]) return LLMK_CACHE_LENGTH_MISMATCH;
+  for (int64_t r = 0; r < B; ++r)
+    if (pos_h[r] + n_steps > pool->capacity) return LLMK_CACHE_CAPACITY_EXCEEDED;
+  memset(&init, 0, sizeof(init));
+  for (int64_t r = 0; r < B; ++r) {
+    init.token[r] = (int32_t)tokens_h[r];
+    init.pos[r] = (int32_t)pos_h[r];
+    init.slot[r] = (int32_t)slots_h[r];
+  }
+  init.rows = (int32_t)B;
+  return LLMK_OK;
+}
+
 }  // namespace
 
 // =========================================================================================================
@@ -707,10 +912,22 @@ int32_t llmk_kv_slot_offset(const llmk_kv_pool* pool, int64_t slot, int64_t pos,
 int64_t llmk_decode_workspace_bytes(const llmk_config* cfg, int64_t batch) {
   int32_t st = config_check(cfg);
   if (st != LLMK_OK) return -st;
-  if (batch != 1) return -LLMK_INVALID_ARGUMENT;
-  DecodePlan D;
-  plan_decode(cfg, nullptr, D);
-  return D.bytes;
+  if (batch < 1) return -LLMK_EMPTY_DIMENSION;
+  if (batch > LLMK_MAX_BATCH) return -LLMK_DIMENSION_TOO_LARGE;
+  int64_t bytes = 0;
+  if (batch == 1) {
+    DecodePlan D;
+    plan_decode(cfg, nullptr, D);
+    bytes = D.bytes;
+  } else if (!batch_config_ok(cfg)) {
+    return -LLMK_INVALID_ARGUMENT;
+  }
+  if (batch_config_ok(cfg)) {
+    BatchPlan P;
+    plan_batch(cfg, batch, nullptr, P);
+    bytes = std::max(bytes, P.bytes);
+  }
+  return bytes;
 }
 
 int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
@@ -772,6 +989,72 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
   if (cs) (void)hipStreamDestroy(cs);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos0 + n_steps;
+  return LLMK_OK;
+}
+
+int32_t llmk_decode_step_batch(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t batch,
+                               const int64_t* slots_h, const int64_t* tokens_h, const int64_t* pos_h, float* logits,
+                               int64_t len_logits, int32_t* tokens_out, int64_t len_tokens, float* hidden,
+                               int64_t len_hidden, void* ws, int64_t len_ws, void* stream) {
+  BatchInit init;
+  int32_t st = batch_checks(cfg, model, pool, batch, slots_h, tokens_h, pos_h, 1, tokens_out, ws, init);
+  if (st != LLMK_OK) return st;
+  if (logits && len_logits != batch * cfg->vocab) return LLMK_LOGITS_LENGTH_MISMATCH;
+  if (len_tokens != batch) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (hidden && len_hidden != batch * cfg->n_layer * cfg->d) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  BatchPlan P;
+  plan_batch(cfg, batch, nullptr, P);
+  if (len_ws < P.bytes) return LLMK_INVALID_ARGUMENT;
+  plan_batch(cfg, batch, ws, P);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
+  if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
+  if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, logits, tokens_out, hidden, s);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos_h[r] + 1;
+  return LLMK_OK;
+}
+
+int32_t llmk_decode_steps_batch(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t batch,
+                                const int64_t* slots_h, const int64_t* tokens0_h, const int64_t* pos0_h,
+                                int64_t n_steps, int32_t* tokens_out, int64_t len_tokens, void* ws, int64_t len_ws,
+                                void* stream) {
+  if (!cfg || !model || !pool || !slots_h || !tokens0_h || !pos0_h || !tokens_out || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return st;
+  if (n_steps < 1) return LLMK_EMPTY_DIMENSION;
+  if (n_steps > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  BatchInit init;
+  st = batch_checks(cfg, model, pool, batch, slots_h, tokens0_h, pos0_h, n_steps, tokens_out, ws, init);
+  if (st != LLMK_OK) return st;
+  if (len_tokens != n_steps * batch) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  BatchPlan P;
+  plan_batch(cfg, batch, nullptr, P);
+  if (len_ws < P.bytes) return LLMK_INVALID_ARGUMENT;
+  plan_batch(cfg, batch, ws, P);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
+  if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+
+  hipStream_t cs = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t ee = enqueue_batch(cfg, model, pool, P, nullptr, tokens_out, nullptr, cs);
+    e = hipStreamEndCapture(cs, &graph);
+    if (ee != hipSuccess) e = ee;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  for (int64_t i = 0; e == hipSuccess && i < n_steps; ++i) e = hipGraphLaunch(exec, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (cs) (void)hipStreamDestroy(cs);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos0_h[r] + n_steps;
   return LLMK_OK;
 }
 

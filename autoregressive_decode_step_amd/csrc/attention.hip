@@ -58,7 +58,9 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
 
   const int G = p.H / p.Hkv;
   const int kvh = blockIdx.y, part = blockIdx.x;
-  const int ctx = p.state ? p.state->pos + 1 : p.ctx;
+  const int row = blockIdx.z;                             // batched decode: the sequence row
+  const bool batched = p.bstate != nullptr;
+  const int ctx = batched ? p.bstate->pos[row] + 1 : (p.state ? p.state->pos + 1 : p.ctx);
   const int span = CH * p.sub_per_wg;
   const int tb = part * span;
   if (tb >= ctx) return;
@@ -70,8 +72,11 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
   const int wave = wv % ATTN_SWAVES;                     // wave within its stream
   const int stid = threadIdx.x % ATTN_STHREADS;          // thread within its stream
   const int64_t rstride = (int64_t)p.Hkv * HD;           // elements between positions
-  const T* Kb = static_cast<const T*>(p.k) + (int64_t)kvh * HD;
-  const T* Vb = static_cast<const T*>(p.v) + (int64_t)kvh * HD;
+  const int64_t rbase = batched ? (int64_t)p.bstate->slot[row] * p.slot_elems : 0;   // the row's slot region
+  const T* Kb = static_cast<const T*>(p.k) + rbase + (int64_t)kvh * HD;
+  const T* Vb = static_cast<const T*>(p.v) + rbase + (int64_t)kvh * HD;
+  const float* qkv_raw = p.qkv_raw ? p.qkv_raw + (batched ? (int64_t)row * p.qkv_stride : 0) : nullptr;
+  unsigned* counters = p.counters + (batched ? (int64_t)row * p.Hkv : 0);
   const float scale = 1.0f / sqrtf((float)HD);
 
   // cooperative tile load by one stream: vector idx -> (K or V, row, vector); rows past te are clamped
@@ -108,8 +113,8 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
   // workgroup rotates its q heads by the position, and the workgroup whose part holds that position
   // rotates k, rounds k and v to the cache dtype, appends them to the cache and patches its tile.
   const int pos = ctx - 1;
-  const bool owner = p.qkv_raw && pos >= tb && pos < te;
-  if (p.qkv_raw) {
+  const bool owner = qkv_raw && pos >= tb && pos < te;
+  if (qkv_raw) {
     constexpr int HALF = HD / 2;
     const float* tab = p.rope_table + (int64_t)pos * HALF * 2;
     for (int i = threadIdx.x; i < (G + (owner ? 1 : 0)) * HALF; i += ATTN_THREADS) {
@@ -117,8 +122,8 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
       const int ia = p.rope_layout == 0 ? j : 2 * j;
       const int ib = p.rope_layout == 0 ? j + HALF : 2 * j + 1;
       const float cs = tab[2 * j], sn = tab[2 * j + 1];
-      const float* src = g < G ? p.qkv_raw + (int64_t)(kvh * G + g) * HD
-                               : p.qkv_raw + (int64_t)p.H * HD + (int64_t)kvh * HD;   // this head's k
+      const float* src = g < G ? qkv_raw + (int64_t)(kvh * G + g) * HD
+                               : qkv_raw + (int64_t)p.H * HD + (int64_t)kvh * HD;   // this head's k
       const float a = src[ia], b = src[ib];
       const float ra = a * cs - b * sn, rb = a * sn + b * cs;
       if (g < G) {
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
       }
     }
     if (owner) {
-      const float* vsrc = p.qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD;
+      const float* vsrc = qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD;
       for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, vsrc[e]);
     }
     __syncthreads();
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
       const int64_t off = (int64_t)pos * p.Hkv * HD + (int64_t)kvh * HD;
       for (int e = threadIdx.x; e < 2 * HD; e += ATTN_THREADS) {
         const int w = e / HD, ee = e % HD;
-        (w == 0 ? static_cast<T*>(p.k_w) : static_cast<T*>(p.v_w))[off + ee] = s_new[w][ee];
+        (w == 0 ? static_cast<T*>(p.k_w) : static_cast<T*>(p.v_w))[rbase + off + ee] = s_new[w][ee];
       }
     }
   } else {
@@ -296,7 +301,8 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
   }
   __syncthreads();
   const int64_t pstride = HD + 2;
-  float* P = p.part + ((int64_t)kvh * p.n_parts + part) * G * pstride;
+  float* part_base = p.part + (batched ? (int64_t)row * p.Hkv * p.n_parts * G * pstride : 0);
+  float* P = part_base + ((int64_t)kvh * p.n_parts + part) * G * pstride;
   for (int i = threadIdx.x; i < G * pstride; i += ATTN_THREADS) {
     const int g = i / pstride, j = i % pstride;
     st_dev(&P[i], j == 0 ? s_m1[g] : j == 1 ? s_l1[g] : s_o1[g][j - 2]);
@@ -306,12 +312,12 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
   stores_done();
   __syncthreads();
   const int np = (ctx + span - 1) / span;
-  if (threadIdx.x == 0) s_last = (take_ticket(&p.counters[kvh]) == (unsigned)(np - 1));
+  if (threadIdx.x == 0) s_last = (take_ticket(&counters[kvh]) == (unsigned)(np - 1));
   __syncthreads();
   if (!s_last) return;
   // every thread issues all its loads at once (max, sum and its output element of every part), so the
   // merge costs one round trip; parts are combined in part order
-  const float* PB = p.part + (int64_t)kvh * p.n_parts * G * pstride;
+  const float* PB = part_base + (int64_t)kvh * p.n_parts * G * pstride;
   const int64_t cstride = (int64_t)G * pstride;
   for (int idx = threadIdx.x; idx < G * HD; idx += ATTN_THREADS) {
     const int g = idx / HD, e = idx % HD;
@@ -336,9 +342,17 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
         O = fmaf(oc[c], w, O);
       }
     }
-    p.out[(int64_t)(kvh * G + g) * HD + e] = O / L;
+    const int64_t oi = (int64_t)(kvh * G + g) * HD + e;
+    if (p.out_hi) {
+      bf16_t hi, lo;
+      split_bf16(O / L, hi, lo);
+      p.out_hi[(int64_t)row * p.H * HD + oi] = hi;
+      p.out_lo[(int64_t)row * p.H * HD + oi] = lo;
+    } else {
+      p.out[oi] = O / L;
+    }
   }
-  if (threadIdx.x == 0) reset_ticket(&p.counters[kvh]);
+  if (threadIdx.x == 0) reset_ticket(&counters[kvh]);
 }
 
 static int tile_rows(int kv_is_bf16, int hd) {
@@ -361,7 +375,8 @@ void attn_plan(AttnParams& p, int64_t max_ctx) {
 
 template <typename T, int HD>
 static hipError_t attn_one(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attn_kernel<T, HD>), dim3((unsigned)p.n_parts, (unsigned)p.Hkv), dim3(ATTN_THREADS), 0, s, p);
+  const unsigned rows = p.bstate ? (unsigned)p.rows : 1u;
+  hipLaunchKernelGGL((attn_kernel<T, HD>), dim3((unsigned)p.n_parts, (unsigned)p.Hkv, rows), dim3(ATTN_THREADS), 0, s, p);
   return hipGetLastError();
 }
 

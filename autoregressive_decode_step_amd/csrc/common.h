@@ -134,6 +134,24 @@ struct DecodeState {
   int32_t pad;
 };
 
+// Batched decode: one entry per sequence row of the batch (rows <= LLMK_MAX_BATCH_ROWS).
+constexpr int LLMK_MAX_BATCH_ROWS = 64;
+struct BatchState {
+  int32_t token[LLMK_MAX_BATCH_ROWS];   // token each row consumes in the next step
+  int32_t pos[LLMK_MAX_BATCH_ROWS];     // its position
+  int32_t slot[LLMK_MAX_BATCH_ROWS];    // the row's slot in the K/V pool
+  int32_t rows;
+  int32_t step;                         // index of the next step within a multi-step call
+  int32_t pad[2];
+};
+
+// hi + lo split of an fp32 value into two bf16 (round to nearest even each): hi + lo carries about 16
+// significant bits, the form the batched projections feed to bf16 matrix cores
+__device__ __forceinline__ void split_bf16(float v, bf16_t& hi, bf16_t& lo) {
+  hi = f32_to_bf16(v);
+  lo = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 }  // namespace llmk

@@ -93,3 +93,45 @@ class Decoder:
 
     def steps(self, token0: int, pos0: int, n: int, tokens_out, slot: int = 0) -> int:
         return decode_steps(self.cfg, self.model, self.pool, slot, token0, pos0, n, tokens_out, self.ws)
+
+
+def upload_kv_source(source: list, device="cuda") -> list:
+    """Per layer (K, V) host arrays [n][Hkv][hd] (pool dtype) -> device tensors of the same shape."""
+    out = []
+    for kk, vv in source:
+        n = kk.shape[0]
+        out.append((to_device(kk, device).view(n, kk.shape[1], kk.shape[2]),
+                    to_device(vv, device).view(n, vv.shape[1], vv.shape[2])))
+    return out
+
+
+def fill_prefix_window(pool: KVPool, slot: int, source_dev: list, start: int, n: int) -> None:
+    """Copy positions [start, start + n) of a device K/V source into positions 0..n-1 of a slot and record
+    its length (device-to-device)."""
+    for l, (kk, vv) in enumerate(source_dev):
+        if n > 0:
+            pool.slot_view(l, slot, "k")[:n] = kk[start:start + n]
+            pool.slot_view(l, slot, "v")[:n] = vv[start:start + n]
+    pool.slot_len[slot] = n
+
+
+class BatchDecoder:
+    """Several slots of a pool driven together through decode_step_batch / decode_steps_batch."""
+
+    def __init__(self, cfg: Config, model: Model, pool: KVPool, batch: int, device="cuda"):
+        from . import decode_step_batch, decode_steps_batch  # noqa: F401
+        self.cfg, self.model, self.pool, self.batch = cfg, model, pool, batch
+        nbytes = decode_workspace_bytes(cfg, batch)
+        if nbytes < 0:
+            raise ValueError(f"config refused for batch {batch}: {-nbytes}")
+        self.ws = workspace(nbytes, device)
+        self.tokens_out = torch.zeros(batch, dtype=torch.int32, device=device)
+
+    def step(self, slots, tokens, pos, logits=None, hidden=None) -> int:
+        from . import decode_step_batch
+        return decode_step_batch(self.cfg, self.model, self.pool, slots, tokens, pos, self.tokens_out, self.ws,
+                                 logits, hidden)
+
+    def steps(self, slots, tokens0, pos0, n: int, tokens_out) -> int:
+        from . import decode_steps_batch
+        return decode_steps_batch(self.cfg, self.model, self.pool, slots, tokens0, pos0, n, tokens_out, self.ws)

@@ -72,6 +72,8 @@ enum {
 /* Ceiling on every dimension: refuses byte counts passed as element counts
  * ([llmk] "Status vocabulary and the shape checks (contract)", "Guarantees"). */
 #define LLMK_MAX_DIM (1LL << 24)
+/* most sequences one batched decode step serves */
+#define LLMK_MAX_BATCH 64
 
 typedef enum { LLMK_F32 = 0, LLMK_BF16 = 1 } llmk_dtype;
 /* Half-split pairs (j, j + hd/2) are the GPT-NeoX/Qwen3 convention ([llmk] "Two
@@ -267,7 +269,9 @@ typedef struct {
 int32_t llmk_kv_slot_offset(const llmk_kv_pool* pool, int64_t slot, int64_t pos, int64_t kv_head,
                             int64_t* offset_h);
 
-/* Bytes of workspace a decode call needs for `batch` rows (negative status if cfg is refused). */
+/* Bytes of workspace a decode call needs for `batch` rows (negative status if cfg is refused). batch 1
+ * covers llmk_decode_step / llmk_decode_steps and, when the config allows the batched path, the batched
+ * entry points with one row; batch 2..LLMK_MAX_BATCH needs bf16 weights in LLMK_W_OUT_IN (else -578). */
 int64_t llmk_decode_workspace_bytes(const llmk_config* cfg, int64_t batch);
 
 /* One decode step of one sequence ([fwd] "What a forward step does"; [llmk] "How this composes into
@@ -296,6 +300,36 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
 int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                           int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
                           void* ws, int64_t len_ws, void* stream);
+
+/* One decode step of `batch` sequences at once ([xpu] "5. The batched decode": every weight row is read
+ * once for all rows of the batch; the projections run as bf16 matrix-core GEMMs with each fp32 activation
+ * carried as a bf16 hi + lo pair, fp32 accumulation). Row r is sequence slot slots_h[r] with input token
+ * tokens_h[r] at position pos_h[r]; each row computes exactly llmk_decode_step's step for its sequence
+ * (its own context length, its own K/V append).
+ *   slots_h, tokens_h, pos_h: host int64 [batch]; slots distinct
+ *   logits    : device fp32 [batch][vocab] or NULL (len_logits = batch * vocab)
+ *   tokens_out: device int32 [batch] (len_tokens = batch)
+ *   hidden    : device fp32 [batch][n_layer][d] or NULL (len_hidden = batch * n_layer * d)
+ * Needs bf16 weights in LLMK_W_OUT_IN. On success slot_len_h[slots_h[r]] = pos_h[r] + 1 for every row.
+ * Codes, in order: 578 (null), config codes, 561 (batch < 1), 564 (batch > LLMK_MAX_BATCH), 578 (model
+ * tensors), 576, pool 578/561/564, 578 (alignment, or weights not bf16 LLMK_W_OUT_IN), then over all
+ * rows: 575 (slot), 578 (a slot repeated), 572 (token), 573 (pos), 566 (pos != slot length), 571
+ * (capacity); then 568 (len_logits), 577 (len_tokens, len_hidden), 578 (workspace). */
+int32_t llmk_decode_step_batch(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t batch,
+                               const int64_t* slots_h, const int64_t* tokens_h, const int64_t* pos_h, float* logits,
+                               int64_t len_logits, int32_t* tokens_out, int64_t len_tokens, float* hidden,
+                               int64_t len_hidden, void* ws, int64_t len_ws, void* stream);
+
+/* n_steps greedy batched steps: row r's step i consumes the token at position pos0_h[r] + i (tokens0_h[r]
+ * for i = 0, else its previous output, fed back on the device) and writes its greedy token to
+ * tokens_out[i * batch + r]. One step is captured into a HIP graph and replayed; returns after `stream`
+ * has finished. tokens_out: device int32 [n_steps][batch] (len_tokens = n_steps * batch).
+ * Codes: as llmk_decode_step_batch (without the logits/hidden checks), plus 561/564 for n_steps; 573 and
+ * 571 take pos0 + n_steps. On success slot_len_h[slots_h[r]] = pos0_h[r] + n_steps. */
+int32_t llmk_decode_steps_batch(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t batch,
+                                const int64_t* slots_h, const int64_t* tokens0_h, const int64_t* pos0_h,
+                                int64_t n_steps, int32_t* tokens_out, int64_t len_tokens, void* ws, int64_t len_ws,
+                                void* stream);
 
 /* dst = src^T for a rows x cols row-major matrix (dst is cols x rows), both device buffers of rows*cols
  * elements of dtype; the one-time repacking of projections into LLMK_W_OUT_IN. dst may not alias src.

@@ -329,3 +329,54 @@ def decode_step(cfg: dict, tensors_ok=True, lens_ok=True, pool_ok=True, pool_dim
     if hidden and len_hidden != cfg["n_layer"] * cfg["d"]:
         return OUTPUT_LEN
     return INVALID if ws_short else OK
+
+
+def decode_step_batch(cfg: dict, batch=1, tensors_ok=True, lens_ok=True, pool_ok=True, pool_dims_bad=False,
+                      batch_weights_ok=True, n_slots=1, capacity=0, slots=(0,), slot_lens=None, tokens=(0,),
+                      pos=(0,), n_steps=1, logits=False, len_logits=0, len_tokens=None, hidden=False, len_hidden=0,
+                      ws_short=False):
+    """Expected status of llmk_decode_step_batch (n_steps = 1) and llmk_decode_steps_batch (logits=False,
+    hidden=False, len_tokens = n_steps * batch expected). slot_lens maps slot -> recorded length (default 0).
+    batch_weights_ok: the weights are bf16 in the output-major layout the batched path runs on."""
+    c = config_check(**cfg)
+    if c != OK:
+        return c
+    if n_steps < 1:
+        return EMPTY
+    if n_steps > MAX_DIM:
+        return TOO_LARGE
+    if batch < 1:
+        return EMPTY
+    if batch > 64:
+        return TOO_LARGE
+    if not tensors_ok:
+        return INVALID
+    if not lens_ok:
+        return WEIGHT_LEN
+    if not pool_ok:
+        return INVALID
+    if pool_dims_bad:
+        return EMPTY
+    if not batch_weights_ok:
+        return INVALID
+    lens = slot_lens or {}
+    rows = range(batch)
+    if any(not (0 <= slots[r] < n_slots) for r in rows):
+        return SLOT
+    if len(set(slots[r] for r in rows)) != batch:
+        return INVALID
+    if any(not (0 <= tokens[r] < cfg["vocab"]) for r in rows):
+        return TOKEN
+    if any(pos[r] < 0 or pos[r] + n_steps > cfg["max_seq"] for r in rows):
+        return POSITION
+    if any(pos[r] != lens.get(slots[r], 0) for r in rows):
+        return CACHE_LEN
+    if any(pos[r] + n_steps > capacity for r in rows):
+        return CAPACITY
+    if logits and len_logits != batch * cfg["vocab"]:
+        return LOGITS_LEN
+    if (len_tokens if len_tokens is not None else n_steps * batch) != n_steps * batch:
+        return OUTPUT_LEN
+    if hidden and len_hidden != batch * cfg["n_layer"] * cfg["d"]:
+        return OUTPUT_LEN
+    return INVALID if ws_short else OK

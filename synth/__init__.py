@@ -214,3 +214,19 @@ def prompt(n: int, vocab: int, seed: int = 1, stream: int = 0) -> np.ndarray:
 
 
 PAGE_PROMPT = (3, 14, 15, 9, 2, 6)   # the Inference Academy page's cache-vs-recompute prompt
+
+
+def ragged_contexts(n: int, lo: int, hi: int, seed: int = 3) -> np.ndarray:
+    """Seeded context lengths, uniform integers in [lo, hi], one per batch row."""
+    return ints((n,), lo, hi, seed, 3_000_000)
+
+
+# A batched pool of many long sequences is filled from one seeded source per layer: slot s's prefix of
+# c_s positions is positions [SLOT_WINDOW_STRIDE * s, SLOT_WINDOW_STRIDE * s + c_s) of the source, so every
+# slot holds different values without drawing (and storing on the host) every slot separately.
+SLOT_WINDOW_STRIDE = 97
+
+
+def slot_window(slot: int) -> int:
+    """First source position of a slot's prefix."""
+    return SLOT_WINDOW_STRIDE * slot

@@ -277,3 +277,78 @@ def test_decode_step_refusals():
     assert kt(kernel=6) == 578 and kt(kernel=-1) == 578
     assert kt(reps=0) == 561
     assert kt(reps=65) == 564
+
+
+@no_gpu
+def test_decode_step_batch_refusals():
+    import numpy as np
+    d, qd, kvd, F, V, L = 16, 16, 8, 24, 40, 2
+    lens = [d * qd, d * kvd, d * kvd, qd * d, d * F, d * F, F * d, d, d]
+    FA = 0x10000
+
+    def model_for(kw, bad_len=False):
+        arr = (llmk.Tensor * (L * 9))()
+        for l in range(L):
+            for t in range(9):
+                arr[l * 9 + t] = llmk.Tensor(FA, lens[t] + (1 if (bad_len and l == 1 and t == 2) else 0))
+        return llmk.ModelStruct(llmk.Tensor(FA, V * d), llmk.Tensor(FA, V * d), llmk.Tensor(FA, d),
+                                llmk.Tensor(FA, 64 * 4), arr), arr
+
+    def run(kw, batch=2, slots=(0, 1), tokens=(0, 0), pos=(0, 0), slot_lens=(0, 0, 0), cap=32, n_slots=3,
+            logits=False, len_logits=None, len_tokens=None, hidden=False, len_hidden=None, ws_short=False,
+            n_steps=None, bad_len=False):
+        cfg = llmk.make_config(**kw)
+        m, _keep = model_for(kw, bad_len)
+        ks = (ctypes.c_void_p * L)(FA, FA)
+        sl = np.array(slot_lens, np.int64)
+        ps = llmk.PoolStruct(ks, ks, L, n_slots, cap, 2, 4, kw["kv_dtype"],
+                             sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        a_s, a_t, a_p = (np.array(v, np.int64) for v in (slots, tokens, pos))
+        ws_need = llmk.decode_workspace_bytes(cfg, max(1, min(batch, 64)))
+        ws = max(ws_need, 1) - (1 if ws_short else 0)
+        if n_steps is None:
+            return llmk.lib.llmk_decode_step_batch(
+                ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), batch, a_s.ctypes.data, a_t.ctypes.data,
+                a_p.ctypes.data, FA if logits else None, batch * V if len_logits is None else len_logits, FA,
+                batch if len_tokens is None else len_tokens, FA if hidden else None,
+                batch * L * d if len_hidden is None else len_hidden, FA, ws, None)
+        return llmk.lib.llmk_decode_steps_batch(
+            ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), batch, a_s.ctypes.data, a_t.ctypes.data,
+            a_p.ctypes.data, n_steps, FA, n_steps * batch if len_tokens is None else len_tokens, FA, ws, None)
+
+    good = _cfg_kwargs(w_dtype=1, w_layout=1)
+    cases = [
+        (dict(batch=0), dict(batch=0)),
+        (dict(batch=65, slots=tuple(range(65)), tokens=(0,) * 65, pos=(0,) * 65, slot_lens=(0,) * 70, n_slots=70),
+         dict(batch=65)),
+        (dict(slots=(0, 3)), dict(slots=(0, 3))),
+        (dict(slots=(1, 1)), dict(slots=(1, 1))),
+        (dict(tokens=(0, 40)), dict(tokens=(0, 40))),
+        (dict(pos=(0, -1)), dict(pos=(0, -1))),
+        (dict(pos=(0, 64), slot_lens=(0, 64, 0), cap=128), dict(pos=(0, 64), slot_lens={1: 64}, capacity=128)),
+        (dict(pos=(0, 5), slot_lens=(0, 4, 0)), dict(pos=(0, 5), slot_lens={1: 4})),
+        (dict(pos=(0, 32), slot_lens=(0, 32, 0), cap=32), dict(pos=(0, 32), slot_lens={1: 32}, capacity=32)),
+        (dict(logits=True, len_logits=79), dict(logits=True, len_logits=79)),
+        (dict(len_tokens=3), dict(len_tokens=3)),
+        (dict(hidden=True, len_hidden=63), dict(hidden=True, len_hidden=63)),
+        (dict(ws_short=True), dict(ws_short=True)),
+        (dict(bad_len=True), dict(lens_ok=False)),
+        (dict(n_steps=0), dict(n_steps=0)),
+        (dict(n_steps=40, pos=(0, 0)), dict(n_steps=40)),
+        (dict(n_steps=3, len_tokens=5), dict(n_steps=3, len_tokens=5)),
+    ]
+    for call_kw, exp_kw in cases:
+        base = dict(batch=2, n_slots=3, capacity=32, slots=(0, 1), tokens=(0, 0), pos=(0, 0))
+        base.update({k: v for k, v in call_kw.items() if k in ("batch", "slots", "tokens", "pos")})
+        base.update(exp_kw)
+        if "n_slots" in call_kw:
+            base["n_slots"] = call_kw["n_slots"]
+        exp = contract.decode_step_batch(good, **base)
+        assert exp != contract.OK, call_kw
+        assert run(good, **call_kw) == exp, (call_kw, exp)
+    # the batched path needs bf16 output-major weights
+    for bad in (_cfg_kwargs(w_dtype=1, w_layout=0), _cfg_kwargs(w_dtype=0, w_layout=1)):
+        exp = contract.decode_step_batch(bad, batch=2, n_slots=3, capacity=32, slots=(0, 1), tokens=(0, 0), pos=(0, 0),
+                                         batch_weights_ok=False)
+        assert run(bad) == exp == 578
+        assert llmk.decode_workspace_bytes(llmk.make_config(**bad), 2) == -578
