@@ -97,6 +97,9 @@ _SIGS = {
                                 _p, _p, _p, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_decode_steps_batch": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64,
                                  _p, _p, _p, _i64, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_decode_batch_kernel_time": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct),
+                                       ctypes.POINTER(PoolStruct), _i64, _p, _p, _p, _i32, _i32, _p,
+                                       ctypes.POINTER(_f32), _p, _i64, _p], _i32),
     "llmk_decode_kernel_time": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                  _i64, _i64, _i64, _i32, _i32, _p, ctypes.POINTER(_f32), _p, _i64, _p], _i32),
 }
@@ -379,4 +382,21 @@ def decode_kernel_time(cfg: Config, model: Model, pool: KVPool, slot, token, pos
     st = lib.llmk_decode_kernel_time(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot,
                                      token, pos, kernel, reps, _ptr(token_out), ctypes.byref(ms), _ptr(ws), _len(ws),
                                      _stream(stream))
+    return st, ms.value
+
+
+BATCH_KERNEL_CLASSES = ("norm_attn", "qkv", "attention", "o", "norm_ffn", "gate_up", "down", "norm_final", "head")
+
+
+def decode_batch_kernel_time(cfg: Config, model: Model, pool: KVPool, slots, tokens, pos, kernel, reps, tokens_out,
+                             ws, stream=None):
+    """Returns (status, milliseconds per launch) of batched kernel class `kernel` (index into
+    BATCH_KERNEL_CLASSES)."""
+    sl, psl = _host_i64(slots)
+    tk, ptk = _host_i64(tokens)
+    ps, pps = _host_i64(pos)
+    ms = _f32(0.0)
+    st = lib.llmk_decode_batch_kernel_time(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct),
+                                           len(sl), psl, ptk, pps, kernel, reps, _ptr(tokens_out), ctypes.byref(ms),
+                                           _ptr(ws), _len(ws), _stream(stream))
     return st, ms.value

@@ -457,6 +457,7 @@ struct BatchPlan {
   float* attn_part = nullptr;
   float* head_val = nullptr;
   int32_t* head_idx = nullptr;
+  int32_t* tok_scratch = nullptr;       // kTimeMaxReps * B tokens: repeated timing launches of the head
   int64_t n_gemm_counters = 0;
   int64_t bytes = 0;
 };
@@ -505,102 +506,127 @@ void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P) {
   P.attn_part = cv.take<float>(B * (int64_t)P.attn.n_parts * c->n_head * (c->head_dim + 2));
   P.head_val = cv.take<float>(B * (int64_t)P.head.n_rblk);
   P.head_idx = cv.take<int32_t>(B * (int64_t)P.head.n_rblk);
+  P.tok_scratch = cv.take<int32_t>(kTimeMaxReps * B);
   P.bytes = cv.off;
 }
 
 int64_t batch_counters_total(const llmk_config* c, const BatchPlan& P) { return P.n_gemm_counters + P.B * c->n_kv; }
 
-// Enqueue one batched decode step; tokens, positions and slots are read from P.state on the device.
-hipError_t enqueue_batch(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, BatchPlan& P,
-                         float* logits, int32_t* tokens_out, float* hidden, hipStream_t s) {
+// The kernels of one batched step, in order: per layer BK_NORM1, BK_QKV, BK_ATTN, BK_O, BK_NORM2, BK_GATEUP,
+// BK_DOWN, then BK_NORMF and BK_HEAD.
+enum BatchKernel { BK_NORM1 = 0, BK_QKV, BK_ATTN, BK_O, BK_NORM2, BK_GATEUP, BK_DOWN, BK_NORMF, BK_HEAD, BK_CLASSES };
+
+// Launch kernel `which` of layer l of a batched step (BK_NORMF / BK_HEAD: the tail, l ignored); tokens,
+// positions and slots are read from P.state on the device.
+hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, BatchPlan& P,
+                               int64_t l, int which, float* logits, int32_t* tokens_out, float* hidden,
+                               hipStream_t s) {
   const int64_t d = c->d, kvd = c->n_kv * c->head_dim;
   const int32_t B = (int32_t)P.B;
   const float eps = (float)c->eps;
-  unsigned* acnt = P.counters + P.n_gemm_counters;
-  hipError_t e = hipSuccess;
-  for (int64_t l = 0; l < c->n_layer && e == hipSuccess; ++l) {
-    const float* g_attn = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
-    const float* g_ffn = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
-    // h = rmsnorm(x) g_attn (layer 0: x = emb[token] first); q|k|v = W h
-    e = bnorm_launch(P.x, l == 0 ? m->emb.ptr : nullptr, 1, P.state, B, d, g_attn, eps, P.h_hi, P.h_lo, s);
-    if (e != hipSuccess) break;
-    BgemmParams q = P.qkv;
-    q.w0 = layer_t(m, l, LLMK_WQ).ptr;
-    q.w1 = layer_t(m, l, LLMK_WK).ptr;
-    q.w2 = layer_t(m, l, LLMK_WV).ptr;
-    q.xhi = P.h_hi;
-    q.xlo = P.h_lo;
-    q.partial = P.partial;
-    q.counters = P.counters;
-    q.y = P.qkv_buf;
-    if ((e = bgemm_launch(q, BG_QKV, s)) != hipSuccess) break;
-    // RoPE, K/V append at each row's position in its slot, attention over the row's context
-    AttnParams a = P.attn;
-    a.q = nullptr;
-    a.qkv_raw = P.qkv_buf;
-    a.qkv_stride = P.qkv.N;
-    a.k = pool->k[l];
-    a.v = pool->v[l];
-    a.k_w = pool->k[l];
-    a.v_w = pool->v[l];
-    a.slot_elems = pool->capacity * kvd;
-    a.rope_table = static_cast<const float*>(m->rope_table.ptr);
-    a.rope_layout = c->rope_layout;
-    a.state = nullptr;
-    a.bstate = P.state;
-    a.part = P.attn_part;
-    a.counters = acnt;
-    a.out = nullptr;
-    a.out_hi = P.att_hi;
-    a.out_lo = P.att_lo;
-    if ((e = attn_launch(a, s)) != hipSuccess) break;
-    // x += Wo att
-    BgemmParams o = P.o;
-    o.w0 = layer_t(m, l, LLMK_WO).ptr;
-    o.xhi = P.att_hi;
-    o.xlo = P.att_lo;
-    o.partial = P.partial;
-    o.counters = P.counters;
-    o.x = P.x;
-    if ((e = bgemm_launch(o, BG_RESID, s)) != hipSuccess) break;
-    // h = rmsnorm(x) g_ffn; u = silu(Wg h) * (Wu h); x += Wd u
-    if ((e = bnorm_launch(P.x, nullptr, 1, P.state, B, d, g_ffn, eps, P.h_hi, P.h_lo, s)) != hipSuccess) break;
-    BgemmParams gu = P.gu;
-    gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
-    gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
-    gu.xhi = P.h_hi;
-    gu.xlo = P.h_lo;
-    gu.partial = P.partial;
-    gu.counters = P.counters;
-    gu.uhi = P.u_hi;
-    gu.ulo = P.u_lo;
-    if ((e = bgemm_launch(gu, BG_GATEUP, s)) != hipSuccess) break;
-    BgemmParams dn = P.down;
-    dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
-    dn.xhi = P.u_hi;
-    dn.xlo = P.u_lo;
-    dn.partial = P.partial;
-    dn.counters = P.counters;
-    dn.x = P.x;
-    dn.hidden = hidden ? hidden + l * d : nullptr;
-    dn.hidden_stride = c->n_layer * d;
-    e = bgemm_launch(dn, BG_RESID, s);
+  switch (which) {
+    case BK_NORM1:   // h = rmsnorm(x) g_attn (layer 0: x = emb[token] first)
+      return bnorm_launch(P.x, l == 0 ? m->emb.ptr : nullptr, 1, P.state, B, d,
+                          static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr), eps, P.h_hi, P.h_lo, s);
+    case BK_QKV: {   // q|k|v = W h
+      BgemmParams q = P.qkv;
+      q.w0 = layer_t(m, l, LLMK_WQ).ptr;
+      q.w1 = layer_t(m, l, LLMK_WK).ptr;
+      q.w2 = layer_t(m, l, LLMK_WV).ptr;
+      q.xhi = P.h_hi;
+      q.xlo = P.h_lo;
+      q.partial = P.partial;
+      q.counters = P.counters;
+      q.y = P.qkv_buf;
+      return bgemm_launch(q, BG_QKV, s);
+    }
+    case BK_ATTN: {  // RoPE, K/V append at each row's position in its slot, attention over the row's context
+      AttnParams a = P.attn;
+      a.q = nullptr;
+      a.qkv_raw = P.qkv_buf;
+      a.qkv_stride = P.qkv.N;
+      a.k = pool->k[l];
+      a.v = pool->v[l];
+      a.k_w = pool->k[l];
+      a.v_w = pool->v[l];
+      a.slot_elems = pool->capacity * kvd;
+      a.rope_table = static_cast<const float*>(m->rope_table.ptr);
+      a.rope_layout = c->rope_layout;
+      a.state = nullptr;
+      a.bstate = P.state;
+      a.part = P.attn_part;
+      a.counters = P.counters + P.n_gemm_counters;
+      a.out = nullptr;
+      a.out_hi = P.att_hi;
+      a.out_lo = P.att_lo;
+      return attn_launch(a, s);
+    }
+    case BK_O: {     // x += Wo att
+      BgemmParams o = P.o;
+      o.w0 = layer_t(m, l, LLMK_WO).ptr;
+      o.xhi = P.att_hi;
+      o.xlo = P.att_lo;
+      o.partial = P.partial;
+      o.counters = P.counters;
+      o.x = P.x;
+      return bgemm_launch(o, BG_RESID, s);
+    }
+    case BK_NORM2:   // h = rmsnorm(x) g_ffn
+      return bnorm_launch(P.x, nullptr, 1, P.state, B, d, static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr),
+                          eps, P.h_hi, P.h_lo, s);
+    case BK_GATEUP: {   // u = silu(Wg h) * (Wu h)
+      BgemmParams gu = P.gu;
+      gu.w0 = layer_t(m, l, LLMK_WGATE).ptr;
+      gu.w1 = layer_t(m, l, LLMK_WUP).ptr;
+      gu.xhi = P.h_hi;
+      gu.xlo = P.h_lo;
+      gu.partial = P.partial;
+      gu.counters = P.counters;
+      gu.uhi = P.u_hi;
+      gu.ulo = P.u_lo;
+      return bgemm_launch(gu, BG_GATEUP, s);
+    }
+    case BK_DOWN: {  // x += Wd u
+      BgemmParams dn = P.down;
+      dn.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
+      dn.xhi = P.u_hi;
+      dn.xlo = P.u_lo;
+      dn.partial = P.partial;
+      dn.counters = P.counters;
+      dn.x = P.x;
+      dn.hidden = hidden ? hidden + l * d : nullptr;
+      dn.hidden_stride = c->n_layer * d;
+      return bgemm_launch(dn, BG_RESID, s);
+    }
+    case BK_NORMF:
+      return bnorm_launch(P.x, nullptr, 1, P.state, B, d, static_cast<const float*>(m->g_final.ptr), eps, P.h_hi,
+                          P.h_lo, s);
+    case BK_HEAD: {  // logits = W_out h; greedy token per row; state advances
+      BgemmParams h = P.head;
+      h.w0 = m->w_out.ptr;
+      h.xhi = P.h_hi;
+      h.xlo = P.h_lo;
+      h.counters = P.counters;
+      h.y = logits;
+      h.part_val = P.head_val;
+      h.part_idx = P.head_idx;
+      h.token_out = tokens_out;
+      h.state = P.state;
+      return bgemm_launch(h, BG_HEAD, s);
+    }
   }
-  if (e != hipSuccess) return e;
-  // logits = W_out rmsnorm(x) g_final; greedy token per row; state advances
-  e = bnorm_launch(P.x, nullptr, 1, P.state, B, d, static_cast<const float*>(m->g_final.ptr), eps, P.h_hi, P.h_lo, s);
-  if (e != hipSuccess) return e;
-  BgemmParams h = P.head;
-  h.w0 = m->w_out.ptr;
-  h.xhi = P.h_hi;
-  h.xlo = P.h_lo;
-  h.counters = P.counters;
-  h.y = logits;
-  h.part_val = P.head_val;
-  h.part_idx = P.head_idx;
-  h.token_out = tokens_out;
-  h.state = P.state;
-  return bgemm_launch(h, BG_HEAD, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t enqueue_batch(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, BatchPlan& P,
+                         float* logits, int32_t* tokens_out, float* hidden, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  for (int64_t l = 0; l < c->n_layer && e == hipSuccess; ++l)
+    for (int k = BK_NORM1; k <= BK_DOWN && e == hipSuccess; ++k)
+      e = launch_batch_kernel(c, m, pool, P, l, k, logits, tokens_out, hidden, s);
+  if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, P, 0, BK_NORMF, logits, tokens_out, hidden, s);
+  if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, P, 0, BK_HEAD, logits, tokens_out, hidden, s);
+  return e;
 }
 
 // Checks of the batched entry points, in the documented order; fills init on success.
@@ -1154,6 +1180,68 @@ int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model,
   if (cs) (void)hipStreamDestroy(cs);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos + 1;
+  *ms_per_launch_h = ms / (float)(reps * per_rep);
+  return LLMK_OK;
+}
+
+int32_t llmk_decode_batch_kernel_time(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool,
+                                      int64_t batch, const int64_t* slots_h, const int64_t* tokens_h,
+                                      const int64_t* pos_h, int32_t kernel, int32_t reps, int32_t* tokens_out,
+                                      float* ms_per_launch_h, void* ws, int64_t len_ws, void* stream) {
+  if (!ms_per_launch_h) return LLMK_INVALID_ARGUMENT;
+  BatchInit init;
+  int32_t st = batch_checks(cfg, model, pool, batch, slots_h, tokens_h, pos_h, 1, tokens_out, ws, init);
+  if (st != LLMK_OK) return st;
+  if (kernel < 0 || kernel >= BK_CLASSES) return LLMK_INVALID_ARGUMENT;
+  if (reps < 1) return LLMK_EMPTY_DIMENSION;
+  if (reps > kTimeMaxReps) return LLMK_DIMENSION_TOO_LARGE;
+  BatchPlan P;
+  plan_batch(cfg, batch, nullptr, P);
+  if (len_ws < P.bytes) return LLMK_INVALID_ARGUMENT;
+  plan_batch(cfg, batch, ws, P);
+  hipStream_t s = as_stream(stream);
+  // one ordinary step leaves valid activations; the state is reset so repeated attention stays at pos
+  hipError_t e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
+  if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
+  if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, nullptr, tokens_out, nullptr, s);
+  if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+
+  const int64_t per_rep = (kernel == BK_NORMF || kernel == BK_HEAD) ? 1 : cfg->n_layer;
+  hipStream_t cs = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t ee = hipSuccess;
+    for (int32_t r = 0; r < reps && ee == hipSuccess; ++r)
+      for (int64_t l = 0; l < per_rep && ee == hipSuccess; ++l)
+        ee = launch_batch_kernel(cfg, model, pool, P, l, kernel, nullptr, P.tok_scratch, nullptr, cs);
+    e = hipStreamEndCapture(cs, &graph);
+    if (ee != hipSuccess) e = ee;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  if (e == hipSuccess) e = hipGraphLaunch(exec, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  // one more ordinary step rewrites what the repeated launches disturbed
+  if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
+  if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, nullptr, tokens_out, nullptr, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (cs) (void)hipStreamDestroy(cs);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos_h[r] + 1;
   *ms_per_launch_h = ms / (float)(reps * per_rep);
   return LLMK_OK;
 }

@@ -105,6 +105,8 @@ def main() -> int:
                     help="times each kernel class's per-layer launches are replayed for its HIP-event timing")
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle steps in the CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("batch1", "batched"), default="batch1",
+                    help="batch1: the 8B-shaped single-sequence step (default); batched: 64 ragged sequences per step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -126,6 +128,8 @@ def main() -> int:
         return 3
     if args.copy_probe > 0:
         return copy_probe(args.copy_probe)
+    if args.workload == "batched":
+        return run_batched(args)
 
     s = synth.L8B
     max_steps_per_call = s.max_seq - N_PRE
@@ -242,6 +246,160 @@ def main() -> int:
     else:
         result["cpu_baseline"] = None
 
+    print(json.dumps(result), flush=True)
+    log(f"total {time.time() - t_start:.1f} s")
+    return 0
+
+
+BATCH = 64                      # sequences per batched step
+CTX_LO, CTX_HI = 512, 8192      # their context lengths, uniform
+BATCH_STEPS = 128               # steps the batched workload runs
+
+
+def batched_step_bytes(s, ctxs, i) -> int:
+    """Algorithmic HBM bytes of batched step i (row r attends ctx_r + i + 1 positions): every weight once,
+    each row's embedding row and attended K/V, the appended K/V, the gains."""
+    wsz, kvsz = 2, 2
+    d, qd, kvd, F, V, L = s.d, s.n_head * s.head_dim, s.n_kv * s.head_dim, s.hidden, s.vocab, s.n_layer
+    weights = L * (d * qd + 2 * d * kvd + qd * d + 3 * d * F) * wsz + V * d * wsz
+    emb = len(ctxs) * d * wsz
+    gains = (2 * L + 1) * d * 4
+    kv = sum(L * (int(c) + i + 1) * kvd * 2 * kvsz for c in ctxs) + len(ctxs) * L * kvd * 2 * kvsz
+    return weights + emb + gains + kv
+
+
+def batched_attention_bytes(s, ctxs) -> int:
+    """Algorithmic bytes of one batched attention launch at positions ctxs: each row's K and V of ctx + 1
+    positions, its raw q|k|v and RoPE row read, its appended K/V and its output written (hi and lo)."""
+    kvd, qd = s.n_kv * s.head_dim, s.n_head * s.head_dim
+    per_row_fixed = (qd + 2 * kvd) * 4 + s.head_dim * 4 + 2 * kvd * 2 + qd * 2 * 2
+    return sum((int(c) + 1) * kvd * 2 * 2 + per_row_fixed for c in ctxs)
+
+
+def run_batched(args) -> int:
+    import torch
+
+    import synth
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd import loader
+
+    s = synth.L8B.with_(name="llama-3-8b-shaped bf16, batched", max_seq=CTX_HI + BATCH_STEPS)
+    steps = args.steps if args.steps != 256 else BATCH_STEPS
+    if steps > BATCH_STEPS or args.warmup > BATCH_STEPS:
+        print(f"the batched workload has room for {BATCH_STEPS} steps per run", file=sys.stderr)
+        return 2
+    t_start = time.time()
+    log(f"generating {s.name} weights and the K/V source")
+    W = synth.model(s, seed=0)
+    ctxs = synth.ragged_contexts(BATCH, CTX_LO, CTX_HI, seed=3).tolist()
+    src = synth.kv_prefix(s, CTX_HI + synth.slot_window(BATCH - 1), seed=2)
+    first = synth.prompt(BATCH, s.vocab, stream=13).tolist()
+    slots = list(range(BATCH))
+    log(f"generated in {time.time() - t_start:.1f} s; uploading")
+    cfg = loader.config_from(s)
+    model = loader.upload_model(cfg, W)
+    pool = loader.new_pool(cfg, BATCH, s.max_seq)
+    src_dev = loader.upload_kv_source(src)
+    for r in range(BATCH):
+        loader.fill_prefix_window(pool, r, src_dev, synth.slot_window(r), ctxs[r])
+    del src_dev
+    dec = loader.BatchDecoder(cfg, model, pool, BATCH)
+    torch.cuda.synchronize()
+    log(f"resident in HBM after {time.time() - t_start:.1f} s (pool {sum(t.numel() for t in pool.k) * 4 / 1e9:.1f} GB)")
+
+    def reset():
+        for r in range(BATCH):
+            pool.slot_len[r] = ctxs[r]
+
+    def run(n, out):
+        reset()
+        st = dec.steps(slots, first, ctxs, n, out)
+        if st != llmk.OK:
+            raise RuntimeError(f"decode_steps_batch: {st} {llmk.status_name(st)}")
+
+    if args.warmup > 0:
+        run(args.warmup, torch.zeros(args.warmup * BATCH, dtype=torch.int32, device="cuda"))
+    toks = torch.zeros(steps * BATCH, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps, toks)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / steps
+    total_bytes = sum(batched_step_bytes(s, ctxs, i) for i in range(steps))
+    gbps = total_bytes / elapsed / 1e9
+    log(f"timed {steps} batched steps: {ms_per_step:.3f} ms/step, {BATCH * steps / elapsed:.0f} tokens/s, "
+        f"{gbps:.0f} GB/s algorithmic")
+
+    reset()
+    avg_ms = {}
+    for k, n in enumerate(llmk.BATCH_KERNEL_CLASSES):
+        st, ms = llmk.decode_batch_kernel_time(cfg, model, pool, slots, first, ctxs, k, args.kernel_reps,
+                                               dec.tokens_out, dec.ws)
+        if st != llmk.OK:
+            raise RuntimeError(f"decode_batch_kernel_time({n}): {st} {llmk.status_name(st)}")
+        avg_ms[n] = ms
+        reset()
+    log("avg kernel us: " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in avg_ms.items()))
+    at_bytes = batched_attention_bytes(s, ctxs)
+    at_gbps = at_bytes / (avg_ms["attention"] * 1e-3) / 1e9
+    per_layer = [n for n in llmk.BATCH_KERNEL_CLASSES if n not in ("norm_final", "head")]
+    kernel_sum_ms = sum(avg_ms[n] for n in per_layer) * s.n_layer + avg_ms["norm_final"] + avg_ms["head"]
+    tokens = toks.cpu().numpy().reshape(steps, BATCH)
+
+    result = {
+        "metric": "decode tokens/s at batch 64 (8B-shaped, ragged contexts) + achieved HBM GB/s vs peak",
+        "value": BATCH * steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama-3-8b-shaped greedy decode, 64 sequences per step, contexts uniform in "
+                               "512..8192 (seeded), bf16 weights and K/V, projections on bf16 matrix cores",
+                   "batch": BATCH, "contexts_mean": float(sum(ctxs) / BATCH), "contexts_min": min(ctxs),
+                   "contexts_max": max(ctxs), "weights": "bf16", "kv": "bf16", "accumulation": "f32",
+                   "activations_into_mfma": "bf16 hi + lo"},
+        "step_hbm_gbps": gbps,
+        "step_frac_of_peak": gbps / PEAK_HBM_GBPS,
+        "step_bytes_mean": total_bytes / steps,
+        "roofline": {"bound": "hbm", "kernel": "batched attention (attn_kernel, 64 rows)", "achieved": at_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": at_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "bytes_per_launch": at_bytes, "avg_launch_us": avg_ms["attention"] * 1e3},
+        "kernels_avg_us": {n: v * 1e3 for n, v in avg_ms.items()},
+        "kernel_sum_ms_per_step": kernel_sum_ms,
+        "first_tokens_row0": tokens[:8, 0].tolist(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = [0, 1]
+        n = 2
+        log(f"oracle baseline: {len(rows)} rows x {n} steps on the host cores")
+        m = oracle.Model(s, W)
+        tc0 = time.perf_counter()
+        agree = True
+        for r in rows:
+            c = m.new_cache(ctxs[r] + n)
+            st0 = synth.slot_window(r)
+            c.fill_prefix([(k[st0:st0 + ctxs[r]], v[st0:st0 + ctxs[r]]) for k, v in src])
+            t = first[r]
+            for i in range(n):
+                lg, _ = m.forward_token(t, ctxs[r] + i, c)
+                t = oracle.argmax(lg)[0]
+                agree = agree and (t == int(tokens[i, r]))
+        tc = time.perf_counter() - tc0
+        result["cpu_baseline"] = {"value": len(rows) * n / tc, "unit": "tokens/s", "cores": oracle.lib().orc_num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"rows {rows} of the same batch, {n} greedy steps each, one row at a time "
+                                            f"(fp64, OpenMP)",
+                                  "tokens_agree_with_gpu": agree}
+    else:
+        result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
     log(f"total {time.time() - t_start:.1f} s")
     return 0

@@ -366,6 +366,19 @@ int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model,
                                 int64_t token, int64_t pos, int32_t kernel, int32_t reps, int32_t* token_out,
                                 float* ms_per_launch_h, void* ws, int64_t len_ws, void* stream);
 
+/* Measurement aid for the batched step, as llmk_decode_kernel_time: the average duration of one launch of
+ * one kernel class of llmk_decode_step_batch. kernel: 0 attention-side RMSNorm, 1 q|k|v, 2 attention,
+ * 3 o, 4 FFN-side RMSNorm, 5 gate|up, 6 down, 7 final RMSNorm, 8 output head with argmax. Runs one
+ * ordinary batched step, replays that class's launches (every layer; the last two once) `reps` times in
+ * one graph between two HIP events on `stream`, then runs the ordinary step once more, so the call leaves
+ * the pool, tokens_out and every slot length exactly as llmk_decode_step_batch does (tokens_out: device
+ * int32 [batch]). Codes: as llmk_decode_step_batch; 578 if ms_per_launch_h is NULL or kernel is not 0..8;
+ * 561 if reps < 1; 564 if reps > 64. */
+int32_t llmk_decode_batch_kernel_time(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool,
+                                      int64_t batch, const int64_t* slots_h, const int64_t* tokens_h,
+                                      const int64_t* pos_h, int32_t kernel, int32_t reps, int32_t* tokens_out,
+                                      float* ms_per_launch_h, void* ws, int64_t len_ws, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
