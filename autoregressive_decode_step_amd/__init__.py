@@ -15,11 +15,14 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libllmk.so")
+# another build of the same library (same exported interface) may be named explicitly
+LIB_PATH = os.environ.get("LLMK_LIBRARY") or LIB_PATH
 
 OK = 560
 F32, BF16 = 0, 1
 ROPE_HALF_SPLIT, ROPE_INTERLEAVED = 0, 1
 W_IN_OUT, W_OUT_IN = 0, 1
+STEP_AUTO, STEP_PER_OP, STEP_PERSISTENT = 0, 1, 2
 WQ, WK, WV, WO, WGATE, WUP, WDOWN, GATTN, GFFN = range(9)
 LAYER_TENSORS = 9
 MAX_DIM = 1 << 24
@@ -43,7 +46,7 @@ class Config(ctypes.Structure):
     """llmk_config"""
     _fields_ = [("vocab", _i64), ("d", _i64), ("n_layer", _i64), ("n_head", _i64), ("n_kv", _i64),
                 ("head_dim", _i64), ("hidden", _i64), ("max_seq", _i64), ("eps", _f64), ("rope_base", _f64),
-                ("rope_layout", _i32), ("w_dtype", _i32), ("kv_dtype", _i32), ("w_layout", _i32)]
+                ("rope_layout", _i32), ("w_dtype", _i32), ("kv_dtype", _i32), ("w_layout", _i32), ("step_path", _i32)]
 
 
 class Tensor(ctypes.Structure):
@@ -250,9 +253,9 @@ def argmax(logits, rows, n, token, logit, ws, stream=None) -> int:
 # ---------------------------------------------------------------------------------------------------------
 
 def make_config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4,
-                rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16, w_layout=W_IN_OUT) -> Config:
+                rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16, w_layout=W_IN_OUT, step_path=0) -> Config:
     return Config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps, rope_base, rope_layout, w_dtype,
-                  kv_dtype, w_layout)
+                  kv_dtype, w_layout, step_path)
 
 
 def transpose(src, dst, rows, cols, stream=None) -> int:

@@ -93,6 +93,8 @@ int32_t config_check(const llmk_config* c) {
   if (!is_dtype(c->w_dtype) || !is_dtype(c->kv_dtype)) return LLMK_INVALID_ARGUMENT;
   if (c->rope_layout != LLMK_ROPE_HALF_SPLIT && c->rope_layout != LLMK_ROPE_INTERLEAVED) return LLMK_INVALID_ARGUMENT;
   if (c->w_layout != LLMK_W_IN_OUT && c->w_layout != LLMK_W_OUT_IN) return LLMK_INVALID_ARGUMENT;
+  if (c->step_path != LLMK_STEP_AUTO && c->step_path != LLMK_STEP_PER_OP && c->step_path != LLMK_STEP_PERSISTENT)
+    return LLMK_INVALID_ARGUMENT;
   if (!(c->eps > 0) || !isfinite(c->eps) || !(c->rope_base > 1.0) || !isfinite(c->rope_base))
     return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({c->vocab, c->d, c->n_layer, c->n_head, c->n_kv, c->head_dim, c->hidden, c->max_seq});
@@ -113,6 +115,8 @@ int32_t config_check(const llmk_config* c) {
       if (rowdot_plan(r, c->w_dtype == LLMK_BF16, GM_PLAIN) != 0) return LLMK_HEAD_SHAPE_INVALID;
     }
   }
+  if (c->step_path == LLMK_STEP_PERSISTENT && (c->w_dtype != LLMK_BF16 || c->w_layout != LLMK_W_OUT_IN))
+    return LLMK_INVALID_ARGUMENT;
   return LLMK_OK;
 }
 
@@ -135,12 +139,23 @@ struct DecodePlan {
   float* head_val = nullptr;
   int32_t* head_idx = nullptr;
   int32_t* tok_scratch = nullptr;   // kTimeMaxReps tokens: where repeated timing launches of the head write
+  // persistent step
+  StepLayer* step_layers = nullptr;     // [n_layer]
+  unsigned* step_sync = nullptr;        // barrier arrivals (64-bit) and the error flag, zero per call
+  float* step_val = nullptr;            // [kStepMaxWG] per-workgroup best logit
+  int32_t* step_idx = nullptr;
+  float* step_x = nullptr;              // activation versions of the persistent step (see StepParams)
+  float* step_qkv = nullptr;
+  float* step_att = nullptr;
+  float* step_u = nullptr;
+  int64_t step_x_stride = 0, step_qkv_stride = 0, step_att_stride = 0, step_u_stride = 0;
   int64_t bytes = 0;
   int n_gemv_counters = 0;
 };
 
 constexpr int kGemvTargetBlocks = 512;
 constexpr int kTimeMaxReps = 64;   // llmk_decode_kernel_time: at most this many replays of a kernel class
+constexpr int kStepMaxWG = 1024;   // the persistent step kernel's workgroups (one per CU), at most
 
 
 void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
@@ -197,6 +212,19 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.head_val = cv.take<float>(D.head.n_blocks);
   D.head_idx = cv.take<int32_t>(D.head.n_blocks);
   D.tok_scratch = cv.take<int32_t>(kTimeMaxReps);
+  D.step_layers = cv.take<StepLayer>(c->n_layer);
+  D.step_sync = cv.take<unsigned>(4);
+  D.step_val = cv.take<float>(kStepMaxWG);
+  D.step_idx = cv.take<int32_t>(kStepMaxWG);
+  auto stride64 = [](int64_t n) { return (n + 63) / 64 * 64; };   // 256-byte aligned versions
+  D.step_x_stride = stride64(d);
+  D.step_qkv_stride = stride64(qd + 2 * kvd);
+  D.step_att_stride = stride64(qd);
+  D.step_u_stride = stride64(F);
+  D.step_x = cv.take<float>((2 * c->n_layer + 1) * D.step_x_stride);
+  D.step_qkv = cv.take<float>(c->n_layer * D.step_qkv_stride);
+  D.step_att = cv.take<float>(c->n_layer * D.step_att_stride);
+  D.step_u = cv.take<float>(c->n_layer * D.step_u_stride);
   D.bytes = cv.off;
 }
 
@@ -415,6 +443,94 @@ hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv
     for (int k = K_QKV; k <= K_DOWN && e == hipSuccess; ++k) e = one(l, k);
   if (e == hipSuccess) e = one(0, K_HEAD);
   return e;
+}
+
+// ---- the persistent step ----
+
+int64_t step_vin_floats(const llmk_config* c) {
+  return std::max(std::max(c->d, c->n_head * c->head_dim), c->hidden);
+}
+
+// Workgroups of the persistent step for this call (0: run one kernel per operation). -1: refused.
+int step_workgroups(const llmk_config* c) {
+  if (c->step_path != LLMK_STEP_PERSISTENT) return 0;
+  int nwg = 0;
+  if (c->w_dtype == LLMK_BF16 && c->w_layout == LLMK_W_OUT_IN && c->n_layer <= STEP_MAX_LAYERS)
+    nwg = step_grid(c->kv_dtype == LLMK_BF16, (int)c->head_dim, step_vin_floats(c));
+  if (nwg > kStepMaxWG) nwg = 0;
+  if (nwg == 0 && c->step_path == LLMK_STEP_PERSISTENT) return -1;
+  return nwg;
+}
+
+// Prelude of a persistent call: zero the counters and the barrier words, set the state, fill the layer table.
+hipError_t step_prelude(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, DecodePlan& D,
+                        int32_t token, int32_t pos, hipStream_t s) {
+  hipError_t e = fill_u32_launch(D.counters, counters_total(c, D), 0u, s);
+  if (e == hipSuccess) e = fill_u32_launch(D.step_sync, 4, 0u, s);
+  if (e == hipSuccess) e = set_state_launch(D.state, token, pos, s);
+  for (int64_t l0 = 0; e == hipSuccess && l0 < c->n_layer; l0 += 8) {
+    StepTableChunk ch{};
+    ch.first = (int32_t)l0;
+    ch.count = (int32_t)std::min<int64_t>(8, c->n_layer - l0);
+    for (int32_t j = 0; j < ch.count; ++j) {
+      StepLayer& L = ch.layers[j];
+      const int64_t l = l0 + j;
+      const int ws[7] = {LLMK_WQ, LLMK_WK, LLMK_WV, LLMK_WO, LLMK_WGATE, LLMK_WUP, LLMK_WDOWN};
+      for (int t = 0; t < 7; ++t) L.w[t] = static_cast<const bf16_t*>(layer_t(m, l, ws[t]).ptr);
+      L.g1 = static_cast<const float*>(layer_t(m, l, LLMK_GATTN).ptr);
+      L.g2 = static_cast<const float*>(layer_t(m, l, LLMK_GFFN).ptr);
+      L.k = pool->k[l];
+      L.v = pool->v[l];
+    }
+    e = step_table_launch(D.step_layers, ch, s);
+  }
+  return e;
+}
+
+StepParams step_params(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, int64_t slot,
+                       DecodePlan& D, int nwg, float* logits, float* hidden, int32_t* token_out) {
+  StepParams p{};
+  p.layers = D.step_layers;
+  p.emb = static_cast<const bf16_t*>(m->emb.ptr);
+  p.w_out = static_cast<const bf16_t*>(m->w_out.ptr);
+  p.g_final = static_cast<const float*>(m->g_final.ptr);
+  p.rope_table = static_cast<const float*>(m->rope_table.ptr);
+  p.n_layer = (int32_t)c->n_layer;
+  p.d = (int32_t)c->d;
+  p.qd = (int32_t)(c->n_head * c->head_dim);
+  p.kvd = (int32_t)(c->n_kv * c->head_dim);
+  p.F = (int32_t)c->hidden;
+  p.V = (int32_t)c->vocab;
+  p.H = (int32_t)c->n_head;
+  p.Hkv = (int32_t)c->n_kv;
+  p.hd = (int32_t)c->head_dim;
+  p.rope_layout = c->rope_layout;
+  p.eps = (float)c->eps;
+  p.nwg = nwg;
+  p.kv_off = slot * pool->capacity * c->n_kv * c->head_dim;
+  p.attn_chunk = D.attn.chunk;
+  p.attn_sub_per_wg = D.attn.sub_per_wg;
+  p.attn_n_parts = D.attn.n_parts;
+  p.state = D.state;
+  p.x = D.step_x;
+  p.qkv = D.step_qkv;
+  p.att = D.step_att;
+  p.u = D.step_u;
+  p.x_stride = D.step_x_stride;
+  p.qkv_stride = D.step_qkv_stride;
+  p.att_stride = D.step_att_stride;
+  p.u_stride = D.step_u_stride;
+  p.attn_part = D.attn_part;
+  p.attn_cnt = D.counters + D.n_gemv_counters;
+  p.logits = logits;
+  p.hidden = hidden;
+  p.head_val = D.step_val;
+  p.head_idx = D.step_idx;
+  p.head_cnt = D.counters + D.n_gemv_counters + c->n_kv;
+  p.bar = reinterpret_cast<unsigned long long*>(D.step_sync);
+  p.err = reinterpret_cast<int32_t*>(D.step_sync + 2);
+  p.token_out = token_out;
+  return p;
 }
 
 // Common checks of decode_step / decode_steps, in the documented order.
@@ -967,10 +1083,20 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
   plan_decode(cfg, nullptr, D);
   if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
   plan_decode(cfg, ws, D);
+  const int nwg = step_workgroups(cfg);
+  if (nwg < 0) return LLMK_INVALID_ARGUMENT;
   hipStream_t s = as_stream(stream);
-  hipError_t e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
-  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
-  if (e == hipSuccess) e = enqueue_step(cfg, model, pool, slot, D, logits, token_out, hidden, s);
+  hipError_t e;
+  if (nwg > 0) {
+    e = step_prelude(cfg, model, pool, D, (int32_t)token, (int32_t)pos, s);
+    if (e == hipSuccess)
+      e = step_launch(step_params(cfg, model, pool, slot, D, nwg, logits, hidden, token_out),
+                      cfg->kv_dtype == LLMK_BF16, step_vin_floats(cfg), s);
+  } else {
+    e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
+    if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
+    if (e == hipSuccess) e = enqueue_step(cfg, model, pool, slot, D, logits, token_out, hidden, s);
+  }
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos + 1;
   return LLMK_OK;
@@ -991,9 +1117,16 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
   plan_decode(cfg, nullptr, D);
   if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
   plan_decode(cfg, ws, D);
+  const int nwg = step_workgroups(cfg);
+  if (nwg < 0) return LLMK_INVALID_ARGUMENT;
   hipStream_t s = as_stream(stream);
-  hipError_t e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
-  if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token0, (int32_t)pos0, s);
+  hipError_t e;
+  if (nwg > 0) {
+    e = step_prelude(cfg, model, pool, D, (int32_t)token0, (int32_t)pos0, s);
+  } else {
+    e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
+    if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token0, (int32_t)pos0, s);
+  }
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
 
   // capture one step (token and position come from the device state) and replay it n_steps times
@@ -1003,17 +1136,21 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
   e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e == hipSuccess) {
-    hipError_t ee = enqueue_step(cfg, model, pool, slot, D, nullptr, tokens_out, nullptr, cs);
+    hipError_t ee = nwg > 0 ? step_launch(step_params(cfg, model, pool, slot, D, nwg, nullptr, nullptr, tokens_out),
+                                          cfg->kv_dtype == LLMK_BF16, step_vin_floats(cfg), cs)
+                            : enqueue_step(cfg, model, pool, slot, D, nullptr, tokens_out, nullptr, cs);
     e = hipStreamEndCapture(cs, &graph);
     if (ee != hipSuccess) e = ee;
   }
   if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
   for (int64_t i = 0; e == hipSuccess && i < n_steps; ++i) e = hipGraphLaunch(exec, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
+  int32_t err = 0;
+  if (e == hipSuccess && nwg > 0) e = hipMemcpy(&err, D.step_sync + 2, sizeof(err), hipMemcpyDeviceToHost);
   if (exec) (void)hipGraphExecDestroy(exec);
   if (graph) (void)hipGraphDestroy(graph);
   if (cs) (void)hipStreamDestroy(cs);
-  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  if (e != hipSuccess || err != 0) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos0 + n_steps;
   return LLMK_OK;
 }

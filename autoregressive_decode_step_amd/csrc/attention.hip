@@ -1,358 +1,14 @@
-// Split-context grouped-query decode attention for gfx950.
-//
-// One query position; head h reads K/V head g = h / G (G = H / Hkv query heads share every K/V row, so
-// each row is read from HBM once for all G of them). The context is cut into parts of consecutive
-// tiles; a workgroup of 8 waves owns one (K/V head, part) and runs two tile streams of 4 waves, each
-// taking every other tile of the part with an online softmax of its own.
-//   - A tile of K and V rows is loaded cooperatively with 16-byte loads into registers while the
-//     previous tile is being computed, then written to LDS (rows padded by 16 B so that a lane reading
-//     its own row and lanes reading one row's consecutive elements are both bank-conflict free).
-//   - Scores: wave w of a stream takes query heads w, w+4; lane t computes q . K[t] from LDS (q
-//     broadcast from LDS), so no cross-lane reduction is needed per row. Softmax statistics are two
-//     wave reductions.
-//   - Output: lane groups take rows of the tile, lanes within a group own 16-byte slices of the head
-//     dimension; the groups are summed once per part (xor shuffles) and the two streams are combined
-//     through LDS.
-//   - Each part writes (max, sum, unnormalised output) per head; the last workgroup of a K/V head merges
-//     the parts by log-sum-exp in part order: m* = max m_c, out = sum_c e^(m_c - m*) o_c /
-//     sum_c e^(m_c - m*) l_c.
-// ("Inside the engine", "1. CausalLM": flash attention split across the context and reduced;
-// "The forward pass end to end", "The code": the per-head softmax attention it computes.)
-#include <float.h>
+// Split-context grouped-query decode attention for gfx950: the kernel and its plan (the workgroup body
+// is in attn_block.h).
 #include <stdlib.h>
 
-#include "kernels.h"
+#include "attn_block.h"
 
 namespace llmk {
 
-constexpr int ATTN_THREADS = 512;
-constexpr int ATTN_STREAMS = 2;                       // tile streams per workgroup
-constexpr int ATTN_SWAVES = 4;                        // waves per stream
-constexpr int ATTN_STHREADS = ATTN_SWAVES * 64;       // threads per stream
-constexpr int ATTN_MAXG_PER_WAVE = 2;                 // query heads per wave (G <= 8)
-
-// positions per tile for a row of `row_bytes`: at most 64, tile of one of K/V at most 16 KiB
-__host__ __device__ constexpr int attn_tile_rows(int row_bytes) {
-  return (16384 / row_bytes) < 64 ? (16384 / row_bytes) : 64;
-}
-
 template <typename T, int HD>
 __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) {
-  constexpr int EPV = 16 / (int)sizeof(T);               // elements per 16-byte vector
-  constexpr int RV = (HD + EPV - 1) / EPV;               // vectors per row (a partial vector when HD < EPV)
-  constexpr int ROWB = (HD * (int)sizeof(T) + 15) / 16 * 16;
-  constexpr int CH = attn_tile_rows(ROWB);               // positions per tile
-  constexpr int RS = RV + 1;                             // padded row stride in vectors
-  constexpr int NVT = 2 * CH * RV;                       // vectors in a K+V tile
-  constexpr int NVL = (NVT + ATTN_STHREADS - 1) / ATTN_STHREADS;   // per stream thread
-  constexpr int LPV = RV;                                // V phase: lanes per row (one 16-B vector each)
-  constexpr int RGV = 64 / LPV;                          // V phase: rows processed at once by a wave
-  constexpr int HDP = HD < 4 ? 4 : HD;
-
-  __shared__ uint4 s_kv[ATTN_STREAMS][2][CH][RS];
-  __shared__ float s_q[8][HDP];
-  __shared__ float s_p[ATTN_STREAMS][8][CH];
-  __shared__ T s_new[2][HDP];                            // the appended k and v row (decode), cache dtype
-  __shared__ float s_m1[8], s_l1[8], s_o1[8][HDP];       // stream 1's softmax state, for the combine
-  __shared__ int s_last;
-
-  const int G = p.H / p.Hkv;
-  const int kvh = blockIdx.y, part = blockIdx.x;
-  const int row = blockIdx.z;                             // batched decode: the sequence row
-  const bool batched = p.bstate != nullptr;
-  const int ctx = batched ? p.bstate->pos[row] + 1 : (p.state ? p.state->pos + 1 : p.ctx);
-  const int span = CH * p.sub_per_wg;
-  const int tb = part * span;
-  if (tb >= ctx) return;
-  const int te = min(tb + span, ctx);
-
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int st = wv / ATTN_SWAVES;                       // tile stream of this wave
-  const int wave = wv % ATTN_SWAVES;                     // wave within its stream
-  const int stid = threadIdx.x % ATTN_STHREADS;          // thread within its stream
-  const int64_t rstride = (int64_t)p.Hkv * HD;           // elements between positions
-  const int64_t rbase = batched ? (int64_t)p.bstate->slot[row] * p.slot_elems : 0;   // the row's slot region
-  const T* Kb = static_cast<const T*>(p.k) + rbase + (int64_t)kvh * HD;
-  const T* Vb = static_cast<const T*>(p.v) + rbase + (int64_t)kvh * HD;
-  const float* qkv_raw = p.qkv_raw ? p.qkv_raw + (batched ? (int64_t)row * p.qkv_stride : 0) : nullptr;
-  unsigned* counters = p.counters + (batched ? (int64_t)row * p.Hkv : 0);
-  const float scale = 1.0f / sqrtf((float)HD);
-
-  // cooperative tile load by one stream: vector idx -> (K or V, row, vector); rows past te are clamped
-  // to te - 1
-  uint4 reg[NVL];
-#define LLMK_LOAD_TILE(T0)                                                                        \
-  _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
-    const int idx = stid + k * ATTN_STHREADS;                                                     \
-    const int which = idx / (CH * RV), rem = idx % (CH * RV);                                     \
-    const int t = min((T0) + rem / RV, te - 1);                                                    \
-    const T* src = (which == 0 ? Kb : Vb) + (int64_t)t * rstride + (rem % RV) * EPV;               \
-    if (HD >= EPV) {                                                                              \
-      reg[k] = idx < NVT ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);          \
-    } else {                                                                                      \
-      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);                               \
-      reg[k] = make_uint4(idx < NVT ? s32[0] : 0u,                                                \
-                          (idx < NVT && HD * (int)sizeof(T) >= 8) ? s32[1] : 0u, 0u, 0u);          \
-    }                                                                                             \
-  }
-#define LLMK_STORE_TILE()                                                                         \
-  _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
-    const int idx = stid + k * ATTN_STHREADS;                                                     \
-    if (idx < NVT) {                                                                              \
-      const int which = idx / (CH * RV), rem = idx % (CH * RV);                                   \
-      s_kv[st][which][rem / RV][rem % RV] = reg[k];                                               \
-    }                                                                                             \
-  }
-
-  const int n_tiles = (te - tb + CH - 1) / CH;
-  // the first tile of each stream is requested before q is staged, so the two latencies overlap
-  if (st < n_tiles) { LLMK_LOAD_TILE(tb + st * CH) }
-
-  // q of the group into LDS. In the decode step q, k and v arrive unrotated (p.qkv_raw): every
-  // workgroup rotates its q heads by the position, and the workgroup whose part holds that position
-  // rotates k, rounds k and v to the cache dtype, appends them to the cache and patches its tile.
-  const int pos = ctx - 1;
-  const bool owner = qkv_raw && pos >= tb && pos < te;
-  if (qkv_raw) {
-    constexpr int HALF = HD / 2;
-    const float* tab = p.rope_table + (int64_t)pos * HALF * 2;
-    for (int i = threadIdx.x; i < (G + (owner ? 1 : 0)) * HALF; i += ATTN_THREADS) {
-      const int g = i / HALF, j = i % HALF;
-      const int ia = p.rope_layout == 0 ? j : 2 * j;
-      const int ib = p.rope_layout == 0 ? j + HALF : 2 * j + 1;
-      const float cs = tab[2 * j], sn = tab[2 * j + 1];
-      const float* src = g < G ? qkv_raw + (int64_t)(kvh * G + g) * HD
-                               : qkv_raw + (int64_t)p.H * HD + (int64_t)kvh * HD;   // this head's k
-      const float a = src[ia], b = src[ib];
-      const float ra = a * cs - b * sn, rb = a * sn + b * cs;
-      if (g < G) {
-        s_q[g][ia] = ra;
-        s_q[g][ib] = rb;
-      } else {
-        store_elem<T>(&s_new[0][0], ia, ra);
-        store_elem<T>(&s_new[0][0], ib, rb);
-      }
-    }
-    if (owner) {
-      const float* vsrc = qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD;
-      for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, vsrc[e]);
-    }
-    __syncthreads();
-    if (owner) {
-      const int64_t off = (int64_t)pos * p.Hkv * HD + (int64_t)kvh * HD;
-      for (int e = threadIdx.x; e < 2 * HD; e += ATTN_THREADS) {
-        const int w = e / HD, ee = e % HD;
-        (w == 0 ? static_cast<T*>(p.k_w) : static_cast<T*>(p.v_w))[rbase + off + ee] = s_new[w][ee];
-      }
-    }
-  } else {
-    for (int i = threadIdx.x; i < G * HD; i += ATTN_THREADS) s_q[i / HD][i % HD] = p.q[(int64_t)kvh * G * HD + i];
-  }
-
-  // per wave and query head: running max and sum (uniform), and a partial output per lane for the
-  // EPV elements of vector `vl` over the rows of row group `rg` (reduced over row groups at the end)
-  const int vl = lane % LPV, rg = lane / LPV;
-  float m_run[ATTN_MAXG_PER_WAVE], l_run[ATTN_MAXG_PER_WAVE], o[ATTN_MAXG_PER_WAVE][EPV];
-#pragma unroll
-  for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
-    m_run[gi] = -INFINITY;
-    l_run[gi] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < EPV; ++k) o[gi][k] = 0.0f;
-  }
-
-  // stream st takes tiles st, st + 2, st + 4, ... of the part; every thread runs all iterations so
-  // that the barriers match, a stream past its last tile idles
-  const int iters = (n_tiles + ATTN_STREAMS - 1) / ATTN_STREAMS;
-  for (int it = 0; it < iters; ++it) {
-    const int t0 = tb + (it * ATTN_STREAMS + st) * CH;
-    const bool act = t0 < te;
-    __syncthreads();                       // previous tiles fully consumed (and q in LDS on entry)
-    if (act) { LLMK_STORE_TILE() }
-    __syncthreads();
-    if (owner) {                           // the appended position: use the new row, not the stale one
-      if (act && pos >= t0 && pos < t0 + CH) {
-        for (int e = stid; e < 2 * HD; e += ATTN_STHREADS) {
-          const int w = e / HD, ee = e % HD;
-          reinterpret_cast<T*>(&s_kv[st][w][pos - t0][0])[ee] = s_new[w][ee];
-        }
-      }
-      __syncthreads();
-    }
-    {
-      const int tn = t0 + ATTN_STREAMS * CH;
-      if (tn < te) { LLMK_LOAD_TILE(tn) }   // next tile in flight while this one is computed
-    }
-    const int n = act ? min(CH, te - t0) : 0;
-
-    // scores and softmax statistics: wave w takes heads w, w + 4; lane t scores position t0 + t
-    float alpha_g[ATTN_MAXG_PER_WAVE];
-#pragma unroll
-    for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
-      const int g = wave + gi * ATTN_SWAVES;
-      alpha_g[gi] = 1.0f;
-      if (g < G && act) {
-        float s = -INFINITY;
-        if (lane < CH) {
-          float part8[EPV];
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) part8[e] = 0.0f;
-          const float* qg = s_q[g];
-#pragma unroll
-          for (int v = 0; v < RV; ++v) {
-            float kf[EPV];
-            if constexpr (sizeof(T) == 2) unpack<bf16_t, 8>(s_kv[st][0][lane][v], kf);
-            else unpack<float, 4>(s_kv[st][0][lane][v], kf);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e)
-              if (v * EPV + e < HD) part8[e] = fmaf(qg[v * EPV + e], kf[e], part8[e]);
-          }
-          float dot = 0.0f;
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) dot += part8[e];
-          if (lane < n) s = dot * scale;
-        }
-        const float m_new = fmaxf(m_run[gi], wave_max(s));
-        const float pr = (lane < n) ? expf(s - m_new) : 0.0f;
-        const float alpha = expf(m_run[gi] - m_new);
-        l_run[gi] = l_run[gi] * alpha + wave_sum(pr);
-        m_run[gi] = m_new;
-        alpha_g[gi] = alpha;
-        if (lane < CH) s_p[st][g][lane] = pr;
-      }
-    }
-    __syncthreads();
-    // o = alpha o + sum_t p_t V[t]: lane (rg, vl) accumulates rows rg, rg + RGV, ... of the tile
-#pragma unroll
-    for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
-      const int g = wave + gi * ATTN_SWAVES;
-      if (g < G && act) {
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) o[gi][k] *= alpha_g[gi];
-#pragma unroll 4
-        for (int t = rg; t < n; t += RGV) {
-          const float pt = s_p[st][g][t];
-          float vf[EPV];
-          if constexpr (sizeof(T) == 2) unpack<bf16_t, 8>(s_kv[st][1][t][vl], vf);
-          else unpack<float, 4>(s_kv[st][1][t][vl], vf);
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) o[gi][k] = fmaf(pt, vf[k], o[gi][k]);
-        }
-      }
-    }
-  }
-#undef LLMK_LOAD_TILE
-#undef LLMK_STORE_TILE
-
-  // reduce the partial outputs over the row groups of each wave (xor shuffles, fixed order)
-#pragma unroll
-  for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi)
-#pragma unroll
-    for (int k = 0; k < EPV; ++k)
-#pragma unroll
-      for (int off = LPV; off < 64; off <<= 1) o[gi][k] += __shfl_xor(o[gi][k], off, 64);
-
-  // ---- stream 1 hands its (max, sum, output) to stream 0 through LDS ----
-  if (st == 1) {
-#pragma unroll
-    for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
-      const int g = wave + gi * ATTN_SWAVES;
-      if (g < G) {
-        if (lane == 0) {
-          s_m1[g] = m_run[gi];
-          s_l1[g] = l_run[gi];
-        }
-        if (rg == 0) {
-#pragma unroll
-          for (int k = 0; k < EPV; ++k)
-            if (vl * EPV + k < HD) s_o1[g][vl * EPV + k] = o[gi][k];
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- this part's (max, sum, output) per head: stream 0 combines the two streams in LDS (each element
-  // read and rewritten by the same lane), then every thread writes consecutive floats of the part ----
-  if (st == 0) {
-#pragma unroll
-    for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
-      const int g = wave + gi * ATTN_SWAVES;
-      if (g < G) {
-        const float m1 = s_m1[g];                        // -inf when stream 1 had no tile
-        const float l1 = s_l1[g];
-        const float ms = fmaxf(m_run[gi], m1);
-        const float w0 = expf(m_run[gi] - ms);
-        const float w1 = m1 == -INFINITY ? 0.0f : expf(m1 - ms);
-        if (rg == 0) {
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) {
-            const int e = vl * EPV + k;
-            if (e < HD) s_o1[g][e] = fmaf(s_o1[g][e], w1, o[gi][k] * w0);
-          }
-        }
-        if (lane == 0) {
-          s_m1[g] = ms;
-          s_l1[g] = fmaf(l1, w1, l_run[gi] * w0);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const int64_t pstride = HD + 2;
-  float* part_base = p.part + (batched ? (int64_t)row * p.Hkv * p.n_parts * G * pstride : 0);
-  float* P = part_base + ((int64_t)kvh * p.n_parts + part) * G * pstride;
-  for (int i = threadIdx.x; i < G * pstride; i += ATTN_THREADS) {
-    const int g = i / pstride, j = i % pstride;
-    st_dev(&P[i], j == 0 ? s_m1[g] : j == 1 ? s_l1[g] : s_o1[g][j - 2]);
-  }
-
-  // ---- last workgroup of this K/V head: log-sum-exp merge of the parts, in part order ----
-  stores_done();
-  __syncthreads();
-  const int np = (ctx + span - 1) / span;
-  if (threadIdx.x == 0) s_last = (take_ticket(&counters[kvh]) == (unsigned)(np - 1));
-  __syncthreads();
-  if (!s_last) return;
-  // every thread issues all its loads at once (max, sum and its output element of every part), so the
-  // merge costs one round trip; parts are combined in part order
-  const float* PB = part_base + (int64_t)kvh * p.n_parts * G * pstride;
-  const int64_t cstride = (int64_t)G * pstride;
-  for (int idx = threadIdx.x; idx < G * HD; idx += ATTN_THREADS) {
-    const int g = idx / HD, e = idx % HD;
-    const float* pg = PB + (int64_t)g * pstride;
-    float mc[ATTN_MAX_PARTS], lc[ATTN_MAX_PARTS], oc[ATTN_MAX_PARTS];
-#pragma unroll
-    for (int c = 0; c < ATTN_MAX_PARTS; ++c) {
-      const int cc = c < np ? c : np - 1;
-      mc[c] = ld_dev(pg + cc * cstride + 0);
-      lc[c] = ld_dev(pg + cc * cstride + 1);
-      oc[c] = ld_dev(pg + cc * cstride + 2 + e);
-    }
-    float ms = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < ATTN_MAX_PARTS; ++c) ms = c < np ? fmaxf(ms, mc[c]) : ms;
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int c = 0; c < ATTN_MAX_PARTS; ++c) {
-      if (c < np) {
-        const float w = expf(mc[c] - ms);
-        L = fmaf(lc[c], w, L);
-        O = fmaf(oc[c], w, O);
-      }
-    }
-    const int64_t oi = (int64_t)(kvh * G + g) * HD + e;
-    if (p.out_hi) {
-      bf16_t hi, lo;
-      split_bf16(O / L, hi, lo);
-      p.out_hi[(int64_t)row * p.H * HD + oi] = hi;
-      p.out_lo[(int64_t)row * p.H * HD + oi] = lo;
-    } else {
-      p.out[oi] = O / L;
-    }
-  }
-  if (threadIdx.x == 0) reset_ticket(&counters[kvh]);
+  attn_block<T, HD>(p, blockIdx.y, blockIdx.x, blockIdx.z);
 }
 
 static int tile_rows(int kv_is_bf16, int hd) {

@@ -201,6 +201,60 @@ hipError_t attn_launch(const AttnParams& p, hipStream_t s);
 inline int64_t attn_part_floats(int64_t H, int64_t hd) { return (int64_t)ATTN_MAX_PARTS * H * (hd + 2); }
 
 // ------------------------------------------------------------------------------------------------
+// The persistent decode-step kernel (one launch per step, one workgroup per CU, grid barriers)
+// ------------------------------------------------------------------------------------------------
+
+struct StepLayer {
+  const bf16_t* w[7];      // wq, wk, wv, wo, gate, up, down, output-major
+  const float* g1;         // attention-side RMSNorm gain
+  const float* g2;         // FFN-side RMSNorm gain
+  void* k;                 // this layer's K and V pool buffers (slot 0)
+  void* v;
+};
+
+struct StepParams {
+  const StepLayer* layers;      // device table [n_layer]
+  const bf16_t* emb;
+  const bf16_t* w_out;
+  const float* g_final;
+  const float* rope_table;
+  int32_t n_layer, d, qd, kvd, F, V, H, Hkv, hd, rope_layout;
+  float eps;
+  int32_t nwg;                  // workgroups (one per CU)
+  int64_t kv_off;               // element offset of the slot in each pool buffer
+  int32_t attn_chunk, attn_sub_per_wg, attn_n_parts, pad0;
+  DecodeState* state;
+  // activations, one buffer version per write in a step (a version is read only after it is written, so
+  // no L2 can hold a stale copy of it): x [2 n_layer + 1][x_stride], q|k|v, attention output and u
+  // [n_layer][*_stride]
+  float* x;
+  float* qkv;
+  float* att;
+  float* u;
+  int64_t x_stride, qkv_stride, att_stride, u_stride;
+  float* attn_part;
+  unsigned* attn_cnt;           // [Hkv]
+  float* logits;                // optional [V]
+  float* hidden;                // optional [n_layer][d]
+  float* head_val;              // [nwg]
+  int32_t* head_idx;
+  unsigned* head_cnt;
+  unsigned long long* bar;      // grid barrier arrivals, zero at the start of a call
+  int32_t* err;                 // set when a barrier wait gives up
+  int32_t* token_out;           // token of step s at token_out[s]
+};
+
+constexpr int STEP_MAX_LAYERS = 128;   // layers the persistent step kernel supports
+// Workgroups the step kernel runs with on the current device (0 if it cannot hold one per CU).
+int step_grid(int kv_is_bf16, int hd, int64_t vin_floats);
+hipError_t step_launch(const StepParams& p, int kv_is_bf16, int64_t vin_floats, hipStream_t s);
+struct StepTableChunk {
+  StepLayer layers[8];
+  int32_t first, count;
+};
+hipError_t step_table_launch(StepLayer* dst, const StepTableChunk& chunk, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------------
 // Elementwise and small kernels
 // ------------------------------------------------------------------------------------------------
 

@@ -16,14 +16,14 @@ _LAYER_MAP = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("gate", "
               ("down", "w_down"), ("n1", "g_attn"), ("n2", "g_ffn"))
 
 
-def config_from(shape, w_layout=W_OUT_IN) -> Config:
+def config_from(shape, w_layout=W_OUT_IN, step_path=0) -> Config:
     """llmk_config from any object with vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps,
     rope_base, rope_layout, w_dtype ('f32'/'bf16') and kv_dtype attributes. upload_model repacks the
-    projections to match w_layout."""
+    projections to match w_layout. step_path: 0 auto, 1 one kernel per operation, 2 persistent."""
     code = {"f32": F32, "bf16": BF16}
     return make_config(shape.vocab, shape.d, shape.n_layer, shape.n_head, shape.n_kv, shape.head_dim, shape.hidden,
                        shape.max_seq, shape.eps, shape.rope_base, shape.rope_layout, code[shape.w_dtype],
-                       code[shape.kv_dtype], w_layout)
+                       code[shape.kv_dtype], w_layout, step_path)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:

@@ -86,6 +86,15 @@ typedef enum { LLMK_ROPE_HALF_SPLIT = 0, LLMK_ROPE_INTERLEAVED = 1 } llmk_rope_l
  * second streams faster and is what llmk_transpose produces, once, at load time. */
 typedef enum { LLMK_W_IN_OUT = 0, LLMK_W_OUT_IN = 1 } llmk_weight_layout;
 
+/* How llmk_decode_step / llmk_decode_steps run the step of one sequence. Both compute the same step
+ * (the same arithmetic up to the order of fp32 sums). The persistent form needs bf16 weights in
+ * LLMK_W_OUT_IN and a device that holds one of its workgroups per CU.
+ *   LLMK_STEP_AUTO       the library's choice for this device and shape (currently one kernel per operation)
+ *   LLMK_STEP_PER_OP     one kernel per operation: 5 per layer (q|k|v, attention, o, gate|up, down) + head
+ *   LLMK_STEP_PERSISTENT one kernel per step, the operations separated by grid barriers; refused (578)
+ *                        where it cannot run */
+typedef enum { LLMK_STEP_AUTO = 0, LLMK_STEP_PER_OP = 1, LLMK_STEP_PERSISTENT = 2 } llmk_step_path;
+
 /* ------------------------------------------------------------------------- */
 /* Contract: host-only, no device needed ([llmk] "Status vocabulary and the    */
 /* shape checks (contract)": four dimension checks, one per consumer).        */
@@ -226,6 +235,7 @@ typedef struct {
   int32_t w_dtype;     /* llmk_dtype of every weight matrix and the embedding table */
   int32_t kv_dtype;    /* llmk_dtype of the K/V pool */
   int32_t w_layout;    /* llmk_weight_layout of the seven per-layer projections */
+  int32_t step_path;   /* llmk_step_path */
 } llmk_config;
 
 /* A device tensor and its element count. */

@@ -267,9 +267,11 @@ def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head):
 
 
 def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4, rope_layout=0,
-                 w_dtype=0, kv_dtype=0, w_layout=0):
+                 w_dtype=0, kv_dtype=0, w_layout=0, step_path=0):
     import math
     if rope_layout not in (0, 1) or w_dtype not in (0, 1) or kv_dtype not in (0, 1) or w_layout not in (0, 1):
+        return INVALID
+    if step_path not in (0, 1, 2):
         return INVALID
     if not (eps > 0 and math.isfinite(eps)) or not (rope_base > 1 and math.isfinite(rope_base)):
         return INVALID
@@ -290,6 +292,8 @@ def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps
         for k in (d, n_head * head_dim, hidden):
             if not any((k // kw) % vec == 0 and k % kw == 0 and -(-(k // kw) // (64 * vec)) <= 8 for kw in (1, 2, 4)):
                 return HEAD_SHAPE
+    if step_path == 2 and (w_dtype != 1 or w_layout != 1):
+        return INVALID    # the persistent step runs bf16 output-major weights only
     return OK
 
 

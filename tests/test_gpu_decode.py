@@ -82,8 +82,8 @@ def compare_runs(o, g, label):
     say(f"{label}: {len(toks_in)} steps, worst logits err {worst_l:.2e}, worst hidden err {worst_h:.2e}")
 
 
-def build(shape, W, n_slots=1, capacity=None, w_layout=llmk.W_OUT_IN):
-    cfg = loader.config_from(shape, w_layout)
+def build(shape, W, n_slots=1, capacity=None, w_layout=llmk.W_OUT_IN, step_path=llmk.STEP_AUTO):
+    cfg = loader.config_from(shape, w_layout, step_path)
     model = loader.upload_model(cfg, W)
     pool = loader.new_pool(cfg, n_slots, capacity or shape.max_seq)
     return cfg, model, pool, loader.Decoder(cfg, model, pool)
@@ -251,14 +251,52 @@ def q06():
     return s, W
 
 
-@pytest.mark.parametrize("w_layout", [llmk.W_IN_OUT, llmk.W_OUT_IN])
-def test_q06_short_prefix_matches_oracle(q06, w_layout):
+@pytest.mark.parametrize("w_layout,step_path", [(llmk.W_IN_OUT, llmk.STEP_AUTO), (llmk.W_OUT_IN, llmk.STEP_PER_OP),
+                                                (llmk.W_OUT_IN, llmk.STEP_PERSISTENT)])
+def test_q06_short_prefix_matches_oracle(q06, w_layout, step_path):
     s, W = q06
     m = oracle.Model(s, W)
     prompt = synth.prompt(8, s.vocab).tolist()
     o = oracle_run(m, s, prompt, n_greedy=3, max_seq=64)
-    cfg, model, pool, dec = build(s, W, capacity=s.max_seq, w_layout=w_layout)
-    compare_runs(o, gpu_teacher_forced(dec, s, o[0], 0), f"q06 8-token prefix weights={w_layout}")
+    cfg, model, pool, dec = build(s, W, capacity=s.max_seq, w_layout=w_layout, step_path=step_path)
+    compare_runs(o, gpu_teacher_forced(dec, s, o[0], 0), f"q06 8-token prefix weights={w_layout} path={step_path}")
+    # free-running from the prompt's last token, graph replay
+    pool.slot_len[0] = len(prompt) - 1
+    toks = torch.zeros(4, dtype=torch.int32, device="cuda")
+    assert dec.steps(prompt[-1], len(prompt) - 1, 4, toks) == llmk.OK
+    assert host(toks).tolist() == o[3][len(prompt) - 1:]
+
+
+TINY_BF16 = synth.TINY.with_(name="tiny-llama bf16 weights", w_dtype="bf16")
+
+
+@pytest.mark.parametrize("layout", [synth.ROPE_HALF_SPLIT, synth.ROPE_INTERLEAVED])
+def test_tiny_bf16_persistent_step_matches_oracle(layout):
+    """The persistent step on the toy shape (bf16 weights): teacher-forced steps against the oracle, then
+    free-running through graph replays, and the K/V it leaves equal to the per-operation path's."""
+    s = TINY_BF16.with_(rope_layout=layout)
+    W = synth.model(s, seed=0)
+    m = oracle.Model(s, W)
+    prompt = synth.prompt(6, s.vocab, stream=21).tolist()
+    o = oracle_run(m, s, prompt, n_greedy=6)
+    cfg, model, pool, dec = build(s, W, step_path=llmk.STEP_PERSISTENT)
+    compare_runs(o, gpu_teacher_forced(dec, s, o[0], 0), f"tiny bf16 persistent layout={layout}")
+    cfg2, model2, pool2, dec2 = build(s, W, step_path=llmk.STEP_PER_OP)
+    for pos, t in enumerate(prompt[:-1]):
+        assert dec2.step(t, pos) == llmk.OK
+    toks = torch.zeros(8, dtype=torch.int32, device="cuda")
+    assert dec2.steps(prompt[-1], len(prompt) - 1, 8, toks) == llmk.OK
+    pool.slot_len[0] = len(prompt) - 1
+    toks_p = torch.zeros(8, dtype=torch.int32, device="cuda")
+    assert dec.steps(prompt[-1], len(prompt) - 1, 8, toks_p) == llmk.OK
+    assert host(toks_p).tolist() == host(toks).tolist()
+    assert host(toks_p).tolist()[:6] == o[3][len(prompt) - 1:len(prompt) - 1 + 6]
+    n = len(prompt) - 1 + 8
+    for l in range(s.n_layer):
+        for which in ("k", "v"):
+            a = host(pool.slot_view(l, 0, which))[:n]
+            b = host(pool2.slot_view(l, 0, which))[:n]
+            assert rel_err(a, b) <= TOL
 
 
 def test_q06_full_context_matches_oracle(q06):
