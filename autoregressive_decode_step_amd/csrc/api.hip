@@ -141,13 +141,19 @@ struct DecodePlan {
   int32_t* tok_scratch = nullptr;   // kTimeMaxReps tokens: where repeated timing launches of the head write
   // persistent step
   StepLayer* step_layers = nullptr;     // [n_layer]
-  unsigned* step_sync = nullptr;        // barrier arrivals (64-bit) and the error flag, zero per call
+  int32_t* step_err = nullptr;          // error flag, zero per call
+  unsigned* step_cnt = nullptr;         // the head's ticket
   float* step_val = nullptr;            // [kStepMaxWG] per-workgroup best logit
   int32_t* step_idx = nullptr;
-  float* step_x = nullptr;              // activation versions of the persistent step (see StepParams)
-  float* step_qkv = nullptr;
-  float* step_att = nullptr;
-  float* step_u = nullptr;
+  uint64_t* step_tagged = nullptr;      // the tagged activations below, one region cleared per call
+  int64_t step_tagged_n = 0;
+  uint64_t* step_x = nullptr;           // (value, tag) activations of the persistent step (see StepParams)
+  uint64_t* step_qkv = nullptr;
+  uint64_t* step_att = nullptr;
+  uint64_t* step_u = nullptr;
+  uint64_t* step_part = nullptr;        // attention parts as (value, tag) pairs
+  uint32_t* step_flags = nullptr;       // readiness flags [n_layer][step_fl_stride]
+  int64_t step_fl_stride = 0;
   int64_t step_x_stride = 0, step_qkv_stride = 0, step_att_stride = 0, step_u_stride = 0;
   int64_t bytes = 0;
   int n_gemv_counters = 0;
@@ -208,23 +214,33 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.logits = cv.take<float>(c->vocab);
   D.partial = cv.take<float>(part > 0 ? part : 1);
   D.counters = cv.take<unsigned>(ncnt + c->n_kv + 1);
-  D.attn_part = cv.take<float>((int64_t)D.attn.n_parts * c->n_head * (c->head_dim + 2));
+  D.attn_part = cv.take<float>(attn_part_floats(c->n_head, c->head_dim));
   D.head_val = cv.take<float>(D.head.n_blocks);
   D.head_idx = cv.take<int32_t>(D.head.n_blocks);
   D.tok_scratch = cv.take<int32_t>(kTimeMaxReps);
   D.step_layers = cv.take<StepLayer>(c->n_layer);
-  D.step_sync = cv.take<unsigned>(4);
+  D.step_err = cv.take<int32_t>(4);
+  D.step_cnt = cv.take<unsigned>(1);
   D.step_val = cv.take<float>(kStepMaxWG);
   D.step_idx = cv.take<int32_t>(kStepMaxWG);
-  auto stride64 = [](int64_t n) { return (n + 63) / 64 * 64; };   // 256-byte aligned versions
-  D.step_x_stride = stride64(d);
-  D.step_qkv_stride = stride64(qd + 2 * kvd);
-  D.step_att_stride = stride64(qd);
-  D.step_u_stride = stride64(F);
-  D.step_x = cv.take<float>((2 * c->n_layer + 1) * D.step_x_stride);
-  D.step_qkv = cv.take<float>(c->n_layer * D.step_qkv_stride);
-  D.step_att = cv.take<float>(c->n_layer * D.step_att_stride);
-  D.step_u = cv.take<float>(c->n_layer * D.step_u_stride);
+  auto stride32 = [](int64_t n) { return (n + 31) / 32 * 32; };   // 256-byte aligned versions
+  D.step_x_stride = stride32(d);
+  D.step_qkv_stride = stride32(qd + 2 * kvd);
+  D.step_att_stride = stride32(qd);
+  D.step_u_stride = stride32(F);
+  const int64_t nx = 2 * c->n_layer * D.step_x_stride, nq = c->n_layer * D.step_qkv_stride;
+  const int64_t na = c->n_layer * D.step_att_stride, nu = c->n_layer * D.step_u_stride;
+  const int64_t np = attn_part_floats(c->n_head, c->head_dim);
+  D.step_fl_stride = (4 * kStepMaxWG + c->n_head + c->n_kv * ATTN_MAX_PARTS + 1) / 2 * 2;
+  const int64_t nf = c->n_layer * D.step_fl_stride / 2;   // in 8-byte units
+  D.step_tagged_n = nx + nq + na + nu + np + nf;
+  D.step_tagged = cv.take<uint64_t>(D.step_tagged_n);
+  D.step_x = D.step_tagged;
+  D.step_qkv = D.step_x + nx;
+  D.step_att = D.step_qkv + nq;
+  D.step_u = D.step_att + na;
+  D.step_part = D.step_u + nu;
+  D.step_flags = reinterpret_cast<uint32_t*>(D.step_part + np);
   D.bytes = cv.off;
 }
 
@@ -447,26 +463,34 @@ hipError_t enqueue_step(const llmk_config* c, const llmk_model* m, const llmk_kv
 
 // ---- the persistent step ----
 
-int64_t step_vin_floats(const llmk_config* c) {
-  return std::max(std::max(c->d, c->n_head * c->head_dim), c->hidden);
+// Whether the persistent step supports this shape (device aside): bf16 output-major weights, rows a whole
+// number of 16-byte loads, every projection input within the LDS it stages into, at most 8 query heads per
+// K/V head (the attention block's limit).
+bool step_shape_ok(const llmk_config* c, int nwg) {
+  const int64_t qd = c->n_head * c->head_dim;
+  if (c->w_dtype != LLMK_BF16 || c->w_layout != LLMK_W_OUT_IN || c->n_layer > STEP_MAX_LAYERS) return false;
+  if (c->d % 8 || qd % 8 || c->hidden % 8) return false;
+  if (std::max(std::max(c->d, qd), c->hidden) > STEP_MAX_VIN) return false;
+  if (c->n_head / c->n_kv > 8) return false;
+  return nwg > 0 && (c->d + nwg - 1) / nwg <= STEP_MAX_RES;
 }
 
 // Workgroups of the persistent step for this call (0: run one kernel per operation). -1: refused.
 int step_workgroups(const llmk_config* c) {
   if (c->step_path != LLMK_STEP_PERSISTENT) return 0;
-  int nwg = 0;
-  if (c->w_dtype == LLMK_BF16 && c->w_layout == LLMK_W_OUT_IN && c->n_layer <= STEP_MAX_LAYERS)
-    nwg = step_grid(c->kv_dtype == LLMK_BF16, (int)c->head_dim, step_vin_floats(c));
-  if (nwg > kStepMaxWG) nwg = 0;
+  int nwg = step_grid(c->kv_dtype == LLMK_BF16, (int)c->head_dim);
+  if (nwg > kStepMaxWG || !step_shape_ok(c, nwg)) nwg = 0;
   if (nwg == 0 && c->step_path == LLMK_STEP_PERSISTENT) return -1;
   return nwg;
 }
 
-// Prelude of a persistent call: zero the counters and the barrier words, set the state, fill the layer table.
+// Prelude of a persistent call: zero the tickets, the error flag and the tagged activations, set the
+// state, fill the layer table.
 hipError_t step_prelude(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, DecodePlan& D,
                         int32_t token, int32_t pos, hipStream_t s) {
-  hipError_t e = fill_u32_launch(D.counters, counters_total(c, D), 0u, s);
-  if (e == hipSuccess) e = fill_u32_launch(D.step_sync, 4, 0u, s);
+  hipError_t e = fill_u32_launch(D.step_cnt, 1, 0u, s);
+  if (e == hipSuccess) e = fill_u32_launch(reinterpret_cast<unsigned*>(D.step_err), 4, 0u, s);
+  if (e == hipSuccess) e = fill_u32_launch(reinterpret_cast<unsigned*>(D.step_tagged), 2 * D.step_tagged_n, 0u, s);
   if (e == hipSuccess) e = set_state_launch(D.state, token, pos, s);
   for (int64_t l0 = 0; e == hipSuccess && l0 < c->n_layer; l0 += 8) {
     StepTableChunk ch{};
@@ -509,8 +533,6 @@ StepParams step_params(const llmk_config* c, const llmk_model* m, const llmk_kv_
   p.nwg = nwg;
   p.kv_off = slot * pool->capacity * c->n_kv * c->head_dim;
   p.attn_chunk = D.attn.chunk;
-  p.attn_sub_per_wg = D.attn.sub_per_wg;
-  p.attn_n_parts = D.attn.n_parts;
   p.state = D.state;
   p.x = D.step_x;
   p.qkv = D.step_qkv;
@@ -520,15 +542,15 @@ StepParams step_params(const llmk_config* c, const llmk_model* m, const llmk_kv_
   p.qkv_stride = D.step_qkv_stride;
   p.att_stride = D.step_att_stride;
   p.u_stride = D.step_u_stride;
-  p.attn_part = D.attn_part;
-  p.attn_cnt = D.counters + D.n_gemv_counters;
+  p.attn_part = D.step_part;
   p.logits = logits;
   p.hidden = hidden;
   p.head_val = D.step_val;
   p.head_idx = D.step_idx;
-  p.head_cnt = D.counters + D.n_gemv_counters + c->n_kv;
-  p.bar = reinterpret_cast<unsigned long long*>(D.step_sync);
-  p.err = reinterpret_cast<int32_t*>(D.step_sync + 2);
+  p.head_cnt = D.step_cnt;
+  p.flags = D.step_flags;
+  p.fl_stride = D.step_fl_stride;
+  p.err = D.step_err;
   p.token_out = token_out;
   return p;
 }
@@ -1091,7 +1113,7 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
     e = step_prelude(cfg, model, pool, D, (int32_t)token, (int32_t)pos, s);
     if (e == hipSuccess)
       e = step_launch(step_params(cfg, model, pool, slot, D, nwg, logits, hidden, token_out),
-                      cfg->kv_dtype == LLMK_BF16, step_vin_floats(cfg), s);
+                      cfg->kv_dtype == LLMK_BF16, s);
   } else {
     e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
     if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
@@ -1137,7 +1159,7 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
   if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e == hipSuccess) {
     hipError_t ee = nwg > 0 ? step_launch(step_params(cfg, model, pool, slot, D, nwg, nullptr, nullptr, tokens_out),
-                                          cfg->kv_dtype == LLMK_BF16, step_vin_floats(cfg), cs)
+                                          cfg->kv_dtype == LLMK_BF16, cs)
                             : enqueue_step(cfg, model, pool, slot, D, nullptr, tokens_out, nullptr, cs);
     e = hipStreamEndCapture(cs, &graph);
     if (ee != hipSuccess) e = ee;
@@ -1146,7 +1168,7 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
   for (int64_t i = 0; e == hipSuccess && i < n_steps; ++i) e = hipGraphLaunch(exec, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   int32_t err = 0;
-  if (e == hipSuccess && nwg > 0) e = hipMemcpy(&err, D.step_sync + 2, sizeof(err), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && nwg > 0) e = hipMemcpy(&err, D.step_err, sizeof(err), hipMemcpyDeviceToHost);
   if (exec) (void)hipGraphExecDestroy(exec);
   if (graph) (void)hipGraphDestroy(graph);
   if (cs) (void)hipStreamDestroy(cs);

@@ -8,7 +8,8 @@ namespace llmk {
 
 template <typename T, int HD>
 __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) {
-  attn_block<T, HD>(p, blockIdx.y, blockIdx.x, blockIdx.z);
+  __shared__ uint4 tiles[attn_tile_vecs<T, HD>()];
+  attn_block<T, HD>(p, blockIdx.y, blockIdx.x, blockIdx.z, tiles);
 }
 
 static int tile_rows(int kv_is_bf16, int hd) {

@@ -38,11 +38,72 @@ __host__ __device__ constexpr int attn_tile_rows(int row_bytes) {
   return (16384 / row_bytes) < 64 ? (16384 / row_bytes) : 64;
 }
 
+// 16-byte vectors of the LDS tile buffer attn_block needs for cache element type T and head size HD
+template <typename T, int HD>
+__host__ __device__ constexpr int attn_tile_vecs() {
+  return ATTN_STREAMS * 2 * attn_tile_rows((HD * (int)sizeof(T) + 15) / 16 * 16) *
+         (((HD + 16 / (int)sizeof(T) - 1) / (16 / (int)sizeof(T))) + 1);
+}
+
+
+// (value, tag) pairs: the value's fp32 bits in the low word, the tag in the high word; one 8-byte store, so
+// a reader sees both or neither
+__device__ __forceinline__ void st_tag(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t tag_of(uint64_t v) { return (uint32_t)(v >> 32); }
+__device__ __forceinline__ float val_of(uint64_t v) { return __uint_as_float((uint32_t)v); }
+
+// Bounded wait: false once the wait has lasted longer than `ticks` of the 100 MHz real-time counter or
+// another workgroup has given up (*err != 0); then *err is set, so every other waiter stops too.
+constexpr uint64_t TAG_WAIT_TICKS = 20000000ull;   // 200 ms
+__device__ __forceinline__ bool tag_wait_more(int32_t* err, uint64_t t0, unsigned& n) {
+  __builtin_amdgcn_s_sleep(1);
+  if ((++n & 15u) == 0u) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > TAG_WAIT_TICKS) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+  }
+  return true;
+}
+
+// Wait until flags[0..n) all equal tag (each producer workgroup stores its flag once its data is stored;
+// the data carries its own tag, so a flag only says when reading the data is worth it). Every thread of
+// the workgroup calls it; thread t watches flags t, t + ATTN_THREADS, ... It ends with a barrier.
+__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t tag, int32_t* err, bool& failed) {
+  if (!failed) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned spins = 0;
+    for (int i = threadIdx.x; i < n && !failed; i += ATTN_THREADS)
+      while ((uint32_t)ld_dev(reinterpret_cast<const int*>(flags) + i) != tag)
+        if (!tag_wait_more(err, t0, spins)) {
+          failed = true;
+          break;
+        }
+  }
+  __syncthreads();
+}
+
+// this workgroup's flag: after a barrier (every wave's stores issued), one store
+__device__ __forceinline__ void set_flag(uint32_t* flag, uint32_t tag) {
+  __syncthreads();
+  if (threadIdx.x == 0) st_dev(reinterpret_cast<int*>(flag), (int)tag);
+}
+
 // One workgroup's share of the attention: context part `part` of K/V head `kvh` of batch row `row` (row 0
 // for a single sequence). Every thread of the workgroup (ATTN_THREADS) must call it with the same
-// arguments; it returns at the same point for all of them.
-template <typename T, int HD>
-__device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, const int part, const int row) {
+// arguments; it returns at the same point for all of them. `tiles` is LDS of attn_tile_vecs<T, HD>()
+// 16-byte vectors.
+// TAG: the decode step's persistent form. q|k|v come as (value, tag) pairs from p.qkv_tag and are waited
+// for until they carry p.tag; the merged output goes to p.out_tag as (value, p.tag) pairs.
+template <typename T, int HD, bool TAG = false>
+__device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, const int part, const int row,
+                                           uint4* tiles) {
   constexpr int EPV = 16 / (int)sizeof(T);               // elements per 16-byte vector
   constexpr int RV = (HD + EPV - 1) / EPV;               // vectors per row (a partial vector when HD < EPV)
   constexpr int ROWB = (HD * (int)sizeof(T) + 15) / 16 * 16;
@@ -54,8 +115,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   constexpr int RGV = 64 / LPV;                          // V phase: rows processed at once by a wave
   constexpr int HDP = HD < 4 ? 4 : HD;
 
-  __shared__ uint4 s_kv[ATTN_STREAMS][2][CH][RS];
+  uint4 (&s_kv)[ATTN_STREAMS][2][CH][RS] = *reinterpret_cast<uint4 (*)[ATTN_STREAMS][2][CH][RS]>(tiles);
   __shared__ float s_q[8][HDP];
+  __shared__ float s_raw[TAG ? (8 + 2) * HDP : 1];     // TAG: this group's q heads, k and v as waited for
   __shared__ float s_p[ATTN_STREAMS][8][CH];
   __shared__ T s_new[2][HDP];                            // the appended k and v row (decode), cache dtype
   __shared__ float s_m1[8], s_l1[8], s_o1[8][HDP];       // stream 1's softmax state, for the combine
@@ -92,11 +154,11 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     const int t = min((T0) + rem / RV, te - 1);                                                    \
     const T* src = (which == 0 ? Kb : Vb) + (int64_t)t * rstride + (rem % RV) * EPV;               \
     if (HD >= EPV) {                                                                              \
-      reg[k] = idx < NVT ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);          \
+      reg[k] = idx < NVT ? gload<uint4>(src) : make_uint4(0, 0, 0, 0);                              \
     } else {                                                                                      \
-      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);                               \
-      reg[k] = make_uint4(idx < NVT ? s32[0] : 0u,                                                \
-                          (idx < NVT && HD * (int)sizeof(T) >= 8) ? s32[1] : 0u, 0u, 0u);          \
+      reg[k] = make_uint4(idx < NVT ? gload<uint32_t>(src) : 0u,                                  \
+                          (idx < NVT && HD * (int)sizeof(T) >= 8) ? gload<uint32_t>(src + 4 / sizeof(T)) : 0u, \
+                          0u, 0u);                                                                \
     }                                                                                             \
   }
 #define LLMK_STORE_TILE()                                                                         \
@@ -116,8 +178,44 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   // workgroup rotates its q heads by the position, and the workgroup whose part holds that position
   // rotates k, rounds k and v to the cache dtype, appends them to the cache and patches its tile.
   const int pos = ctx - 1;
-  const bool owner = qkv_raw && pos >= tb && pos < te;
-  if (qkv_raw) {
+  const bool owner = (TAG || qkv_raw) && pos >= tb && pos < te;
+  if constexpr (TAG) {
+    // wait for the q|k|v producers' flags, then for this group's q heads, k and v: every thread loads all
+    // of its values, then reloads until each carries the step's tag
+    bool fl_failed = false;
+    wait_flags(p.qkv_flags, p.n_qkv_flags, p.tag, p.err, fl_failed);
+    constexpr int NPT = ((8 + 2) * HDP + ATTN_THREADS - 1) / ATTN_THREADS;
+    const int nval = (G + 2) * HD;
+    const uint64_t* src[NPT];
+    uint64_t got[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int i = threadIdx.x + k * ATTN_THREADS;
+      const int g = i / HD, e = i % HD;
+      const int64_t idx = g < G ? (int64_t)(kvh * G + g) * HD + e
+                                : (int64_t)(p.H + (g - G) * p.Hkv) * HD + (int64_t)kvh * HD + e;
+      src[k] = i < nval ? p.qkv_tag + idx : p.qkv_tag;
+      got[k] = i < nval ? ld_tag(src[k]) : ((uint64_t)p.tag << 32);
+    }
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned spins = 0;
+    for (;;) {
+      bool ready = true;
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) ready = ready && tag_of(got[k]) == p.tag;
+      if (ready || !tag_wait_more(p.err, t0, spins)) break;
+#pragma unroll
+      for (int k = 0; k < NPT; ++k)
+        if (tag_of(got[k]) != p.tag) got[k] = ld_tag(src[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int i = threadIdx.x + k * ATTN_THREADS;
+      if (i < nval) s_raw[i] = val_of(got[k]);
+    }
+    __syncthreads();
+  }
+  if (TAG || qkv_raw) {
     constexpr int HALF = HD / 2;
     const float* tab = p.rope_table + (int64_t)pos * HALF * 2;
     for (int i = threadIdx.x; i < (G + (owner ? 1 : 0)) * HALF; i += ATTN_THREADS) {
@@ -125,9 +223,16 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       const int ia = p.rope_layout == 0 ? j : 2 * j;
       const int ib = p.rope_layout == 0 ? j + HALF : 2 * j + 1;
       const float cs = tab[2 * j], sn = tab[2 * j + 1];
-      const float* src = g < G ? qkv_raw + (int64_t)(kvh * G + g) * HD
-                               : qkv_raw + (int64_t)p.H * HD + (int64_t)kvh * HD;   // this head's k
-      const float a = ld_dev(src + ia), b = ld_dev(src + ib);
+      float a, b;
+      if constexpr (TAG) {
+        a = s_raw[g * HD + ia];
+        b = s_raw[g * HD + ib];
+      } else {
+        const float* src = g < G ? qkv_raw + (int64_t)(kvh * G + g) * HD
+                                 : qkv_raw + (int64_t)p.H * HD + (int64_t)kvh * HD;   // this head's k
+        a = ld_dev(src + ia);
+        b = ld_dev(src + ib);
+      }
       const float ra = a * cs - b * sn, rb = a * sn + b * cs;
       if (g < G) {
         s_q[g][ia] = ra;
@@ -138,8 +243,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       }
     }
     if (owner) {
-      const float* vsrc = qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD;
-      for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, ld_dev(vsrc + e));
+      if constexpr (TAG) {
+        for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, s_raw[(G + 1) * HD + e]);
+      } else {
+        const float* vsrc = qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD;
+        for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, ld_dev(vsrc + e));
+      }
     }
     __syncthreads();
     if (owner) {
@@ -216,10 +325,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
           for (int e = 0; e < EPV; ++e) dot += part8[e];
           if (lane < n) s = dot * scale;
         }
-        const float m_new = fmaxf(m_run[gi], wave_max(s));
+        const float m_new = fmaxf(m_run[gi], wave_max_dpp(s));
         const float pr = (lane < n) ? expf(s - m_new) : 0.0f;
         const float alpha = expf(m_run[gi] - m_new);
-        l_run[gi] = l_run[gi] * alpha + wave_sum(pr);
+        l_run[gi] = l_run[gi] * alpha + wave_sum_dpp(pr);
         m_run[gi] = m_new;
         alpha_g[gi] = alpha;
         if (lane < CH) s_p[st][g][lane] = pr;
@@ -304,6 +413,16 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   }
   __syncthreads();
   const int64_t pstride = HD + 2;
+  if constexpr (TAG) {
+    // this part's (max, sum, output) per head as (value, part tag) pairs; a merging workgroup waits for them
+    uint64_t* PT = p.part_tagged + ((int64_t)kvh * p.n_parts + part) * G * pstride;
+    for (int i = threadIdx.x; i < G * pstride; i += ATTN_THREADS) {
+      const int g = i / pstride, j = i % pstride;
+      st_tag(&PT[i], j == 0 ? s_m1[g] : j == 1 ? s_l1[g] : s_o1[g][j - 2], p.part_tag);
+    }
+    set_flag(p.part_flags + (int64_t)kvh * ATTN_MAX_PARTS + part, p.tag);
+    return;
+  }
   float* part_base = p.part + (batched ? (int64_t)row * p.Hkv * p.n_parts * G * pstride : 0);
   float* P = part_base + ((int64_t)kvh * p.n_parts + part) * G * pstride;
   for (int i = threadIdx.x; i < G * pstride; i += ATTN_THREADS) {
@@ -315,7 +434,15 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   stores_done();
   __syncthreads();
   const int np = (ctx + span - 1) / span;
-  if (threadIdx.x == 0) s_last = (take_ticket(&counters[kvh]) == (unsigned)(np - 1));
+  if (threadIdx.x == 0) {
+    s_last = (take_ticket(&counters[kvh]) == (unsigned)(np - 1));
+    // the last workgroup re-arms the counter before any of its output can be seen, so a reader of the
+    // output never finds the counter still counting
+    if (s_last) {
+      reset_ticket(&counters[kvh]);
+      stores_done();
+    }
+  }
   __syncthreads();
   if (!s_last) return;
   // every thread issues all its loads at once (max, sum and its output element of every part), so the
@@ -346,7 +473,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       }
     }
     const int64_t oi = (int64_t)(kvh * G + g) * HD + e;
-    if (p.out_hi) {
+    if constexpr (TAG) {
+      st_tag(p.out_tag + oi, O / L, p.tag);
+    } else if (p.out_hi) {
       bf16_t hi, lo;
       split_bf16(O / L, hi, lo);
       p.out_hi[(int64_t)row * p.H * HD + oi] = hi;
@@ -355,7 +484,81 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       st_dev(&p.out[oi], O / L);
     }
   }
-  if (threadIdx.x == 0) reset_ticket(&counters[kvh]);
+}
+
+// TAG form of the merge: query head g of K/V head kvh, by a workgroup of its own. It waits for the
+// (max, sum, output) of all n_parts parts to carry p.part_tag, combines them by log-sum-exp and writes the
+// head's output as (value, p.tag) pairs. Thread t takes output element t % HD over the parts
+// c = t / HD, t / HD + NS, ... (NS = ATTN_THREADS / HD subsets); the subsets are combined in order through
+// LDS. Every thread of the workgroup must call it.
+template <int HD>
+__device__ __forceinline__ void attn_merge_tagged(const AttnParams& p, const int kvh, const int g, const int n_parts) {
+  constexpr int NS = ATTN_THREADS / HD;                         // part subsets
+  constexpr int NPP = (ATTN_MAX_PARTS + NS - 1) / NS;           // parts per thread, at most
+  __shared__ float s_m[ATTN_THREADS], s_l[ATTN_THREADS], s_o[ATTN_THREADS];
+  const int G = p.H / p.Hkv;
+  const int64_t pstride = HD + 2;
+  const int e = threadIdx.x % HD, sub = threadIdx.x / HD;
+  const uint64_t* PB = p.part_tagged + ((int64_t)kvh * n_parts * G + g) * pstride;
+  const int64_t cstride = (int64_t)G * pstride;
+  bool fl_failed = false;
+  wait_flags(p.part_flags + (int64_t)kvh * ATTN_MAX_PARTS, n_parts, p.tag, p.err, fl_failed);
+  uint64_t m[NPP], l[NPP], o[NPP];
+  const uint64_t ok = (uint64_t)p.part_tag << 32;
+#pragma unroll
+  for (int k = 0; k < NPP; ++k) {
+    const int c = sub + k * NS;
+    m[k] = c < n_parts ? ld_tag(PB + c * cstride) : ok;
+    l[k] = c < n_parts ? ld_tag(PB + c * cstride + 1) : ok;
+    o[k] = c < n_parts ? ld_tag(PB + c * cstride + 2 + e) : ok;
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  unsigned spins = 0;
+  for (;;) {
+    bool ready = true;
+#pragma unroll
+    for (int k = 0; k < NPP; ++k)
+      ready = ready && tag_of(m[k]) == p.part_tag && tag_of(l[k]) == p.part_tag && tag_of(o[k]) == p.part_tag;
+    if (ready || !tag_wait_more(p.err, t0, spins)) break;
+#pragma unroll
+    for (int k = 0; k < NPP; ++k) {
+      const int c = sub + k * NS;
+      if (c < n_parts) {
+        if (tag_of(m[k]) != p.part_tag) m[k] = ld_tag(PB + c * cstride);
+        if (tag_of(l[k]) != p.part_tag) l[k] = ld_tag(PB + c * cstride + 1);
+        if (tag_of(o[k]) != p.part_tag) o[k] = ld_tag(PB + c * cstride + 2 + e);
+      }
+    }
+  }
+  float ms = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NPP; ++k)
+    if (sub + k * NS < n_parts) ms = fmaxf(ms, val_of(m[k]));
+  float L = 0.0f, O = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NPP; ++k) {
+    if (sub + k * NS < n_parts) {
+      const float w = expf(val_of(m[k]) - ms);
+      L = fmaf(val_of(l[k]), w, L);
+      O = fmaf(val_of(o[k]), w, O);
+    }
+  }
+  s_m[threadIdx.x] = ms;
+  s_l[threadIdx.x] = L;
+  s_o[threadIdx.x] = O;
+  __syncthreads();
+  if (threadIdx.x < HD) {
+    float M = -INFINITY;
+    for (int q = 0; q < NS && q < n_parts; ++q) M = fmaxf(M, s_m[q * HD + e]);
+    float LL = 0.0f, OO = 0.0f;
+    for (int q = 0; q < NS && q < n_parts; ++q) {
+      const float w = expf(s_m[q * HD + e] - M);
+      LL = fmaf(s_l[q * HD + e], w, LL);
+      OO = fmaf(s_o[q * HD + e], w, OO);
+    }
+    st_tag(p.out_tag + (int64_t)(kvh * G + g) * HD + e, OO / LL, p.tag);
+  }
+  set_flag(p.att_flags + kvh * G + g, p.tag);
 }
 
 }  // namespace llmk

@@ -86,6 +86,19 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Maximum of v over the 64 lanes, returned to every lane, through DPP lane moves (the structure of
+// wave_sum_dpp; lanes without a source keep -inf).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -167,5 +180,21 @@ __device__ __forceinline__ void split_bf16(float v, bf16_t& hi, bf16_t& lo) {
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// Load of a V from global memory through a pointer the compiler cannot see is global (one read from LDS or
+// from a table): names the global address space so the load is a global (not a flat) load.
+template <typename V>
+__device__ __forceinline__ V gload(const void* ptr) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (sizeof(V) == 16) {
+    return __builtin_bit_cast(V, *(const __attribute__((address_space(1))) u32x4*)ptr);
+  } else if constexpr (sizeof(V) == 8) {
+    return __builtin_bit_cast(V, *(const __attribute__((address_space(1))) u32x2*)ptr);
+  } else {
+    static_assert(sizeof(V) == 4, "gload: 4, 8 or 16 bytes");
+    return __builtin_bit_cast(V, *(const __attribute__((address_space(1))) unsigned*)ptr);
+  }
+}
 
 }  // namespace llmk

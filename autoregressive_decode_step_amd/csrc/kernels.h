@@ -192,6 +192,17 @@ struct AttnParams {
   int64_t qkv_stride;
   bf16_t* out_hi;
   bf16_t* out_lo;
+  // persistent decode step (tagged form): q|k|v and the output as (value, tag) pairs, see attn_block
+  const uint64_t* qkv_tag;
+  uint64_t* out_tag;
+  uint32_t tag;
+  uint32_t part_tag;           // the parts' tag: unique per (step, layer), the part buffer serves every layer
+  uint64_t* part_tagged;       // [Hkv][n_parts][G][hd + 2] (value, part_tag) pairs
+  const uint32_t* qkv_flags;   // the q|k|v producers' flags (n_qkv_flags), waited for before q|k|v is read
+  int32_t n_qkv_flags;
+  uint32_t* part_flags;        // [Hkv][ATTN_MAX_PARTS]: a part's flag, set once its record is stored
+  uint32_t* att_flags;         // [H]: a merged head's flag
+  int32_t* err;
 };
 
 constexpr int ATTN_MAX_PARTS = 32;
@@ -201,7 +212,7 @@ hipError_t attn_launch(const AttnParams& p, hipStream_t s);
 inline int64_t attn_part_floats(int64_t H, int64_t hd) { return (int64_t)ATTN_MAX_PARTS * H * (hd + 2); }
 
 // ------------------------------------------------------------------------------------------------
-// The persistent decode-step kernel (one launch per step, one workgroup per CU, grid barriers)
+// The persistent decode-step kernel (one launch per step, one workgroup per CU)
 // ------------------------------------------------------------------------------------------------
 
 struct StepLayer {
@@ -222,32 +233,36 @@ struct StepParams {
   float eps;
   int32_t nwg;                  // workgroups (one per CU)
   int64_t kv_off;               // element offset of the slot in each pool buffer
-  int32_t attn_chunk, attn_sub_per_wg, attn_n_parts, pad0;
+  int32_t attn_chunk, pad0;     // positions per attention tile
   DecodeState* state;
-  // activations, one buffer version per write in a step (a version is read only after it is written, so
-  // no L2 can hold a stale copy of it): x [2 n_layer + 1][x_stride], q|k|v, attention output and u
-  // [n_layer][*_stride]
-  float* x;
-  float* qkv;
-  float* att;
-  float* u;
+  // activations as (value, tag) pairs, tag = step within the call + 1; cleared before each call.
+  // x [2 n_layer][x_stride]: x after layer l's o (2l) and after its down (2l + 1); q|k|v, attention
+  // output and u [n_layer][*_stride]
+  uint64_t* x;
+  uint64_t* qkv;
+  uint64_t* att;
+  uint64_t* u;
   int64_t x_stride, qkv_stride, att_stride, u_stride;
-  float* attn_part;
-  unsigned* attn_cnt;           // [Hkv]
+  uint64_t* attn_part;          // [Hkv][ATTN_MAX_PARTS][G][hd + 2] (value, tag) pairs, tag unique per layer
   float* logits;                // optional [V]
   float* hidden;                // optional [n_layer][d]
   float* head_val;              // [nwg]
   int32_t* head_idx;
-  unsigned* head_cnt;
-  unsigned long long* bar;      // grid barrier arrivals, zero at the start of a call
-  int32_t* err;                 // set when a barrier wait gives up
+  unsigned* head_cnt;           // zero on entry and exit
+  int32_t* err;                 // set when a wait gives up
   int32_t* token_out;           // token of step s at token_out[s]
+  // readiness flags, [n_layer][fl_stride]: q|k|v [nwg], x after o [nwg], u [nwg], x after down [nwg],
+  // attention output [H], attention parts [Hkv][ATTN_MAX_PARTS]; a flag holds the tag of the step that set it
+  uint32_t* flags;
+  int64_t fl_stride;
 };
 
 constexpr int STEP_MAX_LAYERS = 128;   // layers the persistent step kernel supports
+constexpr int STEP_MAX_VIN = 16384;    // longest projection input (d, H*hd, hidden) it supports
+constexpr int STEP_MAX_RES = 256;      // residual rows per workgroup (d / workgroups, rounded up) it supports
 // Workgroups the step kernel runs with on the current device (0 if it cannot hold one per CU).
-int step_grid(int kv_is_bf16, int hd, int64_t vin_floats);
-hipError_t step_launch(const StepParams& p, int kv_is_bf16, int64_t vin_floats, hipStream_t s);
+int step_grid(int kv_is_bf16, int hd);
+hipError_t step_launch(const StepParams& p, int kv_is_bf16, hipStream_t s);
 struct StepTableChunk {
   StepLayer layers[8];
   int32_t first, count;

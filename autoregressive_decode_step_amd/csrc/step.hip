@@ -1,27 +1,32 @@
 // The whole decode step of one sequence as one persistent kernel (gfx950).
 //
-// A step is a chain of operations each of which needs all of the previous one's output: RMSNorm + q|k|v,
-// attention, o + residual, RMSNorm + gate|up, down + residual, per layer, then the head and the greedy
-// token ("The forward pass end to end", "What a forward step does"). As separate kernels each operation
-// pays a launch, a ramp-up and a drain, about as long as a small projection itself. Here one workgroup per
-// CU runs the whole step: the operations are separated by grid barriers, and every workgroup streams its
-// share of the weights through a ring of 16-byte loads per lane that runs one group of SK_RING loads ahead
-// of the arithmetic, across the barriers, so the next operation's first weights are already on chip when
-// its input becomes available ("Inside the engine", "4. The pipelined decode": keep the device busy
-// between the step's pieces).
+// A step is a chain of operations, each needing all of the previous one's output: RMSNorm + q|k|v,
+// attention, o + residual, RMSNorm + gate|up, down + residual, per layer, then the final norm, the head
+// and the greedy token ("The forward pass end to end", "What a forward step does"). Launched one kernel
+// per operation, every operation pays a launch, a ramp-up and a drain, about as long as a small projection
+// itself. Here one workgroup per CU runs the whole step.
 //
-// Work split. Every projection y = W v is cut into equal row slices, one per workgroup; inside a
-// workgroup the 8 waves split K, lane l of wave w reads 8 consecutive bf16 of a row per load (16 B), and
-// the waves' partial sums meet in LDS. The input vector v (normalised x, the attention output or u) is
-// staged in LDS by every workgroup. The head is cut the same way into chunks of at most SK_ROWS rows.
-// Attention items (K/V head, context part) are spread over the workgroups as in the attention kernel.
+// Weight stream. Every projection y = W v is cut into row ranges, one per workgroup; inside a workgroup
+// wave w takes rows w, w + 8, ... (gate|up: the gate row and the up row of outputs w, w + 8, ...). A wave
+// reads a row as 16-byte loads per lane (512 bf16 per load, coalesced) and dots it with the staged input
+// vector in LDS. Each wave keeps SK_R loads in flight in a register ring, and the ring runs on from one
+// operation into the next: while a workgroup waits for the next operation's input, the first SK_R loads of
+// that operation's weights are already on their way, so HBM stays busy across the step's dependencies
+// ("Inside the engine", "4. The pipelined decode": keep the device busy between the step's pieces).
+// Every operation's load count per wave is padded to a multiple of SK_R (the padding re-reads the wave's
+// last row, from cache, and is not used), so ring slot indices are compile-time constants.
 //
-// Coherence. Activations written in this launch by one workgroup and read by another go through
-// device-scope stores and loads (each XCD's L2 is not coherent with the others); weights and the K/V
-// history are only read, so they use ordinary loads. A barrier is: every thread waits for its own stores,
-// one thread adds 1 to a 64-bit arrival counter and spins (with sleep) until all workgroups of this
-// barrier have arrived. The spin is bounded; a workgroup that gives up sets an error flag and leaves,
-// the others then time out too, and the host reports a device error rather than hanging.
+// Hand-off without barriers. Every activation one workgroup writes and another reads (q|k|v, the
+// attention output, x after each residual add, u) is stored as 8-byte (value, tag) pairs, the tag being
+// the step's number within the call plus one. A reader loads what it needs with device-scope loads (past
+// the non-coherent L2 of its XCD) and reloads until every pair carries the current tag: the data itself
+// is the signal, so a dependency costs one round trip and no writer ever waits for its stores. The
+// buffers are cleared before each call. Every wait is bounded (200 ms of the real-time counter); a
+// workgroup that gives up sets an error flag that stops every other waiter, and the host reports a device
+// error.
+//
+// Norms. RMSNorm(x) * g is applied as (x * g) staged in LDS and the scalar rsqrt(mean(x^2) + eps) applied
+// to each row's dot product, so the dots start as soon as x is staged.
 #include <limits.h>
 
 #include "attn_block.h"
@@ -30,393 +35,624 @@ namespace llmk {
 
 constexpr int SK_THREADS = ATTN_THREADS;   // 512: 8 waves
 constexpr int SK_WAVES = SK_THREADS / 64;
-constexpr int SK_RING = 16;                 // weight loads per lane per group; the ring holds one group
-constexpr int SK_ROWS = 128;                // rows per phase chunk per workgroup
-constexpr int SK_SEG = 512;                 // elements one wave covers per load (64 lanes x 8)
-constexpr int SK_MAX_LAYERS = STEP_MAX_LAYERS;   // layer table held in LDS
-constexpr unsigned SK_SPIN_LIMIT = 1u << 20;   // about a second of waiting
+constexpr int SK_R = 16;                    // weight loads in flight per lane
+constexpr int SK_SEG = 512;                 // elements of one wave load (64 lanes x 8 bf16)
+constexpr int SK_PASS = 4;                  // float4 groups per thread staged per round trip
 
-enum { PK_QKV = 0, PK_O = 1, PK_GU = 2, PK_DN = 3, PK_HEAD = 4 };
+enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DN = 3, OP_HEAD = 4 };
 
-// One phase: a chunk of this workgroup's rows of one operation. Its units are (row r, load i) with
-// i < 2^sh (the loads per row rounded up to a power of two), in the order u = r * 2^sh + i, padded to
-// whole groups of SK_RING units. GATEUP chunks order their rows gate first, then up.
-struct Phase {
-  int kind, l, chunk;
-  int R;                // rows (GATEUP: 2 per output)
-  int row0;             // first global row (GATEUP: first output)
-  int K, KS;            // row length, elements per wave
-  int sh;               // log2 of the loads per row
-  int groups;           // SK_RING-unit groups (0 when R == 0)
+struct SkRange {
+  int lo, n;
 };
 
-__device__ __forceinline__ int sk_cdiv(int a, int b) { return (a + b - 1) / b; }
-__device__ __forceinline__ int sk_clamp0(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
-
-struct Split { int rq, ro, rg, rd, rh; int cq, co, cg, cd, ch; int per_layer; };
-
-__device__ __forceinline__ Split sk_split(const StepParams& p) {
-  Split s;
-  s.rq = sk_cdiv(p.qd + 2 * p.kvd, p.nwg);
-  s.ro = sk_cdiv(p.d, p.nwg);
-  s.rg = sk_cdiv(p.F, p.nwg);             // outputs; rows = 2 per output
-  s.rd = sk_cdiv(p.d, p.nwg);
-  s.rh = sk_cdiv(p.V, p.nwg);
-  s.cq = sk_cdiv(s.rq, SK_ROWS);
-  s.co = sk_cdiv(s.ro, SK_ROWS);
-  s.cg = sk_cdiv(s.rg, SK_ROWS / 2);
-  s.cd = sk_cdiv(s.rd, SK_ROWS);
-  s.ch = sk_cdiv(s.rh, SK_ROWS);
-  s.per_layer = s.cq + s.co + s.cg + s.cd;
-  return s;
+__device__ __forceinline__ SkRange sk_range(int rows, int w, int nwg) {
+  const int lo = (int)(((int64_t)rows * w) / nwg);
+  const int hi = (int)(((int64_t)rows * (w + 1)) / nwg);
+  return {lo, hi - lo};
 }
 
-__device__ __forceinline__ int sk_n_phases(const StepParams& p, const Split& s) { return p.n_layer * s.per_layer + s.ch; }
+// this workgroup's rows of every projection
+struct SkRows {
+  SkRange q, k, v;   // rows of wq, wk, wv
+  SkRange d;         // outputs of o and down (and the residual rows it keeps)
+  SkRange f;         // outputs of gate|up
+  SkRange h;         // rows of the head
+};
 
-__device__ __forceinline__ Phase sk_phase(const StepParams& p, const Split& s, int ph, int w) {
-  Phase f;
-  int kind, l, c;
-  if (ph < p.n_layer * s.per_layer) {
-    l = ph / s.per_layer;
-    c = ph % s.per_layer;
-    if (c < s.cq) { kind = PK_QKV; }
-    else if ((c -= s.cq) < s.co) { kind = PK_O; }
-    else if ((c -= s.co) < s.cg) { kind = PK_GU; }
-    else { c -= s.cg; kind = PK_DN; }
-  } else {
-    kind = PK_HEAD;
-    l = 0;
-    c = ph - p.n_layer * s.per_layer;
-  }
-  f.kind = kind;
-  f.l = l;
-  f.chunk = c;
-  int n_rows, per;   // global rows (outputs) of the operation, rows (outputs) per workgroup
-  switch (kind) {
-    case PK_QKV: n_rows = p.qd + 2 * p.kvd; per = s.rq; f.K = p.d; break;
-    case PK_O: n_rows = p.d; per = s.ro; f.K = p.qd; break;
-    case PK_GU: n_rows = p.F; per = s.rg; f.K = p.d; break;
-    case PK_DN: n_rows = p.d; per = s.rd; f.K = p.F; break;
-    default: n_rows = p.V; per = s.rh; f.K = p.d; break;
-  }
-  const int step = kind == PK_GU ? SK_ROWS / 2 : SK_ROWS;
-  const int mine = sk_clamp0(n_rows - w * per, per);
-  const int in_chunk = sk_clamp0(mine - c * step, step);
-  f.row0 = w * per + c * step;
-  f.R = kind == PK_GU ? 2 * in_chunk : in_chunk;
-  f.KS = (sk_cdiv(f.K, SK_WAVES) + 7) / 8 * 8;
-  const int ni = sk_cdiv(f.KS, SK_SEG);
+// the layer table, staged in LDS once
+struct SkLayer {
+  const bf16_t* w[7];
+  const float* g1;
+  const float* g2;
+  void* k;
+  void* v;
+};
+
+// One projection as one wave streams it. A row is 2^sh load slots (its loads rounded up to a power of
+// two; the extra slots re-read the row's last 16 bytes, which meet zeros of the staged input); load slot u
+// of the wave is slot u & (2^sh - 1) of wave-local row u >> sh.
+struct SkOp {
+  int kind, l;
+  int K, sh;          // row length, log2 of the load slots per row
+  int nrows, npos;    // rows of this wave, its load slots (nrows << sh rounded up to SK_R; 0: none)
+  int n0, n01;        // QKV: the workgroup's rows of wq, of wq and wk (else larger than any row)
+  int kmax;           // byte offset of a row's last 16-byte slice
+  const bf16_t* m0;   // the workgroup's first row of wq / gate / the matrix
+  const bf16_t* m1;   // of wk / up
+  const bf16_t* m2;   // of wv
+};
+
+// c ? a : b on values (a conditional on two struct members would select between their addresses and keep
+// the struct in memory)
+template <typename V>
+__device__ __forceinline__ V sk_sel(bool c, V a, V b) {
+  return c ? a : b;
+}
+
+// a pointer every lane holds the same value of, moved to scalar registers
+template <typename P>
+__device__ __forceinline__ P* sk_uniform(P* ptr) {
+  const uint64_t u = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
+// an op without loads, for the issue side past the last op: every slot reads the head's first 16 bytes
+__device__ __forceinline__ SkOp sk_idle(const StepParams& p) {
+  SkOp f;
+  f.kind = OP_HEAD;
+  f.l = 0;
+  f.K = 8;
   f.sh = 0;
-  while ((1 << f.sh) < ni) ++f.sh;
-  f.groups = sk_cdiv(f.R << f.sh, SK_RING);
+  f.nrows = 1;
+  f.npos = 0;
+  f.n0 = f.n01 = INT_MAX;
+  f.kmax = 0;
+  f.m0 = f.m1 = f.m2 = p.w_out;
   return f;
 }
 
-// the weight row behind local row r of phase f (layer table in LDS; no global memory access)
-__device__ __forceinline__ const bf16_t* sk_row(const StepParams& p, const StepLayer* lt, const Phase& f, int r) {
-  if (f.kind == PK_HEAD) return p.w_out + (int64_t)(f.row0 + r) * p.d;
-  const StepLayer& L = lt[f.l];
-  switch (f.kind) {
-    case PK_QKV: {
-      const int gr = f.row0 + r;
-      if (gr < p.qd) return L.w[0] + (int64_t)gr * p.d;
-      if (gr < p.qd + p.kvd) return L.w[1] + (int64_t)(gr - p.qd) * p.d;
-      return L.w[2] + (int64_t)(gr - p.qd - p.kvd) * p.d;
+__device__ __forceinline__ SkOp sk_op(const StepParams& p, const SkRows& R, const SkLayer* lt, int o, int wave) {
+  SkOp f;
+  int rw;
+  f.n0 = f.n01 = INT_MAX;
+  if (o >= 4 * p.n_layer) {
+    f.kind = OP_HEAD;
+    f.l = 0;
+    f.K = p.d;
+    f.m0 = p.w_out + (int64_t)R.h.lo * p.d;
+    rw = R.h.n;
+  } else {
+    f.l = o >> 2;
+    f.kind = o & 3;
+    const SkLayer& Ly = lt[f.l];
+    switch (f.kind) {
+      case OP_QKV:
+        f.K = p.d;
+        f.m0 = sk_uniform(Ly.w[0]) + (int64_t)R.q.lo * p.d;
+        f.m1 = sk_uniform(Ly.w[1]) + (int64_t)R.k.lo * p.d;
+        f.m2 = sk_uniform(Ly.w[2]) + (int64_t)R.v.lo * p.d;
+        f.n0 = R.q.n;
+        f.n01 = R.q.n + R.k.n;
+        rw = R.q.n + R.k.n + R.v.n;
+        break;
+      case OP_O:
+        f.K = p.qd;
+        f.m0 = sk_uniform(Ly.w[3]) + (int64_t)R.d.lo * p.qd;
+        rw = R.d.n;
+        break;
+      case OP_GU:
+        f.K = p.d;
+        f.m0 = sk_uniform(Ly.w[4]) + (int64_t)R.f.lo * p.d;
+        f.m1 = sk_uniform(Ly.w[5]) + (int64_t)R.f.lo * p.d;
+        rw = R.f.n;
+        break;
+      default:
+        f.K = p.F;
+        f.m0 = sk_uniform(Ly.w[6]) + (int64_t)R.d.lo * p.F;
+        rw = R.d.n;
+        break;
     }
-    case PK_GU: {
-      const int half = f.R >> 1;
-      return (r < half ? L.w[4] + (int64_t)(f.row0 + r) * p.d : L.w[5] + (int64_t)(f.row0 + r - half) * p.d);
-    }
-    case PK_O: return L.w[3] + (int64_t)(f.row0 + r) * p.qd;
-    default: return L.w[6] + (int64_t)(f.row0 + r) * p.F;
   }
+  if (f.kind != OP_QKV) {
+    const bf16_t* m = sk_sel<const bf16_t*>(f.kind == OP_GU, f.m1, f.m0);
+    f.m1 = m;
+    f.m2 = m;
+  }
+  const int lpr = (f.K + SK_SEG - 1) / SK_SEG;
+  f.sh = 0;
+  while ((1 << f.sh) < lpr) ++f.sh;
+  f.kmax = 2 * (f.K - 8);
+  const int mine = rw > wave ? (rw - wave + SK_WAVES - 1) / SK_WAVES : 0;
+  f.nrows = f.kind == OP_GU ? 2 * mine : mine;
+  f.npos = ((f.nrows << f.sh) + SK_R - 1) / SK_R * SK_R;
+  return f;
 }
 
-// grid barrier (see the header comment); returns false after a timeout
-__device__ __forceinline__ bool sk_barrier(const StepParams& p, unsigned long long target, int* s_ok) {
-  stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(p.bar, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned n = 0;
-    int ok = 1;
-    while (__hip_atomic_load(p.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++n > SK_SPIN_LIMIT || ld_dev(p.err) != 0) {
-        ok = 0;
-        st_dev(p.err, 1);
-        break;
+// address of load slot u of op f for this lane (slots past the wave's rows re-read its last row)
+__device__ __forceinline__ const char* sk_addr(const SkOp& f, int u, int wave, int lane16) {
+  const int r = min(u >> f.sh, f.nrows - 1);
+  const int c = u & ((1 << f.sh) - 1);
+  const int q = wave + SK_WAVES * r;
+  const int j = wave + SK_WAVES * (r >> 1);
+  const bool gu = f.kind == OP_GU;
+  const bf16_t* m0 = f.m0;
+  const bf16_t* m1 = f.m1;
+  const bf16_t* m2 = f.m2;
+  const int n0 = f.n0, n01 = f.n01;
+  const bf16_t* base = sk_sel(gu, sk_sel((r & 1) != 0, m1, m0), sk_sel(q < n0, m0, sk_sel(q < n01, m1, m2)));
+  const int row = sk_sel(gu, j, sk_sel(q < n0, q, sk_sel(q < n01, q - n0, q - n01)));
+  const int off = min(c * (SK_SEG * 2) + lane16, f.kmax);
+  return reinterpret_cast<const char*>(base + (int64_t)row * f.K) + off;
+}
+
+// LDS position of input element e (e % 4 == 0 for a float4 group): lane l's 8 elements of segment c sit as
+// two float4 at c*512 + l*4 and c*512 + 256 + l*4, so both reads of a segment are contiguous over the lanes
+__device__ __forceinline__ int sk_vin_pos(int e) {
+  const int c = e >> 9, r = e & 511;
+  return (c << 9) | (((r >> 2) & 1) << 8) | ((r >> 3) << 2) | (r & 3);
+}
+
+// Stage an input vector of n fp32 values into LDS (permuted; zeros up to the padded row length npad):
+// src_tag = (value, tag) pairs waited for, or src_emb = a bf16 row (no wait). gain: multiply by it.
+// res: copy elements [res_lo, res_lo + res_n) unmultiplied to res. Returns this thread's sum of squares.
+__device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t* src_emb, int n, int npad,
+                                          uint32_t tag, const float* gain, float* res, int res_lo, int res_n,
+                                          float* vin, int32_t* err, bool& failed, const uint32_t* flags,
+                                          int nflags) {
+  const int t = threadIdx.x;
+  if (src_tag) wait_flags(flags, nflags, tag, err, failed);
+  const int ng = (n / 4 + SK_THREADS - 1) / SK_THREADS;   // float4 groups per thread (uniform)
+  float ss = 0.0f;
+  for (int k0 = 0; k0 < ng; k0 += SK_PASS) {
+    float v[SK_PASS][4];
+    float4 g[SK_PASS];
+    if (gain) {
+#pragma unroll
+      for (int k = 0; k < SK_PASS; ++k) {
+        const int e = 4 * (t + (k0 + k) * SK_THREADS);
+        if (k0 + k < ng && e < n) g[k] = gload<float4>(gain + e);
       }
     }
-    *s_ok = ok;
-  }
-  __syncthreads();
-  return *s_ok != 0;
-}
-
-// vin[0..n) = x * rsqrt(mean(x^2) + eps) * g. x is a buffer version written earlier in this launch and
-// never read before it in this launch, so no L2 holds a stale copy and ordinary loads see the data.
-__device__ __forceinline__ void sk_stage_norm(const float* x, const float* g, int n, float eps, float* vin,
-                                              float* s_red) {
-  float ss = 0.0f;
-  for (int i = threadIdx.x * 4; i < n; i += SK_THREADS * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(x + i);
-    *reinterpret_cast<float4*>(vin + i) = v;
-    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
-  }
-  ss = wave_sum_dpp(ss);
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.0f;
+    if (src_emb) {
 #pragma unroll
-  for (int w = 0; w < SK_WAVES; ++w) tot += s_red[w];
-  const float scale = 1.0f / sqrtf(tot / (float)n + eps);
-  for (int i = threadIdx.x; i < n; i += SK_THREADS) vin[i] = vin[i] * scale * g[i];
-  __syncthreads();
+      for (int k = 0; k < SK_PASS; ++k) {
+        const int e = 4 * (t + (k0 + k) * SK_THREADS);
+        if (k0 + k < ng && e < n) {
+          const uint2 w = gload<uint2>(src_emb + e);
+          v[k][0] = bf16_lo(w.x);
+          v[k][1] = bf16_hi(w.x);
+          v[k][2] = bf16_lo(w.y);
+          v[k][3] = bf16_hi(w.y);
+        }
+      }
+    } else {
+      // device-scope 16-byte loads (sc1), two (value, tag) pairs each; past n the loads return zeros
+      __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(src_tag), (short)0, n * 8, 0x00020000);
+      uint4 a[SK_PASS], b[SK_PASS];
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      unsigned spins = 0;
+      for (;;) {
+#pragma unroll
+        for (int k = 0; k < SK_PASS; ++k) {
+          if (k0 + k < ng) {
+            const int off = 32 * (t + (k0 + k) * SK_THREADS);
+            a[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16));
+            b[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 16));
+          }
+        }
+        bool ready = true;
+#pragma unroll
+        for (int k = 0; k < SK_PASS; ++k) {
+          const int e = 4 * (t + (k0 + k) * SK_THREADS);
+          if (k0 + k < ng && e < n) ready = ready && a[k].y == tag && a[k].w == tag && b[k].y == tag && b[k].w == tag;
+        }
+        if (ready || failed) break;
+        if (!tag_wait_more(err, t0, spins)) {
+          failed = true;
+          break;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < SK_PASS; ++k) {
+        v[k][0] = __uint_as_float(a[k].x);
+        v[k][1] = __uint_as_float(a[k].z);
+        v[k][2] = __uint_as_float(b[k].x);
+        v[k][3] = __uint_as_float(b[k].z);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < SK_PASS; ++k) {
+      const int e = 4 * (t + (k0 + k) * SK_THREADS);
+      if (k0 + k < ng && e < n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ss = fmaf(v[k][i], v[k][i], ss);
+          if (res && e + i >= res_lo && e + i < res_lo + res_n) res[e + i - res_lo] = v[k][i];
+        }
+        float4 o = make_float4(v[k][0], v[k][1], v[k][2], v[k][3]);
+        if (gain) {
+          o.x *= g[k].x;
+          o.y *= g[k].y;
+          o.z *= g[k].z;
+          o.w *= g[k].w;
+        }
+        *reinterpret_cast<float4*>(vin + sk_vin_pos(e)) = o;
+      }
+    }
+  }
+  for (int e = n + 4 * t; e < npad; e += 4 * SK_THREADS)
+    *reinterpret_cast<float4*>(vin + sk_vin_pos(e)) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  return ss;
 }
 
-// vin[0..n) = src (a buffer version, as above)
-__device__ __forceinline__ void sk_stage_copy(const float* src, int n, float* vin) {
-  for (int i = threadIdx.x * 4; i < n; i += SK_THREADS * 4)
-    *reinterpret_cast<float4*>(vin + i) = *reinterpret_cast<const float4*>(src + i);
+// sum of every thread's x over the workgroup, the same value for all threads
+__device__ __forceinline__ float sk_block_sum(float x, float* s_red) {
+  x = wave_sum_dpp(x);
   __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float t = 0.0f;
+#pragma unroll
+  for (int w = 0; w < SK_WAVES; ++w) t += s_red[w];
+  return t;
+}
+
+// where one op's row results go
+struct SkOut {
+  uint64_t* y;        // QKV: q|k|v of the layer; O/DN: the new x version; GU: u of the layer
+  const float* res;   // O/DN: the workgroup's residual rows of the old x (LDS)
+  float* hidden;      // DN: optional copy of x, this layer's row
+  float* logits;      // HEAD: optional
+  float scale;        // RMSNorm scale of the op's input (1 when there is no norm)
+  uint32_t tag;
+};
+
+// Row results of one wave, lane-parallel: wave-local row r's dot product is in lane r of y (r < 64) or
+// lane r - 64 of y2. Written out once the op's loads are done, so the load loop holds no stores.
+template <int KIND>
+__device__ __forceinline__ void sk_rows_out(float y, float y2, const SkOp& f, const StepParams& p, const SkRows& R,
+                                            const SkOut& out, int wave, int lane, float& best_v, int& best_i) {
+  if constexpr (KIND == OP_GU) {
+    // gate of output j in lane 2j, its up in lane 2j + 1 (of y, then of y2)
+    const float up = __shfl_down(y, 1, 64), up2 = __shfl_down(y2, 1, 64);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lane + 64 * h;
+      if ((lane & 1) == 0 && r < f.nrows) {
+        const float g = (h ? y2 : y) * out.scale, u = (h ? up2 : up) * out.scale;
+        st_tag(out.y + R.f.lo + wave + SK_WAVES * (r >> 1), silu_f(g) * u, out.tag);
+      }
+    }
+  } else if constexpr (KIND == OP_HEAD) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lane + 64 * h;
+      if (r < f.nrows) {
+        const float lg = (h ? y2 : y) * out.scale;
+        const int row = R.h.lo + wave + SK_WAVES * r;
+        if (out.logits) out.logits[row] = lg;
+        if (argmax_better(lg, row, bv, bi)) {
+          bv = lg;
+          bi = row;
+        }
+      }
+    }
+    wave_argmax(bv, bi);
+    if (argmax_better(bv, bi, best_v, best_i)) {
+      best_v = bv;
+      best_i = bi;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lane + 64 * h;
+      if (r < f.nrows) {
+        const float v = h ? y2 : y;
+        const int q = wave + SK_WAVES * r;
+        if constexpr (KIND == OP_QKV) {
+          const int idx = q < f.n0 ? R.q.lo + q
+                                   : (q < f.n01 ? p.qd + R.k.lo + (q - f.n0) : p.qd + p.kvd + R.v.lo + (q - f.n01));
+          st_tag(out.y + idx, v * out.scale, out.tag);
+        } else {
+          const float xn = out.res[q] + v;
+          st_tag(out.y + R.d.lo + q, xn, out.tag);
+          if (KIND == OP_DN && out.hidden) out.hidden[R.d.lo + q] = xn;
+        }
+      }
+    }
+  }
+}
+
+// One block of SK_R ring slots of op f, starting at slot blk: slot j is read and dotted with the staged
+// input, then refilled with slot ib + j of op `is` (when ISSUE). A row's dot product is reduced over the wave
+// at its last slot and put into lane r of y (r < 64) or lane r - 64 of y2.
+template <bool ISSUE>
+__device__ __forceinline__ void sk_block(uint4 (&ring)[SK_R], const SkOp& f, int blk, const SkOp& is, int ib,
+                                         const float* vl, int wave, int lane, int lane16, float& acc0,
+                                         float& acc1, float& y, float& y2) {
+  const int mask = (1 << f.sh) - 1;
+#pragma unroll
+  for (int j = 0; j < SK_R; ++j) {
+    const int u = blk + j;
+    const int c = u & mask;
+    const float4 x0 = *reinterpret_cast<const float4*>(vl + c * SK_SEG);
+    const float4 x1 = *reinterpret_cast<const float4*>(vl + c * SK_SEG + 256);
+    const uint4 r = ring[j];
+    acc0 = fmaf(bf16_lo(r.x), x0.x, acc0);
+    acc1 = fmaf(bf16_hi(r.x), x0.y, acc1);
+    acc0 = fmaf(bf16_lo(r.y), x0.z, acc0);
+    acc1 = fmaf(bf16_hi(r.y), x0.w, acc1);
+    acc0 = fmaf(bf16_lo(r.z), x1.x, acc0);
+    acc1 = fmaf(bf16_hi(r.z), x1.y, acc1);
+    acc0 = fmaf(bf16_lo(r.w), x1.z, acc0);
+    acc1 = fmaf(bf16_hi(r.w), x1.w, acc1);
+    if constexpr (ISSUE) ring[j] = gload<uint4>(sk_addr(is, ib + j, wave, lane16));
+    if (c == mask) {
+      const int rr = u >> f.sh;
+      const float t = wave_sum_dpp(acc0 + acc1);
+      acc0 = acc1 = 0.0f;
+      if (rr < f.nrows) {
+        y = lane == rr ? t : y;
+        y2 = lane == rr - 64 ? t : y2;
+      }
+    }
+  }
+}
+
+// Consume the loads of op f from the ring while refilling each slot right after it is read: with the rest
+// of f, then (when `prefetch`) with the first SK_R slots of nx. Nothing but the ring's loads and the LDS
+// reads of the input touches memory in the loop, so every slot waits only for its own load; one copy of
+// the loop serves every op, which keeps the ring in the same registers throughout.
+__device__ __forceinline__ void sk_consume(uint4 (&ring)[SK_R], const SkOp& f, const SkOp& nx, bool prefetch,
+                                           const float* vl, int wave, int lane, int lane16, float& y, float& y2) {
+  float acc0 = 0.0f, acc1 = 0.0f;
+  y = 0.0f;
+  y2 = 0.0f;
+  if (f.npos <= 0) return;
+  int blk = 0;
+  for (; blk + SK_R < f.npos; blk += SK_R)
+    sk_block<true>(ring, f, blk, f, blk + SK_R, vl, wave, lane, lane16, acc0, acc1, y, y2);
+  if (prefetch) sk_block<true>(ring, f, blk, nx, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
+  else sk_block<false>(ring, f, blk, nx, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(SK_THREADS) void step_kernel(const StepParams p) {
-  extern __shared__ float vin[];                         // the phase's input vector (max(d, qd, F) floats)
-  __shared__ float s_part[SK_ROWS][SK_WAVES + 1];         // per-row partial sums of the 8 waves
-  __shared__ StepLayer s_layers[SK_MAX_LAYERS];
+constexpr int sk_lds_vecs() {
+  return attn_tile_vecs<T, HD>() > STEP_MAX_VIN / 4 ? attn_tile_vecs<T, HD>() : STEP_MAX_VIN / 4;
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p) {
+  // the staged input vector and the attention tiles are never live together: one LDS region
+  __shared__ uint4 s_big[sk_lds_vecs<T, HD>()];
+  __shared__ SkLayer s_layers[STEP_MAX_LAYERS];
+  __shared__ float s_res[STEP_MAX_RES];      // this workgroup's residual rows of x
   __shared__ float s_red[SK_WAVES];
   __shared__ float s_best_v[SK_WAVES];
   __shared__ int s_best_i[SK_WAVES];
-  __shared__ int s_ok;
   __shared__ int s_last;
+  float* vin = reinterpret_cast<float*>(s_big);
 
   const int w = blockIdx.x;
   const int lane = threadIdx.x & 63;
+  const int lane16 = lane * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Split sp = sk_split(p);
-  const int n_ph = sk_n_phases(p, sp);
+  const int nwg = p.nwg;
+  const int L = p.n_layer;
+  const int n_ops = 4 * L + 1;
   const int step = p.state->step;
-  const int nb_step = 5 * p.n_layer + 1;                 // barriers per step
-  unsigned long long bar_idx = (unsigned long long)step * nb_step;   // barriers passed so far in this call
-  const unsigned long long nwg = (unsigned long long)p.nwg;
+  const int tok = p.state->token;
+  const int pos = p.state->pos;
+  const uint32_t tag = (uint32_t)step + 1u;
+  bool failed = false;
 
-  // the layer table in LDS: weight addresses are then computed without global loads (which would make the
-  // ring's loads wait), and every workgroup reads it once
-  for (int i = threadIdx.x; i < p.n_layer; i += SK_THREADS) s_layers[i] = p.layers[i];
+  for (int i = threadIdx.x; i < L; i += SK_THREADS) {
+    const StepLayer& s = p.layers[i];
+    SkLayer& d = s_layers[i];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) d.w[j] = s.w[j];
+    d.g1 = s.g1;
+    d.g2 = s.g2;
+    d.k = s.k;
+    d.v = s.v;
+  }
+  SkRows R;
+  R.q = sk_range(p.qd, w, nwg);
+  R.k = sk_range(p.kvd, w, nwg);
+  R.v = sk_range(p.kvd, w, nwg);
+  R.d = sk_range(p.d, w, nwg);
+  R.f = sk_range(p.F, w, nwg);
+  R.h = sk_range(p.V, w, nwg);
   __syncthreads();
 
-  // activation buffer versions: x_v (v = 0 embedding, 2l+1 after layer l's o, 2l+2 after its down), and
-  // per layer q|k|v, attention output and u
-#define LLMK_SK_X(V) (p.x + (int64_t)(V) * p.x_stride)
-#define LLMK_SK_QKV(L) (p.qkv + (int64_t)(L) * p.qkv_stride)
-#define LLMK_SK_ATT(L) (p.att + (int64_t)(L) * p.att_stride)
-#define LLMK_SK_U(L) (p.u + (int64_t)(L) * p.u_stride)
+#define SK_X(V) (p.x + (int64_t)(V) * p.x_stride)
+#define SK_QKV(LL) (p.qkv + (int64_t)(LL) * p.qkv_stride)
+#define SK_ATT(LL) (p.att + (int64_t)(LL) * p.att_stride)
+#define SK_U(LL) (p.u + (int64_t)(LL) * p.u_stride)
+#define SK_FL(LL, K) (p.flags + (int64_t)(LL) * p.fl_stride + (K) * nwg)   // K: 0 q|k|v, 1 x after o, 2 u, 3 x after down
+#define SK_FL_ATT(LL) (p.flags + (int64_t)(LL) * p.fl_stride + 4 * nwg)
+#define SK_FL_PART(LL) (p.flags + (int64_t)(LL) * p.fl_stride + 4 * nwg + p.H)
 
-  AttnParams ap{};
-  ap.H = p.H;
-  ap.Hkv = p.Hkv;
-  ap.hd = HD;
-  ap.kv_is_bf16 = sizeof(T) == 2;
-  ap.state = p.state;
-  ap.chunk = p.attn_chunk;
-  ap.sub_per_wg = p.attn_sub_per_wg;
-  ap.n_parts = p.attn_n_parts;
-  ap.part = p.attn_part;
-  ap.counters = p.attn_cnt;
-  ap.rope_table = p.rope_table;
-  ap.rope_layout = p.rope_layout;
+  // The ring holds the first SK_R slots of op `ring_op` (-1: nothing). It is not carried across an
+  // attention: the attention block needs the registers, and the o projection's first loads are issued
+  // right after it, while the attention output is waited for.
+  uint4 ring[SK_R];
+  int ring_op = -1;
 
-  // x_0 = emb[token]: each workgroup writes a slice
-  {
-    const int tok = p.state->token;
-    const int per = sk_cdiv(p.d, p.nwg);
-    for (int i = w * per + threadIdx.x; i < min(p.d, (w + 1) * per); i += SK_THREADS)
-      st_dev(LLMK_SK_X(0) + i, bf16_to_f32(p.emb[(int64_t)tok * p.d + i]));
-  }
-
-  // ---- the feed: which group of which phase the ring loads next ----
-  int fph = 0, fg = 0;
-  Phase ff = sk_phase(p, sp, 0, w);
-  while (fph < n_ph && ff.groups == 0) {
-    if (++fph < n_ph) ff = sk_phase(p, sp, fph, w);
-  }
-  uint4 ring[SK_RING];
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  // load j of the feed's current group; lanes with nothing to read load from w_out and hold zero, so every
-  // lane issues every load (straight-line code whose completion the compiler counts)
-#define LLMK_SK_FEED(J)                                                                       \
-  {                                                                                           \
-    const int u_ = fg * SK_RING + (J);                                                        \
-    const int r_ = u_ >> ff.sh, i_ = u_ & ((1 << ff.sh) - 1);                                 \
-    const int k_ = wave * ff.KS + i_ * SK_SEG + lane * 8;                                     \
-    const bool ok_ = fph < n_ph && r_ < ff.R && k_ < min((wave + 1) * ff.KS, ff.K);            \
-    const bf16_t* a_ = ok_ ? sk_row(p, s_layers, ff, r_) + k_ : p.w_out;                      \
-    const uint4 v_ = *reinterpret_cast<const uint4*>(a_);                                     \
-    ring[J] = ok_ ? v_ : zero;                                                                \
-  }
-#define LLMK_SK_FEED_NEXT()                                                                   \
-  if (fph < n_ph && ++fg == ff.groups) {                                                      \
-    fg = 0;                                                                                   \
-    do {                                                                                      \
-      if (++fph < n_ph) ff = sk_phase(p, sp, fph, w);                                         \
-    } while (fph < n_ph && ff.groups == 0);                                                   \
-  }
-#pragma unroll
-  for (int j = 0; j < SK_RING; ++j) LLMK_SK_FEED(j)
-  LLMK_SK_FEED_NEXT()
-
-  float best_v = -INFINITY;   // head: this workgroup's best logit so far (thread 0)
+  float best_v = -INFINITY;   // head: this wave's best logit and its row (lane 0)
   int best_i = INT_MAX;
 
-  for (int ph = 0; ph < n_ph; ++ph) {
-    const Phase f = sk_phase(p, sp, ph, w);
-    // ---- input of the phase ----
-    if (f.chunk == 0) {
-      if (f.kind == PK_O) {
-        if (!sk_barrier(p, ++bar_idx * nwg, &s_ok)) return;
-        // RoPE, K/V append and attention of layer l (this workgroup's items), merged output in att_l
-        const StepLayer& L = s_layers[f.l];
-        ap.qkv_raw = LLMK_SK_QKV(f.l);
-        ap.out = LLMK_SK_ATT(f.l);
-        ap.k = static_cast<const char*>(L.k) + p.kv_off * (int64_t)sizeof(T);
-        ap.v = static_cast<const char*>(L.v) + p.kv_off * (int64_t)sizeof(T);
-        ap.k_w = static_cast<char*>(L.k) + p.kv_off * (int64_t)sizeof(T);
-        ap.v_w = static_cast<char*>(L.v) + p.kv_off * (int64_t)sizeof(T);
-        for (int it = w; it < p.Hkv * p.attn_n_parts; it += p.nwg)
-          attn_block<T, HD>(ap, it / p.attn_n_parts, it % p.attn_n_parts, 0);
-      }
-      if (!sk_barrier(p, ++bar_idx * nwg, &s_ok)) return;
-      switch (f.kind) {
-        case PK_QKV: sk_stage_norm(LLMK_SK_X(2 * f.l), s_layers[f.l].g1, p.d, p.eps, vin, s_red); break;
-        case PK_O: sk_stage_copy(LLMK_SK_ATT(f.l), p.qd, vin); break;
-        case PK_GU: sk_stage_norm(LLMK_SK_X(2 * f.l + 1), s_layers[f.l].g2, p.d, p.eps, vin, s_red); break;
-        case PK_DN: sk_stage_copy(LLMK_SK_U(f.l), p.F, vin); break;
-        default: sk_stage_norm(LLMK_SK_X(2 * p.n_layer), p.g_final, p.d, p.eps, vin, s_red); break;
+  for (int o = 0; o < n_ops; ++o) {
+    const SkOp f = sk_op(p, R, s_layers, o, wave);
+    // the next op with loads for this wave: f's last block prefetches it unless an attention comes first
+    SkOp nx = sk_idle(p);
+    int o_next = n_ops;
+    if (f.npos > 0) {
+      for (int o2 = o + 1; o2 < n_ops; ++o2) {
+        const SkOp g = sk_op(p, R, s_layers, o2, wave);
+        if (g.npos > 0) {
+          nx = g;
+          o_next = o2;
+          break;
+        }
       }
     }
-    // ---- the phase's groups: row dots from the ring while the ring is refilled with the feed's next group
-    float acc = 0.0f;
-    const int lastld = (1 << f.sh) - 1;
-    for (int g = 0; g < f.groups; ++g) {
+    const bool prefetch = o_next < n_ops;
+    if (f.npos > 0 && ring_op != o && f.kind != OP_O) {
 #pragma unroll
-      for (int j = 0; j < SK_RING; ++j) {
-        const int u = g * SK_RING + j;
-        const int r = u >> f.sh, i = u & lastld;
-        // lanes with nothing to read hold zero in the ring; they read a clamped, valid part of vin
-        const int k = min(wave * f.KS + i * SK_SEG + lane * 8, f.K - 8);
-        const float4 v0 = *reinterpret_cast<const float4*>(vin + k);
-        const float4 v1 = *reinterpret_cast<const float4*>(vin + k + 4);
-        float wf[8];
-        unpack<bf16_t, 8>(ring[j], wf);
-        acc = fmaf(wf[0], v0.x, acc);
-        acc = fmaf(wf[1], v0.y, acc);
-        acc = fmaf(wf[2], v0.z, acc);
-        acc = fmaf(wf[3], v0.w, acc);
-        acc = fmaf(wf[4], v1.x, acc);
-        acc = fmaf(wf[5], v1.y, acc);
-        acc = fmaf(wf[6], v1.z, acc);
-        acc = fmaf(wf[7], v1.w, acc);
-        if (i == lastld) {
-          if (r < f.R) {
-            const float s = wave_sum_dpp(acc);
-            if (lane == 0) s_part[r][wave] = s;
-          }
-          acc = 0.0f;
-        }
-        LLMK_SK_FEED(j)
-      }
-      LLMK_SK_FEED_NEXT()
+      for (int j = 0; j < SK_R; ++j) ring[j] = gload<uint4>(sk_addr(f, j, wave, lane16));
     }
-    __syncthreads();
-    // ---- epilogue: the rows' sums over the waves, in wave order ----
-    const int t = threadIdx.x;
-    switch (f.kind) {
-      case PK_QKV:
-        if (t < f.R) {
-          float y = 0.0f;
+    // ---- the op's input ----
+    SkOut out;
+    out.tag = tag;
+    out.scale = 1.0f;
+    out.res = s_res;
+    out.hidden = nullptr;
+    out.logits = p.logits;
+    const int npad = SK_SEG << f.sh;
+    if (f.kind == OP_O) {
+      // RoPE, K/V append and attention of layer l: this workgroup's (K/V head, context part) items, the
+      // parts merged by the last workgroup of each K/V head into the tagged attention output
+      const SkLayer& Ly = s_layers[f.l];
+      const int ctx = pos + 1;
+      const int ch = p.attn_chunk;
+      const int n_sub = (ctx + ch - 1) / ch;
+      int target = nwg / p.Hkv;
+      target = target < 1 ? 1 : (target > ATTN_MAX_PARTS ? ATTN_MAX_PARTS : target);
+      const int spw = (n_sub + target - 1) / target;
+      const int n_parts = (n_sub + spw - 1) / spw;
+      AttnParams ap{};
+      ap.H = p.H;
+      ap.Hkv = p.Hkv;
+      ap.hd = HD;
+      ap.kv_is_bf16 = sizeof(T) == 2;
+      ap.state = p.state;
+      ap.chunk = ch;
+      ap.sub_per_wg = spw;
+      ap.n_parts = n_parts;
+      ap.part_tagged = p.attn_part;
+      ap.part_tag = tag * STEP_MAX_LAYERS + (uint32_t)f.l;
+      ap.rope_table = p.rope_table;
+      ap.rope_layout = p.rope_layout;
+      ap.k = static_cast<const char*>(Ly.k) + p.kv_off * (int64_t)sizeof(T);
+      ap.v = static_cast<const char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
+      ap.k_w = static_cast<char*>(Ly.k) + p.kv_off * (int64_t)sizeof(T);
+      ap.v_w = static_cast<char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
+      ap.qkv_tag = SK_QKV(f.l);
+      ap.out_tag = SK_ATT(f.l);
+      ap.tag = tag;
+      ap.err = p.err;
+      ap.qkv_flags = SK_FL(f.l, 0);
+      ap.n_qkv_flags = nwg;
+      ap.part_flags = SK_FL_PART(f.l);
+      ap.att_flags = SK_FL_ATT(f.l);
+      for (int it = w; it < p.Hkv * n_parts; it += nwg)
+        attn_block<T, HD, true>(ap, it / n_parts, it % n_parts, 0, s_big);
+      // the merges: query head hq by workgroup nwg - 1 - hq (from the end, away from the first items)
+      const int G = p.H / p.Hkv;
+      for (int hq = nwg - 1 - w; hq < p.H; hq += nwg) attn_merge_tagged<HD>(ap, hq / G, hq % G, n_parts);
+      __syncthreads();
+      if (f.npos > 0 && ring_op != o) {
 #pragma unroll
-          for (int q = 0; q < SK_WAVES; ++q) y += s_part[t][q];
-          st_dev(LLMK_SK_QKV(f.l) + f.row0 + t, y);
-        }
-        break;
-      case PK_O:
-      case PK_DN:
-        if (t < f.R) {
-          float y = 0.0f;
-#pragma unroll
-          for (int q = 0; q < SK_WAVES; ++q) y += s_part[t][q];
-          const int n = f.row0 + t;
-          const int v = 2 * f.l + (f.kind == PK_O ? 0 : 1);   // x_v + y -> x_{v+1}
-          const float xn = LLMK_SK_X(v)[n] + y;
-          st_dev(LLMK_SK_X(v + 1) + n, xn);
-          if (f.kind == PK_DN && p.hidden) p.hidden[(int64_t)f.l * p.d + n] = xn;
-        }
-        break;
-      case PK_GU:
-        if (t < f.R / 2) {
-          float g = 0.0f, up = 0.0f;
-#pragma unroll
-          for (int q = 0; q < SK_WAVES; ++q) {
-            g += s_part[t][q];
-            up += s_part[t + f.R / 2][q];
-          }
-          st_dev(LLMK_SK_U(f.l) + f.row0 + t, silu_f(g) * up);
-        }
-        break;
-      default: {   // head: logits and this chunk's best, folded into the workgroup's best
-        float v = -INFINITY;
-        int ix = INT_MAX;
-        if (t < f.R) {
-          float y = 0.0f;
-#pragma unroll
-          for (int q = 0; q < SK_WAVES; ++q) y += s_part[t][q];
-          v = y;
-          ix = f.row0 + t;
-          if (p.logits) p.logits[ix] = y;
-        }
-        wave_argmax(v, ix);
-        if (lane == 0) {
-          s_best_v[wave] = v;
-          s_best_i[wave] = ix;
-        }
-        __syncthreads();
-        if (t == 0) {
-          for (int q = 0; q < SK_WAVES; ++q)
-            if (argmax_better(s_best_v[q], s_best_i[q], best_v, best_i)) {
-              best_v = s_best_v[q];
-              best_i = s_best_i[q];
-            }
-        }
-        break;
+        for (int j = 0; j < SK_R; ++j) ring[j] = gload<uint4>(sk_addr(f, j, wave, lane16));
       }
+      sk_stage(SK_ATT(f.l), nullptr, p.qd, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed, SK_FL_ATT(f.l),
+               p.H);
+      out.y = SK_X(2 * f.l);
+    } else if (f.kind == OP_DN) {
+      __syncthreads();
+      sk_stage(SK_U(f.l), nullptr, p.F, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed, SK_FL(f.l, 2), nwg);
+      out.y = SK_X(2 * f.l + 1);
+      out.hidden = p.hidden ? p.hidden + (int64_t)f.l * p.d : nullptr;
+    } else {
+      // RMSNorm inputs: x before layer l (the embedding row for layer 0), x after layer l's o, final x
+      const uint64_t* src = nullptr;
+      const bf16_t* emb = nullptr;
+      const float* gain;
+      const uint32_t* fl = nullptr;
+      if (f.kind == OP_QKV) {
+        if (f.l == 0) emb = p.emb + (int64_t)tok * p.d;
+        else src = SK_X(2 * f.l - 1);
+        fl = f.l > 0 ? SK_FL(f.l - 1, 3) : nullptr;
+        gain = s_layers[f.l].g1;
+        out.y = SK_QKV(f.l);
+      } else if (f.kind == OP_GU) {
+        src = SK_X(2 * f.l);
+        fl = SK_FL(f.l, 1);
+        gain = s_layers[f.l].g2;
+        out.y = SK_U(f.l);
+      } else {
+        src = SK_X(2 * L - 1);
+        fl = SK_FL(L - 1, 3);
+        gain = p.g_final;
+        out.y = nullptr;
+      }
+      __syncthreads();
+      const float ss = sk_stage(src, emb, p.d, npad, tag, gain, f.kind == OP_HEAD ? nullptr : s_res, R.d.lo, R.d.n,
+                                vin, p.err, failed, fl, nwg);
+      out.scale = 1.0f / sqrtf(sk_block_sum(ss, s_red) / (float)p.d + p.eps);
     }
     __syncthreads();
-  }
-#undef LLMK_SK_FEED
-#undef LLMK_SK_FEED_NEXT
-#undef LLMK_SK_X
-#undef LLMK_SK_QKV
-#undef LLMK_SK_ATT
-#undef LLMK_SK_U
 
-  // ---- greedy token: each workgroup's best, the last one to arrive reduces them ----
+    // ---- the op's loads: dot from the ring, refill the ring ----
+    float y, y2;
+    sk_consume(ring, f, nx, prefetch, vin + lane * 4, wave, lane, lane16, y, y2);
+    if (f.npos > 0) ring_op = prefetch ? o_next : -1;
+    if (f.npos > 0) {
+      switch (f.kind) {
+        case OP_QKV: sk_rows_out<OP_QKV>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
+        case OP_O: sk_rows_out<OP_O>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
+        case OP_GU: sk_rows_out<OP_GU>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
+        case OP_DN: sk_rows_out<OP_DN>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
+        default: sk_rows_out<OP_HEAD>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
+      }
+    }
+    // this workgroup's part of the op is stored: its flag (every workgroup sets it, rows or not)
+    if (f.kind != OP_HEAD) set_flag(SK_FL(f.l, f.kind) + w, tag);
+  }
+#undef SK_X
+#undef SK_QKV
+#undef SK_ATT
+#undef SK_U
+#undef SK_FL
+#undef SK_FL_ATT
+#undef SK_FL_PART
+
+  // ---- greedy token: each workgroup's best, the last workgroup to finish reduces them ----
+  if (lane == 0) {
+    s_best_v[wave] = best_v;
+    s_best_i[wave] = best_i;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    st_dev(&p.head_val[w], best_v);
-    st_dev(&p.head_idx[w], best_i);
+    float v = s_best_v[0];
+    int ix = s_best_i[0];
+    for (int q = 1; q < SK_WAVES; ++q)
+      if (argmax_better(s_best_v[q], s_best_i[q], v, ix)) {
+        v = s_best_v[q];
+        ix = s_best_i[q];
+      }
+    st_dev(&p.head_val[w], v);
+    st_dev(&p.head_idx[w], ix);
     stores_done();
-    s_last = (take_ticket(p.head_cnt) == (unsigned)(p.nwg - 1));
+    s_last = (take_ticket(p.head_cnt) == (unsigned)(nwg - 1));
   }
   __syncthreads();
   if (!s_last) return;
   float v = -INFINITY;
   int ix = INT_MAX;
-  for (int b = threadIdx.x; b < p.nwg; b += SK_THREADS) {
+  for (int b = threadIdx.x; b < nwg; b += SK_THREADS) {
     const float bv = ld_dev(&p.head_val[b]);
     const int bi = ld_dev(&p.head_idx[b]);
-    if (argmax_better(bv, bi, v, ix)) { v = bv; ix = bi; }
+    if (argmax_better(bv, bi, v, ix)) {
+      v = bv;
+      ix = bi;
+    }
   }
   wave_argmax(v, ix);
   if (lane == 0) {
@@ -428,10 +664,13 @@ __global__ __launch_bounds__(SK_THREADS) void step_kernel(const StepParams p) {
     v = s_best_v[0];
     ix = s_best_i[0];
     for (int q = 1; q < SK_WAVES; ++q)
-      if (argmax_better(s_best_v[q], s_best_i[q], v, ix)) { v = s_best_v[q]; ix = s_best_i[q]; }
+      if (argmax_better(s_best_v[q], s_best_i[q], v, ix)) {
+        v = s_best_v[q];
+        ix = s_best_i[q];
+      }
     p.token_out[step] = ix;
     p.state->token = ix;
-    p.state->pos = p.state->pos + 1;
+    p.state->pos = pos + 1;
     p.state->step = step + 1;
     reset_ticket(p.head_cnt);
   }
@@ -453,7 +692,7 @@ static const void* step_kernel_ptr(int kv_is_bf16, int hd) {
   return nullptr;
 }
 
-int step_grid(int kv_is_bf16, int hd, int64_t vin_floats) {
+int step_grid(int kv_is_bf16, int hd) {
   const void* fn = step_kernel_ptr(kv_is_bf16, hd);
   if (!fn) return 0;
   int dev = 0;
@@ -461,22 +700,16 @@ int step_grid(int kv_is_bf16, int hd, int64_t vin_floats) {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, SK_THREADS, (size_t)vin_floats * sizeof(float)) !=
-      hipSuccess)
-    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, SK_THREADS, 0) != hipSuccess) return 0;
   return per_cu >= 1 ? cus : 0;
 }
 
-hipError_t step_launch(const StepParams& p, int kv_is_bf16, int64_t vin_floats, hipStream_t s) {
+hipError_t step_launch(const StepParams& p, int kv_is_bf16, hipStream_t s) {
   const void* fn = step_kernel_ptr(kv_is_bf16, p.hd);
   if (!fn || p.nwg < 1) return hipErrorInvalidValue;
   void* args[] = {const_cast<StepParams*>(&p)};
-  return hipLaunchKernel(fn, dim3((unsigned)p.nwg), dim3(SK_THREADS), args, (size_t)vin_floats * sizeof(float), s);
+  return hipLaunchKernel(fn, dim3((unsigned)p.nwg), dim3(SK_THREADS), args, 0, s);
 }
-
-}  // namespace llmk
-
-namespace llmk {
 
 // The layer table lives in the workspace; it is written by small kernels (layers passed by value, 8 at a
 // time), so filling it needs no host-to-device copy and can sit in a captured graph.
