@@ -184,34 +184,19 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     // of its values, then reloads until each carries the step's tag
     bool fl_failed = false;
     wait_flags(p.qkv_flags, p.n_qkv_flags, p.tag, p.err, fl_failed);
-    constexpr int NPT = ((8 + 2) * HDP + ATTN_THREADS - 1) / ATTN_THREADS;
     const int nval = (G + 2) * HD;
-    const uint64_t* src[NPT];
-    uint64_t got[NPT];
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      const int i = threadIdx.x + k * ATTN_THREADS;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned spins = 0;
+    for (int i = threadIdx.x; i < nval; i += ATTN_THREADS) {
       const int g = i / HD, e = i % HD;
       const int64_t idx = g < G ? (int64_t)(kvh * G + g) * HD + e
                                 : (int64_t)(p.H + (g - G) * p.Hkv) * HD + (int64_t)kvh * HD + e;
-      src[k] = i < nval ? p.qkv_tag + idx : p.qkv_tag;
-      got[k] = i < nval ? ld_tag(src[k]) : ((uint64_t)p.tag << 32);
-    }
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    unsigned spins = 0;
-    for (;;) {
-      bool ready = true;
-#pragma unroll
-      for (int k = 0; k < NPT; ++k) ready = ready && tag_of(got[k]) == p.tag;
-      if (ready || !tag_wait_more(p.err, t0, spins)) break;
-#pragma unroll
-      for (int k = 0; k < NPT; ++k)
-        if (tag_of(got[k]) != p.tag) got[k] = ld_tag(src[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      const int i = threadIdx.x + k * ATTN_THREADS;
-      if (i < nval) s_raw[i] = val_of(got[k]);
+      uint64_t got = ld_tag(p.qkv_tag + idx);
+      while (tag_of(got) != p.tag && !fl_failed) {
+        if (!tag_wait_more(p.err, t0, spins)) fl_failed = true;
+        got = ld_tag(p.qkv_tag + idx);
+      }
+      s_raw[i] = val_of(got);
     }
     __syncthreads();
   }
@@ -495,51 +480,55 @@ template <int HD>
 __device__ __forceinline__ void attn_merge_tagged(const AttnParams& p, const int kvh, const int g, const int n_parts) {
   constexpr int NS = ATTN_THREADS / HD;                         // part subsets
   constexpr int NPP = (ATTN_MAX_PARTS + NS - 1) / NS;           // parts per thread, at most
+  __shared__ float s_pm[ATTN_MAX_PARTS], s_pl[ATTN_MAX_PARTS];  // each part's max and sum
   __shared__ float s_m[ATTN_THREADS], s_l[ATTN_THREADS], s_o[ATTN_THREADS];
   const int G = p.H / p.Hkv;
   const int64_t pstride = HD + 2;
   const int e = threadIdx.x % HD, sub = threadIdx.x / HD;
   const uint64_t* PB = p.part_tagged + ((int64_t)kvh * n_parts * G + g) * pstride;
   const int64_t cstride = (int64_t)G * pstride;
-  bool fl_failed = false;
-  wait_flags(p.part_flags + (int64_t)kvh * ATTN_MAX_PARTS, n_parts, p.tag, p.err, fl_failed);
-  uint64_t m[NPP], l[NPP], o[NPP];
-  const uint64_t ok = (uint64_t)p.part_tag << 32;
+  bool failed = false;
+  wait_flags(p.part_flags + (int64_t)kvh * ATTN_MAX_PARTS, n_parts, p.tag, p.err, failed);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  unsigned spins = 0;
+  // a part's (max, sum): thread c < 2 n_parts waits for one of them
+  if (threadIdx.x < 2 * n_parts) {
+    const int c = threadIdx.x >> 1;
+    const uint64_t* src = PB + c * cstride + (threadIdx.x & 1);
+    uint64_t v = ld_tag(src);
+    while (tag_of(v) != p.part_tag && !failed) {
+      if (!tag_wait_more(p.err, t0, spins)) failed = true;
+      v = ld_tag(src);
+    }
+    ((threadIdx.x & 1) ? s_pl : s_pm)[c] = val_of(v);
+  }
+  // this thread's output element over its parts
+  uint64_t o[NPP];
 #pragma unroll
   for (int k = 0; k < NPP; ++k) {
     const int c = sub + k * NS;
-    m[k] = c < n_parts ? ld_tag(PB + c * cstride) : ok;
-    l[k] = c < n_parts ? ld_tag(PB + c * cstride + 1) : ok;
-    o[k] = c < n_parts ? ld_tag(PB + c * cstride + 2 + e) : ok;
+    o[k] = c < n_parts ? ld_tag(PB + c * cstride + 2 + e) : ((uint64_t)p.part_tag << 32);
   }
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  unsigned spins = 0;
-  for (;;) {
-    bool ready = true;
 #pragma unroll
-    for (int k = 0; k < NPP; ++k)
-      ready = ready && tag_of(m[k]) == p.part_tag && tag_of(l[k]) == p.part_tag && tag_of(o[k]) == p.part_tag;
-    if (ready || !tag_wait_more(p.err, t0, spins)) break;
-#pragma unroll
-    for (int k = 0; k < NPP; ++k) {
-      const int c = sub + k * NS;
-      if (c < n_parts) {
-        if (tag_of(m[k]) != p.part_tag) m[k] = ld_tag(PB + c * cstride);
-        if (tag_of(l[k]) != p.part_tag) l[k] = ld_tag(PB + c * cstride + 1);
-        if (tag_of(o[k]) != p.part_tag) o[k] = ld_tag(PB + c * cstride + 2 + e);
-      }
+  for (int k = 0; k < NPP; ++k) {
+    const int c = sub + k * NS;
+    while (tag_of(o[k]) != p.part_tag && !failed) {
+      if (!tag_wait_more(p.err, t0, spins)) failed = true;
+      o[k] = ld_tag(PB + c * cstride + 2 + e);
     }
   }
+  __syncthreads();
   float ms = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NPP; ++k)
-    if (sub + k * NS < n_parts) ms = fmaxf(ms, val_of(m[k]));
+    if (sub + k * NS < n_parts) ms = fmaxf(ms, s_pm[sub + k * NS]);
   float L = 0.0f, O = 0.0f;
 #pragma unroll
   for (int k = 0; k < NPP; ++k) {
-    if (sub + k * NS < n_parts) {
-      const float w = expf(val_of(m[k]) - ms);
-      L = fmaf(val_of(l[k]), w, L);
+    const int c = sub + k * NS;
+    if (c < n_parts) {
+      const float w = expf(s_pm[c] - ms);
+      L = fmaf(s_pl[c], w, L);
       O = fmaf(val_of(o[k]), w, O);
     }
   }

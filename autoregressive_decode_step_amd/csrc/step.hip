@@ -404,12 +404,11 @@ __device__ __forceinline__ void sk_block(uint4 (&ring)[SK_R], const SkOp& f, int
   }
 }
 
-// Consume the loads of op f from the ring while refilling each slot right after it is read: with the rest
-// of f, then (when `prefetch`) with the first SK_R slots of nx. Nothing but the ring's loads and the LDS
-// reads of the input touches memory in the loop, so every slot waits only for its own load; one copy of
-// the loop serves every op, which keeps the ring in the same registers throughout.
-__device__ __forceinline__ void sk_consume(uint4 (&ring)[SK_R], const SkOp& f, const SkOp& nx, bool prefetch,
-                                           const float* vl, int wave, int lane, int lane16, float& y, float& y2) {
+// Consume the loads of op f from the ring while refilling each slot right after it is read with the slot
+// SK_R further on (the last block refills nothing). Nothing but the ring's loads and the LDS reads of the
+// input touches memory in the loop, so every slot waits only for its own load.
+__device__ __forceinline__ void sk_consume(uint4 (&ring)[SK_R], const SkOp& f, const float* vl, int wave, int lane,
+                                           int lane16, float& y, float& y2) {
   float acc0 = 0.0f, acc1 = 0.0f;
   y = 0.0f;
   y2 = 0.0f;
@@ -417,8 +416,56 @@ __device__ __forceinline__ void sk_consume(uint4 (&ring)[SK_R], const SkOp& f, c
   int blk = 0;
   for (; blk + SK_R < f.npos; blk += SK_R)
     sk_block<true>(ring, f, blk, f, blk + SK_R, vl, wave, lane, lane16, acc0, acc1, y, y2);
-  if (prefetch) sk_block<true>(ring, f, blk, nx, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
-  else sk_block<false>(ring, f, blk, nx, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
+  sk_block<false>(ring, f, blk, f, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
+}
+
+// RoPE, K/V append and attention of layer l in the persistent step: this workgroup's (K/V head, context
+// part) items, then the merges it owns (query head hq by workgroup nwg - 1 - hq, from the end, away from
+// the first items), which write the tagged attention output. The tiles live in the dynamic LDS the staged
+// input uses between ops, and no weight load is in flight meanwhile, so the registers are its own.
+template <typename T, int HD>
+__device__ __forceinline__ void sk_attention(const StepParams* pp, int l, int pos, uint32_t tag) {
+  extern __shared__ uint4 sk_dyn[];
+  const StepParams p = *pp;
+  const int w = blockIdx.x;
+  const int nwg = p.nwg;
+  const StepLayer& Ly = p.layers[l];
+  const int ctx = pos + 1;
+  const int ch = p.attn_chunk;
+  const int n_sub = (ctx + ch - 1) / ch;
+  int target = nwg / p.Hkv;
+  target = target < 1 ? 1 : (target > ATTN_MAX_PARTS ? ATTN_MAX_PARTS : target);
+  const int spw = (n_sub + target - 1) / target;
+  const int n_parts = (n_sub + spw - 1) / spw;
+  uint32_t* fl = p.flags + (int64_t)l * p.fl_stride;
+  AttnParams ap{};
+  ap.H = p.H;
+  ap.Hkv = p.Hkv;
+  ap.hd = HD;
+  ap.kv_is_bf16 = sizeof(T) == 2;
+  ap.state = p.state;
+  ap.chunk = ch;
+  ap.sub_per_wg = spw;
+  ap.n_parts = n_parts;
+  ap.part_tagged = p.attn_part;
+  ap.part_tag = tag * STEP_MAX_LAYERS + (uint32_t)l;
+  ap.rope_table = p.rope_table;
+  ap.rope_layout = p.rope_layout;
+  ap.k = static_cast<const char*>(Ly.k) + p.kv_off * (int64_t)sizeof(T);
+  ap.v = static_cast<const char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
+  ap.k_w = static_cast<char*>(Ly.k) + p.kv_off * (int64_t)sizeof(T);
+  ap.v_w = static_cast<char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
+  ap.qkv_tag = p.qkv + (int64_t)l * p.qkv_stride;
+  ap.out_tag = p.att + (int64_t)l * p.att_stride;
+  ap.tag = tag;
+  ap.err = p.err;
+  ap.qkv_flags = fl;
+  ap.n_qkv_flags = nwg;
+  ap.att_flags = fl + 4 * nwg;
+  ap.part_flags = fl + 4 * nwg + p.H;
+  for (int it = w; it < p.Hkv * n_parts; it += nwg) attn_block<T, HD, true>(ap, it / n_parts, it % n_parts, 0, sk_dyn);
+  const int G = p.H / p.Hkv;
+  for (int hq = nwg - 1 - w; hq < p.H; hq += nwg) attn_merge_tagged<HD>(ap, hq / G, hq % G, n_parts);
 }
 
 template <typename T, int HD>
@@ -428,15 +475,16 @@ constexpr int sk_lds_vecs() {
 
 template <typename T, int HD>
 __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p) {
-  // the staged input vector and the attention tiles are never live together: one LDS region
-  __shared__ uint4 s_big[sk_lds_vecs<T, HD>()];
+  // the staged input vector and the attention tiles are never live together: one region of dynamic LDS
+  // (sk_lds_vecs<T, HD>() vectors)
+  extern __shared__ uint4 sk_dyn[];
   __shared__ SkLayer s_layers[STEP_MAX_LAYERS];
   __shared__ float s_res[STEP_MAX_RES];      // this workgroup's residual rows of x
   __shared__ float s_red[SK_WAVES];
   __shared__ float s_best_v[SK_WAVES];
   __shared__ int s_best_i[SK_WAVES];
   __shared__ int s_last;
-  float* vin = reinterpret_cast<float*>(s_big);
+  float* vin = reinterpret_cast<float*>(sk_dyn);
 
   const int w = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -478,32 +526,17 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
 #define SK_FL_ATT(LL) (p.flags + (int64_t)(LL) * p.fl_stride + 4 * nwg)
 #define SK_FL_PART(LL) (p.flags + (int64_t)(LL) * p.fl_stride + 4 * nwg + p.H)
 
-  // The ring holds the first SK_R slots of op `ring_op` (-1: nothing). It is not carried across an
-  // attention: the attention block needs the registers, and the o projection's first loads are issued
-  // right after it, while the attention output is waited for.
-  uint4 ring[SK_R];
-  int ring_op = -1;
 
   float best_v = -INFINITY;   // head: this wave's best logit and its row (lane 0)
   int best_i = INT_MAX;
 
   for (int o = 0; o < n_ops; ++o) {
     const SkOp f = sk_op(p, R, s_layers, o, wave);
-    // the next op with loads for this wave: f's last block prefetches it unless an attention comes first
-    SkOp nx = sk_idle(p);
-    int o_next = n_ops;
+    // The op's first SK_R loads go out before its input is waited for (after the attention for o, which
+    // needs the registers), so the weights stream while the producers finish.
+    if (f.kind == OP_O) sk_attention<T, HD>(&p, f.l, pos, tag);
+    uint4 ring[SK_R];
     if (f.npos > 0) {
-      for (int o2 = o + 1; o2 < n_ops; ++o2) {
-        const SkOp g = sk_op(p, R, s_layers, o2, wave);
-        if (g.npos > 0) {
-          nx = g;
-          o_next = o2;
-          break;
-        }
-      }
-    }
-    const bool prefetch = o_next < n_ops;
-    if (f.npos > 0 && ring_op != o && f.kind != OP_O) {
 #pragma unroll
       for (int j = 0; j < SK_R; ++j) ring[j] = gload<uint4>(sk_addr(f, j, wave, lane16));
     }
@@ -516,51 +549,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
     out.logits = p.logits;
     const int npad = SK_SEG << f.sh;
     if (f.kind == OP_O) {
-      // RoPE, K/V append and attention of layer l: this workgroup's (K/V head, context part) items, the
-      // parts merged by the last workgroup of each K/V head into the tagged attention output
-      const SkLayer& Ly = s_layers[f.l];
-      const int ctx = pos + 1;
-      const int ch = p.attn_chunk;
-      const int n_sub = (ctx + ch - 1) / ch;
-      int target = nwg / p.Hkv;
-      target = target < 1 ? 1 : (target > ATTN_MAX_PARTS ? ATTN_MAX_PARTS : target);
-      const int spw = (n_sub + target - 1) / target;
-      const int n_parts = (n_sub + spw - 1) / spw;
-      AttnParams ap{};
-      ap.H = p.H;
-      ap.Hkv = p.Hkv;
-      ap.hd = HD;
-      ap.kv_is_bf16 = sizeof(T) == 2;
-      ap.state = p.state;
-      ap.chunk = ch;
-      ap.sub_per_wg = spw;
-      ap.n_parts = n_parts;
-      ap.part_tagged = p.attn_part;
-      ap.part_tag = tag * STEP_MAX_LAYERS + (uint32_t)f.l;
-      ap.rope_table = p.rope_table;
-      ap.rope_layout = p.rope_layout;
-      ap.k = static_cast<const char*>(Ly.k) + p.kv_off * (int64_t)sizeof(T);
-      ap.v = static_cast<const char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
-      ap.k_w = static_cast<char*>(Ly.k) + p.kv_off * (int64_t)sizeof(T);
-      ap.v_w = static_cast<char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
-      ap.qkv_tag = SK_QKV(f.l);
-      ap.out_tag = SK_ATT(f.l);
-      ap.tag = tag;
-      ap.err = p.err;
-      ap.qkv_flags = SK_FL(f.l, 0);
-      ap.n_qkv_flags = nwg;
-      ap.part_flags = SK_FL_PART(f.l);
-      ap.att_flags = SK_FL_ATT(f.l);
-      for (int it = w; it < p.Hkv * n_parts; it += nwg)
-        attn_block<T, HD, true>(ap, it / n_parts, it % n_parts, 0, s_big);
-      // the merges: query head hq by workgroup nwg - 1 - hq (from the end, away from the first items)
-      const int G = p.H / p.Hkv;
-      for (int hq = nwg - 1 - w; hq < p.H; hq += nwg) attn_merge_tagged<HD>(ap, hq / G, hq % G, n_parts);
       __syncthreads();
-      if (f.npos > 0 && ring_op != o) {
-#pragma unroll
-        for (int j = 0; j < SK_R; ++j) ring[j] = gload<uint4>(sk_addr(f, j, wave, lane16));
-      }
       sk_stage(SK_ATT(f.l), nullptr, p.qd, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed, SK_FL_ATT(f.l),
                p.H);
       out.y = SK_X(2 * f.l);
@@ -601,8 +590,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
 
     // ---- the op's loads: dot from the ring, refill the ring ----
     float y, y2;
-    sk_consume(ring, f, nx, prefetch, vin + lane * 4, wave, lane, lane16, y, y2);
-    if (f.npos > 0) ring_op = prefetch ? o_next : -1;
+    sk_consume(ring, f, vin + lane * 4, wave, lane, lane16, y, y2);
     if (f.npos > 0) {
       switch (f.kind) {
         case OP_QKV: sk_rows_out<OP_QKV>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
@@ -692,15 +680,28 @@ static const void* step_kernel_ptr(int kv_is_bf16, int hd) {
   return nullptr;
 }
 
+static size_t step_lds_bytes(int kv_is_bf16, int hd) {
+  switch (hd) {
+#define LLMK_SK_CASE(H) \
+  case H: return 16 * (size_t)(kv_is_bf16 ? sk_lds_vecs<bf16_t, H>() : sk_lds_vecs<float, H>());
+    LLMK_SK_CASE(2) LLMK_SK_CASE(4) LLMK_SK_CASE(8) LLMK_SK_CASE(16) LLMK_SK_CASE(32) LLMK_SK_CASE(64)
+    LLMK_SK_CASE(128) LLMK_SK_CASE(256)
+#undef LLMK_SK_CASE
+  }
+  return 0;
+}
+
 int step_grid(int kv_is_bf16, int hd) {
   const void* fn = step_kernel_ptr(kv_is_bf16, hd);
   if (!fn) return 0;
+  const size_t lds = step_lds_bytes(kv_is_bf16, hd);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, SK_THREADS, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, SK_THREADS, lds) != hipSuccess) return 0;
   return per_cu >= 1 ? cus : 0;
 }
 
@@ -708,7 +709,7 @@ hipError_t step_launch(const StepParams& p, int kv_is_bf16, hipStream_t s) {
   const void* fn = step_kernel_ptr(kv_is_bf16, p.hd);
   if (!fn || p.nwg < 1) return hipErrorInvalidValue;
   void* args[] = {const_cast<StepParams*>(&p)};
-  return hipLaunchKernel(fn, dim3((unsigned)p.nwg), dim3(SK_THREADS), args, 0, s);
+  return hipLaunchKernel(fn, dim3((unsigned)p.nwg), dim3(SK_THREADS), args, step_lds_bytes(kv_is_bf16, p.hd), s);
 }
 
 // The layer table lives in the workspace; it is written by small kernels (layers passed by value, 8 at a
