@@ -93,6 +93,7 @@ _SIGS = {
     "llmk_decode_steps": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _i64,
                            _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_decode_kernel_count": ([ctypes.POINTER(Config)], _i64),
+    "llmk_decode_path": ([ctypes.POINTER(Config)], _i32),
     "llmk_transpose": ([_p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
     "llmk_decode_step_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                    _i64, _i64, _i64, _p, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
@@ -376,6 +377,13 @@ def decode_step_profiled(cfg: Config, model: Model, pool: KVPool, slot, token, p
 
 
 KERNEL_CLASSES = ("qkv", "attention", "o", "gate_up", "down", "head")
+STEP_KERNEL = 6   # decode_kernel_time: the persistent step kernel (one whole step per launch)
+
+
+def decode_path(cfg: Config) -> int:
+    """STEP_PER_OP or STEP_PERSISTENT: the form decode_step takes for cfg on the current device (or a status
+    code >= OK + 1 when cfg is refused)."""
+    return lib.llmk_decode_path(ctypes.byref(cfg))
 
 
 def decode_kernel_time(cfg: Config, model: Model, pool: KVPool, slot, token, pos, kernel, reps, token_out, ws,

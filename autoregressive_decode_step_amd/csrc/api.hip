@@ -287,7 +287,8 @@ int32_t pool_check(const llmk_config* c, const llmk_kv_pool* p) {
 }
 
 // The kernels of one decode step, in order: per layer K_QKV, K_ATTN, K_O, K_GATEUP, K_DOWN, then K_HEAD.
-enum StepKernel { K_QKV = 0, K_ATTN = 1, K_O = 2, K_GATEUP = 3, K_DOWN = 4, K_HEAD = 5, K_CLASSES = 6 };
+enum StepKernel { K_QKV = 0, K_ATTN = 1, K_O = 2, K_GATEUP = 3, K_DOWN = 4, K_HEAD = 5, K_CLASSES = 6,
+                  K_STEP = 6 /* the persistent step kernel (timing aid only) */ };
 
 // Launch kernel `which` of layer l (K_HEAD: the tail, l ignored). Token and position are read from D.state.
 hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, int64_t slot,
@@ -477,7 +478,7 @@ bool step_shape_ok(const llmk_config* c, int nwg) {
 
 // Workgroups of the persistent step for this call (0: run one kernel per operation). -1: refused.
 int step_workgroups(const llmk_config* c) {
-  if (c->step_path != LLMK_STEP_PERSISTENT) return 0;
+  if (c->step_path == LLMK_STEP_PER_OP) return 0;
   int nwg = step_grid(c->kv_dtype == LLMK_BF16, (int)c->head_dim);
   if (nwg > kStepMaxWG || !step_shape_ok(c, nwg)) nwg = 0;
   if (nwg == 0 && c->step_path == LLMK_STEP_PERSISTENT) return -1;
@@ -553,6 +554,54 @@ StepParams step_params(const llmk_config* c, const llmk_model* m, const llmk_kv_
   p.err = D.step_err;
   p.token_out = token_out;
   return p;
+}
+
+// llmk_decode_kernel_time for the persistent step kernel: `reps` steps from (token, pos) as one captured
+// launch replayed between two events, then the ordinary step at (token, pos) again.
+int32_t time_step_kernel(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                         int64_t token, int64_t pos, int32_t reps, int32_t* token_out, float* ms_per_launch_h,
+                         DecodePlan& D, hipStream_t s) {
+  const int nwg = step_workgroups(cfg);
+  if (nwg <= 0) return LLMK_INVALID_ARGUMENT;
+  if (pos + reps > pool->capacity) return LLMK_CACHE_CAPACITY_EXCEEDED;
+  hipStream_t cs = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = step_prelude(cfg, model, pool, D, (int32_t)token, (int32_t)pos, s);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t ee = step_launch(step_params(cfg, model, pool, slot, D, nwg, nullptr, nullptr, D.tok_scratch),
+                                cfg->kv_dtype == LLMK_BF16, cs);
+    e = hipStreamEndCapture(cs, &graph);
+    if (ee != hipSuccess) e = ee;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  for (int32_t r = 0; e == hipSuccess && r < reps; ++r) e = hipGraphLaunch(exec, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  int32_t err = 0;
+  if (e == hipSuccess) e = hipMemcpy(&err, D.step_err, sizeof(err), hipMemcpyDeviceToHost);
+  // the ordinary step at (token, pos): the K/V at pos and token_out as llmk_decode_step leaves them
+  if (e == hipSuccess) e = step_prelude(cfg, model, pool, D, (int32_t)token, (int32_t)pos, s);
+  if (e == hipSuccess)
+    e = step_launch(step_params(cfg, model, pool, slot, D, nwg, nullptr, nullptr, token_out), cfg->kv_dtype == LLMK_BF16, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (cs) (void)hipStreamDestroy(cs);
+  if (e != hipSuccess || err != 0) return LLMK_DEVICE_ERROR;
+  pool->slot_len_h[slot] = pos + 1;
+  *ms_per_launch_h = ms / (float)reps;
+  return LLMK_OK;
 }
 
 // Common checks of decode_step / decode_steps, in the documented order.
@@ -1279,13 +1328,22 @@ int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* mode
   return LLMK_OK;
 }
 
+int32_t llmk_decode_path(const llmk_config* cfg) {
+  if (!cfg) return LLMK_INVALID_ARGUMENT;
+  const int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return st;
+  const int nwg = step_workgroups(cfg);
+  if (nwg < 0) return LLMK_INVALID_ARGUMENT;
+  return nwg > 0 ? LLMK_STEP_PERSISTENT : LLMK_STEP_PER_OP;
+}
+
 int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                                 int64_t token, int64_t pos, int32_t kernel, int32_t reps, int32_t* token_out,
                                 float* ms_per_launch_h, void* ws, int64_t len_ws, void* stream) {
   if (!ms_per_launch_h) return LLMK_INVALID_ARGUMENT;
   int32_t st = decode_checks(cfg, model, pool, slot, token, pos, 1, token_out, ws);
   if (st != LLMK_OK) return st;
-  if (kernel < 0 || kernel >= K_CLASSES) return LLMK_INVALID_ARGUMENT;
+  if (kernel < 0 || kernel > K_STEP) return LLMK_INVALID_ARGUMENT;
   if (reps < 1) return LLMK_EMPTY_DIMENSION;
   if (reps > kTimeMaxReps) return LLMK_DIMENSION_TOO_LARGE;
   DecodePlan D;
@@ -1293,6 +1351,7 @@ int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model,
   if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
   plan_decode(cfg, ws, D);
   hipStream_t s = as_stream(stream);
+  if (kernel == K_STEP) return time_step_kernel(cfg, model, pool, slot, token, pos, reps, token_out, ms_per_launch_h, D, s);
   // one ordinary step leaves valid activations in the workspace; the state is then reset to (token, pos)
   // so that repeated attention launches stay at pos
   hipError_t e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);

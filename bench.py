@@ -25,7 +25,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 N_PRE = 4096                    # filled context before the first timed step
-PMC_FILE = os.path.join(ROOT, "profiles", "rowdot_gate_up_llama8b_pmc.md")
+PMC_FILES = {"gate_up": os.path.join(ROOT, "profiles", "rowdot_gate_up_llama8b_pmc.md"),
+             "step": os.path.join(ROOT, "profiles", "step_kernel_llama8b_pmc.md")}
+STEP_REPS = 64                  # consecutive steps in the persistent kernel's event timing
 
 
 def log(msg: str) -> None:
@@ -53,27 +55,31 @@ def gate_up_bytes(s) -> int:
     return 2 * s.d * s.hidden * wsz + 2 * s.d * 4 + s.hidden * 4
 
 
-def kernel_source_sha() -> str:
+KERNEL_SOURCES = {"gate_up": ("rowdot.hip", "common.h", "kernels.h"),
+                  "step": ("step.hip", "attn_block.h", "common.h", "kernels.h")}
+
+
+def kernel_source_sha(which: str = "gate_up") -> str:
     h = hashlib.sha256()
-    for f in ("rowdot.hip", "common.h", "kernels.h"):
+    for f in KERNEL_SOURCES[which]:
         with open(os.path.join(ROOT, "autoregressive_decode_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles():
-    """HBM bytes per gate|up launch from the committed counter summary ("key: value" lines), if its counters
-    were taken on the current kernel source; None otherwise."""
+def traffic_from_profiles(which: str):
+    """HBM bytes per launch of the dominant kernel (`which`: gate_up or step) from the committed counter
+    summary ("key: value" lines), if its counters were taken on the current kernel source; None otherwise."""
     rec = {}
     try:
-        with open(PMC_FILE) as f:
+        with open(PMC_FILES[which]) as f:
             for line in f:
                 k, sep, v = line.partition(":")
                 if sep:
                     rec[k.strip()] = v.strip()
     except OSError:
         return None
-    if rec.get("source_sha") != kernel_source_sha():
+    if rec.get("source_sha") != kernel_source_sha(which):
         return None
     try:
         return int(rec["hbm_bytes_per_launch"])
@@ -107,6 +113,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", choices=("batch1", "batched"), default="batch1",
                     help="batch1: the 8B-shaped single-sequence step (default); batched: 64 ragged sequences per step")
+    ap.add_argument("--step-path", choices=("auto", "per-op", "persistent"), default="auto",
+                    help="the decode step's form: the library's choice (default), one kernel per operation, or "
+                         "the persistent one-kernel step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -139,13 +148,18 @@ def main() -> int:
     prefix = synth.kv_prefix(s, N_PRE, seed=2)
     first = int(synth.prompt(1, s.vocab, stream=7)[0])
     log(f"generated in {time.time() - t_start:.1f} s; uploading")
-    cfg = loader.config_from(s)
+    path_arg = {"auto": llmk.STEP_AUTO, "per-op": llmk.STEP_PER_OP, "persistent": llmk.STEP_PERSISTENT}[args.step_path]
+    cfg = loader.config_from(s, step_path=path_arg)
+    path = llmk.decode_path(cfg)
+    if path not in (llmk.STEP_PER_OP, llmk.STEP_PERSISTENT):
+        raise RuntimeError(f"decode_path: {path} {llmk.status_name(path)}")
+    persistent = path == llmk.STEP_PERSISTENT
     model = loader.upload_model(cfg, W)
     pool = loader.new_pool(cfg, 1, s.max_seq)
     loader.fill_prefix(pool, 0, prefix)
     dec = loader.Decoder(cfg, model, pool)
     torch.cuda.synchronize()
-    log(f"resident in HBM after {time.time() - t_start:.1f} s")
+    log(f"resident in HBM after {time.time() - t_start:.1f} s; step form: {'persistent' if persistent else 'per-op'}")
 
     def run(n: int, out) -> None:
         done = 0
@@ -178,19 +192,34 @@ def main() -> int:
     tokens = toks.cpu().numpy().tolist()
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {step_gbps:.0f} GB/s algorithmic")
 
-    # per-kernel timing with HIP events on the stream the kernels run on: each class's launches (every layer,
-    # several times over) replayed back to back in one graph, as the step graph runs them
+    # kernel timing with HIP events on the stream the kernels run on
     pool.slot_len[0] = N_PRE
     avg_ms = {}
-    for k, n in enumerate(llmk.KERNEL_CLASSES):
-        st, ms = llmk.decode_kernel_time(cfg, model, pool, 0, first, N_PRE, k, args.kernel_reps, dec.token_out, dec.ws)
+    if persistent:
+        # the persistent form is one kernel per step: STEP_REPS consecutive steps replayed back to back
+        st, ms = llmk.decode_kernel_time(cfg, model, pool, 0, first, N_PRE, llmk.STEP_KERNEL, STEP_REPS,
+                                         dec.token_out, dec.ws)
         if st != llmk.OK:
-            raise RuntimeError(f"decode_kernel_time({n}): {st} {llmk.status_name(st)}")
-        avg_ms[n] = ms
+            raise RuntimeError(f"decode_kernel_time(step): {st} {llmk.status_name(st)}")
         pool.slot_len[0] = N_PRE
-    gu_bytes = gate_up_bytes(s)
-    gu_gbps = gu_bytes / (avg_ms["gate_up"] * 1e-3) / 1e9
-    kernel_sum_ms = sum(avg_ms[n] for n in llmk.KERNEL_CLASSES[:5]) * s.n_layer + avg_ms["head"]
+        avg_ms["step"] = ms
+        k_bytes = sum(step_bytes(s, N_PRE + 1 + i) for i in range(STEP_REPS)) / STEP_REPS
+        k_name = "persistent decode step (step_kernel, the whole step in one launch)"
+        kernel_sum_ms = ms
+    else:
+        # each class's launches (every layer, several times over) replayed back to back in one graph
+        for k, n in enumerate(llmk.KERNEL_CLASSES):
+            st, ms = llmk.decode_kernel_time(cfg, model, pool, 0, first, N_PRE, k, args.kernel_reps, dec.token_out,
+                                             dec.ws)
+            if st != llmk.OK:
+                raise RuntimeError(f"decode_kernel_time({n}): {st} {llmk.status_name(st)}")
+            avg_ms[n] = ms
+            pool.slot_len[0] = N_PRE
+        k_bytes = gate_up_bytes(s)
+        ms = avg_ms["gate_up"]
+        k_name = "gate|up row-dot GEMV (rowdot_kernel, GATEUP epilogue)"
+        kernel_sum_ms = sum(avg_ms[n] for n in llmk.KERNEL_CLASSES[:5]) * s.n_layer + avg_ms["head"]
+    k_gbps = k_bytes / (ms * 1e-3) / 1e9
     log("avg kernel us: " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in avg_ms.items()))
 
     result = {
@@ -213,10 +242,11 @@ def main() -> int:
         "step_hbm_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "step_bytes_mean": total_bytes / args.steps,
-        "roofline": {"bound": "hbm", "kernel": "gate|up row-dot GEMV (rowdot_kernel, GATEUP epilogue)",
-                     "achieved": gu_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gu_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic_from_profiles(), "bytes_per_launch": gu_bytes,
-                     "avg_launch_us": avg_ms["gate_up"] * 1e3},
+        "step_form": "persistent" if persistent else "per-op",
+        "roofline": {"bound": "hbm", "kernel": k_name,
+                     "achieved": k_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic_from_profiles("step" if persistent else "gate_up"),
+                     "bytes_per_launch": k_bytes, "avg_launch_us": ms * 1e3},
         "kernels_avg_us": {n: v * 1e3 for n, v in avg_ms.items()},
         "kernel_sum_ms_per_step": kernel_sum_ms,
         "first_tokens": tokens[:8],

@@ -89,7 +89,7 @@ typedef enum { LLMK_W_IN_OUT = 0, LLMK_W_OUT_IN = 1 } llmk_weight_layout;
 /* How llmk_decode_step / llmk_decode_steps run the step of one sequence. Both compute the same step
  * (the same arithmetic up to the order of fp32 sums). The persistent form needs bf16 weights in
  * LLMK_W_OUT_IN and a device that holds one of its workgroups per CU.
- *   LLMK_STEP_AUTO       the library's choice for this device and shape (currently one kernel per operation)
+ *   LLMK_STEP_AUTO       the persistent kernel where it can run, else one kernel per operation
  *   LLMK_STEP_PER_OP     one kernel per operation: 5 per layer (q|k|v, attention, o, gate|up, down) + head
  *   LLMK_STEP_PERSISTENT one kernel per step, the operations separated by grid barriers; refused (578)
  *                        where it cannot run */
@@ -361,16 +361,25 @@ int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* mode
                                   int64_t token, int64_t pos, int32_t* token_out, float* kernel_ms_h,
                                   int64_t len_kernel_ms, void* ws, int64_t len_ws, void* stream);
 
+/* Which form llmk_decode_step / llmk_decode_steps take for this config on the current device:
+ * LLMK_STEP_PER_OP or LLMK_STEP_PERSISTENT (AUTO resolved). Host-side; queries the device.
+ * Codes: the config's check code if it is invalid; 578 if the config asks for LLMK_STEP_PERSISTENT where it
+ * cannot run. */
+int32_t llmk_decode_path(const llmk_config* cfg);
+
 /* Measurement aid (not on the decode path): the average duration of one launch of one of the step's
  * kernel classes, timed the way the step runs it. kernel: 0 q|k|v, 1 attention, 2 o, 3 gate|up, 4 down,
- * 5 output head. Runs one ordinary decode step at (token, pos), captures that class's launches for every
+ * 5 output head (the kernels of the per-operation form), 6 the persistent step kernel (the whole step;
+ * 578 where the config does not run it). For 6 the `reps` launches are `reps` consecutive steps from
+ * (token, pos) replayed as one captured launch; they also write K/V rows at positions pos + 1 ..
+ * pos + reps - 1, past the slot's length (571 if pos + reps exceeds the capacity). Runs one ordinary decode step at (token, pos), captures that class's launches for every
  * layer (the head: once), `reps` times over, back to back into one HIP graph, replays it once between two
  * HIP events recorded on `stream`, then runs the ordinary step at (token, pos) once more. The repeated
  * launches work on the workspace only (the head's tokens go to workspace scratch, never to token_out), and
  * the final step rewrites what they disturbed, so the call leaves the pool, token_out (the greedy token)
  * and slot_len_h[slot] = pos + 1 exactly as llmk_decode_step does. *ms_per_launch_h (host) receives the
  * elapsed time divided by the number of launches. Synchronizes `stream`.
- * Codes: as llmk_decode_step; 578 if ms_per_launch_h is NULL or kernel is not 0..5; 561 if reps < 1; 564
+ * Codes: as llmk_decode_step; 578 if ms_per_launch_h is NULL or kernel is not 0..6; 561 if reps < 1; 564
  * if reps > 64. */
 int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                                 int64_t token, int64_t pos, int32_t kernel, int32_t reps, int32_t* token_out,
