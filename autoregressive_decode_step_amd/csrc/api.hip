@@ -152,8 +152,6 @@ struct DecodePlan {
   uint64_t* step_att = nullptr;
   uint64_t* step_u = nullptr;
   uint64_t* step_part = nullptr;        // attention parts as (value, tag) pairs
-  uint32_t* step_flags = nullptr;       // readiness flags [n_layer][step_fl_stride]
-  int64_t step_fl_stride = 0;
   int64_t step_x_stride = 0, step_qkv_stride = 0, step_att_stride = 0, step_u_stride = 0;
   int64_t bytes = 0;
   int n_gemv_counters = 0;
@@ -231,16 +229,13 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   const int64_t nx = 2 * c->n_layer * D.step_x_stride, nq = c->n_layer * D.step_qkv_stride;
   const int64_t na = c->n_layer * D.step_att_stride, nu = c->n_layer * D.step_u_stride;
   const int64_t np = attn_part_floats(c->n_head, c->head_dim);
-  D.step_fl_stride = (4 * kStepMaxWG + c->n_head + c->n_kv * ATTN_MAX_PARTS + 1) / 2 * 2;
-  const int64_t nf = c->n_layer * D.step_fl_stride / 2;   // in 8-byte units
-  D.step_tagged_n = nx + nq + na + nu + np + nf;
+  D.step_tagged_n = nx + nq + na + nu + np;
   D.step_tagged = cv.take<uint64_t>(D.step_tagged_n);
   D.step_x = D.step_tagged;
   D.step_qkv = D.step_x + nx;
   D.step_att = D.step_qkv + nq;
   D.step_u = D.step_att + na;
   D.step_part = D.step_u + nu;
-  D.step_flags = reinterpret_cast<uint32_t*>(D.step_part + np);
   D.bytes = cv.off;
 }
 
@@ -549,8 +544,6 @@ StepParams step_params(const llmk_config* c, const llmk_model* m, const llmk_kv_
   p.head_val = D.step_val;
   p.head_idx = D.step_idx;
   p.head_cnt = D.step_cnt;
-  p.flags = D.step_flags;
-  p.fl_stride = D.step_fl_stride;
   p.err = D.step_err;
   p.token_out = token_out;
   return p;

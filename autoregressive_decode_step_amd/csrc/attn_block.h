@@ -72,29 +72,6 @@ __device__ __forceinline__ bool tag_wait_more(int32_t* err, uint64_t t0, unsigne
   return true;
 }
 
-// Wait until flags[0..n) all equal tag (each producer workgroup stores its flag once its data is stored;
-// the data carries its own tag, so a flag only says when reading the data is worth it). Every thread of
-// the workgroup calls it; thread t watches flags t, t + ATTN_THREADS, ... It ends with a barrier.
-__device__ __forceinline__ void wait_flags(const uint32_t* flags, int n, uint32_t tag, int32_t* err, bool& failed) {
-  if (!failed) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    unsigned spins = 0;
-    for (int i = threadIdx.x; i < n && !failed; i += ATTN_THREADS)
-      while ((uint32_t)ld_dev(reinterpret_cast<const int*>(flags) + i) != tag)
-        if (!tag_wait_more(err, t0, spins)) {
-          failed = true;
-          break;
-        }
-  }
-  __syncthreads();
-}
-
-// this workgroup's flag: after a barrier (every wave's stores issued), one store
-__device__ __forceinline__ void set_flag(uint32_t* flag, uint32_t tag) {
-  __syncthreads();
-  if (threadIdx.x == 0) st_dev(reinterpret_cast<int*>(flag), (int)tag);
-}
-
 // One workgroup's share of the attention: context part `part` of K/V head `kvh` of batch row `row` (row 0
 // for a single sequence). Every thread of the workgroup (ATTN_THREADS) must call it with the same
 // arguments; it returns at the same point for all of them. `tiles` is LDS of attn_tile_vecs<T, HD>()
@@ -180,10 +157,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   const int pos = ctx - 1;
   const bool owner = (TAG || qkv_raw) && pos >= tb && pos < te;
   if constexpr (TAG) {
-    // wait for the q|k|v producers' flags, then for this group's q heads, k and v: every thread loads all
-    // of its values, then reloads until each carries the step's tag
+    // this group's q heads, k and v: every thread loads its values, then reloads until each carries the
+    // step's tag (the data is its own readiness signal)
     bool fl_failed = false;
-    wait_flags(p.qkv_flags, p.n_qkv_flags, p.tag, p.err, fl_failed);
+    __syncthreads();
     const int nval = (G + 2) * HD;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     unsigned spins = 0;
@@ -193,6 +170,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
                                 : (int64_t)(p.H + (g - G) * p.Hkv) * HD + (int64_t)kvh * HD + e;
       uint64_t got = ld_tag(p.qkv_tag + idx);
       while (tag_of(got) != p.tag && !fl_failed) {
+        __builtin_amdgcn_s_sleep(8);   // about 0.2 us between reloads of a whole vector
         if (!tag_wait_more(p.err, t0, spins)) fl_failed = true;
         got = ld_tag(p.qkv_tag + idx);
       }
@@ -405,7 +383,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       const int g = i / pstride, j = i % pstride;
       st_tag(&PT[i], j == 0 ? s_m1[g] : j == 1 ? s_l1[g] : s_o1[g][j - 2], p.part_tag);
     }
-    set_flag(p.part_flags + (int64_t)kvh * ATTN_MAX_PARTS + part, p.tag);
+    __syncthreads();
     return;
   }
   float* part_base = p.part + (batched ? (int64_t)row * p.Hkv * p.n_parts * G * pstride : 0);
@@ -488,7 +466,7 @@ __device__ __forceinline__ void attn_merge_tagged(const AttnParams& p, const int
   const uint64_t* PB = p.part_tagged + ((int64_t)kvh * n_parts * G + g) * pstride;
   const int64_t cstride = (int64_t)G * pstride;
   bool failed = false;
-  wait_flags(p.part_flags + (int64_t)kvh * ATTN_MAX_PARTS, n_parts, p.tag, p.err, failed);
+  __syncthreads();
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   unsigned spins = 0;
   // a part's (max, sum): thread c < 2 n_parts waits for one of them
@@ -547,7 +525,7 @@ __device__ __forceinline__ void attn_merge_tagged(const AttnParams& p, const int
     }
     st_tag(p.out_tag + (int64_t)(kvh * G + g) * HD + e, OO / LL, p.tag);
   }
-  set_flag(p.att_flags + kvh * G + g, p.tag);
+  __syncthreads();
 }
 
 }  // namespace llmk

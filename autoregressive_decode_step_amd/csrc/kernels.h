@@ -198,10 +198,6 @@ struct AttnParams {
   uint32_t tag;
   uint32_t part_tag;           // the parts' tag: unique per (step, layer), the part buffer serves every layer
   uint64_t* part_tagged;       // [Hkv][n_parts][G][hd + 2] (value, part_tag) pairs
-  const uint32_t* qkv_flags;   // the q|k|v producers' flags (n_qkv_flags), waited for before q|k|v is read
-  int32_t n_qkv_flags;
-  uint32_t* part_flags;        // [Hkv][ATTN_MAX_PARTS]: a part's flag, set once its record is stored
-  uint32_t* att_flags;         // [H]: a merged head's flag
   int32_t* err;
 };
 
@@ -251,10 +247,6 @@ struct StepParams {
   unsigned* head_cnt;           // zero on entry and exit
   int32_t* err;                 // set when a wait gives up
   int32_t* token_out;           // token of step s at token_out[s]
-  // readiness flags, [n_layer][fl_stride]: q|k|v [nwg], x after o [nwg], u [nwg], x after down [nwg],
-  // attention output [H], attention parts [Hkv][ATTN_MAX_PARTS]; a flag holds the tag of the step that set it
-  uint32_t* flags;
-  int64_t fl_stride;
 };
 
 constexpr int STEP_MAX_LAYERS = 128;   // layers the persistent step kernel supports

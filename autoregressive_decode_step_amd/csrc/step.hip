@@ -199,10 +199,8 @@ __device__ __forceinline__ int sk_vin_pos(int e) {
 // res: copy elements [res_lo, res_lo + res_n) unmultiplied to res. Returns this thread's sum of squares.
 __device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t* src_emb, int n, int npad,
                                           uint32_t tag, const float* gain, float* res, int res_lo, int res_n,
-                                          float* vin, int32_t* err, bool& failed, const uint32_t* flags,
-                                          int nflags) {
+                                          float* vin, int32_t* err, bool& failed) {
   const int t = threadIdx.x;
-  if (src_tag) wait_flags(flags, nflags, tag, err, failed);
   const int ng = (n / 4 + SK_THREADS - 1) / SK_THREADS;   // float4 groups per thread (uniform)
   float ss = 0.0f;
   for (int k0 = 0; k0 < ng; k0 += SK_PASS) {
@@ -250,6 +248,7 @@ __device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t*
           if (k0 + k < ng && e < n) ready = ready && a[k].y == tag && a[k].w == tag && b[k].y == tag && b[k].w == tag;
         }
         if (ready || failed) break;
+        __builtin_amdgcn_s_sleep(8);   // about 0.2 us between reloads of a whole vector
         if (!tag_wait_more(err, t0, spins)) {
           failed = true;
           break;
@@ -437,7 +436,6 @@ __device__ __forceinline__ void sk_attention(const StepParams* pp, int l, int po
   target = target < 1 ? 1 : (target > ATTN_MAX_PARTS ? ATTN_MAX_PARTS : target);
   const int spw = (n_sub + target - 1) / target;
   const int n_parts = (n_sub + spw - 1) / spw;
-  uint32_t* fl = p.flags + (int64_t)l * p.fl_stride;
   AttnParams ap{};
   ap.H = p.H;
   ap.Hkv = p.Hkv;
@@ -459,10 +457,6 @@ __device__ __forceinline__ void sk_attention(const StepParams* pp, int l, int po
   ap.out_tag = p.att + (int64_t)l * p.att_stride;
   ap.tag = tag;
   ap.err = p.err;
-  ap.qkv_flags = fl;
-  ap.n_qkv_flags = nwg;
-  ap.att_flags = fl + 4 * nwg;
-  ap.part_flags = fl + 4 * nwg + p.H;
   for (int it = w; it < p.Hkv * n_parts; it += nwg) attn_block<T, HD, true>(ap, it / n_parts, it % n_parts, 0, sk_dyn);
   const int G = p.H / p.Hkv;
   for (int hq = nwg - 1 - w; hq < p.H; hq += nwg) attn_merge_tagged<HD>(ap, hq / G, hq % G, n_parts);
@@ -522,9 +516,6 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
 #define SK_QKV(LL) (p.qkv + (int64_t)(LL) * p.qkv_stride)
 #define SK_ATT(LL) (p.att + (int64_t)(LL) * p.att_stride)
 #define SK_U(LL) (p.u + (int64_t)(LL) * p.u_stride)
-#define SK_FL(LL, K) (p.flags + (int64_t)(LL) * p.fl_stride + (K) * nwg)   // K: 0 q|k|v, 1 x after o, 2 u, 3 x after down
-#define SK_FL_ATT(LL) (p.flags + (int64_t)(LL) * p.fl_stride + 4 * nwg)
-#define SK_FL_PART(LL) (p.flags + (int64_t)(LL) * p.fl_stride + 4 * nwg + p.H)
 
 
   float best_v = -INFINITY;   // head: this wave's best logit and its row (lane 0)
@@ -550,12 +541,11 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
     const int npad = SK_SEG << f.sh;
     if (f.kind == OP_O) {
       __syncthreads();
-      sk_stage(SK_ATT(f.l), nullptr, p.qd, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed, SK_FL_ATT(f.l),
-               p.H);
+      sk_stage(SK_ATT(f.l), nullptr, p.qd, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
       out.y = SK_X(2 * f.l);
     } else if (f.kind == OP_DN) {
       __syncthreads();
-      sk_stage(SK_U(f.l), nullptr, p.F, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed, SK_FL(f.l, 2), nwg);
+      sk_stage(SK_U(f.l), nullptr, p.F, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
       out.y = SK_X(2 * f.l + 1);
       out.hidden = p.hidden ? p.hidden + (int64_t)f.l * p.d : nullptr;
     } else {
@@ -563,27 +553,23 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
       const uint64_t* src = nullptr;
       const bf16_t* emb = nullptr;
       const float* gain;
-      const uint32_t* fl = nullptr;
       if (f.kind == OP_QKV) {
         if (f.l == 0) emb = p.emb + (int64_t)tok * p.d;
         else src = SK_X(2 * f.l - 1);
-        fl = f.l > 0 ? SK_FL(f.l - 1, 3) : nullptr;
         gain = s_layers[f.l].g1;
         out.y = SK_QKV(f.l);
       } else if (f.kind == OP_GU) {
         src = SK_X(2 * f.l);
-        fl = SK_FL(f.l, 1);
         gain = s_layers[f.l].g2;
         out.y = SK_U(f.l);
       } else {
         src = SK_X(2 * L - 1);
-        fl = SK_FL(L - 1, 3);
         gain = p.g_final;
         out.y = nullptr;
       }
       __syncthreads();
       const float ss = sk_stage(src, emb, p.d, npad, tag, gain, f.kind == OP_HEAD ? nullptr : s_res, R.d.lo, R.d.n,
-                                vin, p.err, failed, fl, nwg);
+                                vin, p.err, failed);
       out.scale = 1.0f / sqrtf(sk_block_sum(ss, s_red) / (float)p.d + p.eps);
     }
     __syncthreads();
@@ -600,16 +586,13 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
         default: sk_rows_out<OP_HEAD>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
       }
     }
-    // this workgroup's part of the op is stored: its flag (every workgroup sets it, rows or not)
-    if (f.kind != OP_HEAD) set_flag(SK_FL(f.l, f.kind) + w, tag);
+    // every wave's row results are out before any wave issues the next op's first loads
+    __syncthreads();
   }
 #undef SK_X
 #undef SK_QKV
 #undef SK_ATT
 #undef SK_U
-#undef SK_FL
-#undef SK_FL_ATT
-#undef SK_FL_PART
 
   // ---- greedy token: each workgroup's best, the last workgroup to finish reduces them ----
   if (lane == 0) {
