@@ -32,6 +32,7 @@ constexpr int ATTN_STREAMS = 2;                       // tile streams per workgr
 constexpr int ATTN_SWAVES = 4;                        // waves per stream
 constexpr int ATTN_STHREADS = ATTN_SWAVES * 64;       // threads per stream
 constexpr int ATTN_MAXG_PER_WAVE = 2;                 // query heads per wave (G <= 8)
+static_assert(ATTN_THREADS % 128 == 0, "a thread's RoPE pair index is the same on every iteration for hd <= 256");
 
 // positions per tile for a row of `row_bytes`: at most 64, tile of one of K/V at most 16 KiB
 __host__ __device__ constexpr int attn_tile_rows(int row_bytes) {
@@ -156,6 +157,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   // rotates k, rounds k and v to the cache dtype, appends them to the cache and patches its tile.
   const int pos = ctx - 1;
   const bool owner = (TAG || qkv_raw) && pos >= tb && pos < te;
+  // the RoPE row of this position: a thread's first (cos, sin) pair is requested before q is waited for
+  constexpr int HALF = HD / 2;
+  const float* tab = p.rope_table + (int64_t)pos * HALF * 2;
+  const float2 cs_first = (TAG || qkv_raw) ? gload<float2>(tab + 2 * (threadIdx.x % HALF)) : make_float2(0.0f, 0.0f);
   if constexpr (TAG) {
     // this group's q heads, k and v: every thread loads its values, then reloads until each carries the
     // step's tag (the data is its own readiness signal)
@@ -179,13 +184,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     __syncthreads();
   }
   if (TAG || qkv_raw) {
-    constexpr int HALF = HD / 2;
-    const float* tab = p.rope_table + (int64_t)pos * HALF * 2;
     for (int i = threadIdx.x; i < (G + (owner ? 1 : 0)) * HALF; i += ATTN_THREADS) {
       const int g = i / HALF, j = i % HALF;
       const int ia = p.rope_layout == 0 ? j : 2 * j;
       const int ib = p.rope_layout == 0 ? j + HALF : 2 * j + 1;
-      const float cs = tab[2 * j], sn = tab[2 * j + 1];
+      // ATTN_THREADS is a multiple of HALF, so j is this thread's prefetched pair on every iteration
+      const float cs = cs_first.x, sn = cs_first.y;
       float a, b;
       if constexpr (TAG) {
         a = s_raw[g * HD + ia];
