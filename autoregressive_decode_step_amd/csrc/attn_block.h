@@ -98,7 +98,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   __shared__ float s_raw[TAG ? (8 + 2) * HDP : 1];     // TAG: this group's q heads, k and v as waited for
   __shared__ float s_p[ATTN_STREAMS][8][CH];
   __shared__ T s_new[2][HDP];                            // the appended k and v row (decode), cache dtype
-  __shared__ float s_m1[8], s_l1[8], s_o1[8][HDP];       // stream 1's softmax state, for the combine
+  // stream 1's softmax state for the combine, in the tile buffer once the tiles are consumed (keeping it
+  // out of the static LDS lets two workgroups share a CU)
+  static_assert(16 + 8 * HDP <= 4 * attn_tile_vecs<T, HD>(), "combine state fits the tile buffer");
+  float* const s_m1 = reinterpret_cast<float*>(tiles);
+  float* const s_l1 = s_m1 + 8;
+  float (&s_o1)[8][HDP] = *reinterpret_cast<float (*)[8][HDP]>(s_m1 + 16);
   __shared__ int s_last;
 
   const int G = p.H / p.Hkv;
@@ -332,7 +337,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
 #pragma unroll
       for (int off = LPV; off < 64; off <<= 1) o[gi][k] += __shfl_xor(o[gi][k], off, 64);
 
-  // ---- stream 1 hands its (max, sum, output) to stream 0 through LDS ----
+  // ---- stream 1 hands its (max, sum, output) to stream 0 through LDS (the tile buffer: every wave is done
+  // with the tiles first) ----
+  __syncthreads();
   if (st == 1) {
 #pragma unroll
     for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
