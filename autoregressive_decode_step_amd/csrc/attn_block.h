@@ -94,7 +94,22 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   constexpr int HDP = HD < 4 ? 4 : HD;
 
   uint4 (&s_kv)[ATTN_STREAMS][2][CH][RS] = *reinterpret_cast<uint4 (*)[ATTN_STREAMS][2][CH][RS]>(tiles);
-  __shared__ float s_q[8][HDP];
+  // Scores on the matrix cores for bf16 K/V with HD a multiple of 32 and 64-position tiles: q is kept as
+  // bf16 hi + lo parts (about 16 significant bits) and each score is taken twice (q hi . K + q lo . K) into fp32
+  constexpr bool MF = sizeof(T) == 2 && HD % 32 == 0 && CH == 16 * ATTN_SWAVES;
+  __shared__ float s_q[MF ? 1 : 8][HDP];
+  __shared__ __align__(16) bf16_t s_qh[MF ? 8 : 1][MF ? HD : 8];
+  __shared__ __align__(16) bf16_t s_ql[MF ? 8 : 1][MF ? HD : 8];
+  auto put_q = [&](int g, int e, float v) {
+    if constexpr (MF) {
+      bf16_t hi, lo;
+      split_bf16(v, hi, lo);
+      s_qh[g][e] = hi;
+      s_ql[g][e] = lo;
+    } else {
+      s_q[g][e] = v;
+    }
+  };
   __shared__ float s_raw[TAG ? (8 + 2) * HDP : 1];     // TAG: this group's q heads, k and v as waited for
   __shared__ float s_p[ATTN_STREAMS][8][CH];
   __shared__ T s_new[2][HDP];                            // the appended k and v row (decode), cache dtype
@@ -207,8 +222,8 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       }
       const float ra = a * cs - b * sn, rb = a * sn + b * cs;
       if (g < G) {
-        s_q[g][ia] = ra;
-        s_q[g][ib] = rb;
+        put_q(g, ia, ra);
+        put_q(g, ib, rb);
       } else {
         store_elem<T>(&s_new[0][0], ia, ra);
         store_elem<T>(&s_new[0][0], ib, rb);
@@ -231,7 +246,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       }
     }
   } else {
-    for (int i = threadIdx.x; i < G * HD; i += ATTN_THREADS) s_q[i / HD][i % HD] = p.q[(int64_t)kvh * G * HD + i];
+    for (int i = threadIdx.x; i < G * HD; i += ATTN_THREADS) put_q(i / HD, i % HD, p.q[(int64_t)kvh * G * HD + i]);
   }
 
   // per wave and query head: running max and sum (uniform), and a partial output per lane for the
@@ -271,6 +286,35 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     const int n = act ? min(CH, te - t0) : 0;
 
     // scores and softmax statistics: wave w takes heads w, w + 4; lane t scores position t0 + t
+    if constexpr (MF) {
+      // S = Q K^T, 16 x 16 blocks: wave w of the stream takes positions 16w .. 16w + 15 of the tile for
+      // every head (lane l: q row l % 16 and K row 16w + l % 16, dims 8 (l / 16) .. + 7 of each 32-wide step;
+      // result: heads 4 (l / 16) .. + 3 of position 16w + l % 16); the scores go to s_p
+      static_assert(CH == 16 * ATTN_SWAVES, "one 16-position block per wave");
+      if (act) {
+        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const int m = lane & 15, kg = lane >> 4;
+        const int prow = wave * 16 + m;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < HD / 32; ++ks) {
+          const uint4 kb = s_kv[st][0][prow][ks * 4 + kg];
+          const uint4 qh = m < G ? *reinterpret_cast<const uint4*>(&s_qh[m][ks * 32 + 8 * kg]) : make_uint4(0, 0, 0, 0);
+          const uint4 ql = m < G ? *reinterpret_cast<const uint4*>(&s_ql[m][ks * 32 + 8 * kg]) : make_uint4(0, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qh), __builtin_bit_cast(bf16x8_t, kb),
+                                                         acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ql), __builtin_bit_cast(bf16x8_t, kb),
+                                                         acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = 4 * kg + i;
+          if (g < G) s_p[st][g][prow] = prow < n ? acc[i] * scale : -INFINITY;
+        }
+      }
+      __syncthreads();
+    }
     float alpha_g[ATTN_MAXG_PER_WAVE];
 #pragma unroll
     for (int gi = 0; gi < ATTN_MAXG_PER_WAVE; ++gi) {
@@ -278,7 +322,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       alpha_g[gi] = 1.0f;
       if (g < G && act) {
         float s = -INFINITY;
-        if (lane < CH) {
+        if constexpr (MF) {
+          s = s_p[st][g][lane];
+        } else if (lane < CH) {
           float part8[EPV];
 #pragma unroll
           for (int e = 0; e < EPV; ++e) part8[e] = 0.0f;
