@@ -618,6 +618,7 @@ int32_t decode_checks(const llmk_config* cfg, const llmk_model* model, const llm
 // ---- batched decode ------------------------------------------------------------------------------------
 
 constexpr int kBatchTargetBlocks = 256;   // the matrix-core kernels hold one workgroup per CU
+constexpr int kBatchAttnTilesPerPart = 10;
 
 struct BatchPlan {
   int64_t B = 0;
@@ -668,7 +669,9 @@ void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P) {
   P.attn.Hkv = (int32_t)c->n_kv;
   P.attn.hd = (int32_t)c->head_dim;
   P.attn.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
-  attn_plan(P.attn, c->max_seq);
+  // every row of the batch brings its own (row, K/V head) pairs, so parts can be long: about 10 tiles each
+  // (measured on the 64-row, 8,320-position pool: 258 us per layer against 312 us at the batch-1 split)
+  attn_plan(P.attn, c->max_seq, kBatchAttnTilesPerPart);
   P.attn.rows = (int32_t)B;
 
   Carve cv(ws);

@@ -203,7 +203,8 @@ struct AttnParams {
 
 constexpr int ATTN_MAX_PARTS = 32;
 // Fills chunk / sub_per_wg / n_parts for contexts up to max_ctx.
-void attn_plan(AttnParams& p, int64_t max_ctx);
+// min_tiles_per_part: the fewest tiles one part should take (parts are capped at ATTN_MAX_PARTS either way).
+void attn_plan(AttnParams& p, int64_t max_ctx, int64_t min_tiles_per_part = 1);
 hipError_t attn_launch(const AttnParams& p, hipStream_t s);
 inline int64_t attn_part_floats(int64_t H, int64_t hd) { return (int64_t)ATTN_MAX_PARTS * H * (hd + 2); }
 
