@@ -253,6 +253,26 @@ def argmax(logits=True, len_logits=0, rows=0, n=0, token=True, ws=True, ws_short
     return INVALID if ws_short else OK
 
 
+SAMPLE_MAX_K = 1024   # survivors the GPU sampler holds (top-k after clamping to n; 1 at temperature 0)
+
+
+def sample(logits=True, len_logits=0, rows=0, n=0, temperature=1.0, top_k=0, top_p=1.0, u=True, len_u=0,
+           token=True):
+    if not (logits and u and token):
+        return INVALID
+    c = _dims(rows, n)
+    if c != OK:
+        return c
+    if len_logits != rows * n:
+        return LOGITS_LEN
+    if len_u != rows:
+        return B_LEN
+    if not (temperature >= 0.0) or not (0.0 < top_p <= 1.0):
+        return INVALID
+    k = 1 if temperature == 0.0 else (n if top_k <= 0 or top_k >= n else top_k)
+    return TOO_LARGE if k > SAMPLE_MAX_K else OK
+
+
 def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head):
     """(status, offset): offset = slot*plane + pos*n_kv*hd + kv_head*hd, plane = capacity*n_kv*hd
     (the pool layout of "Inside the engine", section "3. The K/V cache and the block store")."""
