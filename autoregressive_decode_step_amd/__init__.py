@@ -86,6 +86,8 @@ _SIGS = {
     "llmk_gqa_attend": ([_p, _i64, _p, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_argmax_workspace_bytes": ([_i64, _i64], _i64),
     "llmk_argmax": ([_p, _i64, _i64, _i64, _p, _p, _p, _i64, _p], _i32),
+    "llmk_sample_workspace_bytes": ([_i64, _i64, _f32, _i32], _i64),
+    "llmk_sample": ([_p, _i64, _i64, _i64, _f32, _i32, _f32, _p, _i64, _p, _p, _i64, _p], _i32),
     "llmk_kv_slot_offset": ([ctypes.POINTER(PoolStruct), _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
     "llmk_decode_workspace_bytes": ([ctypes.POINTER(Config), _i64], _i64),
     "llmk_decode_step": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _i64,
@@ -247,6 +249,15 @@ def argmax_workspace_bytes(rows, n) -> int:
 def argmax(logits, rows, n, token, logit, ws, stream=None) -> int:
     return lib.llmk_argmax(_ptr(logits), _len(logits), rows, n, _ptr(token), _ptr(logit), _ptr(ws), _len(ws),
                            _stream(stream))
+
+
+def sample_workspace_bytes(rows, n, temperature, top_k) -> int:
+    return lib.llmk_sample_workspace_bytes(rows, n, temperature, top_k)
+
+
+def sample(logits, rows, n, temperature, top_k, top_p, u, token, ws=None, stream=None) -> int:
+    return lib.llmk_sample(_ptr(logits), _len(logits), rows, n, temperature, top_k, top_p, _ptr(u), _len(u),
+                           _ptr(token), _ptr(ws), _len(ws), _stream(stream))
 
 
 # ---------------------------------------------------------------------------------------------------------

@@ -1108,6 +1108,30 @@ int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64
   return finish(argmax_launch(logits, rows, n, token, logit, pv, pi, cnt, (int32_t)bpr, as_stream(stream)));
 }
 
+int64_t llmk_sample_workspace_bytes(int64_t rows, int64_t n, float temperature, int32_t top_k) {
+  int32_t st = dims_check({rows, n});
+  if (st != LLMK_OK) return -st;
+  const int64_t k = temperature == 0.0f ? 1 : (top_k <= 0 || top_k >= n ? n : top_k);
+  if (k > LLMK_SAMPLE_MAX_K) return -LLMK_DIMENSION_TOO_LARGE;
+  return sample_workspace_bytes(rows, n, (int32_t)k);
+}
+
+int32_t llmk_sample(const float* logits, int64_t len_logits, int64_t rows, int64_t n, float temperature,
+                    int32_t top_k, float top_p, const float* u, int64_t len_u, int32_t* token, void* ws,
+                    int64_t len_ws, void* stream) {
+  if (!logits || !u || !token) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, n});
+  if (st != LLMK_OK) return st;
+  if (len_logits != rows * n) return LLMK_LOGITS_LENGTH_MISMATCH;
+  if (len_u != rows) return LLMK_B_LENGTH_MISMATCH;
+  if (!(temperature >= 0.0f) || !(top_p > 0.0f && top_p <= 1.0f)) return LLMK_INVALID_ARGUMENT;
+  const int64_t k = temperature == 0.0f ? 1 : (top_k <= 0 || top_k >= n ? n : top_k);
+  if (k > LLMK_SAMPLE_MAX_K || rows > LLMK_SAMPLE_MAX_ROWS) return LLMK_DIMENSION_TOO_LARGE;
+  const int64_t need = sample_workspace_bytes(rows, n, (int32_t)k);
+  if (need > 0 && (!ws || len_ws < need || !aligned16(ws))) return LLMK_INVALID_ARGUMENT;
+  return finish(sample_launch(logits, rows, n, temperature, (int32_t)k, top_p, u, token, ws, as_stream(stream)));
+}
+
 int32_t llmk_kv_slot_offset(const llmk_kv_pool* pool, int64_t slot, int64_t pos, int64_t kv_head, int64_t* offset_h) {
   if (!pool || !offset_h) return LLMK_INVALID_ARGUMENT;
   if (slot < 0 || slot >= pool->n_slots) return LLMK_SLOT_OUT_OF_RANGE;

@@ -274,6 +274,17 @@ hipError_t rope_table_launch(float* table, int64_t max_pos, int64_t hd, double b
 hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, int64_t pos0,
                        const float* table, int layout, hipStream_t s);
 hipError_t kv_append_launch(void* cache, int is_bf16, int64_t offset, const float* src, int64_t n, hipStream_t s);
+constexpr int SAMPLE_MAX_K = 1024;   // survivors (top-k after clamping to the row length) the sampler holds
+enum SampleForm { SAMPLE_WIDE = 0, SAMPLE_WAVE_SLICES = 1, SAMPLE_BLOCK_SLICES = 2 };
+struct SamplePlan {
+  int form;        // SampleForm
+  int slices;      // per row (1 for the wide form)
+  int64_t chunk;   // logits per slice
+};
+SamplePlan sample_plan(int64_t n, int32_t k);
+int64_t sample_workspace_bytes(int64_t rows, int64_t n, int32_t k);
+hipError_t sample_launch(const float* logits, int64_t rows, int64_t n, float temperature, int32_t k, float top_p,
+                         const float* draw, int32_t* token, void* ws, hipStream_t s);
 hipError_t argmax_launch(const float* logits, int64_t rows, int64_t n, int32_t* token, float* logit, float* part_val,
                          int32_t* part_idx, unsigned* counters, int32_t blocks_per_row, hipStream_t s);
 hipError_t fill_u32_launch(unsigned* p, int64_t n, unsigned v, hipStream_t s);

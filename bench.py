@@ -102,6 +102,43 @@ def copy_probe(mib: int) -> int:
     return 0
 
 
+def sample_probe(rows: int, reps: int = 50) -> int:
+    """Only the sampling exit: llmk_sample over `rows` vocabulary rows (128,256 logits, N(0, 3)) at
+    temperature 0.8, top-k 50, top-p 0.95, timed with HIP events over `reps` launches."""
+    import torch
+
+    import synth
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd.loader import to_device
+    n = synth.L8B.vocab
+    logits = to_device(synth.normal((rows, n), 600, 0, 3.0).ravel(), "cuda")
+    u = to_device(synth.draws((rows,), 601, 0), "cuda")
+    tok = torch.empty(rows, dtype=torch.int32, device="cuda")
+    ws = llmk.workspace(llmk.sample_workspace_bytes(rows, n, 0.8, 50))
+    stream = torch.cuda.current_stream()
+
+    def once():
+        st = llmk.sample(logits, rows, n, 0.8, 50, 0.95, u, tok, ws)
+        if st != llmk.OK:
+            raise RuntimeError(f"llmk_sample: {st} {llmk.status_name(st)}")
+
+    for _ in range(5):
+        once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        once()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    alg = rows * n * 4
+    print(json.dumps({"sample_probe": {"rows": rows, "n": n, "temperature": 0.8, "top_k": 50, "top_p": 0.95,
+                                       "us_per_launch": round(us, 2), "algorithmic_bytes": alg,
+                                       "achieved_GBps": round(alg / us / 1e3, 1)}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +155,8 @@ def main() -> int:
                          "the persistent one-kernel step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--sample-probe", type=int, default=0, metavar="ROWS",
+                    help="only time the sampling exit over ROWS vocabulary rows and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -137,6 +176,8 @@ def main() -> int:
         return 3
     if args.copy_probe > 0:
         return copy_probe(args.copy_probe)
+    if args.sample_probe > 0:
+        return sample_probe(args.sample_probe)
     if args.workload == "batched":
         return run_batched(args)
 

@@ -222,6 +222,31 @@ int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n);
 int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token,
                     float* logit, void* ws, int64_t len_ws, void* stream);
 
+/* Survivors llmk_sample holds: top_k after clamping to n (1 at temperature 0); rows one call takes. */
+#define LLMK_SAMPLE_MAX_K 1024
+#define LLMK_SAMPLE_MAX_ROWS 65535
+
+/* Workspace bytes llmk_sample needs for these sizes (0: none), or -status for invalid sizes. */
+int64_t llmk_sample_workspace_bytes(int64_t rows, int64_t n, float temperature, int32_t top_k);
+
+/* One draw per row of logits ([dops] "Method": the HuggingFace warper order, temperature, then top-k, then
+ * top-p over the renormalised survivors, survivors in descending logit order with ties to the lower index,
+ * and the token is the inverse CDF at an explicit uniform draw). top-p keeps a survivor while the mass of
+ * the survivors before it is below top_p (the first is always kept); the token is the first kept survivor
+ * whose cumulative renormalised probability exceeds u[r]. temperature 0 is greedy (the lowest index
+ * holding the row maximum). A NaN logit counts as -inf and -0 as +0; a draw below 0 or NaN counts as 0, a
+ * draw of 1 or more takes the last kept survivor with mass. The same row and draw always give the same
+ * token (no float atomics).
+ *   logits: device fp32 [rows][n]; u: device fp32 [rows], one draw in [0, 1) per row; token: device int32
+ *   [rows]. top_k <= 0 or >= n means n. ws: device scratch of len_ws >= llmk_sample_workspace_bytes bytes,
+ *   16-byte aligned (may be NULL when that is 0); its contents need no clearing and are dead after the call.
+ * Codes: 578 (null logits/u/token), 561, 564, 568 (len_logits != rows*n), 563 (len_u != rows), 578
+ * (temperature < 0 or NaN, top_p not in (0, 1]), 564 (survivors min(top_k, n) > LLMK_SAMPLE_MAX_K at a
+ * temperature above 0, or rows > LLMK_SAMPLE_MAX_ROWS), 578 (workspace missing, short or misaligned). */
+int32_t llmk_sample(const float* logits, int64_t len_logits, int64_t rows, int64_t n, float temperature,
+                    int32_t top_k, float top_p, const float* u, int64_t len_u, int32_t* token, void* ws,
+                    int64_t len_ws, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Model, K/V pool and the decode step                                        */
 /* ------------------------------------------------------------------------- */

@@ -254,10 +254,12 @@ def argmax(logits=True, len_logits=0, rows=0, n=0, token=True, ws=True, ws_short
 
 
 SAMPLE_MAX_K = 1024   # survivors the GPU sampler holds (top-k after clamping to n; 1 at temperature 0)
+SAMPLE_MAX_ROWS = 65535   # rows one sampler call takes
 
 
 def sample(logits=True, len_logits=0, rows=0, n=0, temperature=1.0, top_k=0, top_p=1.0, u=True, len_u=0,
-           token=True):
+           token=True, ws_short=False):
+    """ws_short: the call needs a workspace (llmk_sample_workspace_bytes > 0) and gets none or too little."""
     if not (logits and u and token):
         return INVALID
     c = _dims(rows, n)
@@ -270,7 +272,9 @@ def sample(logits=True, len_logits=0, rows=0, n=0, temperature=1.0, top_k=0, top
     if not (temperature >= 0.0) or not (0.0 < top_p <= 1.0):
         return INVALID
     k = 1 if temperature == 0.0 else (n if top_k <= 0 or top_k >= n else top_k)
-    return TOO_LARGE if k > SAMPLE_MAX_K else OK
+    if k > SAMPLE_MAX_K or rows > SAMPLE_MAX_ROWS:
+        return TOO_LARGE
+    return INVALID if ws_short else OK
 
 
 def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head):

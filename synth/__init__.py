@@ -75,6 +75,11 @@ def ints(shape, lo: int, hi: int, seed: int, stream: int) -> np.ndarray:
     return out
 
 
+def draws(shape, seed: int, stream: int) -> np.ndarray:
+    """Seeded uniform draws in [0, 1) on the grid k / 2^24, float32 (every value exact in fp32 and fp64)."""
+    return (ints(shape, 0, (1 << 24) - 1, seed, stream).astype(np.float64) / float(1 << 24)).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------------------------
 # Workload shapes
 # ----------------------------------------------------------------------------------------------

@@ -165,6 +165,49 @@ def test_attend_and_argmax_refusals():
     assert L.llmk_argmax(FAKE, 128256, 1, 128256, FAKE, None, FAKE, need - 1, None) == 578
 
 
+@no_gpu
+def test_sample_refusals():
+    L = llmk.lib
+    nan = float("nan")
+    cases = itertools.product([0, 1, 3], [0, 7, 2000], [0, 1], [-1.0, nan, 0.0, 0.7], [0, 1, 5, 1024, 1025],
+                              [0.0, 0.5, 1.0, 1.5], [0, 1, 3])
+    for rows, n, bad_len, t, k, p, lu in cases:
+        ll = rows * n + bad_len
+        exp = contract.sample(True, ll, rows, n, t, k, p, True, lu, True)
+        if exp != contract.OK:
+            got = L.llmk_sample(FAKE, ll, rows, n, t, k, p, FAKE, lu, FAKE, FAKE, 1 << 40, None)
+            assert got == exp, (rows, n, bad_len, t, k, p, lu)
+    for null in range(3):
+        ptrs = [FAKE, FAKE, FAKE]
+        ptrs[null] = None
+        assert L.llmk_sample(ptrs[0], 7, 1, 7, 1.0, 0, 1.0, ptrs[1], 1, ptrs[2], FAKE, 1 << 40, None) == 578
+    rows = contract.SAMPLE_MAX_ROWS + 1
+    assert L.llmk_sample(FAKE, rows * 9, rows, 9, 1.0, 3, 1.0, FAKE, rows, FAKE, FAKE, 1 << 40, None) == \
+        contract.sample(True, rows * 9, rows, 9, 1.0, 3, 1.0, True, rows, True) == contract.TOO_LARGE
+    # a call that needs a workspace refuses none, a short one and a misaligned one
+    v = 128256
+    need = llmk.sample_workspace_bytes(2, v, 1.0, 50)
+    assert need > 0
+    exp = contract.sample(True, 2 * v, 2, v, 1.0, 50, 0.9, True, 2, True, ws_short=True)
+    for ws, n_ws in [(None, 0), (FAKE, need - 1), (FAKE + 8, need)]:
+        assert L.llmk_sample(FAKE, 2 * v, 2, v, 1.0, 50, 0.9, FAKE, 2, FAKE, ws, n_ws, None) == exp == 578
+
+
+def test_sample_workspace_sizes():
+    # G * k candidates of 8 bytes per row: wave slices of 2,048 logits while G * k <= 8,192, else block
+    # slices of 16,384 logits under the same bound, else the one-workgroup form with no workspace
+    ws = llmk.sample_workspace_bytes
+    assert ws(1, 128256, 1.0, 50) == 63 * 50 * 8           # 63 wave slices
+    assert ws(1, 128256, 1.0, 130) == 63 * 130 * 8
+    assert ws(2, 128256, 1.0, 131) == 2 * 8 * 131 * 8      # 63 * 131 > 8192: 8 block slices
+    assert ws(3, 128256, 0.7, 1024) == 3 * 8 * 1024 * 8
+    assert ws(1, 128256, 0.0, 0) == 63 * 1 * 8             # greedy keeps one survivor
+    assert ws(1, 5000, 1.0, 1000) == 3 * 1000 * 8
+    assert ws(1, 151936, 1.0, 1024) == 0                   # 10 block slices * 1024 > 8192: one workgroup
+    assert ws(1, 2048, 1.0, 3) == 0                        # one slice: one workgroup
+    assert ws(0, 7, 1.0, 3) == -561 and ws(1, 5000, 1.0, 0) == -564
+
+
 def test_kv_slot_offset_closed_form():
     import numpy as np
 
