@@ -87,6 +87,9 @@ _SIGS = {
     "llmk_argmax_workspace_bytes": ([_i64, _i64], _i64),
     "llmk_argmax": ([_p, _i64, _i64, _i64, _p, _p, _p, _i64, _p], _i32),
     "llmk_sample_workspace_bytes": ([_i64, _i64, _f32, _i32], _i64),
+    "llmk_prefill_workspace_bytes": ([ctypes.POINTER(Config), _i64], _i64),
+    "llmk_prefill": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _p, _i64,
+                      _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_sample": ([_p, _i64, _i64, _i64, _f32, _i32, _f32, _p, _i64, _p, _p, _i64, _p], _i32),
     "llmk_kv_slot_offset": ([ctypes.POINTER(PoolStruct), _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
     "llmk_decode_workspace_bytes": ([ctypes.POINTER(Config), _i64], _i64),
@@ -372,6 +375,20 @@ def decode_steps_batch(cfg: Config, model: Model, pool: KVPool, slots, tokens0, 
     return lib.llmk_decode_steps_batch(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct),
                                        len(sl), psl, ptk, pps, n_steps, _ptr(tokens_out), _len(tokens_out), _ptr(ws),
                                        _len(ws), _stream(stream))
+
+
+def prefill_workspace_bytes(cfg: Config, n: int) -> int:
+    return lib.llmk_prefill_workspace_bytes(ctypes.byref(cfg), n)
+
+
+def prefill(cfg: Config, model: Model, pool: KVPool, slot, tokens, pos0, tokens_out, ws, logits=None, hidden=None,
+            stream=None) -> int:
+    """Prefill of the host token sequence `tokens` into `slot` at positions pos0 ..; tokens_out: device int32
+    [len(tokens)], the greedy token after each position."""
+    tk, ptk = _host_i64(tokens)
+    return lib.llmk_prefill(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot, ptk,
+                            len(tk), pos0, _ptr(tokens_out), _len(tokens_out), _ptr(logits), _len(logits),
+                            _ptr(hidden), _len(hidden), _ptr(ws), _len(ws), _stream(stream))
 
 
 def decode_kernel_count(cfg: Config) -> int:

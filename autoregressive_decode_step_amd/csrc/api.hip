@@ -641,6 +641,7 @@ struct BatchPlan {
   int32_t* tok_scratch = nullptr;       // kTimeMaxReps * B tokens: repeated timing launches of the head
   int64_t n_gemm_counters = 0;
   int64_t bytes = 0;
+  bool prefill = false;                 // rows of one chunk: K/V appended for all rows before any attends
 };
 
 // The batched path runs bf16 weights in the output-major layout (matrix-core operands).
@@ -742,6 +743,12 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       a.out = nullptr;
       a.out_hi = P.att_hi;
       a.out_lo = P.att_lo;
+      a.no_append = P.prefill ? 1 : 0;
+      if (P.prefill) {
+        hipError_t e = rope_append_rows_launch(P.qkv_buf, P.qkv.N, P.state, B, a.H, a.Hkv, a.hd, a.rope_table,
+                                               a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, s);
+        if (e != hipSuccess) return e;
+      }
       return attn_launch(a, s);
     }
     case BK_O: {     // x += Wo att
@@ -810,6 +817,35 @@ hipError_t enqueue_batch(const llmk_config* c, const llmk_model* m, const llmk_k
   if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, P, 0, BK_NORMF, logits, tokens_out, hidden, s);
   if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, P, 0, BK_HEAD, logits, tokens_out, hidden, s);
   return e;
+}
+
+// Prefill workspace: the batched plan of a full chunk (or of the smaller last chunk, whichever is larger),
+// then the last chunk's logits [rows][vocab] and hidden states [rows][n_layer][d], copied out for its last row.
+struct PrefillLayout {
+  int64_t rows = 0;        // rows per chunk
+  int64_t logits_off = 0;
+  int64_t hidden_off = 0;
+  int64_t bytes = 0;
+};
+
+PrefillLayout prefill_layout(const llmk_config* c, int64_t n) {
+  PrefillLayout L;
+  L.rows = std::min<int64_t>(n, LLMK_MAX_BATCH);
+  BatchPlan P;
+  plan_batch(c, L.rows, nullptr, P);
+  int64_t plan = P.bytes;
+  if (n % L.rows != 0) {
+    plan_batch(c, n % L.rows, nullptr, P);
+    plan = std::max(plan, P.bytes);
+  }
+  Carve cv(nullptr);
+  cv.off = align_up(plan);
+  L.logits_off = cv.off;
+  cv.take<float>(L.rows * c->vocab);
+  L.hidden_off = cv.off;
+  cv.take<float>(L.rows * c->n_layer * c->d);
+  L.bytes = cv.off;
+  return L;
 }
 
 // Checks of the batched entry points, in the documented order; fills init on success.
@@ -1266,6 +1302,78 @@ int32_t llmk_decode_step_batch(const llmk_config* cfg, const llmk_model* model, 
   if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, logits, tokens_out, hidden, s);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos_h[r] + 1;
+  return LLMK_OK;
+}
+
+int64_t llmk_prefill_workspace_bytes(const llmk_config* cfg, int64_t n) {
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return -st;
+  if (n < 1) return -LLMK_EMPTY_DIMENSION;
+  if (n > kMaxDim) return -LLMK_DIMENSION_TOO_LARGE;
+  if (!batch_config_ok(cfg)) return -LLMK_INVALID_ARGUMENT;
+  return prefill_layout(cfg, n).bytes;
+}
+
+int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                     const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out, int64_t len_tokens,
+                     float* logits, int64_t len_logits, float* hidden, int64_t len_hidden, void* ws, int64_t len_ws,
+                     void* stream) {
+  if (!cfg || !model || !pool || !tokens_h || !tokens_out || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return st;
+  if (n < 1) return LLMK_EMPTY_DIMENSION;
+  if (n > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  if ((st = model_check(cfg, model)) != LLMK_OK) return st;
+  if ((st = model_lengths(cfg, model)) != LLMK_OK) return st;
+  if ((st = pool_check(cfg, pool)) != LLMK_OK) return st;
+  if (!weights_aligned(cfg, model) || !batch_config_ok(cfg)) return LLMK_INVALID_ARGUMENT;
+  if (slot < 0 || slot >= pool->n_slots) return LLMK_SLOT_OUT_OF_RANGE;
+  for (int64_t i = 0; i < n; ++i)
+    if (tokens_h[i] < 0 || tokens_h[i] >= cfg->vocab) return LLMK_TOKEN_OUT_OF_RANGE;
+  if (pos0 < 0 || pos0 + n > cfg->max_seq) return LLMK_POSITION_OUT_OF_RANGE;
+  if (pos0 != pool->slot_len_h[slot]) return LLMK_CACHE_LENGTH_MISMATCH;
+  if (pos0 + n > pool->capacity) return LLMK_CACHE_CAPACITY_EXCEEDED;
+  if (len_tokens != n) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (logits && len_logits != cfg->vocab) return LLMK_LOGITS_LENGTH_MISMATCH;
+  if (hidden && len_hidden != cfg->n_layer * cfg->d) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  const PrefillLayout L = prefill_layout(cfg, n);
+  if (len_ws < L.bytes) return LLMK_INVALID_ARGUMENT;
+
+  hipStream_t s = as_stream(stream);
+  float* const ws_logits = reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits_off);
+  float* const ws_hidden = reinterpret_cast<float*>(static_cast<char*>(ws) + L.hidden_off);
+  hipError_t e = hipSuccess;
+  int64_t last_rows = 0;
+  for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += L.rows) {
+    // one chunk: rows c0 .. c0 + B - 1 of the prompt at positions pos0 + c0 + r, all in this slot
+    const int64_t B = std::min(L.rows, n - c0);
+    const bool last = c0 + B == n;
+    BatchPlan P;
+    plan_batch(cfg, B, ws, P);
+    P.prefill = true;
+    BatchInit init;
+    memset(&init, 0, sizeof(init));
+    for (int64_t r = 0; r < B; ++r) {
+      init.token[r] = (int32_t)tokens_h[c0 + r];
+      init.pos[r] = (int32_t)(pos0 + c0 + r);
+      init.slot[r] = (int32_t)slot;
+    }
+    init.rows = (int32_t)B;
+    e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
+    if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
+    float* const lg = last && logits ? ws_logits : nullptr;
+    float* const hd = last && hidden ? ws_hidden : nullptr;
+    if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, lg, tokens_out + c0, hd, s);
+    last_rows = B;
+  }
+  if (e == hipSuccess && logits)
+    e = hipMemcpyAsync(logits, ws_logits + (last_rows - 1) * cfg->vocab, cfg->vocab * sizeof(float),
+                       hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && hidden)
+    e = hipMemcpyAsync(hidden, ws_hidden + (last_rows - 1) * cfg->n_layer * cfg->d,
+                       cfg->n_layer * cfg->d * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return LLMK_DEVICE_ERROR;
+  pool->slot_len_h[slot] = pos0 + n;
   return LLMK_OK;
 }
 

@@ -176,7 +176,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   // workgroup rotates its q heads by the position, and the workgroup whose part holds that position
   // rotates k, rounds k and v to the cache dtype, appends them to the cache and patches its tile.
   const int pos = ctx - 1;
-  const bool owner = (TAG || qkv_raw) && pos >= tb && pos < te;
+  const bool owner = (TAG || qkv_raw) && !p.no_append && pos >= tb && pos < te;
   // the RoPE row of this position: a thread's first (cos, sin) pair is requested before q is waited for
   constexpr int HALF = HD / 2;
   const float* tab = p.rope_table + (int64_t)pos * HALF * 2;

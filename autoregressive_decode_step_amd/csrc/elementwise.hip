@@ -115,6 +115,43 @@ hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk,
   return hipGetLastError();
 }
 
+// ---- prefill: RoPE on k and the K/V append of every row of a chunk, before any row attends ----------------
+
+template <typename T>
+__global__ void rope_append_rows_kernel(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t H,
+                                        int32_t Hkv, int32_t hd, const float* table, int32_t layout, T* k, T* v,
+                                        int64_t slot_elems) {
+  const int r = blockIdx.x, kvh = blockIdx.y;
+  const int64_t pos = st->pos[r];
+  const float* src = qkv + (int64_t)r * qkv_stride;
+  const float* ks = src + (int64_t)H * hd + (int64_t)kvh * hd;
+  const float* vs = src + (int64_t)(H + Hkv) * hd + (int64_t)kvh * hd;
+  const int64_t off = (int64_t)st->slot[r] * slot_elems + pos * Hkv * hd + (int64_t)kvh * hd;
+  const int half = hd / 2;
+  for (int j = threadIdx.x; j < half; j += blockDim.x) {
+    const int ia = layout == 0 ? j : 2 * j;
+    const int ib = layout == 0 ? j + half : 2 * j + 1;
+    const float cs = table[(pos * half + j) * 2 + 0], sn = table[(pos * half + j) * 2 + 1];
+    const float a = ks[ia], b = ks[ib];
+    store_elem<T>(k + off, ia, a * cs - b * sn);
+    store_elem<T>(k + off, ib, a * sn + b * cs);
+  }
+  for (int e = threadIdx.x; e < hd; e += blockDim.x) store_elem<T>(v + off, e, vs[e]);
+}
+
+hipError_t rope_append_rows_launch(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t rows,
+                                   int32_t H, int32_t Hkv, int32_t hd, const float* rope_table, int32_t rope_layout,
+                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, hipStream_t s) {
+  const dim3 grid((unsigned)rows, (unsigned)Hkv);
+  if (kv_is_bf16)
+    hipLaunchKernelGGL(rope_append_rows_kernel<bf16_t>, grid, dim3(64), 0, s, qkv, qkv_stride, st, H, Hkv, hd,
+                       rope_table, rope_layout, static_cast<bf16_t*>(k), static_cast<bf16_t*>(v), slot_elems);
+  else
+    hipLaunchKernelGGL(rope_append_rows_kernel<float>, grid, dim3(64), 0, s, qkv, qkv_stride, st, H, Hkv, hd,
+                       rope_table, rope_layout, static_cast<float*>(k), static_cast<float*>(v), slot_elems);
+  return hipGetLastError();
+}
+
 // ---- in-place K/V append: cache[offset + i] = round(src[i]) --------------------------------------------
 
 __global__ void kv_append_kernel(void* cache, int is_bf16, int64_t offset, const float* src, int64_t n) {

@@ -183,6 +183,7 @@ struct AttnParams {
   void* v_w;
   const float* rope_table;     // [max_pos][hd/2][2]
   int32_t rope_layout;
+  int32_t no_append;           // prefill: k, v of every row are already in the cache; rotate q only
   // batched decode (bstate non-null): grid.z = rows; row r reads pos and slot from bstate, its K/V region
   // starts slot * slot_elems elements into k / v / k_w / v_w, its q|k|v at qkv_raw + r * qkv_stride, and
   // its output goes, split into bf16 hi/lo, to out_hi / out_lo + r * H * hd
@@ -288,6 +289,11 @@ hipError_t sample_launch(const float* logits, int64_t rows, int64_t n, float tem
 hipError_t argmax_launch(const float* logits, int64_t rows, int64_t n, int32_t* token, float* logit, float* part_val,
                          int32_t* part_idx, unsigned* counters, int32_t blocks_per_row, hipStream_t s);
 hipError_t fill_u32_launch(unsigned* p, int64_t n, unsigned v, hipStream_t s);
+// Prefill: for every row r of the batch state, rotate its k by pos[r], round k and v to the cache dtype and
+// store them at pos[r] of slot[r] (k, v: one layer's pool buffers; qkv: [rows][qkv_stride] raw q|k|v).
+hipError_t rope_append_rows_launch(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t rows,
+                                   int32_t H, int32_t Hkv, int32_t hd, const float* rope_table, int32_t rope_layout,
+                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, hipStream_t s);
 hipError_t set_state_launch(DecodeState* st, int32_t token, int32_t pos, hipStream_t s);
 
 }  // namespace llmk

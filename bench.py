@@ -139,6 +139,43 @@ def sample_probe(rows: int, reps: int = 50) -> int:
     return 0
 
 
+def prefill_probe(shape: str, n: int = 2048, reps: int = 3) -> int:
+    """Only prefill: an n-token seeded prompt into an empty slot of the named shape (q06: Qwen3-0.6B, the
+    2,048-token prefix workload; l8b: Llama-3-8B), timed over `reps` calls after one warm-up call."""
+    import torch
+
+    import synth
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd import loader
+    s = {"q06": synth.Q06, "l8b": synth.L8B}[shape]
+    log(f"generating {s.name} weights")
+    W = synth.model(s, seed=0)
+    cfg = loader.config_from(s)
+    model = loader.upload_model(cfg, W)
+    del W
+    pool = loader.new_pool(cfg, 1, n + 8)
+    tokens = synth.prompt(n, s.vocab, stream=23).tolist()
+    ws = llmk.workspace(llmk.prefill_workspace_bytes(cfg, n))
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+
+    def once():
+        pool.slot_len[0] = 0
+        st = llmk.prefill(cfg, model, pool, 0, tokens, 0, out, ws)
+        if st != llmk.OK:
+            raise RuntimeError(f"llmk_prefill: {st} {llmk.status_name(st)}")
+
+    once()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    print(json.dumps({"prefill_probe": {"shape": s.name, "prompt_tokens": n, "ms_per_prompt": round(ms, 2),
+                                        "tokens_per_s": round(n / ms * 1e3, 1)}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +192,8 @@ def main() -> int:
                          "the persistent one-kernel step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--prefill-probe", choices=("q06", "l8b"), default=None,
+                    help="only time a 2,048-token prefill of the named shape and exit")
     ap.add_argument("--sample-probe", type=int, default=0, metavar="ROWS",
                     help="only time the sampling exit over ROWS vocabulary rows and exit")
     args = ap.parse_args()
@@ -176,6 +215,8 @@ def main() -> int:
         return 3
     if args.copy_probe > 0:
         return copy_probe(args.copy_probe)
+    if args.prefill_probe:
+        return prefill_probe(args.prefill_probe)
     if args.sample_probe > 0:
         return sample_probe(args.sample_probe)
     if args.workload == "batched":

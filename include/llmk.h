@@ -366,6 +366,31 @@ int32_t llmk_decode_steps_batch(const llmk_config* cfg, const llmk_model* model,
                                 int64_t n_steps, int32_t* tokens_out, int64_t len_tokens, void* ws, int64_t len_ws,
                                 void* stream);
 
+/* Workspace bytes llmk_prefill needs for an n-token prompt (the batched plan of one chunk plus the last
+ * chunk's logits and hidden states), or -status: the config's check code, 561/564 for n, 578 where the
+ * batched path cannot run (weights not bf16 output-major). */
+int64_t llmk_prefill_workspace_bytes(const llmk_config* cfg, int64_t n);
+
+/* Prefill of n prompt tokens into one slot ([xpu] "1. CausalLM: the forward path": a prompt chunk is a batch
+ * of rows through the batched projections, and decode is the one-token chunk of the same step). Positions
+ * pos0 .. pos0 + n - 1 of `slot`, in chunks of up to 64 rows: per layer every row of the chunk goes through
+ * the matrix-core q|k|v projection together, then all rows' k (rotated) and v are written to the cache,
+ * then row i attends over positions 0 .. pos0 + i of the slot (causal), then o, gate|up and down as in
+ * llmk_decode_step_batch. The result equals n decode steps fed tokens_h[0..n) one by one.
+ *   tokens_h: host int64 [n]; tokens_out: device int32 [n], the greedy token after each position;
+ *   logits (optional, NULL to skip): device fp32 [vocab] of the last position; hidden (optional): device
+ *   fp32 [n_layer][d], the residual after every layer at the last position. ws: device scratch of len_ws >=
+ *   llmk_prefill_workspace_bytes(cfg, n) bytes, 256-byte aligned, contents dead after the call.
+ * Codes, in order: 578 (null cfg/model/pool/tokens_h/tokens_out/ws), the config's check code, 561/564 (n),
+ * model and pool checks as llmk_decode_step, 578 (weights not bf16 output-major, or misaligned), 575 (slot),
+ * 572 (a token), 573 (pos0 < 0 or pos0 + n > max_seq), 566 (pos0 != slot length), 571 (pos0 + n > capacity),
+ * 577 (len_tokens != n), 568 (len_logits != vocab), 577 (len_hidden != n_layer * d), 578 (workspace).
+ * On success slot_len_h[slot] = pos0 + n; the call returns once the work is queued on `stream`. */
+int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                     const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out, int64_t len_tokens,
+                     float* logits, int64_t len_logits, float* hidden, int64_t len_hidden, void* ws, int64_t len_ws,
+                     void* stream);
+
 /* dst = src^T for a rows x cols row-major matrix (dst is cols x rows), both device buffers of rows*cols
  * elements of dtype; the one-time repacking of projections into LLMK_W_OUT_IN. dst may not alias src.
  * Codes: 578 (null, dtype, aliasing), 561, 564, 562 (len_src), 577 (len_dst). */

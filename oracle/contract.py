@@ -408,3 +408,44 @@ def decode_step_batch(cfg: dict, batch=1, tensors_ok=True, lens_ok=True, pool_ok
     if hidden and len_hidden != batch * cfg["n_layer"] * cfg["d"]:
         return OUTPUT_LEN
     return INVALID if ws_short else OK
+
+
+def prefill(cfg: dict, n=1, tensors_ok=True, lens_ok=True, pool_ok=True, pool_dims_bad=False, batch_weights_ok=True,
+            n_slots=1, capacity=0, slot=0, slot_len=0, tokens=(0,), pos0=0, len_tokens=None, logits=False,
+            len_logits=0, hidden=False, len_hidden=0, ws_short=False):
+    """Expected status of llmk_prefill: the checks of llmk_decode_step_batch for one slot whose rows are the
+    n prompt tokens at positions pos0 .. pos0 + n - 1, with the last position's logits and hidden states."""
+    c = config_check(**cfg)
+    if c != OK:
+        return c
+    if n < 1:
+        return EMPTY
+    if n > MAX_DIM:
+        return TOO_LARGE
+    if not tensors_ok:
+        return INVALID
+    if not lens_ok:
+        return WEIGHT_LEN
+    if not pool_ok:
+        return INVALID
+    if pool_dims_bad:
+        return EMPTY
+    if not batch_weights_ok:
+        return INVALID
+    if not (0 <= slot < n_slots):
+        return SLOT
+    if any(not (0 <= t < cfg["vocab"]) for t in tokens):
+        return TOKEN
+    if pos0 < 0 or pos0 + n > cfg["max_seq"]:
+        return POSITION
+    if pos0 != slot_len:
+        return CACHE_LEN
+    if pos0 + n > capacity:
+        return CAPACITY
+    if (len_tokens if len_tokens is not None else n) != n:
+        return OUTPUT_LEN
+    if logits and len_logits != cfg["vocab"]:
+        return LOGITS_LEN
+    if hidden and len_hidden != cfg["n_layer"] * cfg["d"]:
+        return OUTPUT_LEN
+    return INVALID if ws_short else OK

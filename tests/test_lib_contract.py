@@ -395,3 +395,64 @@ def test_decode_step_batch_refusals():
                                          batch_weights_ok=False)
         assert run(bad) == exp == 578
         assert llmk.decode_workspace_bytes(llmk.make_config(**bad), 2) == -578
+
+
+@no_gpu
+def test_prefill_refusals():
+    import numpy as np
+    d, qd, kvd, F, V, L = 16, 16, 8, 24, 40, 2
+    lens = [d * qd, d * kvd, d * kvd, qd * d, d * F, d * F, F * d, d, d]
+    FA = 0x10000
+
+    def model_for(bad_len=False):
+        arr = (llmk.Tensor * (L * 9))()
+        for l in range(L):
+            for t in range(9):
+                arr[l * 9 + t] = llmk.Tensor(FA, lens[t] + (1 if (bad_len and l == 1 and t == 2) else 0))
+        return llmk.ModelStruct(llmk.Tensor(FA, V * d), llmk.Tensor(FA, V * d), llmk.Tensor(FA, d),
+                                llmk.Tensor(FA, 64 * 4), arr), arr
+
+    def run(kw, n=3, slot=1, tokens=None, pos0=0, slot_lens=(0, 0, 0), cap=32, n_slots=3, len_tokens=None,
+            logits=False, len_logits=V, hidden=False, len_hidden=L * d, ws_short=False, bad_len=False):
+        cfg = llmk.make_config(**kw)
+        m, _keep = model_for(bad_len)
+        ks = (ctypes.c_void_p * L)(FA, FA)
+        sl = np.array(slot_lens, np.int64)
+        ps = llmk.PoolStruct(ks, ks, L, n_slots, cap, 2, 4, kw["kv_dtype"],
+                             sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        tk = np.array(tokens if tokens is not None else [0] * max(n, 0), np.int64)
+        need = llmk.prefill_workspace_bytes(cfg, max(n, 1))
+        ws = max(need, 1) - (1 if ws_short else 0)
+        return llmk.lib.llmk_prefill(ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), slot, tk.ctypes.data, n,
+                                     pos0, FA, n if len_tokens is None else len_tokens, FA if logits else None,
+                                     len_logits, FA if hidden else None, len_hidden, FA, ws, None)
+
+    good = _cfg_kwargs(w_dtype=1, w_layout=1)
+    cases = [
+        (dict(n=0), dict(n=0)),
+        (dict(slot=3), dict(slot=3)),
+        (dict(tokens=[0, 40, 0]), dict(tokens=[0, 40, 0])),
+        (dict(pos0=-1), dict(pos0=-1)),
+        (dict(n=3, pos0=62, slot_lens=(0, 62, 0), cap=128), dict(pos0=62, slot_len=62, capacity=128)),
+        (dict(pos0=5, slot_lens=(0, 4, 0)), dict(pos0=5, slot_len=4)),
+        (dict(pos0=30, slot_lens=(0, 30, 0), cap=32), dict(pos0=30, slot_len=30, capacity=32)),
+        (dict(len_tokens=2), dict(len_tokens=2)),
+        (dict(logits=True, len_logits=3 * V), dict(logits=True, len_logits=3 * V)),
+        (dict(hidden=True, len_hidden=3 * L * d), dict(hidden=True, len_hidden=3 * L * d)),
+        (dict(ws_short=True), dict(ws_short=True)),
+        (dict(bad_len=True), dict(lens_ok=False)),
+    ]
+    for call_kw, exp_kw in cases:
+        base = dict(n=call_kw.get("n", 3), n_slots=3, capacity=32, slot=1, tokens=call_kw.get("tokens", [0] * 3))
+        base.update(exp_kw)
+        exp = contract.prefill(good, **base)
+        assert exp != contract.OK, call_kw
+        assert run(good, **call_kw) == exp, (call_kw, exp)
+    for bad in (_cfg_kwargs(w_dtype=1, w_layout=0), _cfg_kwargs(w_dtype=0, w_layout=1)):
+        exp = contract.prefill(bad, n=3, n_slots=3, capacity=32, slot=1, tokens=[0] * 3, batch_weights_ok=False)
+        assert run(bad) == exp == 578
+        assert llmk.prefill_workspace_bytes(llmk.make_config(**bad), 3) == -578
+    cfg = llmk.make_config(**good)
+    assert llmk.prefill_workspace_bytes(cfg, 0) == -561
+    # 200 tokens run in chunks of 64 rows: the workspace holds one 64-row plan, 64 rows of logits and hidden
+    assert llmk.prefill_workspace_bytes(cfg, 200) >= llmk.decode_workspace_bytes(cfg, 64) + 64 * (V + L * d) * 4
