@@ -819,33 +819,138 @@ hipError_t enqueue_batch(const llmk_config* c, const llmk_model* m, const llmk_k
   return e;
 }
 
-// Prefill workspace: the batched plan of a full chunk (or of the smaller last chunk, whichever is larger),
-// then the last chunk's logits [rows][vocab] and hidden states [rows][n_layer][d], copied out for its last row.
-struct PrefillLayout {
-  int64_t rows = 0;        // rows per chunk
-  int64_t logits_off = 0;
-  int64_t hidden_off = 0;
+// ---- prefill ------------------------------------------------------------------------------------------
+
+constexpr int64_t kPrefillRows = 256;   // rows per chunk: each weight tile serves up to 256 rows
+
+// A chunk of M prompt rows: the batched plan's row buffers, attention and norms, plus the chunk's projections
+// (tiled matrix-core GEMMs), their split partials (also the head's logits [M][vocab]) and the argmax partials.
+struct PrefillPlan {
+  BatchPlan rows;
+  PgemmParams qkv{}, o{}, gu{}, down{}, head{};
+  float* y = nullptr;
+  float* am_val = nullptr;
+  int32_t* am_idx = nullptr;
+  unsigned* am_cnt = nullptr;
+  float* am_logit = nullptr;
+  int32_t am_bpr = 0;
+  float* hidden = nullptr;              // [M][n_layer][d]: the last chunk's hidden states, when asked for
   int64_t bytes = 0;
 };
 
-PrefillLayout prefill_layout(const llmk_config* c, int64_t n) {
-  PrefillLayout L;
-  L.rows = std::min<int64_t>(n, LLMK_MAX_BATCH);
-  BatchPlan P;
-  plan_batch(c, L.rows, nullptr, P);
-  int64_t plan = P.bytes;
-  if (n % L.rows != 0) {
-    plan_batch(c, n % L.rows, nullptr, P);
-    plan = std::max(plan, P.bytes);
+void plan_prefill(const llmk_config* c, int64_t M, void* ws, PrefillPlan& P) {
+  const int64_t d = c->d, qd = c->n_head * c->head_dim, kvd = c->n_kv * c->head_dim, F = c->hidden;
+  plan_batch(c, M, ws, P.rows);
+  P.rows.prefill = true;
+  PgemmParams* gs[5] = {&P.qkv, &P.o, &P.gu, &P.down, &P.head};
+  const int64_t Ns[5] = {qd + 2 * kvd, d, 2 * F, d, c->vocab};
+  const int64_t Ks[5] = {d, qd, d, F, d};
+  int64_t yfl = 0;
+  for (int i = 0; i < 5; ++i) {
+    gs[i]->M = (int32_t)M;
+    gs[i]->N = Ns[i];
+    gs[i]->K = Ks[i];
+    gs[i]->lda = Ks[i];
+    gs[i]->n0 = Ns[i];
+    pgemm_plan(*gs[i], i == 4 ? 1 : kBatchTargetBlocks);   // the head: one split, its partial is the logits
+    yfl = std::max(yfl, (int64_t)gs[i]->ksplit * M * Ns[i]);
   }
-  Carve cv(nullptr);
-  cv.off = align_up(plan);
-  L.logits_off = cv.off;
-  cv.take<float>(L.rows * c->vocab);
-  L.hidden_off = cv.off;
-  cv.take<float>(L.rows * c->n_layer * c->d);
-  L.bytes = cv.off;
-  return L;
+  P.qkv.n0 = qd;
+  P.qkv.n1 = kvd;
+  P.gu.n0 = F;
+  P.gu.n1 = F;
+  Carve cv(ws);
+  cv.off = P.rows.bytes;
+  P.y = cv.take<float>(yfl);
+  P.am_bpr = c->vocab >= 65536 ? 64 : (int32_t)((c->vocab + 1023) / 1024);
+  P.am_val = cv.take<float>(M * P.am_bpr);
+  P.am_idx = cv.take<int32_t>(M * P.am_bpr);
+  P.am_cnt = cv.take<unsigned>(M);
+  P.am_logit = cv.take<float>(M);
+  P.hidden = cv.take<float>(M * c->n_layer * d);
+  P.bytes = cv.off;
+}
+
+int64_t prefill_bytes(const llmk_config* c, int64_t n) {
+  const int64_t rows = std::min(n, kPrefillRows);
+  PrefillPlan P;
+  plan_prefill(c, rows, nullptr, P);
+  int64_t bytes = P.bytes;
+  if (n % rows != 0) {
+    plan_prefill(c, n % rows, nullptr, P);
+    bytes = std::max(bytes, P.bytes);
+  }
+  return bytes;
+}
+
+// One chunk: rows r = 0..M-1 of P at positions state.pos[r] of one slot, through every layer and the head.
+hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, PrefillPlan& P,
+                                 int32_t* tokens_out, bool want_hidden, hipStream_t s) {
+  const int64_t d = c->d;
+  BatchPlan& B = P.rows;
+  hipError_t e = hipSuccess;
+  for (int64_t l = 0; l < c->n_layer && e == hipSuccess; ++l) {
+    e = launch_batch_kernel(c, m, pool, B, l, BK_NORM1, nullptr, nullptr, nullptr, s);
+    if (e == hipSuccess) {
+      PgemmParams g = P.qkv;
+      g.ahi = B.h_hi;
+      g.alo = B.h_lo;
+      g.w0 = layer_t(m, l, LLMK_WQ).ptr;
+      g.w1 = layer_t(m, l, LLMK_WK).ptr;
+      g.w2 = layer_t(m, l, LLMK_WV).ptr;
+      g.y = P.y;
+      g.out = B.qkv_buf;
+      g.ldo = g.N;
+      e = pgemm_launch(g, PG_STORE, s);
+    }
+    if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, B, l, BK_ATTN, nullptr, nullptr, nullptr, s);
+    if (e == hipSuccess) {
+      PgemmParams g = P.o;
+      g.ahi = B.att_hi;
+      g.alo = B.att_lo;
+      g.w0 = layer_t(m, l, LLMK_WO).ptr;
+      g.y = P.y;
+      g.out = B.x;
+      g.ldo = d;
+      e = pgemm_launch(g, PG_RESID, s);
+    }
+    if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, B, l, BK_NORM2, nullptr, nullptr, nullptr, s);
+    if (e == hipSuccess) {
+      PgemmParams g = P.gu;
+      g.ahi = B.h_hi;
+      g.alo = B.h_lo;
+      g.w0 = layer_t(m, l, LLMK_WGATE).ptr;
+      g.w1 = layer_t(m, l, LLMK_WUP).ptr;
+      g.y = P.y;
+      g.uhi = B.u_hi;
+      g.ulo = B.u_lo;
+      e = pgemm_launch(g, PG_GATEUP, s);
+    }
+    if (e == hipSuccess) {
+      PgemmParams g = P.down;
+      g.ahi = B.u_hi;
+      g.alo = B.u_lo;
+      g.w0 = layer_t(m, l, LLMK_WDOWN).ptr;
+      g.y = P.y;
+      g.out = B.x;
+      g.ldo = d;
+      g.hidden = want_hidden ? P.hidden + l * d : nullptr;
+      g.hidden_stride = c->n_layer * d;
+      e = pgemm_launch(g, PG_RESID, s);
+    }
+  }
+  if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, B, 0, BK_NORMF, nullptr, nullptr, nullptr, s);
+  if (e == hipSuccess) {
+    PgemmParams g = P.head;
+    g.ahi = B.h_hi;
+    g.alo = B.h_lo;
+    g.w0 = m->w_out.ptr;
+    g.y = P.y;
+    e = pgemm_launch(g, PG_NONE, s);
+  }
+  if (e == hipSuccess)
+    e = argmax_launch(P.y, P.head.M, c->vocab, tokens_out, P.am_logit, P.am_val, P.am_idx, P.am_cnt, P.am_bpr, s);
+  return e;
 }
 
 // Checks of the batched entry points, in the documented order; fills init on success.
@@ -1311,7 +1416,7 @@ int64_t llmk_prefill_workspace_bytes(const llmk_config* cfg, int64_t n) {
   if (n < 1) return -LLMK_EMPTY_DIMENSION;
   if (n > kMaxDim) return -LLMK_DIMENSION_TOO_LARGE;
   if (!batch_config_ok(cfg)) return -LLMK_INVALID_ARGUMENT;
-  return prefill_layout(cfg, n).bytes;
+  return prefill_bytes(cfg, n);
 }
 
 int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
@@ -1336,42 +1441,35 @@ int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_po
   if (len_tokens != n) return LLMK_OUTPUT_LENGTH_MISMATCH;
   if (logits && len_logits != cfg->vocab) return LLMK_LOGITS_LENGTH_MISMATCH;
   if (hidden && len_hidden != cfg->n_layer * cfg->d) return LLMK_OUTPUT_LENGTH_MISMATCH;
-  const PrefillLayout L = prefill_layout(cfg, n);
-  if (len_ws < L.bytes) return LLMK_INVALID_ARGUMENT;
+  if (len_ws < prefill_bytes(cfg, n)) return LLMK_INVALID_ARGUMENT;
 
   hipStream_t s = as_stream(stream);
-  float* const ws_logits = reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits_off);
-  float* const ws_hidden = reinterpret_cast<float*>(static_cast<char*>(ws) + L.hidden_off);
   hipError_t e = hipSuccess;
-  int64_t last_rows = 0;
-  for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += L.rows) {
-    // one chunk: rows c0 .. c0 + B - 1 of the prompt at positions pos0 + c0 + r, all in this slot
-    const int64_t B = std::min(L.rows, n - c0);
-    const bool last = c0 + B == n;
-    BatchPlan P;
-    plan_batch(cfg, B, ws, P);
-    P.prefill = true;
+  const int64_t rows = std::min(n, kPrefillRows);
+  for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += rows) {
+    // one chunk: prompt rows c0 .. c0 + M - 1 at positions pos0 + c0 + r, all in this slot
+    const int64_t M = std::min(rows, n - c0);
+    const bool last = c0 + M == n;
+    PrefillPlan P;
+    plan_prefill(cfg, M, ws, P);
     BatchInit init;
     memset(&init, 0, sizeof(init));
-    for (int64_t r = 0; r < B; ++r) {
+    for (int64_t r = 0; r < M; ++r) {
       init.token[r] = (int32_t)tokens_h[c0 + r];
       init.pos[r] = (int32_t)(pos0 + c0 + r);
       init.slot[r] = (int32_t)slot;
     }
-    init.rows = (int32_t)B;
-    e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
-    if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
-    float* const lg = last && logits ? ws_logits : nullptr;
-    float* const hd = last && hidden ? ws_hidden : nullptr;
-    if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, lg, tokens_out + c0, hd, s);
-    last_rows = B;
+    init.rows = (int32_t)M;
+    e = fill_u32_launch(P.rows.counters, batch_counters_total(cfg, P.rows), 0u, s);
+    if (e == hipSuccess) e = fill_u32_launch(P.am_cnt, M, 0u, s);
+    if (e == hipSuccess) e = set_batch_state_launch(P.rows.state, init, s);
+    if (e == hipSuccess) e = enqueue_prefill_chunk(cfg, model, pool, P, tokens_out + c0, last && hidden, s);
+    if (e == hipSuccess && last && logits)
+      e = hipMemcpyAsync(logits, P.y + (M - 1) * cfg->vocab, cfg->vocab * sizeof(float), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && last && hidden)
+      e = hipMemcpyAsync(hidden, P.hidden + (M - 1) * cfg->n_layer * cfg->d, cfg->n_layer * cfg->d * sizeof(float),
+                         hipMemcpyDeviceToDevice, s);
   }
-  if (e == hipSuccess && logits)
-    e = hipMemcpyAsync(logits, ws_logits + (last_rows - 1) * cfg->vocab, cfg->vocab * sizeof(float),
-                       hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess && hidden)
-    e = hipMemcpyAsync(hidden, ws_hidden + (last_rows - 1) * cfg->n_layer * cfg->d,
-                       cfg->n_layer * cfg->d * sizeof(float), hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos0 + n;
   return LLMK_OK;

@@ -161,8 +161,9 @@ struct DecodeState {
   int32_t pad;
 };
 
-// Batched decode: one entry per sequence row of the batch (rows <= LLMK_MAX_BATCH_ROWS).
-constexpr int LLMK_MAX_BATCH_ROWS = 64;
+// Batched decode and prefill chunks: one entry per row (rows <= LLMK_MAX_BATCH_ROWS; a decode batch holds at
+// most 64 sequences, a prefill chunk up to 256 rows of one sequence).
+constexpr int LLMK_MAX_BATCH_ROWS = 256;
 struct BatchState {
   int32_t token[LLMK_MAX_BATCH_ROWS];   // token each row consumes in the next step
   int32_t pos[LLMK_MAX_BATCH_ROWS];     // its position

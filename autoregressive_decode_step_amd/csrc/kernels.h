@@ -113,6 +113,32 @@ hipError_t transpose_launch(const void* src, void* dst, int64_t rows, int64_t co
 // X given as bf16 hi and lo parts ([64][K] each, row stride K).
 // ------------------------------------------------------------------------------------------------
 
+// Prefill projections: Y = X W^T over a chunk of M rows, 128 x 128 tiles, K split where the tiles alone do
+// not fill the chip; the epilogue adds the splits in order and applies the operation.
+enum PgemmMode { PG_NONE = 0, PG_STORE = 1, PG_RESID = 2, PG_GATEUP = 3 };
+struct PgemmParams {
+  const bf16_t* ahi;      // X as bf16 hi + lo, [M][lda]
+  const bf16_t* alo;
+  int64_t lda;
+  const void* w0;         // W rows (bf16, K each): [0, n0) of w0, then n1 rows of w1, then the rest of w2
+  const void* w1;
+  const void* w2;
+  int64_t n0, n1;
+  int32_t M;
+  int32_t ksplit;
+  int64_t N, K;
+  int64_t kslice;         // k per split (a multiple of 32)
+  float* y;               // [ksplit][M][N] partial tiles (PG_NONE with one split: the result itself)
+  float* out;             // PG_STORE: out[m * ldo + n] = y; PG_RESID: out[m * ldo + n] += y
+  int64_t ldo;
+  float* hidden;          // PG_RESID, optional: hidden[m * hidden_stride + n] = the updated out
+  int64_t hidden_stride;
+  bf16_t* uhi;            // PG_GATEUP: silu(gate) * up as hi + lo, [M][N / 2] (gate rows first, then up)
+  bf16_t* ulo;
+};
+void pgemm_plan(PgemmParams& p, int target_blocks);
+hipError_t pgemm_launch(const PgemmParams& p, int mode, hipStream_t s);
+
 enum BgemmMode { BG_PLAIN = 0, BG_QKV = 1, BG_RESID = 2, BG_GATEUP = 3, BG_HEAD = 4 };
 
 struct BgemmParams {

@@ -1,0 +1,189 @@
+// Prefill projections on gfx950 matrix cores: Y[m][n] = sum_k X[m][k] W[n][k] for a chunk of prompt rows.
+//
+// A prompt chunk is a batch of rows ("Inside the engine", "1. CausalLM: the forward path": the projections take
+// the batched routes), large enough that every weight tile can be reused by many rows. So unlike the decode
+// batch (skinny, one pass over the weights), the chunk is tiled in both directions: a workgroup (4 waves)
+// owns a 128 x 128 tile of Y, stages 32-wide k slices of its 128 X rows and 128 W rows in LDS (two buffers:
+// the next slice is loaded into registers while the current one is multiplied), and each wave multiplies a
+// 64 x 64 sub-tile with v_mfma_f32_16x16x32_bf16 (4 x 4 tiles of 16 x 16). X is fp32 carried as bf16 hi + lo
+// (each product taken twice into fp32), W is bf16 and exact. Where the tiles alone do not fill the chip, K is
+// split: each split writes its partial tile, and the epilogue kernel adds the splits in order and applies the
+// operation (store, residual add, SiLU-gate into hi/lo).
+//
+// MFMA operands (per wave, 16 x 32 by 32 x 16): lane l holds row l % 16 of the X tile and row l % 16 of the
+// W tile, eight consecutive k of group l / 16 (one 16-byte LDS read each); the 16 x 16 result gives lane l
+// X rows 4 (l / 16) .. + 3 at W row l % 16.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace llmk {
+
+typedef __bf16 pg_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float pg_f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int PG_THREADS = 256;
+constexpr int PG_BM = 128;
+constexpr int PG_BN = 128;
+constexpr int PG_BK = 32;
+constexpr int PG_LDK = 40;   // LDS row stride in bf16 (80 bytes): the 16 rows one operand read touches use
+                             // different banks
+
+__device__ __forceinline__ pg_f32x4_t pg_mfma(const uint4& a, const uint4& b, const pg_f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pg_bf16x8_t, a),
+                                                 __builtin_bit_cast(pg_bf16x8_t, b), c, 0, 0, 0);
+}
+
+// W row n (clamped into [0, N)): rows [0, n0) of w0, then n1 rows of w1, then w2
+__device__ __forceinline__ const bf16_t* pg_wrow(const PgemmParams& p, int64_t n) {
+  const int64_t r = min(n, p.N - 1);
+  if (r < p.n0) return static_cast<const bf16_t*>(p.w0) + r * p.K;
+  if (r < p.n0 + p.n1) return static_cast<const bf16_t*>(p.w1) + (r - p.n0) * p.K;
+  return static_cast<const bf16_t*>(p.w2) + (r - p.n0 - p.n1) * p.K;
+}
+
+__global__ __launch_bounds__(PG_THREADS) void pgemm_kernel(const PgemmParams p) {
+  __shared__ __align__(16) bf16_t s_a[2][2][PG_BM][PG_LDK];   // [buffer][hi, lo][row][k]
+  __shared__ __align__(16) bf16_t s_w[2][PG_BN][PG_LDK];      // [buffer][row][k]
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;                    // this wave's 64 x 64 sub-tile
+  const int64_t m0 = (int64_t)blockIdx.y * PG_BM, n0 = (int64_t)blockIdx.x * PG_BN;
+  const int64_t kb = (int64_t)blockIdx.z * p.kslice;
+  const int64_t ke = min(p.K, kb + p.kslice);
+  const int nk = (int)((ke - kb + PG_BK - 1) / PG_BK);
+
+  // staging: thread t moves 8-element groups g = t and t + 256 of each 128 x 32 tile (row g / 4, group g % 4)
+  const bf16_t* ah[2];
+  const bf16_t* al[2];
+  const bf16_t* wr[2];
+  int srow[2], sk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int g = t + i * PG_THREADS;
+    srow[i] = g >> 2;
+    sk[i] = (g & 3) * 8;
+    const int64_t m = min(m0 + srow[i], (int64_t)p.M - 1);   // rows past M read a valid row; never stored
+    ah[i] = p.ahi + m * p.lda + sk[i];
+    al[i] = p.alo + m * p.lda + sk[i];
+    wr[i] = pg_wrow(p, n0 + srow[i]) + sk[i];
+  }
+  uint4 rah[2], ral[2], rw[2];
+  auto load = [&](int64_t k) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = k + sk[i] < ke;   // K is a multiple of 8: a group is all in or all out
+      rah[i] = ok ? *reinterpret_cast<const uint4*>(ah[i] + k) : make_uint4(0, 0, 0, 0);
+      ral[i] = ok ? *reinterpret_cast<const uint4*>(al[i] + k) : make_uint4(0, 0, 0, 0);
+      rw[i] = ok ? *reinterpret_cast<const uint4*>(wr[i] + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<uint4*>(&s_a[buf][0][srow[i]][sk[i]]) = rah[i];
+      *reinterpret_cast<uint4*>(&s_a[buf][1][srow[i]][sk[i]]) = ral[i];
+      *reinterpret_cast<uint4*>(&s_w[buf][srow[i]][sk[i]]) = rw[i];
+    }
+  };
+
+  pg_f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = pg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int orow = lane & 15, ok8 = (lane >> 4) * 8;
+  if (nk > 0) {
+    load(kb);
+    stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nk) load(kb + (int64_t)(it + 1) * PG_BK);   // the next slice in flight during the products
+    uint4 wop[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wop[j] = *reinterpret_cast<const uint4*>(&s_w[buf][wn * 64 + j * 16 + orow][ok8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 xh = *reinterpret_cast<const uint4*>(&s_a[buf][0][wm * 64 + i * 16 + orow][ok8]);
+      const uint4 xl = *reinterpret_cast<const uint4*>(&s_a[buf][1][wm * 64 + i * 16 + orow][ok8]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = pg_mfma(xh, wop[j], acc[i][j]);
+        acc[i][j] = pg_mfma(xl, wop[j], acc[i][j]);
+      }
+    }
+    // the other buffer was last read before the previous barrier
+    if (it + 1 < nk) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // this split's partial tile: lane l holds rows 4 (l / 16) .. + 3 of each 16-row tile at column l % 16
+  float* y = p.y + (int64_t)blockIdx.z * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 16 + orow;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        if (m < p.M && n < p.N) y[m * p.N + n] = acc[i][j][e];
+      }
+    }
+}
+
+// the splits' sum of element (m, n), in split order
+__device__ __forceinline__ float pg_sum(const PgemmParams& p, int64_t m, int64_t n) {
+  float v = 0.0f;
+  for (int z = 0; z < p.ksplit; ++z) v += p.y[((int64_t)z * p.M + m) * p.N + n];
+  return v;
+}
+
+__global__ void pgemm_epilogue_kernel(const PgemmParams p, int mode) {
+  const int64_t cols = mode == PG_GATEUP ? p.N / 2 : p.N;
+  const int64_t total = (int64_t)p.M * cols;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / cols, n = i % cols;
+    if (mode == PG_STORE) {
+      p.out[m * p.ldo + n] = pg_sum(p, m, n);
+    } else if (mode == PG_RESID) {
+      const float xo = p.out[m * p.ldo + n] + pg_sum(p, m, n);
+      p.out[m * p.ldo + n] = xo;
+      if (p.hidden) p.hidden[m * p.hidden_stride + n] = xo;
+    } else {   // PG_GATEUP: gate rows first, then the same number of up rows
+      const float u = silu_f(pg_sum(p, m, n)) * pg_sum(p, m, n + cols);
+      bf16_t hi, lo;
+      split_bf16(u, hi, lo);
+      p.uhi[m * cols + n] = hi;
+      p.ulo[m * cols + n] = lo;
+    }
+  }
+}
+
+void pgemm_plan(PgemmParams& p, int target_blocks) {
+  const int64_t tiles = ((p.N + PG_BN - 1) / PG_BN) * ((p.M + PG_BM - 1) / PG_BM);
+  int64_t ks = (target_blocks + tiles - 1) / tiles;
+  const int64_t steps = (p.K + PG_BK - 1) / PG_BK;
+  ks = std::max<int64_t>(1, std::min<int64_t>(ks, steps / 8));   // at least 8 k slices per split
+  int64_t slice = (steps + ks - 1) / ks * PG_BK;
+  p.kslice = slice;
+  p.ksplit = (int32_t)((p.K + slice - 1) / slice);
+}
+
+hipError_t pgemm_launch(const PgemmParams& p, int mode, hipStream_t s) {
+  if (p.M < 1 || p.K % 8 != 0 || p.kslice % PG_BK != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((p.N + PG_BN - 1) / PG_BN), (unsigned)((p.M + PG_BM - 1) / PG_BM), (unsigned)p.ksplit);
+  hipLaunchKernelGGL(pgemm_kernel, grid, dim3(PG_THREADS), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || mode == PG_NONE) return e;
+  const int64_t total = (int64_t)p.M * (mode == PG_GATEUP ? p.N / 2 : p.N);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(pgemm_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, mode);
+  return hipGetLastError();
+}
+
+}  // namespace llmk

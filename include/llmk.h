@@ -366,17 +366,17 @@ int32_t llmk_decode_steps_batch(const llmk_config* cfg, const llmk_model* model,
                                 int64_t n_steps, int32_t* tokens_out, int64_t len_tokens, void* ws, int64_t len_ws,
                                 void* stream);
 
-/* Workspace bytes llmk_prefill needs for an n-token prompt (the batched plan of one chunk plus the last
- * chunk's logits and hidden states), or -status: the config's check code, 561/564 for n, 578 where the
+/* Workspace bytes llmk_prefill needs for an n-token prompt (the row buffers, projection partials, logits and
+ * hidden states of one chunk), or -status: the config's check code, 561/564 for n, 578 where the
  * batched path cannot run (weights not bf16 output-major). */
 int64_t llmk_prefill_workspace_bytes(const llmk_config* cfg, int64_t n);
 
 /* Prefill of n prompt tokens into one slot ([xpu] "1. CausalLM: the forward path": a prompt chunk is a batch
  * of rows through the batched projections, and decode is the one-token chunk of the same step). Positions
- * pos0 .. pos0 + n - 1 of `slot`, in chunks of up to 64 rows: per layer every row of the chunk goes through
- * the matrix-core q|k|v projection together, then all rows' k (rotated) and v are written to the cache,
- * then row i attends over positions 0 .. pos0 + i of the slot (causal), then o, gate|up and down as in
- * llmk_decode_step_batch. The result equals n decode steps fed tokens_h[0..n) one by one.
+ * pos0 .. pos0 + n - 1 of `slot`, in chunks of up to 256 rows: per layer the chunk's rows go through the
+ * q|k|v projection together (a tiled matrix-core GEMM, each weight tile serving every row), then all rows'
+ * k (rotated) and v are written to the cache, then row i attends over positions 0 .. pos0 + i of the slot
+ * (causal), then o, gate|up and down the same way; the head's logits of every row give its greedy token. The result equals n decode steps fed tokens_h[0..n) one by one.
  *   tokens_h: host int64 [n]; tokens_out: device int32 [n], the greedy token after each position;
  *   logits (optional, NULL to skip): device fp32 [vocab] of the last position; hidden (optional): device
  *   fp32 [n_layer][d], the residual after every layer at the last position. ws: device scratch of len_ws >=

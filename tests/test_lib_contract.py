@@ -454,5 +454,5 @@ def test_prefill_refusals():
         assert llmk.prefill_workspace_bytes(llmk.make_config(**bad), 3) == -578
     cfg = llmk.make_config(**good)
     assert llmk.prefill_workspace_bytes(cfg, 0) == -561
-    # 200 tokens run in chunks of 64 rows: the workspace holds one 64-row plan, 64 rows of logits and hidden
-    assert llmk.prefill_workspace_bytes(cfg, 200) >= llmk.decode_workspace_bytes(cfg, 64) + 64 * (V + L * d) * 4
+    # 200 tokens are one chunk of 200 rows: the workspace holds its row buffers, its logits and hidden states
+    assert llmk.prefill_workspace_bytes(cfg, 200) >= llmk.decode_workspace_bytes(cfg, 64) + 200 * (V + L * d) * 4
