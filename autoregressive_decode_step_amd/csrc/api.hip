@@ -835,6 +835,8 @@ struct PrefillPlan {
   float* am_logit = nullptr;
   int32_t am_bpr = 0;
   float* hidden = nullptr;              // [M][n_layer][d]: the last chunk's hidden states, when asked for
+  float* fa_part = nullptr;             // chunk attention parts (when the shape takes the chunk attention)
+  int32_t fa_parts = 0;
   int64_t bytes = 0;
 };
 
@@ -868,6 +870,10 @@ void plan_prefill(const llmk_config* c, int64_t M, void* ws, PrefillPlan& P) {
   P.am_cnt = cv.take<unsigned>(M);
   P.am_logit = cv.take<float>(M);
   P.hidden = cv.take<float>(M * c->n_layer * d);
+  if (fattn_supported(c->n_head, c->n_kv, c->head_dim)) {
+    P.fa_parts = (int32_t)fattn_parts(c->max_seq);
+    P.fa_part = cv.take<float>(M * c->n_head * P.fa_parts * (c->head_dim + 2));
+  }
   P.bytes = cv.off;
 }
 
@@ -885,7 +891,7 @@ int64_t prefill_bytes(const llmk_config* c, int64_t n) {
 
 // One chunk: rows r = 0..M-1 of P at positions state.pos[r] of one slot, through every layer and the head.
 hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, PrefillPlan& P,
-                                 int32_t* tokens_out, bool want_hidden, hipStream_t s) {
+                                 int64_t ctx_end, int32_t* tokens_out, bool want_hidden, hipStream_t s) {
   const int64_t d = c->d;
   BatchPlan& B = P.rows;
   hipError_t e = hipSuccess;
@@ -903,7 +909,31 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
       g.ldo = g.N;
       e = pgemm_launch(g, PG_STORE, s);
     }
-    if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, B, l, BK_ATTN, nullptr, nullptr, nullptr, s);
+    if (e == hipSuccess && P.fa_part) {   // the chunk's K/V first, then attention of all rows together
+      FattnParams a{};
+      a.qkv = B.qkv_buf;
+      a.qkv_stride = P.qkv.N;
+      a.st = B.state;
+      a.rows = P.qkv.M;
+      a.H = (int32_t)c->n_head;
+      a.Hkv = (int32_t)c->n_kv;
+      a.k = pool->k[l];
+      a.v = pool->v[l];
+      a.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
+      a.slot_elems = pool->capacity * c->n_kv * c->head_dim;
+      a.rope_table = static_cast<const float*>(m->rope_table.ptr);
+      a.rope_layout = c->rope_layout;
+      a.span = FA_SPAN;
+      a.n_parts = P.fa_parts;
+      a.part = P.fa_part;
+      a.out_hi = B.att_hi;
+      a.out_lo = B.att_lo;
+      e = rope_append_rows_launch(a.qkv, a.qkv_stride, B.state, a.rows, a.H, a.Hkv, (int32_t)c->head_dim, a.rope_table,
+                                  a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, s);
+      if (e == hipSuccess) e = fattn_launch(a, ctx_end, s);
+    } else if (e == hipSuccess) {
+      e = launch_batch_kernel(c, m, pool, B, l, BK_ATTN, nullptr, nullptr, nullptr, s);
+    }
     if (e == hipSuccess) {
       PgemmParams g = P.o;
       g.ahi = B.att_hi;
@@ -1463,7 +1493,7 @@ int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_po
     e = fill_u32_launch(P.rows.counters, batch_counters_total(cfg, P.rows), 0u, s);
     if (e == hipSuccess) e = fill_u32_launch(P.am_cnt, M, 0u, s);
     if (e == hipSuccess) e = set_batch_state_launch(P.rows.state, init, s);
-    if (e == hipSuccess) e = enqueue_prefill_chunk(cfg, model, pool, P, tokens_out + c0, last && hidden, s);
+    if (e == hipSuccess) e = enqueue_prefill_chunk(cfg, model, pool, P, pos0 + c0 + M, tokens_out + c0, last && hidden, s);
     if (e == hipSuccess && last && logits)
       e = hipMemcpyAsync(logits, P.y + (M - 1) * cfg->vocab, cfg->vocab * sizeof(float), hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && last && hidden)

@@ -139,6 +139,31 @@ struct PgemmParams {
 void pgemm_plan(PgemmParams& p, int target_blocks);
 hipError_t pgemm_launch(const PgemmParams& p, int mode, hipStream_t s);
 
+// Prefill attention: 64 query vectors of one K/V head (chunk rows x its query heads) per workgroup over one
+// part of FA_SPAN positions, then a merge of the parts per (row, head) into the output as hi + lo.
+constexpr int FA_SPAN = 256;
+struct FattnParams {
+  const float* qkv;            // [rows][qkv_stride] raw q|k|v (q unrotated)
+  int64_t qkv_stride;
+  const BatchState* st;        // row r: position pos[r], slot slot[r] (one slot for the chunk)
+  int32_t rows;
+  int32_t H, Hkv;
+  const void* k;               // this layer's K / V pool buffers, the chunk's rows already appended
+  const void* v;
+  int32_t kv_is_bf16;
+  int64_t slot_elems;
+  const float* rope_table;
+  int32_t rope_layout;
+  int32_t span;                // FA_SPAN
+  int32_t n_parts;             // capacity of `part` in parts per (row, head)
+  float* part;                 // [rows][H][n_parts][hd + 2]: unnormalised output, max, sum
+  bf16_t* out_hi;              // [rows][H * hd]
+  bf16_t* out_lo;
+};
+bool fattn_supported(int64_t H, int64_t Hkv, int64_t hd);
+int64_t fattn_parts(int64_t max_ctx);
+hipError_t fattn_launch(const FattnParams& p, int64_t max_ctx, hipStream_t s);
+
 enum BgemmMode { BG_PLAIN = 0, BG_QKV = 1, BG_RESID = 2, BG_GATEUP = 3, BG_HEAD = 4 };
 
 struct BgemmParams {
