@@ -88,6 +88,8 @@ _SIGS = {
     "llmk_argmax": ([_p, _i64, _i64, _i64, _p, _p, _p, _i64, _p], _i32),
     "llmk_sample_workspace_bytes": ([_i64, _i64, _f32, _i32], _i64),
     "llmk_prefill_workspace_bytes": ([ctypes.POINTER(Config), _i64], _i64),
+    "llmk_prefill_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64,
+                               _p, _i64, _i64, _p, _i64, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
     "llmk_prefill": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _p, _i64,
                       _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_sample": ([_p, _i64, _i64, _i64, _f32, _i32, _f32, _p, _i64, _p, _p, _i64, _p], _i32),
@@ -389,6 +391,19 @@ def prefill(cfg: Config, model: Model, pool: KVPool, slot, tokens, pos0, tokens_
     return lib.llmk_prefill(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot, ptk,
                             len(tk), pos0, _ptr(tokens_out), _len(tokens_out), _ptr(logits), _len(logits),
                             _ptr(hidden), _len(hidden), _ptr(ws), _len(ws), _stream(stream))
+
+
+PREFILL_PHASES = ("norm", "projections", "attention", "head")
+
+
+def prefill_profiled(cfg: Config, model: Model, pool: KVPool, slot, tokens, pos0, tokens_out, ws, stream=None):
+    """(status, {phase: ms}) of one prefill with HIP events at its phase boundaries."""
+    tk, ptk = _host_i64(tokens)
+    out = (_f32 * len(PREFILL_PHASES))()
+    st = lib.llmk_prefill_profiled(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot, ptk,
+                                   len(tk), pos0, _ptr(tokens_out), _len(tokens_out), out, len(PREFILL_PHASES),
+                                   _ptr(ws), _len(ws), _stream(stream))
+    return st, {n: float(out[i]) for i, n in enumerate(PREFILL_PHASES)}
 
 
 def decode_kernel_count(cfg: Config) -> int:

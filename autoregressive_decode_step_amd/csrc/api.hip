@@ -4,6 +4,8 @@
 #include <algorithm>
 #include <string.h>
 
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -889,14 +891,42 @@ int64_t prefill_bytes(const llmk_config* c, int64_t n) {
   return bytes;
 }
 
+// Measurement aid: HIP events recorded on the stream at the phase boundaries of a prefill; a phase's time is
+// the span between the event before it and the event after it.
+enum PrefillPhase { PF_NORM = 0, PF_PROJ = 1, PF_ATTN = 2, PF_HEAD = 3, PF_CLASSES = 4 };
+struct PhaseTimer {
+  hipStream_t s = nullptr;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> cls;                 // cls[i]: the phase that event i closes (-1: a starting mark)
+  hipError_t err = hipSuccess;
+  void mark(int phase) {
+    hipEvent_t e = nullptr;
+    if (err == hipSuccess) err = hipEventCreate(&e);
+    if (err == hipSuccess) err = hipEventRecord(e, s);
+    if (e) {
+      ev.push_back(e);
+      cls.push_back(phase);
+    }
+  }
+  ~PhaseTimer() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+
 // One chunk: rows r = 0..M-1 of P at positions state.pos[r] of one slot, through every layer and the head.
 hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, const llmk_kv_pool* pool, PrefillPlan& P,
-                                 int64_t ctx_end, int32_t* tokens_out, bool want_hidden, hipStream_t s) {
+                                 int64_t ctx_end, int32_t* tokens_out, bool want_hidden, hipStream_t s,
+                                 PhaseTimer* tm) {
   const int64_t d = c->d;
   BatchPlan& B = P.rows;
   hipError_t e = hipSuccess;
+  auto mark = [&](int phase) {
+    if (tm && e == hipSuccess) tm->mark(phase);
+  };
+  mark(-1);
   for (int64_t l = 0; l < c->n_layer && e == hipSuccess; ++l) {
     e = launch_batch_kernel(c, m, pool, B, l, BK_NORM1, nullptr, nullptr, nullptr, s);
+    mark(PF_NORM);
     if (e == hipSuccess) {
       PgemmParams g = P.qkv;
       g.ahi = B.h_hi;
@@ -909,6 +939,7 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
       g.ldo = g.N;
       e = pgemm_launch(g, PG_STORE, s);
     }
+    mark(PF_PROJ);
     if (e == hipSuccess && P.fa_part) {   // the chunk's K/V first, then attention of all rows together
       FattnParams a{};
       a.qkv = B.qkv_buf;
@@ -934,6 +965,7 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
     } else if (e == hipSuccess) {
       e = launch_batch_kernel(c, m, pool, B, l, BK_ATTN, nullptr, nullptr, nullptr, s);
     }
+    mark(PF_ATTN);
     if (e == hipSuccess) {
       PgemmParams g = P.o;
       g.ahi = B.att_hi;
@@ -944,7 +976,9 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
       g.ldo = d;
       e = pgemm_launch(g, PG_RESID, s);
     }
+    mark(PF_PROJ);
     if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, B, l, BK_NORM2, nullptr, nullptr, nullptr, s);
+    mark(PF_NORM);
     if (e == hipSuccess) {
       PgemmParams g = P.gu;
       g.ahi = B.h_hi;
@@ -968,8 +1002,10 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
       g.hidden_stride = c->n_layer * d;
       e = pgemm_launch(g, PG_RESID, s);
     }
+    mark(PF_PROJ);
   }
   if (e == hipSuccess) e = launch_batch_kernel(c, m, pool, B, 0, BK_NORMF, nullptr, nullptr, nullptr, s);
+  mark(PF_NORM);
   if (e == hipSuccess) {
     PgemmParams g = P.head;
     g.ahi = B.h_hi;
@@ -980,6 +1016,8 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
   }
   if (e == hipSuccess)
     e = argmax_launch(P.y, P.head.M, c->vocab, tokens_out, P.am_logit, P.am_val, P.am_idx, P.am_cnt, P.am_bpr, s);
+  mark(PF_HEAD);
+  if (e == hipSuccess && tm) e = tm->err;
   return e;
 }
 
@@ -1449,10 +1487,14 @@ int64_t llmk_prefill_workspace_bytes(const llmk_config* cfg, int64_t n) {
   return prefill_bytes(cfg, n);
 }
 
-int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
-                     const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out, int64_t len_tokens,
-                     float* logits, int64_t len_logits, float* hidden, int64_t len_hidden, void* ws, int64_t len_ws,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+int32_t prefill_run(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                    const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out, int64_t len_tokens,
+                    float* logits, int64_t len_logits, float* hidden, int64_t len_hidden, void* ws, int64_t len_ws,
+                    hipStream_t s, PhaseTimer* tm) {
   if (!cfg || !model || !pool || !tokens_h || !tokens_out || !ws) return LLMK_INVALID_ARGUMENT;
   int32_t st = config_check(cfg);
   if (st != LLMK_OK) return st;
@@ -1473,7 +1515,6 @@ int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_po
   if (hidden && len_hidden != cfg->n_layer * cfg->d) return LLMK_OUTPUT_LENGTH_MISMATCH;
   if (len_ws < prefill_bytes(cfg, n)) return LLMK_INVALID_ARGUMENT;
 
-  hipStream_t s = as_stream(stream);
   hipError_t e = hipSuccess;
   const int64_t rows = std::min(n, kPrefillRows);
   for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += rows) {
@@ -1493,7 +1534,7 @@ int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_po
     e = fill_u32_launch(P.rows.counters, batch_counters_total(cfg, P.rows), 0u, s);
     if (e == hipSuccess) e = fill_u32_launch(P.am_cnt, M, 0u, s);
     if (e == hipSuccess) e = set_batch_state_launch(P.rows.state, init, s);
-    if (e == hipSuccess) e = enqueue_prefill_chunk(cfg, model, pool, P, pos0 + c0 + M, tokens_out + c0, last && hidden, s);
+    if (e == hipSuccess) e = enqueue_prefill_chunk(cfg, model, pool, P, pos0 + c0 + M, tokens_out + c0, last && hidden, s, tm);
     if (e == hipSuccess && last && logits)
       e = hipMemcpyAsync(logits, P.y + (M - 1) * cfg->vocab, cfg->vocab * sizeof(float), hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && last && hidden)
@@ -1503,6 +1544,40 @@ int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_po
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   pool->slot_len_h[slot] = pos0 + n;
   return LLMK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                     const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out, int64_t len_tokens,
+                     float* logits, int64_t len_logits, float* hidden, int64_t len_hidden, void* ws, int64_t len_ws,
+                     void* stream) {
+  return prefill_run(cfg, model, pool, slot, tokens_h, n, pos0, tokens_out, len_tokens, logits, len_logits, hidden,
+                     len_hidden, ws, len_ws, as_stream(stream), nullptr);
+}
+
+int32_t llmk_prefill_profiled(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                              const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out,
+                              int64_t len_tokens, float* class_ms_h, int64_t len_class_ms, void* ws, int64_t len_ws,
+                              void* stream) {
+  if (!class_ms_h) return LLMK_INVALID_ARGUMENT;
+  if (len_class_ms < PF_CLASSES) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  PhaseTimer tm;
+  tm.s = as_stream(stream);
+  int32_t st = prefill_run(cfg, model, pool, slot, tokens_h, n, pos0, tokens_out, len_tokens, nullptr, 0, nullptr, 0,
+                           ws, len_ws, tm.s, &tm);
+  if (st != LLMK_OK) return st;
+  hipError_t e = hipStreamSynchronize(tm.s);
+  for (int k = 0; k < PF_CLASSES; ++k) class_ms_h[k] = 0.0f;
+  for (size_t i = 1; e == hipSuccess && i < tm.ev.size(); ++i) {
+    if (tm.cls[i] < 0) continue;
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, tm.ev[i - 1], tm.ev[i]);
+    class_ms_h[tm.cls[i]] += ms;
+  }
+  return e == hipSuccess ? LLMK_OK : LLMK_DEVICE_ERROR;
 }
 
 int32_t llmk_decode_steps_batch(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t batch,

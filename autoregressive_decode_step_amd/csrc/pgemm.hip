@@ -34,6 +34,12 @@ __device__ __forceinline__ pg_f32x4_t pg_mfma(const uint4& a, const uint4& b, co
                                                  __builtin_bit_cast(pg_bf16x8_t, b), c, 0, 0, 0);
 }
 
+// v where the mask is all ones, zero where it is zero (a per-word mask: a select of whole vectors would go
+// through memory)
+__device__ __forceinline__ uint4 pg_mask(const uint4& v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 // W row n (clamped into [0, N)): rows [0, n0) of w0, then n1 rows of w1, then w2
 __device__ __forceinline__ const bf16_t* pg_wrow(const PgemmParams& p, int64_t n) {
   const int64_t r = min(n, p.N - 1);
@@ -42,7 +48,7 @@ __device__ __forceinline__ const bf16_t* pg_wrow(const PgemmParams& p, int64_t n
   return static_cast<const bf16_t*>(p.w2) + (r - p.n0 - p.n1) * p.K;
 }
 
-__global__ __launch_bounds__(PG_THREADS) void pgemm_kernel(const PgemmParams p) {
+__global__ __launch_bounds__(PG_THREADS, 1) void pgemm_kernel(const PgemmParams p) {
   __shared__ __align__(16) bf16_t s_a[2][2][PG_BM][PG_LDK];   // [buffer][hi, lo][row][k]
   __shared__ __align__(16) bf16_t s_w[2][PG_BN][PG_LDK];      // [buffer][row][k]
 
@@ -54,7 +60,10 @@ __global__ __launch_bounds__(PG_THREADS) void pgemm_kernel(const PgemmParams p) 
   const int64_t ke = min(p.K, kb + p.kslice);
   const int nk = (int)((ke - kb + PG_BK - 1) / PG_BK);
 
-  // staging: thread t moves 8-element groups g = t and t + 256 of each 128 x 32 tile (row g / 4, group g % 4)
+  // staging: thread t moves 8-element groups g = t and t + 256 of each 128 x 32 tile (row g / 4, group g % 4).
+  // Two register sets in turn keep the loads of slice i + 2 in flight while slice i is multiplied and slice
+  // i + 1 goes to LDS; every load is issued unconditionally (past the end of K, from k = 0) and zeroed when it
+  // is staged, so no load sits in a branch of its own.
   const bf16_t* ah[2];
   const bf16_t* al[2];
   const bf16_t* wr[2];
@@ -65,28 +74,36 @@ __global__ __launch_bounds__(PG_THREADS) void pgemm_kernel(const PgemmParams p) 
     srow[i] = g >> 2;
     sk[i] = (g & 3) * 8;
     const int64_t m = min(m0 + srow[i], (int64_t)p.M - 1);   // rows past M read a valid row; never stored
-    ah[i] = p.ahi + m * p.lda + sk[i];
-    al[i] = p.alo + m * p.lda + sk[i];
-    wr[i] = pg_wrow(p, n0 + srow[i]) + sk[i];
+    ah[i] = p.ahi + m * p.lda;
+    al[i] = p.alo + m * p.lda;
+    wr[i] = pg_wrow(p, n0 + srow[i]);
   }
-  uint4 rah[2], ral[2], rw[2];
-  auto load = [&](int64_t k) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool ok = k + sk[i] < ke;   // K is a multiple of 8: a group is all in or all out
-      rah[i] = ok ? *reinterpret_cast<const uint4*>(ah[i] + k) : make_uint4(0, 0, 0, 0);
-      ral[i] = ok ? *reinterpret_cast<const uint4*>(al[i] + k) : make_uint4(0, 0, 0, 0);
-      rw[i] = ok ? *reinterpret_cast<const uint4*>(wr[i] + k) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&s_a[buf][0][srow[i]][sk[i]]) = rah[i];
-      *reinterpret_cast<uint4*>(&s_a[buf][1][srow[i]][sk[i]]) = ral[i];
-      *reinterpret_cast<uint4*>(&s_w[buf][srow[i]][sk[i]]) = rw[i];
-    }
-  };
+  // a set's k: its groups past the end of K are zeroed when staged (K is a multiple of 8: a group is all in or
+  // all out)
+  uint4 a0h0, a0h1, a0l0, a0l1, w00, w01;   // set 0
+  uint4 a1h0, a1h1, a1l0, a1l1, w10, w11;   // set 1
+  int64_t k0s = 0, k1s = 0;
+#define PG_LOAD(AH0, AH1, AL0, AL1, W0, W1, KS, K)                                      \
+  {                                                                                     \
+    KS = (K);                                                                           \
+    const int64_t c0 = KS + sk[0] < ke ? KS + sk[0] : 0, c1 = KS + sk[1] < ke ? KS + sk[1] : 0; \
+    AH0 = *reinterpret_cast<const uint4*>(ah[0] + c0);                                  \
+    AH1 = *reinterpret_cast<const uint4*>(ah[1] + c1);                                  \
+    AL0 = *reinterpret_cast<const uint4*>(al[0] + c0);                                  \
+    AL1 = *reinterpret_cast<const uint4*>(al[1] + c1);                                  \
+    W0 = *reinterpret_cast<const uint4*>(wr[0] + c0);                                   \
+    W1 = *reinterpret_cast<const uint4*>(wr[1] + c1);                                   \
+  }
+#define PG_STAGE(AH0, AH1, AL0, AL1, W0, W1, KS, BUF)                                   \
+  {                                                                                     \
+    const uint32_t i0 = KS + sk[0] < ke ? ~0u : 0u, i1 = KS + sk[1] < ke ? ~0u : 0u;   \
+    *reinterpret_cast<uint4*>(&s_a[BUF][0][srow[0]][sk[0]]) = pg_mask(AH0, i0);         \
+    *reinterpret_cast<uint4*>(&s_a[BUF][0][srow[1]][sk[1]]) = pg_mask(AH1, i1);         \
+    *reinterpret_cast<uint4*>(&s_a[BUF][1][srow[0]][sk[0]]) = pg_mask(AL0, i0);         \
+    *reinterpret_cast<uint4*>(&s_a[BUF][1][srow[1]][sk[1]]) = pg_mask(AL1, i1);         \
+    *reinterpret_cast<uint4*>(&s_w[BUF][srow[0]][sk[0]]) = pg_mask(W0, i0);             \
+    *reinterpret_cast<uint4*>(&s_w[BUF][srow[1]][sk[1]]) = pg_mask(W1, i1);             \
+  }
 
   pg_f32x4_t acc[4][4];
 #pragma unroll
@@ -95,14 +112,7 @@ __global__ __launch_bounds__(PG_THREADS) void pgemm_kernel(const PgemmParams p) 
     for (int j = 0; j < 4; ++j) acc[i][j] = pg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int orow = lane & 15, ok8 = (lane >> 4) * 8;
-  if (nk > 0) {
-    load(kb);
-    stage(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nk) load(kb + (int64_t)(it + 1) * PG_BK);   // the next slice in flight during the products
+  auto multiply = [&](int buf) {
     uint4 wop[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) wop[j] = *reinterpret_cast<const uint4*>(&s_w[buf][wn * 64 + j * 16 + orow][ok8]);
@@ -116,10 +126,31 @@ __global__ __launch_bounds__(PG_THREADS) void pgemm_kernel(const PgemmParams p) 
         acc[i][j] = pg_mfma(xl, wop[j], acc[i][j]);
       }
     }
-    // the other buffer was last read before the previous barrier
-    if (it + 1 < nk) stage(buf ^ 1);
+  };
+  // slice i lives in LDS buffer i % 2 and comes through register set i % 2; at step i the set of slice i is
+  // free again (its slice is in LDS) and takes slice i + 2, and the other set's slice i + 1 goes to the other
+  // buffer, which was last read before the previous barrier
+  // loads are issued every step (a slice past the last one reads the first again and is never staged), so
+  // each set's registers live only from its load to its staging
+  auto kof = [&](int i) { return i < nk ? kb + (int64_t)i * PG_BK : kb; };
+  PG_LOAD(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, kb)
+  PG_LOAD(a1h0, a1h1, a1l0, a1l1, w10, w11, k1s, kof(1))
+  if (nk > 0) PG_STAGE(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, 0)
+  __syncthreads();
+  for (int it = 0; it < nk; it += 2) {
+    PG_LOAD(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, kof(it + 2))
+    multiply(0);
+    if (it + 1 < nk) PG_STAGE(a1h0, a1h1, a1l0, a1l1, w10, w11, k1s, 1)
     __syncthreads();
+    if (it + 1 < nk) {
+      PG_LOAD(a1h0, a1h1, a1l0, a1l1, w10, w11, k1s, kof(it + 3))
+      multiply(1);
+      if (it + 2 < nk) PG_STAGE(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, 0)
+      __syncthreads();
+    }
   }
+#undef PG_LOAD
+#undef PG_STAGE
 
   // this split's partial tile: lane l holds rows 4 (l / 16) .. + 3 of each 16-row tile at column l % 16
   float* y = p.y + (int64_t)blockIdx.z * p.M * p.N;

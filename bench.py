@@ -176,6 +176,116 @@ def prefill_probe(shape: str, n: int = 2048, reps: int = 3) -> int:
     return 0
 
 
+PREFILL_TOKENS = 2048
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+
+
+def prefill_flops(s, n: int, pos0: int = 0) -> dict:
+    """Algorithmic flops of an n-token prefill from position pos0: the projections (2 flops per weight per row)
+    and causal attention (q.k and p.v over each row's visible positions, 4 hd flops per position and head)."""
+    d, qd, kvd, F, L = s.d, s.n_head * s.head_dim, s.n_kv * s.head_dim, s.hidden, s.n_layer
+    proj = 2 * n * L * (d * (qd + 2 * kvd) + qd * d + 2 * d * F + F * d)
+    attn = 4 * s.head_dim * s.n_head * L * sum(pos0 + i + 1 for i in range(n))
+    head = 2 * n * s.vocab * d
+    return {"projections": proj, "attention": attn, "head": head}
+
+
+def run_prefill(args) -> int:
+    import torch
+
+    import synth
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd import loader
+    s = {"q06": synth.Q06, "l8b": synth.L8B}[args.prefill_shape]
+    n = PREFILL_TOKENS
+    steps = args.steps if args.steps != 256 else 8
+    t_start = time.time()
+    log(f"generating {s.name} weights")
+    W = synth.model(s, seed=0)
+    cfg = loader.config_from(s)
+    model = loader.upload_model(cfg, W)
+    pool = loader.new_pool(cfg, 1, n + 8)
+    tokens = synth.prompt(n, s.vocab, stream=23).tolist()
+    ws = llmk.workspace(llmk.prefill_workspace_bytes(cfg, n))
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"resident in HBM after {time.time() - t_start:.1f} s")
+
+    def once():
+        pool.slot_len[0] = 0
+        st = llmk.prefill(cfg, model, pool, 0, tokens, 0, out, ws)
+        if st != llmk.OK:
+            raise RuntimeError(f"llmk_prefill: {st} {llmk.status_name(st)}")
+
+    for _ in range(max(args.warmup, 1)):
+        once()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        once()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / steps
+    pool.slot_len[0] = 0
+    st, phase_ms = llmk.prefill_profiled(cfg, model, pool, 0, tokens, 0, out, ws)
+    if st != llmk.OK:
+        raise RuntimeError(f"llmk_prefill_profiled: {st} {llmk.status_name(st)}")
+    gpu_tokens = out.cpu().tolist()
+    fl = prefill_flops(s, n)
+    log(f"timed {steps} prompts of {n} tokens: {ms:.2f} ms each, {n / ms * 1e3:.0f} tokens/s; phases (ms) "
+        + ", ".join(f"{k} {v:.2f}" for k, v in phase_ms.items()))
+    dom = max(("projections", "attention"), key=lambda k: phase_ms[k])
+    tflops = fl[dom] / (phase_ms[dom] * 1e-3) / 1e12
+    result = {
+        "metric": f"prefill tokens/s ({n}-token prompt)",
+        "value": n / ms * 1e3,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name} prefill of a {n}-token seeded prompt into an empty slot, chunks of 256 "
+                               "rows, projections and attention on bf16 matrix cores (activations as bf16 hi + lo)",
+                   "prompt_tokens": n, "chunk_rows": 256, "weights": s.w_dtype, "kv": s.kv_dtype,
+                   "accumulation": "f32"},
+        "phase_ms": phase_ms,
+        "roofline": {"bound": "mfma", "kernel": "prefill " + dom + (" (pgemm_kernel + epilogue)" if dom == "projections"
+                                                                    else " (rope_append + fattn_kernel + merge)"),
+                     "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_prompt": fl[dom], "ms_per_prompt": phase_ms[dom],
+                     "note": "algorithmic flops; the bf16 hi + lo activations make the matrix cores execute twice "
+                             "(three times against fp32 K/V) as many"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        k = args.cpu_prefill_tokens
+        log(f"oracle baseline: the first {k} prompt tokens, one at a time, on the host cores")
+        m = oracle.Model(s, W)
+        c = m.new_cache(k)
+        otoks = []
+        tc0 = time.perf_counter()
+        for i in range(k):
+            lg, _ = m.forward_token(tokens[i], i, c)
+            otoks.append(oracle.argmax(lg)[0])
+        tc = time.perf_counter() - tc0
+        result["cpu_baseline"] = {"value": k / tc, "unit": "tokens/s", "cores": oracle.lib().orc_num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"the first {k} tokens of the same prompt, one decode step each (fp64, "
+                                            f"OpenMP)",
+                                  "tokens_agree_with_gpu": otoks == gpu_tokens[:k]}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    log(f"total {time.time() - t_start:.1f} s")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,8 +295,12 @@ def main() -> int:
                     help="times each kernel class's per-layer launches are replayed for its HIP-event timing")
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle steps in the CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("batch1", "batched"), default="batch1",
-                    help="batch1: the 8B-shaped single-sequence step (default); batched: 64 ragged sequences per step")
+    ap.add_argument("--workload", choices=("batch1", "batched", "prefill"), default="batch1",
+                    help="batch1: the 8B-shaped single-sequence step (default); batched: 64 ragged sequences per step; "
+                         "prefill: a 2,048-token prompt (steps = prompts, 8 by default)")
+    ap.add_argument("--prefill-shape", choices=("q06", "l8b"), default="q06",
+                    help="the prefill workload's shape: Qwen3-0.6B (the 2,048-token prefix workload) or Llama-3-8B")
+    ap.add_argument("--cpu-prefill-tokens", type=int, default=24, help="oracle tokens in the prefill CPU baseline")
     ap.add_argument("--step-path", choices=("auto", "per-op", "persistent"), default="auto",
                     help="the decode step's form: the library's choice (default), one kernel per operation, or "
                          "the persistent one-kernel step")
@@ -221,6 +335,8 @@ def main() -> int:
         return sample_probe(args.sample_probe)
     if args.workload == "batched":
         return run_batched(args)
+    if args.workload == "prefill":
+        return run_prefill(args)
 
     s = synth.L8B
     max_steps_per_call = s.max_seq - N_PRE

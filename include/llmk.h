@@ -391,6 +391,17 @@ int32_t llmk_prefill(const llmk_config* cfg, const llmk_model* model, llmk_kv_po
                      float* logits, int64_t len_logits, float* hidden, int64_t len_hidden, void* ws, int64_t len_ws,
                      void* stream);
 
+/* Measurement aid (not on the prefill path): llmk_prefill (logits and hidden not returned) with a HIP event
+ * recorded on `stream` at every boundary between its phases. Waits for the call, then writes the summed
+ * milliseconds of each phase class to class_ms_h: 0 the RMSNorms (and the first layer's embedding gather), 1 the
+ * projections q|k|v, o, gate|up and down (GEMMs and their epilogues), 2 attention (K/V write, chunk attention,
+ * merge), 3 the output head and its argmax. Codes: 578 (class_ms_h NULL), 577 (len_class_ms < 4), then as
+ * llmk_prefill. On success slot_len_h[slot] = pos0 + n. */
+int32_t llmk_prefill_profiled(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                              const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out,
+                              int64_t len_tokens, float* class_ms_h, int64_t len_class_ms, void* ws, int64_t len_ws,
+                              void* stream);
+
 /* dst = src^T for a rows x cols row-major matrix (dst is cols x rows), both device buffers of rows*cols
  * elements of dtype; the one-time repacking of projections into LLMK_W_OUT_IN. dst may not alias src.
  * Codes: 578 (null, dtype, aliasing), 561, 564, 562 (len_src), 577 (len_dst). */

@@ -452,7 +452,21 @@ def test_prefill_refusals():
         exp = contract.prefill(bad, n=3, n_slots=3, capacity=32, slot=1, tokens=[0] * 3, batch_weights_ok=False)
         assert run(bad) == exp == 578
         assert llmk.prefill_workspace_bytes(llmk.make_config(**bad), 3) == -578
+    # the profiled form refuses a missing or short phase buffer first, then as llmk_prefill
     cfg = llmk.make_config(**good)
+    m, _keep = model_for()
+    ks = (ctypes.c_void_p * L)(FA, FA)
+    sl = np.zeros(3, np.int64)
+    ps = llmk.PoolStruct(ks, ks, L, 3, 32, 2, 4, good["kv_dtype"], sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    tk = np.zeros(3, np.int64)
+    ms = (ctypes.c_float * 4)()
+    prof = llmk.lib.llmk_prefill_profiled
+    assert prof(ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), 1, tk.ctypes.data, 3, 0, FA, 3, None, 4, FA,
+                1 << 30, None) == 578
+    assert prof(ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), 1, tk.ctypes.data, 3, 0, FA, 3, ms, 3, FA,
+                1 << 30, None) == 577
+    assert prof(ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), 3, tk.ctypes.data, 3, 0, FA, 3, ms, 4, FA,
+                1 << 30, None) == contract.prefill(good, n=3, n_slots=3, capacity=32, slot=3, tokens=[0] * 3) == 575
     assert llmk.prefill_workspace_bytes(cfg, 0) == -561
     # 200 tokens are one chunk of 200 rows: the workspace holds its row buffers, its logits and hidden states
     assert llmk.prefill_workspace_bytes(cfg, 200) >= llmk.decode_workspace_bytes(cfg, 64) + 200 * (V + L * d) * 4
