@@ -50,24 +50,6 @@ __device__ __forceinline__ float fa_sum16(float v) {
   return v;
 }
 
-// 8 consecutive cache elements as bf16 hi (and lo for an fp32 cache)
-template <typename T>
-__device__ __forceinline__ void fa_load8(const T* src, bf16_t (&hi)[8], bf16_t (&lo)[8]);
-template <>
-__device__ __forceinline__ void fa_load8<bf16_t>(const bf16_t* src, bf16_t (&hi)[8], bf16_t (&lo)[8]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(src);
-  *reinterpret_cast<uint4*>(hi) = v;
-  (void)lo;
-}
-template <>
-__device__ __forceinline__ void fa_load8<float>(const float* src, bf16_t (&hi)[8], bf16_t (&lo)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(src);
-  const float4 b = *reinterpret_cast<const float4*>(src + 4);
-  const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
-}
-
 template <typename T>
 __global__ __launch_bounds__(FA_THREADS) void fattn_kernel(const FattnParams p) {
   constexpr bool LO = sizeof(T) == 4;   // fp32 K/V carry a lo part
@@ -99,27 +81,39 @@ __global__ __launch_bounds__(FA_THREADS) void fattn_kernel(const FattnParams p) 
   // q of the 64 vectors (vector v: chunk row r0 + v / G, query head kvh * G + v % G), rotated by the row's
   // position, as hi + lo; vectors past the chunk are zero
   constexpr int HALF = FA_HD / 2;
-  for (int i = t; i < FA_QV * HALF; i += FA_THREADS) {
-    const int v = i / HALF, j = i % HALF;
+  static_assert(FA_QV * 4 == FA_THREADS && HALF % 4 == 0, "four threads per query vector");
+  {
+    // thread t takes vector t / 4 and rotation pairs 16 (t % 4) .. + 15; every load is issued before any use
+    // (rows past the chunk read the last row and are zeroed)
+    constexpr int NJ = HALF / 4;
+    const int v = t >> 2, j0 = (t & 3) * NJ;
     const int row = r0 + v / G;
-    const int ia = p.rope_layout == 0 ? j : 2 * j;
-    const int ib = p.rope_layout == 0 ? j + HALF : 2 * j + 1;
-    float ra = 0.0f, rb = 0.0f;
-    if (row < r_end) {
-      const float* q = p.qkv + (int64_t)row * p.qkv_stride + (int64_t)(kvh * G + v % G) * FA_HD;
-      const float* tab = p.rope_table + ((int64_t)p.st->pos[row] * HALF + j) * 2;
-      const float cs = tab[0], sn = tab[1];
-      const float a = q[ia], b = q[ib];
-      ra = a * cs - b * sn;
-      rb = a * sn + b * cs;
+    const int rowc = min(row, r_end - 1);
+    const float* q = p.qkv + (int64_t)rowc * p.qkv_stride + (int64_t)(kvh * G + v % G) * FA_HD;
+    const float* tab = p.rope_table + ((int64_t)p.st->pos[rowc] * HALF + j0) * 2;
+    float a[NJ], b[NJ], cs[NJ], sn[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = j0 + jj;
+      a[jj] = q[p.rope_layout == 0 ? j : 2 * j];
+      b[jj] = q[p.rope_layout == 0 ? j + HALF : 2 * j + 1];
+      cs[jj] = tab[2 * jj];
+      sn[jj] = tab[2 * jj + 1];
     }
-    bf16_t h, l;
-    split_bf16(ra, h, l);
-    s_qh[v][ia] = h;
-    s_ql[v][ia] = l;
-    split_bf16(rb, h, l);
-    s_qh[v][ib] = h;
-    s_ql[v][ib] = l;
+    const float keep = row < r_end ? 1.0f : 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = j0 + jj;
+      const int ia = p.rope_layout == 0 ? j : 2 * j;
+      const int ib = p.rope_layout == 0 ? j + HALF : 2 * j + 1;
+      bf16_t h, l;
+      split_bf16(keep * (a[jj] * cs[jj] - b[jj] * sn[jj]), h, l);
+      s_qh[v][ia] = h;
+      s_ql[v][ia] = l;
+      split_bf16(keep * (a[jj] * sn[jj] + b[jj] * cs[jj]), h, l);
+      s_qh[v][ib] = h;
+      s_ql[v][ib] = l;
+    }
   }
 
   // this lane's four query rows (of the wave's 16): vector 16 w + 4 (l / 16) + e, its position
@@ -140,24 +134,71 @@ __global__ __launch_bounds__(FA_THREADS) void fattn_kernel(const FattnParams p) 
 #pragma unroll
   for (int d = 0; d < 8; ++d) o[d] = fa_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int orow = lane & 15, ok8 = (lane >> 4) * 8;
-  for (int t0 = tb; t0 < te; t0 += FA_CH) {
-    __syncthreads();   // q staged (first tile) / the previous tile's K, V and P fully read
-    // K tile [position][dim] and V tile transposed [dim][position]; positions past te repeat te - 1 (masked)
-    for (int i = t; i < FA_CH * (FA_HD / 8); i += FA_THREADS) {
-      const int r = i / (FA_HD / 8), c = (i % (FA_HD / 8)) * 8;
-      const int64_t pos = min(t0 + r, te - 1);
-      bf16_t kh[8], kl[8], vh[8], vl[8];
-      fa_load8<T>(K + pos * rstride + c, kh, kl);
-      fa_load8<T>(V + pos * rstride + c, vh, vl);
-      *reinterpret_cast<uint4*>(&s_kh[r][c]) = *reinterpret_cast<const uint4*>(kh);
-      if constexpr (LO) *reinterpret_cast<uint4*>(&s_kl[r][c]) = *reinterpret_cast<const uint4*>(kl);
+  // K/V tile staging: lane l of wave w takes position l of the tile and dims 8 (w + 4 j) .. + 7 for j = 0..3, so
+  // the transposed V writes of a wave fill contiguous LDS rows. The next tile's loads are issued as soon as
+  // the current tile is in LDS and complete while it is multiplied. Positions past te repeat te - 1 (masked).
+  constexpr int NG = FA_CH * FA_HD / 8 / FA_THREADS;       // 8-element groups per thread and tile
+  constexpr int VPG = sizeof(T) / 2;                        // 16-byte loads per group
+  uint4 kr[NG * VPG], vr[NG * VPG];
+  auto load_tile = [&](int t0) {
+    const int64_t pos = min(t0 + lane, te - 1);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        s_vh[c + k][r] = vh[k];
-        if constexpr (LO) s_vl[c + k][r] = vl[k];
+    for (int j = 0; j < NG; ++j) {
+      const int c = (wave + 4 * j) * 8;
+#pragma unroll
+      for (int u = 0; u < VPG; ++u) {
+        kr[j * VPG + u] = *reinterpret_cast<const uint4*>(K + pos * rstride + c + u * (8 / VPG));
+        vr[j * VPG + u] = *reinterpret_cast<const uint4*>(V + pos * rstride + c + u * (8 / VPG));
       }
     }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int c = (wave + 4 * j) * 8;
+      // pairs of bf16 (element 2e in the low half): the hi parts, and the lo parts of an fp32 cache
+      uint32_t kh[4], kl[4], vh[4], vl[4];
+      if constexpr (LO) {
+        const uint32_t kw[8] = {kr[2 * j].x, kr[2 * j].y, kr[2 * j].z, kr[2 * j].w,
+                                kr[2 * j + 1].x, kr[2 * j + 1].y, kr[2 * j + 1].z, kr[2 * j + 1].w};
+        const uint32_t vw[8] = {vr[2 * j].x, vr[2 * j].y, vr[2 * j].z, vr[2 * j].w,
+                                vr[2 * j + 1].x, vr[2 * j + 1].y, vr[2 * j + 1].z, vr[2 * j + 1].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16_t h0, l0, h1, l1;
+          split_bf16(__uint_as_float(kw[2 * e]), h0, l0);
+          split_bf16(__uint_as_float(kw[2 * e + 1]), h1, l1);
+          kh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          kl[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          split_bf16(__uint_as_float(vw[2 * e]), h0, l0);
+          split_bf16(__uint_as_float(vw[2 * e + 1]), h1, l1);
+          vh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          vl[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        *reinterpret_cast<uint4*>(&s_kl[lane][c]) = make_uint4(kl[0], kl[1], kl[2], kl[3]);
+      } else {
+        kh[0] = kr[j].x, kh[1] = kr[j].y, kh[2] = kr[j].z, kh[3] = kr[j].w;
+        vh[0] = vr[j].x, vh[1] = vr[j].y, vh[2] = vr[j].z, vh[3] = vr[j].w;
+      }
+      *reinterpret_cast<uint4*>(&s_kh[lane][c]) = make_uint4(kh[0], kh[1], kh[2], kh[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_vh[c + 2 * e][lane] = (bf16_t)(vh[e] & 0xFFFFu);
+        s_vh[c + 2 * e + 1][lane] = (bf16_t)(vh[e] >> 16);
+        if constexpr (LO) {
+          s_vl[c + 2 * e][lane] = (bf16_t)(vl[e] & 0xFFFFu);
+          s_vl[c + 2 * e + 1][lane] = (bf16_t)(vl[e] >> 16);
+        }
+      }
+    }
+  };
+
+  const int orow = lane & 15, ok8 = (lane >> 4) * 8;
+  load_tile(tb);
+  for (int t0 = tb; t0 < te; t0 += FA_CH) {
+    __syncthreads();   // q staged (first tile) / the previous tile's K, V and P fully read
+    store_tile();
+    if (t0 + FA_CH < te) load_tile(t0 + FA_CH);
     __syncthreads();
 
     // S = Q K^T for the wave's 16 queries x 64 positions (4 column tiles of 16)
