@@ -13,11 +13,12 @@
 // the survivor order, and the key gives the value back.
 //
 // No float atomics anywhere, so a row and a draw always give the same token. Three forms, by row length and k:
-//   wave slices (the usual one): a row is cut into G slices of 2,048 logits with G * k <= SAMPLE_MERGE_MAX.
-//     One wave per slice holds the slice's keys in registers (32 a lane) and emits the slice's own top-k
-//     (ties to the lower index) to the workspace: every survivor of the row is among them. One workgroup per
-//     row then selects the row's top-k from the G * k candidates (8 a thread, in registers), ranks them in
-//     LDS and draws.
+//   wave slices (the usual one): a row is cut into G slices of 1,024 (else 2,048) logits with G * k <=
+//     SAMPLE_MERGE_MAX. One wave per slice holds the slice's keys in registers (16 or 32 a lane) and emits the
+//     slice's own top-k (ties to the lower index) to the workspace: every survivor of the row is among them.
+//     One workgroup per row then keeps the candidates at or above the k-th largest slice maximum (a floor for
+//     the row's k-th largest) and ranks them in LDS, or, when that leaves too many, selects the row's top-k
+//     from all G * k candidates (8 a thread, in registers); then it draws.
 //   block slices (larger k): the same with slices of 16,384 logits, one 1024-thread workgroup each.
 //   wide (rows too long for either): one workgroup per row selects straight from the logits with a radix
 //     select over LDS histograms (four passes of 8-bit digits, sixteen histogram copies so that lanes hitting
@@ -38,9 +39,8 @@ constexpr int SM_COPIES = 16;              // lane l counts into histogram copy 
 constexpr int SM_STRIDE = SM_BINS + 1;     // the pad puts the copies of one bin in different LDS banks
 constexpr int SAMPLE_MERGE_R = 8;                                // candidates per merge thread
 constexpr int SAMPLE_MERGE_MAX = SM_THREADS * SAMPLE_MERGE_R;    // candidates one row's merge holds
-constexpr int SW_R = 32;                                         // keys per lane of a wave slice
-constexpr int SW_CHUNK = 64 * SW_R;                              // logits per wave slice
-constexpr int SW_WAVES = 4;                                      // wave slices per workgroup
+constexpr int SW_WAVES = 4;                                      // wave slices per workgroup (16 or 32 keys a lane)
+constexpr int SM_TAU_SLICES = 256;                               // slice maxima the merge's bound takes
 constexpr int SB_R = 16;                                         // keys per thread of a block slice
 constexpr int SB_CHUNK = SM_THREADS * SB_R;                      // logits per block slice
 constexpr int SM_INDEX_BITS = 24;                                // indices below 2^24 (rows of at most 2^24)
@@ -339,28 +339,37 @@ __global__ __launch_bounds__(SM_THREADS) void sample_wide_kernel(const float* lo
   sm_finish(s_sorted, k, temperature, top_p, draw[row], token + row, F);
 }
 
-// wave slices, step 1: wave w of workgroup (row r, y) takes slice g = y * SW_WAVES + w and writes its top-k to
-// cand[r][g][0..k) in index order; the slots past the slice's length hold entries that sort last
+// wave slices, step 1: wave w of workgroup (row r, y) takes slice g = y * SW_WAVES + w (64 R logits, R a lane)
+// and writes its top-k to cand[r][g][0..k) in index order; the slots past the slice's length hold entries that
+// sort last
+template <int R>
 __global__ __launch_bounds__(64 * SW_WAVES) void sample_wave_slice_kernel(const float* logits, int64_t n,
                                                                           int32_t slices, int32_t k,
-                                                                          unsigned long long* cand) {
+                                                                          unsigned long long* cand, uint32_t* smax) {
+  constexpr int CHUNK = 64 * R;
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.y * SW_WAVES + (threadIdx.x >> 6);
   if (g >= slices) return;   // wave-uniform; the kernel has no barrier
   const int64_t row = blockIdx.x;
-  const int64_t lo = (int64_t)g * SW_CHUNK, len = min((int64_t)SW_CHUNK, n - lo);
+  const int64_t lo = (int64_t)g * CHUNK, len = min((int64_t)CHUNK, n - lo);
   const float* x = logits + row * n + lo;
   unsigned long long* out = cand + (row * slices + g) * (int64_t)k;
-  uint32_t key[SW_R];
-  sm_load_keys<SW_R, 64>(x, len, lane, key);
+  uint32_t key[R];
+  sm_load_keys<R, 64>(x, len, lane, key);
   const unsigned kl = (unsigned)min((int64_t)k, len);
   for (int64_t j = (int64_t)kl + lane; j < k; j += 64) out[j] = ~0ull;
+  uint32_t mx = 0u;   // the slice's largest key
+#pragma unroll
+  for (int j = 0; j < R; ++j) mx = max(mx, key[j]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  if (lane == 0) smax[row * slices + g] = mx;
   auto index_at = [&](int j) { return (uint32_t)(lo + (int64_t)j * 64 + lane); };
-  const GrpCut cut = grp_select<64, SW_R>(key, index_at, kl, nullptr);
+  const GrpCut cut = grp_select<64, R>(key, index_at, kl, nullptr);
   const unsigned long long below = (1ull << lane) - 1ull;
   unsigned slot = 0u;
 #pragma unroll
-  for (int j = 0; j < SW_R; ++j) {
+  for (int j = 0; j < R; ++j) {
     const bool keep = cut.keeps(key[j], index_at(j));
     const unsigned long long m = __ballot(keep);
     if (keep) out[slot + (unsigned)__popcll(m & below)] = sm_entry(key[j], index_at(j));
@@ -371,9 +380,11 @@ __global__ __launch_bounds__(64 * SW_WAVES) void sample_wave_slice_kernel(const 
 // block slices, step 1: workgroup (row r, slice g) writes its slice's top-k to cand[r][g][0..k) in any order;
 // the slots past the slice's length hold entries that sort last
 __global__ __launch_bounds__(SM_THREADS) void sample_block_slice_kernel(const float* logits, int64_t n,
-                                                                        int32_t k, unsigned long long* cand) {
+                                                                        int32_t k, unsigned long long* cand,
+                                                                        uint32_t* smax) {
   __shared__ unsigned s_red[2 * SM_WAVES];
   __shared__ unsigned s_n;
+  __shared__ uint32_t s_max;
   const int t = threadIdx.x;
   const int g = blockIdx.y, slices = gridDim.y;
   const int64_t row = blockIdx.x;
@@ -384,7 +395,19 @@ __global__ __launch_bounds__(SM_THREADS) void sample_block_slice_kernel(const fl
   sm_load_keys<SB_R, SM_THREADS>(x, len, t, key);
   const unsigned kl = (unsigned)min((int64_t)k, len);
   for (int64_t j = (int64_t)kl + t; j < k; j += SM_THREADS) out[j] = ~0ull;
-  if (t == 0) s_n = 0u;
+  if (t == 0) {
+    s_n = 0u;
+    s_max = 0u;
+  }
+  __syncthreads();
+  uint32_t mx = 0u;   // the slice's largest key
+#pragma unroll
+  for (int j = 0; j < SB_R; ++j) mx = max(mx, key[j]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  if ((t & 63) == 0) atomicMax(&s_max, mx);
+  __syncthreads();
+  if (t == 0) smax[row * slices + g] = s_max;
   auto index_at = [&](int j) { return (uint32_t)(lo + (int64_t)j * SM_THREADS + t); };
   const GrpCut cut = grp_select<SM_THREADS, SB_R>(key, index_at, kl, s_red);   // its barriers order s_n
 #pragma unroll
@@ -392,13 +415,19 @@ __global__ __launch_bounds__(SM_THREADS) void sample_block_slice_kernel(const fl
     if (cut.keeps(key[j], index_at(j))) out[atomicAdd(&s_n, 1u)] = sm_entry(key[j], index_at(j));
 }
 
-// step 2 of either slice form: one workgroup per row selects the top k of the n_cand candidates, ranks them
-// and draws
-__global__ __launch_bounds__(SM_THREADS) void sample_merge_kernel(const unsigned long long* cand, int32_t n_cand,
-                                                                  int32_t k, float temperature, float top_p,
-                                                                  const float* draw, int32_t* token) {
+// step 2 of either slice form: one workgroup per row selects the top k of the n_cand candidates (k per slice),
+// ranks them and draws.
+// With at least k slices, the k-th largest of the slices' maxima is a floor for the row's k-th largest key
+// (those k maxima are k distinct logits), so every survivor is among the candidates at or above it. When they
+// are few (1,024 at most, the usual case) each ranks itself against the others in LDS; otherwise the whole
+// candidate set goes through the bit-by-bit selection.
+__global__ __launch_bounds__(SM_THREADS) void sample_merge_kernel(const unsigned long long* cand,
+                                                                  const uint32_t* smax, int32_t n_cand, int32_t k,
+                                                                  float temperature, float top_p, const float* draw,
+                                                                  int32_t* token) {
   __shared__ unsigned s_red[2 * SM_WAVES];
   __shared__ unsigned s_n;
+  __shared__ uint32_t s_tau;
   __shared__ SmFinishLds F;
   __shared__ unsigned long long s_list[SAMPLE_MAX_K];
   __shared__ unsigned long long s_sorted[SAMPLE_MAX_K];
@@ -416,6 +445,42 @@ __global__ __launch_bounds__(SM_THREADS) void sample_merge_kernel(const unsigned
     e[j] = j * SM_THREADS + t < n_cand ? e[j] : ~0ull;
     key[j] = sm_entry_key(e[j]);   // the entries that sort last have key 0
   }
+  const int slices = n_cand / k;
+  if (slices >= k && slices <= SM_TAU_SLICES) {   // block-uniform
+    if (t == 0) s_n = 0u;
+    if (t < 64) {   // one wave: the k-th largest slice maximum, or a value with exactly k maxima at or above it
+      const uint32_t* sm = smax + row * slices;
+      uint32_t mk[SM_TAU_SLICES / 64];
+#pragma unroll
+      for (int r = 0; r < SM_TAU_SLICES / 64; ++r) mk[r] = r * 64 + t < slices ? sm[r * 64 + t] : 0u;
+      const GrpCut c = grp_select<64, SM_TAU_SLICES / 64>(mk, [&](int r) { return (uint32_t)(r * 64 + t); },
+                                                          (unsigned)k, nullptr);
+      if (t == 0) s_tau = c.iend == 0u ? c.key + 1u : c.key;
+    }
+    __syncthreads();
+    const uint32_t tau = s_tau;
+#pragma unroll
+    for (int j = 0; j < SAMPLE_MERGE_R; ++j) {
+      if (j * SM_THREADS + t < n_cand && key[j] >= tau) {
+        const unsigned slot = atomicAdd(&s_n, 1u);
+        if (slot < SAMPLE_MAX_K) s_list[slot] = e[j];
+      }
+    }
+    __syncthreads();
+    const unsigned m = s_n;
+    if (m <= (unsigned)SAMPLE_MAX_K) {
+      if (t < (int)m) {
+        const unsigned long long mine = s_list[t];
+        int r = 0;
+        for (unsigned i = 0; i < m; ++i) r += s_list[i] < mine ? 1 : 0;
+        if (r < k) s_sorted[r] = mine;
+      }
+      __syncthreads();
+      sm_finish(s_sorted, k, temperature, top_p, draw[row], token + row, F);
+      return;
+    }
+    __syncthreads();   // too many at the floor: the full selection below
+  }
   if (t == 0) s_n = 0u;
   auto index_at = [&](int j) { return (uint32_t)sm_entry_index(e[j]); };
   const GrpCut cut = grp_select<SM_THREADS, SAMPLE_MERGE_R>(key, index_at, (unsigned)k, s_red);
@@ -428,16 +493,20 @@ __global__ __launch_bounds__(SM_THREADS) void sample_merge_kernel(const unsigned
 }
 
 SamplePlan sample_plan(int64_t n, int32_t k) {
-  const int64_t gw = (n + SW_CHUNK - 1) / SW_CHUNK;
-  if (gw > 1 && gw * k <= SAMPLE_MERGE_MAX) return {SAMPLE_WAVE_SLICES, (int)gw, SW_CHUNK};
+  for (int64_t chunk : {64 * 16, 64 * 32}) {   // wave slices: 16, else 32 keys a lane
+    const int64_t gw = (n + chunk - 1) / chunk;
+    if (gw > 1 && gw * k <= SAMPLE_MERGE_MAX) return {SAMPLE_WAVE_SLICES, (int)gw, chunk};
+  }
   const int64_t gb = (n + SB_CHUNK - 1) / SB_CHUNK;
   if (gb > 1 && gb * k <= SAMPLE_MERGE_MAX) return {SAMPLE_BLOCK_SLICES, (int)gb, SB_CHUNK};
   return {SAMPLE_WIDE, 1, n};
 }
 
+// workspace of the slice forms: the candidates [rows][slices][k], then the slice maxima [rows][slices]
 int64_t sample_workspace_bytes(int64_t rows, int64_t n, int32_t k) {
   const SamplePlan p = sample_plan(n, k);
-  return p.form == SAMPLE_WIDE ? 0 : rows * p.slices * (int64_t)k * (int64_t)sizeof(unsigned long long);
+  if (p.form == SAMPLE_WIDE) return 0;
+  return rows * p.slices * ((int64_t)k * (int64_t)sizeof(unsigned long long) + (int64_t)sizeof(uint32_t));
 }
 
 hipError_t sample_launch(const float* logits, int64_t rows, int64_t n, float temperature, int32_t k, float top_p,
@@ -449,16 +518,22 @@ hipError_t sample_launch(const float* logits, int64_t rows, int64_t n, float tem
     return hipGetLastError();
   }
   auto* cand = static_cast<unsigned long long*>(ws);
+  uint32_t* smax = reinterpret_cast<uint32_t*>(cand + rows * p.slices * (int64_t)k);
   if (p.form == SAMPLE_WAVE_SLICES) {
-    hipLaunchKernelGGL(sample_wave_slice_kernel, dim3((unsigned)rows, (unsigned)((p.slices + SW_WAVES - 1) / SW_WAVES)),
-                       dim3(64 * SW_WAVES), 0, s, logits, n, (int32_t)p.slices, k, cand);
+    const dim3 grid((unsigned)rows, (unsigned)((p.slices + SW_WAVES - 1) / SW_WAVES));
+    if (p.chunk == 64 * 16)
+      hipLaunchKernelGGL(sample_wave_slice_kernel<16>, grid, dim3(64 * SW_WAVES), 0, s, logits, n, (int32_t)p.slices,
+                         k, cand, smax);
+    else
+      hipLaunchKernelGGL(sample_wave_slice_kernel<32>, grid, dim3(64 * SW_WAVES), 0, s, logits, n, (int32_t)p.slices,
+                         k, cand, smax);
   } else {
     hipLaunchKernelGGL(sample_block_slice_kernel, dim3((unsigned)rows, (unsigned)p.slices), dim3(SM_THREADS), 0, s,
-                       logits, n, k, cand);
+                       logits, n, k, cand, smax);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sample_merge_kernel, dim3((unsigned)rows), dim3(SM_THREADS), 0, s, cand,
+  hipLaunchKernelGGL(sample_merge_kernel, dim3((unsigned)rows), dim3(SM_THREADS), 0, s, cand, smax,
                      (int32_t)(p.slices * k), k, temperature, top_p, draw, token);
   return hipGetLastError();
 }

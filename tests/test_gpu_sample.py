@@ -96,15 +96,16 @@ def test_batch_of_64_vocab_rows():
     assert check_rows(logits, 0.9, 50, 0.95, u, "batch64") >= 63
 
 
-@pytest.mark.parametrize("k", [50, 300])
-def test_draw_sweep_recovers_the_survivor_order(k):
+@pytest.mark.parametrize("k,n_ties", [(50, 3000), (50, 300), (300, 3000)])
+def test_draw_sweep_recovers_the_survivor_order(k, n_ties):
     # one row repeated with draws at the middle of each survivor's interval: every survivor is hit once,
     # so the tokens spell the survivor order (values, then the lower index among ties); k 50 takes the
-    # wave slices, 300 the block slices
+    # wave slices (300 ties: few enough candidates above the slice-maximum floor to rank directly; 3000: the
+    # full selection), 300 the block slices
     row = synth.normal((V,), 520, 0, 3.0)
     order = np.lexsort((np.arange(V), -row.astype(np.float64)))
     cut = float(row[order[30]])
-    row[synth.ints((3000,), 0, V - 1, 521, 0)] = cut        # ties at the cut, many more than survive
+    row[synth.ints((n_ties,), 0, V - 1, 521, 0)] = cut      # ties at the cut, more than survive
     d = sample_detail(row, 1.0, k, 1.0, 0.0)
     mids = np.concatenate(([0.0], d["cdf"][:-1])) + np.diff(np.concatenate(([0.0], d["cdf"]))) / 2
     u = mids.astype(np.float32)

@@ -194,17 +194,20 @@ def test_sample_refusals():
 
 
 def test_sample_workspace_sizes():
-    # G * k candidates of 8 bytes per row: wave slices of 2,048 logits while G * k <= 8,192, else block
-    # slices of 16,384 logits under the same bound, else the one-workgroup form with no workspace
+    # G * k candidates of 8 bytes and G slice maxima of 4 bytes per row: wave slices of 1,024 logits while
+    # G * k <= 8,192, else of 2,048, else block slices of 16,384 under the same bound, else the one-workgroup
+    # form with no workspace
     ws = llmk.sample_workspace_bytes
-    assert ws(1, 128256, 1.0, 50) == 63 * 50 * 8           # 63 wave slices
-    assert ws(1, 128256, 1.0, 130) == 63 * 130 * 8
-    assert ws(2, 128256, 1.0, 131) == 2 * 8 * 131 * 8      # 63 * 131 > 8192: 8 block slices
-    assert ws(3, 128256, 0.7, 1024) == 3 * 8 * 1024 * 8
-    assert ws(1, 128256, 0.0, 0) == 63 * 1 * 8             # greedy keeps one survivor
-    assert ws(1, 5000, 1.0, 1000) == 3 * 1000 * 8
+    assert ws(1, 128256, 1.0, 50) == 126 * (50 * 8 + 4)          # 126 wave slices of 1,024
+    assert ws(1, 128256, 1.0, 65) == 126 * (65 * 8 + 4)
+    assert ws(1, 128256, 1.0, 130) == 63 * (130 * 8 + 4)         # 126 * 130 > 8192: 63 slices of 2,048
+    assert ws(2, 128256, 1.0, 131) == 2 * 8 * (131 * 8 + 4)      # 63 * 131 > 8192: 8 block slices
+    assert ws(3, 128256, 0.7, 1024) == 3 * 8 * (1024 * 8 + 4)
+    assert ws(1, 128256, 0.0, 0) == 126 * (1 * 8 + 4)            # greedy keeps one survivor
+    assert ws(1, 5000, 1.0, 1000) == 5 * (1000 * 8 + 4)
     assert ws(1, 151936, 1.0, 1024) == 0                   # 10 block slices * 1024 > 8192: one workgroup
-    assert ws(1, 2048, 1.0, 3) == 0                        # one slice: one workgroup
+    assert ws(1, 2048, 1.0, 3) == 2 * (3 * 8 + 4)
+    assert ws(1, 1024, 1.0, 3) == 0                        # one slice: one workgroup
     assert ws(0, 7, 1.0, 3) == -561 and ws(1, 5000, 1.0, 0) == -564
 
 
