@@ -359,6 +359,23 @@ __global__ void set_batch_state_kernel(BatchState* st, const BatchInit init) {
   }
 }
 
+__global__ void batch_advance_kernel(BatchState* st, const int32_t* tok, int32_t* token_out, int32_t rows) {
+  const int step = st->step;
+  for (int b = threadIdx.x; b < rows; b += blockDim.x) {
+    const int32_t t = tok[b];
+    token_out[(int64_t)step * rows + b] = t;
+    st->token[b] = t;
+    st->pos[b] = st->pos[b] + 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) st->step = step + 1;
+}
+
+hipError_t batch_advance_launch(BatchState* st, const int32_t* tok, int32_t* token_out, int32_t rows, hipStream_t s) {
+  hipLaunchKernelGGL(batch_advance_kernel, dim3(1), dim3(64), 0, s, st, tok, token_out, rows);
+  return hipGetLastError();
+}
+
 hipError_t set_batch_state_launch(BatchState* st, const BatchInit& init, hipStream_t s) {
   hipLaunchKernelGGL(set_batch_state_kernel, dim3(1), dim3(LLMK_MAX_BATCH_ROWS), 0, s, st, init);
   return hipGetLastError();

@@ -208,6 +208,9 @@ struct BatchInit {
   int32_t rows;
 };
 hipError_t set_batch_state_launch(BatchState* st, const BatchInit& init, hipStream_t s);
+// After the batched head: row b's greedy token tok[b] goes to token_out[step * rows + b] and becomes the row's
+// next input, its position advances, and the step count too.
+hipError_t batch_advance_launch(BatchState* st, const int32_t* tok, int32_t* token_out, int32_t rows, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------
 // Split-context grouped-query attention for one query position, plus the log-sum-exp merge.
