@@ -619,12 +619,12 @@ int32_t decode_checks(const llmk_config* cfg, const llmk_model* model, const llm
 
 // ---- batched decode ------------------------------------------------------------------------------------
 
-constexpr int kBatchTargetBlocks = 256;   // the matrix-core kernels hold one workgroup per CU
+constexpr int kBatchTargetBlocks = 256;   // workgroups a row GEMM aims for (K is split up to that)
 constexpr int kBatchAttnTilesPerPart = 10;
 
 struct BatchPlan {
   int64_t B = 0;
-  BgemmParams qkv{}, o{}, gu{}, down{}, head{};
+  int64_t qkv_n = 0;                    // q|k|v row length (H + 2 Hkv) hd
   AttnParams attn{};
   BatchState* state = nullptr;
   float* x = nullptr;                   // [B][d] residual stream
@@ -635,13 +635,9 @@ struct BatchPlan {
   bf16_t* att_lo = nullptr;
   bf16_t* u_hi = nullptr;               // [B][F]
   bf16_t* u_lo = nullptr;
-  float* partial = nullptr;
-  unsigned* counters = nullptr;         // gemm counters, then B * Hkv attention counters
+  unsigned* counters = nullptr;         // B * Hkv attention tickets, then B head-argmax tickets
   float* attn_part = nullptr;
-  float* head_val = nullptr;
-  int32_t* head_idx = nullptr;
   int32_t* tok_scratch = nullptr;       // kTimeMaxReps * B tokens: repeated timing launches of the head
-  int64_t n_gemm_counters = 0;
   int64_t bytes = 0;
   bool prefill = false;                 // rows of one chunk: K/V appended for all rows before any attends
   // the decode batch's q|k|v, o, gate|up and down as tiled matrix-core GEMMs (their split partials in py)
@@ -661,22 +657,7 @@ bool batch_config_ok(const llmk_config* c) { return c->w_dtype == LLMK_BF16 && c
 void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P, bool row_gemms = true) {
   const int64_t d = c->d, qd = c->n_head * c->head_dim, kvd = c->n_kv * c->head_dim, F = c->hidden;
   P.B = B;
-  BgemmParams* gs[5] = {&P.qkv, &P.o, &P.gu, &P.down, &P.head};
-  const int modes[5] = {BG_QKV, BG_RESID, BG_GATEUP, BG_RESID, BG_HEAD};
-  const int64_t Ns[5] = {qd + 2 * kvd, d, F, d, c->vocab};
-  const int64_t Ks[5] = {d, qd, d, F, d};
-  int64_t part = 0, ncnt = 0;
-  for (int i = 0; i < 5; ++i) {
-    gs[i]->N = Ns[i];
-    gs[i]->K = Ks[i];
-    gs[i]->B = (int32_t)B;
-    bgemm_plan(*gs[i], modes[i], kBatchTargetBlocks);
-    part = std::max(part, bgemm_partial_floats(*gs[i]));
-    ncnt = std::max(ncnt, (int64_t)gs[i]->n_rblk + 1);
-  }
-  P.qkv.n0 = qd;
-  P.qkv.n1 = kvd;
-  P.n_gemm_counters = ncnt;
+  P.qkv_n = qd + 2 * kvd;
   P.attn.H = (int32_t)c->n_head;
   P.attn.Hkv = (int32_t)c->n_kv;
   P.attn.hd = (int32_t)c->head_dim;
@@ -696,11 +677,8 @@ void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P, bool ro
   P.att_lo = cv.take<bf16_t>(B * qd);
   P.u_hi = cv.take<bf16_t>(B * F);
   P.u_lo = cv.take<bf16_t>(B * F);
-  P.partial = cv.take<float>(part > 0 ? part : 1);
-  P.counters = cv.take<unsigned>(ncnt + B * c->n_kv + B);   // gemm, attention and head-argmax tickets
+  P.counters = cv.take<unsigned>(B * c->n_kv + B);
   P.attn_part = cv.take<float>(B * (int64_t)P.attn.n_parts * c->n_head * (c->head_dim + 2));
-  P.head_val = cv.take<float>(B * (int64_t)P.head.n_rblk);
-  P.head_idx = cv.take<int32_t>(B * (int64_t)P.head.n_rblk);
   P.tok_scratch = cv.take<int32_t>(kTimeMaxReps * B);
   if (row_gemms) {
     // the same tiled GEMM as prefill: with 64 rows it re-reads the activations from L2 less than the skinny
@@ -736,13 +714,13 @@ void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P, bool ro
     P.hbpr = c->vocab >= 65536 ? 64 : (int32_t)((c->vocab + 1023) / 1024);
     P.hval = cv.take<float>(B * P.hbpr);
     P.hidx = cv.take<int32_t>(B * P.hbpr);
-    P.hcnt = P.counters ? P.counters + ncnt + B * c->n_kv : nullptr;
+    P.hcnt = P.counters ? P.counters + B * c->n_kv : nullptr;
   }
   P.bytes = cv.off;
 }
 
 int64_t batch_counters_total(const llmk_config* c, const BatchPlan& P) {
-  return P.n_gemm_counters + P.B * c->n_kv + P.B;
+  return P.B * c->n_kv + P.B;
 }
 
 // The kernels of one batched step, in order: per layer BK_NORM1, BK_QKV, BK_ATTN, BK_O, BK_NORM2, BK_GATEUP,
@@ -777,7 +755,7 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       AttnParams a = P.attn;
       a.q = nullptr;
       a.qkv_raw = P.qkv_buf;
-      a.qkv_stride = P.qkv.N;
+      a.qkv_stride = P.qkv_n;
       a.k = pool->k[l];
       a.v = pool->v[l];
       a.k_w = pool->k[l];
@@ -788,13 +766,13 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       a.state = nullptr;
       a.bstate = P.state;
       a.part = P.attn_part;
-      a.counters = P.counters + P.n_gemm_counters;
+      a.counters = P.counters;
       a.out = nullptr;
       a.out_hi = P.att_hi;
       a.out_lo = P.att_lo;
       a.no_append = P.prefill ? 1 : 0;
       if (P.prefill) {
-        hipError_t e = rope_append_rows_launch(P.qkv_buf, P.qkv.N, P.state, B, a.H, a.Hkv, a.hd, a.rope_table,
+        hipError_t e = rope_append_rows_launch(P.qkv_buf, P.qkv_n, P.state, B, a.H, a.Hkv, a.hd, a.rope_table,
                                                a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, s);
         if (e != hipSuccess) return e;
       }
@@ -840,29 +818,16 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       return bnorm_launch(P.x, nullptr, 1, P.state, B, d, static_cast<const float*>(m->g_final.ptr), eps, P.h_hi,
                           P.h_lo, s);
     case BK_HEAD: {  // logits = W_out h; greedy token per row; state advances
-      if (P.py) {
-        PgemmParams g = P.phead;
-        g.ahi = P.h_hi;
-        g.alo = P.h_lo;
-        g.w0 = m->w_out.ptr;
-        g.y = logits ? logits : P.hlogits;
-        hipError_t e = pgemm_launch(g, PG_NONE, s);
-        if (e == hipSuccess)
-          e = argmax_launch(g.y, B, c->vocab, P.htok, nullptr, P.hval, P.hidx, P.hcnt, P.hbpr, s);
-        if (e == hipSuccess) e = batch_advance_launch(P.state, P.htok, tokens_out, B, s);
-        return e;
-      }
-      BgemmParams h = P.head;
-      h.w0 = m->w_out.ptr;
-      h.xhi = P.h_hi;
-      h.xlo = P.h_lo;
-      h.counters = P.counters;
-      h.y = logits;
-      h.part_val = P.head_val;
-      h.part_idx = P.head_idx;
-      h.token_out = tokens_out;
-      h.state = P.state;
-      return bgemm_launch(h, BG_HEAD, s);
+      if (!P.py) return hipErrorInvalidValue;   // planned without the row GEMMs (prefill has its own head)
+      PgemmParams g = P.phead;
+      g.ahi = P.h_hi;
+      g.alo = P.h_lo;
+      g.w0 = m->w_out.ptr;
+      g.y = logits ? logits : P.hlogits;
+      hipError_t e = pgemm_launch(g, PG_NONE, s);
+      if (e == hipSuccess) e = argmax_launch(g.y, B, c->vocab, P.htok, nullptr, P.hval, P.hidx, P.hcnt, P.hbpr, s);
+      if (e == hipSuccess) e = batch_advance_launch(P.state, P.htok, tokens_out, B, s);
+      return e;
     }
   }
   return hipErrorInvalidValue;

@@ -164,39 +164,6 @@ bool fattn_supported(int64_t H, int64_t Hkv, int64_t hd);
 int64_t fattn_parts(int64_t max_ctx);
 hipError_t fattn_launch(const FattnParams& p, int64_t max_ctx, hipStream_t s);
 
-enum BgemmMode { BG_PLAIN = 0, BG_QKV = 1, BG_RESID = 2, BG_GATEUP = 3, BG_HEAD = 4 };
-
-struct BgemmParams {
-  const void* w0;          // PLAIN/RESID/HEAD: the matrix; QKV: wq; GATEUP: gate
-  const void* w1;          // QKV: wk; GATEUP: up
-  const void* w2;          // QKV: wv
-  int64_t n0, n1;          // QKV: rows of wq and wk
-  int64_t N, K;            // outputs (GATEUP: columns of u), input length
-  int32_t B;               // batch rows, 1..64
-  int32_t n_rblk;          // row blocks (64 weight rows each; GATEUP 32 gate + 32 up)
-  int32_t ksplit;          // K slices; grid = n_rblk * ksplit
-  int32_t pad0;
-  int64_t kslice;          // K per slice (multiple of 128)
-  const bf16_t* xhi;       // [64][K]
-  const bf16_t* xlo;
-  float* partial;          // ksplit > 1: [ksplit][64][n_rblk * 64]
-  unsigned* counters;      // [n_rblk] (HEAD: one more), zero on entry and exit
-  float* y;                // PLAIN/QKV: [B][N]; HEAD: optional logits [B][N]
-  float* x;                // RESID: x[b][n] += y
-  float* hidden;           // RESID: optional copy of the new x, row b at hidden + b * hidden_stride
-  int64_t hidden_stride;
-  bf16_t* uhi;             // GATEUP: u = silu(gate) * up, split, [64][N]
-  bf16_t* ulo;
-  float* part_val;         // HEAD: [64][n_rblk] per-block best
-  int32_t* part_idx;
-  int32_t* token_out;      // HEAD: token of row b at token_out[state->step * B + b]
-  BatchState* state;       // HEAD: token[b] <- argmax, pos[b] += 1, step += 1
-};
-
-// Fills n_rblk / ksplit / kslice (N, K, B set) for about target_blocks workgroups.
-void bgemm_plan(BgemmParams& p, int mode, int target_blocks);
-int64_t bgemm_partial_floats(const BgemmParams& p);
-hipError_t bgemm_launch(const BgemmParams& p, int mode, hipStream_t s);
 // h[b] = rmsnorm(x[b]) * gain split into hi/lo, for rows b < rows; with emb, x[b] is first set to the
 // embedding row of state->token[b] (the first layer).
 hipError_t bnorm_launch(float* x, const void* emb, int emb_is_bf16, const BatchState* state, int32_t rows, int64_t d,
