@@ -195,6 +195,48 @@ __global__ void pgemm_epilogue_kernel(const PgemmParams p, int mode) {
   }
 }
 
+// The same, four columns per thread: grid (column blocks of 1,024, rows); needs the column count, the row
+// strides and every buffer to allow 16-byte accesses (8-byte for the hi/lo outputs).
+__global__ __launch_bounds__(256) void pgemm_epilogue4_kernel(const PgemmParams p, int mode) {
+  const int64_t cols = mode == PG_GATEUP ? p.N / 2 : p.N;
+  const int64_t m = blockIdx.y;
+  const int64_t n = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (n >= cols) return;
+  auto sum4 = [&](int64_t c) {
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int z = 0; z < p.ksplit; ++z) {
+      const float4 y = *reinterpret_cast<const float4*>(p.y + ((int64_t)z * p.M + m) * p.N + c);
+      v.x += y.x;
+      v.y += y.y;
+      v.z += y.z;
+      v.w += y.w;
+    }
+    return v;
+  };
+  if (mode == PG_STORE) {
+    *reinterpret_cast<float4*>(p.out + m * p.ldo + n) = sum4(n);
+  } else if (mode == PG_RESID) {
+    const float4 y = sum4(n);
+    float4 x = *reinterpret_cast<const float4*>(p.out + m * p.ldo + n);
+    x.x += y.x;
+    x.y += y.y;
+    x.z += y.z;
+    x.w += y.w;
+    *reinterpret_cast<float4*>(p.out + m * p.ldo + n) = x;
+    if (p.hidden) *reinterpret_cast<float4*>(p.hidden + m * p.hidden_stride + n) = x;
+  } else {   // PG_GATEUP
+    const float4 g = sum4(n), u = sum4(n + cols);
+    const float e[4] = {silu_f(g.x) * u.x, silu_f(g.y) * u.y, silu_f(g.z) * u.z, silu_f(g.w) * u.w};
+    bf16_t h[4], l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) split_bf16(e[k], h[k], l[k]);
+    *reinterpret_cast<uint2*>(p.uhi + m * cols + n) =
+        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+    *reinterpret_cast<uint2*>(p.ulo + m * cols + n) =
+        make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+  }
+}
+
 void pgemm_plan(PgemmParams& p, int target_blocks) {
   const int64_t tiles = ((p.N + PG_BN - 1) / PG_BN) * ((p.M + PG_BM - 1) / PG_BM);
   int64_t ks = (target_blocks + tiles - 1) / tiles;
@@ -211,7 +253,18 @@ hipError_t pgemm_launch(const PgemmParams& p, int mode, hipStream_t s) {
   hipLaunchKernelGGL(pgemm_kernel, grid, dim3(PG_THREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mode == PG_NONE) return e;
-  const int64_t total = (int64_t)p.M * (mode == PG_GATEUP ? p.N / 2 : p.N);
+  const int64_t cols = mode == PG_GATEUP ? p.N / 2 : p.N;
+  auto al = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; };
+  const bool vec = cols % 4 == 0 && p.N % 4 == 0 && al(p.y, 16) && p.M <= 65535 &&
+                   (mode == PG_GATEUP ? al(p.uhi, 8) && al(p.ulo, 8)
+                                      : p.ldo % 4 == 0 && al(p.out, 16) &&
+                                            (!p.hidden || (al(p.hidden, 16) && p.hidden_stride % 4 == 0)));
+  if (vec) {
+    const dim3 grid((unsigned)((cols + 1023) / 1024), (unsigned)p.M);
+    hipLaunchKernelGGL(pgemm_epilogue4_kernel, grid, dim3(256), 0, s, p, mode);
+    return hipGetLastError();
+  }
+  const int64_t total = (int64_t)p.M * cols;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(pgemm_epilogue_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, mode);
   return hipGetLastError();
