@@ -895,7 +895,7 @@ void plan_prefill(const llmk_config* c, int64_t M, void* ws, PrefillPlan& P) {
   P.am_cnt = cv.take<unsigned>(M);
   P.am_logit = cv.take<float>(M);
   P.hidden = cv.take<float>(M * c->n_layer * d);
-  if (fattn_supported(c->n_head, c->n_kv, c->head_dim)) {
+  if (fattn_supported(c->n_head, c->n_kv, c->head_dim, c->max_seq)) {
     P.fa_parts = (int32_t)fattn_parts(c->max_seq);
     P.fa_part = cv.take<float>(M * c->n_head * P.fa_parts * (c->head_dim + 2));
   }

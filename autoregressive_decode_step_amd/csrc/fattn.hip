@@ -293,19 +293,38 @@ __global__ __launch_bounds__(FA_THREADS) void fattn_kernel(const FattnParams p) 
   }
 }
 
-// combine the parts 0 .. pos / span of (row, head) with weights exp(m_p - m) and write hi + lo
+// combine the parts 0 .. pos / span of (row, head) with their log-sum-exp weights, in part order, eight parts'
+// records loaded at a time (a running maximum rescales what is summed so far), and write hi + lo
+constexpr int FA_MERGE_PARTS = 32;   // parts a merge takes (contexts up to 8,192 positions)
+constexpr int FA_MERGE_GROUP = 8;
 __global__ __launch_bounds__(FA_HD) void fattn_merge_kernel(const FattnParams p) {
   const int row = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
   const int np = p.st->pos[row] / p.span + 1;
   const float* rec = p.part + ((int64_t)row * p.H + h) * p.n_parts * (FA_HD + 2);
-  float m = -INFINITY;
-  for (int q = 0; q < np; ++q) m = fmaxf(m, rec[q * (FA_HD + 2) + FA_HD]);
-  float L = 0.0f, acc = 0.0f;
-  for (int q = 0; q < np; ++q) {
-    const float mq = rec[q * (FA_HD + 2) + FA_HD];
-    const float w = mq == -INFINITY ? 0.0f : expf(mq - m);
-    L += w * rec[q * (FA_HD + 2) + FA_HD + 1];
-    acc += w * rec[q * (FA_HD + 2) + i];
+  float m = -INFINITY, L = 0.0f, acc = 0.0f;
+  for (int q0 = 0; q0 < np; q0 += FA_MERGE_GROUP) {
+    float mq[FA_MERGE_GROUP], lq[FA_MERGE_GROUP], oq[FA_MERGE_GROUP];
+#pragma unroll
+    for (int j = 0; j < FA_MERGE_GROUP; ++j) {   // parts past np read part q0 again and weigh nothing
+      const float* r = rec + (q0 + j < np ? q0 + j : q0) * (FA_HD + 2);
+      mq[j] = r[FA_HD];
+      lq[j] = r[FA_HD + 1];
+      oq[j] = r[i];
+    }
+    float mg = m;
+#pragma unroll
+    for (int j = 0; j < FA_MERGE_GROUP; ++j)
+      if (q0 + j < np) mg = fmaxf(mg, mq[j]);
+    const float sc = m == -INFINITY ? 0.0f : expf(m - mg);
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < FA_MERGE_GROUP; ++j) {
+      const float w = (q0 + j >= np || mq[j] == -INFINITY) ? 0.0f : expf(mq[j] - mg);
+      L += w * lq[j];
+      acc += w * oq[j];
+    }
+    m = mg;
   }
   bf16_t hi, lo;
   split_bf16(acc / L, hi, lo);
@@ -314,14 +333,14 @@ __global__ __launch_bounds__(FA_HD) void fattn_merge_kernel(const FattnParams p)
   p.out_lo[off] = lo;
 }
 
-bool fattn_supported(int64_t H, int64_t Hkv, int64_t hd) {
-  return hd == FA_HD && H % Hkv == 0 && FA_QV % (H / Hkv) == 0;
-}
-
 int64_t fattn_parts(int64_t max_ctx) { return (max_ctx + FA_SPAN - 1) / FA_SPAN; }
 
+bool fattn_supported(int64_t H, int64_t Hkv, int64_t hd, int64_t max_ctx) {
+  return hd == FA_HD && H % Hkv == 0 && FA_QV % (H / Hkv) == 0 && fattn_parts(max_ctx) <= FA_MERGE_PARTS;
+}
+
 hipError_t fattn_launch(const FattnParams& p, int64_t max_ctx, hipStream_t s) {
-  if (!fattn_supported(p.H, p.Hkv, FA_HD) || p.span != FA_SPAN || fattn_parts(max_ctx) > p.n_parts)
+  if (!fattn_supported(p.H, p.Hkv, FA_HD, max_ctx) || p.span != FA_SPAN || fattn_parts(max_ctx) > p.n_parts)
     return hipErrorInvalidValue;
   const int G = p.H / p.Hkv, QR = FA_QV / G;
   const dim3 grid((unsigned)fattn_parts(max_ctx), (unsigned)((p.rows + QR - 1) / QR), (unsigned)p.Hkv);

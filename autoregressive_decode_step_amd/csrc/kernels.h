@@ -160,7 +160,8 @@ struct FattnParams {
   bf16_t* out_hi;              // [rows][H * hd]
   bf16_t* out_lo;
 };
-bool fattn_supported(int64_t H, int64_t Hkv, int64_t hd);
+// the chunk attention takes head dim 128, at most 64 query heads per K/V head and contexts up to 8,192 positions
+bool fattn_supported(int64_t H, int64_t Hkv, int64_t hd, int64_t max_ctx);
 int64_t fattn_parts(int64_t max_ctx);
 hipError_t fattn_launch(const FattnParams& p, int64_t max_ctx, hipStream_t s);
 
