@@ -620,7 +620,7 @@ int32_t decode_checks(const llmk_config* cfg, const llmk_model* model, const llm
 // ---- batched decode ------------------------------------------------------------------------------------
 
 constexpr int kBatchTargetBlocks = 256;   // workgroups a row GEMM aims for (K is split up to that)
-constexpr int kBatchAttnTilesPerPart = 10;
+constexpr int kBatchAttnTilesPerPart = 16;
 
 struct BatchPlan {
   int64_t B = 0;
@@ -662,8 +662,9 @@ void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P, bool ro
   P.attn.Hkv = (int32_t)c->n_kv;
   P.attn.hd = (int32_t)c->head_dim;
   P.attn.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
-  // every row of the batch brings its own (row, K/V head) pairs, so parts can be long: about 10 tiles each
-  // (measured on the 64-row, 8,320-position pool: 258 us per layer against 312 us at the batch-1 split)
+  // every row of the batch brings its own (row, K/V head) pairs, so parts can be long: about 16 tiles each
+  // (measured on the 64-row, 8,320-position pool, us per layer: 312 at the batch-1 split, 299 at 6 tiles, 261
+  // at 10, 235 at 16, 261 at 24, 357 at 40)
   attn_plan(P.attn, c->max_seq, kBatchAttnTilesPerPart);
   P.attn.rows = (int32_t)B;
 
