@@ -290,10 +290,36 @@ def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head):
     return OK, slot * plane + pos * n_kv * head_dim + kv_head * head_dim
 
 
+Q8_GROUP = 128
+
+
+def q8_pack_bytes(rows, cols):
+    """llmk_q8_pack_bytes: bytes of an int8 weight pack, or -1."""
+    if rows < 1 or cols < 1 or rows > MAX_DIM or cols > MAX_DIM or cols % Q8_GROUP:
+        return -1
+    return rows * cols + 4 * rows * (cols // Q8_GROUP)
+
+
+def quantize_q8(w=True, len_w=0, w_dtype=0, rows=0, cols=0, pack=True, len_pack=0):
+    """Expected status of llmk_quantize_q8."""
+    if not (w and pack) or w_dtype not in (0, 1):
+        return INVALID
+    c = _dims(rows, cols)
+    if c != OK:
+        return c
+    if cols % Q8_GROUP:
+        return HEAD_SHAPE
+    if len_w != rows * cols:
+        return WEIGHT_LEN
+    if len_pack != q8_pack_bytes(rows, cols):
+        return OUTPUT_LEN
+    return OK
+
+
 def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4, rope_layout=0,
                  w_dtype=0, kv_dtype=0, w_layout=0, step_path=0):
     import math
-    if rope_layout not in (0, 1) or w_dtype not in (0, 1) or kv_dtype not in (0, 1) or w_layout not in (0, 1):
+    if rope_layout not in (0, 1) or w_dtype not in (0, 1, 2) or kv_dtype not in (0, 1) or w_layout not in (0, 1):
         return INVALID
     if step_path not in (0, 1, 2):
         return INVALID
@@ -304,6 +330,16 @@ def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps
         return c
     if not _attn_shape_ok(n_head, n_kv, head_dim):
         return HEAD_SHAPE
+    if w_dtype == 2:
+        # int8 packs: projection inputs in whole groups of 128, at most 4 loads of 16 codes x 64 lanes per wave
+        # over the widest split that leaves a wave 1,024 codes or more
+        for k in (d, n_head * head_dim, hidden):
+            kw = 4 if k // 4 >= 1024 else 2 if k // 2 >= 1024 else 1
+            if k % Q8_GROUP or -(-(k // kw) // 1024) > 4:
+                return HEAD_SHAPE
+        if w_layout != 1 or step_path == 2:
+            return INVALID
+        return OK
     vec = 4 if w_dtype == 0 else 8
     for width in (d, n_head * head_dim, n_kv * head_dim, hidden):
         if width % vec != 0:
