@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libllmk.so")
 LIB_PATH = os.environ.get("LLMK_LIBRARY") or LIB_PATH
 
 OK = 560
-F32, BF16 = 0, 1
+F32, BF16, Q8 = 0, 1, 2
+Q8_GROUP = 128
 ROPE_HALF_SPLIT, ROPE_INTERLEAVED = 0, 1
 W_IN_OUT, W_OUT_IN = 0, 1
 STEP_AUTO, STEP_PER_OP, STEP_PERSISTENT = 0, 1, 2
@@ -102,6 +103,8 @@ _SIGS = {
     "llmk_decode_kernel_count": ([ctypes.POINTER(Config)], _i64),
     "llmk_decode_path": ([ctypes.POINTER(Config)], _i32),
     "llmk_transpose": ([_p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
+    "llmk_q8_pack_bytes": ([_i64, _i64], _i64),
+    "llmk_quantize_q8": ([_p, _i64, _i32, _i64, _i64, _p, _i64, _p], _i32),
     "llmk_decode_step_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                    _i64, _i64, _i64, _p, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
     "llmk_decode_step_batch": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64,
@@ -273,6 +276,17 @@ def make_config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=
                 rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16, w_layout=W_IN_OUT, step_path=0) -> Config:
     return Config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps, rope_base, rope_layout, w_dtype,
                   kv_dtype, w_layout, step_path)
+
+
+def q8_pack_bytes(rows, cols) -> int:
+    """Bytes of an int8 weight pack of a rows x cols (output-major) matrix; -1 if the shape is refused."""
+    return lib.llmk_q8_pack_bytes(rows, cols)
+
+
+def quantize_q8(w, rows, cols, pack, stream=None) -> int:
+    """Quantize w (fp32 or bf16 tensor, rows x cols, output-major) into pack (uint8 tensor of
+    q8_pack_bytes(rows, cols) bytes)."""
+    return lib.llmk_quantize_q8(_ptr(w), _len(w), _dtype_code(w), rows, cols, _ptr(pack), _len(pack), _stream(stream))
 
 
 def transpose(src, dst, rows, cols, stream=None) -> int:

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "q8.h"
 #include "llmk.h"
 
 using namespace llmk;
@@ -92,7 +93,7 @@ int64_t gemv_t_ws_any(int64_t m, int64_t n, int32_t dt) {
 
 int32_t config_check(const llmk_config* c) {
   if (!c) return LLMK_INVALID_ARGUMENT;
-  if (!is_dtype(c->w_dtype) || !is_dtype(c->kv_dtype)) return LLMK_INVALID_ARGUMENT;
+  if ((!is_dtype(c->w_dtype) && c->w_dtype != LLMK_Q8) || !is_dtype(c->kv_dtype)) return LLMK_INVALID_ARGUMENT;
   if (c->rope_layout != LLMK_ROPE_HALF_SPLIT && c->rope_layout != LLMK_ROPE_INTERLEAVED) return LLMK_INVALID_ARGUMENT;
   if (c->w_layout != LLMK_W_IN_OUT && c->w_layout != LLMK_W_OUT_IN) return LLMK_INVALID_ARGUMENT;
   if (c->step_path != LLMK_STEP_AUTO && c->step_path != LLMK_STEP_PER_OP && c->step_path != LLMK_STEP_PERSISTENT)
@@ -103,6 +104,18 @@ int32_t config_check(const llmk_config* c) {
   if (st != LLMK_OK) return st;
   if (c->n_head % c->n_kv != 0 || c->n_head / c->n_kv > 8 || !attn_head_dim_ok(c->head_dim))
     return LLMK_HEAD_SHAPE_INVALID;
+  if (c->w_dtype == LLMK_Q8) {
+    // int8 packs: the inputs of every projection and of the head in whole groups, a row segment per lane
+    const int64_t ks[3] = {c->d, c->n_head * c->head_dim, c->hidden};
+    for (int64_t k : ks) {
+      RowdotParams r{};
+      r.K = k;
+      r.N = 1;
+      if (rowdot_q8_plan(r, GM_PLAIN) != 0) return LLMK_HEAD_SHAPE_INVALID;
+    }
+    if (c->w_layout != LLMK_W_OUT_IN || c->step_path == LLMK_STEP_PERSISTENT) return LLMK_INVALID_ARGUMENT;
+    return LLMK_OK;
+  }
   const int64_t vec = c->w_dtype == LLMK_BF16 ? 8 : 4;
   const int64_t widths[4] = {c->d, c->n_head * c->head_dim, c->n_kv * c->head_dim, c->hidden};
   for (int64_t w : widths)
@@ -126,6 +139,9 @@ struct DecodePlan {
   int rowdot = 0;                       // 1: output-major weights (row-dot kernels), 0: split-K kernels
   GemvParams qkv{}, o{}, gu{}, down{};
   RowdotParams rqkv{}, ro{}, rgu{}, rdown{};
+  int q8 = 0;                           // 1: int8 weight packs (row-dot over packs, head as row-dot + argmax)
+  RowdotParams rhead{};
+  int32_t* q8_tok = nullptr;            // the int8 head's greedy token
   HeadParams head{};
   AttnParams attn{};
   // workspace regions
@@ -180,7 +196,15 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.ro.K = qd; D.ro.N = d;
   D.rgu.K = d; D.rgu.N = F;
   D.rdown.K = F; D.rdown.N = d;
-  if (D.rowdot) {
+  D.q8 = c->w_dtype == LLMK_Q8;
+  if (D.q8) {
+    D.rhead.K = d; D.rhead.N = c->vocab;
+    rowdot_q8_plan(D.rqkv, GM_QKV);
+    rowdot_q8_plan(D.ro, GM_RESID);
+    rowdot_q8_plan(D.rgu, GM_GATEUP);
+    rowdot_q8_plan(D.rdown, GM_RESID);
+    rowdot_q8_plan(D.rhead, GM_PLAIN);
+  } else if (D.rowdot) {
     rowdot_plan(D.rqkv, bf, GM_QKV);
     rowdot_plan(D.ro, bf, GM_RESID);
     rowdot_plan(D.rgu, bf, GM_GATEUP);
@@ -218,6 +242,7 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.head_val = cv.take<float>(D.head.n_blocks);
   D.head_idx = cv.take<int32_t>(D.head.n_blocks);
   D.tok_scratch = cv.take<int32_t>(kTimeMaxReps);
+  D.q8_tok = cv.take<int32_t>(1);
   D.step_layers = cv.take<StepLayer>(c->n_layer);
   D.step_err = cv.take<int32_t>(4);
   D.step_cnt = cv.take<unsigned>(1);
@@ -256,6 +281,18 @@ int32_t model_check(const llmk_config* c, const llmk_model* m) {
 
 int32_t model_lengths(const llmk_config* c, const llmk_model* m) {
   const int64_t d = c->d, qd = c->n_head * c->head_dim, kvd = c->n_kv * c->head_dim, F = c->hidden;
+  if (c->w_dtype == LLMK_Q8) {   // q8 packs: byte counts
+    if (m->emb.len != c->vocab * d || m->w_out.len != q8_pack_bytes(c->vocab, d) || m->g_final.len != d)
+      return LLMK_WEIGHT_LENGTH_MISMATCH;
+    if (m->rope_table.len != c->max_seq * c->head_dim) return LLMK_WEIGHT_LENGTH_MISMATCH;
+    const int64_t want[LLMK_LAYER_TENSORS] = {q8_pack_bytes(qd, d), q8_pack_bytes(kvd, d), q8_pack_bytes(kvd, d),
+                                              q8_pack_bytes(d, qd), q8_pack_bytes(F, d), q8_pack_bytes(F, d),
+                                              q8_pack_bytes(d, F), d, d};
+    for (int64_t l = 0; l < c->n_layer; ++l)
+      for (int t = 0; t < LLMK_LAYER_TENSORS; ++t)
+        if (layer_t(m, l, t).len != want[t]) return LLMK_WEIGHT_LENGTH_MISMATCH;
+    return LLMK_OK;
+  }
   if (m->emb.len != c->vocab * d || m->w_out.len != c->vocab * d || m->g_final.len != d) return LLMK_WEIGHT_LENGTH_MISMATCH;
   if (m->rope_table.len != c->max_seq * c->head_dim) return LLMK_WEIGHT_LENGTH_MISMATCH;
   const int64_t want[LLMK_LAYER_TENSORS] = {d * qd, d * kvd, d * kvd, qd * d, d * F, d * F, F * d, d, d};
@@ -298,6 +335,23 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
   unsigned* gcnt = D.counters;
   unsigned* acnt = D.counters + D.n_gemv_counters;
   unsigned* hcnt = acnt + c->n_kv;
+  if (which == K_HEAD && D.q8) {
+    // logits = W_out rmsnorm(x) g_final over the int8 head, then the greedy token and the state's advance
+    RowdotParams h = D.rhead;
+    h.w0 = m->w_out.ptr;
+    h.in = D.x;
+    h.in_is_w = 0;
+    h.in_state = nullptr;
+    h.gain = static_cast<const float*>(m->g_final.ptr);
+    h.eps = (float)c->eps;
+    h.y = logits ? logits : D.logits;
+    hipError_t e = rowdot_q8_launch(h, GM_PLAIN, s);
+    const int32_t bpr = std::min<int32_t>(D.head.n_blocks, 128);
+    if (e == hipSuccess)
+      e = argmax_launch(h.y, 1, c->vocab, D.q8_tok, nullptr, D.head_val, D.head_idx, hcnt, bpr, s);
+    if (e == hipSuccess) e = state_advance_launch(D.state, D.q8_tok, token_out, s);
+    return e;
+  }
   if (which == K_HEAD) {
     // logits = W_out rmsnorm(x) g_final; greedy token; state advances
     HeadParams h = D.head;
@@ -346,7 +400,7 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
         r.gain = g_attn;
         r.eps = (float)c->eps;
         r.y = D.qkv_buf;
-        return rowdot_launch(r, GM_QKV, bf, s);
+        return D.q8 ? rowdot_q8_launch(r, GM_QKV, s) : rowdot_launch(r, GM_QKV, bf, s);
       }
       case K_O: {     // x = x + att Wo   (layer 0: x = emb[token] + att Wo)
         RowdotParams o = D.ro;
@@ -355,7 +409,7 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
         o.x = D.x;
         if (l == 0) { o.base = m->emb.ptr; o.base_is_w = 1; o.base_state = D.state; }
         else { o.base = D.x; o.base_is_w = 0; o.base_state = nullptr; }
-        return rowdot_launch(o, GM_RESID, bf, s);
+        return D.q8 ? rowdot_q8_launch(o, GM_RESID, s) : rowdot_launch(o, GM_RESID, bf, s);
       }
       case K_GATEUP: {   // h = rmsnorm(x) g_ffn;  u = silu(h Wgate) * (h Wup)
         RowdotParams gu = D.rgu;
@@ -365,7 +419,7 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
         gu.gain = g_ffn;
         gu.eps = (float)c->eps;
         gu.y = D.u;
-        return rowdot_launch(gu, GM_GATEUP, bf, s);
+        return D.q8 ? rowdot_q8_launch(gu, GM_GATEUP, s) : rowdot_launch(gu, GM_GATEUP, bf, s);
       }
       case K_DOWN: {  // x = x + u Wdown
         RowdotParams dn = D.rdown;
@@ -374,7 +428,7 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
         dn.x = D.x;
         dn.base = D.x;
         dn.hidden = hidden ? hidden + l * d : nullptr;
-        return rowdot_launch(dn, GM_RESID, bf, s);
+        return D.q8 ? rowdot_q8_launch(dn, GM_RESID, s) : rowdot_launch(dn, GM_RESID, bf, s);
       }
     }
     return hipErrorInvalidValue;
@@ -1817,6 +1871,22 @@ int32_t llmk_decode_batch_kernel_time(const llmk_config* cfg, const llmk_model* 
   for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos_h[r] + 1;
   *ms_per_launch_h = ms / (float)(reps * per_rep);
   return LLMK_OK;
+}
+
+int64_t llmk_q8_pack_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim || cols % Q8_GROUP != 0) return -1;
+  return q8_pack_bytes(rows, cols);
+}
+
+int32_t llmk_quantize_q8(const void* w, int64_t len_w, int32_t w_dtype, int64_t rows, int64_t cols, void* pack,
+                         int64_t len_pack, void* stream) {
+  if (!w || !pack || !is_dtype(w_dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, cols});
+  if (st != LLMK_OK) return st;
+  if (cols % Q8_GROUP != 0) return LLMK_HEAD_SHAPE_INVALID;
+  if (len_w != rows * cols) return LLMK_WEIGHT_LENGTH_MISMATCH;
+  if (len_pack != q8_pack_bytes(rows, cols)) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  return finish(q8_quantize_launch(w, w_dtype == LLMK_BF16, rows, cols, pack, as_stream(stream)));
 }
 
 int32_t llmk_transpose(const void* src, int64_t len_src, void* dst, int64_t len_dst, int64_t rows, int64_t cols,

@@ -9,8 +9,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BF16, F32, W_IN_OUT, W_OUT_IN, Config, KVPool, Model, check, decode_step, decode_steps,
-               decode_workspace_bytes, make_config, rope_table_init, transpose, workspace)
+from . import (BF16, F32, Q8, W_IN_OUT, W_OUT_IN, Config, KVPool, Model, check, decode_step, decode_steps,
+               decode_workspace_bytes, make_config, q8_pack_bytes, quantize_q8, rope_table_init, transpose,
+               workspace)
 
 _LAYER_MAP = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("gate", "w_gate"), ("up", "w_up"),
               ("down", "w_down"), ("n1", "g_attn"), ("n2", "g_ffn"))
@@ -18,9 +19,10 @@ _LAYER_MAP = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("gate", "
 
 def config_from(shape, w_layout=W_OUT_IN, step_path=0) -> Config:
     """llmk_config from any object with vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps,
-    rope_base, rope_layout, w_dtype ('f32'/'bf16') and kv_dtype attributes. upload_model repacks the
-    projections to match w_layout. step_path: 0 auto, 1 one kernel per operation, 2 persistent."""
-    code = {"f32": F32, "bf16": BF16}
+    rope_base, rope_layout, w_dtype ('f32'/'bf16'/'q8') and kv_dtype attributes. upload_model repacks the
+    projections to match w_layout. step_path: 0 auto, 1 one kernel per operation, 2 persistent. 'q8' means
+    int8 weight packs of bf16 weights (the projections and the head; the embedding table stays bf16)."""
+    code = {"f32": F32, "bf16": BF16, "q8": Q8}
     return make_config(shape.vocab, shape.d, shape.n_layer, shape.n_head, shape.n_kv, shape.head_dim, shape.hidden,
                        shape.max_seq, shape.eps, shape.rope_base, shape.rope_layout, code[shape.w_dtype],
                        code[shape.kv_dtype], w_layout, step_path)
@@ -38,9 +40,21 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
     return t.to(device)
 
 
+def _q8_pack(a: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+    """Quantize an output-major device matrix into a fresh int8 weight pack (on the device)."""
+    pack = torch.empty(q8_pack_bytes(rows, cols), dtype=torch.uint8, device=a.device)
+    check(quantize_q8(a, rows, cols, pack, stream), "quantize_q8")
+    return pack
+
+
 def upload_model(cfg: Config, W: dict, device="cuda", stream=None) -> Model:
+    """Device weights for cfg. With cfg.w_dtype Q8 the weights come in bf16 (uint16) and every projection and
+    the output head are quantized on the device into int8 weight packs (output-major)."""
+    q8 = cfg.w_dtype == Q8
     emb = to_device(W["emb"], device)
     out = to_device(W["out"], device)
+    if q8:
+        out = _q8_pack(out, cfg.vocab, cfg.d, stream)
     norm = to_device(np.asarray(W["norm"], dtype=np.float32), device)
     layers = []
     for L in W["layers"]:
@@ -56,6 +70,8 @@ def upload_model(cfg: Config, W: dict, device="cuda", stream=None) -> Model:
                 check(transpose(a, t, rows, cols, stream), "transpose")
                 del a
                 a = t
+                if q8:
+                    a = _q8_pack(a, cols, rows, stream)
             dev_layer[dst] = a
         layers.append(dev_layer)
     table = torch.empty(cfg.max_seq * cfg.head_dim, dtype=torch.float32, device=device)

@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 N_PRE = 4096                    # filled context before the first timed step
 PMC_FILES = {"gate_up": os.path.join(ROOT, "profiles", "rowdot_gate_up_llama8b_pmc.md"),
-             "step": os.path.join(ROOT, "profiles", "step_kernel_llama8b_pmc.md")}
+             "step": os.path.join(ROOT, "profiles", "step_kernel_llama8b_pmc.md"),
+             "gate_up_q8": os.path.join(ROOT, "profiles", "rowdot_q8_gate_up_llama8b_pmc.md")}
 STEP_REPS = 64                  # consecutive steps in the persistent kernel's event timing
 
 
@@ -34,14 +35,23 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def step_bytes(s, ctx: int) -> int:
+def q8_pack_bytes(rows: int, cols: int) -> int:
+    """Bytes of an int8 weight pack: a code per weight and an fp32 scale per 128 inputs of a row."""
+    return rows * cols + 4 * rows * (cols // 128)
+
+
+def step_bytes(s, ctx: int, q8: bool = False) -> int:
     """Algorithmic HBM bytes of one decode step attending `ctx` positions: every weight once, the
     embedding row, the gains, the RoPE table row, the K/V of the attended context, the appended K/V,
-    and the logits written once."""
+    and the logits written once. q8: the projections and the head are int8 packs (embedding bf16)."""
     wsz = 2 if s.w_dtype == "bf16" else 4
     kvsz = 2 if s.kv_dtype == "bf16" else 4
     d, qd, kvd, F, V, L = s.d, s.n_head * s.head_dim, s.n_kv * s.head_dim, s.hidden, s.vocab, s.n_layer
-    weights = L * (d * qd + 2 * d * kvd + qd * d + 3 * d * F) * wsz + V * d * wsz + d * wsz
+    if q8:
+        pb = q8_pack_bytes
+        weights = L * (pb(qd, d) + 2 * pb(kvd, d) + pb(d, qd) + 2 * pb(F, d) + pb(d, F)) + pb(V, d) + d * 2
+    else:
+        weights = L * (d * qd + 2 * d * kvd + qd * d + 3 * d * F) * wsz + V * d * wsz + d * wsz
     gains = (2 * L + 1) * d * 4
     rope = s.head_dim * 4
     kv = L * ctx * kvd * 2 * kvsz + L * kvd * 2 * kvsz
@@ -49,14 +59,16 @@ def step_bytes(s, ctx: int) -> int:
     return weights + gains + rope + kv + logits
 
 
-def gate_up_bytes(s) -> int:
+def gate_up_bytes(s, q8: bool = False) -> int:
     """Algorithmic bytes of one gate|up launch: both weight matrices, the input row, its gain, u written."""
     wsz = 2 if s.w_dtype == "bf16" else 4
-    return 2 * s.d * s.hidden * wsz + 2 * s.d * 4 + s.hidden * 4
+    w = 2 * q8_pack_bytes(s.hidden, s.d) if q8 else 2 * s.d * s.hidden * wsz
+    return w + 2 * s.d * 4 + s.hidden * 4
 
 
 KERNEL_SOURCES = {"gate_up": ("rowdot.hip", "common.h", "kernels.h"),
-                  "step": ("step.hip", "attn_block.h", "common.h", "kernels.h")}
+                  "step": ("step.hip", "attn_block.h", "common.h", "kernels.h"),
+                  "gate_up_q8": ("q8.hip", "q8.h", "common.h", "kernels.h")}
 
 
 def kernel_source_sha(which: str = "gate_up") -> str:
@@ -295,7 +307,7 @@ def main() -> int:
                     help="times each kernel class's per-layer launches are replayed for its HIP-event timing")
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle steps in the CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("batch1", "batched", "prefill"), default="batch1",
+    ap.add_argument("--workload", choices=("batch1", "batched", "prefill", "q8"), default="batch1",
                     help="batch1: the 8B-shaped single-sequence step (default); batched: 64 ragged sequences per step; "
                          "prefill: a 2,048-token prompt (steps = prompts, 8 by default)")
     ap.add_argument("--prefill-shape", choices=("q06", "l8b"), default="q06",
@@ -339,6 +351,7 @@ def main() -> int:
         return run_prefill(args)
 
     s = synth.L8B
+    q8 = args.workload == "q8"
     max_steps_per_call = s.max_seq - N_PRE
     t_start = time.time()
     log(f"generating {s.name} weights")
@@ -347,7 +360,7 @@ def main() -> int:
     first = int(synth.prompt(1, s.vocab, stream=7)[0])
     log(f"generated in {time.time() - t_start:.1f} s; uploading")
     path_arg = {"auto": llmk.STEP_AUTO, "per-op": llmk.STEP_PER_OP, "persistent": llmk.STEP_PERSISTENT}[args.step_path]
-    cfg = loader.config_from(s, step_path=path_arg)
+    cfg = loader.config_from(s.with_(w_dtype="q8") if q8 else s, step_path=path_arg)
     path = llmk.decode_path(cfg)
     if path not in (llmk.STEP_PER_OP, llmk.STEP_PERSISTENT):
         raise RuntimeError(f"decode_path: {path} {llmk.status_name(path)}")
@@ -385,7 +398,7 @@ def main() -> int:
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
     ctxs = [N_PRE + 1 + (i % max_steps_per_call) for i in range(args.steps)]
-    total_bytes = sum(step_bytes(s, c) for c in ctxs)
+    total_bytes = sum(step_bytes(s, c, q8) for c in ctxs)
     step_gbps = total_bytes / elapsed / 1e9
     tokens = toks.cpu().numpy().tolist()
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {step_gbps:.0f} GB/s algorithmic")
@@ -413,15 +426,17 @@ def main() -> int:
                 raise RuntimeError(f"decode_kernel_time({n}): {st} {llmk.status_name(st)}")
             avg_ms[n] = ms
             pool.slot_len[0] = N_PRE
-        k_bytes = gate_up_bytes(s)
+        k_bytes = gate_up_bytes(s, q8)
         ms = avg_ms["gate_up"]
-        k_name = "gate|up row-dot GEMV (rowdot_kernel, GATEUP epilogue)"
+        k_name = ("gate|up row-dot GEMV over int8 packs (rowdot_q8_kernel, GATEUP epilogue)" if q8 else
+                  "gate|up row-dot GEMV (rowdot_kernel, GATEUP epilogue)")
         kernel_sum_ms = sum(avg_ms[n] for n in llmk.KERNEL_CLASSES[:5]) * s.n_layer + avg_ms["head"]
     k_gbps = k_bytes / (ms * 1e-3) / 1e9
     log("avg kernel us: " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in avg_ms.items()))
 
     result = {
-        "metric": "decode tokens/s at batch 1 (8B-shaped) + achieved HBM GB/s vs peak",
+        "metric": ("decode tokens/s at batch 1 (8B-shaped, int8 weight packs) + achieved HBM GB/s vs peak" if q8
+                   else "decode tokens/s at batch 1 (8B-shaped) + achieved HBM GB/s vs peak"),
         "value": args.steps / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -433,17 +448,19 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "llama-3-8b-shaped greedy decode, batch 1, bf16 weights and K/V, context 4096",
+        "config": {"workload": ("llama-3-8b-shaped greedy decode, batch 1, int8 weight packs (projections and head; "
+                                "fp32 scale per 128 inputs), bf16 embedding and K/V, context 4096" if q8 else
+                                "llama-3-8b-shaped greedy decode, batch 1, bf16 weights and K/V, context 4096"),
                    "vocab": s.vocab, "d": s.d, "n_layer": s.n_layer, "n_head": s.n_head, "n_kv": s.n_kv,
                    "head_dim": s.head_dim, "hidden": s.hidden, "batch": 1, "context_start": N_PRE,
-                   "weights": "bf16", "kv": "bf16", "accumulation": "f32"},
+                   "weights": "q8" if q8 else "bf16", "kv": "bf16", "accumulation": "f32"},
         "step_hbm_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "step_bytes_mean": total_bytes / args.steps,
         "step_form": "persistent" if persistent else "per-op",
         "roofline": {"bound": "hbm", "kernel": k_name,
                      "achieved": k_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic_from_profiles("step" if persistent else "gate_up"),
+                     "traffic": traffic_from_profiles("step" if persistent else "gate_up_q8" if q8 else "gate_up"),
                      "bytes_per_launch": k_bytes, "avg_launch_us": ms * 1e3},
         "kernels_avg_us": {n: v * 1e3 for n, v in avg_ms.items()},
         "kernel_sum_ms_per_step": kernel_sum_ms,
@@ -454,7 +471,13 @@ def main() -> int:
         import oracle
         n = args.cpu_steps
         log(f"oracle baseline: {n} steps on the host cores")
-        m = oracle.Model(s, W)
+        if q8:
+            from oracle import quant
+            log("oracle: the decoder the int8 packs describe (fp32 copies of q * s)")
+            Wq = quant.quantized_weights(W, f64=False)
+            m = oracle.Model(s, Wq)
+        else:
+            m = oracle.Model(s, W)
         c = m.new_cache(N_PRE + n)
         c.fill_prefix(prefix)
         t = first
@@ -468,7 +491,8 @@ def main() -> int:
         result["cpu_baseline"] = {"value": n / tc, "unit": "tokens/s", "cores": oracle.lib().orc_num_threads(),
                                   "kind": "oracle",
                                   "sample": f"{n} greedy decode steps of the same workload at positions "
-                                            f"{N_PRE}..{N_PRE + n - 1} (fp64, OpenMP)",
+                                            f"{N_PRE}..{N_PRE + n - 1} (fp64, OpenMP"
+                                            + (", weights q * s of the oracle's own quantization)" if q8 else ")"),
                                   "tokens_agree_with_gpu": otoks == tokens[:n]}
         log(f"oracle: {tc / n:.2f} s/step, tokens {otoks} vs gpu {tokens[:n]}")
     else:

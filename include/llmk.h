@@ -75,7 +75,8 @@ enum {
 /* most sequences one batched decode step serves */
 #define LLMK_MAX_BATCH 64
 
-typedef enum { LLMK_F32 = 0, LLMK_BF16 = 1 } llmk_dtype;
+/* LLMK_Q8 is a weight format only (llmk_config.w_dtype, llmk_quantize_q8): see "int8 weight packs" below. */
+typedef enum { LLMK_F32 = 0, LLMK_BF16 = 1, LLMK_Q8 = 2 } llmk_dtype;
 /* Half-split pairs (j, j + hd/2) are the GPT-NeoX/Qwen3 convention ([llmk] "Two
  * gaps, not three"); interleaved pairs (2j, 2j+1) are the layout of [fwd] "The
  * code". [dops] "Method" supports both. */
@@ -257,7 +258,8 @@ typedef struct {
   double eps;          /* RMSNorm epsilon, inside the mean ([fwd] "The code": rmsnorm) */
   double rope_base;    /* RoPE base (1e4 for the toy decoder, 1e6 Qwen3-shaped, 5e5 Llama-3-shaped) */
   int32_t rope_layout; /* llmk_rope_layout */
-  int32_t w_dtype;     /* llmk_dtype of every weight matrix and the embedding table */
+  int32_t w_dtype;     /* llmk_dtype of every weight matrix and the embedding table; LLMK_Q8: the seven
+                          projections and the output head are q8 packs and the embedding table is bf16 */
   int32_t kv_dtype;    /* llmk_dtype of the K/V pool */
   int32_t w_layout;    /* llmk_weight_layout of the seven per-layer projections */
   int32_t step_path;   /* llmk_step_path */
@@ -401,6 +403,35 @@ int32_t llmk_prefill_profiled(const llmk_config* cfg, const llmk_model* model, l
                               const int64_t* tokens_h, int64_t n, int64_t pos0, int32_t* tokens_out,
                               int64_t len_tokens, float* class_ms_h, int64_t len_class_ms, void* ws, int64_t len_ws,
                               void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* int8 weight packs (LLMK_Q8)                                                */
+/* ------------------------------------------------------------------------- */
+/* The pages name int8 weights and q8_K packs as the decode path's next saving on streamed bytes ([xpu]
+ * "1. CausalLM: the forward path"; [llmk] "How this composes into a decode step") without fixing a format;
+ * this one is the library's own. A q8 pack holds a rows x cols matrix, output-major (each row is one
+ * output's weights over cols inputs), in groups of LLMK_Q8_GROUP consecutive inputs of a row: per group the
+ * fp32 scale s = max|w| / 127 and int8 codes q = rint(w / s) (ties to even; 0 for an all-zero group),
+ * decided in fp32; the weight is q * s, |w - q s| <= s / 2. Bytes: rows*cols codes row-major, then
+ * rows*(cols/LLMK_Q8_GROUP) fp32 scales row-major: 1 + 4/128 bytes a weight against 2 for bf16.
+ * A model with w_dtype LLMK_Q8 holds q8 packs, in LLMK_W_OUT_IN, for wq [H*hd x d], wk, wv [Hkv*hd x d],
+ * wo [d x H*hd], w_gate, w_up [F x d], w_down [d x F] and w_out [vocab x d] (each llmk_tensor.len is the
+ * pack's byte count, the pointer 16-byte aligned) and the embedding table in bf16 (vocab*d elements).
+ * d, H*hd and F are multiples of LLMK_Q8_GROUP, at most 16,384. Such a model runs llmk_decode_step,
+ * llmk_decode_steps and the timing aids in the per-operation form; the persistent step, the batched
+ * step and prefill refuse it (578). */
+#define LLMK_Q8_GROUP 128
+
+/* Bytes of a q8 pack of a rows x cols matrix, or -1 if rows or cols is < 1 or > LLMK_MAX_DIM or cols is not
+ * a multiple of LLMK_Q8_GROUP. */
+int64_t llmk_q8_pack_bytes(int64_t rows, int64_t cols);
+
+/* Quantize w (device, rows x cols row-major, output-major, w_dtype LLMK_F32 or LLMK_BF16, finite values)
+ * into the q8 pack at `pack` (device, len_pack bytes, 16-byte aligned), on `stream`. Codes: 578 (null,
+ * w_dtype), 561 (rows or cols < 1), 564 (> LLMK_MAX_DIM), 574 (cols not a multiple of LLMK_Q8_GROUP),
+ * 576 (len_w != rows*cols), 577 (len_pack != llmk_q8_pack_bytes), 579 (launch failed). */
+int32_t llmk_quantize_q8(const void* w, int64_t len_w, int32_t w_dtype, int64_t rows, int64_t cols, void* pack,
+                         int64_t len_pack, void* stream);
 
 /* dst = src^T for a rows x cols row-major matrix (dst is cols x rows), both device buffers of rows*cols
  * elements of dtype; the one-time repacking of projections into LLMK_W_OUT_IN. dst may not alias src.

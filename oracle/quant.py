@@ -17,6 +17,8 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import 
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 GROUP = 128
@@ -43,10 +45,11 @@ def quantize(w) -> tuple[np.ndarray, np.ndarray]:
     return q.reshape(rows, K), s.astype(np.float32)
 
 
-def dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """The weights the codes stand for: q * s of their group, float64 [rows][K] (every product is exact)."""
+def dequantize(q: np.ndarray, s: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """The weights the codes stand for: q * s of their group, [rows][K]; float64 (every product is exact) or
+    float32 (each product rounded once)."""
     rows, K = q.shape
-    g = q.reshape(rows, K // GROUP, GROUP).astype(np.float64) * s.astype(np.float64)[..., None]
+    g = q.reshape(rows, K // GROUP, GROUP).astype(dtype) * s.astype(dtype)[..., None]
     return g.reshape(rows, K)
 
 
@@ -66,14 +69,32 @@ def from_pack(buf: np.ndarray, rows: int, K: int) -> tuple[np.ndarray, np.ndarra
 
 
 def widen(a: np.ndarray) -> np.ndarray:
-    """float32 values of a weight array (uint16 holds bf16 bit patterns)."""
+    """float32 values of a weight array (uint16 holds bf16 bit patterns: the high half of an fp32)."""
     a = np.asarray(a)
     if a.dtype == np.uint16:
-        return (a.astype(np.uint32) << 16).view(np.float32)
+        return np.left_shift(a.astype(np.uint32), 16).view(np.float32)
     return a.astype(np.float32)
 
 
 _PROJ = ("wq", "wk", "wv", "wo", "gate", "up", "down")
+
+
+def _quantized_io(w_io: np.ndarray, dt) -> np.ndarray:
+    """A projection given [in][out], quantized per output row along `in`, as q * s in [in][out] (blocks of
+    output rows on a thread pool; every block is independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+    n_in, n_out = w_io.shape
+    out = np.empty((n_in, n_out), dt)
+    step = 512
+
+    def block(r0):
+        r1 = min(n_out, r0 + step)
+        rows = np.ascontiguousarray(widen(w_io[:, r0:r1]).T)   # [r1 - r0][in]
+        out[:, r0:r1] = dequantize(*quantize(rows), dt).T
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(block, range(0, n_out, step)))
+    return out
 
 
 def quantized_weights(W: dict, f64: bool = True) -> dict:
@@ -82,15 +103,13 @@ def quantized_weights(W: dict, f64: bool = True) -> dict:
     the embedding table stays as it is stored (bf16 in the q8 format) and the gains are fp32. float64 weights
     (exact), or float32 (q * s rounded once; 2^-24 relative) to halve the memory of large shapes."""
     dt = np.float64 if f64 else np.float32
-    out = {"emb": widen(W["emb"]).astype(dt), "norm": np.asarray(W["norm"], np.float32)}
-    out["out"] = np.ascontiguousarray(dequantize(*quantize(widen(W["out"]))).astype(dt))
+    out = {"emb": widen(W["emb"]).astype(dt, copy=False), "norm": np.asarray(W["norm"], np.float32)}
+    out["out"] = np.ascontiguousarray(_quantized_io(np.asarray(W["out"]).T, dt).T)
     layers = []
     for L in W["layers"]:
         M = {"n1": np.asarray(L["n1"], np.float32), "n2": np.asarray(L["n2"], np.float32)}
         for k in _PROJ:
-            wt = np.ascontiguousarray(widen(L[k]).T)            # [out][in]
-            M[k] = np.ascontiguousarray(dequantize(*quantize(wt)).T.astype(dt))
-            del wt
+            M[k] = _quantized_io(np.asarray(L[k]), dt)
         layers.append(M)
     out["layers"] = layers
     return out

@@ -473,3 +473,75 @@ def test_prefill_refusals():
     assert llmk.prefill_workspace_bytes(cfg, 0) == -561
     # 200 tokens are one chunk of 200 rows: the workspace holds its row buffers, its logits and hidden states
     assert llmk.prefill_workspace_bytes(cfg, 200) >= llmk.decode_workspace_bytes(cfg, 64) + 200 * (V + L * d) * 4
+
+
+def test_q8_config_checks_agree_with_oracle():
+    base = dict(vocab=40, d=128, n_layer=2, n_head=2, n_kv=1, head_dim=64, hidden=256, max_seq=64, w_dtype=2,
+                w_layout=1)
+    variants = [dict(), dict(w_layout=0), dict(step_path=2), dict(step_path=1), dict(hidden=200), dict(d=192),
+                dict(head_dim=32, n_head=3, n_kv=1), dict(d=4096, hidden=14336, n_head=32, n_kv=8, head_dim=128),
+                dict(hidden=16384), dict(hidden=16384 + 128), dict(d=1024, hidden=3072), dict(kv_dtype=2)]
+    for v in variants:
+        kw = _cfg_kwargs(**{**base, **v})
+        cfg = llmk.make_config(**kw)
+        got = llmk.decode_workspace_bytes(cfg, 1)
+        exp = contract.config_check(**kw)
+        if exp == contract.OK:
+            assert got > 0, v
+            # the batched path and prefill run bf16 weights only
+            assert llmk.decode_workspace_bytes(cfg, 2) == -contract.INVALID, v
+            assert llmk.prefill_workspace_bytes(cfg, 4) == -contract.INVALID, v
+        else:
+            assert got == -exp, v
+
+
+def test_q8_pack_bytes_and_quantize_refusals():
+    for rows, cols in ((1, 128), (3, 256), (128256, 4096), (0, 128), (4, 0), (4, 100), ((1 << 24) + 1, 128),
+                       (2, (1 << 24) + 128)):
+        assert llmk.q8_pack_bytes(rows, cols) == contract.q8_pack_bytes(rows, cols), (rows, cols)
+    assert llmk.q8_pack_bytes(3, 256) == 3 * 256 + 4 * 3 * 2
+    FA = 0x10000
+    ok = dict(w=True, len_w=4 * 256, w_dtype=1, rows=4, cols=256, pack=True, len_pack=4 * 256 + 32)
+    cases = [dict(), dict(w=False), dict(pack=False), dict(w_dtype=2), dict(w_dtype=-1), dict(rows=0), dict(cols=-128),
+             dict(rows=(1 << 24) + 1), dict(cols=200, len_w=800), dict(len_w=4 * 256 - 1), dict(len_pack=4 * 256),
+             dict(len_pack=4 * 256 + 33)]
+    for c in cases:
+        a = {**ok, **c}
+        exp = contract.quantize_q8(**a)
+        if exp == contract.OK:
+            continue   # only refusals run here (no device)
+        got = llmk.lib.llmk_quantize_q8(FA if a["w"] else None, a["len_w"], a["w_dtype"], a["rows"], a["cols"],
+                                        FA if a["pack"] else None, a["len_pack"], None)
+        assert got == exp, c
+
+
+@no_gpu
+def test_q8_decode_model_lengths():
+    import numpy as np
+    kw = _cfg_kwargs(vocab=40, d=128, n_layer=2, n_head=2, n_kv=1, head_dim=64, hidden=256, max_seq=64, w_dtype=2,
+                     w_layout=1)
+    cfg = llmk.make_config(**kw)
+    d, qd, kvd, F, V, L = 128, 128, 64, 256, 40, 2
+    pb = contract.q8_pack_bytes
+    lens = [pb(qd, d), pb(kvd, d), pb(kvd, d), pb(d, qd), pb(F, d), pb(F, d), pb(d, F), d, d]
+    FA = 0x10000
+    ws_need = llmk.decode_workspace_bytes(cfg, 1)
+
+    def call(bad=None):
+        arr = (llmk.Tensor * (L * 9))()
+        for l in range(L):
+            for t in range(9):
+                arr[l * 9 + t] = llmk.Tensor(FA, lens[t] + (1 if bad == (l, t) else 0))
+        out_len = pb(V, d) + (1 if bad == "out" else 0)
+        emb_len = V * d + (1 if bad == "emb" else 0)
+        m = llmk.ModelStruct(llmk.Tensor(FA, emb_len), llmk.Tensor(FA, out_len), llmk.Tensor(FA, d),
+                             llmk.Tensor(FA, 64 * 64), arr)
+        ks = (ctypes.c_void_p * L)(FA, FA)
+        sl = np.zeros(2, np.int64)
+        ps = llmk.PoolStruct(ks, ks, L, 2, 32, 1, 64, 0, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        # token 40 is out of range: every earlier check passed, nothing is launched
+        return llmk.lib.llmk_decode_step(ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), 0, 40, 0, None, V, FA,
+                                         None, 0, FA, ws_need, None)
+    assert call() == contract.decode_step(kw, token=40) == 572
+    for bad in ((0, 0), (1, 6), (1, 3), "out", "emb"):
+        assert call(bad) == contract.decode_step(kw, lens_ok=False) == 576, bad
