@@ -104,6 +104,8 @@ _SIGS = {
     "llmk_decode_path": ([ctypes.POINTER(Config)], _i32),
     "llmk_transpose": ([_p, _i64, _p, _i64, _i64, _i64, _i32, _p], _i32),
     "llmk_q8_pack_bytes": ([_i64, _i64], _i64),
+    "llmk_decode_steps_sampled": ([_p, _p, _p, _i64, _i64, _i64, _i64, _f32, _i32, _f32, _p, _i64, _p, _i64, _p, _i64,
+                                   _p, _i64, _p], _i32),
     "llmk_quantize_q8": ([_p, _i64, _i32, _i64, _i64, _p, _i64, _p], _i32),
     "llmk_decode_step_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct),
                                    _i64, _i64, _i64, _p, ctypes.POINTER(_f32), _i64, _p, _i64, _p], _i32),
@@ -362,6 +364,17 @@ def decode_steps(cfg: Config, model: Model, pool: KVPool, slot, token0, pos0, n_
     return lib.llmk_decode_steps(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct), slot,
                                  token0, pos0, n_steps, _ptr(tokens_out), _len(tokens_out), _ptr(ws), _len(ws),
                                  _stream(stream))
+
+
+def decode_steps_sampled(cfg: Config, model: Model, pool: KVPool, slot, token0, pos0, n_steps, temperature, top_k,
+                         top_p, draws, tokens_out, ws, sample_ws=None, stream=None) -> int:
+    """n_steps steps, each sampling its token (temperature, top-k, top-p, inverse CDF at draws[i]) inside the
+    captured loop. draws: device fp32 [n_steps]; sample_ws: sample_workspace_bytes(1, vocab, ...) bytes."""
+    return lib.llmk_decode_steps_sampled(ctypes.byref(cfg), ctypes.byref(model.struct), ctypes.byref(pool.struct),
+                                         slot, token0, pos0, n_steps, temperature, top_k, top_p, _ptr(draws),
+                                         _len(draws), _ptr(tokens_out), _len(tokens_out), _ptr(ws), _len(ws),
+                                         _ptr(sample_ws) if sample_ws is not None else None,
+                                         _len(sample_ws) if sample_ws is not None else 0, _stream(stream))
 
 
 def _host_i64(v):

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "loop.h"
 #include "q8.h"
 #include "llmk.h"
 
@@ -142,6 +143,8 @@ struct DecodePlan {
   int q8 = 0;                           // 1: int8 weight packs (row-dot over packs, head as row-dot + argmax)
   RowdotParams rhead{};
   int32_t* q8_tok = nullptr;            // the int8 head's greedy token
+  float* draw1 = nullptr;               // the sampled loop: this step's uniform
+  int32_t* sampled_tok = nullptr;       // and its token
   HeadParams head{};
   AttnParams attn{};
   // workspace regions
@@ -243,6 +246,8 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.head_idx = cv.take<int32_t>(D.head.n_blocks);
   D.tok_scratch = cv.take<int32_t>(kTimeMaxReps);
   D.q8_tok = cv.take<int32_t>(1);
+  D.draw1 = cv.take<float>(1);
+  D.sampled_tok = cv.take<int32_t>(1);
   D.step_layers = cv.take<StepLayer>(c->n_layer);
   D.step_err = cv.take<int32_t>(4);
   D.step_cnt = cv.take<unsigned>(1);
@@ -1480,6 +1485,18 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
   return LLMK_OK;
 }
 
+// Sampling at the end of every step of the captured loop (null: greedy).
+struct LoopSampling {
+  float temperature, top_p;
+  int32_t k;
+  const float* draws;
+  void* ws;
+};
+
+static int32_t decode_steps_run(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, void* ws,
+                                int64_t len_ws, void* stream, const LoopSampling* smp);
+
 int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                           int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
                           void* ws, int64_t len_ws, void* stream) {
@@ -1491,6 +1508,36 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
   st = decode_checks(cfg, model, pool, slot, token0, pos0, n_steps, tokens_out, ws);
   if (st != LLMK_OK) return st;
   if (len_tokens != n_steps) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  return decode_steps_run(cfg, model, pool, slot, token0, pos0, n_steps, tokens_out, ws, len_ws, stream, nullptr);
+}
+
+int32_t llmk_decode_steps_sampled(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                  int64_t token0, int64_t pos0, int64_t n_steps, float temperature, int32_t top_k,
+                                  float top_p, const float* draws, int64_t len_draws, int32_t* tokens_out,
+                                  int64_t len_tokens, void* ws, int64_t len_ws, void* sample_ws,
+                                  int64_t len_sample_ws, void* stream) {
+  if (!cfg || !model || !pool || !tokens_out || !ws || !draws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = config_check(cfg);
+  if (st != LLMK_OK) return st;
+  if (n_steps < 1) return LLMK_EMPTY_DIMENSION;
+  if (n_steps > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  st = decode_checks(cfg, model, pool, slot, token0, pos0, n_steps, tokens_out, ws);
+  if (st != LLMK_OK) return st;
+  if (len_tokens != n_steps) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (len_draws != n_steps) return LLMK_B_LENGTH_MISMATCH;
+  if (!(temperature >= 0.0f) || !(top_p > 0.0f && top_p <= 1.0f)) return LLMK_INVALID_ARGUMENT;
+  const int64_t n = cfg->vocab;
+  const int64_t k = temperature == 0.0f ? 1 : (top_k <= 0 || top_k >= n ? n : top_k);
+  if (k > LLMK_SAMPLE_MAX_K) return LLMK_DIMENSION_TOO_LARGE;
+  const int64_t need = sample_workspace_bytes(1, n, (int32_t)k);
+  if (need > 0 && (!sample_ws || len_sample_ws < need || !aligned16(sample_ws))) return LLMK_INVALID_ARGUMENT;
+  const LoopSampling smp{temperature, top_p, (int32_t)k, draws, sample_ws};
+  return decode_steps_run(cfg, model, pool, slot, token0, pos0, n_steps, tokens_out, ws, len_ws, stream, &smp);
+}
+
+static int32_t decode_steps_run(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, void* ws,
+                                int64_t len_ws, void* stream, const LoopSampling* smp) {
   DecodePlan D;
   plan_decode(cfg, nullptr, D);
   if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
@@ -1514,9 +1561,18 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
   e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e == hipSuccess) {
-    hipError_t ee = nwg > 0 ? step_launch(step_params(cfg, model, pool, slot, D, nwg, nullptr, nullptr, tokens_out),
+    float* lg = smp ? D.logits : nullptr;   // the sampled loop keeps each step's logits for the sampler
+    hipError_t ee = nwg > 0 ? step_launch(step_params(cfg, model, pool, slot, D, nwg, lg, nullptr, tokens_out),
                                           cfg->kv_dtype == LLMK_BF16, cs)
-                            : enqueue_step(cfg, model, pool, slot, D, nullptr, tokens_out, nullptr, cs);
+                            : enqueue_step(cfg, model, pool, slot, D, lg, tokens_out, nullptr, cs);
+    if (smp) {
+      // the head advanced the state with its greedy token; the sampled one replaces it
+      if (ee == hipSuccess) ee = draw_pick_launch(D.state, smp->draws, D.draw1, cs);
+      if (ee == hipSuccess)
+        ee = sample_launch(D.logits, 1, cfg->vocab, smp->temperature, smp->k, smp->top_p, D.draw1, D.sampled_tok,
+                           smp->ws, cs);
+      if (ee == hipSuccess) ee = sampled_token_launch(D.state, D.sampled_tok, tokens_out, cs);
+    }
     e = hipStreamEndCapture(cs, &graph);
     if (ee != hipSuccess) e = ee;
   }

@@ -29,6 +29,7 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "loop.h"
 
 namespace llmk {
 
@@ -535,6 +536,29 @@ hipError_t sample_launch(const float* logits, int64_t rows, int64_t n, float tem
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sample_merge_kernel, dim3((unsigned)rows), dim3(SM_THREADS), 0, s, cand, smax,
                      (int32_t)(p.slices * k), k, temperature, top_p, draw, token);
+  return hipGetLastError();
+}
+
+// ---- glue of the sampled decode loop (one thread each; the state lives on the device) -------------------
+
+__global__ void draw_pick_kernel(const DecodeState* st, const float* draws, float* dst) {
+  if (threadIdx.x == 0) dst[0] = draws[st->step - 1];
+}
+
+__global__ void sampled_token_kernel(DecodeState* st, const int32_t* tok, int32_t* tokens_out) {
+  if (threadIdx.x != 0) return;
+  const int32_t t = tok[0];
+  tokens_out[st->step - 1] = t;
+  st->token = t;
+}
+
+hipError_t draw_pick_launch(const DecodeState* st, const float* draws, float* dst, hipStream_t s) {
+  hipLaunchKernelGGL(draw_pick_kernel, dim3(1), dim3(64), 0, s, st, draws, dst);
+  return hipGetLastError();
+}
+
+hipError_t sampled_token_launch(DecodeState* st, const int32_t* tok, int32_t* tokens_out, hipStream_t s) {
+  hipLaunchKernelGGL(sampled_token_kernel, dim3(1), dim3(64), 0, s, st, tok, tokens_out);
   return hipGetLastError();
 }
 

@@ -338,6 +338,22 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
                           int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
                           void* ws, int64_t len_ws, void* stream);
 
+/* As llmk_decode_steps, with the sampling exit in place of greedy at the end of every step ([dops] "Method":
+ * temperature, then top-k, then top-p over the renormalised survivors, then the inverse CDF at an explicit
+ * uniform; llmk_sample's rule exactly): step i samples its token from its logits with the uniform draws[i],
+ * writes it to tokens_out[i] and feeds it to step i + 1, all inside the captured loop.
+ *   draws: device fp32 [n_steps] (len_draws elements), the caller's uniforms in [0, 1)
+ *   temperature >= 0 (0: greedy), top_k <= 0 or >= vocab: no cut, 0 < top_p <= 1
+ *   sample_ws: device scratch of len_sample_ws >= llmk_sample_workspace_bytes(1, vocab, temperature, top_k)
+ *   bytes, 16-byte aligned (may be NULL where that is 0); ws as for llmk_decode_steps
+ * Codes: as llmk_decode_steps (578 also for a NULL draws), then 563 (len_draws != n_steps), 578 (temperature,
+ * top_p), 564 (more than LLMK_SAMPLE_MAX_K survivors), 578 (sample_ws too small or misaligned). */
+int32_t llmk_decode_steps_sampled(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
+                                  int64_t token0, int64_t pos0, int64_t n_steps, float temperature, int32_t top_k,
+                                  float top_p, const float* draws, int64_t len_draws, int32_t* tokens_out,
+                                  int64_t len_tokens, void* ws, int64_t len_ws, void* sample_ws,
+                                  int64_t len_sample_ws, void* stream);
+
 /* One decode step of `batch` sequences at once ([xpu] "5. The batched decode": every weight row is read
  * once for all rows of the batch; the projections run as bf16 matrix-core GEMMs with each fp32 activation
  * carried as a bf16 hi + lo pair, fp32 accumulation). Row r is sequence slot slots_h[r] with input token

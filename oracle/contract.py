@@ -395,6 +395,27 @@ def decode_step(cfg: dict, tensors_ok=True, lens_ok=True, pool_ok=True, pool_dim
     return INVALID if ws_short else OK
 
 
+def decode_steps_sampled(cfg: dict, draws=True, len_draws=None, n_steps=1, temperature=1.0, top_k=0, top_p=1.0,
+                         sample_ws_short=False, **step_kw):
+    """Expected status of llmk_decode_steps_sampled: llmk_decode_steps' checks (decode_step's keywords, with
+    n_steps), then the sampling arguments in llmk_sample's order."""
+    if not draws:
+        return INVALID
+    ws_short = step_kw.pop("ws_short", False)   # the decode workspace is checked last
+    c = decode_step(cfg, n_steps=n_steps, **step_kw)
+    if c != OK:
+        return c
+    if (n_steps if len_draws is None else len_draws) != n_steps:
+        return B_LEN
+    if not (temperature >= 0.0) or not (0.0 < top_p <= 1.0):
+        return INVALID
+    n = cfg["vocab"]
+    k = 1 if temperature == 0.0 else (n if top_k <= 0 or top_k >= n else top_k)
+    if k > SAMPLE_MAX_K:
+        return TOO_LARGE
+    return INVALID if sample_ws_short or ws_short else OK
+
+
 def decode_step_batch(cfg: dict, batch=1, tensors_ok=True, lens_ok=True, pool_ok=True, pool_dims_bad=False,
                       batch_weights_ok=True, n_slots=1, capacity=0, slots=(0,), slot_lens=None, tokens=(0,),
                       pos=(0,), n_steps=1, logits=False, len_logits=0, len_tokens=None, hidden=False, len_hidden=0,

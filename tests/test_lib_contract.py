@@ -545,3 +545,45 @@ def test_q8_decode_model_lengths():
     assert call() == contract.decode_step(kw, token=40) == 572
     for bad in ((0, 0), (1, 6), (1, 3), "out", "emb"):
         assert call(bad) == contract.decode_step(kw, lens_ok=False) == 576, bad
+
+
+@no_gpu
+def test_decode_steps_sampled_refusals():
+    import numpy as np
+    kw = _cfg_kwargs()
+    cfg = llmk.make_config(**kw)
+    d, qd, kvd, F, V, L = 16, 16, 8, 24, 40, 2
+    lens = [d * qd, d * kvd, d * kvd, qd * d, d * F, d * F, F * d, d, d]
+    FA = 0x10000
+    arr = (llmk.Tensor * (L * 9))()
+    for l in range(L):
+        for t in range(9):
+            arr[l * 9 + t] = llmk.Tensor(FA, lens[t])
+    m = llmk.ModelStruct(llmk.Tensor(FA, V * d), llmk.Tensor(FA, V * d), llmk.Tensor(FA, d), llmk.Tensor(FA, 64 * 4),
+                         arr)
+    ws_need = llmk.decode_workspace_bytes(cfg, 1)
+
+    def call(n=4, token=0, draws=True, len_draws=None, T=1.0, k=0, p=1.0, sws=True, len_sws=1 << 20, ws_len=None):
+        ks = (ctypes.c_void_p * L)(FA, FA)
+        sl = np.zeros(2, np.int64)
+        ps = llmk.PoolStruct(ks, ks, L, 2, 32, 2, 4, 0, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        return llmk.lib.llmk_decode_steps_sampled(ctypes.byref(cfg), ctypes.byref(m), ctypes.byref(ps), 0, token, 0, n,
+                                                  T, k, p, FA if draws else None, n if len_draws is None else len_draws,
+                                                  FA, n, FA, ws_need if ws_len is None else ws_len,
+                                                  FA if sws else None, len_sws, None)
+    base = dict(n_slots=2, capacity=32, slot=0, slot_len=0, token=0, pos=0)
+    cases = [(dict(draws=False), dict(draws=False)), (dict(token=40), dict(token=40)), (dict(n=0), dict(n_steps=0)),
+             (dict(n=40), dict(n_steps=40)), (dict(len_draws=3), dict(len_draws=3)), (dict(T=-1.0), dict(temperature=-1.0)),
+             (dict(T=float("nan")), dict(temperature=float("nan"))), (dict(p=0.0), dict(top_p=0.0)),
+             (dict(p=1.5), dict(top_p=1.5)), (dict(ws_len=ws_need - 1), dict(ws_short=True))]
+    for call_kw, exp_kw in cases:
+        e = dict(base)
+        e.update(exp_kw)
+        n = e.pop("n_steps", 4)
+        exp = contract.decode_steps_sampled(kw, n_steps=n, **e)
+        assert exp != contract.OK, call_kw
+        assert call(**call_kw) == exp, (call_kw, exp)
+    # a 40-entry vocabulary takes the one-workgroup sampler, which needs no workspace (sample_ws may be NULL);
+    # the sampler-workspace refusal is checked on a vocabulary that needs one
+    assert llmk.sample_workspace_bytes(1, V, 1.0, 0) == 0
+    assert llmk.sample_workspace_bytes(1, 128256, 1.0, 50) > 0
