@@ -313,6 +313,9 @@ def main() -> int:
     ap.add_argument("--prefill-shape", choices=("q06", "l8b"), default="q06",
                     help="the prefill workload's shape: Qwen3-0.6B (the 2,048-token prefix workload) or Llama-3-8B")
     ap.add_argument("--cpu-prefill-tokens", type=int, default=24, help="oracle tokens in the prefill CPU baseline")
+    ap.add_argument("--sample", type=lambda v: tuple(float(x) for x in v.split(",")), default=None,
+                    metavar="T,K,P", help="batch-1 workloads: sample every step (temperature, top-k, top-p) inside "
+                                         "the captured loop instead of taking the greedy token")
     ap.add_argument("--step-path", choices=("auto", "per-op", "persistent"), default="auto",
                     help="the decode step's form: the library's choice (default), one kernel per operation, or "
                          "the persistent one-kernel step")
@@ -372,12 +375,21 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"resident in HBM after {time.time() - t_start:.1f} s; step form: {'persistent' if persistent else 'per-op'}")
 
+    if args.sample:
+        s_t, s_k, s_p = args.sample[0], int(args.sample[1]), args.sample[2]
+        draws = torch.from_numpy(synth.draws((max_steps_per_call,), seed=5, stream=31)).cuda()
+        sample_ws = llmk.workspace(max(llmk.sample_workspace_bytes(1, s.vocab, s_t, s_k), 16))
+
     def run(n: int, out) -> None:
         done = 0
         while done < n:
             k = min(max_steps_per_call, n - done)
             pool.slot_len[0] = N_PRE
-            st = dec.steps(first, N_PRE, k, out[done:done + k])
+            if args.sample:
+                st = llmk.decode_steps_sampled(cfg, model, pool, 0, first, N_PRE, k, s_t, s_k, s_p, draws[:k],
+                                               out[done:done + k], dec.ws, sample_ws)
+            else:
+                st = dec.steps(first, N_PRE, k, out[done:done + k])
             if st != llmk.OK:
                 raise RuntimeError(f"decode_steps: {st} {llmk.status_name(st)}")
             done += k
@@ -466,8 +478,13 @@ def main() -> int:
         "kernel_sum_ms_per_step": kernel_sum_ms,
         "first_tokens": tokens[:8],
     }
+    if args.sample:
+        result["config"]["sampling"] = {"temperature": s_t, "top_k": s_k, "top_p": s_p,
+                                        "draws": "seeded uniforms, one per step"}
 
-    if not args.no_cpu_baseline:
+    if args.sample and not args.no_cpu_baseline:
+        log("the CPU baseline runs the greedy workload; skipped for a sampled run")
+    if not args.no_cpu_baseline and not args.sample:
         import oracle
         n = args.cpu_steps
         log(f"oracle baseline: {n} steps on the host cores")
