@@ -175,16 +175,35 @@ __global__ __launch_bounds__(Q8_THREADS) void rowdot_q8_kernel(const RowdotParam
     if (rgi == 0 && lane == 0) ss_lds[kseg] = ss;
   }
 
+  // The R x NACC dots of a batch reduce across the wave together: each halving step trades half of a lane's
+  // values with the partner lane, so M values take M - 1 + log2(64 / M) shuffles instead of 6 M; lane l ends
+  // with the total of value j(l) = sum over steps of (l & o ? h : 0), held by the lanes l % (64 / M) == 0.
+  constexpr int M = R * NACC;
+  constexpr int SPAN = 64 / M;
 #define Q8_CONSUME(BUF, SB, RB)                                                                       \
-  _Pragma("unroll") for (int rr = 0; rr < R; ++rr) {                                                  \
-    _Pragma("unroll") for (int m = 0; m < NACC; ++m) {                                                \
-      float dot = 0.0f;                                                                               \
-      _Pragma("unroll") for (int pp = 0; pp < NP; ++pp)                                               \
-        dot = fmaf(SB[m][rr][pp], q8_chunk_dot(BUF[m][rr][pp], xr[pp]) - xs[pp], dot);                \
-      dot = wave_sum(dot);                                                                            \
-      const int64_t row = (RB) + rr;                                                                  \
-      if (lane == 0 && row < r1) part_lds[row - r0][kseg][m] = dot;                                   \
+  {                                                                                                   \
+    float v[M];                                                                                       \
+    _Pragma("unroll") for (int rr = 0; rr < R; ++rr) {                                                \
+      _Pragma("unroll") for (int m = 0; m < NACC; ++m) {                                              \
+        float dot = 0.0f;                                                                             \
+        _Pragma("unroll") for (int pp = 0; pp < NP; ++pp)                                             \
+          dot = fmaf(SB[m][rr][pp], q8_chunk_dot(BUF[m][rr][pp], xr[pp]) - xs[pp], dot);              \
+        v[rr * NACC + m] = dot;                                                                       \
+      }                                                                                               \
     }                                                                                                 \
+    int j = 0;                                                                                        \
+    _Pragma("unroll") for (int h = M / 2, o = 32; h >= 1; h /= 2, o /= 2) {                           \
+      const bool upper = (lane & o) != 0;                                                             \
+      j += upper ? h : 0;                                                                             \
+      _Pragma("unroll") for (int i = 0; i < h; ++i) {                                                 \
+        const float send = upper ? v[i] : v[i + h];                                                   \
+        const float keep = upper ? v[i + h] : v[i];                                                   \
+        v[i] = keep + __shfl_xor(send, o, 64);                                                        \
+      }                                                                                               \
+    }                                                                                                 \
+    _Pragma("unroll") for (int o = SPAN / 2; o >= 1; o /= 2) v[0] += __shfl_xor(v[0], o, 64);         \
+    const int64_t row = (RB) + j / NACC;                                                              \
+    if ((lane & (SPAN - 1)) == 0 && row < r1) part_lds[row - r0][kseg][j % NACC] = v[0];              \
   }
 
   if (rb < r1) {
