@@ -8,8 +8,14 @@ embedding, 32 layers of norm + q|k|v + RoPE + K/V append + attention + o + norm 
 down, final norm, output head and argmax. Inputs are resident in HBM before the timed region.
 
 Prints one JSON line: tokens/s, ms per step, algorithmic HBM GB/s of the whole step, the roofline of
-the dominant kernel (the gate|up GEMV, timed with HIP events on the stream it runs on), and the oracle's
-throughput on the host cores for a bounded sample of the same workload.
+the dominant kernel (the persistent step kernel, or the gate|up GEMV of the per-operation form, timed with
+HIP events on the stream it runs on), and the oracle's throughput on the host cores for a bounded sample of
+the same workload.
+
+Other workloads (--workload): batched (64 sequences of ragged contexts a step), prefill (a 2,048-token
+prompt, Qwen3-0.6B or Llama-3-8B shape), q8 (the batch-1 workload over int8 weight packs); --sample T,K,P
+samples every batch-1 step inside the captured loop; --copy-probe, --sample-probe and --prefill-probe are
+short runs for counters and traces.
 """
 from __future__ import annotations
 
