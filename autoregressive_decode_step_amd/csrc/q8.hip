@@ -1,6 +1,7 @@
 // int8 weights for the decode step on gfx950: a per-group quantizer and the row-dot GEMV over q8 packs.
 //
-// Format (designed here; the pages name int8 weight packs as the next bandwidth lever without fixing one):
+// Format (the library's own: [xpu] "1. CausalLM: the forward path" has decode read packed int8 weights but
+// gives no layout):
 // each output row of a [rows][K] projection is cut into groups of Q8_GROUP = 128 inputs; a group keeps one
 // fp32 scale s = max|w| / 127 and int8 codes q = rint(w / s) (0 for an all-zero group), so w ~ q * s with
 // |w - q s| <= s / 2. A pack stores every code of the matrix first, then every scale, both row-major, so a

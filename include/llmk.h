@@ -423,9 +423,9 @@ int32_t llmk_prefill_profiled(const llmk_config* cfg, const llmk_model* model, l
 /* ------------------------------------------------------------------------- */
 /* int8 weight packs (LLMK_Q8)                                                */
 /* ------------------------------------------------------------------------- */
-/* The pages name int8 weights and q8_K packs as the decode path's next saving on streamed bytes ([xpu]
- * "1. CausalLM: the forward path"; [llmk] "How this composes into a decode step") without fixing a format;
- * this one is the library's own. A q8 pack holds a rows x cols matrix, output-major (each row is one
+/* Decode reads packed int8 weights in [xpu] "1. CausalLM: the forward path" (and an int8 GPU kernel stands
+ * beside the CPU reference in [llmk] "How this composes into a decode step"), with no layout given; this
+ * format is the library's own. A q8 pack holds a rows x cols matrix, output-major (each row is one
  * output's weights over cols inputs), in groups of LLMK_Q8_GROUP consecutive inputs of a row: per group the
  * fp32 scale s = max|w| / 127 and int8 codes q = rint(w / s) (ties to even; 0 for an all-zero group),
  * decided in fp32; the weight is q * s, |w - q s| <= s / 2. Bytes: rows*cols codes row-major, then
