@@ -29,6 +29,8 @@ def test_grid_values_round_trip_exactly():
     q, s = quant.quantize(w)
     assert np.array_equal(q.astype(np.int64), k)
     assert np.array_equal(quant.dequantize(q, s), w.astype(np.float64))
+    # on the grid every q * s is exact in fp32 too, so the fp32 form of the weights agrees bit for bit
+    assert np.array_equal(quant.dequantize(q, s, np.float32), w)
 
 
 def test_error_within_half_a_step():
@@ -101,6 +103,9 @@ def test_model_projections_group_along_their_input():
             L[k] = np.ascontiguousarray(grid_rows(rng, n_out, n_in)[0].T)
     W["out"] = grid_rows(rng, s0.vocab, s0.d)[0]
     Q = quant.quantized_weights(W)
+    Q32 = quant.quantized_weights(W, f64=False)
+    assert all(np.array_equal(M[k], M32[k].astype(np.float64)) for M, M32 in zip(Q["layers"], Q32["layers"])
+               for k in ("wq", "wk", "wv", "wo", "gate", "up", "down"))
     for L, M in zip(W["layers"], Q["layers"]):
         for k in ("wq", "wk", "wv", "wo", "gate", "up", "down"):
             assert np.array_equal(M[k], L[k].astype(np.float64)), k
