@@ -15,15 +15,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libllmk.so")
-# another build of the same library (same exported interface) may be named explicitly
-LIB_PATH = os.environ.get("LLMK_LIBRARY") or LIB_PATH
 
 OK = 560
+DEVICE_ERROR = 579
 F32, BF16, Q8 = 0, 1, 2
 Q8_GROUP = 128
 ROPE_HALF_SPLIT, ROPE_INTERLEAVED = 0, 1
 W_IN_OUT, W_OUT_IN = 0, 1
 STEP_AUTO, STEP_PER_OP, STEP_PERSISTENT = 0, 1, 2
+TEST_WAIT_GIVE_UP = 1
 WQ, WK, WV, WO, WGATE, WUP, WDOWN, GATTN, GFFN = range(9)
 LAYER_TENSORS = 9
 MAX_DIM = 1 << 24
@@ -47,7 +47,8 @@ class Config(ctypes.Structure):
     """llmk_config"""
     _fields_ = [("vocab", _i64), ("d", _i64), ("n_layer", _i64), ("n_head", _i64), ("n_kv", _i64),
                 ("head_dim", _i64), ("hidden", _i64), ("max_seq", _i64), ("eps", _f64), ("rope_base", _f64),
-                ("rope_layout", _i32), ("w_dtype", _i32), ("kv_dtype", _i32), ("w_layout", _i32), ("step_path", _i32)]
+                ("rope_layout", _i32), ("w_dtype", _i32), ("kv_dtype", _i32), ("w_layout", _i32), ("step_path", _i32),
+                ("test_flags", _i32)]
 
 
 class Tensor(ctypes.Structure):
@@ -65,7 +66,8 @@ class PoolStruct(ctypes.Structure):
     """llmk_kv_pool"""
     _fields_ = [("k", ctypes.POINTER(_p)), ("v", ctypes.POINTER(_p)), ("n_layer", _i64), ("n_slots", _i64),
                 ("capacity", _i64), ("n_kv", _i64), ("head_dim", _i64), ("dtype", _i32),
-                ("slot_len_h", ctypes.POINTER(_i64))]
+                ("slot_len_h", ctypes.POINTER(_i64)), ("len_k_h", ctypes.POINTER(_i64)),
+                ("len_v_h", ctypes.POINTER(_i64))]
 
 
 _SIGS = {
@@ -81,10 +83,14 @@ _SIGS = {
     "llmk_add_rmsnorm": ([_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _f32, _p, _i64, _p], _i32),
     "llmk_silu_mul": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p], _i32),
     "llmk_rope_table_init": ([_p, _i64, _i64, _i64, _f64, _p], _i32),
-    "llmk_rope": ([_p, _i64, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p, _i64, _i64, _i32, _p], _i32),
-    "llmk_kv_append": ([_p, _i64, _i32, _i64, _i64, _p, _i64, _i64, ctypes.POINTER(_i64), _p], _i32),
+    "llmk_rope": ([_p, _i64, _p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32, _p], _i32),
+    "llmk_kv_append_flat": ([_p, _i64, _i32, _i64, _i64, _p, _i64, _i64, ctypes.POINTER(_i64), _p], _i32),
     "llmk_gqa_attend_workspace_bytes": ([_i64, _i64, _i64], _i64),
-    "llmk_gqa_attend": ([_p, _i64, _p, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_gqa_attend_flat": ([_p, _i64, _p, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
+    "llmk_kv_pool_init": ([ctypes.POINTER(PoolStruct)], _i32),
+    "llmk_kv_append": ([ctypes.POINTER(PoolStruct), _i64, _i64, _i32, _i64, _p, _i64, _i64, ctypes.POINTER(_i64),
+                        ctypes.POINTER(_i64), _p], _i32),
+    "llmk_gqa_attend": ([_p, _i64, ctypes.POINTER(PoolStruct), _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_argmax_workspace_bytes": ([_i64, _i64], _i64),
     "llmk_argmax": ([_p, _i64, _i64, _i64, _p, _p, _p, _i64, _p], _i32),
     "llmk_sample_workspace_bytes": ([_i64, _i64, _f32, _i32], _i64),
@@ -228,17 +234,18 @@ def rope_table_init(table, max_pos, head_dim, base, stream=None) -> int:
     return lib.llmk_rope_table_init(_ptr(table), _len(table), max_pos, head_dim, base, _stream(stream))
 
 
-def rope(q, k, rows, n_q_heads, n_k_heads, head_dim, pos0, table, max_pos, layout, stream=None) -> int:
-    return lib.llmk_rope(_ptr(q), _len(q), _ptr(k), _len(k), rows, n_q_heads, n_k_heads, head_dim, pos0, _ptr(table),
-                         _len(table), max_pos, layout, _stream(stream))
+def rope(q, k, rows, n_q_heads, n_k_heads, head_dim, pos, table, max_pos, layout, stream=None) -> int:
+    """In-place RoPE; pos is a device int32 tensor [rows] (row r at position pos[r])."""
+    return lib.llmk_rope(_ptr(q), _len(q), _ptr(k), _len(k), rows, n_q_heads, n_k_heads, head_dim, _ptr(pos),
+                         _len(pos), _ptr(table), _len(table), max_pos, layout, _stream(stream))
 
 
-def kv_append(cache, cache_len, len_cache, new_vals, n_new=None, stream=None):
+def kv_append_flat(cache, cache_len, len_cache, new_vals, n_new=None, stream=None):
     """Returns (status, new_len)."""
     n_new = _len(new_vals) if n_new is None else n_new
     out = _i64(-1)
-    st = lib.llmk_kv_append(_ptr(cache), _len(cache), _dtype_code(cache), cache_len, len_cache, _ptr(new_vals),
-                            _len(new_vals), n_new, ctypes.byref(out), _stream(stream))
+    st = lib.llmk_kv_append_flat(_ptr(cache), _len(cache), _dtype_code(cache), cache_len, len_cache, _ptr(new_vals),
+                                 _len(new_vals), n_new, ctypes.byref(out), _stream(stream))
     return st, out.value
 
 
@@ -246,10 +253,10 @@ def gqa_attend_workspace_bytes(ctx_len, n_head, head_dim) -> int:
     return lib.llmk_gqa_attend_workspace_bytes(ctx_len, n_head, head_dim)
 
 
-def gqa_attend(q, k_cache, v_cache, ctx_len, n_head, n_kv, head_dim, out, ws, stream=None) -> int:
-    return lib.llmk_gqa_attend(_ptr(q), _len(q), _ptr(k_cache), _ptr(v_cache), _len(k_cache), _dtype_code(k_cache),
-                               ctx_len, n_head, n_kv, head_dim, _ptr(out), _len(out), _ptr(ws), _len(ws),
-                               _stream(stream))
+def gqa_attend_flat(q, k_cache, v_cache, ctx_len, n_head, n_kv, head_dim, out, ws, stream=None) -> int:
+    return lib.llmk_gqa_attend_flat(_ptr(q), _len(q), _ptr(k_cache), _ptr(v_cache), _len(k_cache),
+                                    _dtype_code(k_cache), ctx_len, n_head, n_kv, head_dim, _ptr(out), _len(out),
+                                    _ptr(ws), _len(ws), _stream(stream))
 
 
 def argmax_workspace_bytes(rows, n) -> int:
@@ -275,9 +282,10 @@ def sample(logits, rows, n, temperature, top_k, top_p, u, token, ws=None, stream
 # ---------------------------------------------------------------------------------------------------------
 
 def make_config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4,
-                rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16, w_layout=W_IN_OUT, step_path=0) -> Config:
+                rope_layout=ROPE_HALF_SPLIT, w_dtype=BF16, kv_dtype=BF16, w_layout=W_IN_OUT, step_path=0,
+                test_flags=0) -> Config:
     return Config(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps, rope_base, rope_layout, w_dtype,
-                  kv_dtype, w_layout, step_path)
+                  kv_dtype, w_layout, step_path, test_flags)
 
 
 def q8_pack_bytes(rows, cols) -> int:
@@ -329,17 +337,51 @@ class KVPool:
         else:
             self.k, self.v = tensors
         self.slot_len = np.zeros(n_slots, dtype=np.int64)
+        # flat-cache fill of every (layer, slot) K and V buffer, in elements
+        self.len_k = np.zeros((n_layer, n_slots), dtype=np.int64)
+        self.len_v = np.zeros((n_layer, n_slots), dtype=np.int64)
         self._kp = (_p * n_layer)(*[_ptr(t) for t in self.k])
         self._vp = (_p * n_layer)(*[_ptr(t) for t in self.v])
         self.struct = PoolStruct(self._kp, self._vp, n_layer, n_slots, capacity, n_kv, head_dim, dtype,
-                                 self.slot_len.ctypes.data_as(ctypes.POINTER(_i64)))
+                                 self.slot_len.ctypes.data_as(ctypes.POINTER(_i64)),
+                                 self.len_k.ctypes.data_as(ctypes.POINTER(_i64)),
+                                 self.len_v.ctypes.data_as(ctypes.POINTER(_i64)))
         self.capacity, self.n_kv, self.head_dim, self.n_slots = capacity, n_kv, head_dim, n_slots
+        self.n_layer, self.dtype = n_layer, dtype
+        check(lib.llmk_kv_pool_init(ctypes.byref(self.struct)), "kv_pool_init")
+
+    def set_len(self, slot: int, n_pos: int) -> None:
+        """Record that `slot` holds n_pos positions (its K/V written by the caller, e.g. a seeded prefix)."""
+        self.slot_len[slot] = n_pos
+        self.len_k[:, slot] = n_pos * self.n_kv * self.head_dim
+        self.len_v[:, slot] = n_pos * self.n_kv * self.head_dim
 
     def slot_view(self, layer: int, slot: int, which: str = "k"):
         """[capacity][n_kv][head_dim] view of one slot of one layer's K or V buffer."""
         t = (self.k if which == "k" else self.v)[layer]
         plane = self.capacity * self.n_kv * self.head_dim
         return t[slot * plane:(slot + 1) * plane].view(self.capacity, self.n_kv, self.head_dim)
+
+
+def kv_pool_init(pool: KVPool) -> int:
+    """Validate the pool descriptor and mark every slot empty (its records set to 0)."""
+    return lib.llmk_kv_pool_init(ctypes.byref(pool.struct))
+
+
+def kv_append(pool: KVPool, layer, slot, which, cache_len, new_vals, n_new=None, stream=None):
+    """Append new_vals (device fp32) to buffer `which` (0: K, 1: V) of (layer, slot) of the pool.
+    Returns (status, new_len, elem_offset)."""
+    n_new = _len(new_vals) if n_new is None else n_new
+    nl, off = _i64(-1), _i64(-1)
+    st = lib.llmk_kv_append(ctypes.byref(pool.struct), layer, slot, which, cache_len, _ptr(new_vals), _len(new_vals),
+                            n_new, ctypes.byref(nl), ctypes.byref(off), _stream(stream))
+    return st, nl.value, off.value
+
+
+def gqa_attend(q, pool: KVPool, layer, slot, ctx_len, n_head, out, ws, stream=None) -> int:
+    """Attention of q over positions [0, ctx_len) of (layer, slot) of the pool."""
+    return lib.llmk_gqa_attend(_ptr(q), _len(q), ctypes.byref(pool.struct), layer, slot, ctx_len, n_head, _ptr(out),
+                               _len(out), _ptr(ws), _len(ws), _stream(stream))
 
 
 def kv_slot_offset(pool: KVPool, slot, pos, kv_head):

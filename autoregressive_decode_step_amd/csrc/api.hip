@@ -99,6 +99,7 @@ int32_t config_check(const llmk_config* c) {
   if (c->w_layout != LLMK_W_IN_OUT && c->w_layout != LLMK_W_OUT_IN) return LLMK_INVALID_ARGUMENT;
   if (c->step_path != LLMK_STEP_AUTO && c->step_path != LLMK_STEP_PER_OP && c->step_path != LLMK_STEP_PERSISTENT)
     return LLMK_INVALID_ARGUMENT;
+  if (c->test_flags != 0 && c->test_flags != LLMK_TEST_WAIT_GIVE_UP) return LLMK_INVALID_ARGUMENT;
   if (!(c->eps > 0) || !isfinite(c->eps) || !(c->rope_base > 1.0) || !isfinite(c->rope_base))
     return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({c->vocab, c->d, c->n_layer, c->n_head, c->n_kv, c->head_dim, c->hidden, c->max_seq});
@@ -313,6 +314,17 @@ bool weights_aligned(const llmk_config* c, const llmk_model* m) {
     for (int t = 0; t < LLMK_WDOWN + 1; ++t)
       if (!aligned16(layer_t(m, l, t).ptr)) return false;
   return true;
+}
+
+// A decode call advanced `slot` to n_pos positions: the slot record, and the flat-cache records of every
+// layer's K and V buffer where the pool keeps them.
+void pool_advance(llmk_kv_pool* p, int64_t slot, int64_t n_pos) {
+  p->slot_len_h[slot] = n_pos;
+  const int64_t row = p->n_kv * p->head_dim;
+  for (int64_t l = 0; l < p->n_layer; ++l) {
+    if (p->len_k_h) p->len_k_h[l * p->n_slots + slot] = n_pos * row;
+    if (p->len_v_h) p->len_v_h[l * p->n_slots + slot] = n_pos * row;
+  }
 }
 
 int32_t pool_check(const llmk_config* c, const llmk_kv_pool* p) {
@@ -607,6 +619,7 @@ StepParams step_params(const llmk_config* c, const llmk_model* m, const llmk_kv_
   p.head_cnt = D.step_cnt;
   p.err = D.step_err;
   p.token_out = token_out;
+  p.give_up = (c->test_flags & LLMK_TEST_WAIT_GIVE_UP) ? 1 : 0;
   return p;
 }
 
@@ -653,7 +666,7 @@ int32_t time_step_kernel(const llmk_config* cfg, const llmk_model* model, llmk_k
   if (e1) (void)hipEventDestroy(e1);
   if (cs) (void)hipStreamDestroy(cs);
   if (e != hipSuccess || err != 0) return LLMK_DEVICE_ERROR;
-  pool->slot_len_h[slot] = pos + 1;
+  pool_advance(pool, slot, pos + 1);
   *ms_per_launch_h = ms / (float)reps;
   return LLMK_OK;
 }
@@ -1301,9 +1314,10 @@ int32_t llmk_rope_table_init(float* table, int64_t len_table, int64_t max_pos, i
 }
 
 int32_t llmk_rope(float* q, int64_t len_q, float* k, int64_t len_k, int64_t rows, int64_t n_q_heads, int64_t n_k_heads,
-                  int64_t head_dim, int64_t pos0, const float* table, int64_t len_table, int64_t max_pos,
-                  int32_t layout, void* stream) {
-  if (!q || !table || (layout != LLMK_ROPE_HALF_SPLIT && layout != LLMK_ROPE_INTERLEAVED) || (!k && n_k_heads != 0))
+                  int64_t head_dim, const int32_t* pos, int64_t len_pos, const float* table, int64_t len_table,
+                  int64_t max_pos, int32_t layout, void* stream) {
+  if (!q || !table || !pos || (layout != LLMK_ROPE_HALF_SPLIT && layout != LLMK_ROPE_INTERLEAVED) ||
+      (!k && n_k_heads > 0))
     return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({rows, n_q_heads, head_dim, max_pos});
   if (st != LLMK_OK) return st;
@@ -1313,12 +1327,13 @@ int32_t llmk_rope(float* q, int64_t len_q, float* k, int64_t len_k, int64_t rows
   if (len_q != rows * n_q_heads * head_dim) return LLMK_A_LENGTH_MISMATCH;
   if (len_k != rows * n_k_heads * head_dim) return LLMK_B_LENGTH_MISMATCH;
   if (len_table != max_pos * head_dim) return LLMK_WEIGHT_LENGTH_MISMATCH;
-  if (pos0 < 0 || pos0 + rows > max_pos) return LLMK_POSITION_OUT_OF_RANGE;
-  return finish(rope_launch(q, k, rows, n_q_heads, n_k_heads, head_dim, pos0, table, layout, as_stream(stream)));
+  if (len_pos != rows) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  return finish(rope_launch(q, k, rows, n_q_heads, n_k_heads, head_dim, pos, max_pos, table, layout,
+                            as_stream(stream)));
 }
 
-int32_t llmk_kv_append(void* cache, int64_t capacity, int32_t dtype, int64_t cache_len, int64_t len_cache,
-                       const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h, void* stream) {
+int32_t llmk_kv_append_flat(void* cache, int64_t capacity, int32_t dtype, int64_t cache_len, int64_t len_cache,
+                            const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h, void* stream) {
   if (!cache || !new_vals || !is_dtype(dtype)) return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({capacity});
   if (st != LLMK_OK) return st;
@@ -1339,18 +1354,9 @@ int64_t llmk_gqa_attend_workspace_bytes(int64_t ctx_len, int64_t n_head, int64_t
   return c.off;
 }
 
-int32_t llmk_gqa_attend(const float* q, int64_t len_q, const void* k_cache, const void* v_cache, int64_t len_cache,
-                        int32_t kv_dtype, int64_t ctx_len, int64_t n_head, int64_t n_kv, int64_t head_dim, float* out,
-                        int64_t len_out, void* ws, int64_t len_ws, void* stream) {
-  if (!q || !k_cache || !v_cache || !out || !ws || !is_dtype(kv_dtype)) return LLMK_INVALID_ARGUMENT;
-  int32_t st = dims_check({ctx_len, n_head, n_kv, head_dim});
-  if (st != LLMK_OK) return st;
-  if (n_head % n_kv != 0 || n_head / n_kv > 8 || !attn_head_dim_ok(head_dim)) return LLMK_HEAD_SHAPE_INVALID;
-  if (len_q != n_head * head_dim) return LLMK_A_LENGTH_MISMATCH;
-  if (len_cache < ctx_len * n_kv * head_dim) return LLMK_B_LENGTH_MISMATCH;
-  if (len_out != n_head * head_dim) return LLMK_OUTPUT_LENGTH_MISMATCH;
-  if (len_ws < llmk_gqa_attend_workspace_bytes(ctx_len, n_head, head_dim)) return LLMK_INVALID_ARGUMENT;
-  if (!aligned16(k_cache) || !aligned16(v_cache)) return LLMK_INVALID_ARGUMENT;
+// the attention launch shared by llmk_gqa_attend_flat and llmk_gqa_attend (every check done)
+static int32_t gqa_attend_run(const float* q, const void* k_cache, const void* v_cache, int32_t kv_dtype, int64_t ctx_len,
+                              int64_t n_head, int64_t n_kv, int64_t head_dim, float* out, void* ws, void* stream) {
   AttnParams a{};
   a.q = q;
   a.k = k_cache;
@@ -1369,6 +1375,93 @@ int32_t llmk_gqa_attend(const float* q, int64_t len_q, const void* k_cache, cons
   hipError_t e = fill_u32_launch(a.counters, n_kv, 0u, as_stream(stream));
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   return finish(attn_launch(a, as_stream(stream)));
+}
+
+int32_t llmk_gqa_attend_flat(const float* q, int64_t len_q, const void* k_cache, const void* v_cache, int64_t len_cache,
+                             int32_t kv_dtype, int64_t ctx_len, int64_t n_head, int64_t n_kv, int64_t head_dim,
+                             float* out, int64_t len_out, void* ws, int64_t len_ws, void* stream) {
+  if (!q || !k_cache || !v_cache || !out || !ws || !is_dtype(kv_dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({ctx_len, n_head, n_kv, head_dim});
+  if (st != LLMK_OK) return st;
+  if (n_head % n_kv != 0 || n_head / n_kv > 8 || !attn_head_dim_ok(head_dim)) return LLMK_HEAD_SHAPE_INVALID;
+  if (len_q != n_head * head_dim) return LLMK_A_LENGTH_MISMATCH;
+  if (len_cache < ctx_len * n_kv * head_dim) return LLMK_B_LENGTH_MISMATCH;
+  if (len_out != n_head * head_dim) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (len_ws < llmk_gqa_attend_workspace_bytes(ctx_len, n_head, head_dim)) return LLMK_INVALID_ARGUMENT;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return LLMK_INVALID_ARGUMENT;
+  return gqa_attend_run(q, k_cache, v_cache, kv_dtype, ctx_len, n_head, n_kv, head_dim, out, ws, stream);
+}
+
+// A pool descriptor's own fields (no config to compare with): 578 / 561 / 564.
+static int32_t pool_fields_check(const llmk_kv_pool* p) {
+  if (!p || !p->k || !p->v || !p->slot_len_h || !is_dtype(p->dtype)) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({p->n_layer, p->n_slots, p->capacity, p->n_kv, p->head_dim});
+  if (st != LLMK_OK) return st;
+  for (int64_t l = 0; l < p->n_layer; ++l)
+    if (!p->k[l] || !p->v[l] || !aligned16(p->k[l]) || !aligned16(p->v[l])) return LLMK_INVALID_ARGUMENT;
+  return LLMK_OK;
+}
+
+int32_t llmk_kv_pool_init(llmk_kv_pool* pool) {
+  const int32_t st = pool_fields_check(pool);
+  if (st != LLMK_OK) return st;
+  for (int64_t s = 0; s < pool->n_slots; ++s) pool->slot_len_h[s] = 0;
+  for (int64_t i = 0; i < pool->n_layer * pool->n_slots; ++i) {
+    if (pool->len_k_h) pool->len_k_h[i] = 0;
+    if (pool->len_v_h) pool->len_v_h[i] = 0;
+  }
+  return LLMK_OK;
+}
+
+int32_t llmk_kv_append(llmk_kv_pool* pool, int64_t layer, int64_t slot, int32_t which, int64_t cache_len,
+                       const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h,
+                       int64_t* elem_offset_h, void* stream) {
+  if (!new_vals) return LLMK_INVALID_ARGUMENT;
+  int32_t st = pool_fields_check(pool);
+  if (st != LLMK_OK) return st;
+  if (!pool->len_k_h || !pool->len_v_h || (which != 0 && which != 1)) return LLMK_INVALID_ARGUMENT;
+  if (layer < 0 || layer >= pool->n_layer) return LLMK_INVALID_ARGUMENT;
+  if (cache_len < 0 || n_new < 1) return LLMK_EMPTY_DIMENSION;
+  if (cache_len > kMaxDim || n_new > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
+  if (slot < 0 || slot >= pool->n_slots) return LLMK_SLOT_OUT_OF_RANGE;
+  int64_t* rec = (which == 0 ? pool->len_k_h : pool->len_v_h) + layer * pool->n_slots + slot;
+  if (cache_len != *rec) return LLMK_CACHE_LENGTH_MISMATCH;
+  if (len_new != n_new) return LLMK_NEW_LENGTH_MISMATCH;
+  const int64_t plane = pool->capacity * pool->n_kv * pool->head_dim;
+  if (cache_len + n_new > plane) return LLMK_CACHE_CAPACITY_EXCEEDED;
+  void* buf = which == 0 ? pool->k[layer] : pool->v[layer];
+  const int64_t off = slot * plane + cache_len;
+  st = finish(kv_append_launch(buf, pool->dtype == LLMK_BF16, off, new_vals, n_new, as_stream(stream)));
+  if (st != LLMK_OK) return st;
+  *rec = cache_len + n_new;
+  if (new_len_h) *new_len_h = *rec;
+  if (elem_offset_h) *elem_offset_h = off;
+  return LLMK_OK;
+}
+
+int32_t llmk_gqa_attend(const float* q, int64_t len_q, const llmk_kv_pool* pool, int64_t layer, int64_t slot,
+                        int64_t ctx_len, int64_t n_head, float* out, int64_t len_out, void* ws, int64_t len_ws,
+                        void* stream) {
+  if (!q || !out || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = pool_fields_check(pool);
+  if (st != LLMK_OK) return st;
+  if (layer < 0 || layer >= pool->n_layer) return LLMK_INVALID_ARGUMENT;
+  st = dims_check({ctx_len, n_head});
+  if (st != LLMK_OK) return st;
+  if (slot < 0 || slot >= pool->n_slots) return LLMK_SLOT_OUT_OF_RANGE;
+  const int64_t n_kv = pool->n_kv, hd = pool->head_dim;
+  if (n_head % n_kv != 0 || n_head / n_kv > 8 || !attn_head_dim_ok(hd)) return LLMK_HEAD_SHAPE_INVALID;
+  if (len_q != n_head * hd) return LLMK_A_LENGTH_MISMATCH;
+  if (len_out != n_head * hd) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (ctx_len > pool->capacity) return LLMK_POSITION_OUT_OF_RANGE;
+  const int64_t need = ctx_len * n_kv * hd, rec = layer * pool->n_slots + slot;
+  if ((pool->len_k_h && pool->len_k_h[rec] < need) || (pool->len_v_h && pool->len_v_h[rec] < need))
+    return LLMK_CACHE_LENGTH_MISMATCH;
+  if (len_ws < llmk_gqa_attend_workspace_bytes(ctx_len, n_head, hd)) return LLMK_INVALID_ARGUMENT;
+  const int64_t esz = dtype_size(pool->dtype), base = slot * pool->capacity * n_kv * hd * esz;
+  if (base % 16 != 0) return LLMK_INVALID_ARGUMENT;   // the kernel's 16-byte loads need the slot aligned
+  return gqa_attend_run(q, static_cast<const char*>(pool->k[layer]) + base, static_cast<const char*>(pool->v[layer]) + base,
+                        pool->dtype, ctx_len, n_head, n_kv, hd, out, ws, stream);
 }
 
 int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n) {
@@ -1475,13 +1568,23 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
     if (e == hipSuccess)
       e = step_launch(step_params(cfg, model, pool, slot, D, nwg, logits, hidden, token_out),
                       cfg->kv_dtype == LLMK_BF16, s);
+    // a bounded wait that gave up leaves the error flag set: wait for the step and read it (not possible
+    // while the stream is being captured)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (e == hipSuccess) e = hipStreamIsCapturing(s, &cap);
+    if (e == hipSuccess && cap == hipStreamCaptureStatusNone) {
+      int32_t err = 0;
+      e = hipMemcpyAsync(&err, D.step_err, sizeof(err), hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e == hipSuccess && err != 0) return LLMK_DEVICE_ERROR;
+    }
   } else {
     e = fill_u32_launch(D.counters, counters_total(cfg, D), 0u, s);
     if (e == hipSuccess) e = set_state_launch(D.state, (int32_t)token, (int32_t)pos, s);
     if (e == hipSuccess) e = enqueue_step(cfg, model, pool, slot, D, logits, token_out, hidden, s);
   }
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
-  pool->slot_len_h[slot] = pos + 1;
+  pool_advance(pool, slot, pos + 1);
   return LLMK_OK;
 }
 
@@ -1585,7 +1688,7 @@ static int32_t decode_steps_run(const llmk_config* cfg, const llmk_model* model,
   if (graph) (void)hipGraphDestroy(graph);
   if (cs) (void)hipStreamDestroy(cs);
   if (e != hipSuccess || err != 0) return LLMK_DEVICE_ERROR;
-  pool->slot_len_h[slot] = pos0 + n_steps;
+  pool_advance(pool, slot, pos0 + n_steps);
   return LLMK_OK;
 }
 
@@ -1608,7 +1711,7 @@ int32_t llmk_decode_step_batch(const llmk_config* cfg, const llmk_model* model, 
   if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
   if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, logits, tokens_out, hidden, s);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
-  for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos_h[r] + 1;
+  for (int64_t r = 0; r < batch; ++r) pool_advance(pool, slots_h[r], pos_h[r] + 1);
   return LLMK_OK;
 }
 
@@ -1676,7 +1779,7 @@ int32_t prefill_run(const llmk_config* cfg, const llmk_model* model, llmk_kv_poo
                          hipMemcpyDeviceToDevice, s);
   }
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
-  pool->slot_len_h[slot] = pos0 + n;
+  pool_advance(pool, slot, pos0 + n);
   return LLMK_OK;
 }
 
@@ -1753,7 +1856,7 @@ int32_t llmk_decode_steps_batch(const llmk_config* cfg, const llmk_model* model,
   if (graph) (void)hipGraphDestroy(graph);
   if (cs) (void)hipStreamDestroy(cs);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
-  for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos0_h[r] + n_steps;
+  for (int64_t r = 0; r < batch; ++r) pool_advance(pool, slots_h[r], pos0_h[r] + n_steps);
   return LLMK_OK;
 }
 
@@ -1789,7 +1892,7 @@ int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* mode
     if (ev[i]) (void)hipEventDestroy(ev[i]);
   delete[] ev;
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
-  pool->slot_len_h[slot] = pos + 1;
+  pool_advance(pool, slot, pos + 1);
   return LLMK_OK;
 }
 
@@ -1862,7 +1965,7 @@ int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model,
   if (e1) (void)hipEventDestroy(e1);
   if (cs) (void)hipStreamDestroy(cs);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
-  pool->slot_len_h[slot] = pos + 1;
+  pool_advance(pool, slot, pos + 1);
   *ms_per_launch_h = ms / (float)(reps * per_rep);
   return LLMK_OK;
 }
@@ -1924,7 +2027,7 @@ int32_t llmk_decode_batch_kernel_time(const llmk_config* cfg, const llmk_model* 
   if (e1) (void)hipEventDestroy(e1);
   if (cs) (void)hipStreamDestroy(cs);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
-  for (int64_t r = 0; r < batch; ++r) pool->slot_len_h[slots_h[r]] = pos_h[r] + 1;
+  for (int64_t r = 0; r < batch; ++r) pool_advance(pool, slots_h[r], pos_h[r] + 1);
   *ms_per_launch_h = ms / (float)(reps * per_rep);
   return LLMK_OK;
 }
@@ -1942,6 +2045,7 @@ int32_t llmk_quantize_q8(const void* w, int64_t len_w, int32_t w_dtype, int64_t 
   if (cols % Q8_GROUP != 0) return LLMK_HEAD_SHAPE_INVALID;
   if (len_w != rows * cols) return LLMK_WEIGHT_LENGTH_MISMATCH;
   if (len_pack != q8_pack_bytes(rows, cols)) return LLMK_OUTPUT_LENGTH_MISMATCH;
+  if (!aligned16(w) || !aligned16(pack)) return LLMK_INVALID_ARGUMENT;
   return finish(q8_quantize_launch(w, w_dtype == LLMK_BF16, rows, cols, pack, as_stream(stream)));
 }
 

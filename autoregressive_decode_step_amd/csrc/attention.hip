@@ -1,7 +1,5 @@
 // Split-context grouped-query decode attention for gfx950: the kernel and its plan (the workgroup body
 // is in attn_block.h).
-#include <stdlib.h>
-
 #include <algorithm>
 
 #include "attn_block.h"
@@ -22,8 +20,7 @@ static int tile_rows(int kv_is_bf16, int hd) {
 void attn_plan(AttnParams& p, int64_t max_ctx, int64_t min_tiles_per_part) {
   p.chunk = tile_rows(p.kv_is_bf16, p.hd);
   const int64_t n_sub = (max_ctx + p.chunk - 1) / p.chunk;
-  const char* env = getenv("LLMK_ATTN_PARTS");    // measurement sweeps only
-  int64_t target = (env && *env) ? atoi(env) : (n_sub + min_tiles_per_part - 1) / std::max<int64_t>(1, min_tiles_per_part);
+  int64_t target = (n_sub + min_tiles_per_part - 1) / std::max<int64_t>(1, min_tiles_per_part);
   if (target < 1) target = 1;
   if (target > ATTN_MAX_PARTS) target = ATTN_MAX_PARTS;
   int64_t spw = (n_sub + target - 1) / target;

@@ -89,29 +89,31 @@ hipError_t rope_table_launch(float* table, int64_t max_pos, int64_t hd, double b
   return hipGetLastError();
 }
 
-// ---- RoPE on q and k rows, row r at position pos0 + r ---------------------------------------------------
+// ---- RoPE on q and k rows, row r at the device position pos[r] --------------------------------------------
 
-__global__ void rope_kernel(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, int64_t pos0,
-                            const float* table, int layout) {
+__global__ void rope_kernel(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, const int32_t* pos,
+                            int64_t max_pos, const float* table, int layout) {
   const int64_t half = hd / 2, per_row = (nq + nk) * half, n = rows * per_row;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / per_row, rem = i % per_row;
     const int64_t head = rem / half, j = rem % half;
+    const int64_t p = pos[r];
+    if (p < 0 || p >= max_pos) continue;   // no table row: the row stays as it is
     float* v = head < nq ? q + (r * nq + head) * hd : k + (r * nk + (head - nq)) * hd;
     const int64_t ia = layout == 0 ? j : 2 * j;
     const int64_t ib = layout == 0 ? j + half : 2 * j + 1;
-    const float cs = table[((pos0 + r) * half + j) * 2 + 0];
-    const float sn = table[((pos0 + r) * half + j) * 2 + 1];
+    const float cs = table[(p * half + j) * 2 + 0];
+    const float sn = table[(p * half + j) * 2 + 1];
     const float a = v[ia], b = v[ib];
     v[ia] = a * cs - b * sn;
     v[ib] = a * sn + b * cs;
   }
 }
 
-hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, int64_t pos0,
-                       const float* table, int layout, hipStream_t s) {
+hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, const int32_t* pos,
+                       int64_t max_pos, const float* table, int layout, hipStream_t s) {
   hipLaunchKernelGGL(rope_kernel, dim3(grid_for(rows * (nq + nk) * (hd / 2))), dim3(EW_THREADS), 0, s, q, k, rows, nq, nk,
-                     hd, pos0, table, layout);
+                     hd, pos, max_pos, table, layout);
   return hipGetLastError();
 }
 

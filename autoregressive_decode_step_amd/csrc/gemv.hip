@@ -261,18 +261,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_t_kernel(const GemvParams p
 
 int gemv_vec(int w_is_bf16, int vec1) { return vec1 ? 1 : (w_is_bf16 ? 8 : 4); }
 
-// Tuning knobs for measurement sweeps (unset in normal use): LLMK_GEMV_BLOCKS overrides the target
-// workgroup count, LLMK_GEMV_LPR the lanes per row segment (16, 32 or 64).
-static int env_int(const char* name, int def) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : def;
-}
-
 void gemv_plan(GemvParams& p, int w_is_bf16, int vec1, int target_blocks, int min_cols) {
   const int vec = gemv_vec(w_is_bf16, vec1);
-  target_blocks = env_int("LLMK_GEMV_BLOCKS", target_blocks);
-  int lpr = vec1 ? 64 : env_int("LLMK_GEMV_LPR", 16);
-  if (lpr != 16 && lpr != 32 && lpr != 64) lpr = 16;
+  int lpr = vec1 ? 64 : 16;
   while (lpr < 64 && lpr * vec < min_cols) lpr *= 2;
   p.lpr = lpr;
   const int cb = lpr * vec;

@@ -253,7 +253,8 @@ struct StepParams {
   float eps;
   int32_t nwg;                  // workgroups (one per CU)
   int64_t kv_off;               // element offset of the slot in each pool buffer
-  int32_t attn_chunk, pad0;     // positions per attention tile
+  int32_t attn_chunk;           // positions per attention tile
+  int32_t give_up;              // test only: the attention waits for a tag nobody writes (bounded-wait path)
   DecodeState* state;
   // activations as (value, tag) pairs, tag = step within the call + 1; cleared before each call.
   // x [2 n_layer][x_stride]: x after layer l's o (2l) and after its down (2l + 1); q|k|v, attention
@@ -294,8 +295,8 @@ hipError_t add_rmsnorm_launch(float* residual, const float* x, const float* gain
                               float* h, hipStream_t s);
 hipError_t silu_mul_launch(const float* gate, const float* up, float* out, int64_t n, hipStream_t s);
 hipError_t rope_table_launch(float* table, int64_t max_pos, int64_t hd, double base, hipStream_t s);
-hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, int64_t pos0,
-                       const float* table, int layout, hipStream_t s);
+hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, const int32_t* pos,
+                       int64_t max_pos, const float* table, int layout, hipStream_t s);
 hipError_t kv_append_launch(void* cache, int is_bf16, int64_t offset, const float* src, int64_t n, hipStream_t s);
 constexpr int SAMPLE_MAX_K = 1024;   // survivors (top-k after clamping to the row length) the sampler holds
 enum SampleForm { SAMPLE_WIDE = 0, SAMPLE_WAVE_SLICES = 1, SAMPLE_BLOCK_SLICES = 2 };

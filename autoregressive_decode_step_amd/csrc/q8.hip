@@ -257,11 +257,6 @@ __global__ __launch_bounds__(Q8_THREADS) void rowdot_q8_kernel(const RowdotParam
   }
 }
 
-static int q8_env(const char* name, int def) {
-  const char* v = getenv(name);   // measurement sweeps only
-  return (v && *v) ? atoi(v) : def;
-}
-
 int rowdot_q8_plan(RowdotParams& p, int mode) {
   if (p.K % Q8_GROUP != 0) return -1;
   // as many segment waves as keep a segment at one full load per lane (1,024 codes) or more
@@ -274,13 +269,12 @@ int rowdot_q8_plan(RowdotParams& p, int mode) {
   p.np = np <= 1 ? 1 : np <= 2 ? 2 : 4;
   int r = p.np == 1 ? 8 : p.np == 2 ? 4 : 2;
   if (mode == GM_GATEUP) r /= 2;
-  if (q8_env("LLMK_Q8_RX", 1) == 2) r *= 2;   // twice the rows per batch of loads
   p.r = r;
   const int64_t quantum = (int64_t)(Q8_WAVES / kw) * r;
   // workgroups per launch, measured on the Llama-3-8B shape: 512 for gate|up and the down projection (longer
   // rows per workgroup amortise its prologue), 2,048 for the vocabulary-wide head, 1,024 for q|k|v and o
   const int64_t dflt = (mode == GM_GATEUP || (mode == GM_RESID && p.K > p.N)) ? 512 : mode == GM_PLAIN ? 2048 : 1024;
-  const int64_t target = q8_env("LLMK_Q8_BLOCKS", (int)dflt);
+  const int64_t target = dflt;
   int64_t rpb = (p.N + target - 1) / target;
   rpb = (rpb + quantum - 1) / quantum * quantum;
   if (rpb > RD_MAX_ROWS) rpb = RD_MAX_ROWS / quantum * quantum;

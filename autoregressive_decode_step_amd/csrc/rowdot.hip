@@ -175,19 +175,12 @@ __global__ __launch_bounds__(RD_THREADS) void rowdot_kernel(const RowdotParams p
 // host side
 // ------------------------------------------------------------------------------------------------------
 
-static int rd_env(const char* name, int def) {
-  const char* v = getenv(name);   // measurement sweeps only
-  return (v && *v) ? atoi(v) : def;
-}
-
 int rowdot_plan(RowdotParams& p, int w_is_bf16, int mode) {
   const int vec = w_is_bf16 ? 8 : 4;
   if (p.K % vec != 0) return -1;
   // split K over as many of the 4 waves as the vector width allows: each wave holds a quarter of x
   int kw = 4;
   while (kw > 1 && (p.K % kw != 0 || (p.K / kw) % vec != 0)) kw /= 2;
-  kw = rd_env("LLMK_RD_KW", kw);
-  if (kw != 1 && kw != 2 && kw != 4) kw = 1;
   if (p.K % kw != 0 || (p.K / kw) % vec != 0) return -1;
   const int np = (int)((p.K / kw + 64 * vec - 1) / (64 * vec));
   if (np > 8) return -1;
@@ -197,7 +190,7 @@ int rowdot_plan(RowdotParams& p, int w_is_bf16, int mode) {
   if (mode == GM_GATEUP) r = r > 1 ? r / 2 : 1;
   p.r = r;
   const int64_t quantum = (int64_t)(RD_WAVES / kw) * p.r;
-  const int64_t target = rd_env("LLMK_RD_BLOCKS", 1024);
+  const int64_t target = 1024;   // workgroups per launch
   int64_t rpb = (p.N + target - 1) / target;
   rpb = (rpb + quantum - 1) / quantum * quantum;
   if (rpb > RD_MAX_ROWS) rpb = RD_MAX_ROWS / quantum * quantum;

@@ -455,7 +455,7 @@ __device__ __forceinline__ void sk_attention(const StepParams* pp, int l, int po
   ap.v_w = static_cast<char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
   ap.qkv_tag = p.qkv + (int64_t)l * p.qkv_stride;
   ap.out_tag = p.att + (int64_t)l * p.att_stride;
-  ap.tag = tag;
+  ap.tag = p.give_up ? (tag | 0x80000000u) : tag;   // a tag no workgroup writes (tests of the give-up path)
   ap.err = p.err;
   for (int it = w; it < p.Hkv * n_parts; it += nwg) attn_block<T, HD, true>(ap, it / n_parts, it % n_parts, 0, sk_dyn);
   const int G = p.H / p.Hkv;

@@ -90,7 +90,7 @@ def fill_prefix(pool: KVPool, slot: int, prefix: list) -> None:
     for l, (kk, vv) in enumerate(prefix):
         pool.slot_view(l, slot, "k")[:n] = to_device(kk, pool.k[l].device).view(n, pool.n_kv, pool.head_dim)
         pool.slot_view(l, slot, "v")[:n] = to_device(vv, pool.v[l].device).view(n, pool.n_kv, pool.head_dim)
-    pool.slot_len[slot] = n
+    pool.set_len(slot, n)
 
 
 class Decoder:
@@ -128,7 +128,7 @@ def fill_prefix_window(pool: KVPool, slot: int, source_dev: list, start: int, n:
         if n > 0:
             pool.slot_view(l, slot, "k")[:n] = kk[start:start + n]
             pool.slot_view(l, slot, "v")[:n] = vv[start:start + n]
-    pool.slot_len[slot] = n
+    pool.set_len(slot, n)
 
 
 class BatchDecoder:

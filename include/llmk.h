@@ -61,7 +61,9 @@ enum {
   LLMK_CACHE_CAPACITY_EXCEEDED = 571, /* the append would overrun the reserved buffer */
   LLMK_TOKEN_OUT_OF_RANGE = 572,      /* token id not in [0, vocab) */
   LLMK_POSITION_OUT_OF_RANGE = 573,   /* position < 0, or >= the RoPE table / max_seq */
-  LLMK_HEAD_SHAPE_INVALID = 574,      /* n_head % n_kv != 0, odd head_dim, head_dim > 256, or unaligned widths */
+  LLMK_HEAD_SHAPE_INVALID = 574,      /* a shape the kernels do not take: n_head % n_kv != 0, more than 8 query
+                                         heads per K/V head, head_dim odd or > 256 (RoPE) or not a power of two
+                                         in [2, 256] (attention, decode), widths not a whole number of vectors */
   LLMK_SLOT_OUT_OF_RANGE = 575,       /* K/V pool slot not in [0, n_slots) */
   LLMK_WEIGHT_LENGTH_MISMATCH = 576,  /* a model tensor's element count disagrees with the config */
   LLMK_OUTPUT_LENGTH_MISMATCH = 577,  /* an output buffer's element count disagrees with the shape */
@@ -175,27 +177,32 @@ int32_t llmk_rope_table_init(float* table, int64_t len_table, int64_t max_pos, i
                              double base, void* stream);
 
 /* In-place rotary embedding of q [rows][n_q_heads][hd] and k [rows][n_k_heads][hd]; row r is at
- * position pos0 + r. layout selects half-split or interleaved pairs ([dops] "Usage": rope(q, k, pos)
- * in place). k may be NULL with n_k_heads == 0.
- * Codes: 578, 561 (rows, n_q_heads, head_dim < 1, or n_k_heads < 0), 564, 574 (odd hd or > 256),
- * 562 (len_q), 563 (len_k), 576 (len_table != max_pos*hd), 573 (pos0 < 0 or pos0 + rows > max_pos). */
+ * position pos[r], read on the device ([dops] "Usage": rope(q, k, pos) in place), so a step whose
+ * positions live on the device needs no host round trip. layout selects half-split or interleaved pairs.
+ * k may be NULL with n_k_heads == 0.
+ *   pos: device int32 [rows] (len_pos elements). The host cannot see device positions: a row whose
+ *        position is outside [0, max_pos) has no table row and is left unchanged.
+ * Codes: 578 (null q/table/pos, layout, k NULL with n_k_heads > 0), 561 (rows, n_q_heads, head_dim,
+ * max_pos < 1, or n_k_heads < 0), 564, 574 (odd hd or > 256), 562 (len_q), 563 (len_k), 576 (len_table !=
+ * max_pos*hd), 577 (len_pos != rows). */
 int32_t llmk_rope(float* q, int64_t len_q, float* k, int64_t len_k, int64_t rows, int64_t n_q_heads,
-                  int64_t n_k_heads, int64_t head_dim, int64_t pos0, const float* table, int64_t len_table,
-                  int64_t max_pos, int32_t layout, void* stream);
+                  int64_t n_k_heads, int64_t head_dim, const int32_t* pos, int64_t len_pos, const float* table,
+                  int64_t len_table, int64_t max_pos, int32_t layout, void* stream);
 
-/* In-place append into a reserved cache buffer: cache[cache_len + i] = round(new_vals[i]) for
+/* In-place append into one reserved flat cache buffer: cache[cache_len + i] = round(new_vals[i]) for
  * i in [0, n_new), rounded to the cache dtype (fp32 -> bf16 round-to-nearest-even, NaN kept).
  * Existing content is never copied ([llmk] "KV-cache growth and greedy argmax" and "The hot loop
- * doesn't call kv_cache_append_flat": the reserved-capacity, in-place append).
+ * doesn't call kv_cache_append_flat": the reserved-capacity, in-place append). llmk_kv_append is the
+ * same append into one (layer, slot, K or V) buffer of a pool.
  *   cache     : device buffer of `capacity` elements of `dtype`
  *   cache_len : claimed filled length; len_cache: the caller's record of it (566 if different)
  *   new_len_h : host int64, receives cache_len + n_new on success (may be NULL)
  * Codes: 578, 561 (capacity < 1, cache_len < 0, n_new < 1), 564, 566, 567, 571 (cache_len + n_new >
  * capacity). Worked example: cache [0..5], new [100,101,102] -> 9 elements, n = 9. */
-int32_t llmk_kv_append(void* cache, int64_t capacity, int32_t dtype, int64_t cache_len, int64_t len_cache,
-                       const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h, void* stream);
+int32_t llmk_kv_append_flat(void* cache, int64_t capacity, int32_t dtype, int64_t cache_len, int64_t len_cache,
+                            const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h, void* stream);
 
-/* Bytes of workspace llmk_gqa_attend needs. */
+/* Bytes of workspace llmk_gqa_attend_flat and llmk_gqa_attend need. */
 int64_t llmk_gqa_attend_workspace_bytes(int64_t ctx_len, int64_t n_head, int64_t head_dim);
 
 /* Grouped-query decode attention for one query position over a cache of ctx_len positions:
@@ -205,11 +212,13 @@ int64_t llmk_gqa_attend_workspace_bytes(int64_t ctx_len, int64_t n_head, int64_t
  * flash attention split across the context and reduced).
  *   q: device fp32 [n_head][hd]; k_cache, v_cache: device [>= ctx_len][n_kv][hd] of kv_dtype
  *   len_cache: elements in each of k_cache and v_cache; out: device fp32 [n_head][hd]
- * Codes: 578, 561, 564, 574 (n_head % n_kv, odd hd, hd > 256), 562 (len_q), 563 (len_cache <
- * ctx_len*n_kv*hd), 577 (len_out), 578 (workspace). */
-int32_t llmk_gqa_attend(const float* q, int64_t len_q, const void* k_cache, const void* v_cache,
-                        int64_t len_cache, int32_t kv_dtype, int64_t ctx_len, int64_t n_head, int64_t n_kv,
-                        int64_t head_dim, float* out, int64_t len_out, void* ws, int64_t len_ws, void* stream);
+ *   ws: device workspace of len_ws >= llmk_gqa_attend_workspace_bytes bytes (no clearing needed)
+ * Codes: 578, 561, 564, 574 (n_head % n_kv != 0, n_head / n_kv > 8, hd not a power of two in [2, 256]),
+ * 562 (len_q), 563 (len_cache < ctx_len*n_kv*hd), 577 (len_out), 578 (workspace short, caches not
+ * 16-byte aligned). llmk_gqa_attend is the same attention over one (layer, slot) of a pool. */
+int32_t llmk_gqa_attend_flat(const float* q, int64_t len_q, const void* k_cache, const void* v_cache,
+                             int64_t len_cache, int32_t kv_dtype, int64_t ctx_len, int64_t n_head, int64_t n_kv,
+                             int64_t head_dim, float* out, int64_t len_out, void* ws, int64_t len_ws, void* stream);
 
 /* Bytes of workspace llmk_argmax needs. */
 int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n);
@@ -230,9 +239,10 @@ int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64
 /* Workspace bytes llmk_sample needs for these sizes (0: none), or -status for invalid sizes. */
 int64_t llmk_sample_workspace_bytes(int64_t rows, int64_t n, float temperature, int32_t top_k);
 
-/* One draw per row of logits ([dops] "Method": the HuggingFace warper order, temperature, then top-k, then
- * top-p over the renormalised survivors, survivors in descending logit order with ties to the lower index,
- * and the token is the inverse CDF at an explicit uniform draw). top-p keeps a survivor while the mass of
+/* One draw per row of logits ([dops] "Method" fixes the order of the cuts and the tie rule): the logits are
+ * scaled by 1/temperature, only the top_k largest stay (equal logits ranked by the lower index first), the
+ * survivors' probabilities are renormalised and cut by top_p, and the caller's uniform picks the token by
+ * the inverse CDF over what is left. top-p keeps a survivor while the mass of
  * the survivors before it is below top_p (the first is always kept); the token is the first kept survivor
  * whose cumulative renormalised probability exceeds u[r]. temperature 0 is greedy (the lowest index
  * holding the row maximum). A NaN logit counts as -inf and -0 as +0; a draw below 0 or NaN counts as 0, a
@@ -263,7 +273,14 @@ typedef struct {
   int32_t kv_dtype;    /* llmk_dtype of the K/V pool */
   int32_t w_layout;    /* llmk_weight_layout of the seven per-layer projections */
   int32_t step_path;   /* llmk_step_path */
+  int32_t test_flags;  /* 0 in normal use; LLMK_TEST_* bits exercise error paths in tests */
 } llmk_config;
+
+/* llmk_config.test_flags: LLMK_TEST_WAIT_GIVE_UP makes every cross-workgroup wait of the persistent step
+ * wait for a hand-off tag that no workgroup writes, so the first wait runs into its bounded-wait limit
+ * (200 ms), every workgroup then stops waiting and exits, and the call returns 579. Only the persistent
+ * form has such waits; the per-operation form ignores the flag. For tests of the failure path only. */
+#define LLMK_TEST_WAIT_GIVE_UP 1
 
 /* A device tensor and its element count. */
 typedef struct {
@@ -292,14 +309,51 @@ typedef struct {
  * buffer per layer, slot s at element s * plane). Layer l's K buffer holds n_slots * capacity *
  * n_kv * head_dim elements; position p of slot s, K/V head g, element i sits at
  *   s * plane + p * n_kv * head_dim + g * head_dim + i,   plane = capacity * n_kv * head_dim.
- * slot_len_h records how many positions each slot holds; decode steps check it (566) and advance it. */
+ * slot_len_h records how many positions each slot holds; decode steps check it (566) and advance it.
+ * len_k_h / len_v_h, when given, record the filled elements of every (layer, slot) K and V buffer, the
+ * flat cache lengths llmk_kv_append checks and advances ([llmk] "KV-cache growth and greedy argmax":
+ * cache_len -> cache_len + n_new); decode steps and prefill set them to positions * n_kv * head_dim for
+ * every layer of the slots they advance. */
 typedef struct {
   void* const* k;          /* host array [n_layer] of device pointers */
   void* const* v;          /* host array [n_layer] of device pointers */
   int64_t n_layer, n_slots, capacity, n_kv, head_dim;
   int32_t dtype;           /* llmk_dtype */
   int64_t* slot_len_h;     /* host array [n_slots] */
+  int64_t* len_k_h;        /* host array [n_layer][n_slots] or NULL */
+  int64_t* len_v_h;        /* host array [n_layer][n_slots] or NULL */
 } llmk_kv_pool;
+
+/* Validate a pool descriptor and mark every slot empty: slot_len_h, and len_k_h / len_v_h when given, are
+ * set to 0 ([llmk] "The hot loop doesn't call kv_cache_append_flat": the cache is reserved once at its full
+ * capacity, then filled in place). Host only; the device buffers are not touched.
+ * Codes: 578 (null pool, k, v, slot_len_h or a layer buffer, unknown dtype, buffers not 16-byte aligned),
+ * 561 (n_layer, n_slots, capacity, n_kv or head_dim < 1), 564 (> LLMK_MAX_DIM). */
+int32_t llmk_kv_pool_init(llmk_kv_pool* pool);
+
+/* llmk_kv_append_flat on buffer `which` (0: K, 1: V) of `layer` for sequence `slot`: the slot's region is a
+ * flat cache of capacity * n_kv * head_dim elements whose recorded fill is len_k_h / len_v_h[layer * n_slots
+ * + slot]. cache_len is the caller's claim of that fill and n_new the elements appended (a decode token
+ * appends n_kv * head_dim, one position). On success the record becomes cache_len + n_new, *new_len_h gets
+ * it and *elem_offset_h gets the element offset of the first written element in the layer buffer,
+ * slot * plane + cache_len ([xpu] "3. The K/V cache and the block store": slot s at s * plane).
+ *   new_vals: device fp32 [len_new]; new_len_h, elem_offset_h: host int64 (each may be NULL)
+ * Codes: 578 (null pool / new_vals, len_k_h or len_v_h NULL, which not 0 or 1, layer not in [0, n_layer)),
+ * 561 (cache_len < 0, n_new < 1), 564, 575 (slot), 566 (cache_len != recorded fill), 567 (len_new != n_new),
+ * 571 (cache_len + n_new > capacity * n_kv * head_dim). */
+int32_t llmk_kv_append(llmk_kv_pool* pool, int64_t layer, int64_t slot, int32_t which, int64_t cache_len,
+                       const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h,
+                       int64_t* elem_offset_h, void* stream);
+
+/* llmk_gqa_attend_flat over positions [0, ctx_len) of one (layer, slot) of a pool ([fwd] "The code": the
+ * attention over the cached keys and values; [xpu] "3. The K/V cache and the block store").
+ *   q: device fp32 [n_head][head_dim]; out: device fp32 [n_head][head_dim]; ws as for llmk_gqa_attend_flat
+ * Codes: 578 (null, layer not in [0, n_layer)), 561 (ctx_len or n_head < 1), 564, 575 (slot), 574 (as
+ * llmk_gqa_attend_flat with the pool's n_kv and head_dim), 562 (len_q), 577 (len_out), 573 (ctx_len >
+ * capacity), 566 (len_k_h / len_v_h given and either records fewer than ctx_len positions), 578 (workspace). */
+int32_t llmk_gqa_attend(const float* q, int64_t len_q, const llmk_kv_pool* pool, int64_t layer, int64_t slot,
+                        int64_t ctx_len, int64_t n_head, float* out, int64_t len_out, void* ws, int64_t len_ws,
+                        void* stream);
 
 /* Element offset of (slot, pos, kv_head) in each layer buffer of the pool (closed form above).
  * Codes: 578, 575 (slot), 573 (pos not in [0, capacity)), 574 (kv_head not in [0, n_kv)). */
@@ -320,8 +374,11 @@ int64_t llmk_decode_workspace_bytes(const llmk_config* cfg, int64_t batch);
  *   logits     : device fp32 [vocab] or NULL;  token_out: device int32 [1]
  *   hidden     : device fp32 [n_layer][d] (the residual after each layer) or NULL
  * On success pool->slot_len_h[slot] becomes pos + 1.
+ * The persistent form hands activations between workgroups through bounded waits; there the call waits
+ * for the step to finish and returns 579 if a wait gave up (its outputs are then undefined). When `stream`
+ * is being captured into a graph it cannot wait, and such a failure is not reported by this call.
  * Codes: 578, 561/564/574 (config), 576 (model tensor lengths), 575, 572, 573 (pos < 0 or >= max_seq),
- * 566, 571 (pos >= capacity), 568 (len_logits != vocab), 577 (len_hidden), 578 (workspace). */
+ * 566, 571 (pos >= capacity), 568 (len_logits != vocab), 577 (len_hidden), 578 (workspace), 579. */
 int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                          int64_t token, int64_t pos, float* logits, int64_t len_logits, int32_t* token_out,
                          float* hidden, int64_t len_hidden, void* ws, int64_t len_ws, void* stream);
@@ -338,9 +395,8 @@ int32_t llmk_decode_steps(const llmk_config* cfg, const llmk_model* model, llmk_
                           int64_t token0, int64_t pos0, int64_t n_steps, int32_t* tokens_out, int64_t len_tokens,
                           void* ws, int64_t len_ws, void* stream);
 
-/* As llmk_decode_steps, with the sampling exit in place of greedy at the end of every step ([dops] "Method":
- * temperature, then top-k, then top-p over the renormalised survivors, then the inverse CDF at an explicit
- * uniform; llmk_sample's rule exactly): step i samples its token from its logits with the uniform draws[i],
+/* As llmk_decode_steps, with the sampling exit in place of greedy at the end of every step (llmk_sample's
+ * rule exactly; [dops] "Method"): step i samples its token from its logits with the uniform draws[i],
  * writes it to tokens_out[i] and feeds it to step i + 1, all inside the captured loop.
  *   draws: device fp32 [n_steps] (len_draws elements), the caller's uniforms in [0, 1)
  *   temperature >= 0 (0: greedy), top_k <= 0 or >= vocab: no cut, 0 < top_p <= 1
@@ -443,9 +499,10 @@ int32_t llmk_prefill_profiled(const llmk_config* cfg, const llmk_model* model, l
 int64_t llmk_q8_pack_bytes(int64_t rows, int64_t cols);
 
 /* Quantize w (device, rows x cols row-major, output-major, w_dtype LLMK_F32 or LLMK_BF16, finite values)
- * into the q8 pack at `pack` (device, len_pack bytes, 16-byte aligned), on `stream`. Codes: 578 (null,
- * w_dtype), 561 (rows or cols < 1), 564 (> LLMK_MAX_DIM), 574 (cols not a multiple of LLMK_Q8_GROUP),
- * 576 (len_w != rows*cols), 577 (len_pack != llmk_q8_pack_bytes), 579 (launch failed). */
+ * into the q8 pack at `pack` (device, len_pack bytes), on `stream`. Both w and pack must be 16-byte aligned
+ * (the decode step reads packs with 16-byte loads). Codes: 578 (null, w_dtype), 561 (rows or cols < 1),
+ * 564 (> LLMK_MAX_DIM), 574 (cols not a multiple of LLMK_Q8_GROUP), 576 (len_w != rows*cols), 577 (len_pack
+ * != llmk_q8_pack_bytes), 578 (w or pack not 16-byte aligned), 579 (launch failed). */
 int32_t llmk_quantize_q8(const void* w, int64_t len_w, int32_t w_dtype, int64_t rows, int64_t cols, void* pack,
                          int64_t len_pack, void* stream);
 

@@ -167,15 +167,26 @@ def silu_mul(gate=True, len_gate=0, up=True, len_up=0, n=0, out=True, len_out=0)
     return OUTPUT_LEN if len_out != n else OK
 
 
+# Shape limits. Only two of them come from the pages: RoPE rotates pairs, so head_dim is even, and every
+# query head reads one K/V head, so n_head is a multiple of n_kv ("The forward pass end to end", "The
+# code"). The rest are the library's own, as its header documents them for status 574: head_dim at most
+# 256, a power of two for attention and the decode step, and at most 8 query heads per K/V head (the
+# attention kernels keep a group's heads in one workgroup). They are restated here so that the status of
+# every call is predicted; they are limits of the implementation, not of the method.
+LIB_MAX_HEAD_DIM = 256
+LIB_MAX_GROUP = 8
+
+
 def _head_dim_ok(hd):
-    """RoPE needs pairs: an even head dimension of at most 256."""
-    return hd % 2 == 0 and 2 <= hd <= 256
+    """RoPE needs pairs (an even head dimension); the library takes at most LIB_MAX_HEAD_DIM."""
+    return hd % 2 == 0 and 2 <= hd <= LIB_MAX_HEAD_DIM
 
 
 def _attn_shape_ok(n_head, n_kv, hd):
-    """Attention and the decode step: whole query-head groups of at most 8 heads per K/V head, and a
-    power-of-two head dimension in [2, 256]."""
-    return n_head % n_kv == 0 and n_head // n_kv <= 8 and 2 <= hd <= 256 and (hd & (hd - 1)) == 0
+    """Whole query-head groups (the method); at most LIB_MAX_GROUP heads per group and a power-of-two head
+    dimension in [2, LIB_MAX_HEAD_DIM] (the library's kernels)."""
+    return (n_head % n_kv == 0 and n_head // n_kv <= LIB_MAX_GROUP and 2 <= hd <= LIB_MAX_HEAD_DIM
+            and (hd & (hd - 1)) == 0)
 
 
 def rope_table_init(table=True, len_table=0, max_pos=0, head_dim=0, base=1e4):
@@ -190,9 +201,10 @@ def rope_table_init(table=True, len_table=0, max_pos=0, head_dim=0, base=1e4):
     return OUTPUT_LEN if len_table != max_pos * head_dim else OK
 
 
-def rope(q=True, len_q=0, k=True, len_k=0, rows=0, n_q_heads=0, n_k_heads=0, head_dim=0, pos0=0, table=True,
-         len_table=0, max_pos=0, layout=0):
-    if not q or not table or layout not in (0, 1) or (not k and n_k_heads != 0):
+def rope(q=True, len_q=0, k=True, len_k=0, rows=0, n_q_heads=0, n_k_heads=0, head_dim=0, pos=True, len_pos=0,
+         table=True, len_table=0, max_pos=0, layout=0):
+    """Positions are device values the host cannot see: only their count is checked."""
+    if not q or not table or not pos or layout not in (0, 1) or (not k and n_k_heads > 0):
         return INVALID
     c = _dims(rows, n_q_heads, head_dim, max_pos, n_k_heads, allow_zero=(4,))
     if c != OK:
@@ -205,12 +217,12 @@ def rope(q=True, len_q=0, k=True, len_k=0, rows=0, n_q_heads=0, n_k_heads=0, hea
         return B_LEN
     if len_table != max_pos * head_dim:
         return WEIGHT_LEN
-    if pos0 < 0 or pos0 + rows > max_pos:
-        return POSITION
+    if len_pos != rows:
+        return OUTPUT_LEN
     return OK
 
 
-def kv_append(cache=True, capacity=0, dtype=0, cache_len=0, len_cache=0, new_vals=True, len_new=0, n_new=0):
+def kv_append_flat(cache=True, capacity=0, dtype=0, cache_len=0, len_cache=0, new_vals=True, len_new=0, n_new=0):
     if not (cache and new_vals) or dtype not in (0, 1):
         return INVALID
     c = _dims(capacity)
@@ -224,8 +236,8 @@ def kv_append(cache=True, capacity=0, dtype=0, cache_len=0, len_cache=0, new_val
     return OK
 
 
-def gqa_attend(q=True, len_q=0, k_cache=True, v_cache=True, len_cache=0, kv_dtype=0, ctx_len=0, n_head=0, n_kv=0,
-               head_dim=0, out=True, len_out=0, ws=True, ws_short=False):
+def gqa_attend_flat(q=True, len_q=0, k_cache=True, v_cache=True, len_cache=0, kv_dtype=0, ctx_len=0, n_head=0,
+                    n_kv=0, head_dim=0, out=True, len_out=0, ws=True, ws_short=False):
     if not (q and k_cache and v_cache and out and ws) or kv_dtype not in (0, 1):
         return INVALID
     c = _dims(ctx_len, n_head, n_kv, head_dim)
@@ -239,6 +251,83 @@ def gqa_attend(q=True, len_q=0, k_cache=True, v_cache=True, len_cache=0, kv_dtyp
         return B_LEN
     if len_out != n_head * head_dim:
         return OUTPUT_LEN
+    return INVALID if ws_short else OK
+
+
+def _pool_fields(pool):
+    """A pool descriptor's own fields: 578 (null k, v or slot_len array, dtype), 561, 564, then 578 again
+    for a layer buffer that is null or not 16-byte aligned (pool["buffers"] False)."""
+    if not pool.get("arrays", True) or pool.get("dtype", 0) not in (0, 1):
+        return INVALID
+    c = _dims(pool["n_layer"], pool["n_slots"], pool["capacity"], pool["n_kv"], pool["head_dim"])
+    if c != OK:
+        return c
+    return OK if pool.get("buffers", True) else INVALID
+
+
+def kv_pool_init(pool=None):
+    """Status of llmk_kv_pool_init; pool is a dict of the descriptor's fields (None: null pointer)."""
+    if pool is None:
+        return INVALID
+    return _pool_fields(pool)
+
+
+def kv_append(pool=None, layer=0, slot=0, which=0, cache_len=0, recorded=0, new_vals=True, len_new=0, n_new=0):
+    """(status, new_len, elem_offset) of llmk_kv_append into buffer `which` of (layer, slot); `recorded` is
+    the pool's fill record of that buffer. The slot's region is a flat cache of plane elements at
+    slot * plane ("Inside the engine", "3. The K/V cache and the block store"); the append follows the
+    flat cache's rule ("LLM inference kernels", "KV-cache growth and greedy argmax")."""
+    if not new_vals or pool is None:
+        return INVALID, None, None
+    c = _pool_fields(pool)
+    if c != OK:
+        return c, None, None
+    if not pool.get("records", True) or which not in (0, 1) or not (0 <= layer < pool["n_layer"]):
+        return INVALID, None, None
+    if cache_len < 0 or n_new < 1:
+        return EMPTY, None, None
+    if cache_len > MAX_DIM or n_new > MAX_DIM:
+        return TOO_LARGE, None, None
+    if not (0 <= slot < pool["n_slots"]):
+        return SLOT, None, None
+    if cache_len != recorded:
+        return CACHE_LEN, None, None
+    if len_new != n_new:
+        return NEW_LEN, None, None
+    plane = pool["capacity"] * pool["n_kv"] * pool["head_dim"]
+    if cache_len + n_new > plane:
+        return CAPACITY, None, None
+    return OK, cache_len + n_new, slot * plane + cache_len
+
+
+def gqa_attend(q=True, len_q=0, pool=None, layer=0, slot=0, ctx_len=0, n_head=0, out=True, len_out=0, rec_k=None,
+               rec_v=None, ws=True, ws_short=False):
+    """Status of llmk_gqa_attend over (layer, slot) of a pool; rec_k / rec_v: the pool's fill records of
+    that slot's K and V buffers in elements (None: the pool keeps none)."""
+    if not (q and out and ws) or pool is None:
+        return INVALID
+    c = _pool_fields(pool)
+    if c != OK:
+        return c
+    if not (0 <= layer < pool["n_layer"]):
+        return INVALID
+    c = _dims(ctx_len, n_head)
+    if c != OK:
+        return c
+    if not (0 <= slot < pool["n_slots"]):
+        return SLOT
+    n_kv, hd = pool["n_kv"], pool["head_dim"]
+    if not _attn_shape_ok(n_head, n_kv, hd):
+        return HEAD_SHAPE
+    if len_q != n_head * hd:
+        return A_LEN
+    if len_out != n_head * hd:
+        return OUTPUT_LEN
+    if ctx_len > pool["capacity"]:
+        return POSITION
+    need = ctx_len * n_kv * hd
+    if (rec_k is not None and rec_k < need) or (rec_v is not None and rec_v < need):
+        return CACHE_LEN
     return INVALID if ws_short else OK
 
 
@@ -300,8 +389,8 @@ def q8_pack_bytes(rows, cols):
     return rows * cols + 4 * rows * (cols // Q8_GROUP)
 
 
-def quantize_q8(w=True, len_w=0, w_dtype=0, rows=0, cols=0, pack=True, len_pack=0):
-    """Expected status of llmk_quantize_q8."""
+def quantize_q8(w=True, len_w=0, w_dtype=0, rows=0, cols=0, pack=True, len_pack=0, aligned=True):
+    """Expected status of llmk_quantize_q8 (aligned: both buffers start on a 16-byte boundary)."""
     if not (w and pack) or w_dtype not in (0, 1):
         return INVALID
     c = _dims(rows, cols)
@@ -313,15 +402,17 @@ def quantize_q8(w=True, len_w=0, w_dtype=0, rows=0, cols=0, pack=True, len_pack=
         return WEIGHT_LEN
     if len_pack != q8_pack_bytes(rows, cols):
         return OUTPUT_LEN
+    if not aligned:
+        return INVALID
     return OK
 
 
 def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4, rope_layout=0,
-                 w_dtype=0, kv_dtype=0, w_layout=0, step_path=0):
+                 w_dtype=0, kv_dtype=0, w_layout=0, step_path=0, test_flags=0):
     import math
     if rope_layout not in (0, 1) or w_dtype not in (0, 1, 2) or kv_dtype not in (0, 1) or w_layout not in (0, 1):
         return INVALID
-    if step_path not in (0, 1, 2):
+    if step_path not in (0, 1, 2) or test_flags not in (0, 1):
         return INVALID
     if not (eps > 0 and math.isfinite(eps)) or not (rope_base > 1 and math.isfinite(rope_base)):
         return INVALID

@@ -1,9 +1,9 @@
 """THE ORACLE's sampler -- test infrastructure only (see the package docstring).
 
-One draw of the decode step's sampling exit, in fp64, following the order the "decode-ops" page states
-("Method"): the logits are divided by the temperature, the top-k survive, top-p is applied over the
-renormalised survivors, and the token is the inverse CDF at an explicit uniform draw, the survivors taken
-in descending logit order with ties to the lower index. The page gives the order and the tie rule; the
+One draw of the decode step's sampling exit, in fp64, in the order of the cuts the "decode-ops" page
+fixes ("Method"): scale by the temperature, keep the k largest, cut the renormalised survivors by p, then
+let an explicit uniform pick a survivor through the inverse CDF; survivors are ranked by logit, equal
+logits by the lower index first. The page gives the order and the tie rule; the
 top-p cut and the inverse CDF are taken at their plainest readings (the HuggingFace warper rule the page
 names as its reference):
   - top-p keeps a survivor while the probability mass of the survivors before it is below p, so the first

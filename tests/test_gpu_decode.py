@@ -239,6 +239,41 @@ def test_kernel_time_leaves_the_step_state_of_decode_step():
     assert ref[0] == ref[1]
 
 
+def test_persistent_wait_give_up_returns_device_error():
+    """The persistent step's bounded wait, made to give up from the host (a hand-off tag no workgroup
+    writes): every workgroup still exits, llmk_decode_step and llmk_decode_steps return 579 and leave the
+    slot's length alone, and a normal step on the same workspace and pool then matches the oracle."""
+    import time
+    s = TINY_BF16
+    W = synth.model(s, seed=0)
+    cfg, model, pool, dec = build(s, W, step_path=llmk.STEP_PERSISTENT)
+    assert llmk.decode_path(cfg) == llmk.STEP_PERSISTENT
+    bad = loader.config_from(s, llmk.W_OUT_IN, llmk.STEP_PERSISTENT)
+    bad.test_flags = llmk.TEST_WAIT_GIVE_UP
+    say("persistent step with an unreachable hand-off tag (expect 579 after one 200 ms wait)")
+    t0 = time.time()
+    st = llmk.decode_step(bad, model, pool, 0, 3, 0, dec.token_out, dec.ws)
+    assert st == llmk.DEVICE_ERROR, llmk.status_name(st)
+    assert int(pool.slot_len[0]) == 0
+    toks = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = llmk.decode_steps(bad, model, pool, 0, 3, 0, 4, toks, dec.ws)
+    assert st == llmk.DEVICE_ERROR, llmk.status_name(st)
+    assert int(pool.slot_len[0]) == 0
+    elapsed = time.time() - t0
+    say(f"  both calls returned 579 in {elapsed:.2f} s")
+    assert elapsed < 10.0
+    # the per-operation form has no cross-workgroup waits: the flag changes nothing there
+    per_op = loader.config_from(s, llmk.W_OUT_IN, llmk.STEP_PER_OP)
+    per_op.test_flags = llmk.TEST_WAIT_GIVE_UP
+    assert llmk.decode_step(per_op, model, pool, 0, 3, 0, dec.token_out, dec.ws) == llmk.OK
+    pool.slot_len[0] = 0
+    # the same workspace and pool, normal calls: teacher-forced against the oracle again
+    m = oracle.Model(s, W)
+    prompt = synth.prompt(5, s.vocab, stream=22).tolist()
+    o = oracle_run(m, s, prompt, n_greedy=2)
+    compare_runs(o, gpu_teacher_forced(dec, s, o[0], 0), "tiny bf16 persistent after a give-up")
+
+
 # ---------------------------------------------------------------------------------------------
 # Qwen3-0.6B-shaped (bf16 weights, fp32 K/V)
 # ---------------------------------------------------------------------------------------------

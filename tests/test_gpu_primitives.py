@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 import synth
+from oracle import contract
 from tests.conftest import golden
 from tests.gpu_util import TOL, dev, host, rel_err, say
 
@@ -177,7 +178,8 @@ def test_rope_positions_0_to_8191(layout):
     t = torch.empty(rows * hd, dtype=torch.float32, device="cuda")
     assert llmk.rope_table_init(t, rows, hd, base) == llmk.OK
     qd, kd = dev(q), dev(k)
-    assert llmk.rope(qd, kd, rows, nq, nk, hd, 0, t, rows, layout) == llmk.OK
+    pos = torch.arange(rows, dtype=torch.int32, device="cuda")
+    assert llmk.rope(qd, kd, rows, nq, nk, hd, pos, t, rows, layout) == llmk.OK
     _sync()
     q_ref, k_ref = oracle.rope_f32(q, k, rows, nq, nk, hd, 0, base, layout)
     eq, ek = rel_err(host(qd), q_ref), rel_err(host(kd), k_ref)
@@ -191,10 +193,36 @@ def test_rope_single_position_and_tiny_heads():
         t = torch.empty(4096 * hd, dtype=torch.float32, device="cuda")
         assert llmk.rope_table_init(t, 4096, hd, 1e4) == llmk.OK
         qd = dev(q)
-        assert llmk.rope(qd, None, 1, 3, 0, hd, pos0, t, 4096, 0) == llmk.OK
+        pos = torch.tensor([pos0], dtype=torch.int32, device="cuda")
+        assert llmk.rope(qd, None, 1, 3, 0, hd, pos, t, 4096, 0) == llmk.OK
         _sync()
         q_ref, _ = oracle.rope_f32(q, None, 1, 3, 0, hd, pos0, 1e4, 0)
         assert rel_err(host(qd), q_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("layout", [llmk.ROPE_HALF_SPLIT, llmk.ROPE_INTERLEAVED])
+def test_rope_device_positions_per_row(layout):
+    """Each row at its own device position (a batch of sequences at different lengths); rows whose
+    position has no table row are left unchanged."""
+    rows, nq, nk, hd, max_pos, base = 37, 4, 2, 64, 5000, 5e5
+    positions = [int(p) for p in synth.ints((rows,), 0, max_pos - 1, 28, 0)]
+    positions[3], positions[11], positions[20] = -1, max_pos, max_pos - 1
+    q = synth.normal((rows * nq * hd,), 29, 0, 1.0)
+    k = synth.normal((rows * nk * hd,), 29, 1, 1.0)
+    t = torch.empty(max_pos * hd, dtype=torch.float32, device="cuda")
+    assert llmk.rope_table_init(t, max_pos, hd, base) == llmk.OK
+    qd, kd = dev(q), dev(k)
+    pos = torch.tensor(positions, dtype=torch.int32, device="cuda")
+    assert llmk.rope(qd, kd, rows, nq, nk, hd, pos, t, max_pos, layout) == llmk.OK
+    _sync()
+    gq, gk = host(qd).reshape(rows, -1), host(kd).reshape(rows, -1)
+    qr, kr = q.reshape(rows, -1), k.reshape(rows, -1)
+    for r, p in enumerate(positions):
+        if 0 <= p < max_pos:
+            q_ref, k_ref = oracle.rope_f32(qr[r], kr[r], 1, nq, nk, hd, p, base, layout)
+            assert rel_err(gq[r], q_ref) <= 1e-5 and rel_err(gk[r], k_ref) <= 1e-5, (r, p)
+        else:
+            assert np.array_equal(gq[r], qr[r]) and np.array_equal(gk[r], kr[r]), (r, p)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -205,7 +233,7 @@ def test_kv_append_worked_example_in_place():
     g = golden("kv_append_example.json")
     cache = torch.full((16,), -1.0, dtype=torch.float32, device="cuda")
     cache[:6] = torch.tensor(g["cache"], device="cuda")
-    st, n = llmk.kv_append(cache, g["cache_len"], g["cache_len"], dev(np.array(g["new_vals"], np.float32)))
+    st, n = llmk.kv_append_flat(cache, g["cache_len"], g["cache_len"], dev(np.array(g["new_vals"], np.float32)))
     assert st == llmk.OK and n == g["n"]
     _sync()
     c = host(cache)
@@ -217,15 +245,15 @@ def test_kv_append_bf16_rounding_matches_oracle():
     vals = np.concatenate([np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 3 * 2.0 ** -8), np.nan, 3.0e38],
                                     np.float32), synth.normal((4096,), 24, 0, 1.0)])
     cache = torch.zeros(8192, dtype=torch.bfloat16, device="cuda")
-    st, n = llmk.kv_append(cache, 0, 0, dev(vals))
+    st, n = llmk.kv_append_flat(cache, 0, 0, dev(vals))
     assert st == llmk.OK and n == vals.size
     _sync()
     ref = oracle.kv_append_copy(np.zeros(0, np.uint16), vals, "bf16")
     got = host(cache)[:n]
     assert np.array_equal(got, ref)
-    st, n2 = llmk.kv_append(cache, n, n, dev(vals[:3]))
+    st, n2 = llmk.kv_append_flat(cache, n, n, dev(vals[:3]))
     assert st == llmk.OK and n2 == n + 3
-    st, _ = llmk.kv_append(cache, n2, n2, dev(np.zeros(8192 - n2 + 1, np.float32)))
+    st, _ = llmk.kv_append_flat(cache, n2, n2, dev(np.zeros(8192 - n2 + 1, np.float32)))
     assert st == 571
 
 
@@ -244,7 +272,7 @@ def test_gqa_attend_matches_oracle(ctx, H, Hkv, hd, dt):
     v = synth.normal((ctx, Hkv, hd), 27, ctx, 1.0, dt)
     out = torch.full((H * hd,), float("nan"), dtype=torch.float32, device="cuda")
     ws = llmk.workspace(llmk.gqa_attend_workspace_bytes(ctx, H, hd))
-    st = llmk.gqa_attend(dev(q), dev(k), dev(v), ctx, H, Hkv, hd, out, ws)
+    st = llmk.gqa_attend_flat(dev(q), dev(k), dev(v), ctx, H, Hkv, hd, out, ws)
     assert st == llmk.OK, llmk.status_name(st)
     _sync()
     ref = oracle.attend_f32(q, k, v, ctx, H, Hkv, hd)
@@ -255,6 +283,65 @@ def test_gqa_attend_matches_oracle(ctx, H, Hkv, hd, dt):
         assert np.array_equal(host(out).reshape(H, hd),
                               np.repeat(oracle.bf16_to_f64(v[0]) if dt == "bf16" else v[0], H // Hkv, axis=0)
                               .astype(np.float32))
+
+
+# ---------------------------------------------------------------------------------------------
+# the pool-level append and attention: offsets, records and values against the oracle
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_pool_append_offsets_and_attend(dt):
+    """Decode-style appends of one position (n_kv * hd elements) into (layer, slot) buffers of a pool:
+    the offset each call returns equals the closed form bit-exactly, the written values are the oracle's
+    rounding of the new values, nothing else changes, and attention over the slot equals the oracle's."""
+    n_layer, n_slots, cap, Hkv, hd, H = 2, 3, 96, 2, 64, 8
+    kv = llmk.BF16 if dt == "bf16" else llmk.F32
+    pool = llmk.KVPool(n_layer, n_slots, cap, Hkv, hd, kv)
+    row = Hkv * hd
+    fields = dict(n_layer=n_layer, n_slots=n_slots, capacity=cap, n_kv=Hkv, head_dim=hd, dtype=kv)
+    before = {(l, w): host(t).copy() for l in range(n_layer) for w, t in ((0, pool.k[l]), (1, pool.v[l]))}
+    written = {}
+    slot, layer, n_pos = 2, 1, 70
+    vals = {w: synth.normal((n_pos, row), 30 + w, 0, 1.0) for w in (0, 1)}
+    for p in range(n_pos):
+        for w in (0, 1):
+            cl = p * row
+            exp = contract.kv_append(fields, layer, slot, w, cl, cl, True, row, row)
+            st, nl, off = llmk.kv_append(pool, layer, slot, w, cl, dev(vals[w][p]))
+            assert (st, nl, off) == exp, (p, w)
+            st2, off2 = llmk.kv_slot_offset(pool, slot, p, 0)
+            assert st2 == llmk.OK and off2 == off and contract.kv_slot_offset(n_slots, cap, Hkv, hd, slot, p, 0)[1] == off
+    assert pool.len_k[layer, slot] == pool.len_v[layer, slot] == n_pos * row
+    # a wrong claim of the fill is refused and changes nothing
+    st, _, _ = llmk.kv_append(pool, layer, slot, 0, (n_pos - 1) * row, dev(vals[0][0]))
+    assert st == 566 and pool.len_k[layer, slot] == n_pos * row
+    _sync()
+    plane = cap * row
+    for w, t in ((0, pool.k[layer]), (1, pool.v[layer])):
+        got = host(t)
+        ref = oracle.kv_append_copy(np.zeros(0, np.uint16 if dt == "bf16" else np.float32), vals[w].ravel(), dt)
+        assert np.array_equal(got[slot * plane:slot * plane + n_pos * row], ref)
+        rest = np.concatenate([got[:slot * plane], got[slot * plane + n_pos * row:]])
+        old = before[(layer, w)]
+        assert np.array_equal(rest, np.concatenate([old[:slot * plane], old[slot * plane + n_pos * row:]]))
+    for l in range(n_layer):
+        if l != layer:
+            assert np.array_equal(host(pool.k[l]), before[(l, 0)]) and np.array_equal(host(pool.v[l]), before[(l, 1)])
+    # attention over the slot, at several context lengths, against the oracle on the oracle's own K/V
+    for ctx in (1, 33, n_pos):
+        q = synth.normal((H * hd,), 31, ctx, 1.0)
+        kk = oracle.kv_append_copy(np.zeros(0, np.uint16 if dt == "bf16" else np.float32), vals[0][:ctx].ravel(), dt)
+        vv = oracle.kv_append_copy(np.zeros(0, np.uint16 if dt == "bf16" else np.float32), vals[1][:ctx].ravel(), dt)
+        out = torch.full((H * hd,), float("nan"), dtype=torch.float32, device="cuda")
+        ws = llmk.workspace(llmk.gqa_attend_workspace_bytes(ctx, H, hd))
+        assert llmk.gqa_attend(dev(q), pool, layer, slot, ctx, H, out, ws) == llmk.OK
+        _sync()
+        ref = oracle.attend_f32(q, kk.reshape(ctx, Hkv, hd), vv.reshape(ctx, Hkv, hd), ctx, H, Hkv, hd)
+        assert rel_err(host(out), ref) <= TOL, ctx
+    # more positions than the records hold is refused
+    ws = llmk.workspace(llmk.gqa_attend_workspace_bytes(n_pos + 1, H, hd))
+    out = torch.zeros(H * hd, dtype=torch.float32, device="cuda")
+    assert llmk.gqa_attend(dev(q), pool, layer, slot, n_pos + 1, H, out, ws) == 566
 
 
 # ---------------------------------------------------------------------------------------------

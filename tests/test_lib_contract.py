@@ -11,6 +11,7 @@ import itertools
 import os
 import re
 
+import numpy as np
 import pytest
 
 from oracle import contract
@@ -125,13 +126,15 @@ def test_rope_refusals():
             if exp != contract.OK:
                 assert L.llmk_rope_table_init(_nz(t), lt, mp, hd, base, None) == exp
     for q, k, tab in itertools.product([True, False], repeat=3):
-        for rows, nq, nk, hd, pos0, layout in itertools.product([0, 2], [0, 4], [-1, 0, 2], [6, 7], [-1, 0, 9],
-                                                                [0, 1, 2]):
-            for lq, lk, lt in itertools.product([rows * nq * hd, 1], [rows * max(nk, 0) * hd, 1], [10 * hd, 3]):
-                exp = contract.rope(q, lq, k, lk, rows, nq, nk, hd, pos0, tab, lt, 10, layout)
+        for rows, nq, nk, hd, pos, layout in itertools.product([0, 2], [0, 4], [-1, 0, 2], [6, 7], [True, False],
+                                                               [0, 1, 2]):
+            for lq, lk, lt, lp in itertools.product([rows * nq * hd, 1], [rows * max(nk, 0) * hd, 1], [10 * hd, 3],
+                                                    [rows, 3]):
+                exp = contract.rope(q, lq, k, lk, rows, nq, nk, hd, pos, lp, tab, lt, 10, layout)
                 if exp != contract.OK:
-                    got = L.llmk_rope(_nz(q), lq, _nz(k), lk, rows, nq, nk, hd, pos0, _nz(tab), lt, 10, layout, None)
-                    assert got == exp, (q, k, tab, rows, nq, nk, hd, pos0, layout, lq, lk, lt)
+                    got = L.llmk_rope(_nz(q), lq, _nz(k), lk, rows, nq, nk, hd, _nz(pos), lp, _nz(tab), lt, 10,
+                                      layout, None)
+                    assert got == exp, (q, k, tab, rows, nq, nk, hd, pos, layout, lq, lk, lt, lp)
 
 
 @no_gpu
@@ -140,11 +143,86 @@ def test_kv_append_refusals():
     out = ctypes.c_int64(-7)
     for c, nv, dt in itertools.product([True, False], [True, False], [0, 1, 2]):
         for cap, cl, lc, nn, ln in itertools.product([0, 9, 8], [-1, 0, 6], [6, 5], [0, 3], [3, 2]):
-            exp = contract.kv_append(c, cap, dt, cl, lc, nv, ln, nn)
+            exp = contract.kv_append_flat(c, cap, dt, cl, lc, nv, ln, nn)
             if exp != contract.OK:
-                got = L.llmk_kv_append(_nz(c), cap, dt, cl, lc, _nz(nv), ln, nn, ctypes.byref(out), None)
+                got = L.llmk_kv_append_flat(_nz(c), cap, dt, cl, lc, _nz(nv), ln, nn, ctypes.byref(out), None)
                 assert got == exp, (c, nv, dt, cap, cl, lc, nn, ln)
                 assert out.value == -7  # untouched on refusal
+
+
+class _FakePool:
+    """A pool descriptor over fake (never dereferenced) device addresses, for host-only checks."""
+
+    def __init__(self, n_layer=2, n_slots=3, capacity=8, n_kv=2, head_dim=4, dtype=0, arrays=True, buffers=True,
+                 records=True):
+        self.fields = dict(n_layer=n_layer, n_slots=n_slots, capacity=capacity, n_kv=n_kv, head_dim=head_dim,
+                           dtype=dtype, arrays=arrays, buffers=buffers, records=records)
+        nl = max(0, min(n_layer, 4))
+        ptrs = [FAKE] * nl
+        if not buffers and nl:
+            ptrs[-1] = FAKE + 2   # a misaligned layer buffer
+        self.kp = (ctypes.c_void_p * max(nl, 1))(*ptrs)
+        self.vp = (ctypes.c_void_p * max(nl, 1))(*([FAKE] * nl))
+        ns = max(0, min(n_slots, 8))
+        self.slot_len = np.full(max(ns, 1), 5, dtype=np.int64)
+        self.len_k = np.full((max(nl, 1), max(ns, 1)), 7, dtype=np.int64)
+        self.len_v = np.full((max(nl, 1), max(ns, 1)), 7, dtype=np.int64)
+        P = ctypes.POINTER(ctypes.c_int64)
+        self.struct = llmk.PoolStruct(self.kp if arrays else None, self.vp, n_layer, n_slots, capacity, n_kv,
+                                      head_dim, dtype, self.slot_len.ctypes.data_as(P),
+                                      self.len_k.ctypes.data_as(P) if records else None,
+                                      self.len_v.ctypes.data_as(P) if records else None)
+
+
+POOL_CASES = [dict(), dict(arrays=False), dict(buffers=False), dict(dtype=2), dict(n_layer=0), dict(n_slots=-1),
+              dict(capacity=0), dict(head_dim=(1 << 24) + 1), dict(n_kv=0, buffers=False), dict(records=False)]
+
+
+@no_gpu
+def test_kv_pool_init():
+    for c in POOL_CASES:
+        fp = _FakePool(**c)
+        exp = contract.kv_pool_init(fp.fields)
+        got = llmk.lib.llmk_kv_pool_init(ctypes.byref(fp.struct))
+        assert got == exp, c
+        if got == contract.OK:   # every record of every slot marked empty
+            assert not fp.slot_len.any() and (not c.get("records", True) or not (fp.len_k.any() or fp.len_v.any()))
+        else:                    # refused: records untouched
+            assert (fp.slot_len == 5).all()
+    assert llmk.lib.llmk_kv_pool_init(None) == contract.kv_pool_init(None) == 578
+
+
+@no_gpu
+def test_pool_append_and_attend_refusals():
+    L = llmk.lib
+    for c in POOL_CASES:
+        for layer, slot, which, cl, nn, ln, rec in itertools.product([0, 2], [1, 3], [0, 2], [-1, 7, 6], [0, 2],
+                                                                      [2, 1], [7]):
+            fp = _FakePool(**c)
+            exp, _, _ = contract.kv_append(fp.fields, layer, slot, which, cl, rec, True, ln, nn)
+            if exp == contract.OK:
+                continue   # would launch
+            nl, off = ctypes.c_int64(-7), ctypes.c_int64(-7)
+            got = L.llmk_kv_append(ctypes.byref(fp.struct), layer, slot, which, cl, FAKE, ln, nn, ctypes.byref(nl),
+                                   ctypes.byref(off), None)
+            assert got == exp, (c, layer, slot, which, cl, nn, ln)
+            assert nl.value == -7 and off.value == -7 and (fp.len_k == 7).all() and (fp.len_v == 7).all()
+    # overrun of the slot's region: capacity 8 positions x 2 heads x 4 = 64 elements, 7 filled
+    fp = _FakePool()
+    assert contract.kv_append(fp.fields, 0, 0, 0, 7, 7, True, 58, 58)[0] == contract.CAPACITY
+    assert L.llmk_kv_append(ctypes.byref(fp.struct), 0, 0, 0, 7, FAKE, 58, 58, None, None, None) == contract.CAPACITY
+    assert L.llmk_kv_append(ctypes.byref(fp.struct), 0, 0, 0, 7, None, 2, 2, None, None, None) == contract.INVALID
+    for c in POOL_CASES:
+        for layer, slot, ctx, H, lq, lo in itertools.product([0, 2], [0, 3], [0, 1, 2, 9], [4, 3, 32], [16, 5],
+                                                             [16, 6]):
+            fp = _FakePool(**c)
+            rec = 7 if c.get("records", True) else None
+            exp = contract.gqa_attend(True, lq, fp.fields, layer, slot, ctx, H, True, lo, rec, rec)
+            if exp == contract.OK:
+                continue
+            got = L.llmk_gqa_attend(FAKE, lq, ctypes.byref(fp.struct), layer, slot, ctx, H, FAKE, lo, FAKE, 1 << 30,
+                                    None)
+            assert got == exp, (c, layer, slot, ctx, H, lq, lo)
 
 
 @no_gpu
@@ -152,9 +230,10 @@ def test_attend_and_argmax_refusals():
     L = llmk.lib
     for ctx, H, Hkv, hd, dt in itertools.product([0, 5], [4, 6], [2, 4, 3], [4, 6, 512], [0, 1, 7]):
         for lq, lc, lo in itertools.product([H * hd, 1], [ctx * Hkv * hd, 2], [H * hd, 3]):
-            exp = contract.gqa_attend(True, lq, True, True, lc, dt, ctx, H, Hkv, hd, True, lo)
+            exp = contract.gqa_attend_flat(True, lq, True, True, lc, dt, ctx, H, Hkv, hd, True, lo)
             if exp != contract.OK:
-                got = L.llmk_gqa_attend(FAKE, lq, FAKE, FAKE, lc, dt, ctx, H, Hkv, hd, FAKE, lo, FAKE, 1 << 30, None)
+                got = L.llmk_gqa_attend_flat(FAKE, lq, FAKE, FAKE, lc, dt, ctx, H, Hkv, hd, FAKE, lo, FAKE, 1 << 30,
+                                             None)
                 assert got == exp, (ctx, H, Hkv, hd, dt, lq, lc, lo)
     for rows, n, ll in itertools.product([0, 1, 3], [0, 7], [21, 7, 0]):
         exp = contract.argmax(True, ll, rows, n, True)
@@ -239,7 +318,8 @@ def _cfg_kwargs(**over):
 
 
 def test_config_checks_agree_with_oracle():
-    variants = [dict(), dict(vocab=0), dict(d=(1 << 24) + 1), dict(n_head=6), dict(n_kv=3), dict(head_dim=6),
+    variants = [dict(), dict(test_flags=1), dict(test_flags=2), dict(test_flags=-1), dict(vocab=0),
+                dict(d=(1 << 24) + 1), dict(n_head=6), dict(n_kv=3), dict(head_dim=6),
                 dict(head_dim=512), dict(n_head=32, n_kv=2), dict(hidden=22), dict(w_dtype=1), dict(w_dtype=3),
                 dict(rope_layout=2), dict(eps=0.0), dict(rope_base=1.0), dict(max_seq=-4), dict(kv_dtype=1),
                 dict(d=12, w_dtype=0), dict(d=24, w_dtype=1)]
@@ -504,14 +584,16 @@ def test_q8_pack_bytes_and_quantize_refusals():
     ok = dict(w=True, len_w=4 * 256, w_dtype=1, rows=4, cols=256, pack=True, len_pack=4 * 256 + 32)
     cases = [dict(), dict(w=False), dict(pack=False), dict(w_dtype=2), dict(w_dtype=-1), dict(rows=0), dict(cols=-128),
              dict(rows=(1 << 24) + 1), dict(cols=200, len_w=800), dict(len_w=4 * 256 - 1), dict(len_pack=4 * 256),
-             dict(len_pack=4 * 256 + 33)]
+             dict(len_pack=4 * 256 + 33), dict(aligned=False, w_off=2), dict(aligned=False, pack_off=8),
+             dict(aligned=False, pack_off=1, len_pack=7)]
     for c in cases:
         a = {**ok, **c}
+        w_off, pack_off = a.pop("w_off", 0), a.pop("pack_off", 0)
         exp = contract.quantize_q8(**a)
         if exp == contract.OK:
             continue   # only refusals run here (no device)
-        got = llmk.lib.llmk_quantize_q8(FA if a["w"] else None, a["len_w"], a["w_dtype"], a["rows"], a["cols"],
-                                        FA if a["pack"] else None, a["len_pack"], None)
+        got = llmk.lib.llmk_quantize_q8(FA + w_off if a["w"] else None, a["len_w"], a["w_dtype"], a["rows"], a["cols"],
+                                        FA + pack_off if a["pack"] else None, a["len_pack"], None)
         assert got == exp, c
 
 

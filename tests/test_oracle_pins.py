@@ -113,7 +113,14 @@ def test_contract_refusals():
     assert contract.gemv_dims_check(2, 3, 5, 2) == 569
     assert contract.gemv_dims_check(2, 3, 6, 3) == 570
     assert contract.gemv_dims_check(0, 3, 0, 0) == 561
-    assert contract.kv_append(capacity=8, cache_len=6, len_cache=6, n_new=3, len_new=3) == 571
+    assert contract.kv_append_flat(capacity=8, cache_len=6, len_cache=6, n_new=3, len_new=3) == 571
+    # the same append into slot 1 of a pool whose slots hold 4 positions of 2 x 2 elements (plane 16): the
+    # page's cache of 6 grows to 9, written at the slot's base plus the old fill
+    pool = dict(n_layer=1, n_slots=2, capacity=4, n_kv=2, head_dim=2)
+    assert contract.kv_append(pool, 0, 1, 0, 6, 6, True, 3, 3) == (560, 9, 16 + 6)
+    assert contract.kv_append(pool, 0, 1, 1, 6, 5, True, 3, 3)[0] == 566
+    assert contract.kv_append(pool, 0, 1, 0, 14, 14, True, 3, 3)[0] == 571
+    assert contract.kv_append(pool, 0, 2, 0, 6, 6, True, 3, 3)[0] == 575
 
 
 # ---------------------------------------------------------------------------------------------
