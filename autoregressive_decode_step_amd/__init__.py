@@ -93,6 +93,7 @@ _SIGS = {
     "llmk_gqa_attend": ([_p, _i64, ctypes.POINTER(PoolStruct), _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_argmax_workspace_bytes": ([_i64, _i64], _i64),
     "llmk_argmax": ([_p, _i64, _i64, _i64, _p, _p, _p, _i64, _p], _i32),
+    "llmk_argmax_noalloc": ([_p, _i64, _i64, _i64, _p, _p, _p], _i32),
     "llmk_sample_workspace_bytes": ([_i64, _i64, _f32, _i32], _i64),
     "llmk_prefill_workspace_bytes": ([ctypes.POINTER(Config), _i64], _i64),
     "llmk_prefill_profiled": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64,
@@ -266,6 +267,14 @@ def argmax_workspace_bytes(rows, n) -> int:
 def argmax(logits, rows, n, token, logit, ws, stream=None) -> int:
     return lib.llmk_argmax(_ptr(logits), _len(logits), rows, n, _ptr(token), _ptr(logit), _ptr(ws), _len(ws),
                            _stream(stream))
+
+
+ARGMAX_NOALLOC_MAX_ROWS = 256
+
+
+def argmax_noalloc(logits, rows, n, token, logit, stream=None) -> int:
+    """llmk_argmax without a workspace (the library's fixed per-GPU scratch; calls on one GPU must not overlap)."""
+    return lib.llmk_argmax_noalloc(_ptr(logits), _len(logits), rows, n, _ptr(token), _ptr(logit), _stream(stream))
 
 
 def sample_workspace_bytes(rows, n, temperature, top_k) -> int:

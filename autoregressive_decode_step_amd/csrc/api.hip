@@ -2,6 +2,7 @@
 // the decode step from the gfx950 kernels. See include/llmk.h for the contract of every entry point.
 #include <math.h>
 #include <algorithm>
+#include <mutex>
 #include <string.h>
 
 #include <vector>
@@ -15,7 +16,39 @@
 
 using namespace llmk;
 
+// Scratch of llmk_argmax_noalloc, for callers that cannot allocate: the per-block partials and tickets of
+// LLMK_ARGMAX_NOALLOC_MAX_ROWS rows of at most 64 blocks each (two 64 KiB partial arrays and the tickets,
+// each region 256-byte aligned). Every GPU the library runs this entry point on holds its own copy until
+// the process ends. Host code never uses this name as an address: it asks the runtime for the array's
+// address on each device once and passes that pointer.
+static constexpr int64_t kArgmaxScratchBytes = 2 * 65536 + 1024;
+static __device__ __align__(256) unsigned char scratch[kArgmaxScratchBytes];
+
 namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device `stream` runs on, looked up once per device with that device
+// current (nullptr on failure).
+void* scratch_on(hipStream_t stream) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  hipDevice_t dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 constexpr int64_t kMaxDim = LLMK_MAX_DIM;
 constexpr int64_t kAlign = 256;
@@ -1475,14 +1508,10 @@ int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n) {
   return c.off;
 }
 
-int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token, float* logit,
-                    void* ws, int64_t len_ws, void* stream) {
-  if (!logits || !token || !ws) return LLMK_INVALID_ARGUMENT;
-  int32_t st = dims_check({rows, n});
-  if (st != LLMK_OK) return st;
-  if (len_logits != rows * n) return LLMK_LOGITS_LENGTH_MISMATCH;
-  if (len_ws < llmk_argmax_workspace_bytes(rows, n)) return LLMK_INVALID_ARGUMENT;
-  if (rows > 65535) return LLMK_DIMENSION_TOO_LARGE;
+// the argmax launch shared by llmk_argmax and llmk_argmax_noalloc (every check done): partials and tickets
+// carved from `ws`, the tickets cleared by a fill kernel
+static int32_t argmax_run(const float* logits, int64_t rows, int64_t n, int32_t* token, float* logit, void* ws,
+                          void* stream) {
   const int64_t bpr = n >= 65536 ? 64 : (n + 1023) / 1024;
   Carve cv(ws);
   float* pv = cv.take<float>(rows * bpr);
@@ -1491,6 +1520,30 @@ int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64
   hipError_t e = fill_u32_launch(cnt, rows, 0u, as_stream(stream));
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
   return finish(argmax_launch(logits, rows, n, token, logit, pv, pi, cnt, (int32_t)bpr, as_stream(stream)));
+}
+
+int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token, float* logit,
+                    void* ws, int64_t len_ws, void* stream) {
+  if (!logits || !token || !ws) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, n});
+  if (st != LLMK_OK) return st;
+  if (len_logits != rows * n) return LLMK_LOGITS_LENGTH_MISMATCH;
+  if (len_ws < llmk_argmax_workspace_bytes(rows, n)) return LLMK_INVALID_ARGUMENT;
+  if (rows > 65535) return LLMK_DIMENSION_TOO_LARGE;
+  return argmax_run(logits, rows, n, token, logit, ws, stream);
+}
+
+int32_t llmk_argmax_noalloc(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token,
+                            float* logit, void* stream) {
+  if (!logits || !token) return LLMK_INVALID_ARGUMENT;
+  int32_t st = dims_check({rows, n});
+  if (st != LLMK_OK) return st;
+  if (len_logits != rows * n) return LLMK_LOGITS_LENGTH_MISMATCH;
+  if (rows > LLMK_ARGMAX_NOALLOC_MAX_ROWS || llmk_argmax_workspace_bytes(rows, n) > kArgmaxScratchBytes)
+    return LLMK_DIMENSION_TOO_LARGE;
+  void* ws = scratch_on(as_stream(stream));
+  if (!ws) return LLMK_DEVICE_ERROR;
+  return argmax_run(logits, rows, n, token, logit, ws, stream);
 }
 
 int64_t llmk_sample_workspace_bytes(int64_t rows, int64_t n, float temperature, int32_t top_k) {

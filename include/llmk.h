@@ -232,6 +232,18 @@ int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n);
 int32_t llmk_argmax(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token,
                     float* logit, void* ws, int64_t len_ws, void* stream);
 
+/* llmk_argmax for callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same result, with the per-block partials and tickets in a
+ * fixed scratch array the library holds on each GPU (about 129 KiB, kept until the process ends) instead of
+ * a caller workspace. The call allocates nothing. Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (different streams, or host threads) race and must be serialised by the caller.
+ *   token: device int32 [rows]; logit: device fp32 [rows] (may be NULL)
+ * Codes: 578 (null logits/token), 561, 564, 568 (len_logits != rows*n), 564 (rows >
+ * LLMK_ARGMAX_NOALLOC_MAX_ROWS), 579 (the array's address could not be obtained). */
+#define LLMK_ARGMAX_NOALLOC_MAX_ROWS 256
+int32_t llmk_argmax_noalloc(const float* logits, int64_t len_logits, int64_t rows, int64_t n, int32_t* token,
+                            float* logit, void* stream);
+
 /* Survivors llmk_sample holds: top_k after clamping to n (1 at temperature 0); rows one call takes. */
 #define LLMK_SAMPLE_MAX_K 1024
 #define LLMK_SAMPLE_MAX_ROWS 65535
