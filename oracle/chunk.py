@@ -1,0 +1,194 @@
+"""THE ORACLE's chunked forward -- test infrastructure only (see the package docstring).
+
+The decode step of the C oracle (`oracle.Model.forward_token`) applied to many rows at once, in fp64 numpy:
+the same arithmetic, taken a layer at a time over all rows so that the weight products run as matrix
+products (a library primitive) instead of one mat-vec per token. This is how the pages run a prompt: "Inside
+the engine", section "1. CausalLM: the forward path", takes a chunk of prompt rows through each layer, and
+decode is the one-row chunk of the same step; "The forward pass end to end", section "The code", defines
+what every row computes (forward_token). Two forms:
+
+  forward_chunk  rows of ONE sequence at consecutive positions (a prompt, or the tokens a decode run fed
+                 itself, teacher-forced): every row's K/V is appended at its position before any row
+                 attends, and row i attends positions 0..pos0 + i -- exactly what the token-by-token order
+                 sees, because row i never reads a position after its own.
+  forward_rows   one row each of MANY sequences (the batched decode step): every row attends its own
+                 cached prefix plus its own new K/V.
+
+Arithmetic (as the C oracle): fp64 from the exact stored inputs (bf16 and fp32 widen exactly), K/V rounded to
+the cache dtype via fp32 (bf16 by round-to-nearest-even) where they are stored, logits and hidden states
+rounded to fp32 on output. Only the order of the fp64 sums differs from the token-by-token oracle (matrix
+products block their sums), a difference of a few fp64 ulps; the pins hold the two forms together.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+HALF_SPLIT, INTERLEAVED = 0, 1
+
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """Stored values (bf16 bit patterns as uint16, fp32, fp64) widened to fp64, exactly."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def round_kv(v: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """fp64 values stored in the cache dtype: one rounding to fp32, then for bf16 round-to-nearest-even on
+    the fp32 bits (a NaN stays a quiet NaN)."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    if kv_dtype == "f32":
+        return f
+    u = f.view(np.uint32).astype(np.uint64)
+    b = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        b[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return b
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Per row: x * (mean(x^2) + eps)^(-1/2) * g ("The code": rmsnorm, eps inside the mean)."""
+    ms = np.sum(x * x, axis=-1, keepdims=True) / x.shape[-1]
+    return x * (1.0 / np.sqrt(ms + eps)) * to_f64(g)
+
+
+def rope(v: np.ndarray, positions: np.ndarray, base: float, layout: int) -> np.ndarray:
+    """Rotate v [rows][heads][hd] in place, row r by positions[r]: pair j turned by pos * base^(-2j/hd), angles
+    in fp64; half-split pairs (j, j + hd/2), interleaved pairs (2j, 2j + 1) ("decode-ops", "Method")."""
+    hd = v.shape[-1]
+    half = hd // 2
+    j = np.arange(half, dtype=np.float64)
+    inv = np.power(float(base), -(2.0 * j) / float(hd))
+    theta = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]     # [rows][half]
+    c, s = np.cos(theta)[:, None, :], np.sin(theta)[:, None, :]
+    if layout == INTERLEAVED:
+        a, b = v[..., 0::2].copy(), v[..., 1::2].copy()
+        v[..., 0::2] = a * c - b * s
+        v[..., 1::2] = a * s + b * c
+    else:
+        a, b = v[..., :half].copy(), v[..., half:].copy()
+        v[..., :half] = a * c - b * s
+        v[..., half:] = a * s + b * c
+    return v
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int, n_kv: int) -> np.ndarray:
+    """One query row q [n_head][hd] over k, v [ctx][n_kv][hd] (fp64): head h reads K/V head h // (n_head / n_kv);
+    scores q . k / sqrt(hd), softmax with the maximum subtracted, weighted sum of v ("The code")."""
+    hd = q.shape[-1]
+    group = n_head // n_kv
+    out = np.empty((n_head, hd))
+    for g in range(n_kv):
+        qg = q[g * group:(g + 1) * group]                   # [group][hd]
+        s = (qg @ k[:, g, :].T) / np.sqrt(float(hd))         # [group][ctx]
+        s = np.exp(s - s.max(axis=1, keepdims=True))
+        s /= s.sum(axis=1, keepdims=True)
+        out[g * group:(g + 1) * group] = s @ v[:, g, :]
+    return out
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+class Weights:
+    """fp64 copies of a decoder's weights (the dict synth.model / synth.page_draws returns), made one layer at
+    a time on request and dropped by `release`, so an 8B-shaped model never sits in fp64 all at once."""
+
+    def __init__(self, shape, W: dict):
+        self.s, self.W = shape, W
+        self._layer = {}
+
+    def layer(self, l: int) -> dict:
+        if l not in self._layer:
+            self._layer = {l: {k: to_f64(v) for k, v in self.W["layers"][l].items()}}
+        return self._layer[l]
+
+    def release(self) -> None:
+        self._layer = {}
+
+    def emb_rows(self, tokens) -> np.ndarray:
+        return to_f64(self.W["emb"][np.asarray(tokens, dtype=np.int64)])
+
+    def head(self, h: np.ndarray, rows_per_block: int = 8192) -> np.ndarray:
+        """logits = h W_out^T, W_out [V][d] widened a block of vocabulary rows at a time."""
+        out = self.W["out"]
+        V = out.shape[0]
+        lg = np.empty((h.shape[0], V))
+        for r0 in range(0, V, rows_per_block):
+            lg[:, r0:r0 + rows_per_block] = h @ to_f64(out[r0:r0 + rows_per_block]).T
+        return lg
+
+
+def _layer_tail(s, Wl: dict, x: np.ndarray, att: np.ndarray) -> None:
+    """x += att Wo; x += (silu(h Wg) * (h Wu)) Wd with h = rmsnorm(x) g2, for every row (in place)."""
+    x += att @ Wl["wo"]
+    h = rmsnorm(x, Wl["n2"], s.eps)
+    x += (silu(h @ Wl["gate"]) * (h @ Wl["up"])) @ Wl["down"]
+
+
+def forward_chunk(shape, weights: Weights, tokens, pos0: int, cache, want_hidden: bool = True):
+    """Rows tokens[i] at positions pos0 + i of the sequence whose K/V live in `cache` (an oracle.Cache, K/V
+    [max_seq][n_kv][hd] in the cache dtype; positions before pos0 already filled). Writes every row's K/V,
+    returns (logits fp32 [T][V], hidden fp32 [T][L][d] or None)."""
+    s = shape
+    T = len(tokens)
+    pos = pos0 + np.arange(T)
+    H, Hkv, hd = s.n_head, s.n_kv, s.head_dim
+    x = weights.emb_rows(tokens)
+    hidden = np.empty((T, s.n_layer, s.d), dtype=np.float32) if want_hidden else None
+    for l in range(s.n_layer):
+        Wl = weights.layer(l)
+        h = rmsnorm(x, Wl["n1"], s.eps)
+        q = rope((h @ Wl["wq"]).reshape(T, H, hd), pos, s.rope_base, s.rope_layout)
+        k = rope((h @ Wl["wk"]).reshape(T, Hkv, hd), pos, s.rope_base, s.rope_layout)
+        v = (h @ Wl["wv"]).reshape(T, Hkv, hd)
+        cache.k[l][pos0:pos0 + T] = round_kv(k, s.kv_dtype)
+        cache.v[l][pos0:pos0 + T] = round_kv(v, s.kv_dtype)
+        kc = to_f64(cache.k[l][:pos0 + T])
+        vc = to_f64(cache.v[l][:pos0 + T])
+        att = np.empty((T, H * hd))
+        for i in range(T):
+            att[i] = attend(q[i], kc[:pos0 + i + 1], vc[:pos0 + i + 1], H, Hkv).ravel()
+        _layer_tail(s, Wl, x, att)
+        if want_hidden:
+            hidden[:, l] = x
+    weights.release()
+    logits = weights.head(rmsnorm(x, weights.W["norm"], s.eps)).astype(np.float32)
+    cache.length = max(getattr(cache, "length", 0), pos0 + T)
+    return logits, hidden
+
+
+def forward_rows(shape, weights: Weights, tokens, positions, prefix, want_hidden: bool = True):
+    """One decode step of B sequences: row b feeds tokens[b] at positions[b] and attends its own cached
+    positions 0..positions[b] - 1, given by prefix(l, b) -> (K, V) arrays [positions[b]][n_kv][hd] in the cache
+    dtype, plus the K/V it appends. Returns (logits fp32 [B][V], hidden fp32 [B][L][d] or None, new K/V per
+    layer as a list of (K [B][n_kv][hd], V [B][n_kv][hd]) in the cache dtype)."""
+    s = shape
+    B = len(tokens)
+    pos = np.asarray(positions, dtype=np.int64)
+    H, Hkv, hd = s.n_head, s.n_kv, s.head_dim
+    x = weights.emb_rows(tokens)
+    hidden = np.empty((B, s.n_layer, s.d), dtype=np.float32) if want_hidden else None
+    new_kv = []
+    for l in range(s.n_layer):
+        Wl = weights.layer(l)
+        h = rmsnorm(x, Wl["n1"], s.eps)
+        q = rope((h @ Wl["wq"]).reshape(B, H, hd), pos, s.rope_base, s.rope_layout)
+        k = round_kv(rope((h @ Wl["wk"]).reshape(B, Hkv, hd), pos, s.rope_base, s.rope_layout), s.kv_dtype)
+        v = round_kv((h @ Wl["wv"]).reshape(B, Hkv, hd), s.kv_dtype)
+        new_kv.append((k, v))
+        att = np.empty((B, H * hd))
+        for b in range(B):
+            pk, pv = prefix(l, b)
+            assert pk.shape[0] == pos[b] and pv.shape[0] == pos[b]
+            kc = np.concatenate([to_f64(pk), to_f64(k[b:b + 1])])
+            vc = np.concatenate([to_f64(pv), to_f64(v[b:b + 1])])
+            att[b] = attend(q[b], kc, vc, H, Hkv).ravel()
+        _layer_tail(s, Wl, x, att)
+        if want_hidden:
+            hidden[:, l] = x
+    weights.release()
+    logits = weights.head(rmsnorm(x, weights.W["norm"], s.eps)).astype(np.float32)
+    return logits, hidden, new_kv

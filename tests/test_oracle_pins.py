@@ -409,3 +409,109 @@ def test_forward_token_refuses_out_of_range():
         m.forward_token(40, 0, c)
     with pytest.raises(ValueError):
         m.forward_token(1, 8, c)
+
+
+# ---------------------------------------------------------------------------------------------
+# the chunked forward (oracle/chunk.py): the same step for many rows at once, held to the
+# token-by-token oracle (itself pinned above) and to the page's printed tokens
+# ---------------------------------------------------------------------------------------------
+
+from oracle import chunk  # noqa: E402
+
+MID = synth.Shape("mid bf16 (V300 d64 L2 H4/2 hd16 F96)", 300, 64, 2, 4, 2, 16, 96, 96, 1e-5, 1e4,
+                  synth.ROPE_HALF_SPLIT, "bf16", "bf16", 0.08)
+
+
+def _close(a, b, tol=1e-9):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)) <= tol
+
+
+def _bf16_ulps(a, b):
+    """Largest distance in bf16 steps between two arrays of bf16 bit patterns of the same sign pattern."""
+    return int(np.max(np.abs(a.astype(np.int64) - b.astype(np.int64)))) if a.size else 0
+
+
+@pytest.mark.parametrize("shape_name,layout", [("tiny", synth.ROPE_INTERLEAVED), ("tiny", synth.ROPE_HALF_SPLIT),
+                                               ("mid", synth.ROPE_HALF_SPLIT), ("mid", synth.ROPE_INTERLEAVED)])
+def test_chunk_forward_equals_token_by_token(shape_name, layout):
+    """A prompt as two chunks (10 rows, then 30) gives the token-by-token oracle's logits, hidden states and
+    K/V (fp64 sums in another order: relative 1e-9; stored K/V at most one step of their dtype apart)."""
+    if shape_name == "tiny":
+        s = synth.TINY.with_(rope_layout=layout)
+        W = synth.as_f32(synth.page_draws(s))
+    else:
+        s = MID.with_(rope_layout=layout)
+        W = synth.model(s, seed=5)
+    toks = synth.prompt(40, s.vocab, stream=50).tolist()
+    m = oracle.Model(s, W)
+    c1 = m.new_cache(s.max_seq)
+    ref = [m.forward_token(t, p, c1, want_hidden=True) for p, t in enumerate(toks)]
+    c2 = m.new_cache(s.max_seq)
+    w = chunk.Weights(s, W)
+    lg_a, hid_a = chunk.forward_chunk(s, w, toks[:10], 0, c2)
+    lg_b, hid_b = chunk.forward_chunk(s, w, toks[10:], 10, c2)
+    lg, hid = np.concatenate([lg_a, lg_b]), np.concatenate([hid_a, hid_b])
+    for p in range(len(toks)):
+        assert _close(lg[p], ref[p][0]) and _close(hid[p], ref[p][1]), p
+        assert oracle.argmax(lg[p])[0] == oracle.argmax(ref[p][0])[0]
+    for l in range(s.n_layer):
+        for a, b in ((c1.k[l], c2.k[l]), (c1.v[l], c2.v[l])):
+            if s.kv_dtype == "bf16":
+                assert _bf16_ulps(a[:40], b[:40]) <= 1
+            else:
+                assert _close(a[:40], b[:40], 1e-6)
+
+
+def test_chunk_forward_reproduces_the_pages_printed_tokens():
+    """The page's prompt through one chunk, then one-row chunks fed their own greedy tokens: the page's
+    printed first tokens, and the token-by-token oracle's whole run."""
+    g = golden("page_decode.json")
+    s = synth.TINY.with_(rope_layout=synth.ROPE_INTERLEAVED)
+    W = synth.as_f32(synth.page_draws(s, seed=g["config"]["seed"], std=g["config"]["weight_std"]))
+    m = oracle.Model(s, W)
+    ref, _, _ = oracle.generate(m, g["prompt"], g["n_new"], s.max_seq)
+    w = chunk.Weights(s, W)
+    c = m.new_cache(s.max_seq)
+    lg, _ = chunk.forward_chunk(s, w, g["prompt"], 0, c, want_hidden=False)
+    toks = [oracle.argmax(lg[-1])[0]]
+    pos = len(g["prompt"])
+    while len(toks) < g["n_new"]:
+        lg, _ = chunk.forward_chunk(s, w, [toks[-1]], pos, c, want_hidden=False)
+        toks.append(oracle.argmax(lg[0])[0])
+        pos += 1
+    assert toks[:3] == g["printed_first_tokens"]
+    assert toks == ref
+
+
+def test_forward_rows_equals_each_sequence_stepped_alone():
+    """Five sequences at ragged lengths, one batched step: each row's logits, hidden state and appended K/V
+    equal that sequence's token-by-token step."""
+    s = MID
+    W = synth.model(s, seed=6)
+    m = oracle.Model(s, W)
+    lens = [1, 7, 30, 2, 55]
+    caches, toks = [], []
+    for b, n in enumerate(lens):
+        c = m.new_cache(s.max_seq)
+        for p, t in enumerate(synth.prompt(n, s.vocab, stream=60 + b).tolist()):
+            m.forward_token(t, p, c)
+        caches.append(c)
+        toks.append(int(synth.prompt(1, s.vocab, stream=70 + b)[0]))
+    pre = [(np.array([c.k[l][:n].copy() for l in range(s.n_layer)]), np.array([c.v[l][:n].copy() for l in range(s.n_layer)]))
+           for c, n in zip(caches, lens)]
+    w = chunk.Weights(s, W)
+    lg, hid, new_kv = chunk.forward_rows(s, w, toks, lens, lambda l, b: (pre[b][0][l], pre[b][1][l]))
+    for b, (c, n) in enumerate(zip(caches, lens)):
+        ref_lg, ref_hid = m.forward_token(toks[b], n, c, want_hidden=True)
+        assert _close(lg[b], ref_lg) and _close(hid[b], ref_hid), b
+        for l in range(s.n_layer):
+            assert _bf16_ulps(new_kv[l][0][b], c.k[l][n]) <= 1 and _bf16_ulps(new_kv[l][1][b], c.v[l][n]) <= 1
+
+
+def test_round_kv_matches_the_c_oracle_rounding():
+    vals = np.concatenate([np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 3 * 2.0 ** -8), np.nan, 3.0e38,
+                                     -np.inf, 0.0, -0.0]), synth.normal((2000,), 71, 0, 3.0).astype(np.float64)])
+    assert np.array_equal(chunk.round_kv(vals, "bf16"), oracle.f32_to_bf16(vals.astype(np.float32)))
+    assert np.array_equal(chunk.to_f64(chunk.round_kv(vals, "bf16")[8:]),
+                          oracle.bf16_to_f64(oracle.f32_to_bf16(vals[8:].astype(np.float32))))
