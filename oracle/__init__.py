@@ -83,6 +83,9 @@ def lib():
                                    i64, i64, p, p], ctypes.c_int),
             "orc_num_threads": ([], ctypes.c_int),
             "orc_bf16_to_double": ([ctypes.c_uint16], f64),
+            "orc_widen": ([p, i32, i64, p], None),
+            "orc_softmax_rows": ([p, i64, i64, p], None),
+            "orc_silu_mul_inplace": ([p, p, i64], None),
             "orc_float_to_bf16": ([ctypes.c_float], ctypes.c_uint16),
         }
         for name, (args, res) in sig.items():
@@ -234,6 +237,32 @@ def kv_append_copy(cache: np.ndarray, new_vals: np.ndarray, dtype: str = "f32") 
     n = lib().orc_kv_append_copy(_ptr(c), c.size, _ptr(nv), nv.size, dt, _ptr(out))
     assert n == out.size
     return out
+
+
+def widen(a: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Stored fp32 values or bf16 bit patterns (uint16) widened to fp64 (exact), all host threads; into `out`
+    (fp64, contiguous, a.size elements) when given."""
+    src = np.ascontiguousarray(a)
+    if out is None:
+        out = np.empty(src.shape, dtype=np.float64)
+    assert out.dtype == np.float64 and out.flags.c_contiguous and out.size == src.size
+    lib().orc_widen(_ptr(src), _dtype_of(src), src.size, _ptr(out))
+    return out.reshape(src.shape)
+
+
+def softmax_rows(s: np.ndarray, last: np.ndarray) -> np.ndarray:
+    """In place: each row of s [rows][cols] (fp64, contiguous) softmaxed over entries 0..last[row], the rest 0."""
+    assert s.dtype == np.float64 and s.flags.c_contiguous
+    la = np.ascontiguousarray(last, dtype=np.int64)
+    lib().orc_softmax_rows(_ptr(s), s.shape[0], s.shape[1], _ptr(la))
+    return s
+
+
+def silu_mul_inplace(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """In place: g = silu(g) * u (fp64, contiguous, same shape)."""
+    assert g.dtype == np.float64 and u.dtype == np.float64 and g.flags.c_contiguous and u.flags.c_contiguous
+    lib().orc_silu_mul_inplace(_ptr(g), _ptr(u), g.size)
+    return g
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

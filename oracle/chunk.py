@@ -23,13 +23,15 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import silu_mul_inplace, softmax_rows, widen
+
 HALF_SPLIT, INTERLEAVED = 0, 1
 
 
 def to_f64(a: np.ndarray) -> np.ndarray:
     """Stored values (bf16 bit patterns as uint16, fp32, fp64) widened to fp64, exactly."""
-    if a.dtype == np.uint16:
-        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype in (np.uint16, np.float32):
+        return widen(a)
     return np.asarray(a, dtype=np.float64)
 
 
@@ -88,25 +90,56 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int, n_kv: int) 
     return out
 
 
+def attend_causal(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_head: int, n_kv: int, last: np.ndarray) -> np.ndarray:
+    """attend() for many query rows of one sequence at once: row i (q [T][n_head][hd]) sees positions
+    0..last[i] of k, v [ctx][n_kv][hd] (fp64); the positions past last[i] get weight exp(-inf) = 0, so each
+    row's softmax is over exactly its own context. Returns [T][n_head][hd]."""
+    T, hd = q.shape[0], q.shape[-1]
+    group = n_head // n_kv
+    ctx = k.shape[0]
+    out = np.empty((T, n_head, hd))
+    last = np.asarray(last, dtype=np.int64)
+    for g in range(n_kv):
+        kg, vg = np.ascontiguousarray(k[:, g, :]), np.ascontiguousarray(v[:, g, :])
+        for r0 in range(0, T, 256):
+            r1 = min(T, r0 + 256)
+            qg = q[r0:r1, g * group:(g + 1) * group, :].reshape(-1, hd)         # [(r1-r0) group][hd]
+            sc = np.ascontiguousarray(qg @ kg.T / np.sqrt(float(hd)))            # [(r1-r0) group][ctx]
+            softmax_rows(sc, np.repeat(last[r0:r1], group))
+            out[r0:r1, g * group:(g + 1) * group] = (sc @ vg).reshape(r1 - r0, group, hd)
+    return out
+
+
 def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
 class Weights:
     """fp64 copies of a decoder's weights (the dict synth.model / synth.page_draws returns), made one layer at
-    a time on request and dropped by `release`, so an 8B-shaped model never sits in fp64 all at once."""
+    a time on request into buffers reused from layer to layer, so an 8B-shaped model never sits in fp64 all at
+    once (and the host does not fault in fresh pages for every layer)."""
 
     def __init__(self, shape, W: dict):
         self.s, self.W = shape, W
-        self._layer = {}
+        self._l = None
+        self._buf = {}
+
+    def _widen(self, key, a: np.ndarray) -> np.ndarray:
+        b = self._buf.get(key)
+        if b is None or b.size != a.size:
+            b = self._buf[key] = np.empty(a.size, dtype=np.float64)
+        return widen(a, b)
 
     def layer(self, l: int) -> dict:
-        if l not in self._layer:
-            self._layer = {l: {k: to_f64(v) for k, v in self.W["layers"][l].items()}}
-        return self._layer[l]
+        if self._l != l:
+            self._cur = {k: self._widen(k, v) for k, v in self.W["layers"][l].items()}
+            self._l = l
+        return self._cur
 
     def release(self) -> None:
-        self._layer = {}
+        self._l = None
+        self._cur = None
+        self._buf = {}
 
     def emb_rows(self, tokens) -> np.ndarray:
         return to_f64(self.W["emb"][np.asarray(tokens, dtype=np.int64)])
@@ -117,7 +150,8 @@ class Weights:
         V = out.shape[0]
         lg = np.empty((h.shape[0], V))
         for r0 in range(0, V, rows_per_block):
-            lg[:, r0:r0 + rows_per_block] = h @ to_f64(out[r0:r0 + rows_per_block]).T
+            blk = out[r0:r0 + rows_per_block]
+            lg[:, r0:r0 + blk.shape[0]] = h @ self._widen("head" if blk.shape[0] == rows_per_block else "tail", blk).T
         return lg
 
 
@@ -125,7 +159,7 @@ def _layer_tail(s, Wl: dict, x: np.ndarray, att: np.ndarray) -> None:
     """x += att Wo; x += (silu(h Wg) * (h Wu)) Wd with h = rmsnorm(x) g2, for every row (in place)."""
     x += att @ Wl["wo"]
     h = rmsnorm(x, Wl["n2"], s.eps)
-    x += (silu(h @ Wl["gate"]) * (h @ Wl["up"])) @ Wl["down"]
+    x += silu_mul_inplace(np.ascontiguousarray(h @ Wl["gate"]), np.ascontiguousarray(h @ Wl["up"])) @ Wl["down"]
 
 
 def forward_chunk(shape, weights: Weights, tokens, pos0: int, cache, want_hidden: bool = True):
@@ -148,23 +182,50 @@ def forward_chunk(shape, weights: Weights, tokens, pos0: int, cache, want_hidden
         cache.v[l][pos0:pos0 + T] = round_kv(v, s.kv_dtype)
         kc = to_f64(cache.k[l][:pos0 + T])
         vc = to_f64(cache.v[l][:pos0 + T])
-        att = np.empty((T, H * hd))
-        for i in range(T):
-            att[i] = attend(q[i], kc[:pos0 + i + 1], vc[:pos0 + i + 1], H, Hkv).ravel()
+        att = attend_causal(q, kc, vc, H, Hkv, pos).reshape(T, H * hd)
         _layer_tail(s, Wl, x, att)
         if want_hidden:
             hidden[:, l] = x
-    weights.release()
     logits = weights.head(rmsnorm(x, weights.W["norm"], s.eps)).astype(np.float32)
+    weights.release()
     cache.length = max(getattr(cache, "length", 0), pos0 + T)
     return logits, hidden
 
 
-def forward_rows(shape, weights: Weights, tokens, positions, prefix, want_hidden: bool = True):
+def attend_pieces(q: np.ndarray, pieces, n_head: int, n_kv: int) -> np.ndarray:
+    """attend() for one query row over a context given as consecutive pieces [(K, V)], each HEAD-major
+    [n_kv][n][hd] (stored dtype or fp64): the scores of all pieces form one softmax per head, and the output
+    sums every piece's weighted values. Returns [n_head][hd] (fp64)."""
+    hd = q.shape[-1]
+    group = n_head // n_kv
+    pieces = [(k if k.dtype == np.float64 else to_f64(k), v if v.dtype == np.float64 else to_f64(v))
+              for k, v in pieces]
+    ctx = sum(k.shape[1] for k, _ in pieces)
+    sc = np.empty((n_head, ctx))
+    for g in range(n_kv):
+        qg, c0 = q[g * group:(g + 1) * group], 0
+        for k, _ in pieces:
+            m = k.shape[1]
+            sc[g * group:(g + 1) * group, c0:c0 + m] = qg @ k[g].T
+            c0 += m
+    sc /= np.sqrt(float(hd))
+    softmax_rows(sc, np.full(n_head, ctx - 1))
+    out = np.zeros((n_head, hd))
+    for g in range(n_kv):
+        c0 = 0
+        for _, v in pieces:
+            m = v.shape[1]
+            out[g * group:(g + 1) * group] += sc[g * group:(g + 1) * group, c0:c0 + m] @ v[g]
+            c0 += m
+    return out
+
+
+def forward_rows(shape, weights: Weights, tokens, positions, prefix, want_hidden: bool = True, progress=None):
     """One decode step of B sequences: row b feeds tokens[b] at positions[b] and attends its own cached
-    positions 0..positions[b] - 1, given by prefix(l, b) -> (K, V) arrays [positions[b]][n_kv][hd] in the cache
-    dtype, plus the K/V it appends. Returns (logits fp32 [B][V], hidden fp32 [B][L][d] or None, new K/V per
-    layer as a list of (K [B][n_kv][hd], V [B][n_kv][hd]) in the cache dtype)."""
+    positions 0..positions[b] - 1, given by prefix(l, b) as a list of consecutive pieces [(K, V)] (each
+    head-major [n_kv][n][hd], stored dtype or fp64, together positions[b] long), plus the K/V it appends. Returns (logits
+    fp32 [B][V], hidden fp32 [B][L][d] or None, new K/V per layer as a list of (K [B][n_kv][hd], V [B][n_kv][hd])
+    in the cache dtype). progress(l), when given, is called after each layer."""
     s = shape
     B = len(tokens)
     pos = np.asarray(positions, dtype=np.int64)
@@ -181,14 +242,15 @@ def forward_rows(shape, weights: Weights, tokens, positions, prefix, want_hidden
         new_kv.append((k, v))
         att = np.empty((B, H * hd))
         for b in range(B):
-            pk, pv = prefix(l, b)
-            assert pk.shape[0] == pos[b] and pv.shape[0] == pos[b]
-            kc = np.concatenate([to_f64(pk), to_f64(k[b:b + 1])])
-            vc = np.concatenate([to_f64(pv), to_f64(v[b:b + 1])])
-            att[b] = attend(q[b], kc, vc, H, Hkv).ravel()
+            pieces = list(prefix(l, b))
+            assert sum(pk.shape[1] for pk, _ in pieces) == pos[b]
+            new = (k[b:b + 1].transpose(1, 0, 2), v[b:b + 1].transpose(1, 0, 2))
+            att[b] = attend_pieces(q[b], pieces + [new], H, Hkv).ravel()
         _layer_tail(s, Wl, x, att)
         if want_hidden:
             hidden[:, l] = x
-    weights.release()
+        if progress:
+            progress(l)
     logits = weights.head(rmsnorm(x, weights.W["norm"], s.eps)).astype(np.float32)
+    weights.release()
     return logits, hidden, new_kv

@@ -61,6 +61,37 @@ static void store(void* base, int dtype, int64_t i, double v) {
 }
 
 double orc_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
+
+/* Softmax of each row of s [rows][cols] over its first last[r] + 1 entries, in place: the maximum subtracted,
+ * exp, divided by the sum; entries past last[r] become 0 (positions a query row does not see). Rows are
+ * independent, so OpenMP splits them. */
+void orc_softmax_rows(double* s, int64_t rows, int64_t cols, const int64_t* last) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double* row = s + r * cols;
+    const int64_t n = last[r] + 1 < cols ? last[r] + 1 : cols;
+    double m = row[0];
+    for (int64_t t = 1; t < n; ++t) if (row[t] > m) m = row[t];
+    double sum = 0.0;
+    for (int64_t t = 0; t < n; ++t) { row[t] = exp(row[t] - m); sum += row[t]; }
+    for (int64_t t = 0; t < n; ++t) row[t] /= sum;
+    for (int64_t t = n; t < cols; ++t) row[t] = 0.0;
+  }
+}
+
+double orc_silu(double z);
+
+/* g[i] = silu(g[i]) * u[i] in place (fp64), elements split over OpenMP threads. */
+void orc_silu_mul_inplace(double* g, const double* u, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) g[i] = orc_silu(g[i]) * u[i];
+}
+
+/* Widen n stored values (fp32 or bf16) to fp64, exactly; elements are independent, so OpenMP splits them. */
+void orc_widen(const void* src, int dtype, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = load(src, dtype, i);
+}
 uint16_t orc_float_to_bf16(float f) { return float_to_bf16(f); }
 
 /* ---- the primitives ------------------------------------------------------------------ */

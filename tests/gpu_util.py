@@ -29,3 +29,18 @@ def dev(a: np.ndarray):
 
 def say(msg: str) -> None:
     print(msg, flush=True)
+
+
+_WEIGHTS = {}
+
+
+def weights(shape, seed: int = 0) -> dict:
+    """synth.model(shape, seed), kept for the next caller with the same weight shape (one set at a time: an
+    8B-shaped set is 15 GB of host memory). The weights do not depend on max_seq."""
+    import synth
+    key = (shape.vocab, shape.d, shape.n_layer, shape.n_head, shape.n_kv, shape.head_dim, shape.hidden,
+           shape.w_dtype, shape.w_std, seed)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        _WEIGHTS[key] = synth.model(shape, seed=seed)
+    return _WEIGHTS[key]

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import TOL, host, rel_err, say
+from tests.gpu_util import TOL, host, rel_err, say, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def check_rows(shape, m, caches, rows, slots, tokens, pos, g_logits, g_hidden, g
 
 def test_tiny_batch_matches_oracle_per_row():
     s = TINY_BF16
-    W = synth.model(s, seed=0)
+    W = weights(s)
     ctxs = [0, 3, 17, 40, 9]
     slots = [4, 0, 2, 1, 3]
     B = len(slots)
@@ -127,7 +127,7 @@ def kv_vals(a):
 
 def test_batch_of_one_equals_single_sequence_step():
     s = TINY_BF16
-    W = synth.model(s, seed=0)
+    W = weights(s)
     cfg, model, pool = setup(s, W, n_slots=2, capacity=s.max_seq)
     pre = synth.kv_prefix(s, 11, seed=2)
     for slot in (0, 1):
@@ -148,7 +148,7 @@ def test_batch_of_one_equals_single_sequence_step():
 def q06():
     s = synth.Q06
     say("generating Qwen3-0.6B-shaped weights")
-    return s, synth.model(s, seed=0)
+    return s, weights(s)
 
 
 def test_q06_batch_of_16_ragged(q06):

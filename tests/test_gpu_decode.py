@@ -12,7 +12,7 @@ import pytest
 import oracle
 import synth
 from tests.conftest import golden
-from tests.gpu_util import TOL, dev, host, rel_err, say
+from tests.gpu_util import TOL, dev, host, rel_err, say, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -245,7 +245,7 @@ def test_persistent_wait_give_up_returns_device_error():
     slot's length alone, and a normal step on the same workspace and pool then matches the oracle."""
     import time
     s = TINY_BF16
-    W = synth.model(s, seed=0)
+    W = weights(s)
     cfg, model, pool, dec = build(s, W, step_path=llmk.STEP_PERSISTENT)
     assert llmk.decode_path(cfg) == llmk.STEP_PERSISTENT
     bad = loader.config_from(s, llmk.W_OUT_IN, llmk.STEP_PERSISTENT)
@@ -282,7 +282,7 @@ def test_persistent_wait_give_up_returns_device_error():
 def q06():
     s = synth.Q06
     say("generating Qwen3-0.6B-shaped weights")
-    W = synth.model(s, seed=0)
+    W = weights(s)
     return s, W
 
 
@@ -310,7 +310,7 @@ def test_tiny_bf16_persistent_step_matches_oracle(layout):
     """The persistent step on the toy shape (bf16 weights): teacher-forced steps against the oracle, then
     free-running through graph replays, and the K/V it leaves equal to the per-operation path's."""
     s = TINY_BF16.with_(rope_layout=layout)
-    W = synth.model(s, seed=0)
+    W = weights(s)
     m = oracle.Model(s, W)
     prompt = synth.prompt(6, s.vocab, stream=21).tolist()
     o = oracle_run(m, s, prompt, n_greedy=6)

@@ -17,7 +17,7 @@ import pytest
 import oracle
 import synth
 from oracle import sampler
-from tests.gpu_util import host, say
+from tests.gpu_util import host, say, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def clear_of_boundaries(lg, T, k, p, u):
 
 
 def run_case(s, step_path, n_pre, n, T, k, p, label):
-    W = synth.model(s, seed=0)
+    W = weights(s)
     prefix = synth.kv_prefix(s, n_pre, seed=2) if n_pre else None
     first = int(synth.prompt(1, s.vocab, stream=7)[0])
     draws = synth.draws((n,), seed=5, stream=31)

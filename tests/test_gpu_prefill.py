@@ -7,16 +7,15 @@ written at every prompt position (within the bar of the oracle's, or one bf16 st
 cache, at the closed-form offsets), nothing else
 in the pool changed, and a decode continuing from the prefilled cache reproducing the oracle's tokens.
 Sizes: the toy decoder in one chunk and in three (64 + 64 + 22 rows after a 5-position prefix), the
-Qwen3-0.6B shape over 100 prompt tokens (two chunks), the Llama-3-8B shape over 20 tokens after its
-4,096-position prefix, and, at the benchmark's size, a 2,048-token Qwen3-0.6B prompt against 2,048 decode
-steps of the library's own decode path (a property that holds at any size).
+Qwen3-0.6B shape over 100 prompt tokens (two chunks) and the Llama-3-8B shape over 20 tokens after its
+4,096-position prefix. The benchmark's size (a 2,048-token Qwen3-0.6B prompt) is in test_gpu_q06_full.py.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import TOL, host, rel_err, say
+from tests.gpu_util import TOL, host, rel_err, say, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +95,7 @@ TINY_BF16 = synth.TINY.with_(name="tiny-llama bf16 weights", w_dtype="bf16", max
 @pytest.mark.parametrize("pos0,n", [(0, 10), (5, 150)])
 def test_tiny_prefill_matches_oracle(pos0, n):
     s = TINY_BF16
-    W = synth.model(s, seed=0)
+    W = weights(s)
     cfg = loader.config_from(s)
     model = loader.upload_model(cfg, W)
     pool = loader.new_pool(cfg, 3, s.max_seq)
@@ -138,7 +137,7 @@ def test_tiny_prefill_matches_oracle(pos0, n):
 def q06():
     s = synth.Q06
     say("generating Qwen3-0.6B-shaped weights")
-    W = synth.model(s, seed=0)
+    W = weights(s)
     cfg = loader.config_from(s)
     return s, W, cfg, loader.upload_model(cfg, W)
 
@@ -160,40 +159,11 @@ def test_q06_prefill_two_chunks_matches_oracle(q06):
     check_kv(s, pool, 1, cache, 0, n, "q06 prefill")
 
 
-def test_q06_2048_token_prefill_equals_the_decode_path(q06):
-    # the benchmark's prompt: 2,048 tokens in 32 chunks of 64 rows, against 2,048 single decode steps of
-    # the same tokens on a second pool; K/V, greedy tokens and the last logits agree within the bar
-    s, W, cfg, model = q06
-    n = 2048
-    tokens = synth.prompt(n, s.vocab, stream=23).tolist()
-    pool_a = loader.new_pool(cfg, 1, n + 8)
-    pool_b = loader.new_pool(cfg, 1, n + 8)
-    say("q06: 2,048-token prefill")
-    got, g_lg, _ = run_prefill(cfg, model, pool_a, 0, tokens, 0)
-    say("q06: 2,048 decode steps")
-    dec = loader.Decoder(cfg, model, pool_b)
-    outs = torch.zeros(n, dtype=torch.int32, device="cuda")
-    lg_b = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
-    for i, t in enumerate(tokens):
-        assert dec.step(t, i, 0, lg_b if i == n - 1 else None) == llmk.OK
-        outs[i:i + 1].copy_(dec.token_out[:1])
-    torch.cuda.synchronize()
-    dec_toks = host(outs).tolist()
-    diff = [i for i in range(n) if got[i] != dec_toks[i]]
-    say(f"q06 2048: {len(diff)} positions differ (near-ties of two fp32 paths)")
-    assert len(diff) <= 4, diff[:10]
-    assert rel_err(g_lg, host(lg_b)) <= TOL
-    for l in range(s.n_layer):
-        for a, b in ((pool_a.k[l], pool_b.k[l]), (pool_a.v[l], pool_b.v[l])):
-            e = rel_err(kv_vals(host(a)[:n * s.n_kv * s.head_dim]), kv_vals(host(b)[:n * s.n_kv * s.head_dim]))
-            assert e <= TOL, f"layer {l}: {e:.3e}"
-
-
 def test_llama8b_prefill_after_the_4096_prefix_matches_oracle():
     s = synth.L8B
     n_pre, n = 4096, 20
     say("generating 8B-shaped weights")
-    W = synth.model(s, seed=0)
+    W = weights(s)
     prefix = synth.kv_prefix(s, n_pre, seed=2)
     tokens = synth.prompt(n, s.vocab, stream=24).tolist()
     cfg = loader.config_from(s)

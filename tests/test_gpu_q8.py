@@ -14,7 +14,7 @@ import pytest
 import oracle
 import synth
 from oracle import quant
-from tests.gpu_util import TOL, host, rel_err, say
+from tests.gpu_util import TOL, host, rel_err, say, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +67,7 @@ def _margin(lg):
 
 def _q8_case(s, n_pre, n_steps, f64, label):
     say(f"{label}: weights")
-    W = synth.model(s, seed=0)
+    W = weights(s)
     prefix = synth.kv_prefix(s, n_pre, seed=2) if n_pre else None
     first = int(synth.prompt(1, s.vocab, stream=7)[0])
 

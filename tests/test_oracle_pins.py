@@ -501,7 +501,11 @@ def test_forward_rows_equals_each_sequence_stepped_alone():
     pre = [(np.array([c.k[l][:n].copy() for l in range(s.n_layer)]), np.array([c.v[l][:n].copy() for l in range(s.n_layer)]))
            for c, n in zip(caches, lens)]
     w = chunk.Weights(s, W)
-    lg, hid, new_kv = chunk.forward_rows(s, w, toks, lens, lambda l, b: (pre[b][0][l], pre[b][1][l]))
+    def prefix(l, b):   # the cached positions in two head-major pieces (the split of a context is immaterial)
+        k, v, h = pre[b][0][l].transpose(1, 0, 2), pre[b][1][l].transpose(1, 0, 2), lens[b] // 2
+        return [(k[:, :h], v[:, :h]), (k[:, h:], v[:, h:])]
+
+    lg, hid, new_kv = chunk.forward_rows(s, w, toks, lens, prefix)
     for b, (c, n) in enumerate(zip(caches, lens)):
         ref_lg, ref_hid = m.forward_token(toks[b], n, c, want_hidden=True)
         assert _close(lg[b], ref_lg) and _close(hid[b], ref_hid), b
