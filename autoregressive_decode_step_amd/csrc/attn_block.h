@@ -189,17 +189,37 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     const int nval = (G + 2) * HD;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     unsigned spins = 0;
-    for (int i = threadIdx.x; i < nval; i += ATTN_THREADS) {
+    // a thread's values (at most QW of them, G <= 8 and HD <= 256) are loaded together and every one not yet
+    // carrying the tag is reloaded in the same round
+    constexpr int QW = (10 * HDP + ATTN_THREADS - 1) / ATTN_THREADS;
+    uint64_t got[QW];
+    int64_t gidx[QW];
+#pragma unroll
+    for (int k = 0; k < QW; ++k) {
+      const int i = threadIdx.x + k * ATTN_THREADS;
       const int g = i / HD, e = i % HD;
-      const int64_t idx = g < G ? (int64_t)(kvh * G + g) * HD + e
-                                : (int64_t)(p.H + (g - G) * p.Hkv) * HD + (int64_t)kvh * HD + e;
-      uint64_t got = ld_tag(p.qkv_tag + idx);
-      while (tag_of(got) != p.tag && !fl_failed) {
-        __builtin_amdgcn_s_sleep(8);   // about 0.2 us between reloads of a whole vector
-        if (!tag_wait_more(p.err, t0, spins)) fl_failed = true;
-        got = ld_tag(p.qkv_tag + idx);
+      gidx[k] = g < G ? (int64_t)(kvh * G + g) * HD + e
+                      : (int64_t)(p.H + (g - G) * p.Hkv) * HD + (int64_t)kvh * HD + e;
+      got[k] = i < nval ? ld_tag(p.qkv_tag + gidx[k]) : ((uint64_t)p.tag << 32);
+    }
+    for (;;) {
+      bool ready = true;
+#pragma unroll
+      for (int k = 0; k < QW; ++k) ready = ready && tag_of(got[k]) == p.tag;
+      if (ready || fl_failed) break;
+      __builtin_amdgcn_s_sleep(8);   // about 0.2 us between reloads
+      if (!tag_wait_more(p.err, t0, spins)) {
+        fl_failed = true;
+        break;
       }
-      s_raw[i] = val_of(got);
+#pragma unroll
+      for (int k = 0; k < QW; ++k)
+        if (tag_of(got[k]) != p.tag) got[k] = ld_tag(p.qkv_tag + gidx[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < QW; ++k) {
+      const int i = threadIdx.x + k * ATTN_THREADS;
+      if (i < nval) s_raw[i] = val_of(got[k]);
     }
     __syncthreads();
   }
@@ -537,19 +557,27 @@ __device__ __forceinline__ void attn_merge_tagged(const AttnParams& p, const int
     }
     ((threadIdx.x & 1) ? s_pl : s_pm)[c] = val_of(v);
   }
-  // this thread's output element over its parts
+  // this thread's output element over its parts: every part not yet carrying the tag is reloaded in the
+  // same round, so the wait ends one round trip after the last part lands
   uint64_t o[NPP];
 #pragma unroll
   for (int k = 0; k < NPP; ++k) {
     const int c = sub + k * NS;
     o[k] = c < n_parts ? ld_tag(PB + c * cstride + 2 + e) : ((uint64_t)p.part_tag << 32);
   }
+  for (;;) {
+    bool ready = true;
 #pragma unroll
-  for (int k = 0; k < NPP; ++k) {
-    const int c = sub + k * NS;
-    while (tag_of(o[k]) != p.part_tag && !failed) {
-      if (!tag_wait_more(p.err, t0, spins)) failed = true;
-      o[k] = ld_tag(PB + c * cstride + 2 + e);
+    for (int k = 0; k < NPP; ++k) ready = ready && tag_of(o[k]) == p.part_tag;
+    if (ready || failed) break;
+    if (!tag_wait_more(p.err, t0, spins)) {
+      failed = true;
+      break;
+    }
+#pragma unroll
+    for (int k = 0; k < NPP; ++k) {
+      const int c = sub + k * NS;
+      if (tag_of(o[k]) != p.part_tag) o[k] = ld_tag(PB + c * cstride + 2 + e);
     }
   }
   __syncthreads();

@@ -418,24 +418,17 @@ __device__ __forceinline__ void sk_consume(uint4 (&ring)[SK_R], const SkOp& f, c
   sk_block<false>(ring, f, blk, f, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
 }
 
-// RoPE, K/V append and attention of layer l in the persistent step: this workgroup's (K/V head, context
-// part) items, then the merges it owns (query head hq by workgroup nwg - 1 - hq, from the end, away from
-// the first items), which write the tagged attention output. The tiles live in the dynamic LDS the staged
-// input uses between ops, and no weight load is in flight meanwhile, so the registers are its own.
+// The attention parameters of layer l in the persistent step: (K/V head, context part) items over the context
+// 0..pos, parts tagged per layer, q|k|v and the merged output as tagged activations.
 template <typename T, int HD>
-__device__ __forceinline__ void sk_attention(const StepParams* pp, int l, int pos, uint32_t tag) {
-  extern __shared__ uint4 sk_dyn[];
-  const StepParams p = *pp;
-  const int w = blockIdx.x;
-  const int nwg = p.nwg;
-  const StepLayer& Ly = p.layers[l];
+__device__ __forceinline__ AttnParams sk_attn_params(const StepParams& p, int l, int pos, uint32_t tag) {
   const int ctx = pos + 1;
   const int ch = p.attn_chunk;
   const int n_sub = (ctx + ch - 1) / ch;
-  int target = nwg / p.Hkv;
+  int target = p.nwg / p.Hkv;
   target = target < 1 ? 1 : (target > ATTN_MAX_PARTS ? ATTN_MAX_PARTS : target);
   const int spw = (n_sub + target - 1) / target;
-  const int n_parts = (n_sub + spw - 1) / spw;
+  const StepLayer& Ly = p.layers[l];
   AttnParams ap{};
   ap.H = p.H;
   ap.Hkv = p.Hkv;
@@ -444,7 +437,7 @@ __device__ __forceinline__ void sk_attention(const StepParams* pp, int l, int po
   ap.state = p.state;
   ap.chunk = ch;
   ap.sub_per_wg = spw;
-  ap.n_parts = n_parts;
+  ap.n_parts = (n_sub + spw - 1) / spw;
   ap.part_tagged = p.attn_part;
   ap.part_tag = tag * STEP_MAX_LAYERS + (uint32_t)l;
   ap.rope_table = p.rope_table;
@@ -457,9 +450,31 @@ __device__ __forceinline__ void sk_attention(const StepParams* pp, int l, int po
   ap.out_tag = p.att + (int64_t)l * p.att_stride;
   ap.tag = p.give_up ? (tag | 0x80000000u) : tag;   // a tag no workgroup writes (tests of the give-up path)
   ap.err = p.err;
-  for (int it = w; it < p.Hkv * n_parts; it += nwg) attn_block<T, HD, true>(ap, it / n_parts, it % n_parts, 0, sk_dyn);
+  return ap;
+}
+
+// RoPE, K/V append and attention of layer l: this workgroup's (K/V head, context part) items, each part's
+// (max, sum, output) stored tagged. The tiles live in the dynamic LDS the staged input uses between ops, and
+// no weight load is in flight meanwhile, so the registers are the attention's own.
+template <typename T, int HD>
+__device__ __forceinline__ void sk_attention_items(const StepParams* pp, int l, int pos, uint32_t tag) {
+  extern __shared__ uint4 sk_dyn[];
+  const StepParams p = *pp;
+  const AttnParams ap = sk_attn_params<T, HD>(p, l, pos, tag);
+  for (int it = blockIdx.x; it < p.Hkv * ap.n_parts; it += p.nwg)
+    attn_block<T, HD, true>(ap, it / ap.n_parts, it % ap.n_parts, 0, sk_dyn);
+}
+
+// The merges this workgroup owns (query head hq by workgroup nwg - 1 - hq, from the end, away from the first
+// items), which write the tagged attention output. They run after the workgroup's first o weight loads are
+// issued (a merge holds few registers): a merging workgroup has no item, so those loads go out as soon as its
+// q|k|v rows are done and have landed long before the parts it waits for.
+template <typename T, int HD>
+__device__ __forceinline__ void sk_attention_merges(const StepParams* pp, int l, int pos, uint32_t tag) {
+  const StepParams p = *pp;
+  const AttnParams ap = sk_attn_params<T, HD>(p, l, pos, tag);
   const int G = p.H / p.Hkv;
-  for (int hq = nwg - 1 - w; hq < p.H; hq += nwg) attn_merge_tagged<HD>(ap, hq / G, hq % G, n_parts);
+  for (int hq = p.nwg - 1 - (int)blockIdx.x; hq < p.H; hq += p.nwg) attn_merge_tagged<HD>(ap, hq / G, hq % G, ap.n_parts);
 }
 
 template <typename T, int HD>
@@ -523,14 +538,15 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
 
   for (int o = 0; o < n_ops; ++o) {
     const SkOp f = sk_op(p, R, s_layers, o, wave);
-    // The op's first SK_R loads go out before its input is waited for (after the attention for o, which
-    // needs the registers), so the weights stream while the producers finish.
-    if (f.kind == OP_O) sk_attention<T, HD>(&p, f.l, pos, tag);
+    // The op's first SK_R loads go out before its input is waited for (for o: after this workgroup's attention
+    // items, which need the registers, and before its merges), so the weights stream while the producers finish.
+    if (f.kind == OP_O) sk_attention_items<T, HD>(&p, f.l, pos, tag);
     uint4 ring[SK_R];
     if (f.npos > 0) {
 #pragma unroll
       for (int j = 0; j < SK_R; ++j) ring[j] = gload<uint4>(sk_addr(f, j, wave, lane16));
     }
+    if (f.kind == OP_O) sk_attention_merges<T, HD>(&p, f.l, pos, tag);
     // ---- the op's input ----
     SkOut out;
     out.tag = tag;
