@@ -13,9 +13,12 @@ HIP events on the stream it runs on), and the oracle's throughput on the host co
 the same workload.
 
 Other workloads (--workload): batched (64 sequences of ragged contexts a step), prefill (a 2,048-token
-prompt, Qwen3-0.6B or Llama-3-8B shape), q8 (the batch-1 workload over int8 weight packs); --sample T,K,P
-samples every batch-1 step inside the captured loop; --copy-probe, --sample-probe and --prefill-probe are
-short runs for counters and traces.
+prompt, Qwen3-0.6B or Llama-3-8B shape), q8 (the batch-1 workload over int8 weight packs), q06 (the
+Qwen3-0.6B-shaped decode: 128 greedy steps after a 2,048-token prompt the library prefills), primitives (the
+primitive microbenchmark: gemv_t 4096 x 4096 bf16 cold and warm, add_rmsnorm 1 x 4096, RoPE on 32 + 8 heads
+over 8,192 positions, argmax over 128,256 logits with planted ties, and the in-place K/V append's cost shape);
+--sample T,K,P samples every batch-1 step inside the captured loop; --copy-probe, --sample-probe and
+--prefill-probe are short runs for counters and traces.
 """
 from __future__ import annotations
 
@@ -313,9 +316,10 @@ def main() -> int:
                     help="times each kernel class's per-layer launches are replayed for its HIP-event timing")
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle steps in the CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("batch1", "batched", "prefill", "q8"), default="batch1",
+    ap.add_argument("--workload", choices=("batch1", "batched", "prefill", "q8", "q06", "primitives"), default="batch1",
                     help="batch1: the 8B-shaped single-sequence step (default); batched: 64 ragged sequences per step; "
-                         "prefill: a 2,048-token prompt (steps = prompts, 8 by default)")
+                         "prefill: a 2,048-token prompt (steps = prompts, 8 by default); q06: Qwen3-0.6B-shaped decode "
+                         "after a 2,048-token prompt; primitives: the primitive microbenchmark")
     ap.add_argument("--prefill-shape", choices=("q06", "l8b"), default="q06",
                     help="the prefill workload's shape: Qwen3-0.6B (the 2,048-token prefix workload) or Llama-3-8B")
     ap.add_argument("--cpu-prefill-tokens", type=int, default=24, help="oracle tokens in the prefill CPU baseline")
@@ -358,6 +362,10 @@ def main() -> int:
         return run_batched(args)
     if args.workload == "prefill":
         return run_prefill(args)
+    if args.workload == "q06":
+        return run_q06(args)
+    if args.workload == "primitives":
+        return run_primitives(args)
 
     s = synth.L8B
     q8 = args.workload == "q8"
@@ -523,6 +531,289 @@ def main() -> int:
 
     print(json.dumps(result), flush=True)
     log(f"total {time.time() - t_start:.1f} s")
+    return 0
+
+
+Q06_PROMPT = 2048               # tokens the Qwen3-0.6B-shaped workload prefills before decoding
+Q06_STEPS = 128                 # greedy steps it decodes (positions 2,048..2,175)
+
+
+def run_q06(args) -> int:
+    """The Qwen3-0.6B-shaped decode: a seeded 2,048-token prompt through the library's prefill, then greedy
+    steps at positions 2,048..2,175 (one captured step replayed per token), timed like the 8B workload."""
+    import torch
+
+    import synth
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd import loader
+    s = synth.Q06
+    steps = args.steps if args.steps != 256 else Q06_STEPS
+    if steps > Q06_STEPS or args.warmup > Q06_STEPS:
+        print(f"the q06 workload has room for {Q06_STEPS} steps per run", file=sys.stderr)
+        return 2
+    t_start = time.time()
+    log(f"generating {s.name} weights")
+    W = synth.model(s, seed=0)
+    cfg = loader.config_from(s)
+    model = loader.upload_model(cfg, W)
+    pool = loader.new_pool(cfg, 1, s.max_seq)
+    prompt = synth.prompt(Q06_PROMPT, s.vocab, stream=23).tolist()
+    pws = llmk.workspace(llmk.prefill_workspace_bytes(cfg, Q06_PROMPT))
+    ptoks = torch.zeros(Q06_PROMPT, dtype=torch.int32, device="cuda")
+    st = llmk.prefill(cfg, model, pool, 0, prompt, 0, ptoks, pws)
+    if st != llmk.OK:
+        raise RuntimeError(f"llmk_prefill: {st} {llmk.status_name(st)}")
+    del pws
+    first = int(ptoks[-1].item())
+    dec = loader.Decoder(cfg, model, pool)
+    persistent = llmk.decode_path(cfg) == llmk.STEP_PERSISTENT
+    torch.cuda.synchronize()
+    log(f"prompt prefilled, resident in HBM after {time.time() - t_start:.1f} s; step form: "
+        f"{'persistent' if persistent else 'per-op'}")
+
+    def run(n, out):
+        pool.slot_len[0] = Q06_PROMPT
+        st = dec.steps(first, Q06_PROMPT, n, out)
+        if st != llmk.OK:
+            raise RuntimeError(f"decode_steps: {st} {llmk.status_name(st)}")
+
+    if args.warmup > 0:
+        run(args.warmup, torch.zeros(args.warmup, dtype=torch.int32, device="cuda"))
+    toks = torch.zeros(steps, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps, toks)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / steps
+    total_bytes = sum(step_bytes(s, Q06_PROMPT + 1 + i) for i in range(steps))
+    gbps = total_bytes / elapsed / 1e9
+    log(f"timed {steps} steps: {ms_per_step:.3f} ms/step, {steps / elapsed:.0f} tokens/s, {gbps:.0f} GB/s algorithmic")
+    pool.slot_len[0] = Q06_PROMPT
+    reps = min(STEP_REPS, Q06_STEPS)
+    kind = llmk.STEP_KERNEL if persistent else llmk.KERNEL_CLASSES.index("gate_up")
+    st, kms = llmk.decode_kernel_time(cfg, model, pool, 0, first, Q06_PROMPT, kind, reps if persistent else 4,
+                                      dec.token_out, dec.ws)
+    if st != llmk.OK:
+        raise RuntimeError(f"decode_kernel_time: {st} {llmk.status_name(st)}")
+    k_bytes = (sum(step_bytes(s, Q06_PROMPT + 1 + i) for i in range(reps)) / reps if persistent
+               else gate_up_bytes(s))
+    k_gbps = k_bytes / (kms * 1e-3) / 1e9
+    result = {
+        "metric": "decode tokens/s at batch 1 (Qwen3-0.6B-shaped, after a 2,048-token prompt) + achieved HBM GB/s",
+        "value": steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-0.6b-shaped greedy decode, batch 1, a seeded 2,048-token prompt prefilled by "
+                               "the library, then steps at positions 2,048..2,175; bf16 weights, fp32 K/V",
+                   "vocab": s.vocab, "d": s.d, "n_layer": s.n_layer, "n_head": s.n_head, "n_kv": s.n_kv,
+                   "head_dim": s.head_dim, "hidden": s.hidden, "batch": 1, "context_start": Q06_PROMPT,
+                   "weights": "bf16", "kv": "f32", "accumulation": "f32"},
+        "step_hbm_gbps": gbps,
+        "step_frac_of_peak": gbps / PEAK_HBM_GBPS,
+        "step_bytes_mean": total_bytes / steps,
+        "step_form": "persistent" if persistent else "per-op",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("persistent decode step (step_kernel)" if persistent else
+                                "gate|up row-dot GEMV (rowdot_kernel, GATEUP epilogue)"),
+                     "achieved": k_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
+                     "traffic": None, "bytes_per_launch": k_bytes, "avg_launch_us": kms * 1e3},
+        "first_tokens": toks[:8].cpu().tolist(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n = args.cpu_steps
+        log(f"oracle baseline: {n} steps over a 2,048-position cache on the host cores")
+        m = oracle.Model(s, W)
+        c = m.new_cache(Q06_PROMPT + n)
+        c.fill_prefix(synth.kv_prefix(s, Q06_PROMPT, seed=2))
+        t = first
+        tc0 = time.perf_counter()
+        for i in range(n):
+            lg, _ = m.forward_token(t, Q06_PROMPT + i, c)
+            t = oracle.argmax(lg)[0]
+        tc = time.perf_counter() - tc0
+        result["cpu_baseline"] = {"value": n / tc, "unit": "tokens/s", "cores": oracle.lib().orc_num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{n} greedy decode steps at positions {Q06_PROMPT}..{Q06_PROMPT + n - 1} "
+                                            "over a 2,048-position cache of seeded K/V (the same sizes and work as the "
+                                            "timed steps; the prompt itself is not run through the oracle here, so the "
+                                            "tokens are not compared) (fp64, OpenMP)"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    log(f"total {time.time() - t_start:.1f} s")
+    return 0
+
+
+def run_primitives(args) -> int:
+    """The primitive microbenchmark, each primitive through the C ABI on seeded inputs: many calls captured in a
+    graph on the stream the binding launches on and replayed between HIP events (device time per call), and each
+    primitive of the oracle timed on the host cores for the same inputs."""
+    import torch
+
+    import synth
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd.loader import to_device
+    stream = torch.cuda.Stream()      # default priority; graphs are captured on it and replayed on it
+    torch.cuda.set_stream(stream)
+
+    def timed(fn, reps):
+        """Device time per call: `reps` calls captured once into a graph, the graph replayed between two events
+        (so host launch costs are not counted), after an eager warm-up."""
+        for _ in range(3):
+            fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps   # us per call
+
+    def check(st, what):
+        if st != llmk.OK:
+            raise RuntimeError(f"{what}: {st} {llmk.status_name(st)}")
+
+    out = {}
+    # gemv_t: y = A^T x, A 4096 x 4096 bf16 N(0, 0.02), x fp32 N(0, 1); cold = 16 rotated copies (537 MB, past
+    # the 256 MB of last-level cache), warm = one copy
+    m = n = 4096
+    a_np = synth.normal((m, n), 10, 0, 0.02, "bf16")
+    x_np = synth.normal((m,), 10, 1, 1.0)
+    copies = [to_device(a_np) for _ in range(16)]
+    x = to_device(x_np)
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = llmk.workspace(llmk.gemv_t_workspace_bytes(m, n, llmk.BF16))
+    gb = m * n * 2 + m * 4 + n * 4
+    check(llmk.gemv_t(copies[0], x, y, m, n, ws), "gemv_t")
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    cold = timed(lambda i: check(llmk.gemv_t(copies[i % 16], x, y, m, n, ws), "gemv_t"), 160)
+    warm = timed(lambda i: check(llmk.gemv_t(copies[0], x, y, m, n, ws), "gemv_t"), 160)
+    if not torch.equal(y, y_eager):   # every copy holds the same A: a replayed call gives the eager result, bit for bit
+        raise RuntimeError("gemv_t: a replayed call differs from the eager one")
+    out["gemv_t_4096x4096_bf16"] = {"algorithmic_bytes": gb, "us_cold": cold, "GBps_cold": gb / cold / 1e3,
+                                    "frac_cold": gb / cold / 1e3 / PEAK_HBM_GBPS, "us_warm": warm,
+                                    "GBps_warm": gb / warm / 1e3, "cold_copies": 16}
+    del copies
+    # add_rmsnorm 1 x 4096: residual and x N(0, 1), gain 1 + N(0, 0.1), eps 1e-5
+    r_np = synth.normal((4096,), 11, 0, 1.0)
+    xr_np = synth.normal((4096,), 11, 1, 1.0)
+    g_np = synth.normal((4096,), 11, 2, 0.1, mean=1.0)
+    r, xr, g, h = to_device(r_np), to_device(xr_np), to_device(g_np), torch.empty(4096, dtype=torch.float32,
+                                                                                     device="cuda")
+    us = timed(lambda i: check(llmk.add_rmsnorm(r, xr, g, h, 1, 4096, 1e-5), "add_rmsnorm"), 500)
+    out["add_rmsnorm_1x4096"] = {"algorithmic_bytes": 81920, "us": us, "GBps": 81920 / us / 1e3}
+    # RoPE: q [8192][32][128], k [8192][8][128] fp32 N(0, 1), row r at position r, base 1e4 and 5e5; one position
+    # alone (its latency) and the whole sweep in one launch
+    rows, nq, nk, hd = 8192, 32, 8, 128
+    q_np = synth.normal((rows * nq * hd,), 12, 0, 1.0)
+    k_np = synth.normal((rows * nk * hd,), 12, 1, 1.0)
+    qd, kd = to_device(q_np), to_device(k_np)
+    pos = torch.arange(rows, dtype=torch.int32, device="cuda")
+    rope = {}
+    for base in (1e4, 5e5):
+        tab = torch.empty(rows * hd, dtype=torch.float32, device="cuda")
+        check(llmk.rope_table_init(tab, rows, hd, base), "rope_table_init")
+        sweep = timed(lambda i: check(llmk.rope(qd, kd, rows, nq, nk, hd, pos, tab, rows, 0), "rope"), 50)
+        one = timed(lambda i: check(llmk.rope(qd[:nq * hd], kd[:nk * hd], 1, nq, nk, hd, pos[4095:4096], tab, rows, 0),
+                                    "rope"), 500)
+        b = rows * 41472
+        rope[f"base_{base:g}"] = {"us_one_position": one, "us_sweep_8192": sweep, "sweep_bytes": b,
+                                  "GBps_sweep": b / sweep / 1e3}
+    out["rope_32q_8k_hd128"] = rope
+    # argmax over 128,256 fp32 N(0, 3) with planted exact ties across a workgroup slice boundary
+    V = 128256
+    lg_np = synth.normal((V,), 13, 0, 3.0)
+    mx = float(lg_np.max()) + 0.5
+    lg_np[[2003, 2004, 90000]] = mx
+    lg = to_device(lg_np)
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    val = torch.empty(1, dtype=torch.float32, device="cuda")
+    aws = llmk.workspace(llmk.argmax_workspace_bytes(1, V))
+    us = timed(lambda i: check(llmk.argmax(lg, 1, V, tok, val, aws), "argmax"), 500)
+    out["argmax_128256"] = {"algorithmic_bytes": V * 4, "us": us, "GBps": V * 4 / us / 1e3,
+                            "token": int(tok.item()), "planted_tie_lowest_index": 2003}
+    # the in-place K/V append's cost shape: one decode token's K row (8 heads x 128 = 1,024 elements) appended to a
+    # bf16 cache holding 2,048 and 133,120 elements; per-element time growth (the gate is 3x)
+    cache = torch.zeros(140000, dtype=torch.bfloat16, device="cuda")
+    newv = to_device(synth.normal((1024,), 14, 0, 1.0))
+    per = {}
+    for filled in (2048, 133120):
+        us = timed(lambda i: check(llmk.kv_append_flat(cache, filled, filled, newv)[0], "kv_append_flat"), 500)
+        per[filled] = us / 1024
+    out["kv_append_cost_shape"] = {"n_new": 1024, "us_per_element_at_2048": per[2048],
+                                   "us_per_element_at_133120": per[133120], "growth": per[133120] / per[2048],
+                                   "gate": 3.0}
+    log("primitives: " + json.dumps(out))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("oracle baseline: each primitive on the host cores")
+        c = {}
+        t0 = time.perf_counter()
+        for _ in range(5):
+            oracle.gemv_t_f32(a_np, x_np)
+        c["gemv_t_4096x4096_bf16_us"] = (time.perf_counter() - t0) / 5 * 1e6
+        t0 = time.perf_counter()
+        for _ in range(200):
+            oracle.add_rmsnorm_f32(r_np, xr_np, g_np, 1, 4096, 1e-5)
+        c["add_rmsnorm_1x4096_us"] = (time.perf_counter() - t0) / 200 * 1e6
+        t0 = time.perf_counter()
+        oracle.rope_f32(q_np, k_np, rows, nq, nk, hd, 0, 1e4, 0)
+        c["rope_sweep_8192_us"] = (time.perf_counter() - t0) * 1e6
+        t0 = time.perf_counter()
+        for _ in range(20):
+            o_tok, _ = oracle.argmax(lg_np)
+        c["argmax_128256_us"] = (time.perf_counter() - t0) / 20 * 1e6
+        c["argmax_token"] = o_tok
+        cpu = {"value": gb / c["gemv_t_4096x4096_bf16_us"] / 1e3, "unit": "GB/s", "cores": oracle.lib().orc_num_threads(),
+               "kind": "oracle",
+               "sample": "each primitive of the oracle on the same inputs (fp64): gemv_t 5 calls, add_rmsnorm 200, "
+                         "the RoPE sweep once, argmax 20; value = the oracle gemv_t's algorithmic GB/s",
+               "per_primitive": c}
+    g = out["gemv_t_4096x4096_bf16"]
+    result = {
+        "metric": "primitive microbench: gemv_t 4096x4096 bf16 GB/s (cold) with add_rmsnorm, RoPE and argmax latencies",
+        "value": g["GBps_cold"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": 160,
+        "warmup": 3,
+        "ms_per_step": g["us_cold"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "primitive microbench: gemv_t A 4096x4096 bf16 N(0,0.02), x fp32 N(0,1) (16 rotated "
+                               "copies of A for the cold figure); add_rmsnorm 1x4096; RoPE on 32 q + 8 k heads at hd 128, "
+                               "positions 0..8191; argmax over 128,256 fp32 N(0,3) with planted exact ties; in-place "
+                               "K/V append cost shape"},
+        "primitives": out,
+        "roofline": {"bound": "hbm", "kernel": "gemv_t (gemv_t_kernel, split-K over A[in][out]), cold",
+                     "achieved": g["GBps_cold"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": g["frac_cold"],
+                     "traffic": None, "bytes_per_launch": gb, "avg_launch_us": g["us_cold"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    if out["argmax_128256"]["token"] != 2003:
+        raise RuntimeError("argmax: planted tie not resolved to the lowest index")
     return 0
 
 

@@ -410,3 +410,30 @@ def test_transpose_bit_exact(rows, cols, dt):
     assert llmk.transpose(src, dst, rows, cols) == llmk.OK
     _sync()
     assert np.array_equal(host(dst).reshape(cols, rows), a.T)
+
+
+# ---------------------------------------------------------------------------------------------
+# the in-place append's cost shape
+# ---------------------------------------------------------------------------------------------
+
+def test_kv_append_cost_is_flat_in_the_cache_length():
+    """Appending one decode token's row (1,024 elements) in place costs the same per element whether the cache
+    holds 2,048 or 133,120 elements ("LLM inference kernels", "The hot loop doesn't call kv_cache_append_flat":
+    the copying append grows with the cache, the in-place one does not; the gate allows 3x)."""
+    cache = torch.zeros(140000, dtype=torch.bfloat16, device="cuda")
+    newv = dev(synth.normal((1024,), 14, 0, 1.0))
+    stream = torch.cuda.current_stream()
+    per = {}
+    for filled in (2048, 133120):
+        for _ in range(5):
+            assert llmk.kv_append_flat(cache, filled, filled, newv)[0] == llmk.OK
+        _sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(400):
+            assert llmk.kv_append_flat(cache, filled, filled, newv)[0] == llmk.OK
+        e1.record(stream)
+        _sync()
+        per[filled] = e0.elapsed_time(e1) / 400 / 1024
+    say(f"append per element: {per[2048] * 1e6:.3f} ns at 2,048, {per[133120] * 1e6:.3f} ns at 133,120")
+    assert per[133120] <= 3.0 * per[2048]
