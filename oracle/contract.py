@@ -256,13 +256,107 @@ def gqa_attend_flat(q=True, len_q=0, k_cache=True, v_cache=True, len_cache=0, kv
 
 def _pool_fields(pool):
     """A pool descriptor's own fields: 578 (null k, v or slot_len array, dtype), 561, 564, then 578 again
-    for a layer buffer that is null or not 16-byte aligned (pool["buffers"] False)."""
+    for a layer buffer that is null or not 16-byte aligned (pool["buffers"] False), then the pages when the
+    pool has them (pool["pages"])."""
     if not pool.get("arrays", True) or pool.get("dtype", 0) not in (0, 1):
         return INVALID
     c = _dims(pool["n_layer"], pool["n_slots"], pool["capacity"], pool["n_kv"], pool["head_dim"])
     if c != OK:
         return c
-    return OK if pool.get("buffers", True) else INVALID
+    if not pool.get("buffers", True):
+        return INVALID
+    return _pages_fields(pool) if pool.get("pages") else OK
+
+
+def _pages_fields(pool):
+    """Paged pool ("Inside the engine", "3. The K/V cache and the block store": fixed blocks of block_tokens
+    positions): 578 for a null table / host table / refcount array (pages["arrays"] False), block_tokens not a
+    power of two in [64, 65536] or max_blocks != ceil(capacity / block_tokens); 561 for n_blocks < 1; 564 for
+    n_blocks or n_slots * max_blocks above MAX_DIM."""
+    g = pool["pages"]
+    bt = g["block_tokens"]
+    if not g.get("arrays", True):
+        return INVALID
+    if bt < 64 or bt > 65536 or bt & (bt - 1):
+        return INVALID
+    if g["max_blocks"] != -(-pool["capacity"] // bt):
+        return INVALID
+    if g["n_blocks"] < 1:
+        return EMPTY
+    if g["n_blocks"] > MAX_DIM or pool["n_slots"] * g["max_blocks"] > MAX_DIM:
+        return TOO_LARGE
+    return OK
+
+
+def _paged(pool):
+    """A pool for the paged-only entry points: its fields, then 578 when it has no pages."""
+    if pool is None:
+        return INVALID
+    c = _pool_fields(pool)
+    if c != OK:
+        return c
+    return OK if pool.get("pages") else INVALID
+
+
+def kv_reserve(pool=None, slot=0, pos_begin=0, pos_end=0, need=0, n_free=0, capturing=False):
+    """Status of llmk_kv_reserve; need: the blocks the reservation takes (fresh and copied, the oracle block
+    manager's count), n_free: the pool's free blocks, capturing: the stream is being captured."""
+    c = _paged(pool)
+    if c != OK:
+        return c
+    if pos_begin < 0 or pos_end <= pos_begin:
+        return EMPTY
+    if pos_end > MAX_DIM:
+        return TOO_LARGE
+    if not (0 <= slot < pool["n_slots"]):
+        return SLOT
+    if pos_end > pool["capacity"] or need > n_free:
+        return CAPACITY
+    return INVALID if (need > 0 and capturing) else OK
+
+
+def kv_fork(pool=None, src=0, dst=1, n_pos=1, src_len=0, dst_len=0, dst_blocks=0, src_blocks_ok=True,
+            capturing=False):
+    """Status of llmk_kv_fork; src_len / dst_len: the slots' recorded positions, dst_blocks: blocks dst holds,
+    src_blocks_ok: every one of src's first n_pos positions has a block."""
+    c = _paged(pool)
+    if c != OK:
+        return c
+    if src == dst:
+        return INVALID
+    if n_pos < 1:
+        return EMPTY
+    if n_pos > MAX_DIM:
+        return TOO_LARGE
+    if not (0 <= src < pool["n_slots"] and 0 <= dst < pool["n_slots"]):
+        return SLOT
+    if n_pos > src_len or dst_len != 0 or dst_blocks or not src_blocks_ok:
+        return CACHE_LEN
+    return INVALID if capturing else OK
+
+
+def kv_release(pool=None, slot=0):
+    """Status of llmk_kv_release."""
+    c = _paged(pool)
+    if c != OK:
+        return c
+    return OK if 0 <= slot < pool["n_slots"] else SLOT
+
+
+def kv_admit(pool=None, n_uncached=0, admit=True, n_free=0):
+    """(status, admit) of llmk_kv_admit: admit when the free blocks cover ceil(n_uncached / block_tokens) plus
+    one block of headroom ("Inside the engine", "2. The scheduler: continuous batching", "Admission")."""
+    if not admit:
+        return INVALID, None
+    c = _paged(pool)
+    if c != OK:
+        return c, None
+    if n_uncached < 0:
+        return EMPTY, None
+    if n_uncached > MAX_DIM:
+        return TOO_LARGE, None
+    bt = pool["pages"]["block_tokens"]
+    return OK, int(n_free >= -(-n_uncached // bt) + 1)
 
 
 def kv_pool_init(pool=None):
@@ -272,11 +366,14 @@ def kv_pool_init(pool=None):
     return _pool_fields(pool)
 
 
-def kv_append(pool=None, layer=0, slot=0, which=0, cache_len=0, recorded=0, new_vals=True, len_new=0, n_new=0):
+def kv_append(pool=None, layer=0, slot=0, which=0, cache_len=0, recorded=0, new_vals=True, len_new=0, n_new=0,
+              need=0, n_free=0, capturing=False, row_of=None):
     """(status, new_len, elem_offset) of llmk_kv_append into buffer `which` of (layer, slot); `recorded` is
     the pool's fill record of that buffer. The slot's region is a flat cache of plane elements at
     slot * plane ("Inside the engine", "3. The K/V cache and the block store"); the append follows the
-    flat cache's rule ("LLM inference kernels", "KV-cache growth and greedy argmax")."""
+    flat cache's rule ("LLM inference kernels", "KV-cache growth and greedy argmax"). A paged pool first
+    reserves the positions the elements fall in (need / n_free / capturing as for kv_reserve) and the offset is
+    that of the first element through the table: row_of(position) is the position's cache row after it."""
     if not new_vals or pool is None:
         return INVALID, None, None
     c = _pool_fields(pool)
@@ -294,16 +391,25 @@ def kv_append(pool=None, layer=0, slot=0, which=0, cache_len=0, recorded=0, new_
         return CACHE_LEN, None, None
     if len_new != n_new:
         return NEW_LEN, None, None
-    plane = pool["capacity"] * pool["n_kv"] * pool["head_dim"]
+    row = pool["n_kv"] * pool["head_dim"]
+    plane = pool["capacity"] * row
     if cache_len + n_new > plane:
         return CAPACITY, None, None
+    if pool.get("pages"):
+        if need > n_free:
+            return CAPACITY, None, None
+        if need > 0 and capturing:
+            return INVALID, None, None
+        p0 = cache_len // row
+        return OK, cache_len + n_new, (row_of(p0) * row + cache_len - p0 * row) if row_of else None
     return OK, cache_len + n_new, slot * plane + cache_len
 
 
 def gqa_attend(q=True, len_q=0, pool=None, layer=0, slot=0, ctx_len=0, n_head=0, out=True, len_out=0, rec_k=None,
-               rec_v=None, ws=True, ws_short=False):
+               rec_v=None, ws=True, ws_short=False, blocks_ok=True):
     """Status of llmk_gqa_attend over (layer, slot) of a pool; rec_k / rec_v: the pool's fill records of
-    that slot's K and V buffers in elements (None: the pool keeps none)."""
+    that slot's K and V buffers in elements (None: the pool keeps none); blocks_ok (paged pools): every
+    position of [0, ctx_len) has a block."""
     if not (q and out and ws) or pool is None:
         return INVALID
     c = _pool_fields(pool)
@@ -323,7 +429,7 @@ def gqa_attend(q=True, len_q=0, pool=None, layer=0, slot=0, ctx_len=0, n_head=0,
         return A_LEN
     if len_out != n_head * hd:
         return OUTPUT_LEN
-    if ctx_len > pool["capacity"]:
+    if ctx_len > pool["capacity"] or (pool.get("pages") and not blocks_ok):
         return POSITION
     need = ctx_len * n_kv * hd
     if (rec_k is not None and rec_k < need) or (rec_v is not None and rec_v < need):
@@ -366,15 +472,21 @@ def sample(logits=True, len_logits=0, rows=0, n=0, temperature=1.0, top_k=0, top
     return INVALID if ws_short else OK
 
 
-def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head):
+def kv_slot_offset(n_slots, capacity, n_kv, head_dim, slot, pos, kv_head, table=None, block_tokens=None):
     """(status, offset): offset = slot*plane + pos*n_kv*hd + kv_head*hd, plane = capacity*n_kv*hd
-    (the pool layout of "Inside the engine", section "3. The K/V cache and the block store")."""
+    (the pool layout of "Inside the engine", section "3. The K/V cache and the block store"); with a block
+    table ([slot][block], -1: none), offset = (table[slot][pos // bt] * bt + pos % bt)*n_kv*hd + kv_head*hd."""
     if not (0 <= slot < n_slots):
         return SLOT, None
     if not (0 <= pos < capacity):
         return POSITION, None
     if not (0 <= kv_head < n_kv):
         return HEAD_SHAPE, None
+    if table is not None:
+        b = table[slot][pos // block_tokens]
+        if b < 0:
+            return POSITION, None
+        return OK, (b * block_tokens + pos % block_tokens) * n_kv * head_dim + kv_head * head_dim
     plane = capacity * n_kv * head_dim
     return OK, slot * plane + pos * n_kv * head_dim + kv_head * head_dim
 
