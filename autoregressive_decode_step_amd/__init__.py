@@ -17,6 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libllmk.so")
 
 OK = 560
+CACHE_LENGTH_MISMATCH = 566
+CACHE_CAPACITY_EXCEEDED = 571
 DEVICE_ERROR = 579
 F32, BF16, Q8 = 0, 1, 2
 Q8_GROUP = 128
@@ -62,12 +64,18 @@ class ModelStruct(ctypes.Structure):
                 ("layers", ctypes.POINTER(Tensor))]
 
 
+class PagesStruct(ctypes.Structure):
+    """llmk_kv_pages"""
+    _fields_ = [("block_tokens", _i64), ("n_blocks", _i64), ("max_blocks", _i64), ("table", _p),
+                ("table_h", ctypes.POINTER(_i32)), ("refcount_h", ctypes.POINTER(_i32)), ("n_free", _i64)]
+
+
 class PoolStruct(ctypes.Structure):
     """llmk_kv_pool"""
     _fields_ = [("k", ctypes.POINTER(_p)), ("v", ctypes.POINTER(_p)), ("n_layer", _i64), ("n_slots", _i64),
                 ("capacity", _i64), ("n_kv", _i64), ("head_dim", _i64), ("dtype", _i32),
                 ("slot_len_h", ctypes.POINTER(_i64)), ("len_k_h", ctypes.POINTER(_i64)),
-                ("len_v_h", ctypes.POINTER(_i64))]
+                ("len_v_h", ctypes.POINTER(_i64)), ("pages", ctypes.POINTER(PagesStruct))]
 
 
 _SIGS = {
@@ -102,6 +110,10 @@ _SIGS = {
                       _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p], _i32),
     "llmk_sample": ([_p, _i64, _i64, _i64, _f32, _i32, _f32, _p, _i64, _p, _p, _i64, _p], _i32),
     "llmk_kv_slot_offset": ([ctypes.POINTER(PoolStruct), _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
+    "llmk_kv_reserve": ([ctypes.POINTER(PoolStruct), _i64, _i64, _i64, _p], _i32),
+    "llmk_kv_fork": ([ctypes.POINTER(PoolStruct), _i64, _i64, _i64, _p], _i32),
+    "llmk_kv_release": ([ctypes.POINTER(PoolStruct), _i64], _i32),
+    "llmk_kv_admit": ([ctypes.POINTER(PoolStruct), _i64, ctypes.POINTER(_i32)], _i32),
     "llmk_decode_workspace_bytes": ([ctypes.POINTER(Config), _i64], _i64),
     "llmk_decode_step": ([ctypes.POINTER(Config), ctypes.POINTER(ModelStruct), ctypes.POINTER(PoolStruct), _i64, _i64,
                           _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p], _i32),
@@ -334,12 +346,17 @@ class Model:
 
 
 class KVPool:
-    """Slot-indexed K/V pool: per layer one K and one V tensor of n_slots*capacity*n_kv*head_dim elements."""
+    """Slot-indexed K/V pool: per layer one K and one V tensor of n_slots*capacity*n_kv*head_dim elements.
+    With block_tokens (and n_blocks) the pool is paged: each layer tensor holds n_blocks blocks of block_tokens
+    positions, and slots reach them through a block table (device int32 [n_slots][max_blocks]) whose host
+    mirror (table_h), reference counts and free count the library keeps."""
 
-    def __init__(self, n_layer, n_slots, capacity, n_kv, head_dim, dtype, device="cuda", tensors=None):
+    def __init__(self, n_layer, n_slots, capacity, n_kv, head_dim, dtype, device="cuda", tensors=None,
+                 block_tokens=None, n_blocks=None):
         import torch
         tdt = torch.bfloat16 if dtype == BF16 else torch.float32
-        n = n_slots * capacity * n_kv * head_dim
+        self.paged = block_tokens is not None
+        n = (n_blocks * block_tokens if self.paged else n_slots * capacity) * n_kv * head_dim
         if tensors is None:
             self.k = [torch.zeros(n, dtype=tdt, device=device) for _ in range(n_layer)]
             self.v = [torch.zeros(n, dtype=tdt, device=device) for _ in range(n_layer)]
@@ -355,9 +372,52 @@ class KVPool:
                                  self.slot_len.ctypes.data_as(ctypes.POINTER(_i64)),
                                  self.len_k.ctypes.data_as(ctypes.POINTER(_i64)),
                                  self.len_v.ctypes.data_as(ctypes.POINTER(_i64)))
+        if self.paged:
+            self.block_tokens, self.n_blocks = block_tokens, n_blocks
+            self.max_blocks = -(-capacity // block_tokens)
+            self.table = torch.full((n_slots * self.max_blocks,), -1, dtype=torch.int32, device=device)
+            self.table_h = np.full((n_slots, self.max_blocks), -1, dtype=np.int32)
+            self.refcount = np.zeros(n_blocks, dtype=np.int32)
+            self.pages = PagesStruct(block_tokens, n_blocks, self.max_blocks, _ptr(self.table),
+                                     self.table_h.ctypes.data_as(ctypes.POINTER(_i32)),
+                                     self.refcount.ctypes.data_as(ctypes.POINTER(_i32)), 0)
+            self.struct.pages = ctypes.pointer(self.pages)
         self.capacity, self.n_kv, self.head_dim, self.n_slots = capacity, n_kv, head_dim, n_slots
         self.n_layer, self.dtype = n_layer, dtype
         check(lib.llmk_kv_pool_init(ctypes.byref(self.struct)), "kv_pool_init")
+
+    @property
+    def n_free(self) -> int:
+        return int(self.pages.n_free)
+
+    def _rows(self, slot: int, start: int, n: int):
+        """(cache row, count) runs covering positions [start, start + n) of a slot (paged: through table_h)."""
+        if not self.paged:
+            return [(slot * self.capacity + start, n)]
+        runs, p, bt = [], start, self.block_tokens
+        while p < start + n:
+            b = int(self.table_h[slot, p // bt])
+            if b < 0:
+                raise ValueError(f"slot {slot} position {p}: no block reserved")
+            c = min(start + n - p, bt - p % bt)
+            runs.append((b * bt + p % bt, c))
+            p += c
+        return runs
+
+    def write_positions(self, layer: int, slot: int, which: str, start: int, values) -> None:
+        """Device copy of values ([n][n_kv][head_dim], pool dtype) into positions [start, start + n) of a slot
+        (paged: the positions must be reserved)."""
+        t = (self.k if which == "k" else self.v)[layer].view(-1, self.n_kv, self.head_dim)
+        i = 0
+        for r, c in self._rows(slot, start, values.shape[0]):
+            t[r:r + c] = values[i:i + c]
+            i += c
+
+    def read_positions(self, layer: int, slot: int, which: str, start: int, n: int):
+        """Device copy of positions [start, start + n) of a slot, [n][n_kv][head_dim]."""
+        import torch
+        t = (self.k if which == "k" else self.v)[layer].view(-1, self.n_kv, self.head_dim)
+        return torch.cat([t[r:r + c] for r, c in self._rows(slot, start, n)]) if n > 0 else t[:0].clone()
 
     def set_len(self, slot: int, n_pos: int) -> None:
         """Record that `slot` holds n_pos positions (its K/V written by the caller, e.g. a seeded prefix)."""
@@ -366,7 +426,9 @@ class KVPool:
         self.len_v[:, slot] = n_pos * self.n_kv * self.head_dim
 
     def slot_view(self, layer: int, slot: int, which: str = "k"):
-        """[capacity][n_kv][head_dim] view of one slot of one layer's K or V buffer."""
+        """[capacity][n_kv][head_dim] view of one slot of one layer's K or V buffer (contiguous pools)."""
+        if self.paged:
+            raise ValueError("a paged slot is not one view: use read_positions / write_positions")
         t = (self.k if which == "k" else self.v)[layer]
         plane = self.capacity * self.n_kv * self.head_dim
         return t[slot * plane:(slot + 1) * plane].view(self.capacity, self.n_kv, self.head_dim)
@@ -391,6 +453,28 @@ def gqa_attend(q, pool: KVPool, layer, slot, ctx_len, n_head, out, ws, stream=No
     """Attention of q over positions [0, ctx_len) of (layer, slot) of the pool."""
     return lib.llmk_gqa_attend(_ptr(q), _len(q), ctypes.byref(pool.struct), layer, slot, ctx_len, n_head, _ptr(out),
                                _len(out), _ptr(ws), _len(ws), _stream(stream))
+
+
+def kv_reserve(pool: KVPool, slot, pos_begin, pos_end, stream=None) -> int:
+    """Paged pools: make positions [pos_begin, pos_end) of a slot writable (fresh or copied blocks)."""
+    return lib.llmk_kv_reserve(ctypes.byref(pool.struct), slot, pos_begin, pos_end, _stream(stream))
+
+
+def kv_fork(pool: KVPool, src, dst, n_pos, stream=None) -> int:
+    """Paged pools: slot dst shares the blocks of the first n_pos positions of slot src."""
+    return lib.llmk_kv_fork(ctypes.byref(pool.struct), src, dst, n_pos, _stream(stream))
+
+
+def kv_release(pool: KVPool, slot) -> int:
+    """Paged pools: drop every block of a slot and mark it empty."""
+    return lib.llmk_kv_release(ctypes.byref(pool.struct), slot)
+
+
+def kv_admit(pool: KVPool, n_uncached):
+    """Paged pools: (status, admit) for a request whose uncached suffix is n_uncached positions."""
+    out = _i32(-1)
+    st = lib.llmk_kv_admit(ctypes.byref(pool.struct), n_uncached, ctypes.byref(out))
+    return st, out.value
 
 
 def kv_slot_offset(pool: KVPool, slot, pos, kv_head):

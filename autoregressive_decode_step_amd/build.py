@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libllmk.so")
-SOURCES = ["api.hip", "gemv.hip", "rowdot.hip", "batch.hip", "attention.hip", "step.hip", "elementwise.hip", "sample.hip", "pgemm.hip", "fattn.hip", "q8.hip"]
+SOURCES = ["api.hip", "gemv.hip", "rowdot.hip", "batch.hip", "attention.hip", "step.hip", "elementwise.hip", "sample.hip", "pgemm.hip", "fattn.hip", "q8.hip", "kvpages.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "kvpages.h"
 #include "loop.h"
 #include "q8.h"
 #include "llmk.h"
@@ -367,7 +368,24 @@ int32_t pool_check(const llmk_config* c, const llmk_kv_pool* p) {
   for (int64_t l = 0; l < p->n_layer; ++l)
     if (!p->k[l] || !p->v[l]) return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({p->n_slots, p->capacity});
+  if (st == LLMK_OK && p->pages) st = pages_check(p);
   return st;
+}
+
+// Paged pools: reserve the positions the call writes ([begin, end) of each slot); contiguous pools: nothing.
+int32_t pool_reserve(llmk_kv_pool* p, const KvReserve* req, int64_t n, hipStream_t s) {
+  return p->pages ? pages_reserve(p, req, n, s) : LLMK_OK;
+}
+int32_t pool_reserve1(llmk_kv_pool* p, int64_t slot, int64_t begin, int64_t end, hipStream_t s) {
+  const KvReserve r{slot, begin, end};
+  return pool_reserve(p, &r, 1, s);
+}
+// the positions [pos[r], pos[r] + n) of every row's slot, all or none
+int32_t batch_reserve(llmk_kv_pool* p, int64_t B, const int64_t* slots, const int64_t* pos, int64_t n, hipStream_t s) {
+  if (!p->pages) return LLMK_OK;
+  std::vector<KvReserve> r((size_t)B);
+  for (int64_t i = 0; i < B; ++i) r[(size_t)i] = KvReserve{slots[i], pos[i], pos[i] + n};
+  return pages_reserve(p, r.data(), B, s);
 }
 
 // The kernels of one decode step, in order: per layer K_QKV, K_ATTN, K_O, K_GATEUP, K_DOWN, then K_HEAD.
@@ -380,7 +398,7 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
                          hipStream_t s) {
   const int bf = c->w_dtype == LLMK_BF16;
   const int64_t d = c->d, kvd = c->n_kv * c->head_dim;
-  const int64_t kv_off = slot * pool->capacity * kvd;
+  const int64_t kv_off = pool->pages ? 0 : slot * pool->capacity * kvd;
   const int64_t kvsz = dtype_size(c->kv_dtype);
   unsigned* gcnt = D.counters;
   unsigned* acnt = D.counters + D.n_gemv_counters;
@@ -429,6 +447,8 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
     a.v = static_cast<const char*>(pool->v[l]) + kv_off * kvsz;
     a.k_w = static_cast<char*>(pool->k[l]) + kv_off * kvsz;
     a.v_w = static_cast<char*>(pool->v[l]) + kv_off * kvsz;
+    a.pg = pages_view(pool);
+    a.pg.table = pages_slot_row(pool, slot);
     a.rope_table = static_cast<const float*>(m->rope_table.ptr);
     a.rope_layout = c->rope_layout;
     a.state = D.state;
@@ -633,7 +653,9 @@ StepParams step_params(const llmk_config* c, const llmk_model* m, const llmk_kv_
   p.rope_layout = c->rope_layout;
   p.eps = (float)c->eps;
   p.nwg = nwg;
-  p.kv_off = slot * pool->capacity * c->n_kv * c->head_dim;
+  p.kv_off = pool->pages ? 0 : slot * pool->capacity * c->n_kv * c->head_dim;
+  p.kv_table = pages_slot_row(pool, slot);
+  p.kv_shift = pages_shift(pool);
   p.attn_chunk = D.attn.chunk;
   p.state = D.state;
   p.x = D.step_x;
@@ -867,6 +889,7 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       a.k_w = pool->k[l];
       a.v_w = pool->v[l];
       a.slot_elems = pool->capacity * kvd;
+      a.pg = pages_view(pool);
       a.rope_table = static_cast<const float*>(m->rope_table.ptr);
       a.rope_layout = c->rope_layout;
       a.state = nullptr;
@@ -879,7 +902,8 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       a.no_append = P.prefill ? 1 : 0;
       if (P.prefill) {
         hipError_t e = rope_append_rows_launch(P.qkv_buf, P.qkv_n, P.state, B, a.H, a.Hkv, a.hd, a.rope_table,
-                                               a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, s);
+                                               a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, a.pg,
+                                               s);
         if (e != hipSuccess) return e;
       }
       return attn_launch(a, s);
@@ -1081,6 +1105,7 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
       a.v = pool->v[l];
       a.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
       a.slot_elems = pool->capacity * c->n_kv * c->head_dim;
+      a.pg = pages_view(pool);
       a.rope_table = static_cast<const float*>(m->rope_table.ptr);
       a.rope_layout = c->rope_layout;
       a.span = FA_SPAN;
@@ -1089,7 +1114,7 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
       a.out_hi = B.att_hi;
       a.out_lo = B.att_lo;
       e = rope_append_rows_launch(a.qkv, a.qkv_stride, B.state, a.rows, a.H, a.Hkv, (int32_t)c->head_dim, a.rope_table,
-                                  a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, s);
+                                  a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, a.pg, s);
       if (e == hipSuccess) e = fattn_launch(a, ctx_end, s);
     } else if (e == hipSuccess) {
       e = launch_batch_kernel(c, m, pool, B, l, BK_ATTN, nullptr, nullptr, nullptr, s);
@@ -1389,8 +1414,10 @@ int64_t llmk_gqa_attend_workspace_bytes(int64_t ctx_len, int64_t n_head, int64_t
 
 // the attention launch shared by llmk_gqa_attend_flat and llmk_gqa_attend (every check done)
 static int32_t gqa_attend_run(const float* q, const void* k_cache, const void* v_cache, int32_t kv_dtype, int64_t ctx_len,
-                              int64_t n_head, int64_t n_kv, int64_t head_dim, float* out, void* ws, void* stream) {
+                              int64_t n_head, int64_t n_kv, int64_t head_dim, float* out, void* ws, void* stream,
+                              const KvPaging& pg = KvPaging{}) {
   AttnParams a{};
+  a.pg = pg;
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -1425,15 +1452,19 @@ int32_t llmk_gqa_attend_flat(const float* q, int64_t len_q, const void* k_cache,
   return gqa_attend_run(q, k_cache, v_cache, kv_dtype, ctx_len, n_head, n_kv, head_dim, out, ws, stream);
 }
 
-// A pool descriptor's own fields (no config to compare with): 578 / 561 / 564.
-static int32_t pool_fields_check(const llmk_kv_pool* p) {
+}  // extern "C"
+
+// A pool descriptor's own fields (no config to compare with): 578 / 561 / 564, then the pages.
+int32_t llmk::pool_fields_check(const llmk_kv_pool* p) {
   if (!p || !p->k || !p->v || !p->slot_len_h || !is_dtype(p->dtype)) return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({p->n_layer, p->n_slots, p->capacity, p->n_kv, p->head_dim});
   if (st != LLMK_OK) return st;
   for (int64_t l = 0; l < p->n_layer; ++l)
     if (!p->k[l] || !p->v[l] || !aligned16(p->k[l]) || !aligned16(p->v[l])) return LLMK_INVALID_ARGUMENT;
-  return LLMK_OK;
+  return p->pages ? pages_check(p) : LLMK_OK;
 }
+
+extern "C" {
 
 int32_t llmk_kv_pool_init(llmk_kv_pool* pool) {
   const int32_t st = pool_fields_check(pool);
@@ -1442,6 +1473,11 @@ int32_t llmk_kv_pool_init(llmk_kv_pool* pool) {
   for (int64_t i = 0; i < pool->n_layer * pool->n_slots; ++i) {
     if (pool->len_k_h) pool->len_k_h[i] = 0;
     if (pool->len_v_h) pool->len_v_h[i] = 0;
+  }
+  if (llmk_kv_pages* g = pool->pages) {
+    for (int64_t i = 0; i < pool->n_slots * g->max_blocks; ++i) g->table_h[i] = -1;
+    for (int64_t b = 0; b < g->n_blocks; ++b) g->refcount_h[b] = 0;
+    g->n_free = g->n_blocks;
   }
   return LLMK_OK;
 }
@@ -1460,11 +1496,21 @@ int32_t llmk_kv_append(llmk_kv_pool* pool, int64_t layer, int64_t slot, int32_t 
   int64_t* rec = (which == 0 ? pool->len_k_h : pool->len_v_h) + layer * pool->n_slots + slot;
   if (cache_len != *rec) return LLMK_CACHE_LENGTH_MISMATCH;
   if (len_new != n_new) return LLMK_NEW_LENGTH_MISMATCH;
-  const int64_t plane = pool->capacity * pool->n_kv * pool->head_dim;
+  const int64_t row = pool->n_kv * pool->head_dim, plane = pool->capacity * row;
   if (cache_len + n_new > plane) return LLMK_CACHE_CAPACITY_EXCEEDED;
   void* buf = which == 0 ? pool->k[layer] : pool->v[layer];
-  const int64_t off = slot * plane + cache_len;
-  st = finish(kv_append_launch(buf, pool->dtype == LLMK_BF16, off, new_vals, n_new, as_stream(stream)));
+  int64_t off = slot * plane + cache_len;
+  if (pool->pages) {
+    // the positions the elements fall in, then the elements through the slot's table row
+    const int64_t p0 = cache_len / row;
+    st = pool_reserve1(pool, slot, p0, (cache_len + n_new + row - 1) / row, as_stream(stream));
+    if (st != LLMK_OK) return st;
+    off = pages_row(pool, slot, p0) * row + (cache_len - p0 * row);
+    st = finish(kv_append_paged_launch(buf, pool->dtype == LLMK_BF16, pages_slot_row(pool, slot), pages_shift(pool),
+                                       row, cache_len, new_vals, n_new, as_stream(stream)));
+  } else {
+    st = finish(kv_append_launch(buf, pool->dtype == LLMK_BF16, off, new_vals, n_new, as_stream(stream)));
+  }
   if (st != LLMK_OK) return st;
   *rec = cache_len + n_new;
   if (new_len_h) *new_len_h = *rec;
@@ -1487,14 +1533,19 @@ int32_t llmk_gqa_attend(const float* q, int64_t len_q, const llmk_kv_pool* pool,
   if (len_q != n_head * hd) return LLMK_A_LENGTH_MISMATCH;
   if (len_out != n_head * hd) return LLMK_OUTPUT_LENGTH_MISMATCH;
   if (ctx_len > pool->capacity) return LLMK_POSITION_OUT_OF_RANGE;
+  if (pool->pages)
+    for (int64_t p0 = 0; p0 < ctx_len; p0 += pool->pages->block_tokens)
+      if (pages_row(pool, slot, p0) < 0) return LLMK_POSITION_OUT_OF_RANGE;
   const int64_t need = ctx_len * n_kv * hd, rec = layer * pool->n_slots + slot;
   if ((pool->len_k_h && pool->len_k_h[rec] < need) || (pool->len_v_h && pool->len_v_h[rec] < need))
     return LLMK_CACHE_LENGTH_MISMATCH;
   if (len_ws < llmk_gqa_attend_workspace_bytes(ctx_len, n_head, hd)) return LLMK_INVALID_ARGUMENT;
-  const int64_t esz = dtype_size(pool->dtype), base = slot * pool->capacity * n_kv * hd * esz;
+  const int64_t esz = dtype_size(pool->dtype), base = pool->pages ? 0 : slot * pool->capacity * n_kv * hd * esz;
   if (base % 16 != 0) return LLMK_INVALID_ARGUMENT;   // the kernel's 16-byte loads need the slot aligned
+  KvPaging pg = pages_view(pool);
+  pg.table = pages_slot_row(pool, slot);
   return gqa_attend_run(q, static_cast<const char*>(pool->k[layer]) + base, static_cast<const char*>(pool->v[layer]) + base,
-                        pool->dtype, ctx_len, n_head, n_kv, hd, out, ws, stream);
+                        pool->dtype, ctx_len, n_head, n_kv, hd, out, ws, stream, pg);
 }
 
 int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n) {
@@ -1576,6 +1627,13 @@ int32_t llmk_kv_slot_offset(const llmk_kv_pool* pool, int64_t slot, int64_t pos,
   if (pos < 0 || pos >= pool->capacity) return LLMK_POSITION_OUT_OF_RANGE;
   if (kv_head < 0 || kv_head >= pool->n_kv) return LLMK_HEAD_SHAPE_INVALID;
   const int64_t row = pool->n_kv * pool->head_dim;
+  if (pool->pages) {
+    if (!pool->pages->table_h || pool->pages->block_tokens < 1) return LLMK_INVALID_ARGUMENT;
+    const int64_t r = pages_row(pool, slot, pos);
+    if (r < 0) return LLMK_POSITION_OUT_OF_RANGE;
+    *offset_h = r * row + kv_head * pool->head_dim;
+    return LLMK_OK;
+  }
   *offset_h = slot * pool->capacity * row + pos * row + kv_head * pool->head_dim;
   return LLMK_OK;
 }
@@ -1615,6 +1673,7 @@ int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_k
   const int nwg = step_workgroups(cfg);
   if (nwg < 0) return LLMK_INVALID_ARGUMENT;
   hipStream_t s = as_stream(stream);
+  if ((st = pool_reserve1(pool, slot, pos, pos + 1, s)) != LLMK_OK) return st;
   hipError_t e;
   if (nwg > 0) {
     e = step_prelude(cfg, model, pool, D, (int32_t)token, (int32_t)pos, s);
@@ -1701,6 +1760,9 @@ static int32_t decode_steps_run(const llmk_config* cfg, const llmk_model* model,
   const int nwg = step_workgroups(cfg);
   if (nwg < 0) return LLMK_INVALID_ARGUMENT;
   hipStream_t s = as_stream(stream);
+  // every position the replays write is reserved before the capture
+  const int32_t st = pool_reserve1(pool, slot, pos0, pos0 + n_steps, s);
+  if (st != LLMK_OK) return st;
   hipError_t e;
   if (nwg > 0) {
     e = step_prelude(cfg, model, pool, D, (int32_t)token0, (int32_t)pos0, s);
@@ -1760,6 +1822,7 @@ int32_t llmk_decode_step_batch(const llmk_config* cfg, const llmk_model* model, 
   if (len_ws < P.bytes) return LLMK_INVALID_ARGUMENT;
   plan_batch(cfg, batch, ws, P);
   hipStream_t s = as_stream(stream);
+  if ((st = batch_reserve(pool, batch, slots_h, pos_h, 1, s)) != LLMK_OK) return st;
   hipError_t e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
   if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
   if (e == hipSuccess) e = enqueue_batch(cfg, model, pool, P, logits, tokens_out, hidden, s);
@@ -1804,6 +1867,7 @@ int32_t prefill_run(const llmk_config* cfg, const llmk_model* model, llmk_kv_poo
   if (logits && len_logits != cfg->vocab) return LLMK_LOGITS_LENGTH_MISMATCH;
   if (hidden && len_hidden != cfg->n_layer * cfg->d) return LLMK_OUTPUT_LENGTH_MISMATCH;
   if (len_ws < prefill_bytes(cfg, n)) return LLMK_INVALID_ARGUMENT;
+  if ((st = pool_reserve1(pool, slot, pos0, pos0 + n, s)) != LLMK_OK) return st;
 
   hipError_t e = hipSuccess;
   const int64_t rows = std::min(n, kPrefillRows);
@@ -1888,6 +1952,7 @@ int32_t llmk_decode_steps_batch(const llmk_config* cfg, const llmk_model* model,
   if (len_ws < P.bytes) return LLMK_INVALID_ARGUMENT;
   plan_batch(cfg, batch, ws, P);
   hipStream_t s = as_stream(stream);
+  if ((st = batch_reserve(pool, batch, slots_h, pos0_h, n_steps, s)) != LLMK_OK) return st;
   hipError_t e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
   if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);
   if (e != hipSuccess) return LLMK_DEVICE_ERROR;
@@ -1932,6 +1997,7 @@ int32_t llmk_decode_step_profiled(const llmk_config* cfg, const llmk_model* mode
   if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
   plan_decode(cfg, ws, D);
   hipStream_t s = as_stream(stream);
+  if ((st = pool_reserve1(pool, slot, pos, pos + 1, s)) != LLMK_OK) return st;
   hipEvent_t* ev = new hipEvent_t[2 * nk]();
   hipError_t e = hipSuccess;
   int64_t made = 0;
@@ -1972,6 +2038,8 @@ int32_t llmk_decode_kernel_time(const llmk_config* cfg, const llmk_model* model,
   if (len_ws < D.bytes) return LLMK_INVALID_ARGUMENT;
   plan_decode(cfg, ws, D);
   hipStream_t s = as_stream(stream);
+  if (kernel == K_STEP && pos + reps > pool->capacity) return LLMK_CACHE_CAPACITY_EXCEEDED;
+  if ((st = pool_reserve1(pool, slot, pos, pos + (kernel == K_STEP ? reps : 1), s)) != LLMK_OK) return st;
   if (kernel == K_STEP) return time_step_kernel(cfg, model, pool, slot, token, pos, reps, token_out, ms_per_launch_h, D, s);
   // one ordinary step leaves valid activations in the workspace; the state is then reset to (token, pos)
   // so that repeated attention launches stay at pos
@@ -2039,6 +2107,7 @@ int32_t llmk_decode_batch_kernel_time(const llmk_config* cfg, const llmk_model* 
   if (len_ws < P.bytes) return LLMK_INVALID_ARGUMENT;
   plan_batch(cfg, batch, ws, P);
   hipStream_t s = as_stream(stream);
+  if ((st = batch_reserve(pool, batch, slots_h, pos_h, 1, s)) != LLMK_OK) return st;
   // one ordinary step leaves valid activations; the state is reset so repeated attention stays at pos
   hipError_t e = fill_u32_launch(P.counters, batch_counters_total(cfg, P), 0u, s);
   if (e == hipSuccess) e = set_batch_state_launch(P.state, init, s);

@@ -135,7 +135,11 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   const int wave = wv % ATTN_SWAVES;                     // wave within its stream
   const int stid = threadIdx.x % ATTN_STHREADS;          // thread within its stream
   const int64_t rstride = (int64_t)p.Hkv * HD;           // elements between positions
-  const int64_t rbase = batched ? (int64_t)p.bstate->slot[row] * p.slot_elems : 0;   // the row's slot region
+  // the row's slot region (contiguous pool), or its row of the block table (paged pool: tiles are a divisor of
+  // the block, so every position of a tile sits in one block and the tile's rows are consecutive)
+  const int32_t* const trow =
+      p.pg.table ? p.pg.table + (batched ? (int64_t)p.bstate->slot[row] * p.pg.stride : 0) : nullptr;
+  const int64_t rbase = batched && !trow ? (int64_t)p.bstate->slot[row] * p.slot_elems : 0;
   const T* Kb = static_cast<const T*>(p.k) + rbase + (int64_t)kvh * HD;
   const T* Vb = static_cast<const T*>(p.v) + rbase + (int64_t)kvh * HD;
   const float* qkv_raw = p.qkv_raw ? p.qkv_raw + (batched ? (int64_t)row * p.qkv_stride : 0) : nullptr;
@@ -143,14 +147,15 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   const float scale = 1.0f / sqrtf((float)HD);
 
   // cooperative tile load by one stream: vector idx -> (K or V, row, vector); rows past te are clamped
-  // to te - 1
+  // to te - 1; a paged tile starts at the cache row of its first position
   uint4 reg[NVL];
 #define LLMK_LOAD_TILE(T0)                                                                        \
+  const int64_t tile_row0 = trow ? kv_block_row(trow, p.pg.shift, (T0)) - (T0) : 0;               \
   _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
     const int idx = stid + k * ATTN_STHREADS;                                                     \
     const int which = idx / (CH * RV), rem = idx % (CH * RV);                                     \
     const int t = min((T0) + rem / RV, te - 1);                                                    \
-    const T* src = (which == 0 ? Kb : Vb) + (int64_t)t * rstride + (rem % RV) * EPV;               \
+    const T* src = (which == 0 ? Kb : Vb) + (tile_row0 + t) * rstride + (rem % RV) * EPV;          \
     if (HD >= EPV) {                                                                              \
       reg[k] = idx < NVT ? gload<uint4>(src) : make_uint4(0, 0, 0, 0);                              \
     } else {                                                                                      \
@@ -259,7 +264,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     }
     __syncthreads();
     if (owner) {
-      const int64_t off = (int64_t)pos * p.Hkv * HD + (int64_t)kvh * HD;
+      const int64_t off = (trow ? kv_block_row(trow, p.pg.shift, pos) : (int64_t)pos) * p.Hkv * HD + (int64_t)kvh * HD;
       for (int e = threadIdx.x; e < 2 * HD; e += ATTN_THREADS) {
         const int w = e / HD, ee = e % HD;
         (w == 0 ? static_cast<T*>(p.k_w) : static_cast<T*>(p.v_w))[rbase + off + ee] = s_new[w][ee];

@@ -198,4 +198,18 @@ __device__ __forceinline__ V gload(const void* ptr) {
   }
 }
 
+// ---- paged K/V: a slot's positions reach their blocks through its row of the block table ----------------
+
+// The block table as the kernels take it: table == nullptr for contiguous slots.
+struct KvPaging {
+  const int32_t* table;   // [n_slots][stride] block ids
+  int64_t stride;         // entries per slot
+  int32_t shift;          // log2 of the positions per block
+};
+
+// Cache row of position t of the slot whose table row is `trow` (blocks of 1 << shift positions).
+__device__ __forceinline__ int64_t kv_block_row(const int32_t* trow, int shift, int64_t t) {
+  return ((int64_t)trow[t >> shift] << shift) | (t & ((int64_t(1) << shift) - 1));
+}
+
 }  // namespace llmk

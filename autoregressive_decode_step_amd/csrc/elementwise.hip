@@ -122,13 +122,14 @@ hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk,
 template <typename T>
 __global__ void rope_append_rows_kernel(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t H,
                                         int32_t Hkv, int32_t hd, const float* table, int32_t layout, T* k, T* v,
-                                        int64_t slot_elems) {
+                                        int64_t slot_elems, KvPaging pg) {
   const int r = blockIdx.x, kvh = blockIdx.y;
   const int64_t pos = st->pos[r];
   const float* src = qkv + (int64_t)r * qkv_stride;
   const float* ks = src + (int64_t)H * hd + (int64_t)kvh * hd;
   const float* vs = src + (int64_t)(H + Hkv) * hd + (int64_t)kvh * hd;
-  const int64_t off = (int64_t)st->slot[r] * slot_elems + pos * Hkv * hd + (int64_t)kvh * hd;
+  const int64_t off = (pg.table ? kv_block_row(pg.table + (int64_t)st->slot[r] * pg.stride, pg.shift, pos) * Hkv * hd
+                                : (int64_t)st->slot[r] * slot_elems + pos * Hkv * hd) + (int64_t)kvh * hd;
   const int half = hd / 2;
   for (int j = threadIdx.x; j < half; j += blockDim.x) {
     const int ia = layout == 0 ? j : 2 * j;
@@ -143,14 +144,15 @@ __global__ void rope_append_rows_kernel(const float* qkv, int64_t qkv_stride, co
 
 hipError_t rope_append_rows_launch(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t rows,
                                    int32_t H, int32_t Hkv, int32_t hd, const float* rope_table, int32_t rope_layout,
-                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, hipStream_t s) {
+                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, const KvPaging& pg,
+                                   hipStream_t s) {
   const dim3 grid((unsigned)rows, (unsigned)Hkv);
   if (kv_is_bf16)
     hipLaunchKernelGGL(rope_append_rows_kernel<bf16_t>, grid, dim3(64), 0, s, qkv, qkv_stride, st, H, Hkv, hd,
-                       rope_table, rope_layout, static_cast<bf16_t*>(k), static_cast<bf16_t*>(v), slot_elems);
+                       rope_table, rope_layout, static_cast<bf16_t*>(k), static_cast<bf16_t*>(v), slot_elems, pg);
   else
     hipLaunchKernelGGL(rope_append_rows_kernel<float>, grid, dim3(64), 0, s, qkv, qkv_stride, st, H, Hkv, hd,
-                       rope_table, rope_layout, static_cast<float*>(k), static_cast<float*>(v), slot_elems);
+                       rope_table, rope_layout, static_cast<float*>(k), static_cast<float*>(v), slot_elems, pg);
   return hipGetLastError();
 }
 

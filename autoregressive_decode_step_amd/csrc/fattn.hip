@@ -73,7 +73,10 @@ __global__ __launch_bounds__(FA_THREADS) void fattn_kernel(const FattnParams p) 
   if (tb > qpos_max) return;                     // no query of this tile reaches this part
   const int te = min(tb + p.span, qpos_max + 1);
   const int64_t rstride = (int64_t)p.Hkv * FA_HD;
-  const int64_t rbase = (int64_t)p.st->slot[r0] * p.slot_elems + (int64_t)kvh * FA_HD;
+  // the chunk's slot: its region (contiguous pool) or its row of the block table (paged pool; a tile of FA_CH
+  // positions sits in one block)
+  const int32_t* const trow = p.pg.table ? p.pg.table + (int64_t)p.st->slot[r0] * p.pg.stride : nullptr;
+  const int64_t rbase = (trow ? 0 : (int64_t)p.st->slot[r0] * p.slot_elems) + (int64_t)kvh * FA_HD;
   const T* K = static_cast<const T*>(p.k) + rbase;
   const T* V = static_cast<const T*>(p.v) + rbase;
   const float scale = 1.0f / sqrtf((float)FA_HD);
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(FA_THREADS) void fattn_kernel(const FattnParams p) 
   constexpr int VPG = sizeof(T) / 2;                        // 16-byte loads per group
   uint4 kr[NG * VPG], vr[NG * VPG];
   auto load_tile = [&](int t0) {
-    const int64_t pos = min(t0 + lane, te - 1);
+    const int64_t pos = (trow ? kv_block_row(trow, p.pg.shift, t0) - t0 : 0) + min(t0 + lane, te - 1);
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const int c = (wave + 4 * j) * 8;

@@ -152,6 +152,7 @@ struct FattnParams {
   const void* v;
   int32_t kv_is_bf16;
   int64_t slot_elems;
+  KvPaging pg;                 // paged pool: rows through the chunk slot's table row (then slot_elems unused)
   const float* rope_table;
   int32_t rope_layout;
   int32_t span;                // FA_SPAN
@@ -212,6 +213,10 @@ struct AttnParams {
   const BatchState* bstate;
   int32_t rows;                // grid.z when bstate is set
   int64_t slot_elems;
+  // paged pool (pg.table set): position t of the sequence is cache row kv_block_row(trow, pg.shift, t) of
+  // k / v / k_w / v_w (no slot offset), trow = pg.table (single sequence: its own row) or, batched,
+  // pg.table + slot * pg.stride
+  KvPaging pg;
   int64_t qkv_stride;
   bf16_t* out_hi;
   bf16_t* out_lo;
@@ -252,7 +257,9 @@ struct StepParams {
   int32_t n_layer, d, qd, kvd, F, V, H, Hkv, hd, rope_layout;
   float eps;
   int32_t nwg;                  // workgroups (one per CU)
-  int64_t kv_off;               // element offset of the slot in each pool buffer
+  int64_t kv_off;               // element offset of the slot in each pool buffer (0 for a paged pool)
+  const int32_t* kv_table;      // paged pool: the slot's row of the block table (else nullptr)
+  int32_t kv_shift;             // log2 of the positions per block
   int32_t attn_chunk;           // positions per attention tile
   int32_t give_up;              // test only: the attention waits for a tag nobody writes (bounded-wait path)
   DecodeState* state;
@@ -298,6 +305,18 @@ hipError_t rope_table_launch(float* table, int64_t max_pos, int64_t hd, double b
 hipError_t rope_launch(float* q, float* k, int64_t rows, int64_t nq, int64_t nk, int64_t hd, const int32_t* pos,
                        int64_t max_pos, const float* table, int layout, hipStream_t s);
 hipError_t kv_append_launch(void* cache, int is_bf16, int64_t offset, const float* src, int64_t n, hipStream_t s);
+// Paged append: element f = first + i (i < n) of a slot's flat cache goes to position f / row_elems, element
+// f % row_elems, through the slot's table row trow (blocks of 1 << shift positions).
+hipError_t kv_append_paged_launch(void* cache, int is_bf16, const int32_t* trow, int shift, int64_t row_elems,
+                                  int64_t first, const float* src, int64_t n, hipStream_t s);
+// Block-table writes: table[idx[i]] = val[i] for i < n, carried by value in the launch.
+constexpr int TABLE_EDITS = 48;
+struct TableEdits {
+  int64_t idx[TABLE_EDITS];
+  int32_t val[TABLE_EDITS];
+  int32_t n;
+};
+hipError_t table_set_launch(int32_t* table, const TableEdits& e, hipStream_t s);
 constexpr int SAMPLE_MAX_K = 1024;   // survivors (top-k after clamping to the row length) the sampler holds
 enum SampleForm { SAMPLE_WIDE = 0, SAMPLE_WAVE_SLICES = 1, SAMPLE_BLOCK_SLICES = 2 };
 struct SamplePlan {
@@ -316,7 +335,8 @@ hipError_t fill_u32_launch(unsigned* p, int64_t n, unsigned v, hipStream_t s);
 // store them at pos[r] of slot[r] (k, v: one layer's pool buffers; qkv: [rows][qkv_stride] raw q|k|v).
 hipError_t rope_append_rows_launch(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t rows,
                                    int32_t H, int32_t Hkv, int32_t hd, const float* rope_table, int32_t rope_layout,
-                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, hipStream_t s);
+                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, const KvPaging& pg,
+                                   hipStream_t s);
 hipError_t set_state_launch(DecodeState* st, int32_t token, int32_t pos, hipStream_t s);
 
 }  // namespace llmk

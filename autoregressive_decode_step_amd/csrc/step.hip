@@ -446,6 +446,8 @@ __device__ __forceinline__ AttnParams sk_attn_params(const StepParams& p, int l,
   ap.v = static_cast<const char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
   ap.k_w = static_cast<char*>(Ly.k) + p.kv_off * (int64_t)sizeof(T);
   ap.v_w = static_cast<char*>(Ly.v) + p.kv_off * (int64_t)sizeof(T);
+  ap.pg.table = p.kv_table;
+  ap.pg.shift = p.kv_shift;
   ap.qkv_tag = p.qkv + (int64_t)l * p.qkv_stride;
   ap.out_tag = p.att + (int64_t)l * p.att_stride;
   ap.tag = p.give_up ? (tag | 0x80000000u) : tag;   // a tag no workgroup writes (tests of the give-up path)

@@ -10,8 +10,8 @@ import numpy as np
 import torch
 
 from . import (BF16, F32, Q8, W_IN_OUT, W_OUT_IN, Config, KVPool, Model, check, decode_step, decode_steps,
-               decode_workspace_bytes, make_config, q8_pack_bytes, quantize_q8, rope_table_init, transpose,
-               workspace)
+               decode_workspace_bytes, kv_reserve, make_config, q8_pack_bytes, quantize_q8, rope_table_init,
+               transpose, workspace)
 
 _LAYER_MAP = (("wq", "wq"), ("wk", "wk"), ("wv", "wv"), ("wo", "wo"), ("gate", "w_gate"), ("up", "w_up"),
               ("down", "w_down"), ("n1", "g_attn"), ("n2", "g_ffn"))
@@ -79,17 +79,25 @@ def upload_model(cfg: Config, W: dict, device="cuda", stream=None) -> Model:
     return Model(cfg, emb, out, norm, table, layers)
 
 
-def new_pool(cfg: Config, n_slots: int, capacity: int, device="cuda") -> KVPool:
-    return KVPool(cfg.n_layer, n_slots, capacity, cfg.n_kv, cfg.head_dim, cfg.kv_dtype, device)
+def new_pool(cfg: Config, n_slots: int, capacity: int, device="cuda", block_tokens=None, n_blocks=None) -> KVPool:
+    """A contiguous pool, or with block_tokens and n_blocks a paged one."""
+    return KVPool(cfg.n_layer, n_slots, capacity, cfg.n_kv, cfg.head_dim, cfg.kv_dtype, device,
+                  block_tokens=block_tokens, n_blocks=n_blocks)
+
+
+def _reserve(pool: KVPool, slot: int, n: int) -> None:
+    if pool.paged and n > 0:
+        check(kv_reserve(pool, slot, 0, n), "kv_reserve")
 
 
 def fill_prefix(pool: KVPool, slot: int, prefix: list) -> None:
     """Copy host K/V for positions 0..n-1 (per layer (K, V), each [n][n_kv][hd] in the pool dtype) into a
-    slot and record its length."""
+    slot (a paged pool reserves its blocks first) and record its length."""
     n = prefix[0][0].shape[0]
+    _reserve(pool, slot, n)
     for l, (kk, vv) in enumerate(prefix):
-        pool.slot_view(l, slot, "k")[:n] = to_device(kk, pool.k[l].device).view(n, pool.n_kv, pool.head_dim)
-        pool.slot_view(l, slot, "v")[:n] = to_device(vv, pool.v[l].device).view(n, pool.n_kv, pool.head_dim)
+        pool.write_positions(l, slot, "k", 0, to_device(kk, pool.k[l].device).view(n, pool.n_kv, pool.head_dim))
+        pool.write_positions(l, slot, "v", 0, to_device(vv, pool.v[l].device).view(n, pool.n_kv, pool.head_dim))
     pool.set_len(slot, n)
 
 
@@ -124,10 +132,11 @@ def upload_kv_source(source: list, device="cuda") -> list:
 def fill_prefix_window(pool: KVPool, slot: int, source_dev: list, start: int, n: int) -> None:
     """Copy positions [start, start + n) of a device K/V source into positions 0..n-1 of a slot and record
     its length (device-to-device)."""
+    _reserve(pool, slot, n)
     for l, (kk, vv) in enumerate(source_dev):
         if n > 0:
-            pool.slot_view(l, slot, "k")[:n] = kk[start:start + n]
-            pool.slot_view(l, slot, "v")[:n] = vv[start:start + n]
+            pool.write_positions(l, slot, "k", 0, kk[start:start + n])
+            pool.write_positions(l, slot, "v", 0, vv[start:start + n])
     pool.set_len(slot, n)
 
 

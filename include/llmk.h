@@ -317,10 +317,42 @@ typedef struct {
   const llmk_tensor* layers; /* host array [n_layer * LLMK_LAYER_TENSORS] */
 } llmk_model;
 
+/* Paged K/V blocks ([xpu] "3. The K/V cache and the block store": the cache is paged in fixed blocks of
+ * block_tokens positions, shared between sequences by reference count with copy-on-write, and a full pool
+ * refuses the append). With llmk_kv_pool.pages set, each layer buffer is a store of n_blocks blocks, and
+ * position p of slot s, K/V head g, element i sits at
+ *   (b * block_tokens + p % block_tokens) * n_kv * head_dim + g * head_dim + i,
+ *   b = table[s * max_blocks + p / block_tokens],
+ * so each layer buffer holds n_blocks * block_tokens * n_kv * head_dim elements. One block id names the same
+ * positions in every layer's K and V buffer. capacity stays the most positions one slot may hold.
+ * The caller allocates every array and the library keeps them consistent: before an entry point writes
+ * positions of a slot it reserves them, in slot order and then block order:
+ *   - a table entry of -1 takes the lowest-numbered free block;
+ *   - an entry whose block other slots also hold (refcount > 1) is copied first: the lowest-numbered free
+ *     block receives the whole block (every layer, K and V), the old block's refcount drops by one and the
+ *     entry moves to the copy (copy-on-write);
+ *   - when the free blocks cannot cover every block the call needs, it returns 571 and changes nothing;
+ *   - when the stream is being captured into a graph and the reservation needs device work (a copy or a
+ *     table write), it returns 578: a captured graph would repeat that work on every replay (reserve ahead
+ *     with llmk_kv_reserve instead).
+ * These codes apply to every entry point that writes a paged pool (decode steps single and batched,
+ * prefill, llmk_kv_append); their other checks run first. The device table is written by the library (stream-ordered kernels) as entries change; entries that were
+ * never reserved are never read. A block's refcount is the number of table entries that hold it. */
+typedef struct {
+  int64_t block_tokens;    /* positions per block: a power of two in [64, 65536] */
+  int64_t n_blocks;        /* blocks in each layer buffer, at most LLMK_MAX_DIM */
+  int64_t max_blocks;      /* table entries per slot: ceil(capacity / block_tokens) */
+  int32_t* table;          /* device int32 [n_slots][max_blocks] */
+  int32_t* table_h;        /* host int32 [n_slots][max_blocks]: the block of each entry, -1 for none */
+  int32_t* refcount_h;     /* host int32 [n_blocks] */
+  int64_t n_free;          /* blocks with refcount 0 */
+} llmk_kv_pages;
+
 /* Slot-indexed device K/V pool ([xpu] "3. The K/V cache and the block store": one K and one V
- * buffer per layer, slot s at element s * plane). Layer l's K buffer holds n_slots * capacity *
- * n_kv * head_dim elements; position p of slot s, K/V head g, element i sits at
+ * buffer per layer, slot s at element s * plane). Without pages (pages == NULL), layer l's K buffer holds
+ * n_slots * capacity * n_kv * head_dim elements; position p of slot s, K/V head g, element i sits at
  *   s * plane + p * n_kv * head_dim + g * head_dim + i,   plane = capacity * n_kv * head_dim.
+ * With pages, positions reach their blocks through the block table (llmk_kv_pages above).
  * slot_len_h records how many positions each slot holds; decode steps check it (566) and advance it.
  * len_k_h / len_v_h, when given, record the filled elements of every (layer, slot) K and V buffer, the
  * flat cache lengths llmk_kv_append checks and advances ([llmk] "KV-cache growth and greedy argmax":
@@ -334,13 +366,17 @@ typedef struct {
   int64_t* slot_len_h;     /* host array [n_slots] */
   int64_t* len_k_h;        /* host array [n_layer][n_slots] or NULL */
   int64_t* len_v_h;        /* host array [n_layer][n_slots] or NULL */
+  llmk_kv_pages* pages;    /* NULL: contiguous slots */
 } llmk_kv_pool;
 
 /* Validate a pool descriptor and mark every slot empty: slot_len_h, and len_k_h / len_v_h when given, are
  * set to 0 ([llmk] "The hot loop doesn't call kv_cache_append_flat": the cache is reserved once at its full
- * capacity, then filled in place). Host only; the device buffers are not touched.
- * Codes: 578 (null pool, k, v, slot_len_h or a layer buffer, unknown dtype, buffers not 16-byte aligned),
- * 561 (n_layer, n_slots, capacity, n_kv or head_dim < 1), 564 (> LLMK_MAX_DIM). */
+ * capacity, then filled in place). With pages, every table_h entry becomes -1, every refcount 0 and n_free
+ * n_blocks. Host only; the device buffers (and the device table) are not touched.
+ * Codes: 578 (null pool, k, v, slot_len_h or a layer buffer, unknown dtype, buffers not 16-byte aligned;
+ * pages with a null table, table_h or refcount_h, block_tokens not a power of two in [64, 65536],
+ * max_blocks != ceil(capacity / block_tokens)), 561 (n_layer, n_slots, capacity, n_kv, head_dim or n_blocks
+ * < 1), 564 (> LLMK_MAX_DIM, or n_slots * max_blocks > LLMK_MAX_DIM). The pages are checked after the rest. */
 int32_t llmk_kv_pool_init(llmk_kv_pool* pool);
 
 /* llmk_kv_append_flat on buffer `which` (0: K, 1: V) of `layer` for sequence `slot`: the slot's region is a
@@ -349,10 +385,14 @@ int32_t llmk_kv_pool_init(llmk_kv_pool* pool);
  * appends n_kv * head_dim, one position). On success the record becomes cache_len + n_new, *new_len_h gets
  * it and *elem_offset_h gets the element offset of the first written element in the layer buffer,
  * slot * plane + cache_len ([xpu] "3. The K/V cache and the block store": slot s at s * plane).
+ * With pages the positions the new elements fall in are reserved first (llmk_kv_reserve's rules), element e
+ * of the slot's flat cache goes to position e / (n_kv * head_dim) through the table, and *elem_offset_h is
+ * the offset of the first written element.
  *   new_vals: device fp32 [len_new]; new_len_h, elem_offset_h: host int64 (each may be NULL)
  * Codes: 578 (null pool / new_vals, len_k_h or len_v_h NULL, which not 0 or 1, layer not in [0, n_layer)),
  * 561 (cache_len < 0, n_new < 1), 564, 575 (slot), 566 (cache_len != recorded fill), 567 (len_new != n_new),
- * 571 (cache_len + n_new > capacity * n_kv * head_dim). */
+ * 571 (cache_len + n_new > capacity * n_kv * head_dim, or, with pages, too few free blocks), 578 (with
+ * pages: the stream is being captured and the reserve has device work). */
 int32_t llmk_kv_append(llmk_kv_pool* pool, int64_t layer, int64_t slot, int32_t which, int64_t cache_len,
                        const float* new_vals, int64_t len_new, int64_t n_new, int64_t* new_len_h,
                        int64_t* elem_offset_h, void* stream);
@@ -362,15 +402,51 @@ int32_t llmk_kv_append(llmk_kv_pool* pool, int64_t layer, int64_t slot, int32_t 
  *   q: device fp32 [n_head][head_dim]; out: device fp32 [n_head][head_dim]; ws as for llmk_gqa_attend_flat
  * Codes: 578 (null, layer not in [0, n_layer)), 561 (ctx_len or n_head < 1), 564, 575 (slot), 574 (as
  * llmk_gqa_attend_flat with the pool's n_kv and head_dim), 562 (len_q), 577 (len_out), 573 (ctx_len >
- * capacity), 566 (len_k_h / len_v_h given and either records fewer than ctx_len positions), 578 (workspace). */
+ * capacity, or, with pages, a position of [0, ctx_len) without a block), 566 (len_k_h / len_v_h given and
+ * either records fewer than ctx_len positions), 578 (workspace). With pages the kernel reads through the
+ * table. */
 int32_t llmk_gqa_attend(const float* q, int64_t len_q, const llmk_kv_pool* pool, int64_t layer, int64_t slot,
                         int64_t ctx_len, int64_t n_head, float* out, int64_t len_out, void* ws, int64_t len_ws,
                         void* stream);
 
-/* Element offset of (slot, pos, kv_head) in each layer buffer of the pool (closed form above).
- * Codes: 578, 575 (slot), 573 (pos not in [0, capacity)), 574 (kv_head not in [0, n_kv)). */
+/* Element offset of (slot, pos, kv_head) in each layer buffer of the pool (closed forms above; with pages,
+ * through the host mirror of the table).
+ * Codes: 578, 575 (slot), 573 (pos not in [0, capacity), or, with pages, its block not reserved),
+ * 574 (kv_head not in [0, n_kv)). */
 int32_t llmk_kv_slot_offset(const llmk_kv_pool* pool, int64_t slot, int64_t pos, int64_t kv_head,
                             int64_t* offset_h);
+
+/* Paged pools only: make positions [pos_begin, pos_end) of `slot` writable by the rules above (fresh blocks
+ * for entries of -1, copies for shared blocks) ([xpu] "2. The scheduler: continuous batching": the K/V
+ * reserve phase of a step). Every entry point that writes positions does this itself; a caller reserves
+ * ahead to keep later calls free of device work, e.g. before capturing a graph of decode steps.
+ * The block copies and table writes are enqueued on `stream`.
+ * Codes: 578 (null, pool without pages, or the stream is being captured and the reserve has device work),
+ * 561 (pos_begin < 0 or pos_end <= pos_begin), 564, 575 (slot), 571 (pos_end > capacity, or too few free
+ * blocks: nothing changed). */
+int32_t llmk_kv_reserve(llmk_kv_pool* pool, int64_t slot, int64_t pos_begin, int64_t pos_end, void* stream);
+
+/* Paged pools only: slot dst takes the first n_pos positions of slot src by sharing the blocks that hold
+ * them (each refcount + 1; [xpu] "3. The K/V cache and the block store": sequences forked from a common
+ * prefix share its blocks). dst must be empty (no positions, no blocks). Afterwards slot_len_h[dst] = n_pos
+ * and, when given, dst's len_k_h / len_v_h records are n_pos * n_kv * head_dim. The first write of either
+ * slot into a shared block copies it. dst's table row is written on `stream`.
+ * Codes: 578 (null, pool without pages, src == dst), 561 (n_pos < 1), 564, 575 (src or dst),
+ * 566 (n_pos > slot_len_h[src], or dst not empty). */
+int32_t llmk_kv_fork(llmk_kv_pool* pool, int64_t src, int64_t dst, int64_t n_pos, void* stream);
+
+/* Paged pools only: drop every block of `slot` (refcount - 1 each; a block reaching 0 is free), clear its
+ * table row (host mirror) and mark it empty (slot_len_h and, when given, its len_k_h / len_v_h records 0)
+ * ([xpu] "2. The scheduler: continuous batching": completions free blocks). Host only.
+ * Codes: 578 (null, pool without pages), 575 (slot). */
+int32_t llmk_kv_release(llmk_kv_pool* pool, int64_t slot);
+
+/* Paged pools only: the admission rule ([xpu] "2. The scheduler: continuous batching", "Admission": the free
+ * blocks must cover the request's whole uncached suffix plus one block of decode headroom per layer that is
+ * not windowed). A block here spans every layer (no layer is windowed), so the headroom is one block:
+ *   *admit_h = n_free >= ceil(n_uncached / block_tokens) + 1.
+ * Codes: 578 (null, pool without pages), 561 (n_uncached < 0), 564. */
+int32_t llmk_kv_admit(const llmk_kv_pool* pool, int64_t n_uncached, int32_t* admit_h);
 
 /* Bytes of workspace a decode call needs for `batch` rows (negative status if cfg is refused). batch 1
  * covers llmk_decode_step / llmk_decode_steps and, when the config allows the batched path, the batched
@@ -390,7 +466,8 @@ int64_t llmk_decode_workspace_bytes(const llmk_config* cfg, int64_t batch);
  * for the step to finish and returns 579 if a wait gave up (its outputs are then undefined). When `stream`
  * is being captured into a graph it cannot wait, and such a failure is not reported by this call.
  * Codes: 578, 561/564/574 (config), 576 (model tensor lengths), 575, 572, 573 (pos < 0 or >= max_seq),
- * 566, 571 (pos >= capacity), 568 (len_logits != vocab), 577 (len_hidden), 578 (workspace), 579. */
+ * 566, 571 (pos >= capacity), 568 (len_logits != vocab), 577 (len_hidden), 578 (workspace), then the paged
+ * reservation's 571 / 578, 579. */
 int32_t llmk_decode_step(const llmk_config* cfg, const llmk_model* model, llmk_kv_pool* pool, int64_t slot,
                          int64_t token, int64_t pos, float* logits, int64_t len_logits, int32_t* token_out,
                          float* hidden, int64_t len_hidden, void* ws, int64_t len_ws, void* stream);

@@ -154,7 +154,7 @@ class _FakePool:
     """A pool descriptor over fake (never dereferenced) device addresses, for host-only checks."""
 
     def __init__(self, n_layer=2, n_slots=3, capacity=8, n_kv=2, head_dim=4, dtype=0, arrays=True, buffers=True,
-                 records=True):
+                 records=True, paged=False, bt=64, n_blocks=4, max_blocks=None, parrays=True):
         self.fields = dict(n_layer=n_layer, n_slots=n_slots, capacity=capacity, n_kv=n_kv, head_dim=head_dim,
                            dtype=dtype, arrays=arrays, buffers=buffers, records=records)
         nl = max(0, min(n_layer, 4))
@@ -172,23 +172,42 @@ class _FakePool:
                                       head_dim, dtype, self.slot_len.ctypes.data_as(P),
                                       self.len_k.ctypes.data_as(P) if records else None,
                                       self.len_v.ctypes.data_as(P) if records else None)
+        if paged:
+            mb = -(-capacity // bt) if max_blocks is None else max_blocks
+            self.fields["pages"] = dict(block_tokens=bt, n_blocks=n_blocks, max_blocks=mb, arrays=parrays)
+            self.table_h = np.full((max(ns, 1), max(min(mb, 64), 1)), 9, dtype=np.int32)
+            self.refcount = np.full(max(min(n_blocks, 64), 1), 9, dtype=np.int32)
+            P32 = ctypes.POINTER(ctypes.c_int32)
+            self.pages = llmk.PagesStruct(bt, n_blocks, mb, FAKE if parrays else None,
+                                          self.table_h.ctypes.data_as(P32), self.refcount.ctypes.data_as(P32), 5)
+            self.struct.pages = ctypes.pointer(self.pages)
 
 
 POOL_CASES = [dict(), dict(arrays=False), dict(buffers=False), dict(dtype=2), dict(n_layer=0), dict(n_slots=-1),
               dict(capacity=0), dict(head_dim=(1 << 24) + 1), dict(n_kv=0, buffers=False), dict(records=False)]
+# paged pools: good ones, and one bad field each
+PAGED_CASES = [dict(paged=True), dict(paged=True, capacity=130, bt=64, n_blocks=7), dict(paged=True, bt=32),
+               dict(paged=True, bt=96), dict(paged=True, bt=131072), dict(paged=True, max_blocks=2),
+               dict(paged=True, n_blocks=0), dict(paged=True, n_blocks=(1 << 24) + 1), dict(paged=True, parrays=False),
+               dict(paged=True, n_slots=-1), dict(paged=True, capacity=1 << 24, n_slots=100),
+               dict(paged=True, buffers=False, bt=32)]
 
 
 @no_gpu
 def test_kv_pool_init():
-    for c in POOL_CASES:
+    for c in POOL_CASES + PAGED_CASES:
         fp = _FakePool(**c)
         exp = contract.kv_pool_init(fp.fields)
         got = llmk.lib.llmk_kv_pool_init(ctypes.byref(fp.struct))
         assert got == exp, c
         if got == contract.OK:   # every record of every slot marked empty
             assert not fp.slot_len.any() and (not c.get("records", True) or not (fp.len_k.any() or fp.len_v.any()))
+            if c.get("paged"):   # no block held, every block free
+                assert (fp.table_h == -1).all() and not fp.refcount.any() and fp.pages.n_free == fp.pages.n_blocks
         else:                    # refused: records untouched
             assert (fp.slot_len == 5).all()
+            if c.get("paged"):
+                assert (fp.table_h == 9).all() and fp.pages.n_free == 5
     assert llmk.lib.llmk_kv_pool_init(None) == contract.kv_pool_init(None) == 578
 
 
@@ -669,3 +688,109 @@ def test_decode_steps_sampled_refusals():
     # the sampler-workspace refusal is checked on a vocabulary that needs one
     assert llmk.sample_workspace_bytes(1, V, 1.0, 0) == 0
     assert llmk.sample_workspace_bytes(1, 128256, 1.0, 50) > 0
+
+
+@no_gpu
+def test_paged_entry_points_pool_refusals():
+    # every pool refusal of the paged-only entry points, and 578 for a pool without pages
+    L = llmk.lib
+    for c in POOL_CASES + PAGED_CASES:
+        fp = _FakePool(**c)
+        L.llmk_kv_pool_init(ctypes.byref(fp.struct))
+        f, ps = fp.fields, ctypes.byref(fp.struct)
+        exp = contract.kv_release(f, 1)
+        if exp != contract.OK:
+            assert L.llmk_kv_release(ps, 1) == exp, c
+            assert L.llmk_kv_reserve(ps, 1, 0, 1, None) == contract.kv_reserve(f, 1, 0, 1) == exp, c
+            assert L.llmk_kv_fork(ps, 0, 1, 1, None) == contract.kv_fork(f, 0, 1, 1) == exp, c
+            adm = ctypes.c_int32(-7)
+            assert L.llmk_kv_admit(ps, 3, ctypes.byref(adm)) == contract.kv_admit(f, 3)[0] == exp, c
+            assert adm.value == -7
+    for fn in (lambda: L.llmk_kv_release(None, 0), lambda: L.llmk_kv_reserve(None, 0, 0, 1, None),
+               lambda: L.llmk_kv_fork(None, 0, 1, 1, None), lambda: L.llmk_kv_admit(None, 0, ctypes.byref(ctypes.c_int32()))):
+        assert fn() == contract.INVALID
+    fp = _FakePool(paged=True)
+    assert L.llmk_kv_admit(ctypes.byref(fp.struct), 0, None) == contract.kv_admit(fp.fields, 0, admit=False)[0] == 578
+
+
+def _paged_state():
+    """A full paged pool (4 blocks of 64, 3 slots of up to 130 positions) and the oracle block manager in the
+    same state: slot 0 holds blocks [0, 1] (100 positions), slot 1 [0, 2] (120, sharing block 0 with slot 0),
+    slot 2 [3] (10)."""
+    from oracle.paged import BlockManager
+    fp = _FakePool(paged=True, capacity=130, bt=64, n_blocks=4)
+    assert llmk.lib.llmk_kv_pool_init(ctypes.byref(fp.struct)) == contract.OK
+    bm = BlockManager(3, 130, 4, 64)
+    bm.table = [[0, 1, -1], [0, 2, -1], [3, -1, -1]]
+    bm.ref = [2, 1, 1, 1]
+    bm.length = [100, 120, 10]
+    fp.table_h[:] = np.array(bm.table, dtype=np.int32)
+    fp.refcount[:] = np.array(bm.ref, dtype=np.int32)
+    fp.pages.n_free = bm.n_free()
+    fp.slot_len[:] = bm.length
+    fp.len_k[:] = fp.len_v[:] = np.array(bm.length) * 8
+    return fp, bm
+
+
+def _same(fp, bm):
+    return (fp.table_h.tolist() == bm.table and fp.refcount.tolist() == bm.ref and fp.pages.n_free == bm.n_free()
+            and fp.slot_len.tolist() == bm.length)
+
+
+@no_gpu
+def test_paged_block_manager_host_paths_match_oracle():
+    """The library's host bookkeeping against the oracle's block manager wherever it needs no device work:
+    reservations inside private blocks, refusals when full (nothing changes), release, admission, offsets."""
+    L = llmk.lib
+    fp, bm = _paged_state()
+    ps = ctypes.byref(fp.struct)
+    f = fp.fields
+    # inside a private block: nothing to take (no device work), accepted
+    for slot, b, e in [(0, 100, 101), (1, 120, 128), (2, 10, 64)]:
+        st, copies = bm.reserve([(slot, b, e)])
+        assert st == contract.OK and copies == []
+        assert L.llmk_kv_reserve(ps, slot, b, e, None) == contract.kv_reserve(f, slot, b, e, 0, 0) == st
+        assert _same(fp, bm)
+    # a fresh block, a copy of shared block 0, both, past the capacity: refused, nothing changed
+    for slot, b, e, need in [(1, 120, 129, 1), (0, 60, 61, 1), (0, 60, 130, 2), (2, 0, 131, 0)]:
+        st, _ = bm.reserve([(slot, b, e)])
+        assert st == contract.CAPACITY
+        assert L.llmk_kv_reserve(ps, slot, b, e, None) == contract.kv_reserve(f, slot, b, e, need, 0) == st
+        assert _same(fp, bm)
+    # an append into a fresh block with none free: 571, records untouched
+    st, nl, off = contract.kv_append(f, 0, 1, 0, 120 * 8, 120 * 8, True, 8 * 9, 8 * 9, need=1, n_free=0)
+    assert st == contract.CAPACITY
+    assert L.llmk_kv_append(ps, 0, 1, 0, 120 * 8, FAKE, 72, 72, None, None, None) == st
+    assert _same(fp, bm) and fp.len_k[0, 1] == 960
+    # attention over positions without a block: 573
+    rec = 130 * 8
+    exp = contract.gqa_attend(True, 16, f, 0, 2, 70, 4, True, 16, rec, rec, blocks_ok=False)
+    fp.len_k[:] = fp.len_v[:] = rec
+    assert L.llmk_gqa_attend(FAKE, 16, ps, 0, 2, 70, 4, FAKE, 16, FAKE, 1 << 30, None) == exp == contract.POSITION
+    # fork refusals
+    for src, dst, n, exp_args in [(0, 0, 5, {}), (0, 1, 5, dict(dst_len=120)), (0, 2, 5, dict(dst_len=10)),
+                                  (0, 1, 0, {}), (0, 3, 5, {}), (1, 2, 121, dict(dst_len=10))]:
+        exp = contract.kv_fork(f, src, dst, n, src_len=bm.length[src] if src < 3 else 0, **exp_args)
+        assert exp != contract.OK
+        assert L.llmk_kv_fork(ps, src, dst, n, None) == exp, (src, dst, n)
+        assert _same(fp, bm)
+    # release: slot 0 drops blocks 0 (still held by slot 1) and 1 (freed)
+    bm.release(0)
+    assert L.llmk_kv_release(ps, 0) == contract.kv_release(f, 0) == contract.OK
+    assert _same(fp, bm) and fp.pages.n_free == 1 and not fp.len_k[:, 0].any()
+    assert L.llmk_kv_release(ps, 3) == contract.kv_release(f, 3) == contract.SLOT
+    # admission with one free block: an empty suffix fits (its headroom block), one more position does not
+    for n in (0, 1, 64, 65):
+        adm = ctypes.c_int32(-1)
+        assert L.llmk_kv_admit(ps, n, ctypes.byref(adm)) == contract.OK
+        assert (adm.value, contract.kv_admit(f, n, n_free=1)[1]) == (int(bm.admit(n)), int(bm.admit(n)))
+    assert L.llmk_kv_admit(ps, -1, ctypes.byref(adm)) == contract.kv_admit(f, -1)[0] == contract.EMPTY
+    # offsets through the table
+    out = ctypes.c_int64(-1)
+    for slot, pos, kvh in [(1, 0, 0), (1, 70, 1), (2, 5, 1), (0, 5, 0), (1, 129, 0)]:
+        exp = contract.kv_slot_offset(3, 130, 2, 4, slot, pos, kvh, table=bm.table, block_tokens=64)
+        assert L.llmk_kv_slot_offset(ps, slot, pos, kvh, ctypes.byref(out)) == exp[0], (slot, pos)
+        if exp[0] == contract.OK:
+            assert out.value == exp[1]
+    assert contract.kv_slot_offset(3, 130, 2, 4, 1, 70, 1, table=bm.table, block_tokens=64) == \
+        (contract.OK, (2 * 64 + 6) * 8 + 4)
