@@ -146,11 +146,26 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   unsigned* counters = p.counters + (batched ? (int64_t)row * p.Hkv : 0);
   const float scale = 1.0f / sqrtf((float)HD);
 
+  // paged: the part's table entries (the first ATTN_TBL of them) are staged in LDS while the first tiles
+  // load, so a later tile finds its block without a global load in front of its own loads
+  constexpr int ATTN_TBL = 64;
+  __shared__ int32_t s_tbl[ATTN_TBL];
+  const int blk0 = trow ? (tb >> p.pg.shift) : 0;
+  if (trow && (int)threadIdx.x < min(((te - 1) >> p.pg.shift) - blk0 + 1, ATTN_TBL))
+    s_tbl[threadIdx.x] = trow[blk0 + threadIdx.x];
+  // cache row of a tile's first position minus that position (0 for a contiguous slot)
+  auto tile_base = [&](int T0, bool staged) -> int64_t {
+    if (!trow) return 0;
+    const int j = (T0 >> p.pg.shift) - blk0;
+    const int32_t b = staged && j < ATTN_TBL ? s_tbl[j] : trow[T0 >> p.pg.shift];
+    return (((int64_t)b << p.pg.shift) | (T0 & ((1 << p.pg.shift) - 1))) - T0;
+  };
+
   // cooperative tile load by one stream: vector idx -> (K or V, row, vector); rows past te are clamped
   // to te - 1; a paged tile starts at the cache row of its first position
   uint4 reg[NVL];
-#define LLMK_LOAD_TILE(T0)                                                                        \
-  const int64_t tile_row0 = trow ? kv_block_row(trow, p.pg.shift, (T0)) - (T0) : 0;               \
+#define LLMK_LOAD_TILE(T0, STAGED)                                                                \
+  const int64_t tile_row0 = tile_base((T0), (STAGED));                                             \
   _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
     const int idx = stid + k * ATTN_STHREADS;                                                     \
     const int which = idx / (CH * RV), rem = idx % (CH * RV);                                     \
@@ -175,7 +190,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
 
   const int n_tiles = (te - tb + CH - 1) / CH;
   // the first tile of each stream is requested before q is staged, so the two latencies overlap
-  if (st < n_tiles) { LLMK_LOAD_TILE(tb + st * CH) }
+  if (st < n_tiles) { LLMK_LOAD_TILE(tb + st * CH, false) }
 
   // q of the group into LDS. In the decode step q, k and v arrive unrotated (p.qkv_raw): every
   // workgroup rotates its q heads by the position, and the workgroup whose part holds that position
@@ -306,7 +321,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     }
     {
       const int tn = t0 + ATTN_STREAMS * CH;
-      if (tn < te) { LLMK_LOAD_TILE(tn) }   // next tile in flight while this one is computed
+      if (tn < te) { LLMK_LOAD_TILE(tn, true) }   // next tile in flight while this one is computed
     }
     const int n = act ? min(CH, te - t0) : 0;
 

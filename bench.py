@@ -44,6 +44,23 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def paged_pool(cfg, n_slots: int, capacity: int, lengths, bt: int):
+    """A paged pool whose slot i holds blocks for lengths[i] positions, reserved one block of every slot in
+    turn so that each slot's blocks lie scattered through the store (block j of slot i is block
+    j * n_slots + i while every slot still needs one)."""
+    import autoregressive_decode_step_amd as llmk
+    from autoregressive_decode_step_amd import loader
+    n_blocks = sum(-(-n // bt) for n in lengths)
+    pool = loader.new_pool(cfg, n_slots, capacity, block_tokens=bt, n_blocks=n_blocks)
+    for j in range(max(-(-n // bt) for n in lengths)):
+        for i, n in enumerate(lengths):
+            if j * bt < n:
+                st = llmk.kv_reserve(pool, i, j * bt, min(n, (j + 1) * bt))
+                if st != llmk.OK:
+                    raise RuntimeError(f"kv_reserve: {st} {llmk.status_name(st)}")
+    return pool
+
+
 def q8_pack_bytes(rows: int, cols: int) -> int:
     """Bytes of an int8 weight pack: a code per weight and an fp32 scale per 128 inputs of a row."""
     return rows * cols + 4 * rows * (cols // 128)
@@ -326,6 +343,8 @@ def main() -> int:
     ap.add_argument("--sample", type=lambda v: tuple(float(x) for x in v.split(",")), default=None,
                     metavar="T,K,P", help="batch-1 workloads: sample every step (temperature, top-k, top-p) inside "
                                          "the captured loop instead of taking the greedy token")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK_TOKENS",
+                    help="batch1 / batched: hold the K/V in a paged pool of blocks of this many positions")
     ap.add_argument("--step-path", choices=("auto", "per-op", "persistent"), default="auto",
                     help="the decode step's form: the library's choice (default), one kernel per operation, or "
                          "the persistent one-kernel step")
@@ -383,7 +402,11 @@ def main() -> int:
         raise RuntimeError(f"decode_path: {path} {llmk.status_name(path)}")
     persistent = path == llmk.STEP_PERSISTENT
     model = loader.upload_model(cfg, W)
-    pool = loader.new_pool(cfg, 1, s.max_seq)
+    if args.paged:
+        # slot 0 runs; slot 1 only interleaves its blocks with slot 0's
+        pool = paged_pool(cfg, 2, s.max_seq, [s.max_seq, s.max_seq], args.paged)
+    else:
+        pool = loader.new_pool(cfg, 1, s.max_seq)
     loader.fill_prefix(pool, 0, prefix)
     dec = loader.Decoder(cfg, model, pool)
     torch.cuda.synchronize()
@@ -479,7 +502,9 @@ def main() -> int:
                                 "llama-3-8b-shaped greedy decode, batch 1, bf16 weights and K/V, context 4096"),
                    "vocab": s.vocab, "d": s.d, "n_layer": s.n_layer, "n_head": s.n_head, "n_kv": s.n_kv,
                    "head_dim": s.head_dim, "hidden": s.hidden, "batch": 1, "context_start": N_PRE,
-                   "weights": "q8" if q8 else "bf16", "kv": "bf16", "accumulation": "f32"},
+                   "weights": "q8" if q8 else "bf16", "kv": "bf16", "accumulation": "f32",
+                   "kv_pool": (f"paged, {args.paged}-position blocks interleaved with another slot's" if args.paged
+                               else "contiguous slot")},
         "step_hbm_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "step_bytes_mean": total_bytes / args.steps,
@@ -864,7 +889,10 @@ def run_batched(args) -> int:
     log(f"generated in {time.time() - t_start:.1f} s; uploading")
     cfg = loader.config_from(s)
     model = loader.upload_model(cfg, W)
-    pool = loader.new_pool(cfg, BATCH, s.max_seq)
+    if args.paged:
+        pool = paged_pool(cfg, BATCH, s.max_seq, [c + BATCH_STEPS for c in ctxs], args.paged)
+    else:
+        pool = loader.new_pool(cfg, BATCH, s.max_seq)
     src_dev = loader.upload_kv_source(src)
     for r in range(BATCH):
         loader.fill_prefix_window(pool, r, src_dev, synth.slot_window(r), ctxs[r])
@@ -930,7 +958,9 @@ def run_batched(args) -> int:
                                "512..8192 (seeded), bf16 weights and K/V, projections on bf16 matrix cores",
                    "batch": BATCH, "contexts_mean": float(sum(ctxs) / BATCH), "contexts_min": min(ctxs),
                    "contexts_max": max(ctxs), "weights": "bf16", "kv": "bf16", "accumulation": "f32",
-                   "activations_into_mfma": "bf16 hi + lo"},
+                   "activations_into_mfma": "bf16 hi + lo",
+                   "kv_pool": (f"paged, {args.paged}-position blocks, every slot's blocks interleaved with the "
+                               f"others'" if args.paged else "contiguous slots")},
         "step_hbm_gbps": gbps,
         "step_frac_of_peak": gbps / PEAK_HBM_GBPS,
         "step_bytes_mean": total_bytes / steps,
