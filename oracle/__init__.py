@@ -21,9 +21,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, F64 = 0, 1, 2
+F32, BF16, F64, Q8 = 0, 1, 2, 3
 HALF_SPLIT, INTERLEAVED = 0, 1
-_DT = {"f32": F32, "bf16": BF16, "f64": F64}
+_DT = {"f32": F32, "bf16": BF16, "f64": F64, "q8": Q8}
 
 
 def build() -> str:
@@ -87,6 +87,7 @@ def lib():
             "orc_softmax_rows": ([p, i64, i64, p], None),
             "orc_silu_mul_inplace": ([p, p, i64], None),
             "orc_float_to_bf16": ([ctypes.c_float], ctypes.c_uint16),
+            "orc_q8_row": ([p, i64, p, ctypes.POINTER(ctypes.c_float)], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -317,20 +318,69 @@ class Model:
         return logits, hidden
 
 
+def q8_row(x):
+    """(codes int8 [n], scale float32) of one K/V row in the int8 cache format (oracle.c: orc_q8_row)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    q = np.zeros(x.shape[0], dtype=np.int8)
+    s = ctypes.c_float(0.0)
+    lib().orc_q8_row(_ptr(x), x.shape[0], q.ctypes.data, ctypes.byref(s))
+    return q, np.float32(s.value)
+
+
+def q8_rows_value(codes, scales) -> np.ndarray:
+    """What int8 rows stand for: codes [..., hd] times their row's scale [...], exact in fp64."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
 class Cache:
-    """Per-layer K and V, each [max_seq][n_kv][hd] in the shape's K/V dtype ([fwd] KVCache)."""
+    """Per-layer K and V, each [max_seq][n_kv][hd] in the shape's K/V dtype ([fwd] KVCache). For the int8
+    K/V dtype ("q8") each layer's K and V is one byte buffer, the codes [max_seq][n_kv][hd] followed by the
+    fp32 scales [max_seq][n_kv]; codes(l, which) and scales(l, which) view its two parts."""
 
     def __init__(self, shape, max_seq: int):
-        npdt = {"f32": np.float32, "bf16": np.uint16}[shape.kv_dtype]
-        self.k = [np.zeros((max_seq, shape.n_kv, shape.head_dim), dtype=npdt) for _ in range(shape.n_layer)]
-        self.v = [np.zeros((max_seq, shape.n_kv, shape.head_dim), dtype=npdt) for _ in range(shape.n_layer)]
+        self.q8 = shape.kv_dtype == "q8"
+        self._rows, self._hd, self._n_kv = max_seq * shape.n_kv, shape.head_dim, shape.n_kv
+        if self.q8:
+            nb = self._rows * shape.head_dim + 4 * self._rows
+            self.k = [np.zeros(nb, dtype=np.uint8) for _ in range(shape.n_layer)]
+            self.v = [np.zeros(nb, dtype=np.uint8) for _ in range(shape.n_layer)]
+        else:
+            npdt = {"f32": np.float32, "bf16": np.uint16}[shape.kv_dtype]
+            self.k = [np.zeros((max_seq, shape.n_kv, shape.head_dim), dtype=npdt) for _ in range(shape.n_layer)]
+            self.v = [np.zeros((max_seq, shape.n_kv, shape.head_dim), dtype=npdt) for _ in range(shape.n_layer)]
         self.length = 0
         self._kp = (ctypes.c_void_p * shape.n_layer)(*[a.ctypes.data for a in self.k])
         self._vp = (ctypes.c_void_p * shape.n_layer)(*[a.ctypes.data for a in self.v])
         self._c = _Cache(self._kp, self._vp, max_seq)
 
+    def codes(self, l: int, which: str = "k") -> np.ndarray:
+        """int8 cache: the codes of layer l's K or V, [max_seq][n_kv][hd] (a view)."""
+        b = (self.k if which == "k" else self.v)[l]
+        return b[:self._rows * self._hd].view(np.int8).reshape(-1, self._n_kv, self._hd)
+
+    def scales(self, l: int, which: str = "k") -> np.ndarray:
+        """int8 cache: the scales of layer l's K or V, [max_seq][n_kv] (a view)."""
+        b = (self.k if which == "k" else self.v)[l]
+        return b[self._rows * self._hd:].view(np.float32).reshape(-1, self._n_kv)
+
+    def values(self, l: int, which: str, n: int) -> np.ndarray:
+        """Positions 0..n-1 of layer l's K or V as the values the cache holds, fp64 [n][n_kv][hd]."""
+        if self.q8:
+            return q8_rows_value(self.codes(l, which)[:n], self.scales(l, which)[:n])
+        return widen((self.k if which == "k" else self.v)[l][:n])
+
     def fill_prefix(self, prefix: list):
-        """Load seeded K/V (synth.kv_prefix) into positions 0..n-1."""
+        """Load seeded K/V (synth.kv_prefix; for the int8 cache synth.kv_prefix_q8, per layer
+        ((K codes, K scales), (V codes, V scales))) into positions 0..n-1."""
+        if self.q8:
+            n = prefix[0][0][0].shape[0]
+            for l, ((kq, ks), (vq, vs)) in enumerate(prefix):
+                self.codes(l, "k")[:n] = kq
+                self.scales(l, "k")[:n] = ks
+                self.codes(l, "v")[:n] = vq
+                self.scales(l, "v")[:n] = vs
+            self.length = n
+            return
         n = prefix[0][0].shape[0]
         for l, (kk, vv) in enumerate(prefix):
             self.k[l][:n] = kk

@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import silu_mul_inplace, softmax_rows, widen
+from . import q8_rows_value, silu_mul_inplace, softmax_rows, widen
 
 HALF_SPLIT, INTERLEAVED = 0, 1
 
@@ -47,6 +47,39 @@ def round_kv(v: np.ndarray, kv_dtype: str) -> np.ndarray:
     if nan.any():
         b[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
     return b
+
+
+def quantize_kv(v: np.ndarray):
+    """The int8 cache format (oracle.c, orc_q8_row) over every row of v [..., hd] at once: values rounded to
+    fp32; per row s = max|x| / 127 and codes rint(x / s) clamped to [-127, 127], both divisions fp32 and ties
+    to even; a zero row has s = 0 and codes 0. Returns (codes int8 [..., hd], scales float32 [...])."""
+    x = np.asarray(v, dtype=np.float64).astype(np.float32)
+    s = np.divide(np.max(np.abs(x), axis=-1), np.float32(127), dtype=np.float32)
+    nz = s > 0
+    den = np.where(nz, s, np.float32(1))[..., None]
+    q = np.where(nz[..., None], np.rint(np.divide(x, den, dtype=np.float32)), np.float32(0))
+    return np.clip(q, -127, 127).astype(np.int8), s.astype(np.float32)
+
+
+def store_kv(cache, l: int, pos0: int, k: np.ndarray, v: np.ndarray) -> None:
+    """Rows pos0.. of layer l's K and V ([T][n_kv][hd], fp64) into an oracle Cache in its dtype."""
+    T = k.shape[0]
+    if getattr(cache, "q8", False):
+        for which, val in (("k", k), ("v", v)):
+            codes, scales = quantize_kv(val)
+            cache.codes(l, which)[pos0:pos0 + T] = codes
+            cache.scales(l, which)[pos0:pos0 + T] = scales
+        return
+    kv_dtype = "f32" if cache.k[l].dtype == np.float32 else "bf16"
+    cache.k[l][pos0:pos0 + T] = round_kv(k, kv_dtype)
+    cache.v[l][pos0:pos0 + T] = round_kv(v, kv_dtype)
+
+
+def cached_kv(cache, l: int, n: int):
+    """Positions 0..n-1 of layer l's K and V as the values the cache holds (fp64)."""
+    if getattr(cache, "q8", False):
+        return cache.values(l, "k", n), cache.values(l, "v", n)
+    return to_f64(cache.k[l][:n]), to_f64(cache.v[l][:n])
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
@@ -178,10 +211,8 @@ def forward_chunk(shape, weights: Weights, tokens, pos0: int, cache, want_hidden
         q = rope((h @ Wl["wq"]).reshape(T, H, hd), pos, s.rope_base, s.rope_layout)
         k = rope((h @ Wl["wk"]).reshape(T, Hkv, hd), pos, s.rope_base, s.rope_layout)
         v = (h @ Wl["wv"]).reshape(T, Hkv, hd)
-        cache.k[l][pos0:pos0 + T] = round_kv(k, s.kv_dtype)
-        cache.v[l][pos0:pos0 + T] = round_kv(v, s.kv_dtype)
-        kc = to_f64(cache.k[l][:pos0 + T])
-        vc = to_f64(cache.v[l][:pos0 + T])
+        store_kv(cache, l, pos0, k, v)
+        kc, vc = cached_kv(cache, l, pos0 + T)
         att = attend_causal(q, kc, vc, H, Hkv, pos).reshape(T, H * hd)
         _layer_tail(s, Wl, x, att)
         if want_hidden:
@@ -225,7 +256,8 @@ def forward_rows(shape, weights: Weights, tokens, positions, prefix, want_hidden
     positions 0..positions[b] - 1, given by prefix(l, b) as a list of consecutive pieces [(K, V)] (each
     head-major [n_kv][n][hd], stored dtype or fp64, together positions[b] long), plus the K/V it appends. Returns (logits
     fp32 [B][V], hidden fp32 [B][L][d] or None, new K/V per layer as a list of (K [B][n_kv][hd], V [B][n_kv][hd])
-    in the cache dtype). progress(l), when given, is called after each layer."""
+    in the cache dtype; for the int8 cache ((K codes, K scales), (V codes, V scales))). progress(l), when given, is
+    called after each layer."""
     s = shape
     B = len(tokens)
     pos = np.asarray(positions, dtype=np.int64)
@@ -237,9 +269,15 @@ def forward_rows(shape, weights: Weights, tokens, positions, prefix, want_hidden
         Wl = weights.layer(l)
         h = rmsnorm(x, Wl["n1"], s.eps)
         q = rope((h @ Wl["wq"]).reshape(B, H, hd), pos, s.rope_base, s.rope_layout)
-        k = round_kv(rope((h @ Wl["wk"]).reshape(B, Hkv, hd), pos, s.rope_base, s.rope_layout), s.kv_dtype)
-        v = round_kv((h @ Wl["wv"]).reshape(B, Hkv, hd), s.kv_dtype)
-        new_kv.append((k, v))
+        k = rope((h @ Wl["wk"]).reshape(B, Hkv, hd), pos, s.rope_base, s.rope_layout)
+        v = (h @ Wl["wv"]).reshape(B, Hkv, hd)
+        if s.kv_dtype == "q8":
+            kq, vq = quantize_kv(k), quantize_kv(v)
+            new_kv.append((kq, vq))
+            k, v = q8_rows_value(*kq), q8_rows_value(*vq)
+        else:
+            k, v = round_kv(k, s.kv_dtype), round_kv(v, s.kv_dtype)
+            new_kv.append((k, v))
         att = np.empty((B, H * hd))
         for b in range(B):
             pieces = list(prefix(l, b))

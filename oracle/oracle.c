@@ -25,7 +25,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2, ORC_Q8 = 3 };
 enum { ORC_HALF_SPLIT = 0, ORC_INTERLEAVED = 1 };
 
 /* ---- storage types ------------------------------------------------------------------ */
@@ -61,6 +61,48 @@ static void store(void* base, int dtype, int64_t i, double v) {
 }
 
 double orc_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
+
+/* int8 K/V rows. The pages name int8 K/V caches ("decode-ops", its opening paragraph: the int8-KV CPU
+ * attention; "Inside the engine", "1. CausalLM": int8 copies) without fixing a format, so this is the
+ * library's own, defined here: one row of n values (a position's K or V for one K/V head) is kept as n int8
+ * codes and one fp32 scale. Each value is first rounded to fp32 (as for every cache dtype); the scale is
+ * s = max|x| / 127 (one fp32 division); a code is q = rint(x / s) (one fp32 division, ties to even),
+ * clamped to [-127, 127]; a row of zeros has s = 0 and codes 0. The value the row stands for is q * s,
+ * exact in fp64, so |x - q s| <= s / 2 for every element (plus the fp32 rounding of x and of x / s). */
+void orc_q8_row(const double* x, int64_t n, int8_t* q, float* s_out) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    const float a = fabsf((float)x[i]);
+    if (a > amax) amax = a;
+  }
+  const float s = amax / 127.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float r = s > 0.0f ? rintf((float)x[i] / s) : 0.0f;
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    q[i] = (int8_t)r;
+  }
+  *s_out = s;
+}
+
+/* A layer's int8 cache buffer: codes [max_seq][n_kv][hd], then scales fp32 [max_seq][n_kv]. */
+static float q8_scale(const void* buf, int64_t codes_bytes, int64_t row) {
+  float s;
+  memcpy(&s, (const char*)buf + codes_bytes + 4 * row, 4);
+  return s;
+}
+static void q8_store_row(void* buf, int64_t codes_bytes, int64_t row, int64_t hd, const double* x) {
+  float s;
+  orc_q8_row(x, hd, (int8_t*)buf + row * hd, &s);
+  memcpy((char*)buf + codes_bytes + 4 * row, &s, 4);
+}
+/* Rows 0..n-1 of a layer's int8 cache as the values they stand for (q * s), [n][n_kv][hd] fp64. */
+static void q8_dequantize(const void* buf, int64_t codes_bytes, int64_t n_rows, int64_t hd, double* out) {
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const double s = (double)q8_scale(buf, codes_bytes, r);
+    for (int64_t i = 0; i < hd; ++i) out[r * hd + i] = (double)((const int8_t*)buf)[r * hd + i] * s;
+  }
+}
 
 /* Softmax of each row of s [rows][cols] over its first last[r] + 1 entries, in place: the maximum subtracted,
  * exp, divided by the sum; entries past last[r] become 0 (positions a query row does not see). Rows are
@@ -334,7 +376,8 @@ typedef struct {
 } orc_weights;
 
 /* Per-layer K and V caches, each [max_seq][n_kv][hd] in kv_dtype, position-major
- * ([fwd] "The code": KVCache keeps one entry per position and layer). */
+ * ([fwd] "The code": KVCache keeps one entry per position and layer); for ORC_Q8 each buffer holds the codes
+ * [max_seq][n_kv][hd] followed by the scales [max_seq][n_kv] (orc_q8_row). */
 typedef struct {
   void* const* k;
   void* const* v;
@@ -373,11 +416,27 @@ int orc_forward_token(const orc_shape* s, const orc_weights* w, const orc_cache*
     orc_gemv_t(w->wv[l], s->w_dtype, h, d, kvd, v);
     orc_rope(q, s->n_head, hd, pos, s->rope_base, s->rope_layout);
     orc_rope(k, s->n_kv, hd, pos, s->rope_base, s->rope_layout);
-    for (int64_t i = 0; i < kvd; ++i) {
-      store(c->k[l], s->kv_dtype, pos * kvd + i, k[i]);
-      store(c->v[l], s->kv_dtype, pos * kvd + i, v[i]);
+    if (s->kv_dtype == ORC_Q8) {
+      /* each head's row quantized into the cache, then attention over what the rows stand for */
+      const int64_t codes_bytes = c->max_seq * kvd;
+      for (int64_t g = 0; g < s->n_kv; ++g) {
+        q8_store_row(c->k[l], codes_bytes, pos * s->n_kv + g, hd, k + g * hd);
+        q8_store_row(c->v[l], codes_bytes, pos * s->n_kv + g, hd, v + g * hd);
+      }
+      double* kd = (double*)malloc(sizeof(double) * (size_t)((pos + 1) * kvd));
+      double* vd = (double*)malloc(sizeof(double) * (size_t)((pos + 1) * kvd));
+      q8_dequantize(c->k[l], codes_bytes, (pos + 1) * s->n_kv, hd, kd);
+      q8_dequantize(c->v[l], codes_bytes, (pos + 1) * s->n_kv, hd, vd);
+      orc_attend(q, kd, vd, ORC_F64, pos + 1, s->n_head, s->n_kv, hd, att);
+      free(kd);
+      free(vd);
+    } else {
+      for (int64_t i = 0; i < kvd; ++i) {
+        store(c->k[l], s->kv_dtype, pos * kvd + i, k[i]);
+        store(c->v[l], s->kv_dtype, pos * kvd + i, v[i]);
+      }
+      orc_attend(q, c->k[l], c->v[l], s->kv_dtype, pos + 1, s->n_head, s->n_kv, hd, att);
     }
-    orc_attend(q, c->k[l], c->v[l], s->kv_dtype, pos + 1, s->n_head, s->n_kv, hd, att);
     orc_gemv_t(w->wo[l], s->w_dtype, att, qd, d, y);
     for (int64_t i = 0; i < d; ++i) x[i] += y[i];
     orc_rmsnorm(x, w->n2[l], d, s->eps, h);

@@ -213,6 +213,22 @@ def kv_prefix(s: Shape, n_pos: int, seed: int = 2, slot: int = 0) -> list:
     return out
 
 
+def kv_prefix_q8(s: Shape, n_pos: int, seed: int = 2) -> list:
+    """Seeded int8 K/V for positions 0..n_pos-1 of every layer: per layer ((K codes, K scales), (V codes, V
+    scales)), codes int8 [n][n_kv][hd] uniform in [-127, 127], scales float32 [n][n_kv] = 0.02 + 0.01 |N(0, 1)|
+    (rows of about N(0, 1) magnitudes). Drawn directly as bytes, like the other inputs: nothing is quantized."""
+    out = []
+    for l in range(s.n_layer):
+        pair = []
+        for w in range(2):
+            st = 2 * l + w
+            q = ints((n_pos, s.n_kv, s.head_dim), -127, 127, seed, 4000 + st).astype(np.int8)
+            sc = (0.02 + 0.01 * np.abs(normal((n_pos, s.n_kv), seed, 5000 + st))).astype(np.float32)
+            pair.append((q, sc))
+        out.append(tuple(pair))
+    return out
+
+
 def prompt(n: int, vocab: int, seed: int = 1, stream: int = 0) -> np.ndarray:
     """Seeded uniform token ids in [0, vocab)."""
     return ints((n,), 0, vocab - 1, seed, 2_000_000 + stream)
