@@ -354,9 +354,13 @@ class KVPool:
     def __init__(self, n_layer, n_slots, capacity, n_kv, head_dim, dtype, device="cuda", tensors=None,
                  block_tokens=None, n_blocks=None):
         import torch
-        tdt = torch.bfloat16 if dtype == BF16 else torch.float32
         self.paged = block_tokens is not None
-        n = (n_blocks * block_tokens if self.paged else n_slots * capacity) * n_kv * head_dim
+        self.rows = n_blocks * block_tokens if self.paged else n_slots * capacity
+        n = self.rows * n_kv * head_dim
+        if dtype == Q8:   # int8 rows: the codes of every row, then an fp32 scale per (row, K/V head)
+            tdt, n = torch.uint8, n + 4 * self.rows * n_kv
+        else:
+            tdt = torch.bfloat16 if dtype == BF16 else torch.float32
         if tensors is None:
             self.k = [torch.zeros(n, dtype=tdt, device=device) for _ in range(n_layer)]
             self.v = [torch.zeros(n, dtype=tdt, device=device) for _ in range(n_layer)]
@@ -404,20 +408,40 @@ class KVPool:
             p += c
         return runs
 
+    def codes(self, layer: int, which: str = "k"):
+        """int8 pool: the codes of a layer's K or V buffer, [rows][n_kv][head_dim] int8 (a view)."""
+        import torch
+        b = (self.k if which == "k" else self.v)[layer]
+        return b[:self.rows * self.n_kv * self.head_dim].view(torch.int8).view(-1, self.n_kv, self.head_dim)
+
+    def scales(self, layer: int, which: str = "k"):
+        """int8 pool: the scales of a layer's K or V buffer, [rows][n_kv] float32 (a view)."""
+        import torch
+        b = (self.k if which == "k" else self.v)[layer]
+        return b[self.rows * self.n_kv * self.head_dim:].view(torch.float32).view(-1, self.n_kv)
+
+    def _parts(self, layer: int, which: str):
+        if self.dtype == Q8:
+            return [self.codes(layer, which), self.scales(layer, which)]
+        return [(self.k if which == "k" else self.v)[layer].view(-1, self.n_kv, self.head_dim)]
+
     def write_positions(self, layer: int, slot: int, which: str, start: int, values) -> None:
-        """Device copy of values ([n][n_kv][head_dim], pool dtype) into positions [start, start + n) of a slot
-        (paged: the positions must be reserved)."""
-        t = (self.k if which == "k" else self.v)[layer].view(-1, self.n_kv, self.head_dim)
+        """Device copy of values ([n][n_kv][head_dim], pool dtype; an int8 pool takes (codes [n][n_kv][hd],
+        scales [n][n_kv])) into positions [start, start + n) of a slot (paged: the positions must be reserved)."""
+        vals = list(values) if self.dtype == Q8 else [values]
         i = 0
-        for r, c in self._rows(slot, start, values.shape[0]):
-            t[r:r + c] = values[i:i + c]
+        for r, c in self._rows(slot, start, vals[0].shape[0]):
+            for t, v in zip(self._parts(layer, which), vals):
+                t[r:r + c] = v[i:i + c]
             i += c
 
     def read_positions(self, layer: int, slot: int, which: str, start: int, n: int):
-        """Device copy of positions [start, start + n) of a slot, [n][n_kv][head_dim]."""
+        """Device copy of positions [start, start + n) of a slot, [n][n_kv][head_dim] (an int8 pool: (codes,
+        scales))."""
         import torch
-        t = (self.k if which == "k" else self.v)[layer].view(-1, self.n_kv, self.head_dim)
-        return torch.cat([t[r:r + c] for r, c in self._rows(slot, start, n)]) if n > 0 else t[:0].clone()
+        out = [torch.cat([t[r:r + c] for r, c in self._rows(slot, start, n)]) if n > 0 else t[:0].clone()
+               for t in self._parts(layer, which)]
+        return tuple(out) if self.dtype == Q8 else out[0]
 
     def set_len(self, slot: int, n_pos: int) -> None:
         """Record that `slot` holds n_pos positions (its K/V written by the caller, e.g. a seeded prefix)."""
@@ -427,8 +451,8 @@ class KVPool:
 
     def slot_view(self, layer: int, slot: int, which: str = "k"):
         """[capacity][n_kv][head_dim] view of one slot of one layer's K or V buffer (contiguous pools)."""
-        if self.paged:
-            raise ValueError("a paged slot is not one view: use read_positions / write_positions")
+        if self.paged or self.dtype == Q8:
+            raise ValueError("a paged or int8 slot is not one view: use read_positions / write_positions")
         t = (self.k if which == "k" else self.v)[layer]
         plane = self.capacity * self.n_kv * self.head_dim
         return t[slot * plane:(slot + 1) * plane].view(self.capacity, self.n_kv, self.head_dim)

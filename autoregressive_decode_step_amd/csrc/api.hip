@@ -67,7 +67,8 @@ int32_t dims_check(std::initializer_list<int64_t> dims) {
 }
 
 inline bool is_dtype(int32_t t) { return t == LLMK_F32 || t == LLMK_BF16; }
-inline int64_t dtype_size(int32_t t) { return t == LLMK_BF16 ? 2 : 4; }
+inline bool is_kv_dtype(int32_t t) { return is_dtype(t) || t == LLMK_Q8; }
+inline int64_t dtype_size(int32_t t) { return t == LLMK_Q8 ? 1 : t == LLMK_BF16 ? 2 : 4; }
 inline bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 inline bool rope_head_dim_ok(int64_t hd) { return hd >= 2 && hd <= 256 && hd % 2 == 0; }
 inline bool attn_head_dim_ok(int64_t hd) { return hd >= 2 && hd <= 256 && pow2(hd); }
@@ -128,7 +129,7 @@ int64_t gemv_t_ws_any(int64_t m, int64_t n, int32_t dt) {
 
 int32_t config_check(const llmk_config* c) {
   if (!c) return LLMK_INVALID_ARGUMENT;
-  if ((!is_dtype(c->w_dtype) && c->w_dtype != LLMK_Q8) || !is_dtype(c->kv_dtype)) return LLMK_INVALID_ARGUMENT;
+  if ((!is_dtype(c->w_dtype) && c->w_dtype != LLMK_Q8) || !is_kv_dtype(c->kv_dtype)) return LLMK_INVALID_ARGUMENT;
   if (c->rope_layout != LLMK_ROPE_HALF_SPLIT && c->rope_layout != LLMK_ROPE_INTERLEAVED) return LLMK_INVALID_ARGUMENT;
   if (c->w_layout != LLMK_W_IN_OUT && c->w_layout != LLMK_W_OUT_IN) return LLMK_INVALID_ARGUMENT;
   if (c->step_path != LLMK_STEP_AUTO && c->step_path != LLMK_STEP_PER_OP && c->step_path != LLMK_STEP_PERSISTENT)
@@ -140,6 +141,8 @@ int32_t config_check(const llmk_config* c) {
   if (st != LLMK_OK) return st;
   if (c->n_head % c->n_kv != 0 || c->n_head / c->n_kv > 8 || !attn_head_dim_ok(c->head_dim))
     return LLMK_HEAD_SHAPE_INVALID;
+  if (c->kv_dtype == LLMK_Q8 && c->head_dim % 16 != 0) return LLMK_HEAD_SHAPE_INVALID;   // whole 16-code loads
+  if (c->kv_dtype == LLMK_Q8 && c->step_path == LLMK_STEP_PERSISTENT) return LLMK_INVALID_ARGUMENT;
   if (c->w_dtype == LLMK_Q8) {
     // int8 packs: the inputs of every projection and of the head in whole groups, a row segment per lane
     const int64_t ks[3] = {c->d, c->n_head * c->head_dim, c->hidden};
@@ -255,6 +258,7 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   D.attn.Hkv = (int32_t)c->n_kv;
   D.attn.hd = (int32_t)c->head_dim;
   D.attn.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
+  D.attn.kv_q8 = c->kv_dtype == LLMK_Q8;
   attn_plan(D.attn, c->max_seq);
 
   int64_t part = 0;
@@ -447,6 +451,12 @@ hipError_t launch_kernel(const llmk_config* c, const llmk_model* m, const llmk_k
     a.v = static_cast<const char*>(pool->v[l]) + kv_off * kvsz;
     a.k_w = static_cast<char*>(pool->k[l]) + kv_off * kvsz;
     a.v_w = static_cast<char*>(pool->v[l]) + kv_off * kvsz;
+    if (a.kv_q8) {   // the slot's scales (kv_off / head_dim rows of scales in)
+      a.k_scale_w = pool_scales(pool, pool->k[l]) + kv_off / c->head_dim;
+      a.v_scale_w = pool_scales(pool, pool->v[l]) + kv_off / c->head_dim;
+      a.k_scale = a.k_scale_w;
+      a.v_scale = a.v_scale_w;
+    }
     a.pg = pages_view(pool);
     a.pg.table = pages_slot_row(pool, slot);
     a.rope_table = static_cast<const float*>(m->rope_table.ptr);
@@ -599,7 +609,7 @@ bool step_shape_ok(const llmk_config* c, int nwg) {
 
 // Workgroups of the persistent step for this call (0: run one kernel per operation). -1: refused.
 int step_workgroups(const llmk_config* c) {
-  if (c->step_path == LLMK_STEP_PER_OP) return 0;
+  if (c->step_path == LLMK_STEP_PER_OP || c->kv_dtype == LLMK_Q8) return 0;   // the int8 cache: per operation
   int nwg = step_grid(c->kv_dtype == LLMK_BF16, (int)c->head_dim);
   if (nwg > kStepMaxWG || !step_shape_ok(c, nwg)) nwg = 0;
   if (nwg == 0 && c->step_path == LLMK_STEP_PERSISTENT) return -1;
@@ -789,6 +799,7 @@ void plan_batch(const llmk_config* c, int64_t B, void* ws, BatchPlan& P, bool ro
   P.attn.Hkv = (int32_t)c->n_kv;
   P.attn.hd = (int32_t)c->head_dim;
   P.attn.kv_is_bf16 = c->kv_dtype == LLMK_BF16;
+  P.attn.kv_q8 = c->kv_dtype == LLMK_Q8;
   // every row of the batch brings its own (row, K/V head) pairs, so parts can be long: about 16 tiles each
   // (measured on the 64-row, 8,320-position pool, us per layer: 312 at the batch-1 split, 299 at 6 tiles, 261
   // at 10, 235 at 16, 261 at 24, 357 at 40)
@@ -890,6 +901,12 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       a.v_w = pool->v[l];
       a.slot_elems = pool->capacity * kvd;
       a.pg = pages_view(pool);
+      if (a.kv_q8) {
+        a.k_scale_w = pool_scales(pool, pool->k[l]);
+        a.v_scale_w = pool_scales(pool, pool->v[l]);
+        a.k_scale = a.k_scale_w;
+        a.v_scale = a.v_scale_w;
+      }
       a.rope_table = static_cast<const float*>(m->rope_table.ptr);
       a.rope_layout = c->rope_layout;
       a.state = nullptr;
@@ -902,8 +919,8 @@ hipError_t launch_batch_kernel(const llmk_config* c, const llmk_model* m, const 
       a.no_append = P.prefill ? 1 : 0;
       if (P.prefill) {
         hipError_t e = rope_append_rows_launch(P.qkv_buf, P.qkv_n, P.state, B, a.H, a.Hkv, a.hd, a.rope_table,
-                                               a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, a.pg,
-                                               s);
+                                               a.rope_layout, pool->k[l], pool->v[l], c->kv_dtype, a.slot_elems, a.pg,
+                                               a.k_scale_w, a.v_scale_w, s);
         if (e != hipSuccess) return e;
       }
       return attn_launch(a, s);
@@ -1025,7 +1042,7 @@ void plan_prefill(const llmk_config* c, int64_t M, void* ws, PrefillPlan& P) {
   P.am_cnt = cv.take<unsigned>(M);
   P.am_logit = cv.take<float>(M);
   P.hidden = cv.take<float>(M * c->n_layer * d);
-  if (fattn_supported(c->n_head, c->n_kv, c->head_dim, c->max_seq)) {
+  if (c->kv_dtype != LLMK_Q8 && fattn_supported(c->n_head, c->n_kv, c->head_dim, c->max_seq)) {
     P.fa_parts = (int32_t)fattn_parts(c->max_seq);
     P.fa_part = cv.take<float>(M * c->n_head * P.fa_parts * (c->head_dim + 2));
   }
@@ -1114,7 +1131,8 @@ hipError_t enqueue_prefill_chunk(const llmk_config* c, const llmk_model* m, cons
       a.out_hi = B.att_hi;
       a.out_lo = B.att_lo;
       e = rope_append_rows_launch(a.qkv, a.qkv_stride, B.state, a.rows, a.H, a.Hkv, (int32_t)c->head_dim, a.rope_table,
-                                  a.rope_layout, pool->k[l], pool->v[l], a.kv_is_bf16, a.slot_elems, a.pg, s);
+                                  a.rope_layout, pool->k[l], pool->v[l], c->kv_dtype, a.slot_elems, a.pg, nullptr, nullptr,
+                                  s);
       if (e == hipSuccess) e = fattn_launch(a, ctx_end, s);
     } else if (e == hipSuccess) {
       e = launch_batch_kernel(c, m, pool, B, l, BK_ATTN, nullptr, nullptr, nullptr, s);
@@ -1415,9 +1433,13 @@ int64_t llmk_gqa_attend_workspace_bytes(int64_t ctx_len, int64_t n_head, int64_t
 // the attention launch shared by llmk_gqa_attend_flat and llmk_gqa_attend (every check done)
 static int32_t gqa_attend_run(const float* q, const void* k_cache, const void* v_cache, int32_t kv_dtype, int64_t ctx_len,
                               int64_t n_head, int64_t n_kv, int64_t head_dim, float* out, void* ws, void* stream,
-                              const KvPaging& pg = KvPaging{}) {
+                              const KvPaging& pg = KvPaging{}, const float* k_scale = nullptr,
+                              const float* v_scale = nullptr) {
   AttnParams a{};
   a.pg = pg;
+  a.kv_q8 = kv_dtype == LLMK_Q8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -1456,9 +1478,10 @@ int32_t llmk_gqa_attend_flat(const float* q, int64_t len_q, const void* k_cache,
 
 // A pool descriptor's own fields (no config to compare with): 578 / 561 / 564, then the pages.
 int32_t llmk::pool_fields_check(const llmk_kv_pool* p) {
-  if (!p || !p->k || !p->v || !p->slot_len_h || !is_dtype(p->dtype)) return LLMK_INVALID_ARGUMENT;
+  if (!p || !p->k || !p->v || !p->slot_len_h || !is_kv_dtype(p->dtype)) return LLMK_INVALID_ARGUMENT;
   int32_t st = dims_check({p->n_layer, p->n_slots, p->capacity, p->n_kv, p->head_dim});
   if (st != LLMK_OK) return st;
+  if (p->dtype == LLMK_Q8 && p->head_dim % 16 != 0) return LLMK_HEAD_SHAPE_INVALID;
   for (int64_t l = 0; l < p->n_layer; ++l)
     if (!p->k[l] || !p->v[l] || !aligned16(p->k[l]) || !aligned16(p->v[l])) return LLMK_INVALID_ARGUMENT;
   return p->pages ? pages_check(p) : LLMK_OK;
@@ -1488,7 +1511,8 @@ int32_t llmk_kv_append(llmk_kv_pool* pool, int64_t layer, int64_t slot, int32_t 
   if (!new_vals) return LLMK_INVALID_ARGUMENT;
   int32_t st = pool_fields_check(pool);
   if (st != LLMK_OK) return st;
-  if (!pool->len_k_h || !pool->len_v_h || (which != 0 && which != 1)) return LLMK_INVALID_ARGUMENT;
+  if (!pool->len_k_h || !pool->len_v_h || (which != 0 && which != 1) || pool->dtype == LLMK_Q8)
+    return LLMK_INVALID_ARGUMENT;
   if (layer < 0 || layer >= pool->n_layer) return LLMK_INVALID_ARGUMENT;
   if (cache_len < 0 || n_new < 1) return LLMK_EMPTY_DIMENSION;
   if (cache_len > kMaxDim || n_new > kMaxDim) return LLMK_DIMENSION_TOO_LARGE;
@@ -1544,8 +1568,14 @@ int32_t llmk_gqa_attend(const float* q, int64_t len_q, const llmk_kv_pool* pool,
   if (base % 16 != 0) return LLMK_INVALID_ARGUMENT;   // the kernel's 16-byte loads need the slot aligned
   KvPaging pg = pages_view(pool);
   pg.table = pages_slot_row(pool, slot);
+  const float* ksc = nullptr;
+  const float* vsc = nullptr;
+  if (pool->dtype == LLMK_Q8) {   // the slot's scales (base / head_dim rows of scales in)
+    ksc = pool_scales(pool, pool->k[layer]) + base / hd;
+    vsc = pool_scales(pool, pool->v[layer]) + base / hd;
+  }
   return gqa_attend_run(q, static_cast<const char*>(pool->k[layer]) + base, static_cast<const char*>(pool->v[layer]) + base,
-                        pool->dtype, ctx_len, n_head, n_kv, hd, out, ws, stream, pg);
+                        pool->dtype, ctx_len, n_head, n_kv, hd, out, ws, stream, pg, ksc, vsc);
 }
 
 int64_t llmk_argmax_workspace_bytes(int64_t rows, int64_t n) {

@@ -12,13 +12,13 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(const AttnParams p) 
   attn_block<T, HD>(p, blockIdx.y, blockIdx.x, blockIdx.z, tiles);
 }
 
-static int tile_rows(int kv_is_bf16, int hd) {
+static int tile_rows(int kv_is_bf16, int hd) {   // an int8 cache's tiles are staged as bf16
   const int row_bytes = ((hd * (kv_is_bf16 ? 2 : 4)) + 15) / 16 * 16;
   return attn_tile_rows(row_bytes);
 }
 
 void attn_plan(AttnParams& p, int64_t max_ctx, int64_t min_tiles_per_part) {
-  p.chunk = tile_rows(p.kv_is_bf16, p.hd);
+  p.chunk = tile_rows(p.kv_is_bf16 || p.kv_q8, p.hd);
   const int64_t n_sub = (max_ctx + p.chunk - 1) / p.chunk;
   int64_t target = (n_sub + min_tiles_per_part - 1) / std::max<int64_t>(1, min_tiles_per_part);
   if (target < 1) target = 1;
@@ -51,8 +51,20 @@ static hipError_t attn_hd(const AttnParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+static hipError_t attn_hd_q8(const AttnParams& p, hipStream_t s) {
+  switch (p.hd) {   // int8 rows are whole 16-code loads
+    case 16: return attn_one<int8_t, 16>(p, s);
+    case 32: return attn_one<int8_t, 32>(p, s);
+    case 64: return attn_one<int8_t, 64>(p, s);
+    case 128: return attn_one<int8_t, 128>(p, s);
+    case 256: return attn_one<int8_t, 256>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t attn_launch(const AttnParams& p, hipStream_t s) {
   if (p.H / p.Hkv > 8 || p.H % p.Hkv != 0) return hipErrorInvalidValue;
+  if (p.kv_q8) return attn_hd_q8(p, s);
   return p.kv_is_bf16 ? attn_hd<bf16_t>(p, s) : attn_hd<float>(p, s);
 }
 

@@ -23,6 +23,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace llmk {
@@ -39,11 +41,23 @@ __host__ __device__ constexpr int attn_tile_rows(int row_bytes) {
   return (16384 / row_bytes) < 64 ? (16384 / row_bytes) : 64;
 }
 
+// The int8 cache (T = int8_t): rows of codes with one fp32 scale per (position, K/V head); its tiles are held
+// in LDS as bf16 (every code is exact in bf16), so TS is the element type of the staged tiles.
+template <typename T>
+using attn_staged_t = typename std::conditional<std::is_same<T, int8_t>::value, bf16_t, T>::type;
+
 // 16-byte vectors of the LDS tile buffer attn_block needs for cache element type T and head size HD
 template <typename T, int HD>
 __host__ __device__ constexpr int attn_tile_vecs() {
-  return ATTN_STREAMS * 2 * attn_tile_rows((HD * (int)sizeof(T) + 15) / 16 * 16) *
-         (((HD + 16 / (int)sizeof(T) - 1) / (16 / (int)sizeof(T))) + 1);
+  using TS = attn_staged_t<T>;
+  return ATTN_STREAMS * 2 * attn_tile_rows((HD * (int)sizeof(TS) + 15) / 16 * 16) *
+         (((HD + 16 / (int)sizeof(TS) - 1) / (16 / (int)sizeof(TS))) + 1);
+}
+
+// Two int8 codes (bytes sh / 8 and sh / 8 + 1 of w) as a pair of bf16, the first in the low half: exact.
+__device__ __forceinline__ uint32_t i8_pair_bf16(uint32_t w, int sh) {
+  const float a = (float)(int8_t)(w >> sh), b = (float)(int8_t)(w >> (sh + 8));
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
 }
 
 
@@ -82,12 +96,17 @@ __device__ __forceinline__ bool tag_wait_more(int32_t* err, uint64_t t0, unsigne
 template <typename T, int HD, bool TAG = false>
 __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, const int part, const int row,
                                            uint4* tiles) {
-  constexpr int EPV = 16 / (int)sizeof(T);               // elements per 16-byte vector
+  constexpr bool Q8 = std::is_same<T, int8_t>::value;   // int8 codes, a scale per (position, K/V head)
+  using TS = attn_staged_t<T>;                           // element type of the tiles in LDS
+  constexpr int EPV = 16 / (int)sizeof(TS);              // staged elements per 16-byte vector
   constexpr int RV = (HD + EPV - 1) / EPV;               // vectors per row (a partial vector when HD < EPV)
-  constexpr int ROWB = (HD * (int)sizeof(T) + 15) / 16 * 16;
+  constexpr int ROWB = (HD * (int)sizeof(TS) + 15) / 16 * 16;
   constexpr int CH = attn_tile_rows(ROWB);               // positions per tile
   constexpr int RS = RV + 1;                             // padded row stride in vectors
-  constexpr int NVT = 2 * CH * RV;                       // vectors in a K+V tile
+  constexpr int EPG = 16 / (int)sizeof(T);               // cache elements per 16-byte load
+  constexpr int RVG = (HD + EPG - 1) / EPG;              // loads per row
+  static_assert(!Q8 || (HD % 16 == 0 && RV == 2 * RVG), "int8 rows are whole 16-code loads");
+  constexpr int NVT = 2 * CH * RVG;                      // loads in a K+V tile
   constexpr int NVL = (NVT + ATTN_STHREADS - 1) / ATTN_STHREADS;   // per stream thread
   constexpr int LPV = RV;                                // V phase: lanes per row (one 16-B vector each)
   constexpr int RGV = 64 / LPV;                          // V phase: rows processed at once by a wave
@@ -96,7 +115,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   uint4 (&s_kv)[ATTN_STREAMS][2][CH][RS] = *reinterpret_cast<uint4 (*)[ATTN_STREAMS][2][CH][RS]>(tiles);
   // Scores on the matrix cores for bf16 K/V with HD a multiple of 32 and 64-position tiles: q is kept as
   // bf16 hi + lo parts (about 16 significant bits) and each score is taken twice (q hi . K + q lo . K) into fp32
-  constexpr bool MF = sizeof(T) == 2 && HD % 32 == 0 && CH == 16 * ATTN_SWAVES;
+  constexpr bool MF = sizeof(TS) == 2 && HD % 32 == 0 && CH == 16 * ATTN_SWAVES;
   __shared__ float s_q[MF ? 1 : 8][HDP];
   __shared__ __align__(16) bf16_t s_qh[MF ? 8 : 1][MF ? HD : 8];
   __shared__ __align__(16) bf16_t s_ql[MF ? 8 : 1][MF ? HD : 8];
@@ -112,7 +131,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   };
   __shared__ float s_raw[TAG ? (8 + 2) * HDP : 1];     // TAG: this group's q heads, k and v as waited for
   __shared__ float s_p[ATTN_STREAMS][8][CH];
-  __shared__ T s_new[2][HDP];                            // the appended k and v row (decode), cache dtype
+  __shared__ TS s_new[2][HDP];                           // the appended k and v row (decode), as staged
+  __shared__ float s_newf[Q8 ? 2 : 1][Q8 ? HDP : 1];    // int8 cache: the new rows before quantization
+  __shared__ float s_news[2];                            // and their scales
+  __shared__ float s_sc[Q8 ? ATTN_STREAMS : 1][2][Q8 ? CH : 1];   // int8 cache: the tile rows' scales
   // stream 1's softmax state for the combine, in the tile buffer once the tiles are consumed (keeping it
   // out of the static LDS lets two workgroups share a CU)
   static_assert(16 + 8 * HDP <= 4 * attn_tile_vecs<T, HD>(), "combine state fits the tile buffer");
@@ -142,6 +164,10 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   const int64_t rbase = batched && !trow ? (int64_t)p.bstate->slot[row] * p.slot_elems : 0;
   const T* Kb = static_cast<const T*>(p.k) + rbase + (int64_t)kvh * HD;
   const T* Vb = static_cast<const T*>(p.v) + rbase + (int64_t)kvh * HD;
+  // int8 cache: scale of cache row r (of this slot's region, or of the store when paged) at [r * Hkv]
+  const int64_t sbase = (rbase / rstride) * p.Hkv + kvh;
+  const float* Ks = Q8 ? p.k_scale + sbase : nullptr;
+  const float* Vs = Q8 ? p.v_scale + sbase : nullptr;
   const float* qkv_raw = p.qkv_raw ? p.qkv_raw + (batched ? (int64_t)row * p.qkv_stride : 0) : nullptr;
   unsigned* counters = p.counters + (batched ? (int64_t)row * p.Hkv : 0);
   const float scale = 1.0f / sqrtf((float)HD);
@@ -164,29 +190,43 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
   // cooperative tile load by one stream: vector idx -> (K or V, row, vector); rows past te are clamped
   // to te - 1; a paged tile starts at the cache row of its first position
   uint4 reg[NVL];
+  float sreg = 0.0f;                                     // int8 cache: one row's scale per thread < 2 CH
 #define LLMK_LOAD_TILE(T0, STAGED)                                                                \
   const int64_t tile_row0 = tile_base((T0), (STAGED));                                             \
   _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
     const int idx = stid + k * ATTN_STHREADS;                                                     \
-    const int which = idx / (CH * RV), rem = idx % (CH * RV);                                     \
-    const int t = min((T0) + rem / RV, te - 1);                                                    \
-    const T* src = (which == 0 ? Kb : Vb) + (tile_row0 + t) * rstride + (rem % RV) * EPV;          \
-    if (HD >= EPV) {                                                                              \
+    const int which = idx / (CH * RVG), rem = idx % (CH * RVG);                                   \
+    const int t = min((T0) + rem / RVG, te - 1);                                                   \
+    const T* src = (which == 0 ? Kb : Vb) + (tile_row0 + t) * rstride + (rem % RVG) * EPG;         \
+    if (HD >= EPG) {                                                                              \
       reg[k] = idx < NVT ? gload<uint4>(src) : make_uint4(0, 0, 0, 0);                              \
     } else {                                                                                      \
       reg[k] = make_uint4(idx < NVT ? gload<uint32_t>(src) : 0u,                                  \
                           (idx < NVT && HD * (int)sizeof(T) >= 8) ? gload<uint32_t>(src + 4 / sizeof(T)) : 0u, \
                           0u, 0u);                                                                \
     }                                                                                             \
+  }                                                                                               \
+  if (Q8 && stid < 2 * CH) {                                                                      \
+    const int t = min((T0) + stid % CH, te - 1);                                                   \
+    sreg = (stid < CH ? Ks : Vs)[(tile_row0 + t) * p.Hkv];                                         \
   }
 #define LLMK_STORE_TILE()                                                                         \
   _Pragma("unroll") for (int k = 0; k < NVL; ++k) {                                               \
     const int idx = stid + k * ATTN_STHREADS;                                                     \
     if (idx < NVT) {                                                                              \
-      const int which = idx / (CH * RV), rem = idx % (CH * RV);                                   \
-      s_kv[st][which][rem / RV][rem % RV] = reg[k];                                               \
+      const int which = idx / (CH * RVG), rem = idx % (CH * RVG);                                 \
+      if constexpr (Q8) {                                                                         \
+        const uint4 c = reg[k];                                                                   \
+        s_kv[st][which][rem / RVG][2 * (rem % RVG)] =                                             \
+            make_uint4(i8_pair_bf16(c.x, 0), i8_pair_bf16(c.x, 16), i8_pair_bf16(c.y, 0), i8_pair_bf16(c.y, 16)); \
+        s_kv[st][which][rem / RVG][2 * (rem % RVG) + 1] =                                         \
+            make_uint4(i8_pair_bf16(c.z, 0), i8_pair_bf16(c.z, 16), i8_pair_bf16(c.w, 0), i8_pair_bf16(c.w, 16)); \
+      } else {                                                                                    \
+        s_kv[st][which][rem / RV][rem % RV] = reg[k];                                             \
+      }                                                                                           \
     }                                                                                             \
-  }
+  }                                                                                               \
+  if (Q8 && stid < 2 * CH) s_sc[st][stid / CH][stid % CH] = sreg;
 
   const int n_tiles = (te - tb + CH - 1) / CH;
   // the first tile of each stream is requested before q is staged, so the two latencies overlap
@@ -264,25 +304,50 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       if (g < G) {
         put_q(g, ia, ra);
         put_q(g, ib, rb);
+      } else if constexpr (Q8) {
+        s_newf[0][ia] = ra;
+        s_newf[0][ib] = rb;
       } else {
         store_elem<T>(&s_new[0][0], ia, ra);
         store_elem<T>(&s_new[0][0], ib, rb);
       }
     }
     if (owner) {
-      if constexpr (TAG) {
-        for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, s_raw[(G + 1) * HD + e]);
-      } else {
-        const float* vsrc = qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD;
-        for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) store_elem<T>(&s_new[1][0], e, ld_dev(vsrc + e));
+      for (int e = threadIdx.x; e < HD; e += ATTN_THREADS) {
+        float val;
+        if constexpr (TAG) val = s_raw[(G + 1) * HD + e];
+        else val = ld_dev(qkv_raw + (int64_t)(p.H + p.Hkv) * HD + (int64_t)kvh * HD + e);
+        if constexpr (Q8) s_newf[1][e] = val;
+        else store_elem<T>(&s_new[1][0], e, val);
       }
     }
     __syncthreads();
     if (owner) {
-      const int64_t off = (trow ? kv_block_row(trow, p.pg.shift, pos) : (int64_t)pos) * p.Hkv * HD + (int64_t)kvh * HD;
-      for (int e = threadIdx.x; e < 2 * HD; e += ATTN_THREADS) {
-        const int w = e / HD, ee = e % HD;
-        (w == 0 ? static_cast<T*>(p.k_w) : static_cast<T*>(p.v_w))[rbase + off + ee] = s_new[w][ee];
+      const int64_t crow = trow ? kv_block_row(trow, p.pg.shift, pos) : (int64_t)pos;   // cache row of pos
+      const int64_t off = crow * p.Hkv * HD + (int64_t)kvh * HD;
+      if constexpr (Q8) {
+        // wave w < 2 quantizes the new k (w = 0) or v row: s = max|x| / 127, codes rint(x / s) clamped to 127
+        if (wv < 2) {
+          float amax = 0.0f;
+          for (int e = lane; e < HD; e += 64) amax = fmaxf(amax, fabsf(s_newf[wv][e]));
+          const float sc = wave_max_dpp(amax) / 127.0f;
+          int8_t* dst = static_cast<int8_t*>(wv == 0 ? p.k_w : p.v_w) + rbase + off;
+          for (int e = lane; e < HD; e += 64) {
+            const float r = sc > 0.0f ? fminf(fmaxf(rintf(s_newf[wv][e] / sc), -127.0f), 127.0f) : 0.0f;
+            dst[e] = (int8_t)r;
+            s_new[wv][e] = (bf16_t)(__float_as_uint(r) >> 16);
+          }
+          if (lane == 0) {
+            s_news[wv] = sc;
+            (wv == 0 ? p.k_scale_w : p.v_scale_w)[(rbase / rstride + crow) * p.Hkv + kvh] = sc;
+          }
+        }
+        __syncthreads();
+      } else {
+        for (int e = threadIdx.x; e < 2 * HD; e += ATTN_THREADS) {
+          const int w = e / HD, ee = e % HD;
+          (w == 0 ? static_cast<T*>(p.k_w) : static_cast<T*>(p.v_w))[rbase + off + ee] = s_new[w][ee];
+        }
       }
     }
   } else {
@@ -314,8 +379,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       if (act && pos >= t0 && pos < t0 + CH) {
         for (int e = stid; e < 2 * HD; e += ATTN_STHREADS) {
           const int w = e / HD, ee = e % HD;
-          reinterpret_cast<T*>(&s_kv[st][w][pos - t0][0])[ee] = s_new[w][ee];
+          reinterpret_cast<TS*>(&s_kv[st][w][pos - t0][0])[ee] = s_new[w][ee];
         }
+        if (Q8 && stid < 2) s_sc[st][stid][pos - t0] = s_news[stid];
       }
       __syncthreads();
     }
@@ -350,7 +416,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int g = 4 * kg + i;
-          if (g < G) s_p[st][g][prow] = prow < n ? acc[i] * scale : -INFINITY;
+          if (g < G) s_p[st][g][prow] = prow < n ? acc[i] * (Q8 ? scale * s_sc[st][0][prow] : scale) : -INFINITY;
         }
       }
       __syncthreads();
@@ -372,7 +438,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
 #pragma unroll
           for (int v = 0; v < RV; ++v) {
             float kf[EPV];
-            if constexpr (sizeof(T) == 2) unpack<bf16_t, 8>(s_kv[st][0][lane][v], kf);
+            if constexpr (sizeof(TS) == 2) unpack<bf16_t, 8>(s_kv[st][0][lane][v], kf);
             else unpack<float, 4>(s_kv[st][0][lane][v], kf);
 #pragma unroll
             for (int e = 0; e < EPV; ++e)
@@ -381,7 +447,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
           float dot = 0.0f;
 #pragma unroll
           for (int e = 0; e < EPV; ++e) dot += part8[e];
-          if (lane < n) s = dot * scale;
+          if (lane < n) s = dot * (Q8 ? scale * s_sc[st][0][lane] : scale);
         }
         const float m_new = fmaxf(m_run[gi], wave_max_dpp(s));
         const float pr = (lane < n) ? expf(s - m_new) : 0.0f;
@@ -402,9 +468,9 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
         for (int k = 0; k < EPV; ++k) o[gi][k] *= alpha_g[gi];
 #pragma unroll 4
         for (int t = rg; t < n; t += RGV) {
-          const float pt = s_p[st][g][t];
+          const float pt = Q8 ? s_p[st][g][t] * s_sc[st][1][t] : s_p[st][g][t];
           float vf[EPV];
-          if constexpr (sizeof(T) == 2) unpack<bf16_t, 8>(s_kv[st][1][t][vl], vf);
+          if constexpr (sizeof(TS) == 2) unpack<bf16_t, 8>(s_kv[st][1][t][vl], vf);
           else unpack<float, 4>(s_kv[st][1][t][vl], vf);
 #pragma unroll
           for (int k = 0; k < EPV; ++k) o[gi][k] = fmaf(pt, vf[k], o[gi][k]);

@@ -4,6 +4,7 @@
 #include <limits.h>
 
 #include "kernels.h"
+#include "llmk.h"
 
 namespace llmk {
 
@@ -142,17 +143,59 @@ __global__ void rope_append_rows_kernel(const float* qkv, int64_t qkv_stride, co
   for (int e = threadIdx.x; e < hd; e += blockDim.x) store_elem<T>(v + off, e, vs[e]);
 }
 
+// The int8 cache: one wave per (row, K/V head) rotates k into LDS, then quantizes k and v (s = max|x| / 127,
+// codes rint(x / s) clamped to 127) and stores codes and scales.
+__global__ __launch_bounds__(64) void rope_append_rows_q8_kernel(const float* qkv, int64_t qkv_stride,
+                                                                 const BatchState* st, int32_t H, int32_t Hkv,
+                                                                 int32_t hd, const float* table, int32_t layout,
+                                                                 int8_t* k, int8_t* v, int64_t slot_elems,
+                                                                 KvPaging pg, float* k_scale, float* v_scale) {
+  __shared__ float s_x[2][256];
+  const int r = blockIdx.x, kvh = blockIdx.y, lane = threadIdx.x;
+  const int64_t pos = st->pos[r];
+  const float* src = qkv + (int64_t)r * qkv_stride;
+  const float* ks = src + (int64_t)H * hd + (int64_t)kvh * hd;
+  const float* vs = src + (int64_t)(H + Hkv) * hd + (int64_t)kvh * hd;
+  const int64_t crow = pg.table ? kv_block_row(pg.table + (int64_t)st->slot[r] * pg.stride, pg.shift, pos)
+                                : (int64_t)st->slot[r] * (slot_elems / ((int64_t)Hkv * hd)) + pos;
+  const int half = hd / 2;
+  for (int j = lane; j < half; j += 64) {
+    const int ia = layout == 0 ? j : 2 * j;
+    const int ib = layout == 0 ? j + half : 2 * j + 1;
+    const float cs = table[(pos * half + j) * 2 + 0], sn = table[(pos * half + j) * 2 + 1];
+    const float a = ks[ia], b = ks[ib];
+    s_x[0][ia] = a * cs - b * sn;
+    s_x[0][ib] = a * sn + b * cs;
+  }
+  for (int e = lane; e < hd; e += 64) s_x[1][e] = vs[e];
+  __syncthreads();
+  for (int w = 0; w < 2; ++w) {
+    float amax = 0.0f;
+    for (int e = lane; e < hd; e += 64) amax = fmaxf(amax, fabsf(s_x[w][e]));
+    const float sc = wave_max_dpp(amax) / 127.0f;
+    int8_t* dst = (w == 0 ? k : v) + crow * Hkv * hd + (int64_t)kvh * hd;
+    for (int e = lane; e < hd; e += 64)
+      dst[e] = (int8_t)(sc > 0.0f ? fminf(fmaxf(rintf(s_x[w][e] / sc), -127.0f), 127.0f) : 0.0f);
+    if (lane == 0) (w == 0 ? k_scale : v_scale)[crow * Hkv + kvh] = sc;
+  }
+}
+
 hipError_t rope_append_rows_launch(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t rows,
                                    int32_t H, int32_t Hkv, int32_t hd, const float* rope_table, int32_t rope_layout,
-                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, const KvPaging& pg,
-                                   hipStream_t s) {
+                                   void* k, void* v, int32_t kv_dtype, int64_t slot_elems, const KvPaging& pg,
+                                   float* k_scale, float* v_scale, hipStream_t s) {
   const dim3 grid((unsigned)rows, (unsigned)Hkv);
-  if (kv_is_bf16)
+  if (kv_dtype == LLMK_Q8) {
+    if (hd > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rope_append_rows_q8_kernel, grid, dim3(64), 0, s, qkv, qkv_stride, st, H, Hkv, hd, rope_table,
+                       rope_layout, static_cast<int8_t*>(k), static_cast<int8_t*>(v), slot_elems, pg, k_scale, v_scale);
+  } else if (kv_dtype == LLMK_BF16) {
     hipLaunchKernelGGL(rope_append_rows_kernel<bf16_t>, grid, dim3(64), 0, s, qkv, qkv_stride, st, H, Hkv, hd,
                        rope_table, rope_layout, static_cast<bf16_t*>(k), static_cast<bf16_t*>(v), slot_elems, pg);
-  else
+  } else {
     hipLaunchKernelGGL(rope_append_rows_kernel<float>, grid, dim3(64), 0, s, qkv, qkv_stride, st, H, Hkv, hd,
                        rope_table, rope_layout, static_cast<float*>(k), static_cast<float*>(v), slot_elems, pg);
+  }
   return hipGetLastError();
 }
 

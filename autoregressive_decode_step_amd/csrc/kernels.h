@@ -190,6 +190,11 @@ struct AttnParams {
   const void* k;         // [>= ctx][Hkv][hd] (the sequence's region)
   const void* v;
   int32_t kv_is_bf16;
+  int32_t kv_q8;               // int8 cache: k / v hold codes, k_scale / v_scale one scale per (row, K/V head)
+  const float* k_scale;        // [rows][Hkv], rows counted as for k (the slot's region, or the block store)
+  const float* v_scale;
+  float* k_scale_w;
+  float* v_scale_w;
   int32_t H, Hkv, hd;
   int32_t ctx;                 // used when state == nullptr
   const DecodeState* state;    // non-null: ctx = state->pos + 1
@@ -333,10 +338,12 @@ hipError_t argmax_launch(const float* logits, int64_t rows, int64_t n, int32_t* 
 hipError_t fill_u32_launch(unsigned* p, int64_t n, unsigned v, hipStream_t s);
 // Prefill: for every row r of the batch state, rotate its k by pos[r], round k and v to the cache dtype and
 // store them at pos[r] of slot[r] (k, v: one layer's pool buffers; qkv: [rows][qkv_stride] raw q|k|v).
+// kv_dtype LLMK_Q8: each (row, K/V head) of k and v is quantized to codes and a scale (k_scale, v_scale: the
+// buffers' scales, one per cache row and K/V head).
 hipError_t rope_append_rows_launch(const float* qkv, int64_t qkv_stride, const BatchState* st, int32_t rows,
                                    int32_t H, int32_t Hkv, int32_t hd, const float* rope_table, int32_t rope_layout,
-                                   void* k, void* v, int32_t kv_is_bf16, int64_t slot_elems, const KvPaging& pg,
-                                   hipStream_t s);
+                                   void* k, void* v, int32_t kv_dtype, int64_t slot_elems, const KvPaging& pg,
+                                   float* k_scale, float* v_scale, hipStream_t s);
 hipError_t set_state_launch(DecodeState* st, int32_t token, int32_t pos, hipStream_t s);
 
 }  // namespace llmk

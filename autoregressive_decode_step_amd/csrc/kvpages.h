@@ -41,4 +41,11 @@ const int32_t* pages_slot_row(const llmk_kv_pool* p, int64_t slot);
 // log2 of the block size.
 int pages_shift(const llmk_kv_pool* p);
 
+// Cache rows of each layer buffer: n_slots * capacity, or n_blocks * block_tokens for a paged pool.
+int64_t pool_rows(const llmk_kv_pool* p);
+
+// An int8 pool's layer buffer holds the codes of every cache row, then one fp32 scale per (row, K/V head):
+// the scales of buffer `buf`.
+float* pool_scales(const llmk_kv_pool* p, void* buf);
+
 }  // namespace llmk

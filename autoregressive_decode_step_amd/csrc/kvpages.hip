@@ -93,6 +93,14 @@ int32_t pages_check(const llmk_kv_pool* p) {
 
 int pages_shift(const llmk_kv_pool* p) { return p->pages ? shift_of(p->pages->block_tokens) : 0; }
 
+int64_t pool_rows(const llmk_kv_pool* p) {
+  return p->pages ? p->pages->n_blocks * p->pages->block_tokens : p->n_slots * p->capacity;
+}
+
+float* pool_scales(const llmk_kv_pool* p, void* buf) {
+  return reinterpret_cast<float*>(static_cast<char*>(buf) + pool_rows(p) * p->n_kv * p->head_dim);
+}
+
 KvPaging pages_view(const llmk_kv_pool* p) {
   KvPaging v{};
   if (p->pages) {
@@ -165,15 +173,22 @@ int32_t pages_reserve(llmk_kv_pool* p, const KvReserve* req, int64_t n, hipStrea
     }
   }
   g->n_free -= need;
-  // copy-on-write: the whole block, every layer, K and V
+  // copy-on-write: the whole block, every layer, K and V (an int8 pool's scales too)
   hipError_t e = hipSuccess;
-  const int64_t bytes = BT * p->n_kv * p->head_dim * (p->dtype == LLMK_BF16 ? 2 : 4);
+  const bool q8 = p->dtype == LLMK_Q8;
+  const int64_t bytes = BT * p->n_kv * p->head_dim * (q8 ? 1 : p->dtype == LLMK_BF16 ? 2 : 4);
+  const int64_t sbytes = BT * p->n_kv * 4;
   for (const auto& c : copies)
     for (int64_t l = 0; l < p->n_layer && e == hipSuccess; ++l)
       for (int w = 0; w < 2 && e == hipSuccess; ++w) {
         char* buf = static_cast<char*>(w == 0 ? p->k[l] : p->v[l]);
         e = hipMemcpyAsync(buf + (int64_t)c.second * bytes, buf + (int64_t)c.first * bytes, (size_t)bytes,
                            hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && q8) {
+          char* sc = reinterpret_cast<char*>(pool_scales(p, buf));
+          e = hipMemcpyAsync(sc + (int64_t)c.second * sbytes, sc + (int64_t)c.first * sbytes, (size_t)sbytes,
+                             hipMemcpyDeviceToDevice, s);
+        }
       }
   if (e == hipSuccess) e = flush_edits(g->table, edits, s);
   return e == hipSuccess ? LLMK_OK : LLMK_DEVICE_ERROR;

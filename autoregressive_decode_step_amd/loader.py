@@ -35,6 +35,8 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
         t = torch.from_numpy(a.reshape(-1))
     elif a.dtype == np.uint16:
         t = torch.from_numpy(a.reshape(-1).view(np.int16)).view(torch.bfloat16)
+    elif a.dtype == np.int8:
+        t = torch.from_numpy(a.reshape(-1))
     else:
         raise TypeError(f"weights must be float32 or bf16 bits (uint16), got {a.dtype}")
     return t.to(device)
@@ -93,11 +95,17 @@ def _reserve(pool: KVPool, slot: int, n: int) -> None:
 def fill_prefix(pool: KVPool, slot: int, prefix: list) -> None:
     """Copy host K/V for positions 0..n-1 (per layer (K, V), each [n][n_kv][hd] in the pool dtype) into a
     slot (a paged pool reserves its blocks first) and record its length."""
-    n = prefix[0][0].shape[0]
+    q8 = pool.dtype == Q8    # prefix per layer ((K codes, K scales), (V codes, V scales))
+    n = (prefix[0][0][0] if q8 else prefix[0][0]).shape[0]
     _reserve(pool, slot, n)
+    dv = pool.k[0].device
     for l, (kk, vv) in enumerate(prefix):
-        pool.write_positions(l, slot, "k", 0, to_device(kk, pool.k[l].device).view(n, pool.n_kv, pool.head_dim))
-        pool.write_positions(l, slot, "v", 0, to_device(vv, pool.v[l].device).view(n, pool.n_kv, pool.head_dim))
+        for which, x in (("k", kk), ("v", vv)):
+            if q8:
+                val = (to_device(x[0], dv).view(n, pool.n_kv, pool.head_dim), to_device(x[1], dv).view(n, pool.n_kv))
+            else:
+                val = to_device(x, dv).view(n, pool.n_kv, pool.head_dim)
+            pool.write_positions(l, slot, which, 0, val)
     pool.set_len(slot, n)
 
 
@@ -120,13 +128,13 @@ class Decoder:
 
 
 def upload_kv_source(source: list, device="cuda") -> list:
-    """Per layer (K, V) host arrays [n][Hkv][hd] (pool dtype) -> device tensors of the same shape."""
-    out = []
-    for kk, vv in source:
-        n = kk.shape[0]
-        out.append((to_device(kk, device).view(n, kk.shape[1], kk.shape[2]),
-                    to_device(vv, device).view(n, vv.shape[1], vv.shape[2])))
-    return out
+    """Per layer (K, V) host arrays [n][Hkv][hd] (pool dtype; int8: (codes [n][Hkv][hd], scales [n][Hkv])) ->
+    device tensors of the same shape."""
+    def up(x):
+        if isinstance(x, tuple):
+            return tuple(to_device(a, device).view(a.shape) for a in x)
+        return to_device(x, device).view(x.shape)
+    return [(up(kk), up(vv)) for kk, vv in source]
 
 
 def fill_prefix_window(pool: KVPool, slot: int, source_dev: list, start: int, n: int) -> None:
@@ -135,8 +143,9 @@ def fill_prefix_window(pool: KVPool, slot: int, source_dev: list, start: int, n:
     _reserve(pool, slot, n)
     for l, (kk, vv) in enumerate(source_dev):
         if n > 0:
-            pool.write_positions(l, slot, "k", 0, kk[start:start + n])
-            pool.write_positions(l, slot, "v", 0, vv[start:start + n])
+            for which, x in (("k", kk), ("v", vv)):
+                val = tuple(a[start:start + n] for a in x) if isinstance(x, tuple) else x[start:start + n]
+                pool.write_positions(l, slot, which, 0, val)
     pool.set_len(slot, n)
 
 

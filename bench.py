@@ -343,6 +343,8 @@ def main() -> int:
     ap.add_argument("--sample", type=lambda v: tuple(float(x) for x in v.split(",")), default=None,
                     metavar="T,K,P", help="batch-1 workloads: sample every step (temperature, top-k, top-p) inside "
                                          "the captured loop instead of taking the greedy token")
+    ap.add_argument("--kv", choices=("bf16", "q8"), default="bf16",
+                    help="batched: the K/V cache dtype (q8: int8 rows with an fp32 scale per position and head)")
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK_TOKENS",
                     help="batch1 / batched: hold the K/V in a paged pool of blocks of this many positions")
     ap.add_argument("--step-path", choices=("auto", "per-op", "persistent"), default="auto",
@@ -847,15 +849,23 @@ CTX_LO, CTX_HI = 512, 8192      # their context lengths, uniform
 BATCH_STEPS = 128               # steps the batched workload runs
 
 
+def kv_position_bytes(s) -> int:
+    """Bytes one position's K or V row takes in one layer: n_kv * head_dim elements of the cache dtype, and
+    for the int8 cache one code each plus an fp32 scale per K/V head."""
+    kvd = s.n_kv * s.head_dim
+    return kvd + 4 * s.n_kv if s.kv_dtype == "q8" else kvd * (2 if s.kv_dtype == "bf16" else 4)
+
+
 def batched_step_bytes(s, ctxs, i) -> int:
     """Algorithmic HBM bytes of batched step i (row r attends ctx_r + i + 1 positions): every weight once,
     each row's embedding row and attended K/V, the appended K/V, the gains."""
-    wsz, kvsz = 2, 2
+    wsz = 2
     d, qd, kvd, F, V, L = s.d, s.n_head * s.head_dim, s.n_kv * s.head_dim, s.hidden, s.vocab, s.n_layer
     weights = L * (d * qd + 2 * d * kvd + qd * d + 3 * d * F) * wsz + V * d * wsz
     emb = len(ctxs) * d * wsz
     gains = (2 * L + 1) * d * 4
-    kv = sum(L * (int(c) + i + 1) * kvd * 2 * kvsz for c in ctxs) + len(ctxs) * L * kvd * 2 * kvsz
+    kvp = kv_position_bytes(s)
+    kv = sum(L * (int(c) + i + 1) * 2 * kvp for c in ctxs) + len(ctxs) * L * 2 * kvp
     return weights + emb + gains + kv
 
 
@@ -863,8 +873,9 @@ def batched_attention_bytes(s, ctxs) -> int:
     """Algorithmic bytes of one batched attention launch at positions ctxs: each row's K and V of ctx + 1
     positions, its raw q|k|v and RoPE row read, its appended K/V and its output written (hi and lo)."""
     kvd, qd = s.n_kv * s.head_dim, s.n_head * s.head_dim
-    per_row_fixed = (qd + 2 * kvd) * 4 + s.head_dim * 4 + 2 * kvd * 2 + qd * 2 * 2
-    return sum((int(c) + 1) * kvd * 2 * 2 + per_row_fixed for c in ctxs)
+    kvp = kv_position_bytes(s)
+    per_row_fixed = (qd + 2 * kvd) * 4 + s.head_dim * 4 + 2 * kvp + qd * 2 * 2
+    return sum((int(c) + 1) * 2 * kvp + per_row_fixed for c in ctxs)
 
 
 def run_batched(args) -> int:
@@ -875,6 +886,8 @@ def run_batched(args) -> int:
     from autoregressive_decode_step_amd import loader
 
     s = synth.L8B.with_(name="llama-3-8b-shaped bf16, batched", max_seq=CTX_HI + BATCH_STEPS)
+    if args.kv == "q8":
+        s = s.with_(name="llama-3-8b-shaped bf16, int8 K/V, batched", kv_dtype="q8")
     steps = args.steps if args.steps != 256 else BATCH_STEPS
     if steps > BATCH_STEPS or args.warmup > BATCH_STEPS:
         print(f"the batched workload has room for {BATCH_STEPS} steps per run", file=sys.stderr)
@@ -883,7 +896,8 @@ def run_batched(args) -> int:
     log(f"generating {s.name} weights and the K/V source")
     W = synth.model(s, seed=0)
     ctxs = synth.ragged_contexts(BATCH, CTX_LO, CTX_HI, seed=3).tolist()
-    src = synth.kv_prefix(s, CTX_HI + synth.slot_window(BATCH - 1), seed=2)
+    src = (synth.kv_prefix_q8 if args.kv == "q8" else synth.kv_prefix)(s, CTX_HI + synth.slot_window(BATCH - 1),
+                                                                        seed=2)
     first = synth.prompt(BATCH, s.vocab, stream=13).tolist()
     slots = list(range(BATCH))
     log(f"generated in {time.time() - t_start:.1f} s; uploading")
@@ -942,7 +956,9 @@ def run_batched(args) -> int:
     tokens = toks.cpu().numpy().reshape(steps, BATCH)
 
     result = {
-        "metric": "decode tokens/s at batch 64 (8B-shaped, ragged contexts) + achieved HBM GB/s vs peak",
+        "metric": ("decode tokens/s at batch 64 (8B-shaped, ragged contexts, int8 K/V) + achieved HBM GB/s vs peak"
+                   if args.kv == "q8" else
+                   "decode tokens/s at batch 64 (8B-shaped, ragged contexts) + achieved HBM GB/s vs peak"),
         "value": BATCH * steps / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -955,9 +971,11 @@ def run_batched(args) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "llama-3-8b-shaped greedy decode, 64 sequences per step, contexts uniform in "
-                               "512..8192 (seeded), bf16 weights and K/V, projections on bf16 matrix cores",
+                               "512..8192 (seeded), bf16 weights, " + ("int8 K/V rows with an fp32 scale each"
+                                                                        if args.kv == "q8" else "bf16 K/V")
+                               + ", projections on bf16 matrix cores",
                    "batch": BATCH, "contexts_mean": float(sum(ctxs) / BATCH), "contexts_min": min(ctxs),
-                   "contexts_max": max(ctxs), "weights": "bf16", "kv": "bf16", "accumulation": "f32",
+                   "contexts_max": max(ctxs), "weights": "bf16", "kv": args.kv, "accumulation": "f32",
                    "activations_into_mfma": "bf16 hi + lo",
                    "kv_pool": (f"paged, {args.paged}-position blocks, every slot's blocks interleaved with the "
                                f"others'" if args.paged else "contiguous slots")},
@@ -982,7 +1000,9 @@ def run_batched(args) -> int:
         for r in rows:
             c = m.new_cache(ctxs[r] + n)
             st0 = synth.slot_window(r)
-            c.fill_prefix([(k[st0:st0 + ctxs[r]], v[st0:st0 + ctxs[r]]) for k, v in src])
+            def win(x):
+                return tuple(a[st0:st0 + ctxs[r]] for a in x) if isinstance(x, tuple) else x[st0:st0 + ctxs[r]]
+            c.fill_prefix([(win(k), win(v)) for k, v in src])
             t = first[r]
             for i in range(n):
                 lg, _ = m.forward_token(t, ctxs[r] + i, c)

@@ -77,7 +77,8 @@ enum {
 /* most sequences one batched decode step serves */
 #define LLMK_MAX_BATCH 64
 
-/* LLMK_Q8 is a weight format only (llmk_config.w_dtype, llmk_quantize_q8): see "int8 weight packs" below. */
+/* LLMK_Q8 is an int8 format: of the weights (llmk_config.w_dtype, llmk_quantize_q8; see "int8 weight packs"
+ * below) and of the K/V pool (llmk_config.kv_dtype, llmk_kv_pool.dtype; see the pool below). */
 typedef enum { LLMK_F32 = 0, LLMK_BF16 = 1, LLMK_Q8 = 2 } llmk_dtype;
 /* Half-split pairs (j, j + hd/2) are the GPT-NeoX/Qwen3 convention ([llmk] "Two
  * gaps, not three"); interleaved pairs (2j, 2j+1) are the layout of [fwd] "The
@@ -282,7 +283,8 @@ typedef struct {
   int32_t rope_layout; /* llmk_rope_layout */
   int32_t w_dtype;     /* llmk_dtype of every weight matrix and the embedding table; LLMK_Q8: the seven
                           projections and the output head are q8 packs and the embedding table is bf16 */
-  int32_t kv_dtype;    /* llmk_dtype of the K/V pool */
+  int32_t kv_dtype;    /* llmk_dtype of the K/V pool; LLMK_Q8: int8 rows (llmk_kv_pool), head_dim a multiple of
+                          16 (574), decode steps run one kernel per operation (LLMK_STEP_PERSISTENT: 578) */
   int32_t w_layout;    /* llmk_weight_layout of the seven per-layer projections */
   int32_t step_path;   /* llmk_step_path */
   int32_t test_flags;  /* 0 in normal use; LLMK_TEST_* bits exercise error paths in tests */
@@ -353,6 +355,15 @@ typedef struct {
  * n_slots * capacity * n_kv * head_dim elements; position p of slot s, K/V head g, element i sits at
  *   s * plane + p * n_kv * head_dim + g * head_dim + i,   plane = capacity * n_kv * head_dim.
  * With pages, positions reach their blocks through the block table (llmk_kv_pages above).
+ * int8 pool (dtype LLMK_Q8; the pages name int8 K/V caches without a format, [dops] opening paragraph,
+ * [xpu] "1. CausalLM", so the format is this library's): every (position, K/V head) row of head_dim values
+ * is stored as head_dim int8 codes and one fp32 scale, s = max|x| / 127, code = rint(x / s) (both fp32
+ * divisions, ties to even) clamped to [-127, 127] (a zero row: s = 0, codes 0); the row stands for code * s.
+ * Each layer buffer holds the codes of every cache row at the element offsets above (one byte each), then,
+ * from byte rows * n_kv * head_dim on, the scales fp32 [rows][n_kv] (rows = n_slots * capacity, or
+ * n_blocks * block_tokens with pages): the scale of (cache row r, K/V head g) at index r * n_kv + g. head_dim
+ * is a multiple of 16. The decode steps (single, batched), prefill and llmk_gqa_attend take int8 pools;
+ * llmk_kv_append (a flat append of elements) refuses them.
  * slot_len_h records how many positions each slot holds; decode steps check it (566) and advance it.
  * len_k_h / len_v_h, when given, record the filled elements of every (layer, slot) K and V buffer, the
  * flat cache lengths llmk_kv_append checks and advances ([llmk] "KV-cache growth and greedy argmax":
@@ -376,7 +387,8 @@ typedef struct {
  * Codes: 578 (null pool, k, v, slot_len_h or a layer buffer, unknown dtype, buffers not 16-byte aligned;
  * pages with a null table, table_h or refcount_h, block_tokens not a power of two in [64, 65536],
  * max_blocks != ceil(capacity / block_tokens)), 561 (n_layer, n_slots, capacity, n_kv, head_dim or n_blocks
- * < 1), 564 (> LLMK_MAX_DIM, or n_slots * max_blocks > LLMK_MAX_DIM). The pages are checked after the rest. */
+ * < 1), 564 (> LLMK_MAX_DIM, or n_slots * max_blocks > LLMK_MAX_DIM), 574 (dtype LLMK_Q8 and head_dim not a
+ * multiple of 16, checked after the dimensions). The pages are checked after the rest. */
 int32_t llmk_kv_pool_init(llmk_kv_pool* pool);
 
 /* llmk_kv_append_flat on buffer `which` (0: K, 1: V) of `layer` for sequence `slot`: the slot's region is a
@@ -389,7 +401,8 @@ int32_t llmk_kv_pool_init(llmk_kv_pool* pool);
  * of the slot's flat cache goes to position e / (n_kv * head_dim) through the table, and *elem_offset_h is
  * the offset of the first written element.
  *   new_vals: device fp32 [len_new]; new_len_h, elem_offset_h: host int64 (each may be NULL)
- * Codes: 578 (null pool / new_vals, len_k_h or len_v_h NULL, which not 0 or 1, layer not in [0, n_layer)),
+ * Codes: 578 (null pool / new_vals, len_k_h or len_v_h NULL, which not 0 or 1, an int8 pool, layer not in
+ * [0, n_layer)),
  * 561 (cache_len < 0, n_new < 1), 564, 575 (slot), 566 (cache_len != recorded fill), 567 (len_new != n_new),
  * 571 (cache_len + n_new > capacity * n_kv * head_dim, or, with pages, too few free blocks), 578 (with
  * pages: the stream is being captured and the reserve has device work). */

@@ -255,14 +255,16 @@ def gqa_attend_flat(q=True, len_q=0, k_cache=True, v_cache=True, len_cache=0, kv
 
 
 def _pool_fields(pool):
-    """A pool descriptor's own fields: 578 (null k, v or slot_len array, dtype), 561, 564, then 578 again
-    for a layer buffer that is null or not 16-byte aligned (pool["buffers"] False), then the pages when the
-    pool has them (pool["pages"])."""
-    if not pool.get("arrays", True) or pool.get("dtype", 0) not in (0, 1):
+    """A pool descriptor's own fields: 578 (null k, v or slot_len array, dtype), 561, 564, 574 (an int8 pool
+    whose head_dim is not a multiple of 16), then 578 again for a layer buffer that is null or not 16-byte
+    aligned (pool["buffers"] False), then the pages when the pool has them (pool["pages"])."""
+    if not pool.get("arrays", True) or pool.get("dtype", 0) not in (0, 1, 2):
         return INVALID
     c = _dims(pool["n_layer"], pool["n_slots"], pool["capacity"], pool["n_kv"], pool["head_dim"])
     if c != OK:
         return c
+    if pool.get("dtype", 0) == 2 and pool["head_dim"] % 16:
+        return HEAD_SHAPE   # int8 rows of whole 16-code loads
     if not pool.get("buffers", True):
         return INVALID
     return _pages_fields(pool) if pool.get("pages") else OK
@@ -379,7 +381,8 @@ def kv_append(pool=None, layer=0, slot=0, which=0, cache_len=0, recorded=0, new_
     c = _pool_fields(pool)
     if c != OK:
         return c, None, None
-    if not pool.get("records", True) or which not in (0, 1) or not (0 <= layer < pool["n_layer"]):
+    if not pool.get("records", True) or which not in (0, 1) or pool.get("dtype", 0) == 2 \
+            or not (0 <= layer < pool["n_layer"]):
         return INVALID, None, None
     if cache_len < 0 or n_new < 1:
         return EMPTY, None, None
@@ -522,7 +525,7 @@ def quantize_q8(w=True, len_w=0, w_dtype=0, rows=0, cols=0, pack=True, len_pack=
 def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps=1e-5, rope_base=1e4, rope_layout=0,
                  w_dtype=0, kv_dtype=0, w_layout=0, step_path=0, test_flags=0):
     import math
-    if rope_layout not in (0, 1) or w_dtype not in (0, 1, 2) or kv_dtype not in (0, 1) or w_layout not in (0, 1):
+    if rope_layout not in (0, 1) or w_dtype not in (0, 1, 2) or kv_dtype not in (0, 1, 2) or w_layout not in (0, 1):
         return INVALID
     if step_path not in (0, 1, 2) or test_flags not in (0, 1):
         return INVALID
@@ -533,6 +536,10 @@ def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps
         return c
     if not _attn_shape_ok(n_head, n_kv, head_dim):
         return HEAD_SHAPE
+    if kv_dtype == 2 and head_dim % 16:
+        return HEAD_SHAPE   # the int8 cache's rows are whole loads of 16 codes
+    if kv_dtype == 2 and step_path == 2:
+        return INVALID      # the int8 cache runs one kernel per operation
     if w_dtype == 2:
         # int8 packs: projection inputs in whole groups of 128, at most 4 loads of 16 codes x 64 lanes per wave
         # over the widest split that leaves a wave 1,024 codes or more

@@ -183,8 +183,10 @@ class _FakePool:
             self.struct.pages = ctypes.pointer(self.pages)
 
 
-POOL_CASES = [dict(), dict(arrays=False), dict(buffers=False), dict(dtype=2), dict(n_layer=0), dict(n_slots=-1),
-              dict(capacity=0), dict(head_dim=(1 << 24) + 1), dict(n_kv=0, buffers=False), dict(records=False)]
+POOL_CASES = [dict(), dict(arrays=False), dict(buffers=False), dict(dtype=3), dict(n_layer=0), dict(n_slots=-1),
+              dict(capacity=0), dict(head_dim=(1 << 24) + 1), dict(n_kv=0, buffers=False), dict(records=False),
+              dict(dtype=2), dict(dtype=2, head_dim=16), dict(dtype=2, head_dim=16, buffers=False),
+              dict(dtype=2, head_dim=24, buffers=False)]
 # paged pools: good ones, and one bad field each
 PAGED_CASES = [dict(paged=True), dict(paged=True, capacity=130, bt=64, n_blocks=7), dict(paged=True, bt=32),
                dict(paged=True, bt=96), dict(paged=True, bt=131072), dict(paged=True, max_blocks=2),
@@ -341,7 +343,9 @@ def test_config_checks_agree_with_oracle():
                 dict(d=(1 << 24) + 1), dict(n_head=6), dict(n_kv=3), dict(head_dim=6),
                 dict(head_dim=512), dict(n_head=32, n_kv=2), dict(hidden=22), dict(w_dtype=1), dict(w_dtype=3),
                 dict(rope_layout=2), dict(eps=0.0), dict(rope_base=1.0), dict(max_seq=-4), dict(kv_dtype=1),
-                dict(d=12, w_dtype=0), dict(d=24, w_dtype=1)]
+                dict(d=12, w_dtype=0), dict(d=24, w_dtype=1), dict(kv_dtype=2), dict(kv_dtype=3),
+                dict(kv_dtype=2, head_dim=16), dict(kv_dtype=2, head_dim=16, step_path=2),
+                dict(kv_dtype=2, head_dim=16, step_path=1, w_dtype=1)]
     for v in variants:
         kw = _cfg_kwargs(**v)
         cfg = llmk.make_config(**kw)
