@@ -267,6 +267,7 @@ struct StepParams {
   int32_t kv_shift;             // log2 of the positions per block
   int32_t attn_chunk;           // positions per attention tile
   int32_t give_up;              // test only: the attention waits for a tag nobody writes (bounded-wait path)
+  int32_t qw;                   // the projections and the head are int8 packs (layers' w[] and w_out point at packs)
   DecodeState* state;
   // activations as (value, tag) pairs, tag = step within the call + 1; cleared before each call.
   // x [2 n_layer][x_stride]: x after layer l's o (2l) and after its down (2l + 1); q|k|v, attention
@@ -289,8 +290,8 @@ struct StepParams {
 constexpr int STEP_MAX_LAYERS = 128;   // layers the persistent step kernel supports
 constexpr int STEP_MAX_VIN = 16384;    // longest projection input (d, H*hd, hidden) it supports
 constexpr int STEP_MAX_RES = 256;      // residual rows per workgroup (d / workgroups, rounded up) it supports
-// Workgroups the step kernel runs with on the current device (0 if it cannot hold one per CU).
-int step_grid(int kv_is_bf16, int hd);
+// Workgroups the step kernel runs with on the current device (0 if it cannot hold one per CU); qw: int8 packs.
+int step_grid(int kv_is_bf16, int hd, int qw);
 hipError_t step_launch(const StepParams& p, int kv_is_bf16, hipStream_t s);
 struct StepTableChunk {
   StepLayer layers[8];

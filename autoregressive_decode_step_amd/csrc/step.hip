@@ -27,7 +27,14 @@
 //
 // Norms. RMSNorm(x) * g is applied as (x * g) staged in LDS and the scalar rsqrt(mean(x^2) + eps) applied
 // to each row's dot product, so the dots start as soon as x is staged.
+//
+// int8 weight packs (QW). The same stream over the codes of the library's int8 packs: a lane's 16-byte load
+// holds 16 codes of one group, so a wave load covers 1,024 inputs, and a second ring of 4-byte loads brings
+// each slot's group scale; a slot's 16 products are summed, then scaled ("Inside the engine", "1. CausalLM":
+// decode reads packed weights).
 #include <limits.h>
+
+#include <type_traits>
 
 #include "attn_block.h"
 
@@ -37,6 +44,14 @@ constexpr int SK_THREADS = ATTN_THREADS;   // 512: 8 waves
 constexpr int SK_WAVES = SK_THREADS / 64;
 constexpr int SK_R = 16;                    // weight loads in flight per lane
 constexpr int SK_SEG = 512;                 // elements of one wave load (64 lanes x 8 bf16)
+// int8 weight packs (QW): a lane loads 16 codes, so a wave load covers 1,024 elements of a row, and every
+// 16 codes of a lane lie in one group of SK_QG inputs with its own fp32 scale
+constexpr int SK_SEG_Q = 1024;
+constexpr int SK_QG = 128;
+template <bool QW>
+__host__ __device__ constexpr int sk_seg() {
+  return QW ? SK_SEG_Q : SK_SEG;
+}
 constexpr int SK_PASS = 4;                  // float4 groups per thread staged per round trip
 
 enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DN = 3, OP_HEAD = 4 };
@@ -71,15 +86,22 @@ struct SkLayer {
 // One projection as one wave streams it. A row is 2^sh load slots (its loads rounded up to a power of
 // two; the extra slots re-read the row's last 16 bytes, which meet zeros of the staged input); load slot u
 // of the wave is slot u & (2^sh - 1) of wave-local row u >> sh.
-struct SkOp {
+struct SkScales {      // int8 packs: the scales of the first rows below (K / SK_QG per row)
+  const float* s0;
+  const float* s1;
+  const float* s2;
+};
+struct SkNoScales {};
+template <bool QW>
+struct SkOp : std::conditional<QW, SkScales, SkNoScales>::type {
   int kind, l;
   int K, sh;          // row length, log2 of the load slots per row
   int nrows, npos;    // rows of this wave, its load slots (nrows << sh rounded up to SK_R; 0: none)
   int n0, n01;        // QKV: the workgroup's rows of wq, of wq and wk (else larger than any row)
   int kmax;           // byte offset of a row's last 16-byte slice
-  const bf16_t* m0;   // the workgroup's first row of wq / gate / the matrix
-  const bf16_t* m1;   // of wk / up
-  const bf16_t* m2;   // of wv
+  const char* m0;     // the workgroup's first row of wq / gate / the matrix (bf16 elements, or int8 codes)
+  const char* m1;     // of wk / up
+  const char* m2;     // of wv
 };
 
 // c ? a : b on values (a conditional on two struct members would select between their addresses and keep
@@ -98,30 +120,38 @@ __device__ __forceinline__ P* sk_uniform(P* ptr) {
   return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
 
-// an op without loads, for the issue side past the last op: every slot reads the head's first 16 bytes
-__device__ __forceinline__ SkOp sk_idle(const StepParams& p) {
-  SkOp f;
-  f.kind = OP_HEAD;
-  f.l = 0;
-  f.K = 8;
-  f.sh = 0;
-  f.nrows = 1;
-  f.npos = 0;
-  f.n0 = f.n01 = INT_MAX;
-  f.kmax = 0;
-  f.m0 = f.m1 = f.m2 = p.w_out;
-  return f;
+// The workgroup's first row `lo` of a [rows][K] matrix: bf16 elements, or the codes of an int8 pack (whose
+// scales, K / SK_QG per row, follow all rows * K codes; *sc gets the first row's).
+template <bool QW>
+__device__ __forceinline__ const char* sk_rows_of(const bf16_t* m, int rows, int K, int lo, const float** sc) {
+  if constexpr (QW) {
+    const char* b = reinterpret_cast<const char*>(sk_uniform(m));
+    *sc = reinterpret_cast<const float*>(b + (int64_t)rows * K) + (int64_t)lo * (K / SK_QG);
+    return b + (int64_t)lo * K;
+  } else {
+    return reinterpret_cast<const char*>(sk_uniform(m) + (int64_t)lo * K);
+  }
 }
 
-__device__ __forceinline__ SkOp sk_op(const StepParams& p, const SkRows& R, const SkLayer* lt, int o, int wave) {
-  SkOp f;
+template <bool QW>
+__device__ __forceinline__ SkOp<QW> sk_op(const StepParams& p, const SkRows& R, const SkLayer* lt, int o, int wave) {
+  SkOp<QW> f;
   int rw;
   f.n0 = f.n01 = INT_MAX;
+  const float* sdummy;
+  const float** s0 = &sdummy;
+  const float** s1 = &sdummy;
+  const float** s2 = &sdummy;
+  if constexpr (QW) {
+    s0 = &f.s0;
+    s1 = &f.s1;
+    s2 = &f.s2;
+  }
   if (o >= 4 * p.n_layer) {
     f.kind = OP_HEAD;
     f.l = 0;
     f.K = p.d;
-    f.m0 = p.w_out + (int64_t)R.h.lo * p.d;
+    f.m0 = sk_rows_of<QW>(p.w_out, p.V, p.d, R.h.lo, s0);
     rw = R.h.n;
   } else {
     f.l = o >> 2;
@@ -130,73 +160,90 @@ __device__ __forceinline__ SkOp sk_op(const StepParams& p, const SkRows& R, cons
     switch (f.kind) {
       case OP_QKV:
         f.K = p.d;
-        f.m0 = sk_uniform(Ly.w[0]) + (int64_t)R.q.lo * p.d;
-        f.m1 = sk_uniform(Ly.w[1]) + (int64_t)R.k.lo * p.d;
-        f.m2 = sk_uniform(Ly.w[2]) + (int64_t)R.v.lo * p.d;
+        f.m0 = sk_rows_of<QW>(Ly.w[0], p.qd, p.d, R.q.lo, s0);
+        f.m1 = sk_rows_of<QW>(Ly.w[1], p.kvd, p.d, R.k.lo, s1);
+        f.m2 = sk_rows_of<QW>(Ly.w[2], p.kvd, p.d, R.v.lo, s2);
         f.n0 = R.q.n;
         f.n01 = R.q.n + R.k.n;
         rw = R.q.n + R.k.n + R.v.n;
         break;
       case OP_O:
         f.K = p.qd;
-        f.m0 = sk_uniform(Ly.w[3]) + (int64_t)R.d.lo * p.qd;
+        f.m0 = sk_rows_of<QW>(Ly.w[3], p.d, p.qd, R.d.lo, s0);
         rw = R.d.n;
         break;
       case OP_GU:
         f.K = p.d;
-        f.m0 = sk_uniform(Ly.w[4]) + (int64_t)R.f.lo * p.d;
-        f.m1 = sk_uniform(Ly.w[5]) + (int64_t)R.f.lo * p.d;
+        f.m0 = sk_rows_of<QW>(Ly.w[4], p.F, p.d, R.f.lo, s0);
+        f.m1 = sk_rows_of<QW>(Ly.w[5], p.F, p.d, R.f.lo, s1);
         rw = R.f.n;
         break;
       default:
         f.K = p.F;
-        f.m0 = sk_uniform(Ly.w[6]) + (int64_t)R.d.lo * p.F;
+        f.m0 = sk_rows_of<QW>(Ly.w[6], p.d, p.F, R.d.lo, s0);
         rw = R.d.n;
         break;
     }
   }
   if (f.kind != OP_QKV) {
-    const bf16_t* m = sk_sel<const bf16_t*>(f.kind == OP_GU, f.m1, f.m0);
-    f.m1 = m;
-    f.m2 = m;
+    const bool gu = f.kind == OP_GU;
+    f.m1 = f.m2 = sk_sel<const char*>(gu, f.m1, f.m0);
+    if constexpr (QW) f.s1 = f.s2 = sk_sel<const float*>(gu, f.s1, f.s0);
   }
-  const int lpr = (f.K + SK_SEG - 1) / SK_SEG;
+  const int lpr = (f.K + sk_seg<QW>() - 1) / sk_seg<QW>();
   f.sh = 0;
   while ((1 << f.sh) < lpr) ++f.sh;
-  f.kmax = 2 * (f.K - 8);
+  f.kmax = QW ? f.K - 16 : 2 * (f.K - 8);
   const int mine = rw > wave ? (rw - wave + SK_WAVES - 1) / SK_WAVES : 0;
   f.nrows = f.kind == OP_GU ? 2 * mine : mine;
   f.npos = ((f.nrows << f.sh) + SK_R - 1) / SK_R * SK_R;
   return f;
 }
 
-// address of load slot u of op f for this lane (slots past the wave's rows re-read its last row)
-__device__ __forceinline__ const char* sk_addr(const SkOp& f, int u, int wave, int lane16) {
+// address of load slot u of op f for this lane (slots past the wave's rows re-read its last row); with int8
+// packs *sa gets the address of the slot's scale (the group of the lane's 16 codes)
+template <bool QW>
+__device__ __forceinline__ const char* sk_addr(const SkOp<QW>& f, int u, int wave, int lane16, const float** sa) {
   const int r = min(u >> f.sh, f.nrows - 1);
   const int c = u & ((1 << f.sh) - 1);
   const int q = wave + SK_WAVES * r;
   const int j = wave + SK_WAVES * (r >> 1);
   const bool gu = f.kind == OP_GU;
-  const bf16_t* m0 = f.m0;
-  const bf16_t* m1 = f.m1;
-  const bf16_t* m2 = f.m2;
+  const char* m0 = f.m0;
+  const char* m1 = f.m1;
+  const char* m2 = f.m2;
   const int n0 = f.n0, n01 = f.n01;
-  const bf16_t* base = sk_sel(gu, sk_sel((r & 1) != 0, m1, m0), sk_sel(q < n0, m0, sk_sel(q < n01, m1, m2)));
+  const char* base = sk_sel(gu, sk_sel((r & 1) != 0, m1, m0), sk_sel(q < n0, m0, sk_sel(q < n01, m1, m2)));
   const int row = sk_sel(gu, j, sk_sel(q < n0, q, sk_sel(q < n01, q - n0, q - n01)));
-  const int off = min(c * (SK_SEG * 2) + lane16, f.kmax);
-  return reinterpret_cast<const char*>(base + (int64_t)row * f.K) + off;
+  if constexpr (QW) {
+    const int off = min(c * SK_SEG_Q + lane16, f.kmax);
+    const float* sb = sk_sel(gu, sk_sel((r & 1) != 0, f.s1, f.s0), sk_sel(q < n0, f.s0, sk_sel(q < n01, f.s1, f.s2)));
+    *sa = sb + (int64_t)row * (f.K / SK_QG) + off / SK_QG;
+    return base + (int64_t)row * f.K + off;
+  } else {
+    const int off = min(c * (SK_SEG * 2) + lane16, f.kmax);
+    return reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(base) + (int64_t)row * f.K) + off;
+  }
 }
 
-// LDS position of input element e (e % 4 == 0 for a float4 group): lane l's 8 elements of segment c sit as
-// two float4 at c*512 + l*4 and c*512 + 256 + l*4, so both reads of a segment are contiguous over the lanes
+// LDS position of input element e (e % 4 == 0 for a float4 group). bf16 rows: lane l's 8 elements of
+// segment c sit as two float4 at c*512 + l*4 and c*512 + 256 + l*4; int8 rows: lane l's 16 elements of
+// segment c as four float4 at c*1024 + k*256 + l*4. Every read of a segment is contiguous over the lanes.
+template <bool QW>
 __device__ __forceinline__ int sk_vin_pos(int e) {
-  const int c = e >> 9, r = e & 511;
-  return (c << 9) | (((r >> 2) & 1) << 8) | ((r >> 3) << 2) | (r & 3);
+  if constexpr (QW) {
+    const int c = e >> 10, r = e & 1023;
+    return (c << 10) | (((r >> 2) & 3) << 8) | ((r >> 4) << 2) | (r & 3);
+  } else {
+    const int c = e >> 9, r = e & 511;
+    return (c << 9) | (((r >> 2) & 1) << 8) | ((r >> 3) << 2) | (r & 3);
+  }
 }
 
 // Stage an input vector of n fp32 values into LDS (permuted; zeros up to the padded row length npad):
 // src_tag = (value, tag) pairs waited for, or src_emb = a bf16 row (no wait). gain: multiply by it.
 // res: copy elements [res_lo, res_lo + res_n) unmultiplied to res. Returns this thread's sum of squares.
+template <bool QW>
 __device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t* src_emb, int n, int npad,
                                           uint32_t tag, const float* gain, float* res, int res_lo, int res_n,
                                           float* vin, int32_t* err, bool& failed) {
@@ -278,12 +325,12 @@ __device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t*
           o.z *= g[k].z;
           o.w *= g[k].w;
         }
-        *reinterpret_cast<float4*>(vin + sk_vin_pos(e)) = o;
+        *reinterpret_cast<float4*>(vin + sk_vin_pos<QW>(e)) = o;
       }
     }
   }
   for (int e = n + 4 * t; e < npad; e += 4 * SK_THREADS)
-    *reinterpret_cast<float4*>(vin + sk_vin_pos(e)) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    *reinterpret_cast<float4*>(vin + sk_vin_pos<QW>(e)) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   return ss;
 }
 
@@ -311,8 +358,8 @@ struct SkOut {
 
 // Row results of one wave, lane-parallel: wave-local row r's dot product is in lane r of y (r < 64) or
 // lane r - 64 of y2. Written out once the op's loads are done, so the load loop holds no stores.
-template <int KIND>
-__device__ __forceinline__ void sk_rows_out(float y, float y2, const SkOp& f, const StepParams& p, const SkRows& R,
+template <int KIND, typename Op>
+__device__ __forceinline__ void sk_rows_out(float y, float y2, const Op& f, const StepParams& p, const SkRows& R,
                                             const SkOut& out, int wave, int lane, float& best_v, int& best_i) {
   if constexpr (KIND == OP_GU) {
     // gate of output j in lane 2j, its up in lane 2j + 1 (of y, then of y2)
@@ -370,27 +417,54 @@ __device__ __forceinline__ void sk_rows_out(float y, float y2, const SkOp& f, co
 // One block of SK_R ring slots of op f, starting at slot blk: slot j is read and dotted with the staged
 // input, then refilled with slot ib + j of op `is` (when ISSUE). A row's dot product is reduced over the wave
 // at its last slot and put into lane r of y (r < 64) or lane r - 64 of y2.
-template <bool ISSUE>
-__device__ __forceinline__ void sk_block(uint4 (&ring)[SK_R], const SkOp& f, int blk, const SkOp& is, int ib,
-                                         const float* vl, int wave, int lane, int lane16, float& acc0,
-                                         float& acc1, float& y, float& y2) {
+// Dot of 4 int8 codes (one word) with 4 inputs. (Taking the codes as unsigned bytes q + 128, one conversion
+// each, and subtracting 128 times the staged input's group sums was measured slower here: 2.78 against
+// 2.67 ms for the 8B step; the group sum is one more LDS read in front of every slot's last FMAs.)
+__device__ __forceinline__ float sk_dot4_i8(uint32_t w, const float4& x, float acc) {
+  acc = fmaf((float)(int8_t)w, x.x, acc);
+  acc = fmaf((float)(int8_t)(w >> 8), x.y, acc);
+  acc = fmaf((float)(int8_t)(w >> 16), x.z, acc);
+  return fmaf((float)(int8_t)(w >> 24), x.w, acc);
+}
+
+template <bool ISSUE, bool QW>
+__device__ __forceinline__ void sk_block(uint4 (&ring)[SK_R], float (&sring)[SK_R], const SkOp<QW>& f, int blk,
+                                         const SkOp<QW>& is, int ib, const float* vl, int wave, int lane, int lane16,
+                                         float& acc0, float& acc1, float& y, float& y2) {
   const int mask = (1 << f.sh) - 1;
 #pragma unroll
   for (int j = 0; j < SK_R; ++j) {
     const int u = blk + j;
     const int c = u & mask;
-    const float4 x0 = *reinterpret_cast<const float4*>(vl + c * SK_SEG);
-    const float4 x1 = *reinterpret_cast<const float4*>(vl + c * SK_SEG + 256);
     const uint4 r = ring[j];
-    acc0 = fmaf(bf16_lo(r.x), x0.x, acc0);
-    acc1 = fmaf(bf16_hi(r.x), x0.y, acc1);
-    acc0 = fmaf(bf16_lo(r.y), x0.z, acc0);
-    acc1 = fmaf(bf16_hi(r.y), x0.w, acc1);
-    acc0 = fmaf(bf16_lo(r.z), x1.x, acc0);
-    acc1 = fmaf(bf16_hi(r.z), x1.y, acc1);
-    acc0 = fmaf(bf16_lo(r.w), x1.z, acc0);
-    acc1 = fmaf(bf16_hi(r.w), x1.w, acc1);
-    if constexpr (ISSUE) ring[j] = gload<uint4>(sk_addr(is, ib + j, wave, lane16));
+    if constexpr (QW) {
+      // 16 codes times the lane's 16 inputs, then times the group's scale
+      const float* xv = vl + c * SK_SEG_Q;
+      const float4 x0 = *reinterpret_cast<const float4*>(xv);
+      const float4 x1 = *reinterpret_cast<const float4*>(xv + 256);
+      const float4 x2 = *reinterpret_cast<const float4*>(xv + 512);
+      const float4 x3 = *reinterpret_cast<const float4*>(xv + 768);
+      const float d0 = sk_dot4_i8(r.z, x2, sk_dot4_i8(r.x, x0, 0.0f));
+      const float d1 = sk_dot4_i8(r.w, x3, sk_dot4_i8(r.y, x1, 0.0f));
+      acc0 = fmaf(d0, sring[j], acc0);
+      acc1 = fmaf(d1, sring[j], acc1);
+    } else {
+      const float4 x0 = *reinterpret_cast<const float4*>(vl + c * SK_SEG);
+      const float4 x1 = *reinterpret_cast<const float4*>(vl + c * SK_SEG + 256);
+      acc0 = fmaf(bf16_lo(r.x), x0.x, acc0);
+      acc1 = fmaf(bf16_hi(r.x), x0.y, acc1);
+      acc0 = fmaf(bf16_lo(r.y), x0.z, acc0);
+      acc1 = fmaf(bf16_hi(r.y), x0.w, acc1);
+      acc0 = fmaf(bf16_lo(r.z), x1.x, acc0);
+      acc1 = fmaf(bf16_hi(r.z), x1.y, acc1);
+      acc0 = fmaf(bf16_lo(r.w), x1.z, acc0);
+      acc1 = fmaf(bf16_hi(r.w), x1.w, acc1);
+    }
+    if constexpr (ISSUE) {
+      const float* sa = nullptr;
+      ring[j] = gload<uint4>(sk_addr<QW>(is, ib + j, wave, lane16, &sa));
+      if constexpr (QW) sring[j] = gload<float>(sa);
+    }
     if (c == mask) {
       const int rr = u >> f.sh;
       const float t = wave_sum_dpp(acc0 + acc1);
@@ -406,16 +480,17 @@ __device__ __forceinline__ void sk_block(uint4 (&ring)[SK_R], const SkOp& f, int
 // Consume the loads of op f from the ring while refilling each slot right after it is read with the slot
 // SK_R further on (the last block refills nothing). Nothing but the ring's loads and the LDS reads of the
 // input touches memory in the loop, so every slot waits only for its own load.
-__device__ __forceinline__ void sk_consume(uint4 (&ring)[SK_R], const SkOp& f, const float* vl, int wave, int lane,
-                                           int lane16, float& y, float& y2) {
+template <bool QW>
+__device__ __forceinline__ void sk_consume(uint4 (&ring)[SK_R], float (&sring)[SK_R], const SkOp<QW>& f, const float* vl,
+                                           int wave, int lane, int lane16, float& y, float& y2) {
   float acc0 = 0.0f, acc1 = 0.0f;
   y = 0.0f;
   y2 = 0.0f;
   if (f.npos <= 0) return;
   int blk = 0;
   for (; blk + SK_R < f.npos; blk += SK_R)
-    sk_block<true>(ring, f, blk, f, blk + SK_R, vl, wave, lane, lane16, acc0, acc1, y, y2);
-  sk_block<false>(ring, f, blk, f, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
+    sk_block<true, QW>(ring, sring, f, blk, f, blk + SK_R, vl, wave, lane, lane16, acc0, acc1, y, y2);
+  sk_block<false, QW>(ring, sring, f, blk, f, 0, vl, wave, lane, lane16, acc0, acc1, y, y2);
 }
 
 // The attention parameters of layer l in the persistent step: (K/V head, context part) items over the context
@@ -484,7 +559,7 @@ constexpr int sk_lds_vecs() {
   return attn_tile_vecs<T, HD>() > STEP_MAX_VIN / 4 ? attn_tile_vecs<T, HD>() : STEP_MAX_VIN / 4;
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool QW>
 __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p) {
   // the staged input vector and the attention tiles are never live together: one region of dynamic LDS
   // (sk_lds_vecs<T, HD>() vectors)
@@ -539,14 +614,19 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
   int best_i = INT_MAX;
 
   for (int o = 0; o < n_ops; ++o) {
-    const SkOp f = sk_op(p, R, s_layers, o, wave);
+    const SkOp<QW> f = sk_op<QW>(p, R, s_layers, o, wave);
     // The op's first SK_R loads go out before its input is waited for (for o: after this workgroup's attention
     // items, which need the registers, and before its merges), so the weights stream while the producers finish.
     if (f.kind == OP_O) sk_attention_items<T, HD>(&p, f.l, pos, tag);
     uint4 ring[SK_R];
+    float sring[SK_R];   // int8 packs: each slot's scale
     if (f.npos > 0) {
 #pragma unroll
-      for (int j = 0; j < SK_R; ++j) ring[j] = gload<uint4>(sk_addr(f, j, wave, lane16));
+      for (int j = 0; j < SK_R; ++j) {
+        const float* sa = nullptr;
+        ring[j] = gload<uint4>(sk_addr<QW>(f, j, wave, lane16, &sa));
+        if constexpr (QW) sring[j] = gload<float>(sa);
+      }
     }
     if (f.kind == OP_O) sk_attention_merges<T, HD>(&p, f.l, pos, tag);
     // ---- the op's input ----
@@ -556,14 +636,14 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
     out.res = s_res;
     out.hidden = nullptr;
     out.logits = p.logits;
-    const int npad = SK_SEG << f.sh;
+    const int npad = sk_seg<QW>() << f.sh;
     if (f.kind == OP_O) {
       __syncthreads();
-      sk_stage(SK_ATT(f.l), nullptr, p.qd, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
+      sk_stage<QW>(SK_ATT(f.l), nullptr, p.qd, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
       out.y = SK_X(2 * f.l);
     } else if (f.kind == OP_DN) {
       __syncthreads();
-      sk_stage(SK_U(f.l), nullptr, p.F, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
+      sk_stage<QW>(SK_U(f.l), nullptr, p.F, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
       out.y = SK_X(2 * f.l + 1);
       out.hidden = p.hidden ? p.hidden + (int64_t)f.l * p.d : nullptr;
     } else {
@@ -586,7 +666,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
         out.y = nullptr;
       }
       __syncthreads();
-      const float ss = sk_stage(src, emb, p.d, npad, tag, gain, f.kind == OP_HEAD ? nullptr : s_res, R.d.lo, R.d.n,
+      const float ss = sk_stage<QW>(src, emb, p.d, npad, tag, gain, f.kind == OP_HEAD ? nullptr : s_res, R.d.lo, R.d.n,
                                 vin, p.err, failed);
       out.scale = 1.0f / sqrtf(sk_block_sum(ss, s_red) / (float)p.d + p.eps);
     }
@@ -594,7 +674,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
 
     // ---- the op's loads: dot from the ring, refill the ring ----
     float y, y2;
-    sk_consume(ring, f, vin + lane * 4, wave, lane, lane16, y, y2);
+    sk_consume<QW>(ring, sring, f, vin + lane * 4, wave, lane, lane16, y, y2);
     if (f.npos > 0) {
       switch (f.kind) {
         case OP_QKV: sk_rows_out<OP_QKV>(y, y2, f, p, R, out, wave, lane, best_v, best_i); break;
@@ -665,15 +745,24 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
   }
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool QW>
 static const void* step_fn() {
-  return reinterpret_cast<const void*>(&step_kernel<T, HD>);
+  return reinterpret_cast<const void*>(&step_kernel<T, HD, QW>);
 }
 
-static const void* step_kernel_ptr(int kv_is_bf16, int hd) {
+// int8 weight packs run with head dims 64, 128 and 256 (the shapes whose widths are whole groups of 128)
+static const void* step_kernel_ptr(int kv_is_bf16, int hd, int qw) {
+  if (qw) {
+    switch (hd) {
+      case 64: return kv_is_bf16 ? step_fn<bf16_t, 64, true>() : step_fn<float, 64, true>();
+      case 128: return kv_is_bf16 ? step_fn<bf16_t, 128, true>() : step_fn<float, 128, true>();
+      case 256: return kv_is_bf16 ? step_fn<bf16_t, 256, true>() : step_fn<float, 256, true>();
+    }
+    return nullptr;
+  }
   switch (hd) {
 #define LLMK_SK_CASE(H) \
-  case H: return kv_is_bf16 ? step_fn<bf16_t, H>() : step_fn<float, H>();
+  case H: return kv_is_bf16 ? step_fn<bf16_t, H, false>() : step_fn<float, H, false>();
     LLMK_SK_CASE(2) LLMK_SK_CASE(4) LLMK_SK_CASE(8) LLMK_SK_CASE(16) LLMK_SK_CASE(32) LLMK_SK_CASE(64)
     LLMK_SK_CASE(128) LLMK_SK_CASE(256)
 #undef LLMK_SK_CASE
@@ -692,8 +781,8 @@ static size_t step_lds_bytes(int kv_is_bf16, int hd) {
   return 0;
 }
 
-int step_grid(int kv_is_bf16, int hd) {
-  const void* fn = step_kernel_ptr(kv_is_bf16, hd);
+int step_grid(int kv_is_bf16, int hd, int qw) {
+  const void* fn = step_kernel_ptr(kv_is_bf16, hd, qw);
   if (!fn) return 0;
   const size_t lds = step_lds_bytes(kv_is_bf16, hd);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return 0;
@@ -707,7 +796,7 @@ int step_grid(int kv_is_bf16, int hd) {
 }
 
 hipError_t step_launch(const StepParams& p, int kv_is_bf16, hipStream_t s) {
-  const void* fn = step_kernel_ptr(kv_is_bf16, p.hd);
+  const void* fn = step_kernel_ptr(kv_is_bf16, p.hd, p.qw);
   if (!fn || p.nwg < 1) return hipErrorInvalidValue;
   void* args[] = {const_cast<StepParams*>(&p)};
   return hipLaunchKernel(fn, dim3((unsigned)p.nwg), dim3(SK_THREADS), args, step_lds_bytes(kv_is_bf16, p.hd), s);

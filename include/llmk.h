@@ -92,8 +92,10 @@ typedef enum { LLMK_W_IN_OUT = 0, LLMK_W_OUT_IN = 1 } llmk_weight_layout;
 
 /* How llmk_decode_step / llmk_decode_steps run the step of one sequence. Both compute the same step
  * (the same arithmetic up to the order of fp32 sums). The persistent form needs bf16 weights in
- * LLMK_W_OUT_IN and a device that holds one of its workgroups per CU.
- *   LLMK_STEP_AUTO       the persistent kernel where it can run, else one kernel per operation
+ * LLMK_W_OUT_IN (or int8 packs with head_dim 64..256), a bf16 or fp32 K/V cache, and a device that holds
+ * one of its workgroups per CU.
+ *   LLMK_STEP_AUTO       the persistent kernel where it can run, else one kernel per operation; int8
+ *                        packs take one kernel per operation (they stream faster that way)
  *   LLMK_STEP_PER_OP     one kernel per operation: 5 per layer (q|k|v, attention, o, gate|up, down) + head
  *   LLMK_STEP_PERSISTENT one kernel per step, the operations separated by grid barriers; refused (578)
  *                        where it cannot run */
@@ -592,8 +594,9 @@ int32_t llmk_prefill_profiled(const llmk_config* cfg, const llmk_model* model, l
  * wo [d x H*hd], w_gate, w_up [F x d], w_down [d x F] and w_out [vocab x d] (each llmk_tensor.len is the
  * pack's byte count, the pointer 16-byte aligned) and the embedding table in bf16 (vocab*d elements).
  * d, H*hd and F are multiples of LLMK_Q8_GROUP, at most 16,384. Such a model runs llmk_decode_step,
- * llmk_decode_steps and the timing aids in the per-operation form; the persistent step, the batched
- * step and prefill refuse it (578). */
+ * llmk_decode_steps (sampled too) and the timing aids, in the persistent form where it can run (head_dim
+ * 64..256, a bf16 or fp32 K/V cache) and else one kernel per operation; the batched step and prefill refuse
+ * it (578). */
 #define LLMK_Q8_GROUP 128
 
 /* Bytes of a q8 pack of a rows x cols matrix, or -1 if rows or cols is < 1 or > LLMK_MAX_DIM or cols is not

@@ -547,7 +547,7 @@ def config_check(vocab, d, n_layer, n_head, n_kv, head_dim, hidden, max_seq, eps
             kw = 4 if k // 4 >= 1024 else 2 if k // 2 >= 1024 else 1
             if k % Q8_GROUP or -(-(k // kw) // 1024) > 4:
                 return HEAD_SHAPE
-        if w_layout != 1 or step_path == 2:
+        if w_layout != 1:
             return INVALID
         return OK
     vec = 4 if w_dtype == 0 else 8

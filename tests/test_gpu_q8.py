@@ -1,7 +1,9 @@
 """int8 weight packs on the GPU (llmk_quantize_q8 and the q8 decode step) against the oracle.
 
 The quantizer's packs equal the oracle's byte for byte (codes are decided in fp32 on both sides). The decode
-step over packs quantized on the device is checked against the oracle running the decoder the packs describe
+step over packs quantized on the device, in both forms (one kernel per operation, and the persistent step
+kernel streaming the packs, the form the library picks), is checked against the oracle running the decoder the
+packs describe
 (its own quantization of the same bf16 weights, weights q * s): greedy tokens bit-exact (or a reported
 near-tie), logits and per-layer hidden states within the bar. Sizes: a small decoder whose every projection
 spans several row blocks with a ragged last one (vocab 1,000, d 256, F 384), the Qwen3-0.6B shape after a
@@ -66,22 +68,31 @@ def _margin(lg):
 
 
 def _q8_case(s, n_pre, n_steps, f64, label):
+    """Both step forms (one kernel per operation, and the persistent step kernel streaming the packs) against
+    the oracle on its own quantization: a free run and teacher-forced steps."""
     say(f"{label}: weights")
     W = weights(s)
     prefix = synth.kv_prefix(s, n_pre, seed=2) if n_pre else None
     first = int(synth.prompt(1, s.vocab, stream=7)[0])
 
     say(f"{label}: GPU upload and quantization")
-    cfg = loader.config_from(s.with_(w_dtype="q8"))
-    assert llmk.decode_path(cfg) == llmk.STEP_PER_OP
-    model = loader.upload_model(cfg, W)
-    pool = loader.new_pool(cfg, 1, n_pre + n_steps)
-    if prefix:
-        loader.fill_prefix(pool, 0, prefix)
-    dec = loader.Decoder(cfg, model, pool)
-    toks = torch.zeros(n_steps, dtype=torch.int32, device="cuda")
-    assert dec.steps(first, n_pre, n_steps, toks) == llmk.OK
-    gpu_free = host(toks).tolist()
+    cfgs = {path: loader.config_from(s.with_(w_dtype="q8"), step_path=path)
+            for path in (llmk.STEP_PER_OP, llmk.STEP_PERSISTENT)}
+    assert llmk.decode_path(loader.config_from(s.with_(w_dtype="q8"))) == llmk.STEP_PER_OP   # auto: per-op streams packs faster
+    model = loader.upload_model(cfgs[llmk.STEP_PER_OP], W)
+
+    def new_dec(cfg):
+        pool = loader.new_pool(cfg, 1, n_pre + n_steps)
+        if prefix:
+            loader.fill_prefix(pool, 0, prefix)
+        return loader.Decoder(cfg, model, pool)
+
+    gpu_free = {}
+    for path, cfg in cfgs.items():
+        assert llmk.decode_path(cfg) == path
+        toks = torch.zeros(n_steps, dtype=torch.int32, device="cuda")
+        assert new_dec(cfg).steps(first, n_pre, n_steps, toks) == llmk.OK
+        gpu_free[path] = host(toks).tolist()
 
     say(f"{label}: oracle on its own quantization")
     m = oracle.Model(s, quant.quantized_weights(W, f64=f64))
@@ -97,29 +108,29 @@ def _q8_case(s, n_pre, n_steps, f64, label):
         o_lg.append(lg)
         o_hid.append(hid)
         ties.append(_margin(lg))
-    say(f"{label}: gpu {gpu_free} oracle {o_tok}")
+    say(f"{label}: gpu per-op {gpu_free[llmk.STEP_PER_OP]} persistent {gpu_free[llmk.STEP_PERSISTENT]} "
+        f"oracle {o_tok}")
 
-    # teacher-forced steps on a second pool: logits, hidden states and the token of each step
-    pool2 = loader.new_pool(cfg, 1, n_pre + n_steps)
-    if prefix:
-        loader.fill_prefix(pool2, 0, prefix)
-    dec2 = loader.Decoder(cfg, model, pool2)
-    ins = [first] + o_tok[:-1]
-    for i, tin in enumerate(ins):
-        lg = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
-        hid = torch.empty(s.n_layer * s.d, dtype=torch.float32, device="cuda")
-        assert dec2.step(tin, n_pre + i, 0, lg, hid) == llmk.OK
-        torch.cuda.synchronize()
-        el = rel_err(host(lg), o_lg[i])
-        eh = rel_err(host(hid).reshape(s.n_layer, s.d), o_hid[i])
-        say(f"{label}: step {i}: logits err {el:.2e} hidden err {eh:.2e}")
-        assert el <= TOL and eh <= TOL
-        g = int(host(dec2.token_out)[0])
-        assert g == o_tok[i] or ties[i], f"{label}: step {i}: token {g} != oracle {o_tok[i]}"
-    for i, (g, w) in enumerate(zip(gpu_free, o_tok)):
-        if g != w:
-            assert ties[i], f"{label}: free-running step {i}: {g} != {w}"
-            break   # after a near-tie the two continuations differ by construction
+    for path, cfg in cfgs.items():
+        name = "per-op" if path == llmk.STEP_PER_OP else "persistent"
+        # teacher-forced steps on a fresh pool: logits, hidden states and the token of each step
+        dec2 = new_dec(cfg)
+        ins = [first] + o_tok[:-1]
+        for i, tin in enumerate(ins):
+            lg = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
+            hid = torch.empty(s.n_layer * s.d, dtype=torch.float32, device="cuda")
+            assert dec2.step(tin, n_pre + i, 0, lg, hid) == llmk.OK
+            torch.cuda.synchronize()
+            el = rel_err(host(lg), o_lg[i])
+            eh = rel_err(host(hid).reshape(s.n_layer, s.d), o_hid[i])
+            say(f"{label} {name}: step {i}: logits err {el:.2e} hidden err {eh:.2e}")
+            assert el <= TOL and eh <= TOL
+            g = int(host(dec2.token_out)[0])
+            assert g == o_tok[i] or ties[i], f"{label} {name}: step {i}: token {g} != oracle {o_tok[i]}"
+        for i, (g, w) in enumerate(zip(gpu_free[path], o_tok)):
+            if g != w:
+                assert ties[i], f"{label} {name}: free-running step {i}: {g} != {w}"
+                break   # after a near-tie the two continuations differ by construction
 
 
 SMALL = synth.TINY.with_(name="q8 test decoder", vocab=1000, d=256, n_layer=2, n_head=4, n_kv=2, head_dim=64,
