@@ -8,7 +8,7 @@
 // 64 x 64 sub-tile with v_mfma_f32_16x16x32_bf16 (4 x 4 tiles of 16 x 16). X is fp32 carried as bf16 hi + lo
 // (each product taken twice into fp32), W is bf16 and exact. Where the tiles alone do not fill the chip, K is
 // split: each split writes its partial tile, and the epilogue kernel adds the splits in order and applies the
-// operation (store, residual add, SiLU-gate into hi/lo).
+// operation (store, residual add, SiLU-gate into hi/lo). Up to 64 rows (the decode batch) take 64 x 128 tiles.
 //
 // MFMA operands (per wave, 16 x 32 by 32 x 16): lane l holds row l % 16 of the X tile and row l % 16 of the
 // W tile, eight consecutive k of group l / 16 (one 16-byte LDS read each); the 16 x 16 result gives lane l
@@ -25,9 +25,8 @@ typedef float pg_f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int PG_THREADS = 256;
 constexpr int PG_BM = 128;
 constexpr int PG_BN = 128;
-constexpr int PG_BK = 32;
-constexpr int PG_LDK = 40;   // LDS row stride in bf16 (80 bytes): the 16 rows one operand read touches use
-                             // different banks
+constexpr int PG_BK = 32;     // k per slice of 128-row tiles
+constexpr int PG_BK64 = 64;   // k per slice of 64-row tiles
 
 __device__ __forceinline__ pg_f32x4_t pg_mfma(const uint4& a, const uint4& b, const pg_f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pg_bf16x8_t, a),
@@ -48,82 +47,108 @@ __device__ __forceinline__ const bf16_t* pg_wrow(const PgemmParams& p, int64_t n
   return static_cast<const bf16_t*>(p.w2) + (r - p.n0 - p.n1) * p.K;
 }
 
-__global__ __launch_bounds__(PG_THREADS, 1) void pgemm_kernel(const PgemmParams p) {
-  __shared__ __align__(16) bf16_t s_a[2][2][PG_BM][PG_LDK];   // [buffer][hi, lo][row][k]
-  __shared__ __align__(16) bf16_t s_w[2][PG_BN][PG_LDK];      // [buffer][row][k]
+// BM = 128: each wave multiplies a 64 x 64 sub-tile, slices of BK = 32. BM = 64 (a decode batch of up to 64
+// rows): a 64 x 128 tile, each wave 64 x 32, so no matrix-core work goes to rows that do not exist, with slices
+// of BK = 64 so twice the weight bytes are on their way per barrier.
+template <int BM, int BK>
+__global__ __launch_bounds__(PG_THREADS, BM == 64 ? 2 : 1) void pgemm_kernel(const PgemmParams p) {
+  static_assert((BM == 64 || BM == 128) && BK % 32 == 0, "64 or 128 rows, k slices of 32 or more");
+  constexpr int LDK = BK + 8;                        // LDS row stride in bf16 (80 or 144 bytes): the 16 rows
+                                                     // one operand read touches use different banks
+  constexpr int GPR = BK / 8;                        // 8-element groups per tile row
+  constexpr int XG = BM * GPR / PG_THREADS;          // groups of the X tile per thread
+  constexpr int WG = PG_BN * GPR / PG_THREADS;       // groups of the W tile per thread
+  constexpr int WN = BM == 64 ? 4 : 2;               // waves along N
+  constexpr int TN = PG_BN / WN / 16;                // 16-column tiles per wave
+  __shared__ __align__(16) bf16_t s_a[2][2][BM][LDK];        // [buffer][hi, lo][row][k]
+  __shared__ __align__(16) bf16_t s_w[2][PG_BN][LDK];        // [buffer][row][k]
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;                    // this wave's 64 x 64 sub-tile
-  const int64_t m0 = (int64_t)blockIdx.y * PG_BM, n0 = (int64_t)blockIdx.x * PG_BN;
+  const int wm = wave / WN, wn = wave % WN;                   // this wave's 64 x (16 TN) sub-tile
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * PG_BN;
   const int64_t kb = (int64_t)blockIdx.z * p.kslice;
   const int64_t ke = min(p.K, kb + p.kslice);
-  const int nk = (int)((ke - kb + PG_BK - 1) / PG_BK);
+  const int nk = (int)((ke - kb + BK - 1) / BK);
 
-  // staging: thread t moves 8-element groups g = t and t + 256 of each 128 x 32 tile (row g / 4, group g % 4).
+  // staging: thread t moves 8-element groups g = t, t + 256, ... of each tile (row g / GPR, group g % GPR).
   // Two register sets in turn keep the loads of slice i + 2 in flight while slice i is multiplied and slice
   // i + 1 goes to LDS; every load is issued unconditionally (past the end of K, from k = 0) and zeroed when it
   // is staged, so no load sits in a branch of its own.
-  const bf16_t* ah[2];
-  const bf16_t* al[2];
-  const bf16_t* wr[2];
-  int srow[2], sk[2];
+  const bf16_t* ah[XG];
+  const bf16_t* al[XG];
+  int xrow[XG], xk[XG];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < XG; ++i) {
     const int g = t + i * PG_THREADS;
-    srow[i] = g >> 2;
-    sk[i] = (g & 3) * 8;
-    const int64_t m = min(m0 + srow[i], (int64_t)p.M - 1);   // rows past M read a valid row; never stored
+    xrow[i] = g / GPR;
+    xk[i] = (g % GPR) * 8;
+    const int64_t m = min(m0 + xrow[i], (int64_t)p.M - 1);   // rows past M read a valid row; never stored
     ah[i] = p.ahi + m * p.lda;
     al[i] = p.alo + m * p.lda;
-    wr[i] = pg_wrow(p, n0 + srow[i]);
+  }
+  const bf16_t* wr[WG];
+  int wrow[WG], wk[WG];
+#pragma unroll
+  for (int i = 0; i < WG; ++i) {
+    const int g = t + i * PG_THREADS;
+    wrow[i] = g / GPR;
+    wk[i] = (g % GPR) * 8;
+    wr[i] = pg_wrow(p, n0 + wrow[i]);
   }
   // a set's k: its groups past the end of K are zeroed when staged (K is a multiple of 8: a group is all in or
   // all out)
-  uint4 a0h0, a0h1, a0l0, a0l1, w00, w01;   // set 0
-  uint4 a1h0, a1h1, a1l0, a1l1, w10, w11;   // set 1
-  int64_t k0s = 0, k1s = 0;
-#define PG_LOAD(AH0, AH1, AL0, AL1, W0, W1, KS, K)                                      \
+  uint4 xh[2][XG], xl[2][XG], wv[2][WG];
+  int64_t ks[2] = {0, 0};
+#define PG_LOAD(S, K)                                                                   \
   {                                                                                     \
-    KS = (K);                                                                           \
-    const int64_t c0 = KS + sk[0] < ke ? KS + sk[0] : 0, c1 = KS + sk[1] < ke ? KS + sk[1] : 0; \
-    AH0 = *reinterpret_cast<const uint4*>(ah[0] + c0);                                  \
-    AH1 = *reinterpret_cast<const uint4*>(ah[1] + c1);                                  \
-    AL0 = *reinterpret_cast<const uint4*>(al[0] + c0);                                  \
-    AL1 = *reinterpret_cast<const uint4*>(al[1] + c1);                                  \
-    W0 = *reinterpret_cast<const uint4*>(wr[0] + c0);                                   \
-    W1 = *reinterpret_cast<const uint4*>(wr[1] + c1);                                   \
+    ks[S] = (K);                                                                        \
+    _Pragma("unroll") for (int i = 0; i < XG; ++i) {                                    \
+      const int64_t c = ks[S] + xk[i] < ke ? ks[S] + xk[i] : 0;                         \
+      xh[S][i] = *reinterpret_cast<const uint4*>(ah[i] + c);                            \
+      xl[S][i] = *reinterpret_cast<const uint4*>(al[i] + c);                            \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < WG; ++i) {                                    \
+      const int64_t c = ks[S] + wk[i] < ke ? ks[S] + wk[i] : 0;                         \
+      wv[S][i] = *reinterpret_cast<const uint4*>(wr[i] + c);                            \
+    }                                                                                   \
   }
-#define PG_STAGE(AH0, AH1, AL0, AL1, W0, W1, KS, BUF)                                   \
+#define PG_STAGE(S, BUF)                                                                \
   {                                                                                     \
-    const uint32_t i0 = KS + sk[0] < ke ? ~0u : 0u, i1 = KS + sk[1] < ke ? ~0u : 0u;   \
-    *reinterpret_cast<uint4*>(&s_a[BUF][0][srow[0]][sk[0]]) = pg_mask(AH0, i0);         \
-    *reinterpret_cast<uint4*>(&s_a[BUF][0][srow[1]][sk[1]]) = pg_mask(AH1, i1);         \
-    *reinterpret_cast<uint4*>(&s_a[BUF][1][srow[0]][sk[0]]) = pg_mask(AL0, i0);         \
-    *reinterpret_cast<uint4*>(&s_a[BUF][1][srow[1]][sk[1]]) = pg_mask(AL1, i1);         \
-    *reinterpret_cast<uint4*>(&s_w[BUF][srow[0]][sk[0]]) = pg_mask(W0, i0);             \
-    *reinterpret_cast<uint4*>(&s_w[BUF][srow[1]][sk[1]]) = pg_mask(W1, i1);             \
+    _Pragma("unroll") for (int i = 0; i < XG; ++i) {                                    \
+      const uint32_t in = ks[S] + xk[i] < ke ? ~0u : 0u;                                \
+      *reinterpret_cast<uint4*>(&s_a[BUF][0][xrow[i]][xk[i]]) = pg_mask(xh[S][i], in);   \
+      *reinterpret_cast<uint4*>(&s_a[BUF][1][xrow[i]][xk[i]]) = pg_mask(xl[S][i], in);   \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < WG; ++i) {                                    \
+      const uint32_t in = ks[S] + wk[i] < ke ? ~0u : 0u;                                \
+      *reinterpret_cast<uint4*>(&s_w[BUF][wrow[i]][wk[i]]) = pg_mask(wv[S][i], in);      \
+    }                                                                                   \
   }
 
-  pg_f32x4_t acc[4][4];
+  pg_f32x4_t acc[4][TN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = pg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < TN; ++j) acc[i][j] = pg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int orow = lane & 15, ok8 = (lane >> 4) * 8;
   auto multiply = [&](int buf) {
-    uint4 wop[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wop[j] = *reinterpret_cast<const uint4*>(&s_w[buf][wn * 64 + j * 16 + orow][ok8]);
+    for (int kk = 0; kk < BK; kk += 32) {
+      uint4 wop[TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 xh = *reinterpret_cast<const uint4*>(&s_a[buf][0][wm * 64 + i * 16 + orow][ok8]);
-      const uint4 xl = *reinterpret_cast<const uint4*>(&s_a[buf][1][wm * 64 + i * 16 + orow][ok8]);
+      for (int j = 0; j < TN; ++j)
+        wop[j] = *reinterpret_cast<const uint4*>(&s_w[buf][wn * (16 * TN) + j * 16 + orow][kk + ok8]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = pg_mfma(xh, wop[j], acc[i][j]);
-        acc[i][j] = pg_mfma(xl, wop[j], acc[i][j]);
+      for (int i = 0; i < 4; ++i) {
+        const uint4 ah_ = *reinterpret_cast<const uint4*>(&s_a[buf][0][wm * 64 + i * 16 + orow][kk + ok8]);
+        const uint4 al_ = *reinterpret_cast<const uint4*>(&s_a[buf][1][wm * 64 + i * 16 + orow][kk + ok8]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = pg_mfma(ah_, wop[j], acc[i][j]);
+          acc[i][j] = pg_mfma(al_, wop[j], acc[i][j]);
+        }
       }
     }
   };
@@ -132,20 +157,20 @@ __global__ __launch_bounds__(PG_THREADS, 1) void pgemm_kernel(const PgemmParams 
   // buffer, which was last read before the previous barrier
   // loads are issued every step (a slice past the last one reads the first again and is never staged), so
   // each set's registers live only from its load to its staging
-  auto kof = [&](int i) { return i < nk ? kb + (int64_t)i * PG_BK : kb; };
-  PG_LOAD(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, kb)
-  PG_LOAD(a1h0, a1h1, a1l0, a1l1, w10, w11, k1s, kof(1))
-  if (nk > 0) PG_STAGE(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, 0)
+  auto kof = [&](int i) { return i < nk ? kb + (int64_t)i * BK : kb; };
+  PG_LOAD(0, kb)
+  PG_LOAD(1, kof(1))
+  if (nk > 0) PG_STAGE(0, 0)
   __syncthreads();
   for (int it = 0; it < nk; it += 2) {
-    PG_LOAD(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, kof(it + 2))
+    PG_LOAD(0, kof(it + 2))
     multiply(0);
-    if (it + 1 < nk) PG_STAGE(a1h0, a1h1, a1l0, a1l1, w10, w11, k1s, 1)
+    if (it + 1 < nk) PG_STAGE(1, 1)
     __syncthreads();
     if (it + 1 < nk) {
-      PG_LOAD(a1h0, a1h1, a1l0, a1l1, w10, w11, k1s, kof(it + 3))
+      PG_LOAD(1, kof(it + 3))
       multiply(1);
-      if (it + 2 < nk) PG_STAGE(a0h0, a0h1, a0l0, a0l1, w00, w01, k0s, 0)
+      if (it + 2 < nk) PG_STAGE(0, 0)
       __syncthreads();
     }
   }
@@ -157,8 +182,8 @@ __global__ __launch_bounds__(PG_THREADS, 1) void pgemm_kernel(const PgemmParams 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + orow;
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = n0 + wn * (16 * TN) + j * 16 + orow;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
@@ -237,20 +262,29 @@ __global__ __launch_bounds__(256) void pgemm_epilogue4_kernel(const PgemmParams 
   }
 }
 
+// rows per tile: 64 for up to 64 rows (a decode batch, a short last prompt chunk), else 128; k per slice
+static int pg_bm(int32_t M) { return M <= 64 ? 64 : PG_BM; }
+static int pg_bk(int32_t M) { return M <= 64 ? PG_BK64 : PG_BK; }
+
 void pgemm_plan(PgemmParams& p, int target_blocks) {
-  const int64_t tiles = ((p.N + PG_BN - 1) / PG_BN) * ((p.M + PG_BM - 1) / PG_BM);
+  const int64_t tiles = ((p.N + PG_BN - 1) / PG_BN) * ((p.M + pg_bm(p.M) - 1) / pg_bm(p.M));
   int64_t ks = (target_blocks + tiles - 1) / tiles;
-  const int64_t steps = (p.K + PG_BK - 1) / PG_BK;
+  const int bk = pg_bk(p.M);
+  const int64_t steps = (p.K + bk - 1) / bk;
   ks = std::max<int64_t>(1, std::min<int64_t>(ks, steps / 8));   // at least 8 k slices per split
-  int64_t slice = (steps + ks - 1) / ks * PG_BK;
+  int64_t slice = (steps + ks - 1) / ks * bk;
   p.kslice = slice;
   p.ksplit = (int32_t)((p.K + slice - 1) / slice);
 }
 
 hipError_t pgemm_launch(const PgemmParams& p, int mode, hipStream_t s) {
-  if (p.M < 1 || p.K % 8 != 0 || p.kslice % PG_BK != 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((p.N + PG_BN - 1) / PG_BN), (unsigned)((p.M + PG_BM - 1) / PG_BM), (unsigned)p.ksplit);
-  hipLaunchKernelGGL(pgemm_kernel, grid, dim3(PG_THREADS), 0, s, p);
+  if (p.M < 1 || p.K % 8 != 0 || p.kslice % pg_bk(p.M) != 0) return hipErrorInvalidValue;
+  const int bm = pg_bm(p.M);
+  const dim3 grid((unsigned)((p.N + PG_BN - 1) / PG_BN), (unsigned)((p.M + bm - 1) / bm), (unsigned)p.ksplit);
+  if (bm == 64)
+    hipLaunchKernelGGL((pgemm_kernel<64, PG_BK64>), grid, dim3(PG_THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL((pgemm_kernel<128, PG_BK>), grid, dim3(PG_THREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mode == PG_NONE) return e;
   const int64_t cols = mode == PG_GATEUP ? p.N / 2 : p.N;
