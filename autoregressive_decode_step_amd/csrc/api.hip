@@ -613,9 +613,6 @@ bool step_shape_ok(const llmk_config* c, int nwg) {
 // Workgroups of the persistent step for this call (0: run one kernel per operation). -1: refused.
 int step_workgroups(const llmk_config* c) {
   if (c->step_path == LLMK_STEP_PER_OP || c->kv_dtype == LLMK_Q8) return 0;   // the int8 cache: per operation
-  // int8 packs take the persistent step only when asked for: one kernel per operation streams them faster
-  // (2.655 against 2.694 ms per Llama-3.1-8B step at batch 1)
-  if (c->w_dtype == LLMK_Q8 && c->step_path != LLMK_STEP_PERSISTENT) return 0;
   int nwg = step_grid(c->kv_dtype == LLMK_BF16, (int)c->head_dim, c->w_dtype == LLMK_Q8);
   if (nwg > kStepMaxWG || !step_shape_ok(c, nwg)) nwg = 0;
   if (nwg == 0 && c->step_path == LLMK_STEP_PERSISTENT) return -1;

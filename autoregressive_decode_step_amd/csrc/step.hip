@@ -42,7 +42,7 @@ namespace llmk {
 
 constexpr int SK_THREADS = ATTN_THREADS;   // 512: 8 waves
 constexpr int SK_WAVES = SK_THREADS / 64;
-constexpr int SK_R = 16;                    // weight loads in flight per lane
+constexpr int SK_R = 8;                     // weight loads in flight per lane
 constexpr int SK_SEG = 512;                 // elements of one wave load (64 lanes x 8 bf16)
 // int8 weight packs (QW): a lane loads 16 codes, so a wave load covers 1,024 elements of a row, and every
 // 16 codes of a lane lie in one group of SK_QG inputs with its own fp32 scale

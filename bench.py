@@ -36,7 +36,8 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 N_PRE = 4096                    # filled context before the first timed step
 PMC_FILES = {"gate_up": os.path.join(ROOT, "profiles", "rowdot_gate_up_llama8b_pmc.md"),
              "step": os.path.join(ROOT, "profiles", "step_kernel_llama8b_pmc.md"),
-             "gate_up_q8": os.path.join(ROOT, "profiles", "rowdot_q8_gate_up_llama8b_pmc.md")}
+             "gate_up_q8": os.path.join(ROOT, "profiles", "rowdot_q8_gate_up_llama8b_pmc.md"),
+             "step_q8": os.path.join(ROOT, "profiles", "step_kernel_q8_llama8b_pmc.md")}
 STEP_REPS = 64                  # consecutive steps in the persistent kernel's event timing
 
 
@@ -94,7 +95,8 @@ def gate_up_bytes(s, q8: bool = False) -> int:
 
 KERNEL_SOURCES = {"gate_up": ("rowdot.hip", "common.h", "kernels.h"),
                   "step": ("step.hip", "attn_block.h", "common.h", "kernels.h"),
-                  "gate_up_q8": ("q8.hip", "q8.h", "common.h", "kernels.h")}
+                  "gate_up_q8": ("q8.hip", "q8.h", "common.h", "kernels.h"),
+                  "step_q8": ("step.hip", "attn_block.h", "common.h", "kernels.h")}
 
 
 def kernel_source_sha(which: str = "gate_up") -> str:
@@ -106,7 +108,7 @@ def kernel_source_sha(which: str = "gate_up") -> str:
 
 
 def traffic_from_profiles(which: str):
-    """HBM bytes per launch of the dominant kernel (`which`: gate_up or step) from the committed counter
+    """HBM bytes per launch of the dominant kernel (`which`: a PMC_FILES key) from the committed counter
     summary ("key: value" lines), if its counters were taken on the current kernel source; None otherwise."""
     rec = {}
     try:
@@ -465,7 +467,7 @@ def main() -> int:
             raise RuntimeError(f"decode_kernel_time(step): {st} {llmk.status_name(st)}")
         pool.slot_len[0] = N_PRE
         avg_ms["step"] = ms
-        k_bytes = sum(step_bytes(s, N_PRE + 1 + i) for i in range(STEP_REPS)) / STEP_REPS
+        k_bytes = sum(step_bytes(s, N_PRE + 1 + i, q8) for i in range(STEP_REPS)) / STEP_REPS
         k_name = "persistent decode step (step_kernel, the whole step in one launch)"
         kernel_sum_ms = ms
     else:
@@ -513,7 +515,8 @@ def main() -> int:
         "step_form": "persistent" if persistent else "per-op",
         "roofline": {"bound": "hbm", "kernel": k_name,
                      "achieved": k_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": k_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic_from_profiles("step" if persistent else "gate_up_q8" if q8 else "gate_up"),
+                     "traffic": traffic_from_profiles(("step_q8" if q8 else "step") if persistent else
+                                                      ("gate_up_q8" if q8 else "gate_up")),
                      "bytes_per_launch": k_bytes, "avg_launch_us": ms * 1e3},
         "kernels_avg_us": {n: v * 1e3 for n, v in avg_ms.items()},
         "kernel_sum_ms_per_step": kernel_sum_ms,

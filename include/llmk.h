@@ -94,11 +94,10 @@ typedef enum { LLMK_W_IN_OUT = 0, LLMK_W_OUT_IN = 1 } llmk_weight_layout;
  * (the same arithmetic up to the order of fp32 sums). The persistent form needs bf16 weights in
  * LLMK_W_OUT_IN (or int8 packs with head_dim 64..256), a bf16 or fp32 K/V cache, and a device that holds
  * one of its workgroups per CU.
- *   LLMK_STEP_AUTO       the persistent kernel where it can run, else one kernel per operation; int8
- *                        packs take one kernel per operation (they stream faster that way)
+ *   LLMK_STEP_AUTO       the persistent kernel where it can run, else one kernel per operation
  *   LLMK_STEP_PER_OP     one kernel per operation: 5 per layer (q|k|v, attention, o, gate|up, down) + head
- *   LLMK_STEP_PERSISTENT one kernel per step, the operations separated by grid barriers; refused (578)
- *                        where it cannot run */
+ *   LLMK_STEP_PERSISTENT one kernel per step, each operation waiting for the tagged outputs of the one
+ *                        before it; refused (578) where it cannot run */
 typedef enum { LLMK_STEP_AUTO = 0, LLMK_STEP_PER_OP = 1, LLMK_STEP_PERSISTENT = 2 } llmk_step_path;
 
 /* ------------------------------------------------------------------------- */

@@ -78,7 +78,7 @@ def _q8_case(s, n_pre, n_steps, f64, label):
     say(f"{label}: GPU upload and quantization")
     cfgs = {path: loader.config_from(s.with_(w_dtype="q8"), step_path=path)
             for path in (llmk.STEP_PER_OP, llmk.STEP_PERSISTENT)}
-    assert llmk.decode_path(loader.config_from(s.with_(w_dtype="q8"))) == llmk.STEP_PER_OP   # auto: per-op streams packs faster
+    assert llmk.decode_path(loader.config_from(s.with_(w_dtype="q8"))) == llmk.STEP_PERSISTENT   # auto: where it runs
     model = loader.upload_model(cfgs[llmk.STEP_PER_OP], W)
 
     def new_dec(cfg):
