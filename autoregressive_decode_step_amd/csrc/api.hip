@@ -204,12 +204,12 @@ struct DecodePlan {
   unsigned* step_cnt = nullptr;         // the head's ticket
   float* step_val = nullptr;            // [kStepMaxWG] per-workgroup best logit
   int32_t* step_idx = nullptr;
-  uint64_t* step_tagged = nullptr;      // the tagged activations below, one region cleared per call
-  int64_t step_tagged_n = 0;
-  uint64_t* step_x = nullptr;           // (value, tag) activations of the persistent step (see StepParams)
-  uint64_t* step_qkv = nullptr;
-  uint64_t* step_att = nullptr;
-  uint64_t* step_u = nullptr;
+  uint32_t* step_tagged = nullptr;      // the tagged activations and parts below, one region cleared per call
+  int64_t step_tagged_words = 0;        // its 4-byte words
+  uint32_t* step_x = nullptr;           // tagged activations of the persistent step (see StepParams)
+  uint32_t* step_qkv = nullptr;
+  uint32_t* step_att = nullptr;
+  uint32_t* step_u = nullptr;
   uint64_t* step_part = nullptr;        // attention parts as (value, tag) pairs
   int64_t step_x_stride = 0, step_qkv_stride = 0, step_att_stride = 0, step_u_stride = 0;
   int64_t bytes = 0;
@@ -300,13 +300,14 @@ void plan_decode(const llmk_config* c, void* ws, DecodePlan& D) {
   const int64_t nx = 2 * c->n_layer * D.step_x_stride, nq = c->n_layer * D.step_qkv_stride;
   const int64_t na = c->n_layer * D.step_att_stride, nu = c->n_layer * D.step_u_stride;
   const int64_t np = attn_part_floats(c->n_head, c->head_dim);
-  D.step_tagged_n = nx + nq + na + nu + np;
-  D.step_tagged = cv.take<uint64_t>(D.step_tagged_n);
+  // activations (4 bytes each, every stride a multiple of 32), then the parts (8 bytes each), contiguous
+  D.step_tagged_words = nx + nq + na + nu + 2 * np;
+  D.step_tagged = cv.take<uint32_t>(D.step_tagged_words);
   D.step_x = D.step_tagged;
   D.step_qkv = D.step_x + nx;
   D.step_att = D.step_qkv + nq;
   D.step_u = D.step_att + na;
-  D.step_part = D.step_u + nu;
+  D.step_part = reinterpret_cast<uint64_t*>(D.step_u + nu);
   D.bytes = cv.off;
 }
 
@@ -625,7 +626,7 @@ hipError_t step_prelude(const llmk_config* c, const llmk_model* m, const llmk_kv
                         int32_t token, int32_t pos, hipStream_t s) {
   hipError_t e = fill_u32_launch(D.step_cnt, 1, 0u, s);
   if (e == hipSuccess) e = fill_u32_launch(reinterpret_cast<unsigned*>(D.step_err), 4, 0u, s);
-  if (e == hipSuccess) e = fill_u32_launch(reinterpret_cast<unsigned*>(D.step_tagged), 2 * D.step_tagged_n, 0u, s);
+  if (e == hipSuccess) e = fill_u32_launch(D.step_tagged, D.step_tagged_words, 0u, s);
   if (e == hipSuccess) e = set_state_launch(D.state, token, pos, s);
   for (int64_t l0 = 0; e == hipSuccess && l0 < c->n_layer; l0 += 8) {
     StepTableChunk ch{};

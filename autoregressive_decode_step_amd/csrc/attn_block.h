@@ -72,6 +72,21 @@ __device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
 __device__ __forceinline__ uint32_t tag_of(uint64_t v) { return (uint32_t)(v >> 32); }
 __device__ __forceinline__ float val_of(uint64_t v) { return __uint_as_float((uint32_t)v); }
 
+// Activations of the persistent step (x, q|k|v, the attention output, u) carry their tag in the two low
+// mantissa bits of the fp32 value: 1 + the parity of the step within the call. Every such value is written
+// once per step and the buffers are cleared (0) before a call, so a reader sees the current step's tag only
+// on the current step's value. Dropping the two bits changes a value by less than 2^-21 of it; the hand-off
+// moves 4 bytes a value instead of 8.
+__device__ __forceinline__ uint32_t act_tag(uint32_t step) { return 1u + (step & 1u); }
+__device__ __forceinline__ void st_act(uint32_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, (__float_as_uint(v) & ~3u) | tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_act(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool act_has(uint32_t b, uint32_t tag) { return (b & 3u) == tag; }
+__device__ __forceinline__ float act_val(uint32_t b) { return __uint_as_float(b & ~3u); }
+
 // Bounded wait: false once the wait has lasted longer than `ticks` of the 100 MHz real-time counter or
 // another workgroup has given up (*err != 0); then *err is set, so every other waiter stops too.
 constexpr uint64_t TAG_WAIT_TICKS = 20000000ull;   // 200 ms
@@ -91,8 +106,8 @@ __device__ __forceinline__ bool tag_wait_more(int32_t* err, uint64_t t0, unsigne
 // for a single sequence). Every thread of the workgroup (ATTN_THREADS) must call it with the same
 // arguments; it returns at the same point for all of them. `tiles` is LDS of attn_tile_vecs<T, HD>()
 // 16-byte vectors.
-// TAG: the decode step's persistent form. q|k|v come as (value, tag) pairs from p.qkv_tag and are waited
-// for until they carry p.tag; the merged output goes to p.out_tag as (value, p.tag) pairs.
+// TAG: the decode step's persistent form. q|k|v come as tagged activations from p.qkv_tag and are waited
+// for until they carry p.tag; the merged output goes to p.out_tag tagged with p.tag.
 template <typename T, int HD, bool TAG = false>
 __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, const int part, const int row,
                                            uint4* tiles) {
@@ -252,7 +267,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     // a thread's values (at most QW of them, G <= 8 and HD <= 256) are loaded together and every one not yet
     // carrying the tag is reloaded in the same round
     constexpr int QW = (10 * HDP + ATTN_THREADS - 1) / ATTN_THREADS;
-    uint64_t got[QW];
+    uint32_t got[QW];
     int64_t gidx[QW];
 #pragma unroll
     for (int k = 0; k < QW; ++k) {
@@ -260,12 +275,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       const int g = i / HD, e = i % HD;
       gidx[k] = g < G ? (int64_t)(kvh * G + g) * HD + e
                       : (int64_t)(p.H + (g - G) * p.Hkv) * HD + (int64_t)kvh * HD + e;
-      got[k] = i < nval ? ld_tag(p.qkv_tag + gidx[k]) : ((uint64_t)p.tag << 32);
+      got[k] = i < nval ? ld_act(p.qkv_tag + gidx[k]) : p.tag;
     }
     for (;;) {
       bool ready = true;
 #pragma unroll
-      for (int k = 0; k < QW; ++k) ready = ready && tag_of(got[k]) == p.tag;
+      for (int k = 0; k < QW; ++k) ready = ready && act_has(got[k], p.tag);
       if (ready || fl_failed) break;
       __builtin_amdgcn_s_sleep(8);   // about 0.2 us between reloads
       if (!tag_wait_more(p.err, t0, spins)) {
@@ -274,12 +289,12 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
       }
 #pragma unroll
       for (int k = 0; k < QW; ++k)
-        if (tag_of(got[k]) != p.tag) got[k] = ld_tag(p.qkv_tag + gidx[k]);
+        if (!act_has(got[k], p.tag)) got[k] = ld_act(p.qkv_tag + gidx[k]);
     }
 #pragma unroll
     for (int k = 0; k < QW; ++k) {
       const int i = threadIdx.x + k * ATTN_THREADS;
-      if (i < nval) s_raw[i] = val_of(got[k]);
+      if (i < nval) s_raw[i] = act_val(got[k]);
     }
     __syncthreads();
   }
@@ -600,7 +615,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     }
     const int64_t oi = (int64_t)(kvh * G + g) * HD + e;
     if constexpr (TAG) {
-      st_tag(p.out_tag + oi, O / L, p.tag);
+      st_act(p.out_tag + oi, O / L, p.tag);
     } else if (p.out_hi) {
       bf16_t hi, lo;
       split_bf16(O / L, hi, lo);
@@ -614,7 +629,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
 
 // TAG form of the merge: query head g of K/V head kvh, by a workgroup of its own. It waits for the
 // (max, sum, output) of all n_parts parts to carry p.part_tag, combines them by log-sum-exp and writes the
-// head's output as (value, p.tag) pairs. Thread t takes output element t % HD over the parts
+// head's output as activations tagged p.tag. Thread t takes output element t % HD over the parts
 // c = t / HD, t / HD + NS, ... (NS = ATTN_THREADS / HD subsets); the subsets are combined in order through
 // LDS. Every thread of the workgroup must call it.
 template <int HD>
@@ -694,7 +709,7 @@ __device__ __forceinline__ void attn_merge_tagged(const AttnParams& p, const int
       LL = fmaf(s_l[q * HD + e], w, LL);
       OO = fmaf(s_o[q * HD + e], w, OO);
     }
-    st_tag(p.out_tag + (int64_t)(kvh * G + g) * HD + e, OO / LL, p.tag);
+    st_act(p.out_tag + (int64_t)(kvh * G + g) * HD + e, OO / LL, p.tag);
   }
   __syncthreads();
 }

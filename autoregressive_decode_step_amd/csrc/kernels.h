@@ -225,10 +225,11 @@ struct AttnParams {
   int64_t qkv_stride;
   bf16_t* out_hi;
   bf16_t* out_lo;
-  // persistent decode step (tagged form): q|k|v and the output as (value, tag) pairs, see attn_block
-  const uint64_t* qkv_tag;
-  uint64_t* out_tag;
-  uint32_t tag;
+  // persistent decode step (tagged form): q|k|v and the output as tagged activations (act_tag in the two
+  // low mantissa bits, see attn_block), the parts as (value, part_tag) pairs
+  const uint32_t* qkv_tag;
+  uint32_t* out_tag;
+  uint32_t tag;                // the activations' tag of this step (1 or 2; 3, which no step writes: give-up tests)
   uint32_t part_tag;           // the parts' tag: unique per (step, layer), the part buffer serves every layer
   uint64_t* part_tagged;       // [Hkv][n_parts][G][hd + 2] (value, part_tag) pairs
   int32_t* err;
@@ -269,13 +270,13 @@ struct StepParams {
   int32_t give_up;              // test only: the attention waits for a tag nobody writes (bounded-wait path)
   int32_t qw;                   // the projections and the head are int8 packs (layers' w[] and w_out point at packs)
   DecodeState* state;
-  // activations as (value, tag) pairs, tag = step within the call + 1; cleared before each call.
+  // activations as tagged fp32 words (act_tag(step) in the two low mantissa bits); cleared before each call.
   // x [2 n_layer][x_stride]: x after layer l's o (2l) and after its down (2l + 1); q|k|v, attention
   // output and u [n_layer][*_stride]
-  uint64_t* x;
-  uint64_t* qkv;
-  uint64_t* att;
-  uint64_t* u;
+  uint32_t* x;
+  uint32_t* qkv;
+  uint32_t* att;
+  uint32_t* u;
   int64_t x_stride, qkv_stride, att_stride, u_stride;
   uint64_t* attn_part;          // [Hkv][ATTN_MAX_PARTS][G][hd + 2] (value, tag) pairs, tag unique per layer
   float* logits;                // optional [V]

@@ -17,11 +17,12 @@
 // last row, from cache, and is not used), so ring slot indices are compile-time constants.
 //
 // Hand-off without barriers. Every activation one workgroup writes and another reads (q|k|v, the
-// attention output, x after each residual add, u) is stored as 8-byte (value, tag) pairs, the tag being
-// the step's number within the call plus one. A reader loads what it needs with device-scope loads (past
-// the non-coherent L2 of its XCD) and reloads until every pair carries the current tag: the data itself
-// is the signal, so a dependency costs one round trip and no writer ever waits for its stores. The
-// buffers are cleared before each call. Every wait is bounded (200 ms of the real-time counter); a
+// attention output, x after each residual add, u) is stored as an fp32 word whose two low mantissa bits
+// hold a tag, 1 + the parity of the step within the call (the attention's partial results, whose count
+// changes with the context, as 8-byte (value, tag) pairs with a tag per step and layer). A reader loads
+// what it needs with device-scope loads (past the non-coherent L2 of its XCD) and reloads until every value
+// carries the current tag: the data itself is the signal, so a dependency costs one round trip and no
+// writer ever waits for its stores. The buffers are cleared before each call. Every wait is bounded (200 ms of the real-time counter); a
 // workgroup that gives up sets an error flag that stops every other waiter, and the host reports a device
 // error.
 //
@@ -241,10 +242,10 @@ __device__ __forceinline__ int sk_vin_pos(int e) {
 }
 
 // Stage an input vector of n fp32 values into LDS (permuted; zeros up to the padded row length npad):
-// src_tag = (value, tag) pairs waited for, or src_emb = a bf16 row (no wait). gain: multiply by it.
+// src_tag = tagged activations waited for, or src_emb = a bf16 row (no wait). gain: multiply by it.
 // res: copy elements [res_lo, res_lo + res_n) unmultiplied to res. Returns this thread's sum of squares.
 template <bool QW>
-__device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t* src_emb, int n, int npad,
+__device__ __forceinline__ float sk_stage(const uint32_t* src_tag, const bf16_t* src_emb, int n, int npad,
                                           uint32_t tag, const float* gain, float* res, int res_lo, int res_n,
                                           float* vin, int32_t* err, bool& failed) {
   const int t = threadIdx.x;
@@ -273,26 +274,26 @@ __device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t*
         }
       }
     } else {
-      // device-scope 16-byte loads (sc1), two (value, tag) pairs each; past n the loads return zeros
+      // device-scope 16-byte loads (sc1), four tagged values each; past n the loads return zeros
       __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(src_tag), (short)0, n * 8, 0x00020000);
-      uint4 a[SK_PASS], b[SK_PASS];
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src_tag), (short)0, n * 4, 0x00020000);
+      uint4 a[SK_PASS];
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       unsigned spins = 0;
       for (;;) {
 #pragma unroll
         for (int k = 0; k < SK_PASS; ++k) {
           if (k0 + k < ng) {
-            const int off = 32 * (t + (k0 + k) * SK_THREADS);
+            const int off = 16 * (t + (k0 + k) * SK_THREADS);
             a[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16));
-            b[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 16));
           }
         }
         bool ready = true;
 #pragma unroll
         for (int k = 0; k < SK_PASS; ++k) {
           const int e = 4 * (t + (k0 + k) * SK_THREADS);
-          if (k0 + k < ng && e < n) ready = ready && a[k].y == tag && a[k].w == tag && b[k].y == tag && b[k].w == tag;
+          if (k0 + k < ng && e < n)
+            ready = ready && act_has(a[k].x, tag) && act_has(a[k].y, tag) && act_has(a[k].z, tag) && act_has(a[k].w, tag);
         }
         if (ready || failed) break;
         __builtin_amdgcn_s_sleep(8);   // about 0.2 us between reloads of a whole vector
@@ -303,10 +304,10 @@ __device__ __forceinline__ float sk_stage(const uint64_t* src_tag, const bf16_t*
       }
 #pragma unroll
       for (int k = 0; k < SK_PASS; ++k) {
-        v[k][0] = __uint_as_float(a[k].x);
-        v[k][1] = __uint_as_float(a[k].z);
-        v[k][2] = __uint_as_float(b[k].x);
-        v[k][3] = __uint_as_float(b[k].z);
+        v[k][0] = act_val(a[k].x);
+        v[k][1] = act_val(a[k].y);
+        v[k][2] = act_val(a[k].z);
+        v[k][3] = act_val(a[k].w);
       }
     }
 #pragma unroll
@@ -348,12 +349,12 @@ __device__ __forceinline__ float sk_block_sum(float x, float* s_red) {
 
 // where one op's row results go
 struct SkOut {
-  uint64_t* y;        // QKV: q|k|v of the layer; O/DN: the new x version; GU: u of the layer
+  uint32_t* y;        // QKV: q|k|v of the layer; O/DN: the new x version; GU: u of the layer
   const float* res;   // O/DN: the workgroup's residual rows of the old x (LDS)
   float* hidden;      // DN: optional copy of x, this layer's row
   float* logits;      // HEAD: optional
   float scale;        // RMSNorm scale of the op's input (1 when there is no norm)
-  uint32_t tag;
+  uint32_t tag;       // act_tag of the step
 };
 
 // Row results of one wave, lane-parallel: wave-local row r's dot product is in lane r of y (r < 64) or
@@ -369,7 +370,7 @@ __device__ __forceinline__ void sk_rows_out(float y, float y2, const Op& f, cons
       const int r = lane + 64 * h;
       if ((lane & 1) == 0 && r < f.nrows) {
         const float g = (h ? y2 : y) * out.scale, u = (h ? up2 : up) * out.scale;
-        st_tag(out.y + R.f.lo + wave + SK_WAVES * (r >> 1), silu_f(g) * u, out.tag);
+        st_act(out.y + R.f.lo + wave + SK_WAVES * (r >> 1), silu_f(g) * u, out.tag);
       }
     }
   } else if constexpr (KIND == OP_HEAD) {
@@ -403,10 +404,10 @@ __device__ __forceinline__ void sk_rows_out(float y, float y2, const Op& f, cons
         if constexpr (KIND == OP_QKV) {
           const int idx = q < f.n0 ? R.q.lo + q
                                    : (q < f.n01 ? p.qd + R.k.lo + (q - f.n0) : p.qd + p.kvd + R.v.lo + (q - f.n01));
-          st_tag(out.y + idx, v * out.scale, out.tag);
+          st_act(out.y + idx, v * out.scale, out.tag);
         } else {
           const float xn = out.res[q] + v;
-          st_tag(out.y + R.d.lo + q, xn, out.tag);
+          st_act(out.y + R.d.lo + q, xn, out.tag);
           if (KIND == OP_DN && out.hidden) out.hidden[R.d.lo + q] = xn;
         }
       }
@@ -525,7 +526,7 @@ __device__ __forceinline__ AttnParams sk_attn_params(const StepParams& p, int l,
   ap.pg.shift = p.kv_shift;
   ap.qkv_tag = p.qkv + (int64_t)l * p.qkv_stride;
   ap.out_tag = p.att + (int64_t)l * p.att_stride;
-  ap.tag = p.give_up ? (tag | 0x80000000u) : tag;   // a tag no workgroup writes (tests of the give-up path)
+  ap.tag = p.give_up ? 3u : act_tag(tag - 1u);   // 3: a tag no workgroup writes (tests of the give-up path)
   ap.err = p.err;
   return ap;
 }
@@ -582,7 +583,8 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
   const int step = p.state->step;
   const int tok = p.state->token;
   const int pos = p.state->pos;
-  const uint32_t tag = (uint32_t)step + 1u;
+  const uint32_t tag = (uint32_t)step + 1u;      // the attention parts' (with the layer)
+  const uint32_t atag = act_tag((uint32_t)step);  // the activations'  
   bool failed = false;
 
   for (int i = threadIdx.x; i < L; i += SK_THREADS) {
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
     if (f.kind == OP_O) sk_attention_merges<T, HD>(&p, f.l, pos, tag);
     // ---- the op's input ----
     SkOut out;
-    out.tag = tag;
+    out.tag = atag;
     out.scale = 1.0f;
     out.res = s_res;
     out.hidden = nullptr;
@@ -639,16 +641,16 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
     const int npad = sk_seg<QW>() << f.sh;
     if (f.kind == OP_O) {
       __syncthreads();
-      sk_stage<QW>(SK_ATT(f.l), nullptr, p.qd, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
+      sk_stage<QW>(SK_ATT(f.l), nullptr, p.qd, npad, atag, nullptr, nullptr, 0, 0, vin, p.err, failed);
       out.y = SK_X(2 * f.l);
     } else if (f.kind == OP_DN) {
       __syncthreads();
-      sk_stage<QW>(SK_U(f.l), nullptr, p.F, npad, tag, nullptr, nullptr, 0, 0, vin, p.err, failed);
+      sk_stage<QW>(SK_U(f.l), nullptr, p.F, npad, atag, nullptr, nullptr, 0, 0, vin, p.err, failed);
       out.y = SK_X(2 * f.l + 1);
       out.hidden = p.hidden ? p.hidden + (int64_t)f.l * p.d : nullptr;
     } else {
       // RMSNorm inputs: x before layer l (the embedding row for layer 0), x after layer l's o, final x
-      const uint64_t* src = nullptr;
+      const uint32_t* src = nullptr;
       const bf16_t* emb = nullptr;
       const float* gain;
       if (f.kind == OP_QKV) {
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
         out.y = nullptr;
       }
       __syncthreads();
-      const float ss = sk_stage<QW>(src, emb, p.d, npad, tag, gain, f.kind == OP_HEAD ? nullptr : s_res, R.d.lo, R.d.n,
+      const float ss = sk_stage<QW>(src, emb, p.d, npad, atag, gain, f.kind == OP_HEAD ? nullptr : s_res, R.d.lo, R.d.n,
                                 vin, p.err, failed);
       out.scale = 1.0f / sqrtf(sk_block_sum(ss, s_red) / (float)p.d + p.eps);
     }
