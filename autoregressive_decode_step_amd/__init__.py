@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libllmk.so")
 OK = 560
 CACHE_LENGTH_MISMATCH = 566
 CACHE_CAPACITY_EXCEEDED = 571
+INVALID_ARGUMENT = 578
 DEVICE_ERROR = 579
 F32, BF16, Q8 = 0, 1, 2
 Q8_GROUP = 128

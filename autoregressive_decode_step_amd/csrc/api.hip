@@ -608,7 +608,12 @@ bool step_shape_ok(const llmk_config* c, int nwg) {
   if (c->d % 8 || qd % 8 || c->hidden % 8) return false;
   if (std::max(std::max(c->d, qd), c->hidden) > STEP_MAX_VIN) return false;
   if (c->n_head / c->n_kv > 8) return false;
-  return nwg > 0 && (c->d + nwg - 1) / nwg <= STEP_MAX_RES;
+  if (nwg <= 0) return false;
+  // a workgroup's rows of each projection: the residual rows it keeps, and at most STEP_MAX_WAVE_ROWS a wave
+  auto most = [nwg](int64_t n) { return (n + nwg - 1) / nwg; };
+  const int64_t kvd = c->n_kv * c->head_dim, wg_rows = (int64_t)STEP_MAX_WAVE_ROWS * 8;
+  if (most(c->d) > STEP_MAX_RES) return false;
+  return most(qd) + 2 * most(kvd) <= wg_rows && 2 * most(c->hidden) <= wg_rows && most(c->vocab) <= wg_rows;
 }
 
 // Workgroups of the persistent step for this call (0: run one kernel per operation). -1: refused.

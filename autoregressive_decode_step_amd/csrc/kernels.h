@@ -291,6 +291,7 @@ struct StepParams {
 constexpr int STEP_MAX_LAYERS = 128;   // layers the persistent step kernel supports
 constexpr int STEP_MAX_VIN = 16384;    // longest projection input (d, H*hd, hidden) it supports
 constexpr int STEP_MAX_RES = 256;      // residual rows per workgroup (d / workgroups, rounded up) it supports
+constexpr int STEP_MAX_WAVE_ROWS = 128;  // output rows one wave of it holds (gate|up: gate and up rows count apart)
 // Workgroups the step kernel runs with on the current device (0 if it cannot hold one per CU); qw: int8 packs.
 int step_grid(int kv_is_bf16, int hd, int qw);
 hipError_t step_launch(const StepParams& p, int kv_is_bf16, hipStream_t s);

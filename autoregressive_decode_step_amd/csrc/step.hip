@@ -43,6 +43,7 @@ namespace llmk {
 
 constexpr int SK_THREADS = ATTN_THREADS;   // 512: 8 waves
 constexpr int SK_WAVES = SK_THREADS / 64;
+static_assert(SK_WAVES == 8 && STEP_MAX_WAVE_ROWS == 2 * 64, "a wave keeps its row results in two registers of 64 lanes");
 constexpr int SK_R = 8;                     // weight loads in flight per lane
 constexpr int SK_SEG = 512;                 // elements of one wave load (64 lanes x 8 bf16)
 // int8 weight packs (QW): a lane loads 16 codes, so a wave load covers 1,024 elements of a row, and every

@@ -355,3 +355,19 @@ def test_q06_full_context_matches_oracle(q06):
     toks = torch.zeros(3, dtype=torch.int32, device="cuda")
     assert dec2.steps(first, n_pre, 3, toks) == llmk.OK
     assert host(toks).tolist() == o[3]
+
+
+@pytest.mark.gpu
+def test_persistent_form_refused_past_its_rows_per_workgroup():
+    """A wave of the persistent step keeps at most 128 row results, so a vocabulary of more than 1,024 rows per
+    workgroup (here 8 x 1,024 x the CU count + 1) takes one kernel per operation, and asking for the persistent
+    form is refused (578)."""
+    import torch as _t
+    cus = _t.cuda.get_device_properties(0).multi_processor_count
+    big = TINY_BF16.with_(vocab=1024 * cus + 1)
+    auto = loader.config_from(big, llmk.W_OUT_IN)
+    assert llmk.decode_path(auto) == llmk.STEP_PER_OP
+    forced = loader.config_from(big, llmk.W_OUT_IN, llmk.STEP_PERSISTENT)
+    assert llmk.decode_path(forced) == llmk.INVALID_ARGUMENT
+    fits = TINY_BF16.with_(vocab=1024 * cus)
+    assert llmk.decode_path(loader.config_from(fits, llmk.W_OUT_IN)) == llmk.STEP_PERSISTENT
