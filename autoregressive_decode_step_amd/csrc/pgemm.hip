@@ -192,6 +192,142 @@ __global__ __launch_bounds__(PG_THREADS, BM == 64 ? 2 : 1) void pgemm_kernel(con
     }
 }
 
+// ---- decode batches (up to 64 rows): every weight byte once, straight into matrix-core operand registers ----
+//
+// With 64 rows a weight tile is used by one row block only, so nothing is gained by staging it in LDS, and a
+// tile kernel that does so keeps one 64-wide k slice of weights in flight per workgroup between its barriers
+// (about 32 KB a CU, far short of what HBM latency needs). Here each wave streams its own TN tiles of 16
+// weight rows for the split's whole k range as B operands of v_mfma_f32_16x16x32_bf16 (lane l: row l % 16,
+// k group l / 16, one 16-byte load), through a ring of 2 SG_KS TN loads that is refilled as it is read, the
+// same way the batch-1 step streams its rows: 8 waves keep 16 KB each in flight. Only the activations (64 rows
+// of bf16 hi + lo) go through LDS, in chunks of SG_KC k shared by the waves, one barrier a chunk; they are
+// re-read from L2 once per 128 TN columns. Each product is taken for hi and lo into fp32 like the tile kernel.
+constexpr int SG_THREADS = 512;
+constexpr int SG_WAVES = SG_THREADS / 64;
+constexpr int SG_KC = 128;                 // k per chunk of activations in LDS
+constexpr int SG_KS = SG_KC / 32;          // matrix-core k steps per chunk
+constexpr int SG_LDX = SG_KC + 8;          // LDS row stride of a chunk in bf16 (272 bytes)
+constexpr int SG_XV = 2 * 64 * SG_KC / 8 / SG_THREADS;   // 16-byte groups of a chunk (hi and lo) per thread
+constexpr int SG_CPT = SG_WAVES * 16;      // columns per workgroup and column tile of a wave
+
+template <int TN>
+__global__ __launch_bounds__(SG_THREADS, 1) void sgemm_kernel(const PgemmParams p) {
+  constexpr int PER = SG_KS * TN;          // ring slots a chunk takes (k step major, then column tile)
+  constexpr int RC = TN >= 4 ? 1 : 2;      // chunks of weight loads the ring holds ahead
+  constexpr int R = RC * PER;
+  __shared__ __align__(16) bf16_t s_x[2][2][64][SG_LDX];   // [buffer][hi, lo][row][k]
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t kb = (int64_t)blockIdx.z * p.kslice;
+  const int64_t ke = min(p.K, kb + p.kslice);
+  const int nc = (int)((ke - kb + SG_KC - 1) / SG_KC);
+  const int64_t nb = ((int64_t)blockIdx.x * SG_WAVES + wave) * 16 * TN;   // this wave's first column
+  // the workgroups of a split do not all start at the same k: chunk c is chunk (c + rot) % nc of the split
+  const int rot = (int)(blockIdx.x % (unsigned)nc);
+  auto chunk_k = [&](int c) { return kb + (int64_t)((c + rot) % nc) * SG_KC; };
+
+  // this lane's weight row of each column tile (rows past N read row N - 1 and are never stored) and k group
+  const bf16_t* wrow[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) wrow[j] = pg_wrow(p, nb + 16 * j + (lane & 15));
+  const int kg = 8 * (lane >> 4);
+  // weight load of k step s (counted from kb) of column tile j; past ke it reads k = 0 (its products meet
+  // activations that are zero there)
+  auto wload = [&](int s, int j) {
+    const int64_t k = chunk_k(s / SG_KS) + 32 * (int64_t)(s % SG_KS) + kg;
+    return *reinterpret_cast<const uint4*>(wrow[j] + (k < ke ? k : 0));
+  };
+
+  // activation chunk c: thread t moves groups g = t + 512 i (hi for g < 1024, then lo): row (g % 1024) / 16,
+  // k group g % 16; rows past M read row M - 1, groups past ke are zeroed when stored
+  uint4 xr[SG_XV];
+  auto xload = [&](int c) {
+    const int64_t k0 = chunk_k(c < nc ? c : 0);
+#pragma unroll
+    for (int i = 0; i < SG_XV; ++i) {
+      const int g = t + i * SG_THREADS, rem = g & 1023;
+      const int64_t m = min(rem >> 4, p.M - 1);
+      const int64_t k = k0 + 8 * (rem & 15);
+      xr[i] = *reinterpret_cast<const uint4*>((g < 1024 ? p.ahi : p.alo) + m * p.lda + (k < ke ? k : 0));
+    }
+  };
+  auto xstore = [&](int c, int buf) {
+    const int64_t k0 = c < nc ? chunk_k(c) : ke;   // past the last chunk: all zero
+#pragma unroll
+    for (int i = 0; i < SG_XV; ++i) {
+      const int g = t + i * SG_THREADS, rem = g & 1023;
+      const uint32_t in = k0 + 8 * (rem & 15) < ke ? ~0u : 0u;
+      *reinterpret_cast<uint4*>(&s_x[buf][g >> 10][rem >> 4][8 * (rem & 15)]) = pg_mask(xr[i], in);
+    }
+  };
+
+  pg_f32x4_t acc[4][TN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = pg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // prologue: chunk 0's activations, then the first two chunks' weight loads
+  uint4 ring[R];
+  xload(0);
+  xstore(0, 0);
+#pragma unroll
+  for (int q = 0; q < R; ++q) ring[q] = wload(q / TN, q % TN);   // chunks 0 .. RC - 1
+  __syncthreads();
+
+  // chunk c in buffer B, its weights in ring half H: the next chunk's activations are loaded first (so that
+  // waiting for them later waits for none of the weight loads issued after), every slot is refilled with the
+  // same slot two chunks on as soon as it is read, and loads past the last chunk re-read valid addresses
+  auto chunk = [&](int c, int B, int H) __attribute__((always_inline)) {
+    xload(c + 1);
+#pragma unroll
+    for (int s = 0; s < SG_KS; ++s) {
+      uint4 ah[4], al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ah[i] = *reinterpret_cast<const uint4*>(&s_x[B][0][16 * i + (lane & 15)][32 * s + kg]);
+        al[i] = *reinterpret_cast<const uint4*>(&s_x[B][1][16 * i + (lane & 15)][32 * s + kg]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int q = (H % RC) * PER + s * TN + j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i][j] = pg_mfma(ah[i], ring[q], acc[i][j]);
+          acc[i][j] = pg_mfma(al[i], ring[q], acc[i][j]);
+        }
+        // the refill reuses the slot's registers once its products are issued, and goes out here rather than
+        // after the chunk's products (where the scheduler would move it, and the ring would run dry each chunk)
+        ring[q] = wload((c + RC < nc ? c + RC : 0) * SG_KS + s, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    xstore(c + 1, B ^ 1);
+    __syncthreads();
+  };
+  // chunks in pairs with nothing conditional in the loop, so that every slot's wait counts exactly the loads
+  // issued after it (an odd last chunk is followed by one whose activations are all zero)
+  for (int c = 0; c < nc; c += 2) {
+    chunk(c, 0, 0);
+    chunk(c + 1, 1, 1);
+  }
+
+  // this split's partial tile: lane l holds rows 4 (l / 16) .. + 3 of each 16-row tile at column l % 16
+  float* y = p.y + (int64_t)blockIdx.z * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = nb + 16 * j + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = 16 * i + (lane >> 4) * 4 + e;
+        if (m < p.M && n < p.N) y[m * p.N + n] = acc[i][j][e];
+      }
+    }
+}
+
 // the splits' sum of element (m, n), in split order
 __device__ __forceinline__ float pg_sum(const PgemmParams& p, int64_t m, int64_t n) {
   float v = 0.0f;
@@ -266,7 +402,26 @@ __global__ __launch_bounds__(256) void pgemm_epilogue4_kernel(const PgemmParams 
 static int pg_bm(int32_t M) { return M <= 64 ? 64 : PG_BM; }
 static int pg_bk(int32_t M) { return M <= 64 ? PG_BK64 : PG_BK; }
 
+// Rows up to 64 with at least 64 groups of 256 columns (gate|up, the head) take the register-streamed kernel;
+// narrower ones (q|k|v, o, down), which it could only fill with many short k splits, the 64 x 128 tiles.
+static bool sg_use(int32_t M, int64_t N) { return M <= 64 && N >= 64 * 2 * SG_CPT; }
+// column tiles per wave: 2, or 4 where 2 would give more column groups than the 256 CUs hold at once (the
+// vocabulary head: one round of workgroups instead of two; measured 255 against 272 us on the 8B head)
+static int sg_tn(int64_t N) { return (N + 2 * SG_CPT - 1) / (2 * SG_CPT) > 256 ? 4 : 2; }
+
 void pgemm_plan(PgemmParams& p, int target_blocks) {
+  if (sg_use(p.M, p.N)) {
+    // column groups of 256, k split in whole chunks (at least two a split) so that the workgroups, one a CU,
+    // fit the target at once
+    const int tn = sg_tn(p.N);
+    const int64_t groups = (p.N + tn * SG_CPT - 1) / (tn * SG_CPT);
+    const int64_t chunks = (p.K + SG_KC - 1) / SG_KC;
+    int64_t ks = (int64_t)target_blocks / groups;
+    ks = std::max<int64_t>(1, std::min<int64_t>(ks, chunks / 2));
+    p.kslice = (chunks + ks - 1) / ks * SG_KC;
+    p.ksplit = (int32_t)((p.K + p.kslice - 1) / p.kslice);
+    return;
+  }
   const int64_t tiles = ((p.N + PG_BN - 1) / PG_BN) * ((p.M + pg_bm(p.M) - 1) / pg_bm(p.M));
   int64_t ks = (target_blocks + tiles - 1) / tiles;
   const int bk = pg_bk(p.M);
@@ -278,13 +433,24 @@ void pgemm_plan(PgemmParams& p, int target_blocks) {
 }
 
 hipError_t pgemm_launch(const PgemmParams& p, int mode, hipStream_t s) {
-  if (p.M < 1 || p.K % 8 != 0 || p.kslice % pg_bk(p.M) != 0) return hipErrorInvalidValue;
-  const int bm = pg_bm(p.M);
-  const dim3 grid((unsigned)((p.N + PG_BN - 1) / PG_BN), (unsigned)((p.M + bm - 1) / bm), (unsigned)p.ksplit);
-  if (bm == 64)
-    hipLaunchKernelGGL((pgemm_kernel<64, PG_BK64>), grid, dim3(PG_THREADS), 0, s, p);
-  else
-    hipLaunchKernelGGL((pgemm_kernel<128, PG_BK>), grid, dim3(PG_THREADS), 0, s, p);
+  if (p.M < 1 || p.K % 8 != 0) return hipErrorInvalidValue;
+  if (sg_use(p.M, p.N)) {
+    if (p.kslice % SG_KC != 0) return hipErrorInvalidValue;
+    const int tn = sg_tn(p.N);
+    const dim3 grid((unsigned)((p.N + tn * SG_CPT - 1) / (tn * SG_CPT)), 1, (unsigned)p.ksplit);
+    if (tn == 4)
+      hipLaunchKernelGGL(sgemm_kernel<4>, grid, dim3(SG_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL(sgemm_kernel<2>, grid, dim3(SG_THREADS), 0, s, p);
+  } else {
+    if (p.kslice % pg_bk(p.M) != 0) return hipErrorInvalidValue;
+    const int bm = pg_bm(p.M);
+    const dim3 grid((unsigned)((p.N + PG_BN - 1) / PG_BN), (unsigned)((p.M + bm - 1) / bm), (unsigned)p.ksplit);
+    if (bm == 64)
+      hipLaunchKernelGGL((pgemm_kernel<64, PG_BK64>), grid, dim3(PG_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL((pgemm_kernel<128, PG_BK>), grid, dim3(PG_THREADS), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mode == PG_NONE) return e;
   const int64_t cols = mode == PG_GATEUP ? p.N / 2 : p.N;
