@@ -1,10 +1,11 @@
 // The sampling exit of a decode step for gfx950: one draw per row of logits.
 //
-// Order of the "decode-ops" page ("Method"): divide by the temperature, keep the top-k, apply top-p over
-// the renormalised survivors, and take the inverse CDF at the caller's uniform draw, the survivors in
-// descending order with ties to the lower index. Top-p keeps a survivor while the mass of the survivors
-// before it is below p (so the kept set is the shortest prefix reaching p, the HuggingFace warper rule the
-// page names); the token is the first kept survivor whose cumulative renormalised probability exceeds u.
+// Stages in the sequence of the "decode-ops" page ("Method"): temperature, the k-largest cut, the
+// probability-mass cut, then the caller's uniform draw chooses among what is left by its cumulative
+// distribution; candidates rank by logit, equal logits lower index first. A candidate stays while the weight
+// ranked ahead of it is under p (the shortest prefix whose weight reaches p: the HuggingFace warper rule the
+// page names), and the token is the first staying candidate where the running share of the staying weight
+// passes u.
 // Temperature 0 is the greedy exit: the lowest index holding the maximum.
 //
 // A positive temperature does not change the order of the logits, so the survivors are chosen on the raw

@@ -545,9 +545,9 @@ __device__ __forceinline__ void sk_attention_items(const StepParams* pp, int l, 
 }
 
 // The merges this workgroup owns (query head hq by workgroup nwg - 1 - hq, from the end, away from the first
-// items), which write the tagged attention output. They run after the workgroup's first o weight loads are
-// issued (a merge holds few registers): a merging workgroup has no item, so those loads go out as soon as its
-// q|k|v rows are done and have landed long before the parts it waits for.
+// items), which write the tagged attention output. They run before the workgroup's first o weight loads are
+// issued: loads return in order, so a merge polling behind those loads would see its parts only once they had
+// landed (measured: 3.1725 against 3.179 ms a step with 8 loads a lane in the ring).
 template <typename T, int HD>
 __device__ __forceinline__ void sk_attention_merges(const StepParams* pp, int l, int pos, uint32_t tag) {
   const StepParams p = *pp;
@@ -619,8 +619,12 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
   for (int o = 0; o < n_ops; ++o) {
     const SkOp<QW> f = sk_op<QW>(p, R, s_layers, o, wave);
     // The op's first SK_R loads go out before its input is waited for (for o: after this workgroup's attention
-    // items, which need the registers, and before its merges), so the weights stream while the producers finish.
-    if (f.kind == OP_O) sk_attention_items<T, HD>(&p, f.l, pos, tag);
+    // items, which need the registers, and after its merges, whose polls would otherwise return only once those
+    // loads had landed), so the weights stream while the producers finish.
+    if (f.kind == OP_O) {
+      sk_attention_items<T, HD>(&p, f.l, pos, tag);
+      sk_attention_merges<T, HD>(&p, f.l, pos, tag);
+    }
     uint4 ring[SK_R];
     float sring[SK_R];   // int8 packs: each slot's scale
     if (f.npos > 0) {
@@ -631,7 +635,6 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
         if constexpr (QW) sring[j] = gload<float>(sa);
       }
     }
-    if (f.kind == OP_O) sk_attention_merges<T, HD>(&p, f.l, pos, tag);
     // ---- the op's input ----
     SkOut out;
     out.tag = atag;

@@ -253,12 +253,12 @@ int32_t llmk_argmax_noalloc(const float* logits, int64_t len_logits, int64_t row
 /* Workspace bytes llmk_sample needs for these sizes (0: none), or -status for invalid sizes. */
 int64_t llmk_sample_workspace_bytes(int64_t rows, int64_t n, float temperature, int32_t top_k);
 
-/* One draw per row of logits ([dops] "Method" fixes the order of the cuts and the tie rule): the logits are
- * scaled by 1/temperature, only the top_k largest stay (equal logits ranked by the lower index first), the
- * survivors' probabilities are renormalised and cut by top_p, and the caller's uniform picks the token by
- * the inverse CDF over what is left. top-p keeps a survivor while the mass of
- * the survivors before it is below top_p (the first is always kept); the token is the first kept survivor
- * whose cumulative renormalised probability exceeds u[r]. temperature 0 is greedy (the lowest index
+/* One sampled token per row of logits ([dops] "Method" sets the sequence of the cuts and how ties rank).
+ * Candidates: the top_k largest logits, equal logits ranked lower index first. Their weights: softmax of
+ * logit / temperature over the candidates. Walking the candidates in rank order, one stays while the total
+ * weight of those ranked ahead of it is under top_p, so the first always stays; the row's token is the first
+ * staying candidate at which the running sum of the staying weights, taken as a fraction of their total,
+ * passes u[r]. temperature 0 is greedy (the lowest index
  * holding the row maximum). A NaN logit counts as -inf and -0 as +0; a draw below 0 or NaN counts as 0, a
  * draw of 1 or more takes the last kept survivor with mass. The same row and draw always give the same
  * token (no float atomics).

@@ -1,9 +1,9 @@
 """THE ORACLE's sampler -- test infrastructure only (see the package docstring).
 
-One draw of the decode step's sampling exit, in fp64, in the order of the cuts the "decode-ops" page
-fixes ("Method"): scale by the temperature, keep the k largest, cut the renormalised survivors by p, then
-let an explicit uniform pick a survivor through the inverse CDF; survivors are ranked by logit, equal
-logits by the lower index first. The page gives the order and the tie rule; the
+One draw of the decode step's sampling exit, in fp64, with its stages in the sequence the "decode-ops" page
+sets out ("Method"): temperature first, then the k-largest cut, then the probability-mass cut, then a
+caller-supplied uniform chooses the token from what is left by its cumulative distribution; candidates rank by
+logit, equal logits by the lower index first. The page gives the sequence and the tie rule; the
 top-p cut and the inverse CDF are taken at their plainest readings (the HuggingFace warper rule the page
 names as its reference):
   - top-p keeps a survivor while the probability mass of the survivors before it is below p, so the first

@@ -5,8 +5,9 @@ CDF at the step's uniform) applied to the oracle's logits of that step, the toke
 all inside the captured loop. The GPU samples from fp32 logits that agree with the oracle's within the bar, so a
 step's token must equal the oracle's unless a decision of that step sits within 1e-4 of a boundary (the
 uniform against a cumulative probability, the mass before a survivor against top-p, the k-th against the
-(k+1)-th scaled logit); such a difference ends the comparison (the continuations differ from there by
-construction), and at least half the steps must agree. Temperature 0 reproduces the greedy loop. Sizes: the toy
+(k+1)-th scaled logit); there the oracle takes the GPU's token as the next input, so every one of the steps is
+compared on the same inputs, and all but those boundary steps must agree. Temperature 0 reproduces the greedy
+loop. Sizes: the toy
 decoder (a 40-entry vocabulary: the one-workgroup sampler), the Qwen3-0.6B shape (151,936 logits: the sliced
 sampler) in the per-operation form, and the Llama-3-8B shape after its 4,096-position prefix in the persistent
 form the benchmark times.
@@ -80,20 +81,21 @@ def run_case(s, step_path, n_pre, n, T, k, p, label):
     c = m.new_cache(n_pre + n)
     if prefix:
         c.fill_prefix(prefix)
-    t, compared = first, 0
+    t, equal, boundary = first, 0, []
     for i in range(n):
         lg, _ = m.forward_token(t, n_pre + i, c)
         u = float(draws[i])
         want = sampler.sample(lg, T, k, p, u)
         if got[i] != want:
-            # equal tokens keep both continuations on the same inputs; a differing one must sit at a boundary
+            # a differing token must sit at a boundary; the oracle then follows the GPU's token
             assert not clear_of_boundaries(lg, T, k, p, u), f"{label}: step {i}: gpu {got[i]} oracle {want}"
-            say(f"{label}: step {i} sits within {EPS} of a boundary: gpu {got[i]}, oracle {want}; comparison ends")
-            break
-        compared += 1
-        t = want
-    say(f"{label}: {compared} of {n} steps equal, tokens {got}")
-    assert compared >= n // 2
+            say(f"{label}: step {i} sits within {EPS} of a boundary: gpu {got[i]}, oracle {want}; the oracle follows")
+            boundary.append(i)
+        else:
+            equal += 1
+        t = got[i]
+    say(f"{label}: {equal} of {n} steps equal, boundary steps {boundary}, tokens {got}")
+    assert equal + len(boundary) == n and len(boundary) <= max(1, n // 8)
     return got
 
 
