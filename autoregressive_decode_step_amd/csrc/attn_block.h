@@ -214,7 +214,7 @@ __device__ __forceinline__ void attn_block(const AttnParams& p, const int kvh, c
     const int t = min((T0) + rem / RVG, te - 1);                                                   \
     const T* src = (which == 0 ? Kb : Vb) + (tile_row0 + t) * rstride + (rem % RVG) * EPG;         \
     if (HD >= EPG) {                                                                              \
-      reg[k] = idx < NVT ? gload<uint4>(src) : make_uint4(0, 0, 0, 0);                              \
+      reg[k] = idx < NVT ? gload_stream(src) : make_uint4(0, 0, 0, 0);                              \
     } else {                                                                                      \
       reg[k] = make_uint4(idx < NVT ? gload<uint32_t>(src) : 0u,                                  \
                           (idx < NVT && HD * (int)sizeof(T) >= 8) ? gload<uint32_t>(src + 4 / sizeof(T)) : 0u, \

@@ -198,6 +198,21 @@ __device__ __forceinline__ V gload(const void* ptr) {
   }
 }
 
+// A 16-byte load of data read once and not again soon (weights streamed by a decode step): marked
+// non-temporal, so the lines it brings do not displace what the caches hold for other reads (the activations
+// workgroups hand each other, the attention's working set). Measured on the persistent 8B step: 3.176 -> 2.940 ms.
+__device__ __forceinline__ uint4 gload_stream(const void* ptr) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)ptr));
+}
+
+// load_raw for a weight stream: the 16-byte slices non-temporal (gload_stream), narrower ones as load_raw
+template <typename T, int VEC>
+__device__ __forceinline__ typename Raw<T, VEC>::type load_raw_stream(const T* p) {
+  if constexpr (sizeof(typename Raw<T, VEC>::type) == 16) return gload_stream(p);
+  else return load_raw<T, VEC>(p);
+}
+
 // ---- paged K/V: a slot's positions reach their blocks through its row of the block table ----------------
 
 // The block table as the kernels take it: table == nullptr for contiguous slots.

@@ -126,8 +126,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_t_kernel(const GemvParams p
 #define LLMK_ISSUE(RA, RB, R)                                         \
   _Pragma("unroll") for (int u = 0; u < U; ++u) {                     \
     const int64_t rr = min((R) + u * RPI + lr, last);                 \
-    RA[u] = load_raw<T, VEC>(wa + rr * lda);                          \
-    if (NACC == 2) RB[u] = load_raw<T, VEC>(wb + rr * lda);           \
+    RA[u] = load_raw_stream<T, VEC>(wa + rr * lda);                   \
+    if (NACC == 2) RB[u] = load_raw_stream<T, VEC>(wb + rr * lda);    \
   }
   LLMK_ISSUE(a0, b0, kw0)
 
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void head_kernel(const HeadParams p) 
       for (int pp = 0; pp < NP; ++pp) {
         const int64_t cidx = (int64_t)(pp * 64 + lane) * VEC;
         const int64_t cc = cidx < p.cols ? cidx : 0;
-        cur[rr][pp] = load_raw<T, VEC>(W + row * p.cols + cc);
+        cur[rr][pp] = load_raw_stream<T, VEC>(W + row * p.cols + cc);
       }
     }
   };

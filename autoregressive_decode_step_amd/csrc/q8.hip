@@ -121,7 +121,7 @@ __global__ __launch_bounds__(Q8_THREADS) void rowdot_q8_kernel(const RowdotParam
       _Pragma("unroll") for (int pp = 0; pp < NP; ++pp) {                                             \
         const int64_t cc = (int64_t)(pp * 64 + lane) * Q8_V;                                          \
         const int64_t col = c0 + (cc < seg ? cc : 0);                                                 \
-        BUF[m][rr][pp] = *reinterpret_cast<const uint4*>(cw + col);                                   \
+        BUF[m][rr][pp] = gload_stream(cw + col);                                                      \
         SB[m][rr][pp] = sw[col / Q8_GROUP];                                                           \
       }                                                                                               \
     }                                                                                                 \

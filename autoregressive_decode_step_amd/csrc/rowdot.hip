@@ -60,7 +60,7 @@ __global__ __launch_bounds__(RD_THREADS) void rowdot_kernel(const RowdotParams p
       const T* base = LLMK_ROW_PTR(row, m) + c0;                                       \
       _Pragma("unroll") for (int pp = 0; pp < NP; ++pp) {                              \
         const int64_t cc = (int64_t)(pp * 64 + lane) * VEC;                            \
-        BUF[m][rr][pp] = load_raw<T, VEC>(base + (cc < seg ? cc : 0));                 \
+        BUF[m][rr][pp] = load_raw_stream<T, VEC>(base + (cc < seg ? cc : 0));          \
       }                                                                                \
     }                                                                                  \
   }

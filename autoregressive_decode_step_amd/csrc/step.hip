@@ -464,7 +464,7 @@ __device__ __forceinline__ void sk_block(uint4 (&ring)[SK_R], float (&sring)[SK_
     }
     if constexpr (ISSUE) {
       const float* sa = nullptr;
-      ring[j] = gload<uint4>(sk_addr<QW>(is, ib + j, wave, lane16, &sa));
+      ring[j] = gload_stream(sk_addr<QW>(is, ib + j, wave, lane16, &sa));
       if constexpr (QW) sring[j] = gload<float>(sa);
     }
     if (c == mask) {
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
 #pragma unroll
       for (int j = 0; j < SK_R; ++j) {
         const float* sa = nullptr;
-        ring[j] = gload<uint4>(sk_addr<QW>(f, j, wave, lane16, &sa));
+        ring[j] = gload_stream(sk_addr<QW>(f, j, wave, lane16, &sa));
         if constexpr (QW) sring[j] = gload<float>(sa);
       }
     }
