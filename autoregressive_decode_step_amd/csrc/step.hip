@@ -599,12 +599,15 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
     d.v = s.v;
   }
   SkRows R;
-  R.q = sk_range(p.qd, w, nwg);
-  R.k = sk_range(p.kvd, w, nwg);
-  R.v = sk_range(p.kvd, w, nwg);
-  R.d = sk_range(p.d, w, nwg);
-  R.f = sk_range(p.F, w, nwg);
-  R.h = sk_range(p.V, w, nwg);
+  // workgroup w runs on XCD w % 8: the rows of XCD x's workgroups are one contiguous eighth of each matrix
+  // (measured 0.35% faster than giving workgroup w the w-th share)
+  const int wc = nwg % 8 == 0 ? (w % 8) * (nwg / 8) + w / 8 : w;
+  R.q = sk_range(p.qd, wc, nwg);
+  R.k = sk_range(p.kvd, wc, nwg);
+  R.v = sk_range(p.kvd, wc, nwg);
+  R.d = sk_range(p.d, wc, nwg);
+  R.f = sk_range(p.F, wc, nwg);
+  R.h = sk_range(p.V, wc, nwg);
   __syncthreads();
 
 #define SK_X(V) (p.x + (int64_t)(V) * p.x_stride)
