@@ -599,9 +599,12 @@ __global__ __launch_bounds__(SK_THREADS, 1) void step_kernel(const StepParams p)
     d.v = s.v;
   }
   SkRows R;
-  // workgroup w runs on XCD w % 8: the rows of XCD x's workgroups are one contiguous eighth of each matrix
-  // (measured 0.35% faster than giving workgroup w the w-th share)
-  const int wc = nwg % 8 == 0 ? (w % 8) * (nwg / 8) + w / 8 : w;
+  // Workgroup w runs on XCD w % 8. Where a workgroup's share of gate|up is large (at least 256 KB; 917 KB in the
+  // Llama-3-8B shape) the rows of XCD x's workgroups form one contiguous eighth of each matrix: measured 0.35%
+  // faster there than workgroup w taking the w-th share, and 1.1% slower in the Qwen3-0.6B shape (48 KB a
+  // workgroup), which keeps the w-th share.
+  const int64_t gu_share = (int64_t)(p.F / nwg) * 2 * p.d * (QW ? 1 : 2);
+  const int wc = nwg % 8 == 0 && gu_share >= (256 << 10) ? (w % 8) * (nwg / 8) + w / 8 : w;
   R.q = sk_range(p.qd, wc, nwg);
   R.k = sk_range(p.kvd, wc, nwg);
   R.v = sk_range(p.kvd, wc, nwg);
